@@ -1,0 +1,177 @@
+"""Pins for the reference planner (oracle/planner_ref.py).
+
+The pages fix no formula for chunk positions or tile orders (Syncopate summary
+page, "Core method", paper sec. 5.1-5.2, Fig. 6), so this planner is pinned
+by (1) hand-worked fixtures in tests/golden/plan_fixtures.json, (2) a direct
+simulation of ring all-gather and ring reduce-scatter message passing,
+(3) invariants checked over a brute-force enumeration of small descriptors,
+with the dependency sets recomputed row by row.
+"""
+import itertools
+import json
+import os
+
+import pytest
+
+from oracle import planner_ref as P
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "plan_fixtures.json")
+
+
+def _desc(d):
+    kw = dict(d)
+    return P.PlanDesc(**{("explicit_order" if k == "explicit_order" else k): v for k, v in kw.items()})
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLD))["cases"], ids=lambda c: c["name"])
+def test_hand_worked_fixture(case):
+    t = P.plan_ref(_desc(case["desc"]))
+    for key, want in case["expect"].items():
+        assert list(getattr(t, key)) == want, key
+
+
+def _simulate_ring_allgather(W, r, d):
+    """Each rank forwards what it last received to rank+d; returns the shards rank
+    r holds, in the order it gets them (its own first)."""
+    last = list(range(W))
+    got = [[w] for w in range(W)]
+    for _ in range(W - 1):
+        incoming = [last[(w - d) % W] for w in range(W)]
+        for w in range(W):
+            got[w].append(incoming[w])
+        last = incoming
+    return got[r]
+
+
+def _simulate_ring_reduce_scatter(W, r, d):
+    """Ring reduce-scatter that forwards to rank+d and ends with every rank holding
+    its own shard fully reduced.  Returns the order in which rank r's own partial
+    results are consumed (added into the travelling sums)."""
+    # at step 0 rank w starts the sum for the shard that must end at w + d*(W-1)
+    carry = {w: ((w + d * (W - 1)) % W, {w}) for w in range(W)}
+    used = {w: [carry[w][0]] for w in range(W)}
+    for _ in range(W - 1):
+        nxt = {}
+        for w in range(W):
+            shard, who = carry[(w - d) % W]
+            nxt[w] = (shard, who | {w})
+            used[w].append(shard)
+        carry = nxt
+    for w in range(W):
+        assert carry[w][0] == w and carry[w][1] == set(range(W))
+    return used[r]
+
+
+@pytest.mark.parametrize("W,r,d", [(W, r, d) for W in (1, 2, 3, 4, 8) for r in range(W) for d in (1, -1)])
+def test_ring_positions_follow_message_passing(W, r, d):
+    ag = P.plan_ref(P.PlanDesc(op=P.OP_AG_GEMM, m=W, n=1, k=1, world=W, rank=r, ring_dir=d,
+                               tile_m=1, tile_n=1))
+    assert ag.arrival == _simulate_ring_allgather(W, r, d)
+    rs = P.plan_ref(P.PlanDesc(op=P.OP_GEMM_RS, m=W, n=1, k=1, world=W, rank=r, ring_dir=d,
+                               tile_m=1, tile_n=1))
+    assert rs.arrival == _simulate_ring_reduce_scatter(W, r, d)
+    assert rs.arrival[-1] == r
+
+
+def _check_invariants(desc, t):
+    C, T = t.num_chunks, t.num_tiles
+    M = desc.world * desc.n if desc.op == P.OP_RING_ATTN else desc.m
+    # chunks partition [0, M): contiguous, non-empty
+    assert t.chunk_begin[0] == 0 and t.chunk_begin[-1] == M and len(t.chunk_begin) == C + 1
+    assert all(t.chunk_begin[c] < t.chunk_begin[c + 1] for c in range(C))
+    # arrival is a permutation, chunk_pos its inverse
+    assert sorted(t.arrival) == list(range(C))
+    assert all(t.chunk_pos[t.arrival[p]] == p for p in range(C))
+    assert sorted(t.tile_order) == list(range(T))
+    # deps == brute force, row by row
+    for tile in range(T):
+        i = tile // t.tiles_n
+        deps = t.dep_idx[t.dep_ptr[tile]:t.dep_ptr[tile + 1]]
+        if desc.op == P.OP_RING_ATTN:
+            want = list(range(C))
+        else:
+            rows = range(i * desc.tile_m, min((i + 1) * desc.tile_m, desc.m))
+            want = sorted({next(c for c in range(C) if t.chunk_begin[c] <= row < t.chunk_begin[c + 1])
+                           for row in rows})
+        assert deps == want
+    # inv is the transpose of deps
+    pairs_dep = {(tile, c) for tile in range(T) for c in t.dep_idx[t.dep_ptr[tile]:t.dep_ptr[tile + 1]]}
+    pairs_inv = {(tile, c) for c in range(C) for tile in t.inv_idx[t.inv_ptr[c]:t.inv_ptr[c + 1]]}
+    assert pairs_dep == pairs_inv and len(t.dep_idx) == len(t.inv_idx)
+    assert all(t.inv_idx[t.inv_ptr[c]:t.inv_ptr[c + 1]] == sorted(t.inv_idx[t.inv_ptr[c]:t.inv_ptr[c + 1]])
+               for c in range(C))
+    assert t.tiles_in == [t.inv_ptr[c + 1] - t.inv_ptr[c] for c in range(C)]
+    # keys: the last (AG) or first (RS) position among a tile's chunks
+    for tile in range(T):
+        ps = [t.chunk_pos[c] for c in t.dep_idx[t.dep_ptr[tile]:t.dep_ptr[tile + 1]]]
+        assert t.tile_key[tile] == (min(ps) if desc.op == P.OP_GEMM_RS else max(ps))
+    keys = [t.tile_key[x] for x in t.tile_order]
+    if desc.tile_order in (P.ORDER_CHUNK_MAJOR, P.ORDER_SWIZZLED):
+        assert keys == sorted(keys)
+    else:
+        assert t.tile_order == list(range(T))
+    # the local shard is resident for AG/attention only
+    for c in range(C):
+        own = (c // desc.split) == desc.rank
+        assert t.resident[c] == int(own and desc.local_resident and desc.op != P.OP_GEMM_RS)
+    # aligned case: one dependency per tile, equal tile counts per chunk
+    if desc.op != P.OP_RING_ATTN:
+        R = desc.m // desc.world
+        if R % desc.split == 0 and (R // desc.split) % desc.tile_m == 0:
+            assert all(t.dep_ptr[x + 1] - t.dep_ptr[x] == 1 for x in range(T))
+            assert set(t.tiles_in) == {(R // desc.split // desc.tile_m) * t.tiles_n}
+
+
+def _enumerate():
+    for op in (P.OP_AG_GEMM, P.OP_GEMM_RS):
+        for W in (1, 2, 3, 4):
+            for rows_per in (1, 2, 3, 5):
+                m = W * rows_per
+                for s in range(1, min(3, rows_per) + 1):
+                    for tm in (1, 2, 3, 4):
+                        if -(-m // tm) > 8:
+                            continue
+                        for order in (0, 1, 2):
+                            for d in (1, -1):
+                                for r in range(W):
+                                    yield P.PlanDesc(op=op, m=m, n=5, k=3, world=W, rank=r, ring_dir=d,
+                                                     split=s, tile_m=tm, tile_n=2, tile_order=order,
+                                                     group_m=2)
+    for W, n, s, tm in itertools.product((1, 2, 3), (2, 3), (1, 2), (1, 3)):
+        yield P.PlanDesc(op=P.OP_RING_ATTN, m=5, n=n, k=8, world=W, rank=W - 1, split=s, tile_m=tm,
+                         tile_n=1, heads_q=4, heads_kv=2, tile_order=1)
+
+
+def test_invariants_brute_force_enumeration():
+    count = 0
+    for desc in _enumerate():
+        _check_invariants(desc, P.plan_ref(desc))
+        count += 1
+    assert count > 1000
+
+
+def test_explicit_orders_all_permutations():
+    for perm in itertools.permutations(range(4)):
+        desc = P.PlanDesc(op=P.OP_AG_GEMM, m=8, n=3, k=2, world=4, rank=2, pattern=P.PAT_EXPLICIT,
+                          explicit_order=list(perm), split=2, tile_m=3, tile_n=2)
+        t = P.plan_ref(desc)
+        _check_invariants(desc, t)
+        assert [t.arrival[p] // 2 for p in range(0, 8, 2)] == list(perm)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(m=10, world=4),                       # m % world
+    dict(split=0), dict(split=3),             # split out of [1, R]
+    dict(rank=4), dict(ring_dir=0), dict(op=9), dict(tile_order=5),
+    dict(pattern=1, explicit_order=[0, 0, 1, 2]),
+])
+def test_rejects_invalid(bad):
+    base = dict(op=P.OP_AG_GEMM, m=8, n=4, k=4, world=4, split=1, tile_m=2, tile_n=2)
+    base.update(bad)
+    with pytest.raises(P.PlanError):
+        P.plan_ref(P.PlanDesc(**base))
+
+
+def test_attention_requires_grouped_heads():
+    with pytest.raises(P.PlanError):
+        P.plan_ref(P.PlanDesc(op=P.OP_RING_ATTN, m=4, n=4, k=8, world=2, tile_m=2, heads_q=3, heads_kv=2))
