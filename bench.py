@@ -1,0 +1,189 @@
+"""Benchmark: AG-GEMM share, Llama-3-8B FFN up-projection at TP=8, on one MI355X.
+
+One step = one sync_ag_gemm call: the copy agent stages the 7 peer chunks of
+A (8192 x 4096 bf16, 8 shards of 1024 rows, N(0,1)/64) from the peer HBM
+region while the persistent MFMA GEMM multiplies the gathered A by
+B (4096 x 1792 bf16) into C (8192 x 1792 fp32), each tile waiting on the
+chunks it reads.  Inputs are resident in HBM before the timed region.
+
+Printed: one JSON line with the metric (TFLOP/s of the overlapped call), the
+overlap efficiency (overlapped time / max(compute-only, copy-only)), the
+roofline of the dominant kernel (the GEMM; its launch duration from HIP events
+recorded by the library on the GEMM's own stream during the timed steps), and
+the CPU oracle's throughput on a bounded sample of the same product.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "AG-GEMM TFLOP/s (bf16, % MFMA peak) + overlap efficiency, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+M, N, K, WORLD = 8192, 1792, 4096, 8
+DIVISOR = 64.0
+
+BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64)}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--backend", default="cu32", choices=sorted(BACKENDS))
+    p.add_argument("--split", type=int, default=1)
+    p.add_argument("--tile", default="256x256")
+    p.add_argument("--order", default="chunk_major", choices=["row_major", "chunk_major", "swizzled"])
+    p.add_argument("--c-dtype", default="f32", choices=["f32", "bf16"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported on this single-GPU "
+              "build (the multi-GPU exchange is not part of it).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from communication_overlap_gemm_amd import _abi as A
+    from communication_overlap_gemm_amd import inputs
+
+    dev = torch.device("cuda:0")
+    tm, tn = (int(x) for x in args.tile.split("x"))
+    order = {"row_major": A.SYNC_ORDER_ROW_MAJOR, "chunk_major": A.SYNC_ORDER_CHUNK_MAJOR,
+             "swizzled": A.SYNC_ORDER_SWIZZLED}[args.order]
+    c_dtype = A.SYNC_DTYPE_F32 if args.c_dtype == "f32" else A.SYNC_DTYPE_BF16
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, split=args.split, tile_m=tm, tile_n=tn,
+                                   tile_order=order))
+    tabs = A.sync_plan_export(plan)
+
+    a_bits, b_bits = inputs.gemm_operands(M, N, K, DIVISOR)
+    a_peer = torch.from_numpy(a_bits.view(np.int16)).to(dev)
+    b = torch.from_numpy(b_bits.view(np.int16)).to(dev)
+    a_local = torch.zeros_like(a_peer)
+    for c in range(tabs["num_chunks"]):
+        if tabs["resident"][c]:
+            r0, r1 = tabs["chunk_begin"][c], tabs["chunk_begin"][c + 1]
+            a_local[r0:r1] = a_peer[r0:r1]
+    c_out = torch.empty((M, N), dtype=torch.float32 if c_dtype == A.SYNC_DTYPE_F32 else torch.int16, device=dev)
+    nws = A.sync_workspace_size(plan)
+    ws_raw = torch.zeros(nws // 4 + 64, dtype=torch.int32, device=dev)
+    ws = ws_raw[((-ws_raw.data_ptr()) % 256) // 4:]
+    stream = torch.cuda.current_stream()
+    A.sync_workspace_init(plan, ws, stream)
+
+    backend, cus = BACKENDS[args.backend]
+
+    def timed_loop(cfg, steps, warmup):
+        for _ in range(warmup):
+            A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c_out, c_dtype, ws, stream, None)
+        torch.cuda.synchronize()
+        A.sync_read_timings(0)  # drop warm-up records
+        cfg_t = A.make_cfg(cfg.backend, cfg.copy_cus, cfg.timeout_ns, None, cfg.flags | A.SYNC_RUN_TIMED)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            A.sync_ag_gemm(plan, cfg_t, a_peer, a_local, b, c_out, c_dtype, ws, stream, None)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        rc, chunk = A.sync_workspace_status(ws, stream)
+        if rc != A.SYNC_OK:
+            raise SystemExit(f"device wait timed out on chunk {chunk}")
+        recs = A.sync_read_timings(4096)
+        return wall, recs
+
+    # overlapped (the metric), compute-only on the full chip, copy-only
+    t_ovl, recs = timed_loop(A.make_cfg(backend, cus), args.steps, args.warmup)
+    k_ms = float(np.mean([r[0] for r in recs]))
+    cp_ms = float(np.mean([r[1] for r in recs]))
+    t_comp, recs_c = timed_loop(A.make_cfg(A.SYNC_COPY_PRESET), args.steps, args.warmup)
+    k_comp_ms = float(np.mean([r[0] for r in recs_c]))
+    t_copy, recs_p = timed_loop(A.make_cfg(backend, cus, flags=A.SYNC_RUN_COPY_ONLY), args.steps, args.warmup)
+    copy_only_ms = float(np.mean([r[1] for r in recs_p]))
+
+    flops = 2.0 * M * N * K
+    value = flops / t_ovl / 1e12
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    copied = sum(int(tabs["chunk_begin"][c + 1] - tabs["chunk_begin"][c]) for c in range(tabs["num_chunks"])
+                 if not tabs["resident"][c]) * K * 2
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_ovl * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "AG-GEMM share, Llama-3-8B FFN up-projection at TP=8: A 8192x4096 bf16 gathered from "
+                        "8 row chunks (N(0,1)/64), B 4096x1792 bf16, C 8192x1792 " + args.c_dtype,
+            "m": M, "n": N, "k": K, "world": WORLD, "split": args.split, "tile": args.tile,
+            "tile_order": args.order, "copy_backend": args.backend, "b_layout": "kn",
+        },
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "overlap": {
+            "t_overlap_ms": round(t_ovl * 1e3, 4),
+            "t_compute_only_ms": round(t_comp * 1e3, 4),
+            "t_copy_only_ms": round(t_copy * 1e3, 4),
+            "ratio": round(t_ovl / max(t_comp, t_copy), 4),
+            "gemm_kernel_ms_overlapped": round(k_ms, 4),
+            "gemm_kernel_ms_compute_only": round(k_comp_ms, 4),
+            "copy_agent_ms": round(copy_only_ms, 4),
+            "copy_agent_GBps": round(2 * copied / (copy_only_ms * 1e-3) / 1e9, 1),
+            "copy_agent_ms_in_overlap": round(cp_ms, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "gemm_persistent<256,256,KN,f32,AG>",
+            "flops_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a_bits, b_bits, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(a_bits, b_bits, target_s):
+    """The fp64 oracle on the first R rows of A (R sized for ~target_s seconds)."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.gemm_f64(a_bits[:rows], b_bits, rows, N, K, threads=threads)
+    probe = time.perf_counter() - t0
+    rows = int(max(16, min(M, rows * target_s / max(probe, 1e-3))))
+    rows -= rows % 16
+    t0 = time.perf_counter()
+    oracle.gemm_f64(np.ascontiguousarray(a_bits[:rows]), b_bits, rows, N, K, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle GEMM on the first {rows} of {M} rows of A (full N={N}, K={K}); {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,63 @@
+"""Builds libsync_overlap.so (the C-ABI library) for gfx950 with hipcc.
+
+Every source is compiled to an object under _build/ (in parallel) and linked
+into communication_overlap_gemm_amd/libsync_overlap.so.  HIP sources are
+compiled with packed-FP32 instruction selection disabled.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libsync_overlap.so")
+ARCH = os.environ.get("SYNC_OFFLOAD_ARCH", "gfx950")
+
+HIP_SOURCES = ["kernels/gemm_persistent.hip", "kernels/copy_agent.hip", "kernels/ring_attn.hip", "runtime.cpp"]
+CXX_SOURCES = ["planner.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-x", "hip", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
+    path = os.path.join(CSRC, src)
+    if src in CXX_SOURCES:
+        cmd = ["g++"] + COMMON + ["-Wall", "-c", path, "-o", obj]
+    else:
+        cmd = [HIPCC] + COMMON + HIP_FLAGS + ["-c", path, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {src}\n{err}")
+    if err.strip() and verbose:
+        print(err)
+    return obj
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    sources = [s for s in HIP_SOURCES + CXX_SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), sources))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-Wl,--no-undefined"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,103 @@
+// Device helpers shared by the gfx950 kernels: bf16 vector types, the
+// cross-XCD flag protocol (bounded relaxed polling, one acquire; release then
+// publish), and the workspace layout.
+//
+// Flag protocol.  The pages' asynchronous backends signal chunk completion
+// through global-memory flags (Syncopate summary page, "Core method", paper
+// sec. 5.2, Fig. 7).  On MI355X the producer (copy agent, SDMA engine or GEMM
+// epilogue) and the consumer may sit on different XCDs, each with its own L2,
+// so the producer publishes with an agent-scope release (its stores are
+// written back past its L2) and the consumer, after seeing the flag with
+// relaxed agent-scope polls, performs one agent-scope acquire (stale lines in
+// its own caches are dropped) before it reads the chunk.  Flags hold the
+// epoch of the call that raised them, so they are never cleared between
+// calls; every wait is bounded by a wall-clock limit and reports the chunk it
+// gave up on in the workspace error word.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace syncov {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Workspace header words (uint32 index).  The flag and counter arrays follow
+// at the offsets the host computes (see runtime.cpp: ws_layout()).
+enum : int {
+  WS_EPOCH = 0,      // epoch of the current call (bumped by the begin kernel)
+  WS_ERR_CODE = 1,   // 0 = fine, else ERR_* below
+  WS_ERR_CHUNK = 2,  // chunk whose wait expired first
+  WS_TICKET = 3,     // reserved for dynamic tile tickets
+  WS_HEADER_WORDS = 64
+};
+enum : uint32_t { ERR_TIMEOUT = 1u };
+
+__device__ __forceinline__ uint32_t ld_relaxed_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_release_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t add_acq_rel_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool epoch_reached(uint32_t flag, uint32_t epoch) {
+  return static_cast<int32_t>(flag - epoch) >= 0;
+}
+
+// Records a timeout for `chunk` if no error is recorded yet.
+__device__ __forceinline__ void record_timeout(uint32_t* hdr, int32_t chunk) {
+  uint32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(hdr + WS_ERR_CODE, &expected, ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    __hip_atomic_store(hdr + WS_ERR_CHUNK, static_cast<uint32_t>(chunk), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Single-lane bounded wait for flags[c] to reach `epoch`.  Returns false when
+// the wall-clock limit passes or another wait has already recorded an error
+// (so that every waiter on a withheld chunk gives up promptly).  No acquire
+// here: the caller performs one after all its waits succeed.
+__device__ __forceinline__ bool wait_flag(const uint32_t* flags, int32_t c, uint32_t epoch, uint32_t* hdr,
+                                          uint64_t timeout_ticks) {
+  if (epoch_reached(ld_relaxed_agent(flags + c), epoch)) return true;
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    __builtin_amdgcn_s_sleep(2);
+    if (epoch_reached(ld_relaxed_agent(flags + c), epoch)) return true;
+    if (ld_relaxed_agent(hdr + WS_ERR_CODE) != 0) return false;
+    if (wall_clock64() - t0 > timeout_ticks) {
+      record_timeout(hdr, c);
+      return false;
+    }
+  }
+}
+
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+// Round-to-nearest-even float -> bf16 bits (inputs are finite in this library;
+// NaN is kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Persistent-kernel slot of workgroup `b` out of `g`: workgroups are handed to
+// XCDs round-robin, so consecutive slots are made to live on one XCD, and the
+// tiles one XCD works on at a time are neighbours in the traversal order
+// (they share A rows or B columns in that XCD's L2).
+__device__ __forceinline__ int32_t xcd_slot(int32_t b, int32_t g, int32_t nxcd) {
+  if (nxcd <= 1 || g % nxcd) return b;
+  return (b % nxcd) * (g / nxcd) + b / nxcd;
+}
+
+}  // namespace syncov

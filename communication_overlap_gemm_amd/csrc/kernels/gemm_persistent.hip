@@ -1,0 +1,309 @@
+// Persistent bf16 MFMA GEMM for gfx950 whose tile traversal follows a chunk
+// plan: in AG mode every tile first waits for the ready flags of the chunks of
+// A it reads; in RS mode every stored tile counts toward the chunks of C it
+// wrote and the last one raises the chunk's done flag.
+//
+// Method: Syncopate summary page, "Core method" (paper sec. 5, 5.2, Fig. 6):
+// one fused kernel; the chunk-tile dependency graph tells each tile which
+// chunks it consumes or produces; waits are inserted before consumption; the
+// tile scheduler visits chunks in communication order.  Entwine abstract:
+// tiles are ordered so output is produced for communication at a steady pace.
+//
+// gfx950 design (not the pages' Hopper/Triton design):
+//  * 256 threads = 4 wave64s in a 2x2 grid; each wave owns a (TM/2)x(TN/2)
+//    block of C built from v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
+//  * K advances 64 at a time through a double-buffered LDS ring; one barrier
+//    per step; the next step's global loads are in flight during the MFMAs.
+//  * Operands are read with raw buffer loads from a per-tile base (32-bit
+//    offsets; reads past the end return zero, so ragged M/N need no branches).
+//  * A and B fragments are stored k-contiguous in LDS (B is transposed on the
+//    way in when it is [k][n]) with a 16-byte XOR swizzle, so every fragment
+//    is one ds_read_b128 and reads are free of bank conflicts.
+//  * The epilogue stages 32-row strips of the accumulators through LDS and
+//    writes C with 16-byte buffer stores, rows past M dropped by the hardware.
+//  * One workgroup per CU walks the plan's tile order with a static stride;
+//    slots are remapped so that each XCD takes consecutive tiles of the order.
+#include "device_common.hpp"
+#include "launch_args.hpp"
+
+namespace syncov {
+
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kTK = 64;          // K per LDS stage
+constexpr int kThreads = 256;    // 4 waves
+constexpr int kSlots = kTK / 8;  // 16-byte slots per LDS row
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any num_records used here
+
+// Raw buffer resource over [base, base + bytes); word 3 selects 32-bit data
+// format as gfx9 raw buffer accesses expect.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2_t buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// 16-byte slot swizzle: rows r..r+15 reading one logical slot land in
+// distinct banks, and so do the 8 slots of one row.
+__device__ __forceinline__ int swz(int row, int slot) { return slot ^ ((row ^ (row >> 3)) & 7); }
+
+template <int TM, int TN, int BL, int CT, bool RS>
+__global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
+  constexpr int WM = TM / 2, WN = TN / 2;
+  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int A_LD = TM / 32;                             // 16-byte A loads per thread per stage
+  constexpr int B_LD_NK = TN / 32;                          // NK: 16-byte B loads per thread
+  constexpr int B_UNITS = (kTK / 8) * (TN / 4) / kThreads;  // KN: 8x4 blocks per thread
+  constexpr int ES = CT == 0 ? 4 : 2;                       // C element size
+  constexpr int SP = WN + 32 / ES;                          // staged strip pitch (elements), +32 B
+  static_assert(TM % 64 == 0 && TN % 128 == 0, "tile");
+  static_assert(B_UNITS >= 1, "tile too small for the KN loader");
+  static_assert(4 * 32 * SP * ES <= 2 * (TM + TN) * kSlots * 16, "epilogue staging must fit the LDS ring");
+
+  __shared__ u32x4_t smem[2 * (TM + TN) * kSlots];
+  __shared__ int32_t s_skip;
+  u32x4_t* const As0 = smem;
+  u32x4_t* const Bs0 = smem + 2 * TM * kSlots;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t epoch = a.hdr[WS_EPOCH];
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const int nk = static_cast<int>(K / kTK);
+
+  u32x4_t ra[A_LD];
+  u32x4_t rbn[BL == 1 ? B_LD_NK : 1];
+  u32x2_t rbk[BL == 0 ? B_UNITS : 1][8];
+
+  const int32_t slot0 = xcd_slot(blockIdx.x, gridDim.x, a.nxcd);
+  for (int32_t p = slot0; p < a.num_tiles; p += gridDim.x) {
+    const int32_t t = a.order[p];
+    const int32_t ti = t / a.tiles_n, tj = t - ti * a.tiles_n;
+    const int64_t m0 = static_cast<int64_t>(ti) * TM, n0 = static_cast<int64_t>(tj) * TN;
+    const int rows_valid = static_cast<int>((M - m0) < TM ? (M - m0) : TM);
+    const int cols_valid = static_cast<int>((N - n0) < TN ? (N - n0) : TN);
+
+    if constexpr (!RS) {
+      if (tid == 0) {
+        bool ok = true;
+        for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e)
+          ok = wait_flag(a.flags, a.dep_idx[e], epoch, a.hdr, a.timeout_ticks);
+        if (ok) acquire_agent();
+        s_skip = ok ? 0 : 1;
+      }
+      __syncthreads();
+      const int skip = s_skip;
+      __syncthreads();
+      if (skip) continue;  // a chunk never arrived: this tile of C is left untouched
+    }
+
+    const uint16_t* const a_tile = a.A + m0 * K;
+    auto load_a = [&](int64_t k0) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a_tile + k0, static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2);
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) {
+        const int row = i * 32 + (tid >> 3), sl = tid & 7;
+        ra[i] = buf_load_b128(rs, static_cast<uint32_t>((row * K + sl * 8) * 2));
+      }
+    };
+    auto store_a = [&](int buf) {
+      u32x4_t* As = As0 + buf * TM * kSlots;
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) {
+        const int row = i * 32 + (tid >> 3), sl = tid & 7;
+        As[row * kSlots + swz(row, sl)] = ra[i];
+      }
+    };
+    auto load_b = [&](int64_t k0) {
+      if constexpr (BL == 1) {
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(a.B + n0 * K + k0, static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2);
+#pragma unroll
+        for (int i = 0; i < B_LD_NK; ++i) {
+          const int row = i * 32 + (tid >> 3), sl = tid & 7;
+          rbn[i] = buf_load_b128(rs, static_cast<uint32_t>((row * K + sl * 8) * 2));
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.B + k0 * N + n0, (K - k0) * N * 2 - n0 * 2);
+#pragma unroll
+        for (int u = 0; u < B_UNITS; ++u) {
+          const int unit = tid + kThreads * u;
+          const int ng = unit % (TN / 4), kg = unit / (TN / 4);
+          const bool in = ng * 4 < cols_valid;
+          // the 8 k-rows differ by a wave-uniform stride: it goes in the scalar
+          // offset, the lane's column in the (range-checked) vector offset
+          const uint32_t voff = in ? static_cast<uint32_t>((kg * 8 * N + ng * 4) * 2) : kOutOfRange;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk)
+            rbk[u][kk] = buf_load_b64(rs, voff, static_cast<uint32_t>(kk * N * 2));
+        }
+      }
+    };
+    auto store_b = [&](int buf) {
+      u32x4_t* Bs = Bs0 + buf * TN * kSlots;
+      if constexpr (BL == 1) {
+#pragma unroll
+        for (int i = 0; i < B_LD_NK; ++i) {
+          const int row = i * 32 + (tid >> 3), sl = tid & 7;
+          Bs[row * kSlots + swz(row, sl)] = rbn[i];
+        }
+      } else {
+        // transpose 8 k-rows x 4 n-columns into 4 k-contiguous vectors
+#pragma unroll
+        for (int u = 0; u < B_UNITS; ++u) {
+          const int unit = tid + kThreads * u;
+          const int ng = unit % (TN / 4), kg = unit / (TN / 4);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            u32x4_t w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t lo = rbk[u][2 * j][v >> 1], hi = rbk[u][2 * j + 1][v >> 1];
+              w[j] = (v & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            const int nl = ng * 4 + v;
+            Bs[nl * kSlots + swz(nl, kg)] = w;
+          }
+        }
+      }
+    };
+
+    f32x16_t acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = f32x16_t{};
+
+    load_a(0);
+    load_b(0);
+    store_a(0);
+    store_b(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        load_a(static_cast<int64_t>(kt + 1) * kTK);
+        load_b(static_cast<int64_t>(kt + 1) * kTK);
+      }
+      const u32x4_t* As = As0 + cur * TM * kSlots;
+      const u32x4_t* Bs = Bs0 + cur * TN * kSlots;
+#pragma unroll
+      for (int kk = 0; kk < kTK / 16; ++kk) {
+        const int sl = kk * 2 + (lane >> 5);
+        bf16x8_t af[MI], bfv[NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int r = wm * WM + i * 32 + (lane & 31);
+          af[i] = __builtin_bit_cast(bf16x8_t, As[r * kSlots + swz(r, sl)]);
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int r = wn * WN + j * 32 + (lane & 31);
+          bfv[j] = __builtin_bit_cast(bf16x8_t, Bs[r * kSlots + swz(r, sl)]);
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+      }
+      if (more) {
+        store_a(cur ^ 1);
+        store_b(cur ^ 1);
+      }
+      __syncthreads();
+    }
+
+    // Epilogue.  Accumulator element e of a 32x32 block sits at row
+    // 8*(e/4) + 4*(lane/32) + e%4, column lane%32.  Each wave writes one
+    // 32-row strip at a time into its own LDS region (row-major, padded
+    // pitch), then reads it back 16 bytes per lane and stores whole rows.
+    {
+      char* const stage = reinterpret_cast<char*>(smem) + wave * 32 * SP * ES;
+      constexpr int LPR = WN * ES / 16;  // lanes per staged row
+      constexpr int RPI = 64 / LPR;      // rows per store instruction
+      const int rr = lane / LPR, rc = (lane % LPR) * (16 / ES);
+      const bool col_ok = wn * WN + rc < cols_valid;
+      const int row_bytes = static_cast<int>(N) * ES;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3), c = j * 32 + (lane & 31);
+            if constexpr (CT == 0)
+              *reinterpret_cast<float*>(stage + (r * SP + c) * ES) = acc[i][j][e];
+            else
+              *reinterpret_cast<uint16_t*>(stage + (r * SP + c) * ES) = f32_to_bf16_rne(acc[i][j][e]);
+          }
+        __syncthreads();
+        const int strip = wm * WM + i * 32;  // first tile row of this strip
+        const int rows_left = rows_valid - strip;
+        const __amdgpu_buffer_rsrc_t cs =
+            make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
+                      rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int r = it * RPI + rr;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (r * SP + rc) * ES);
+          if (col_ok)
+            __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
+        }
+        __syncthreads();
+      }
+    }
+
+    if constexpr (RS) {
+      release_agent();  // this thread's C stores are visible device-wide
+      __syncthreads();
+      if (tid == 0) {
+        for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) {
+          const int32_t c = a.dep_idx[e];
+          const uint32_t old = add_acq_rel_agent(a.counters + c, 1u);
+          if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) st_release_agent(a.flags + c, epoch);
+        }
+      }
+    }
+  }
+}
+
+// Host-side launcher: picks the template instance; hipErrorInvalidValue for a
+// variant that does not exist.
+hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid,
+                       hipStream_t stream) {
+#define SYNC_GEMM_CASE(TM_, TN_, BL_, CT_)                                                               \
+  if (tm == TM_ && tn == TN_ && b_layout == BL_ && c_dtype == CT_) {                                     \
+    if (rs)                                                                                              \
+      hipLaunchKernelGGL((gemm_persistent<TM_, TN_, BL_, CT_, true>), dim3(grid), dim3(kThreads), 0,     \
+                         stream, a);                                                                     \
+    else                                                                                                 \
+      hipLaunchKernelGGL((gemm_persistent<TM_, TN_, BL_, CT_, false>), dim3(grid), dim3(kThreads), 0,    \
+                         stream, a);                                                                     \
+    return hipGetLastError();                                                                            \
+  }
+#define SYNC_GEMM_TILES(BL_, CT_) \
+  SYNC_GEMM_CASE(256, 256, BL_, CT_) SYNC_GEMM_CASE(256, 128, BL_, CT_) SYNC_GEMM_CASE(128, 128, BL_, CT_)
+  SYNC_GEMM_TILES(0, 0)
+  SYNC_GEMM_TILES(0, 1)
+  SYNC_GEMM_TILES(1, 0)
+  SYNC_GEMM_TILES(1, 1)
+#undef SYNC_GEMM_TILES
+#undef SYNC_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+bool gemm_variant_exists(int tm, int tn) {
+  return (tm == 256 && tn == 256) || (tm == 256 && tn == 128) || (tm == 128 && tn == 128);
+}
+
+}  // namespace syncov

@@ -1,0 +1,45 @@
+// Kernel argument blocks shared by the host runtime and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace syncov {
+
+// Persistent GEMM (gemm_persistent.hip).
+struct GemmArgs {
+  const uint16_t* A;  // bf16 [M][K]
+  const uint16_t* B;  // bf16 [K][N] (KN) or [N][K] (NK)
+  void* C;            // [M][N] fp32 or bf16
+  int64_t M, N, K;
+  const int32_t* order;  // tile traversal, num_tiles entries
+  int32_t num_tiles, tiles_n;
+  const int64_t* dep_ptr;  // tile -> chunks CSR
+  const int32_t* dep_idx;
+  const int32_t* tiles_in;  // RS: tiles per chunk
+  uint32_t* flags;          // AG: ready flags; RS: done flags
+  uint32_t* counters;       // RS: stored-tile counters (zeroed by the begin kernel)
+  uint32_t* hdr;            // workspace header
+  uint64_t timeout_ticks;   // wall-clock ticks allowed per wait
+  int32_t nxcd;             // XCDs (for the workgroup -> slot remap)
+};
+
+// Copy agent (copy_agent.hip).
+struct CopyArgs {
+  const char* src[2];  // up to two tensors per chunk (attention: K and V)
+  char* dst[2];
+  int64_t row_bytes[2];
+  int32_t ntensors;
+  int32_t num_chunks;
+  const int64_t* chunk_begin;  // C+1 row bounds
+  const int32_t* arrival;      // chunk id per position
+  const int32_t* resident;     // copy-in: chunks already in place (skipped)
+  const int64_t* slot_row;     // copy-out: first staging row of each position (C+1)
+  uint32_t* out_flags;         // raised per chunk when its copy is complete
+  const uint32_t* wait_flags;  // copy-out: done flags to wait for
+  uint32_t* parts;             // per-chunk count of finished workgroups
+  uint32_t* hdr;
+  uint64_t timeout_ticks;
+  int32_t copy_out;
+};
+
+}  // namespace syncov

@@ -1,0 +1,716 @@
+// Host runtime behind the C ABI in sync_overlap.h: plans with lazily uploaded
+// device tables, the workspace layout, the library's streams (plain and
+// CU-masked) and events, and the launch sequences of the copy backends.
+//
+// Call shape (Syncopate summary page, "Core method", paper sec. 5.2 and
+// Fig. 7; review page, Fig. 5 caption): the communication of a plan runs
+// beside one fused compute kernel and signals chunk completion through
+// global-memory flags.  On one MI355X the "peers" are a second HBM region;
+// the copy agent is either the SDMA engine or a copy kernel on CUs that the
+// GEMM does not use.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels/device_common.hpp"
+#include "kernels/launch_args.hpp"
+#include "planner.hpp"
+#include "sync_overlap.h"
+
+namespace syncov {
+
+hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid, hipStream_t s);
+bool gemm_variant_exists(int tm, int tn);
+hipError_t launch_copy_agent(const CopyArgs& a, int grid, hipStream_t s);
+hipError_t launch_begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters, uint32_t* parts, int32_t num_chunks,
+                             const int32_t* resident, int32_t preset_all, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s);
+
+}  // namespace syncov
+
+using namespace syncov;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return SYNC_EHIP;
+}
+
+#define HIP_TRY(expr)                             \
+  do {                                            \
+    hipError_t _e = (expr);                       \
+    if (_e != hipSuccess) return hip_fail(_e, #expr); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// ---- per-device state ----------------------------------------------------
+struct MaskedPair {
+  hipStream_t copy = nullptr, gemm = nullptr;
+  int gemm_cus = 0;
+};
+
+// The library owns exactly two streams per device, a copy stream masked to
+// the copy CUs and a GEMM stream masked to the rest, so that together with
+// the caller's stream it stays within the runtime's default of four hardware
+// queues: a copy stream that shared a hardware queue with the spinning GEMM
+// could never run.  The pair is rebuilt when the copy-CU count changes.
+struct DeviceState {
+  bool ready = false;
+  int device = 0;
+  int num_cus = 0, num_xcds = 1, clock_khz = 0;
+  int64_t wall_khz = 100000;
+  std::string arch;
+  MaskedPair pair;
+  int pair_copy_cus = -1;
+  // SYNC_RUN_TIMED: ring of event quadruples (kernel start/end, copy start/end)
+  struct Timed {
+    hipEvent_t k0 = nullptr, k1 = nullptr, c0 = nullptr, c1 = nullptr;
+    bool has_kernel = false, has_copy = false;
+  };
+  std::vector<Timed> ring;
+  int64_t ring_head = 0, ring_count = 0;
+  hipEvent_t ev_fork = nullptr, ev_copy = nullptr, ev_gemm = nullptr;
+  std::mutex mu;  // serialises launch sequences (the events and streams are shared)
+};
+
+std::mutex g_devices_mu;
+std::map<int, std::unique_ptr<DeviceState>> g_devices;
+
+int current_device_state(DeviceState** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_devices_mu);
+  auto& slot = g_devices[dev];
+  if (!slot) slot = std::make_unique<DeviceState>();
+  DeviceState& d = *slot;
+  if (!d.ready) {
+    d.device = dev;
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, dev));
+    d.arch = prop.gcnArchName;
+    if (d.arch.rfind("gfx950", 0) != 0) return fail(SYNC_ENODEV, "device " + std::to_string(dev) + " is " + d.arch + ", not gfx950");
+    d.num_cus = prop.multiProcessorCount;
+    d.clock_khz = prop.clockRate;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0) d.num_xcds = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) == hipSuccess && v > 0) d.wall_khz = v;
+    HIP_TRY(hipEventCreateWithFlags(&d.ev_fork, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&d.ev_copy, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&d.ev_gemm, hipEventDisableTiming));
+    d.ready = true;
+  }
+  *out = &d;
+  return SYNC_OK;
+}
+
+// CU mask bits for the copy agent: `copy_cus` CUs spread evenly over the XCDs.
+// Logical CU i of the mask lives on XCD i % num_xcds (round-robin numbering),
+// so the first copy_cus bits give copy_cus / num_xcds CUs on every XCD.
+// SYNC_CU_MASK_LAYOUT=blocked switches to XCD-major numbering.
+std::vector<uint32_t> copy_mask_bits(int num_cus, int num_xcds, int copy_cus, bool complement) {
+  std::vector<char> is_copy(num_cus, 0);
+  const char* env = std::getenv("SYNC_CU_MASK_LAYOUT");
+  const bool blocked = env && std::strcmp(env, "blocked") == 0;
+  if (!blocked) {
+    for (int i = 0; i < copy_cus && i < num_cus; ++i) is_copy[i] = 1;
+  } else {
+    const int per_xcd = num_cus / num_xcds, take = copy_cus / num_xcds;
+    for (int x = 0; x < num_xcds; ++x)
+      for (int i = 0; i < take; ++i) is_copy[x * per_xcd + i] = 1;
+  }
+  std::vector<uint32_t> words((num_cus + 31) / 32, 0u);
+  for (int i = 0; i < num_cus; ++i)
+    if (is_copy[i] != complement) words[i / 32] |= 1u << (i % 32);
+  return words;
+}
+
+int masked_pair(DeviceState& d, int copy_cus, MaskedPair** out) {
+  if (d.pair_copy_cus != copy_cus) {
+    if (d.pair.copy) {
+      // pending work on the old streams still completes; release happens after it
+      (void)hipStreamDestroy(d.pair.copy);
+      (void)hipStreamDestroy(d.pair.gemm);
+      d.pair = MaskedPair{};
+      d.pair_copy_cus = -1;
+    }
+    MaskedPair mp;
+    auto cm = copy_mask_bits(d.num_cus, d.num_xcds, copy_cus, false);
+    auto gm = copy_mask_bits(d.num_cus, d.num_xcds, copy_cus, true);
+    HIP_TRY(hipExtStreamCreateWithCUMask(&mp.copy, static_cast<uint32_t>(cm.size()), cm.data()));
+    HIP_TRY(hipExtStreamCreateWithCUMask(&mp.gemm, static_cast<uint32_t>(gm.size()), gm.data()));
+    mp.gemm_cus = d.num_cus - copy_cus;
+    d.pair = mp;
+    d.pair_copy_cus = copy_cus;
+  }
+  *out = &d.pair;
+  return SYNC_OK;
+}
+
+constexpr int kTimingRing = 1024;
+
+// Next timing slot (creates its events on first use); nullptr when not timed.
+int timing_slot(DeviceState& d, bool timed, DeviceState::Timed** out) {
+  *out = nullptr;
+  if (!timed) return SYNC_OK;
+  if (d.ring.empty()) d.ring.resize(kTimingRing);
+  DeviceState::Timed& t = d.ring[d.ring_head % kTimingRing];
+  if (!t.k0) {
+    HIP_TRY(hipEventCreate(&t.k0));
+    HIP_TRY(hipEventCreate(&t.k1));
+    HIP_TRY(hipEventCreate(&t.c0));
+    HIP_TRY(hipEventCreate(&t.c1));
+  }
+  t.has_kernel = t.has_copy = false;
+  ++d.ring_head;
+  if (d.ring_count < kTimingRing) ++d.ring_count;
+  *out = &t;
+  return SYNC_OK;
+}
+
+}  // namespace
+
+// ---- plans -------------------------------------------------------------------
+struct DeviceTables {
+  int32_t* tile_order = nullptr;
+  int64_t* dep_ptr = nullptr;
+  int32_t* dep_idx = nullptr;
+  int32_t* tiles_in = nullptr;
+  int64_t* chunk_begin = nullptr;
+  int32_t* arrival = nullptr;
+  int32_t* resident = nullptr;
+  int64_t* slot_row = nullptr;
+  void* block = nullptr;  // one allocation holding all of the above
+};
+
+struct sync_plan_s {
+  Plan plan;
+  std::vector<int64_t> slot_row;  // staging row of each send position (C+1)
+  std::mutex mu;
+  std::map<int, DeviceTables> dev;
+};
+
+namespace {
+
+template <typename T>
+void put(char*& cur, std::vector<char>& host, const std::vector<T>& v, T** dst, char* base) {
+  const size_t off = cur - host.data();
+  std::memcpy(cur, v.data(), v.size() * sizeof(T));
+  *dst = reinterpret_cast<T*>(base + off);
+  cur += align_up(static_cast<int64_t>(v.size() * sizeof(T)), 256);
+}
+
+int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
+  std::lock_guard<std::mutex> lk(p->mu);
+  auto it = p->dev.find(dev);
+  if (it != p->dev.end()) {
+    *out = &it->second;
+    return SYNC_OK;
+  }
+  const Plan& pl = p->plan;
+  auto sz = [](size_t n, size_t e) { return align_up(static_cast<int64_t>(n * e), 256); };
+  const int64_t total = sz(pl.tile_order.size(), 4) + sz(pl.dep_ptr.size(), 8) + sz(pl.dep_idx.size(), 4) +
+                        sz(pl.tiles_in.size(), 4) + sz(pl.chunk_begin.size(), 8) + sz(pl.arrival.size(), 4) +
+                        sz(pl.resident.size(), 4) + sz(p->slot_row.size(), 8) + 256;
+  std::vector<char> host(static_cast<size_t>(total), 0);
+  void* block = nullptr;
+  HIP_TRY(hipMalloc(&block, static_cast<size_t>(total)));
+  DeviceTables t;
+  t.block = block;
+  char* cur = host.data();
+  char* base = static_cast<char*>(block);
+  put(cur, host, pl.tile_order, &t.tile_order, base);
+  put(cur, host, pl.dep_ptr, &t.dep_ptr, base);
+  put(cur, host, pl.dep_idx, &t.dep_idx, base);
+  put(cur, host, pl.tiles_in, &t.tiles_in, base);
+  put(cur, host, pl.chunk_begin, &t.chunk_begin, base);
+  put(cur, host, pl.arrival, &t.arrival, base);
+  put(cur, host, pl.resident, &t.resident, base);
+  put(cur, host, p->slot_row, &t.slot_row, base);
+  hipError_t e = hipMemcpy(block, host.data(), static_cast<size_t>(total), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(block);
+    return hip_fail(e, "hipMemcpy(plan tables)");
+  }
+  *out = &p->dev.emplace(dev, t).first->second;
+  return SYNC_OK;
+}
+
+// Workspace layout: 256-byte header, then four uint32[C] arrays, each padded
+// to 256 bytes: flags (ready / done), counters (GEMM tiles stored per chunk),
+// parts (copy workgroups finished per chunk), sent (copy-out done).
+struct WsView {
+  uint32_t *hdr, *flags, *counters, *parts, *sent;
+};
+
+int64_t ws_array_bytes(int32_t C) { return align_up(static_cast<int64_t>(C) * 4, 256); }
+
+WsView ws_view(void* ws, int32_t C) {
+  char* b = static_cast<char*>(ws);
+  const int64_t a = ws_array_bytes(C);
+  WsView v;
+  v.hdr = reinterpret_cast<uint32_t*>(b);
+  v.flags = reinterpret_cast<uint32_t*>(b + 256);
+  v.counters = reinterpret_cast<uint32_t*>(b + 256 + a);
+  v.parts = reinterpret_cast<uint32_t*>(b + 256 + 2 * a);
+  v.sent = reinterpret_cast<uint32_t*>(b + 256 + 3 * a);
+  return v;
+}
+
+struct CallCtx {
+  DeviceState* dev = nullptr;
+  DeviceTables* tab = nullptr;
+  WsView ws{};
+  sync_copy_cfg cfg{};
+  uint64_t timeout_ticks = 0;
+};
+
+int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, CallCtx& cx) {
+  if (!plan) return fail(SYNC_EINVAL, "plan is NULL");
+  if (plan->plan.desc.op != op) return fail(SYNC_EINVAL, "plan was built for a different op");
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(SYNC_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  sync_copy_cfg cfg{};
+  cfg.backend = SYNC_COPY_SDMA;
+  if (cfg_in) cfg = *cfg_in;
+  for (int i = 0; i < 3; ++i)
+    if (cfg.reserved[i]) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
+  if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_HOST_GATED) return fail(SYNC_EINVAL, "bad backend");
+  if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
+  if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED))
+    return fail(SYNC_EINVAL, "unknown cfg.flags bits");
+  if ((cfg.flags & SYNC_RUN_COPY_ONLY) && (cfg.flags & SYNC_RUN_COMPUTE_ONLY))
+    return fail(SYNC_EINVAL, "COPY_ONLY and COMPUTE_ONLY are exclusive");
+  if ((cfg.flags & SYNC_RUN_COPY_ONLY) && cfg.backend == SYNC_COPY_PRESET)
+    return fail(SYNC_EINVAL, "COPY_ONLY needs a copy backend");
+  int rc = current_device_state(&cx.dev);
+  if (rc) return rc;
+  if (cfg.backend == SYNC_COPY_CU) {
+    if (cfg.copy_cus < cx.dev->num_xcds || cfg.copy_cus % cx.dev->num_xcds || cfg.copy_cus > cx.dev->num_cus / 2)
+      return fail(SYNC_EINVAL, "copy_cus must be a multiple of the XCD count and at most half the CUs");
+  }
+  rc = device_tables(plan, cx.dev->device, &cx.tab);
+  if (rc) return rc;
+  cx.ws = ws_view(ws, plan->plan.num_chunks);
+  cx.cfg = cfg;
+  const uint64_t ns = cfg.timeout_ns ? cfg.timeout_ns : 2000000000ull;
+  cx.timeout_ticks = ns / 1000000ull * static_cast<uint64_t>(cx.dev->wall_khz) +
+                     (ns % 1000000ull) * static_cast<uint64_t>(cx.dev->wall_khz) / 1000000ull;
+  return SYNC_OK;
+}
+
+// Enqueues, on `s`, SDMA copies of every non-resident chunk in arrival order,
+// each followed by a one-lane kernel that raises the chunk's flag (stream
+// order puts it after the copy has landed).  HOST_GATED first makes the stream
+// wait for the chunk's host word.
+// Measured limitation of this path under the HIP runtime: once the persistent
+// GEMM is running, the runtime does not start the next SDMA copy on the copy
+// stream until the GEMM exits, so only chunks copied before the GEMM starts
+// overlap; later ones time out.  The CU backend does not have this limit.
+int enqueue_sdma_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2], char* const dst[2],
+                         const int64_t row_bytes[2], int ntensors, hipStream_t s) {
+  for (int32_t p = 0; p < pl.num_chunks; ++p) {
+    const int32_t c = pl.arrival[p];
+    if (pl.resident[c]) continue;
+    if (cx.cfg.backend == SYNC_COPY_HOST_GATED)
+      HIP_TRY(hipStreamWaitValue32(s, const_cast<uint32_t*>(cx.cfg.host_gates + c), 1u, hipStreamWaitValueGte,
+                                   0xffffffffu));
+    const int64_t r0 = pl.chunk_begin[c], r1 = pl.chunk_begin[c + 1];
+    for (int x = 0; x < ntensors; ++x)
+      HIP_TRY(hipMemcpyAsync(dst[x] + r0 * row_bytes[x], src[x] + r0 * row_bytes[x],
+                             static_cast<size_t>((r1 - r0) * row_bytes[x]), hipMemcpyDeviceToDeviceNoCU, s));
+    HIP_TRY(launch_publish_flag(cx.ws.hdr, cx.ws.flags, c, s));
+  }
+  return SYNC_OK;
+}
+
+int check_gemm_shape(const Plan& pl) {
+  const auto& d = pl.desc;
+  if (d.k % 64) return fail(SYNC_EUNSUPPORTED, "k must be a multiple of 64");
+  if (d.n % 8) return fail(SYNC_EUNSUPPORTED, "n must be a multiple of 8");
+  if (!gemm_variant_exists(d.tile_m, d.tile_n))
+    return fail(SYNC_EUNSUPPORTED, "no kernel for tile " + std::to_string(d.tile_m) + "x" + std::to_string(d.tile_n));
+  if (d.m * d.k * 2 >= (int64_t(1) << 40) || d.k * d.n * 2 >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(d.tile_m) * d.k * 2 >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(d.tile_m) * d.n * 4 >= (int64_t(1) << 31))
+    return fail(SYNC_EUNSUPPORTED, "operand too large for 32-bit buffer offsets");
+  return SYNC_OK;
+}
+
+int gemm_wg_per_cu(const Plan& pl) { return (pl.desc.tile_m == 128 && pl.desc.tile_n == 128) ? 2 : 1; }
+
+GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const void* B, void* C) {
+  GemmArgs g{};
+  g.A = static_cast<const uint16_t*>(A);
+  g.B = static_cast<const uint16_t*>(B);
+  g.C = C;
+  g.M = pl.desc.m;
+  g.N = pl.desc.n;
+  g.K = pl.desc.k;
+  g.order = cx.tab->tile_order;
+  g.num_tiles = pl.num_tiles;
+  g.tiles_n = pl.tiles_n;
+  g.dep_ptr = cx.tab->dep_ptr;
+  g.dep_idx = cx.tab->dep_idx;
+  g.tiles_in = cx.tab->tiles_in;
+  g.flags = cx.ws.flags;
+  g.counters = cx.ws.counters;
+  g.hdr = cx.ws.hdr;
+  g.timeout_ticks = cx.timeout_ticks;
+  g.nxcd = cx.dev->num_xcds;
+  return g;
+}
+
+}  // namespace
+
+// ---- C ABI ---------------------------------------------------------------------
+extern "C" {
+
+int sync_plan(const sync_plan_desc* desc, sync_plan_t* out) {
+  if (!desc || !out) return fail(SYNC_EINVAL, "desc and out must be non-NULL");
+  *out = nullptr;
+  auto p = std::make_unique<sync_plan_s>();
+  std::string err;
+  if (!build_plan(*desc, p->plan, err)) return fail(SYNC_EINVAL, err);
+  const Plan& pl = p->plan;
+  p->slot_row.assign(pl.num_chunks + 1, 0);
+  for (int32_t s = 0; s < pl.num_chunks; ++s) {
+    const int32_t c = pl.arrival[s];
+    p->slot_row[s + 1] = p->slot_row[s] + (pl.chunk_begin[c + 1] - pl.chunk_begin[c]);
+  }
+  *out = p.release();
+  return SYNC_OK;
+}
+
+void sync_plan_destroy(sync_plan_t plan) {
+  if (!plan) return;
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : plan->dev) {
+    if (have) (void)hipSetDevice(kv.first);
+    (void)hipFree(kv.second.block);
+  }
+  if (have) (void)hipSetDevice(cur);
+  delete plan;
+}
+
+int sync_plan_get_info(sync_plan_t plan, sync_plan_info* out) {
+  if (!plan || !out) return fail(SYNC_EINVAL, "plan and out must be non-NULL");
+  const Plan& p = plan->plan;
+  out->num_chunks = p.num_chunks;
+  out->num_tiles = p.num_tiles;
+  out->tiles_m = p.tiles_m;
+  out->tiles_n = p.tiles_n;
+  out->num_deps = static_cast<int64_t>(p.dep_idx.size());
+  return SYNC_OK;
+}
+
+int sync_plan_export(sync_plan_t plan, sync_plan_tables* out) {
+  if (!plan || !out) return fail(SYNC_EINVAL, "plan and out must be non-NULL");
+  const Plan& p = plan->plan;
+  auto cp = [](auto* dst, const auto& v) {
+    if (dst) std::memcpy(dst, v.data(), v.size() * sizeof(v[0]));
+  };
+  cp(out->chunk_begin, p.chunk_begin);
+  cp(out->chunk_pos, p.chunk_pos);
+  cp(out->arrival, p.arrival);
+  cp(out->resident, p.resident);
+  cp(out->tiles_in, p.tiles_in);
+  cp(out->tile_order, p.tile_order);
+  cp(out->tile_key, p.tile_key);
+  cp(out->dep_ptr, p.dep_ptr);
+  cp(out->dep_idx, p.dep_idx);
+  cp(out->inv_ptr, p.inv_ptr);
+  cp(out->inv_idx, p.inv_idx);
+  return SYNC_OK;
+}
+
+size_t sync_workspace_size(sync_plan_t plan) {
+  if (!plan) return 0;
+  return static_cast<size_t>(256 + 4 * ws_array_bytes(plan->plan.num_chunks));
+}
+
+int sync_workspace_init(sync_plan_t plan, void* ws, void* stream) {
+  if (!plan || !ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(SYNC_EINVAL, "bad plan or workspace");
+  DeviceState* d = nullptr;
+  int rc = current_device_state(&d);
+  if (rc) return rc;
+  HIP_TRY(launch_fill_u32(static_cast<uint32_t*>(ws), static_cast<int64_t>(sync_workspace_size(plan) / 4), 0u,
+                          static_cast<hipStream_t>(stream)));
+  return SYNC_OK;
+}
+
+int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk) {
+  if (!ws) return fail(SYNC_EINVAL, "workspace is NULL");
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  uint32_t h[3] = {0, 0, 0};
+  HIP_TRY(hipMemcpy(h, ws, sizeof h, hipMemcpyDeviceToHost));
+  if (err_chunk) *err_chunk = h[WS_ERR_CODE] ? static_cast<int32_t>(h[WS_ERR_CHUNK]) : -1;
+  if (h[WS_ERR_CODE] == ERR_TIMEOUT)
+    return fail(SYNC_ETIMEOUT, "a device-side wait timed out on chunk " + std::to_string(h[WS_ERR_CHUNK]));
+  if (h[WS_ERR_CODE]) return fail(SYNC_EHIP, "unknown workspace error word");
+  return SYNC_OK;
+}
+
+int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local, const void* b, void* c,
+                 int32_t c_dtype, void* ws, void* compute, void* copy) {
+  CallCtx cx;
+  int rc = prepare(plan, cfg, ws, SYNC_OP_AG_GEMM, cx);
+  if (rc) return rc;
+  const Plan& pl = plan->plan;
+  if ((rc = check_gemm_shape(pl))) return rc;
+  if (c_dtype != SYNC_DTYPE_F32 && c_dtype != SYNC_DTYPE_BF16) return fail(SYNC_EINVAL, "bad c_dtype");
+  const bool need_peer = cx.cfg.backend != SYNC_COPY_PRESET && !(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
+  if (!a_local || !b || !c || (need_peer && !a_peer)) return fail(SYNC_EINVAL, "NULL operand");
+  if (!aligned16(a_local) || !aligned16(b) || !aligned16(c) || (a_peer && !aligned16(a_peer)))
+    return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
+  DeviceState& d = *cx.dev;
+  std::lock_guard<std::mutex> lk(d.mu);
+  hipStream_t cs = static_cast<hipStream_t>(compute);
+  const bool copy_only = cx.cfg.flags & SYNC_RUN_COPY_ONLY;
+  const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
+  DeviceState::Timed* tm = nullptr;
+  if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
+  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, pl.num_chunks, cx.tab->resident,
+                            compute_only ? 1 : 0, cs));
+  GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
+  auto gemm_on = [&](hipStream_t st, int grid) -> int {
+    if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
+    HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, false, grid, st));
+    if (tm) {
+      HIP_TRY(hipEventRecord(tm->k1, st));
+      tm->has_kernel = true;
+    }
+    return SYNC_OK;
+  };
+  const char* src[2] = {static_cast<const char*>(a_peer), nullptr};
+  char* dst[2] = {static_cast<char*>(a_local), nullptr};
+  const int64_t rb[2] = {pl.desc.k * 2, 0};
+
+  if (cx.cfg.backend == SYNC_COPY_CU) {
+    MaskedPair* mp = nullptr;
+    if ((rc = masked_pair(d, cx.cfg.copy_cus, &mp))) return rc;
+    HIP_TRY(hipEventRecord(d.ev_fork, cs));
+    if (!(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY)) {
+      CopyArgs ca{};
+      ca.src[0] = src[0];
+      ca.dst[0] = dst[0];
+      ca.row_bytes[0] = rb[0];
+      ca.ntensors = 1;
+      ca.num_chunks = pl.num_chunks;
+      ca.chunk_begin = cx.tab->chunk_begin;
+      ca.arrival = cx.tab->arrival;
+      ca.resident = cx.tab->resident;
+      ca.out_flags = cx.ws.flags;
+      ca.parts = cx.ws.parts;
+      ca.hdr = cx.ws.hdr;
+      ca.timeout_ticks = cx.timeout_ticks;
+      HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
+      if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
+      HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * 2, mp->copy));
+      if (tm) {
+        HIP_TRY(hipEventRecord(tm->c1, mp->copy));
+        tm->has_copy = true;
+      }
+      HIP_TRY(hipEventRecord(d.ev_copy, mp->copy));
+    }
+    if (!copy_only) {
+      HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
+      if ((rc = gemm_on(mp->gemm, mp->gemm_cus * gemm_wg_per_cu(pl)))) return rc;
+      HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
+      HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
+    }
+    if (!(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY)) HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
+    return SYNC_OK;
+  }
+
+  if (compute_only) return gemm_on(cs, d.num_cus * gemm_wg_per_cu(pl));
+  // SDMA: the chunk data moves on the SDMA engine, but the HIP runtime runs
+  // each 4-byte flag copy as a small blit kernel, which needs a free CU while
+  // the persistent GEMM spins.  So the GEMM runs on a CU-masked stream that
+  // leaves one CU per XCD to the copy stream.
+  MaskedPair* mp = nullptr;
+  if ((rc = masked_pair(d, d.num_xcds, &mp))) return rc;
+  hipStream_t ss = copy ? static_cast<hipStream_t>(copy) : mp->copy;
+  HIP_TRY(hipEventRecord(d.ev_fork, cs));
+  HIP_TRY(hipStreamWaitEvent(ss, d.ev_fork, 0));
+  if (tm) HIP_TRY(hipEventRecord(tm->c0, ss));
+  if ((rc = enqueue_sdma_copy_in(pl, cx, src, dst, rb, 1, ss))) return rc;
+  if (tm) {
+    HIP_TRY(hipEventRecord(tm->c1, ss));
+    tm->has_copy = true;
+  }
+  HIP_TRY(hipEventRecord(d.ev_copy, ss));
+  if (!copy_only) {
+    HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
+    if ((rc = gemm_on(mp->gemm, mp->gemm_cus * gemm_wg_per_cu(pl)))) return rc;
+    HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
+    HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
+  }
+  HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
+  return SYNC_OK;
+}
+
+int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c, int32_t c_dtype,
+                 void* staging, void* ws, void* compute, void* copy) {
+  (void)copy;
+  CallCtx cx;
+  int rc = prepare(plan, cfg, ws, SYNC_OP_GEMM_RS, cx);
+  if (rc) return rc;
+  const Plan& pl = plan->plan;
+  if ((rc = check_gemm_shape(pl))) return rc;
+  if (c_dtype != SYNC_DTYPE_F32 && c_dtype != SYNC_DTYPE_BF16) return fail(SYNC_EINVAL, "bad c_dtype");
+  if (cx.cfg.backend == SYNC_COPY_SDMA || cx.cfg.backend == SYNC_COPY_HOST_GATED)
+    return fail(SYNC_EUNSUPPORTED, "GEMM-RS copy-out runs on dedicated CUs (CU backend) or not at all (PRESET)");
+  const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
+  if (cx.cfg.flags & SYNC_RUN_COPY_ONLY) return fail(SYNC_EINVAL, "COPY_ONLY is not defined for GEMM-RS");
+  if (!a || !b || !c || (!compute_only && !staging)) return fail(SYNC_EINVAL, "NULL operand");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c) || (staging && !aligned16(staging)))
+    return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
+  DeviceState& d = *cx.dev;
+  std::lock_guard<std::mutex> lk(d.mu);
+  hipStream_t cs = static_cast<hipStream_t>(compute);
+  DeviceState::Timed* tm = nullptr;
+  if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
+  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, pl.num_chunks, nullptr, 0, cs));
+  GemmArgs g = make_gemm_args(pl, cx, a, b, c);
+  auto gemm_on = [&](hipStream_t st, int grid) -> int {
+    if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
+    HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, true, grid, st));
+    if (tm) {
+      HIP_TRY(hipEventRecord(tm->k1, st));
+      tm->has_kernel = true;
+    }
+    return SYNC_OK;
+  };
+  if (compute_only && cx.cfg.backend == SYNC_COPY_PRESET) return gemm_on(cs, d.num_cus * gemm_wg_per_cu(pl));
+  MaskedPair* mp = nullptr;
+  if ((rc = masked_pair(d, cx.cfg.copy_cus, &mp))) return rc;
+  HIP_TRY(hipEventRecord(d.ev_fork, cs));
+  HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
+  if ((rc = gemm_on(mp->gemm, mp->gemm_cus * gemm_wg_per_cu(pl)))) return rc;
+  HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
+  if (!compute_only) {
+    CopyArgs ca{};
+    const int64_t es = c_dtype == SYNC_DTYPE_F32 ? 4 : 2;
+    ca.src[0] = static_cast<const char*>(c);
+    ca.dst[0] = static_cast<char*>(staging);
+    ca.row_bytes[0] = pl.desc.n * es;
+    ca.ntensors = 1;
+    ca.num_chunks = pl.num_chunks;
+    ca.chunk_begin = cx.tab->chunk_begin;
+    ca.arrival = cx.tab->arrival;
+    ca.resident = cx.tab->resident;
+    ca.slot_row = cx.tab->slot_row;
+    ca.out_flags = cx.ws.sent;
+    ca.wait_flags = cx.ws.flags;
+    ca.parts = cx.ws.parts;
+    ca.hdr = cx.ws.hdr;
+    ca.timeout_ticks = cx.timeout_ticks;
+    ca.copy_out = 1;
+    HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
+    if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
+    HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * 2, mp->copy));
+    if (tm) {
+      HIP_TRY(hipEventRecord(tm->c1, mp->copy));
+      tm->has_copy = true;
+    }
+    HIP_TRY(hipEventRecord(d.ev_copy, mp->copy));
+    HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
+  }
+  HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
+  return SYNC_OK;
+}
+
+int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q, const void* k_peer,
+                        const void* v_peer, void* k_local, void* v_local, float* o, float* m_state, float* l_state,
+                        float* lse, float scale, int32_t flags, void* ws, void* compute, void* copy) {
+  (void)plan; (void)cfg; (void)q; (void)k_peer; (void)v_peer; (void)k_local; (void)v_local; (void)o;
+  (void)m_state; (void)l_state; (void)lse; (void)scale; (void)flags; (void)ws; (void)compute; (void)copy;
+  return fail(SYNC_EUNSUPPORTED, "ring-attention step not built yet");
+}
+
+int sync_get_device_info(sync_device_info* out) {
+  if (!out) return fail(SYNC_EINVAL, "out is NULL");
+  DeviceState* d = nullptr;
+  int rc = current_device_state(&d);
+  if (rc) return rc;
+  std::memset(out, 0, sizeof *out);
+  out->device = d->device;
+  out->num_cus = d->num_cus;
+  out->num_xcds = d->num_xcds;
+  out->clock_khz = d->clock_khz;
+  out->wall_clock_khz = d->wall_khz;
+  std::snprintf(out->arch, sizeof out->arch, "%s", d->arch.c_str());
+  return SYNC_OK;
+}
+
+int sync_read_timings(int32_t max, sync_timing* out, int32_t* count) {
+  if (!count || (max > 0 && !out)) return fail(SYNC_EINVAL, "bad arguments");
+  *count = 0;
+  DeviceState* d = nullptr;
+  int rc = current_device_state(&d);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(d->mu);
+  const int64_t n = d->ring_count;
+  for (int64_t i = 0; i < n; ++i) {
+    DeviceState::Timed& t = d->ring[(d->ring_head - n + i) % kTimingRing];
+    sync_timing r{0.f, 0.f};
+    if (t.has_kernel) {
+      HIP_TRY(hipEventSynchronize(t.k1));
+      HIP_TRY(hipEventElapsedTime(&r.kernel_ms, t.k0, t.k1));
+    }
+    if (t.has_copy) {
+      HIP_TRY(hipEventSynchronize(t.c1));
+      HIP_TRY(hipEventElapsedTime(&r.copy_ms, t.c0, t.c1));
+    }
+    if (*count < max) out[(*count)++] = r;
+  }
+  d->ring_count = 0;
+  return SYNC_OK;
+}
+
+const char* sync_last_error(void) { return g_err.c_str(); }
+
+void sync_shutdown(void) {
+  std::lock_guard<std::mutex> lk(g_devices_mu);
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_devices) {
+    DeviceState& d = *kv.second;
+    if (!d.ready) continue;
+    (void)hipSetDevice(kv.first);
+    if (d.pair.copy) {
+      (void)hipStreamDestroy(d.pair.copy);
+      (void)hipStreamDestroy(d.pair.gemm);
+    }
+    for (auto& t : d.ring)
+      for (hipEvent_t e : {t.k0, t.k1, t.c0, t.c1})
+        if (e) (void)hipEventDestroy(e);
+    (void)hipEventDestroy(d.ev_fork);
+    (void)hipEventDestroy(d.ev_copy);
+    (void)hipEventDestroy(d.ev_gemm);
+  }
+  g_devices.clear();
+  if (have) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

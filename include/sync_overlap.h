@@ -1,0 +1,273 @@
+/*
+ * sync_overlap.h -- C ABI of libsync_overlap.so: one GPU's share of a
+ * chunk-overlapped collective GEMM on MI355X (gfx950).
+ *
+ * Sources for what the calls compute:
+ *   [SYN-S] "Syncopate: Efficient Multi-GPU AI Kernels via Automatic
+ *           Chunk-Centric Compute-Communication Overlap", paper summary page
+ *           (awesome-system-papers), sections "Core method" (paper sec. 5.1,
+ *           5.2, Fig. 6, Fig. 7) and "Experiments" (paper sec. 6.1, Fig. 8-9).
+ *   [SYN-A] the same paper's abstract (arXiv 2601.20595 catalogue record).
+ *   [SYN-R] the pith.science review page of that paper: captions of Fig. 3-7.
+ *   [ENT]   "Entwine" abstract (arXiv 2609.11562, arxivdaily page).
+ *
+ * The pages state the problem as "a local tile kernel plus a chunk schedule"
+ * [SYN-A]: the caller describes the chunk plan with sync_plan(); the tile
+ * kernel is this library's persistent bf16 MFMA GEMM (or the ring-attention
+ * step), whose tile traversal the plan reorders [SYN-S, Fig. 6] and whose
+ * tiles wait in-kernel on per-chunk ready flags (AG) or raise per-chunk done
+ * flags in send order (RS) [SYN-S "Core method"; ENT].  One GPU stands in for
+ * every peer: the peers' shards sit in a separate HBM region and a copy agent
+ * stages them in (SDMA engine, or load/store on dedicated CUs) [SYN-S, Fig. 7].
+ *
+ * Conventions for every call:
+ *   - Return value: SYNC_OK (0) or a negative SYNC_E* code; on error,
+ *     sync_last_error() returns a thread-local message.  No call aborts.
+ *   - Device pointers are plain HIP device addresses owned by the caller and
+ *     must be 16-byte aligned.  Host pointers are marked "host".
+ *   - Streams are hipStream_t passed as void*; NULL means the null stream.
+ *   - Launch calls are stream-ordered and asynchronous: SYNC_OK means the work
+ *     was enqueued on `compute` (which the call joins back to before
+ *     returning).  Device-side failures (a wait that timed out) are read
+ *     afterwards with sync_workspace_status().
+ *   - All matrices are row-major.  bf16 = IEEE bfloat16 bit patterns.
+ */
+#ifndef SYNC_OVERLAP_H
+#define SYNC_OVERLAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  SYNC_OK = 0,
+  SYNC_EINVAL = -1,       /* bad argument: null/misaligned pointer, bad descriptor */
+  SYNC_EUNSUPPORTED = -2, /* valid plan but no kernel variant for it (shape, tile) */
+  SYNC_EHIP = -3,         /* a HIP runtime call failed; message holds its string */
+  SYNC_ETIMEOUT = -4,     /* a device-side chunk wait ran past its time limit */
+  SYNC_ENOMEM = -5,       /* host or device allocation failed */
+  SYNC_ENODEV = -6        /* no usable gfx950 device */
+};
+
+/* ---- plan descriptor --------------------------------------------------- */
+enum { SYNC_OP_AG_GEMM = 1, SYNC_OP_GEMM_RS = 2, SYNC_OP_RING_ATTN = 3 };
+enum { SYNC_PAT_RING = 0, SYNC_PAT_EXPLICIT = 1 };
+enum { SYNC_ORDER_ROW_MAJOR = 0, SYNC_ORDER_CHUNK_MAJOR = 1, SYNC_ORDER_SWIZZLED = 2 };
+enum { SYNC_B_KN = 0, SYNC_B_NK = 1 };      /* B as [k][n], or [n][k] (Linear weight) */
+enum { SYNC_DTYPE_F32 = 0, SYNC_DTYPE_BF16 = 1 };
+
+/*
+ * A chunk plan [SYN-S "Core method", paper sec. 5.1: communication as P2P or
+ * collective operations on chunks, each a block of a logical tensor holding
+ * one or more tiles; ring is one of the patterns; plans may be user-written
+ * or instantiated from templates].
+ *
+ * GEMM ops: C[m][n] = A[m][k] . B.  The chunked tensor is A (AG) or C (RS),
+ *   split into `world` row shards of m/world rows, each cut into `split`
+ *   sub-chunks by floor bounds: chunk c = w*split + q covers rows
+ *   [w*R + floor(q*R/split), w*R + floor((q+1)*R/split)), R = m/world.
+ * RING_ATTN: m = query rows Sq, n = tokens per KV block, k = head dim d;
+ *   the chunked tensors are K and V ([world*n][heads_kv][d]).
+ * Ring order (pattern RING, direction d = ring_dir):
+ *   AG / attention: the shard consumed at step s is (rank - d*s) mod world
+ *   (step 0 is the local shard); RS: the shard sent at step s is
+ *   (rank - d*(s+1)) mod world (own shard last).  EXPLICIT: explicit_order
+ *   (host, `world` entries, a permutation) lists shards in that order.
+ * Tiles: tile t = i*tiles_n + j covers C rows [i*tile_m, ..) and columns
+ *   [j*tile_n, ..) (attention: work item t = i*heads_q + h).  A tile depends
+ *   on every chunk its rows meet; its key is the last (AG) / first (RS)
+ *   position among them.  Tile order [SYN-S, paper sec. 5.2, Fig. 6; ENT]:
+ *   ROW_MAJOR (t ascending), CHUNK_MAJOR (key, i, j) or SWIZZLED
+ *   (key, i / group_m, j, i).
+ */
+typedef struct {
+  int32_t op;             /* SYNC_OP_* */
+  int32_t world;          /* W >= 1 */
+  int32_t rank;           /* 0 <= rank < W */
+  int32_t ring_dir;       /* +1 or -1 */
+  int64_t m, n, k;
+  int32_t pattern;        /* SYNC_PAT_* */
+  int32_t split;          /* 1 <= split <= rows per shard */
+  const int32_t* explicit_order; /* host; read only during sync_plan() */
+  int32_t tile_m, tile_n; /* GEMM tile (kernel variants: 256x256, 256x128, 128x128); attention: tile_m query rows */
+  int32_t tile_order;     /* SYNC_ORDER_* */
+  int32_t group_m;        /* SWIZZLED group height in tile rows; 0 = 4 */
+  int32_t local_resident; /* 1: the rank's own shard is already in place (AG, attention) */
+  int32_t heads_q, heads_kv; /* RING_ATTN only; heads_q % heads_kv == 0 */
+  int32_t b_layout;       /* SYNC_B_KN or SYNC_B_NK (GEMM ops) */
+  int32_t reserved[4];    /* must be zero */
+} sync_plan_desc;
+
+typedef struct sync_plan_s* sync_plan_t;
+
+/* Builds a plan on the CPU (no GPU needed).  *out is owned by the caller and
+ * released with sync_plan_destroy().  The plan is immutable and may be shared
+ * between threads.  EINVAL for an invalid descriptor. */
+int sync_plan(const sync_plan_desc* desc, sync_plan_t* out);
+
+/* Frees a plan and its device copies.  Only after every call using it has
+ * completed on the device. */
+void sync_plan_destroy(sync_plan_t plan);
+
+typedef struct {
+  int32_t num_chunks;  /* C = world * split */
+  int32_t num_tiles;   /* T = tiles_m * tiles_n */
+  int32_t tiles_m, tiles_n;
+  int64_t num_deps;    /* total (tile, chunk) dependency pairs */
+} sync_plan_info;
+
+int sync_plan_get_info(sync_plan_t plan, sync_plan_info* out);
+
+/* Caller-owned host arrays; a NULL member is skipped.  Sizes from
+ * sync_plan_get_info: chunk_begin[C+1], chunk_pos[C], arrival[C] (chunk id
+ * at each position), resident[C], tiles_in[C] (tiles per chunk),
+ * tile_order[T], tile_key[T] (by tile id), dep_ptr[T+1], dep_idx[num_deps],
+ * inv_ptr[C+1], inv_idx[num_deps]. */
+typedef struct {
+  int64_t* chunk_begin;
+  int32_t* chunk_pos;
+  int32_t* arrival;
+  int32_t* resident;
+  int32_t* tiles_in;
+  int32_t* tile_order;
+  int32_t* tile_key;
+  int64_t* dep_ptr;
+  int32_t* dep_idx;
+  int64_t* inv_ptr;
+  int32_t* inv_idx;
+} sync_plan_tables;
+
+int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
+
+/* ---- copy agent configuration ------------------------------------------ */
+/* Backends [SYN-S "Core method", paper sec. 5.2, Fig. 7: the same plan lowers
+ * to a copy engine or to load/store on dedicated SMs, both signalling through
+ * global-memory flags]:
+ *   PRESET      no copy; every chunk is marked ready before the kernel
+ *               (compute-only; the caller provides the whole input)
+ *   SDMA        per chunk, an SDMA-engine copy then a one-lane flag kernel, on
+ *               the library's copy stream (masked to one CU per XCD; the GEMM
+ *               runs on the other CUs).  Known limit: under the HIP runtime the
+ *               next SDMA copy does not start while the persistent GEMM runs,
+ *               so chunks not copied before the GEMM starts time out.
+ *   CU          one copy kernel on `copy_cus` dedicated CUs (CU-masked
+ *               stream); the GEMM runs on the remaining CUs
+ *   HOST_GATED  as SDMA, but chunk c's copy first waits until the host word
+ *               host_gates[c] becomes non-zero (tests: delayed or withheld
+ *               chunks) */
+enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOST_GATED = 3 };
+
+/* mode bits for sync_copy_cfg.flags */
+enum {
+  SYNC_RUN_COPY_ONLY = 1,    /* run only the copy agent (copy-only timing) */
+  SYNC_RUN_COMPUTE_ONLY = 2, /* with CU backend: run only the GEMM on its CU share, flags preset */
+  SYNC_RUN_TIMED = 4         /* record device events around the copy agent and the compute kernel,
+                                on the streams they run on; read with sync_read_timings() */
+};
+
+typedef struct {
+  int32_t backend;          /* SYNC_COPY_* */
+  int32_t copy_cus;         /* CU backend: dedicated copy CUs, 8..128, multiple of 8 */
+  uint64_t timeout_ns;      /* bound on every device-side wait; 0 = 2 s */
+  const uint32_t* host_gates; /* HOST_GATED: pinned host words (hipHostMalloc), one per chunk */
+  int32_t flags;            /* SYNC_RUN_* bits */
+  int32_t reserved[3];      /* must be zero */
+} sync_copy_cfg;
+
+/* ---- workspace ---------------------------------------------------------- */
+/* Device scratch for flags, counters, the epoch and the error word.  Owned by
+ * the caller, at least sync_workspace_size() bytes, 256-byte aligned; one
+ * workspace must not be used by two calls that may overlap in time. */
+size_t sync_workspace_size(sync_plan_t plan);
+
+/* Zeroes the workspace with a fill kernel on `stream` (call once after
+ * allocation).  Later calls bump a device-side epoch instead of clearing. */
+int sync_workspace_init(sync_plan_t plan, void* ws, void* stream);
+
+/* Synchronises `stream`, then reads the workspace error word.  Returns
+ * SYNC_OK, or SYNC_ETIMEOUT with *err_chunk (may be NULL) = the chunk whose
+ * wait expired first. */
+int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk);
+
+/* ---- launch calls --------------------------------------------------------- */
+/* AG-GEMM share [SYN-S "Experiments", paper sec. 6.1, Fig. 8: AG-GEMM;
+ * "Core method": tiles wait until the chunks they consume have arrived].
+ *   a_peer  bf16 [m][k]: every shard at its natural rows (stands in for the
+ *           peers' memory); read-only.
+ *   a_local bf16 [m][k]: the resident shard's rows are filled by the caller;
+ *           the copy agent writes every other chunk's rows (PRESET: the caller
+ *           fills all rows).
+ *   b       bf16, [k][n] (SYNC_B_KN) or [n][k] (SYNC_B_NK).
+ *   c       [m][n], c_dtype fp32 or bf16 (round to nearest even).
+ * Kernel constraints (else EUNSUPPORTED): k % 64 == 0, n % 8 == 0, tile
+ * (tile_m, tile_n) in {(256,256), (256,128), (128,128)}. */
+int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local,
+                 const void* b, void* c, int32_t c_dtype, void* ws, void* compute, void* copy);
+
+/* GEMM-RS share [SYN-S "Experiments": GEMM-RS; ENT: tiles reordered so output
+ * for communication is produced at a steady pace; SM-based fine-grained
+ * communication].  The GEMM visits tiles in send order; when the last tile of
+ * chunk c is stored it raises done[c]; the copy agent (CU backend: dedicated
+ * CUs; SDMA: not supported, EUNSUPPORTED) waits for done[c] in send order and
+ * copies the chunk's rows of c into `staging`, slot p = chunk arrival[p]
+ * (slots packed back to back in send order).
+ *   a bf16 [m][k]; b bf16 as in sync_ag_gemm; c and staging [m][n] c_dtype.
+ * PRESET: the GEMM alone (done flags raised, no copy-out). */
+int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
+                 int32_t c_dtype, void* staging, void* ws, void* compute, void* copy);
+
+/* Ring-attention local step [SYN-S "Experiments", paper sec. 6.1 and Fig. 9:
+ * RingAttention].  KV blocks (chunks of K and V token rows) are staged from
+ * k_peer/v_peer into k_local/v_local in arrival order; each (query tile, head)
+ * work item folds every block, in arrival order, into an fp32 online-softmax
+ * state (m, l, O).
+ *   q bf16 [m][heads_q][k]; k_*, v_* bf16 [world*n][heads_kv][k];
+ *   o fp32 [m][heads_q][k]; m_state, l_state fp32 [heads_q][m];
+ *   lse fp32 [heads_q][m] or NULL (written when FINALIZE).
+ *   flags: SYNC_ATTN_INIT starts from m=-inf, l=0, O=0 (else reads the
+ *   state); SYNC_ATTN_FINALIZE writes O/l to o and m + ln l to lse.
+ * Kernel constraints: k (head dim) == 128, tile_m == 128. */
+enum { SYNC_ATTN_INIT = 1, SYNC_ATTN_FINALIZE = 2 };
+int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q,
+                        const void* k_peer, const void* v_peer, void* k_local, void* v_local,
+                        float* o, float* m_state, float* l_state, float* lse, float scale,
+                        int32_t flags, void* ws, void* compute, void* copy);
+
+/* Durations of the most recent SYNC_RUN_TIMED calls on the current device
+ * (a ring of 1024), oldest first; waits for those events.  kernel_ms is the
+ * compute kernel (GEMM or attention) from just before its launch to just
+ * after it, on its own stream; copy_ms spans the copy agent's work (0 if none).
+ * Reading empties the ring.  *count = records written to out (<= max). */
+typedef struct {
+  float kernel_ms;
+  float copy_ms;
+} sync_timing;
+
+int sync_read_timings(int32_t max, sync_timing* out, int32_t* count);
+
+/* ---- device facts and housekeeping -------------------------------------- */
+typedef struct {
+  int32_t device;        /* HIP device ordinal (current device) */
+  int32_t num_cus;       /* multiprocessor count */
+  int32_t num_xcds;      /* XCDs (8 on MI355X) */
+  int32_t clock_khz;     /* peak shader clock */
+  int64_t wall_clock_khz;/* device wall clock used for wait time limits */
+  char arch[64];         /* gcnArchName */
+} sync_device_info;
+
+int sync_get_device_info(sync_device_info* out);
+
+/* Thread-local message for the last failing call on this thread. */
+const char* sync_last_error(void);
+
+/* Destroys the library's streams and events on every device. */
+void sync_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SYNC_OVERLAP_H */

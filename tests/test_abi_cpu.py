@@ -1,0 +1,78 @@
+"""The C-ABI library loads without a GPU, exports every entry point the header
+declares, and its CPU-side argument checks reject bad input."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from communication_overlap_gemm_amd import _abi as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sync_overlap.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sync_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_names():
+    assert sorted(A.EXPORTED_SYMBOLS) == _declared()
+
+
+@pytest.mark.parametrize("name", _declared())
+def test_library_exports_symbol(name):
+    lib = ctypes.CDLL(A.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(m=10, world=4), "divisible"),
+    (dict(split=0), "split"),
+    (dict(split=99), "split"),
+    (dict(rank=-1), "rank"),
+    (dict(ring_dir=2), "ring_dir"),
+    (dict(op=7), "op"),
+    (dict(tile_order=9), "tile_order"),
+    (dict(b_layout=3), "b_layout"),
+    (dict(pattern=1, explicit_order=[0, 1, 1, 2]), "permutation"),
+    (dict(pattern=1), "explicit_order"),
+])
+def test_plan_rejects(bad, msg):
+    kw = dict(op=1, m=8, n=8, k=64, world=4, tile_m=2, tile_n=2)
+    kw.update(bad)
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_plan(A.make_desc(**kw))
+    assert ei.value.code == A.SYNC_EINVAL and msg in ei.value.message
+
+
+def test_reserved_must_be_zero():
+    d = A.make_desc(1, 8, 8, 64, 4, tile_m=2, tile_n=2)
+    d.reserved[1] = 5
+    with pytest.raises(A.SyncError):
+        A.sync_plan(d)
+
+
+def test_null_arguments():
+    lib = A.lib()
+    assert lib.sync_plan(None, None) == A.SYNC_EINVAL
+    assert lib.sync_plan_get_info(None, None) == A.SYNC_EINVAL
+    assert lib.sync_workspace_size(None) == 0
+    assert lib.sync_ag_gemm(None, None, None, None, None, None, 0, None, None, None) == A.SYNC_EINVAL
+    assert lib.sync_gemm_rs(None, None, None, None, None, 0, None, None, None, None) == A.SYNC_EINVAL
+    assert "plan" in A.sync_last_error()
+
+
+def test_wrong_op_for_plan():
+    p = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, 8, 8, 64, 4, tile_m=2, tile_n=2))
+    rc = A.lib().sync_ag_gemm(p.handle, None, None, None, None, None, 0, 256, None, None)
+    assert rc == A.SYNC_EINVAL and "different op" in A.sync_last_error()
+
+
+def test_workspace_size_scales_with_chunks():
+    p1 = A.sync_plan(A.make_desc(1, 64, 8, 64, 4, split=1, tile_m=2, tile_n=2))
+    p2 = A.sync_plan(A.make_desc(1, 4096, 8, 64, 4, split=256, tile_m=2, tile_n=2))
+    assert A.sync_workspace_size(p1) == 256 + 4 * 256
+    assert A.sync_workspace_size(p2) == 256 + 4 * 4096

@@ -1,0 +1,77 @@
+"""The library's C++ planner (called through the C ABI, no GPU needed) must
+produce tables bit-identical to the oracle planner's, for every descriptor of
+a brute-force enumeration plus the workload configurations."""
+import itertools
+
+import numpy as np
+import pytest
+
+from communication_overlap_gemm_amd import _abi as A
+from oracle import planner_ref as P
+
+KEYS = ["chunk_begin", "chunk_pos", "arrival", "resident", "tiles_in", "tile_order", "tile_key", "dep_ptr",
+        "dep_idx", "inv_ptr", "inv_idx"]
+
+
+def _both(**kw):
+    ref = P.plan_ref(P.PlanDesc(**kw))
+    kw2 = dict(kw)
+    order = kw2.pop("explicit_order", None)
+    lib = A.sync_plan_export(A.sync_plan(A.make_desc(explicit_order=order, **kw2)))
+    return ref, lib
+
+
+def _same(ref, lib):
+    assert lib["num_chunks"] == ref.num_chunks and lib["num_tiles"] == ref.num_tiles
+    assert lib["tiles_m"] == ref.tiles_m and lib["tiles_n"] == ref.tiles_n
+    for key in KEYS:
+        assert np.array_equal(lib[key], np.asarray(getattr(ref, key), dtype=lib[key].dtype)), key
+
+
+def _enumerate():
+    for op in (P.OP_AG_GEMM, P.OP_GEMM_RS):
+        for W in (1, 2, 3, 4):
+            for rows_per in (1, 2, 5):
+                m = W * rows_per
+                for s in range(1, min(3, rows_per) + 1):
+                    for tm, order, d in itertools.product((1, 2, 4), (0, 1, 2), (1, -1)):
+                        yield dict(op=op, m=m, n=5, k=3, world=W, rank=W - 1, ring_dir=d, split=s, tile_m=tm,
+                                   tile_n=2, tile_order=order, group_m=2)
+    for W, n, s, tm in itertools.product((1, 2, 3), (2, 3), (1, 2), (1, 3)):
+        yield dict(op=P.OP_RING_ATTN, m=5, n=n, k=8, world=W, rank=0, split=s, tile_m=tm, tile_n=1,
+                   heads_q=4, heads_kv=2, tile_order=1)
+
+
+def test_enumeration_bit_exact():
+    n = 0
+    for kw in _enumerate():
+        _same(*_both(**kw))
+        n += 1
+    assert n > 500
+
+
+WORKLOADS = [
+    # tiny AG-GEMM share: 4 shards of 256 rows, 128x128 tiles
+    dict(op=1, m=1024, n=1024, k=1024, world=4, tile_m=128, tile_n=128),
+    # Llama-3-8B FFN up-projection AG share, split 1..4, 256x256 tiles
+    *[dict(op=1, m=8192, n=1792, k=4096, world=8, split=s, tile_m=256, tile_n=256, tile_order=o)
+      for s in (1, 2, 3, 4) for o in (0, 1, 2)],
+    # Llama-3-8B FFN down-projection RS share
+    dict(op=2, m=8192, n=4096, k=1792, world=8, tile_m=256, tile_n=256),
+    # 70B-like AG share, chunk-size sweep
+    *[dict(op=1, m=16384, n=3584, k=8192, world=8, split=s, tile_m=256, tile_n=256, tile_order=o)
+      for s in (1, 4, 16, 64) for o in (0, 1, 2)],
+    # ring-attention step: 4096 queries, 8 KV blocks of 4096 tokens, 32/8 heads
+    dict(op=3, m=4096, n=4096, k=128, world=8, tile_m=128, tile_n=1, heads_q=32, heads_kv=8),
+]
+
+
+@pytest.mark.parametrize("kw", WORKLOADS)
+def test_workload_plans_bit_exact(kw):
+    _same(*_both(**kw))
+
+
+def test_explicit_order_bit_exact():
+    for perm in itertools.permutations(range(4)):
+        _same(*_both(op=1, m=12, n=4, k=64, world=4, rank=1, pattern=1, explicit_order=list(perm), split=3,
+                      tile_m=2, tile_n=2, tile_order=2, group_m=3))
