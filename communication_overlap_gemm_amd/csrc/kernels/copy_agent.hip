@@ -29,7 +29,9 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kCopyThreads = 256;
 constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
 
-// Copies bytes [lo, hi) of src to dst (16-byte granules; both 16-byte aligned).
+// Copies bytes [lo, hi) of src to dst (16-byte granules; both 16-byte aligned),
+// kUnroll loads in flight per thread.  STREAM selects non-temporal accesses.
+template <bool STREAM>
 __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* __restrict__ dst, int64_t lo,
                                            int64_t hi) {
   const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src);
@@ -37,20 +39,58 @@ __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* _
   int64_t g = lo / 16 + threadIdx.x;
   const int64_t gend = hi / 16;
   const int64_t step = kCopyThreads;
+  auto ld = [](const u32x4_t* p) { return STREAM ? __builtin_nontemporal_load(p) : *p; };
+  auto st = [](u32x4_t v, u32x4_t* p) {
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(v, p);
+    else
+      *p = v;
+  };
   for (; g + (kUnroll - 1) * step < gend; g += kUnroll * step) {
     u32x4_t v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(s + g + u * step);
+    for (int u = 0; u < kUnroll; ++u) v[u] = ld(s + g + u * step);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) d[g + u * step] = v[u];
+    for (int u = 0; u < kUnroll; ++u) st(v[u], d + g + u * step);
   }
-  for (; g < gend; g += step) d[g] = __builtin_nontemporal_load(s + g);
+  for (; g < gend; g += step) st(ld(s + g), d + g);
 }
 
+// Publication.  A chunk is complete when every workgroup's stores of it are
+// visible device-wide.  Each workgroup first drains its stores into its XCD's
+// L2 (workgroup-scope release = wait for the stores), then counts itself in a
+// per-(chunk, XCD) counter; the last workgroup of each XCD writes that L2 back
+// with one agent-scope release (which covers the other workgroups' lines in
+// the same L2) and adds the XCD's workgroups to the chunk's total; whoever
+// completes the total raises the flag.  One L2 writeback per XCD per chunk
+// instead of one per workgroup.  A census at kernel start tells each
+// workgroup how many of the grid's workgroups share its XCD.
 __global__ __launch_bounds__(kCopyThreads) void copy_agent(CopyArgs a) {
   __shared__ int32_t s_ok;
+  __shared__ uint32_t s_mine;
   const uint32_t epoch = a.hdr[WS_EPOCH];
   const int64_t G = gridDim.x, b = blockIdx.x;
+  const int xcc = xcc_id();
+  if (threadIdx.x == 0) {
+    add_acq_rel_agent(a.hdr + WS_CENSUS + xcc, 1u);
+    add_acq_rel_agent(a.hdr + WS_CENSUS_TOTAL, 1u);
+    // every workgroup of this grid is resident at once (the grid is sized to
+    // the dedicated CUs), so the census completes; the wait is still bounded
+    const uint64_t t0 = wall_clock64();
+    bool ok = true;
+    while (ld_relaxed_agent(a.hdr + WS_CENSUS_TOTAL) < static_cast<uint32_t>(G)) {
+      __builtin_amdgcn_s_sleep(1);
+      if (wall_clock64() - t0 > a.timeout_ticks) {
+        record_timeout(a.hdr, -1);
+        ok = false;
+        break;
+      }
+    }
+    s_mine = ok ? ld_relaxed_agent(a.hdr + WS_CENSUS + xcc) : 0u;
+  }
+  __syncthreads();
+  const uint32_t mine = s_mine;
+  if (mine == 0) return;
   for (int32_t p = 0; p < a.num_chunks; ++p) {
     const int32_t c = a.arrival[p];
     if (!a.copy_out && a.resident[c]) continue;
@@ -71,13 +111,20 @@ __global__ __launch_bounds__(kCopyThreads) void copy_agent(CopyArgs a) {
       const int64_t bytes = (r1 - r0) * a.row_bytes[x];
       const int64_t granules = bytes / 16;
       const int64_t lo = granules * b / G * 16, hi = granules * (b + 1) / G * 16;
-      copy_range(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
+      if (a.streaming)
+        copy_range<true>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
+      else
+        copy_range<false>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
     }
-    release_agent();  // this thread's stores are visible device-wide
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores have reached the L2
     __syncthreads();
     if (threadIdx.x == 0) {
-      const uint32_t old = add_acq_rel_agent(a.parts + c, 1u);
-      if (old + 1u == static_cast<uint32_t>(G)) st_release_agent(a.out_flags + c, epoch);
+      const uint32_t old = add_acq_rel_agent(a.xparts + c * kMaxXcd + xcc, 1u);
+      if (old + 1u == mine) {
+        release_agent();  // write this XCD's L2 back: every workgroup of this XCD has stored
+        const uint32_t done = add_acq_rel_agent(a.parts + c, mine);
+        if (done + mine == static_cast<uint32_t>(G)) st_release_agent(a.out_flags + c, epoch);
+      }
     }
   }
 }
@@ -86,8 +133,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_agent(CopyArgs a) {
 // counters, and raises the flags of chunks that need no copy (resident ones,
 // or all of them for compute-only runs).  One workgroup.
 __global__ __launch_bounds__(256) void begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters,
-                                                  uint32_t* parts, int32_t num_chunks, const int32_t* resident,
-                                                  int32_t preset_all) {
+                                                  uint32_t* parts, uint32_t* xparts, int32_t num_chunks,
+                                                  const int32_t* resident, int32_t preset_all) {
   __shared__ uint32_t s_epoch;
   if (threadIdx.x == 0) {
     uint32_t e = hdr[WS_EPOCH] + 1u;
@@ -96,8 +143,11 @@ __global__ __launch_bounds__(256) void begin_call(uint32_t* hdr, uint32_t* flags
     hdr[WS_ERR_CODE] = 0u;
     hdr[WS_ERR_CHUNK] = 0u;
     hdr[WS_TICKET] = 0u;
+    hdr[WS_CENSUS_TOTAL] = 0u;
     s_epoch = e;
   }
+  if (threadIdx.x < kMaxXcd) hdr[WS_CENSUS + threadIdx.x] = 0u;
+  for (int32_t i = threadIdx.x; i < num_chunks * kMaxXcd; i += blockDim.x) xparts[i] = 0u;
   __syncthreads();
   const uint32_t e = s_epoch;
   for (int32_t c = threadIdx.x; c < num_chunks; c += blockDim.x) {
@@ -126,14 +176,22 @@ hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStr
   return hipGetLastError();
 }
 
+// Copy-agent workgroups that fit on one CU at once (the census needs the whole
+// grid resident).
+int copy_agent_max_wg_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, copy_agent, kCopyThreads, 0) != hipSuccess) return 1;
+  return n < 1 ? 1 : n;
+}
+
 hipError_t launch_copy_agent(const CopyArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(copy_agent, dim3(grid), dim3(kCopyThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters, uint32_t* parts, int32_t num_chunks,
-                             const int32_t* resident, int32_t preset_all, hipStream_t s) {
-  hipLaunchKernelGGL(begin_call, dim3(1), dim3(256), 0, s, hdr, flags, counters, parts, num_chunks, resident,
+hipError_t launch_begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters, uint32_t* parts, uint32_t* xparts,
+                             int32_t num_chunks, const int32_t* resident, int32_t preset_all, hipStream_t s) {
+  hipLaunchKernelGGL(begin_call, dim3(1), dim3(256), 0, s, hdr, flags, counters, parts, xparts, num_chunks, resident,
                      preset_all);
   return hipGetLastError();
 }

@@ -25,14 +25,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Workspace header words (uint32 index).  The flag and counter arrays follow
-// at the offsets the host computes (see runtime.cpp: ws_layout()).
+// at offsets the host computes from the plan's chunk count.
 enum : int {
   WS_EPOCH = 0,      // epoch of the current call (bumped by the begin kernel)
   WS_ERR_CODE = 1,   // 0 = fine, else ERR_* below
   WS_ERR_CHUNK = 2,  // chunk whose wait expired first
   WS_TICKET = 3,     // reserved for dynamic tile tickets
+  WS_CENSUS_TOTAL = 4,  // copy agent: workgroups that have started
+  WS_CENSUS = 16,       // copy agent: workgroups started per XCD (16 slots)
   WS_HEADER_WORDS = 64
 };
+constexpr int kMaxXcd = 16;
+
+// XCD (XCC) this wave runs on.
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kMaxXcd - 1); }
 enum : uint32_t { ERR_TIMEOUT = 1u };
 
 __device__ __forceinline__ uint32_t ld_relaxed_agent(const uint32_t* p) {

@@ -264,9 +264,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     }
 
     if constexpr (RS) {
-      release_agent();  // this thread's C stores are visible device-wide
+      // every wave's C stores have reached the L2; then one agent-scope release
+      // (a write-back of this XCD's L2, covering all four waves) before counting
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __syncthreads();
       if (tid == 0) {
+        release_agent();
         for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) {
           const int32_t c = a.dep_idx[e];
           const uint32_t old = add_acq_rel_agent(a.counters + c, 1u);

@@ -37,9 +37,11 @@ struct CopyArgs {
   uint32_t* out_flags;         // raised per chunk when its copy is complete
   const uint32_t* wait_flags;  // copy-out: done flags to wait for
   uint32_t* parts;             // per-chunk count of finished workgroups
+  uint32_t* xparts;            // per (chunk, XCD) count of finished workgroups, C x 16
   uint32_t* hdr;
   uint64_t timeout_ticks;
   int32_t copy_out;
+  int32_t streaming;  // non-temporal loads and stores
 };
 
 }  // namespace syncov

@@ -30,8 +30,9 @@ namespace syncov {
 hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid, hipStream_t s);
 bool gemm_variant_exists(int tm, int tn);
 hipError_t launch_copy_agent(const CopyArgs& a, int grid, hipStream_t s);
-hipError_t launch_begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters, uint32_t* parts, int32_t num_chunks,
-                             const int32_t* resident, int32_t preset_all, hipStream_t s);
+int copy_agent_max_wg_per_cu();
+hipError_t launch_begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters, uint32_t* parts, uint32_t* xparts,
+                             int32_t num_chunks, const int32_t* resident, int32_t preset_all, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s);
 
@@ -58,6 +59,10 @@ int hip_fail(hipError_t e, const char* what) {
     hipError_t _e = (expr);                       \
     if (_e != hipSuccess) return hip_fail(_e, #expr); \
   } while (0)
+
+// Default copy-agent workgroups per dedicated CU (measured fastest: more
+// workgroups add per-chunk synchronisation without adding bandwidth).
+constexpr int kCopyWgPerCu = 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -257,9 +262,10 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
 
 // Workspace layout: 256-byte header, then four uint32[C] arrays, each padded
 // to 256 bytes: flags (ready / done), counters (GEMM tiles stored per chunk),
-// parts (copy workgroups finished per chunk), sent (copy-out done).
+// parts (copy workgroups finished per chunk), sent (copy-out done); then
+// xparts, uint32[C][16] (copy workgroups finished per chunk and XCD).
 struct WsView {
-  uint32_t *hdr, *flags, *counters, *parts, *sent;
+  uint32_t *hdr, *flags, *counters, *parts, *sent, *xparts;
 };
 
 int64_t ws_array_bytes(int32_t C) { return align_up(static_cast<int64_t>(C) * 4, 256); }
@@ -273,6 +279,7 @@ WsView ws_view(void* ws, int32_t C) {
   v.counters = reinterpret_cast<uint32_t*>(b + 256 + a);
   v.parts = reinterpret_cast<uint32_t*>(b + 256 + 2 * a);
   v.sent = reinterpret_cast<uint32_t*>(b + 256 + 3 * a);
+  v.xparts = reinterpret_cast<uint32_t*>(b + 256 + 4 * a);
   return v;
 }
 
@@ -291,8 +298,10 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   sync_copy_cfg cfg{};
   cfg.backend = SYNC_COPY_SDMA;
   if (cfg_in) cfg = *cfg_in;
-  for (int i = 0; i < 3; ++i)
-    if (cfg.reserved[i]) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
+  if (cfg.reserved) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
+  if (cfg.copy_wg_per_cu < 0 || cfg.copy_wg_per_cu > 16) return fail(SYNC_EINVAL, "copy_wg_per_cu must be in [0, 16]");
+  if (cfg.copy_wg_per_cu == 0) cfg.copy_wg_per_cu = kCopyWgPerCu;
+  cfg.copy_wg_per_cu = std::min(cfg.copy_wg_per_cu, copy_agent_max_wg_per_cu());  // whole grid resident
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_HOST_GATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED))
@@ -445,7 +454,8 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out) {
 
 size_t sync_workspace_size(sync_plan_t plan) {
   if (!plan) return 0;
-  return static_cast<size_t>(256 + 4 * ws_array_bytes(plan->plan.num_chunks));
+  const int32_t C = plan->plan.num_chunks;
+  return static_cast<size_t>(256 + 4 * ws_array_bytes(C) + align_up(static_cast<int64_t>(C) * 4 * kMaxXcd, 256));
 }
 
 int sync_workspace_init(sync_plan_t plan, void* ws, void* stream) {
@@ -489,7 +499,8 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
   const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
-  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, pl.num_chunks, cx.tab->resident,
+  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, cx.ws.xparts, pl.num_chunks,
+                            cx.tab->resident,
                             compute_only ? 1 : 0, cs));
   GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
   auto gemm_on = [&](hipStream_t st, int grid) -> int {
@@ -521,11 +532,13 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
       ca.resident = cx.tab->resident;
       ca.out_flags = cx.ws.flags;
       ca.parts = cx.ws.parts;
+      ca.xparts = cx.ws.xparts;
       ca.hdr = cx.ws.hdr;
       ca.timeout_ticks = cx.timeout_ticks;
+      ca.streaming = cx.cfg.copy_streaming;
       HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
       if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
-      HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * 2, mp->copy));
+      HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * cx.cfg.copy_wg_per_cu, mp->copy));
       if (tm) {
         HIP_TRY(hipEventRecord(tm->c1, mp->copy));
         tm->has_copy = true;
@@ -590,7 +603,8 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
   hipStream_t cs = static_cast<hipStream_t>(compute);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
-  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, pl.num_chunks, nullptr, 0, cs));
+  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, cx.ws.xparts, pl.num_chunks, nullptr,
+                            0, cs));
   GemmArgs g = make_gemm_args(pl, cx, a, b, c);
   auto gemm_on = [&](hipStream_t st, int grid) -> int {
     if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
@@ -623,12 +637,14 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
     ca.out_flags = cx.ws.sent;
     ca.wait_flags = cx.ws.flags;
     ca.parts = cx.ws.parts;
+    ca.xparts = cx.ws.xparts;
     ca.hdr = cx.ws.hdr;
     ca.timeout_ticks = cx.timeout_ticks;
     ca.copy_out = 1;
+    ca.streaming = cx.cfg.copy_streaming;
     HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
     if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
-    HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * 2, mp->copy));
+    HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * cx.cfg.copy_wg_per_cu, mp->copy));
     if (tm) {
       HIP_TRY(hipEventRecord(tm->c1, mp->copy));
       tm->has_copy = true;

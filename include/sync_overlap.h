@@ -175,7 +175,10 @@ typedef struct {
   uint64_t timeout_ns;      /* bound on every device-side wait; 0 = 2 s */
   const uint32_t* host_gates; /* HOST_GATED: pinned host words (hipHostMalloc), one per chunk */
   int32_t flags;            /* SYNC_RUN_* bits */
-  int32_t reserved[3];      /* must be zero */
+  int32_t copy_wg_per_cu;   /* CU backend: copy workgroups per dedicated CU; 0 = 1; clamped to
+                                what fits on a CU at once */
+  int32_t copy_streaming;   /* CU backend: 1 = non-temporal loads/stores in the copy agent; 0 = plain */
+  int32_t reserved;         /* must be zero */
 } sync_copy_cfg;
 
 /* ---- workspace ---------------------------------------------------------- */

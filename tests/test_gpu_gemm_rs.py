@@ -1,0 +1,129 @@
+"""GEMM-RS share on the GPU, through the C ABI, against the oracle.
+
+The GEMM visits tiles in send order; each stored tile counts toward the
+chunks of C it wrote, the last one raises the chunk's done flag, and the copy
+agent on dedicated CUs copies each finished chunk, in send order, into its
+staging slot (Syncopate summary page, "Experiments": GEMM-RS; Entwine
+abstract: reordered tiles feeding fine-grained SM-based communication).
+Checks: C within the fp32 parity bar; staging slot p bitwise equal to the rows
+of chunk arrival[p] of C (it is a copy); every done counter equals the
+chunk's tile count; every done and sent flag holds the call's epoch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from communication_overlap_gemm_amd import _abi as A
+from communication_overlap_gemm_amd import inputs
+
+from gpu_util import bf16_poison, dev_bits, host_bits, shard_frobenius, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def ws_arrays(ws, num_chunks):
+    w = ws.cpu().numpy().view(np.uint32)
+    a = -(-4 * num_chunks // 256) * 256 // 4
+    hdr, rest = w[:64], w[64:]
+    return hdr, rest[:num_chunks], rest[a:a + num_chunks], rest[2 * a:2 * a + num_chunks], rest[3 * a:3 * a + num_chunks]
+
+
+def run_rs(m, n, k, world, a_bits, b_bits, split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
+           backend=A.SYNC_COPY_CU, copy_cus=16, c_dtype=A.SYNC_DTYPE_F32, rank=0, layout=A.SYNC_B_KN):
+    print(f"[rs] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
+          f"cus={copy_cus} dtype={c_dtype}", flush=True)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, world, rank=rank, split=split, tile_m=tile[0],
+                                   tile_n=tile[1], tile_order=order, b_layout=layout))
+    tabs = A.sync_plan_export(plan)
+    a = dev_bits(a_bits)
+    b = dev_bits(b_bits)
+    if c_dtype == A.SYNC_DTYPE_F32:
+        c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+        staging = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    else:
+        c = bf16_poison((m, n))
+        staging = bf16_poison((m, n))
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    A.sync_gemm_rs(plan, A.make_cfg(backend, copy_cus=copy_cus), a, b, c, c_dtype, staging, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    torch.cuda.synchronize()
+    hdr, flags, counters, parts, sent = ws_arrays(ws, tabs["num_chunks"])
+    assert np.array_equal(counters, tabs["tiles_in"].astype(np.uint32))
+    assert np.all(flags == hdr[0])
+    if backend != A.SYNC_COPY_PRESET:
+        assert np.all(sent == hdr[0])
+    cn = c.cpu().numpy()
+    st = staging.cpu().numpy()
+    return cn, st, tabs
+
+
+def check_staging(cn, st, tabs):
+    row = 0
+    for p in range(tabs["num_chunks"]):
+        ch = tabs["arrival"][p]
+        r0, r1 = tabs["chunk_begin"][ch], tabs["chunk_begin"][ch + 1]
+        assert np.array_equal(st[row:row + r1 - r0].view(np.uint8), cn[r0:r1].view(np.uint8)), f"slot {p}"
+        row += r1 - r0
+    assert row == cn.shape[0]
+
+
+@pytest.mark.parametrize("order", [A.SYNC_ORDER_ROW_MAJOR, A.SYNC_ORDER_CHUNK_MAJOR, A.SYNC_ORDER_SWIZZLED])
+def test_tiny_rs(order):
+    m, n, k, W = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 16.0)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    cn, st, tabs = run_rs(m, n, k, W, a, b, order=order)
+    assert shard_frobenius(cn.astype(np.float64), ref, W) <= 1e-3
+    check_staging(cn, st, tabs)
+    assert list(tabs["arrival"]) == [3, 2, 1, 0]  # ring send order of rank 0, own chunk last
+
+
+@pytest.mark.parametrize("m,n,k,world,split,tile,rank", [
+    (1000, 520, 320, 4, 3, (128, 128), 1),   # ragged, chunks of 83/84 rows under 128-row tiles
+    (968, 264, 192, 2, 5, (256, 128), 0),
+    (512, 256, 128, 8, 2, (256, 256), 5),    # 32-row chunks, 8 per tile
+])
+def test_ragged_rs(m, n, k, world, split, tile, rank):
+    a, b = inputs.gemm_operands(m, n, k, 16.0)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    cn, st, tabs = run_rs(m, n, k, world, a, b, split=split, tile=tile, rank=rank, copy_cus=8)
+    assert shard_frobenius(cn.astype(np.float64), ref, world) <= 1e-3
+    check_staging(cn, st, tabs)
+
+
+def test_rs_bf16_and_preset():
+    m, n, k, W = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 16.0)
+    cn, st, tabs = run_rs(m, n, k, W, a, b, c_dtype=A.SYNC_DTYPE_BF16, copy_cus=32)
+    check_staging(cn, st, tabs)
+    c32, _, _ = run_rs(m, n, k, W, a, b, backend=A.SYNC_COPY_PRESET)
+    want = inputs.f32_to_bf16_bits(c32).view(np.int16)
+    assert np.array_equal(cn, want)  # bf16 output is the fp32 result rounded to nearest even
+
+
+M3, N3, K3, W3 = 8192, 4096, 1792, 8
+
+
+def test_full_size_rs_exact_integers():
+    a, b = inputs.gemm_operands(M3, N3, K3, 1.0, integer=True)
+    cn, st, tabs = run_rs(M3, N3, K3, W3, a, b, tile=(256, 256), copy_cus=32)
+    assert np.all(cn == np.round(cn))
+    rng = np.random.default_rng(3)
+    rows, cols = rng.integers(0, M3, 4000), rng.integers(0, N3, 4000)
+    assert np.array_equal(cn[rows, cols].astype(np.float64), oracle.gemm_f64_sampled(a, b, M3, N3, K3, rows, cols))
+    check_staging(cn, st, tabs)
+
+
+def test_full_size_rs_normal():
+    a, b = inputs.gemm_operands(M3, N3, K3, 64.0)
+    cn, st, tabs = run_rs(M3, N3, K3, W3, a, b, tile=(256, 256), copy_cus=32)
+    rng = np.random.default_rng(4)
+    rows, cols = rng.integers(0, M3, 20000), rng.integers(0, N3, 20000)
+    ref = oracle.gemm_f64_sampled(a, b, M3, N3, K3, rows, cols)
+    for s in range(W3):
+        sel = rows // (M3 // W3) == s
+        assert np.linalg.norm(cn[rows[sel], cols[sel]] - ref[sel]) / np.linalg.norm(ref[sel]) <= 1e-3
+    check_staging(cn, st, tabs)
