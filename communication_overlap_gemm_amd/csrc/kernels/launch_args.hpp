@@ -44,4 +44,26 @@ struct CopyArgs {
   int32_t streaming;  // non-temporal loads and stores
 };
 
+// Ring-attention step (ring_attn.hip).
+struct AttnArgs {
+  const uint16_t* q;  // bf16 [sq][heads_q][128]
+  const uint16_t* k;  // bf16 [world*n][heads_kv][128] (local copy, filled by the copy agent)
+  const uint16_t* v;
+  float* o;           // [sq][heads_q][128]
+  float* m_state;     // [heads_q][sq]
+  float* l_state;
+  float* lse;         // [heads_q][sq] or null
+  int64_t sq;
+  int32_t heads_q, heads_kv, heads_per_item;
+  float scale;
+  int32_t init, finalize;
+  const int64_t* chunk_begin;  // key-row bounds of the KV chunks
+  const int32_t* arrival;
+  int32_t num_chunks;
+  const uint32_t* flags;
+  uint32_t* hdr;
+  uint64_t timeout_ticks;
+  int32_t nxcd;
+};
+
 }  // namespace syncov

@@ -1,0 +1,299 @@
+// Ring-attention local step for gfx950: the rank's queries meet every KV
+// block, block by block in the order the blocks arrive, folding each into an
+// fp32 online-softmax state (m, l, O).
+//
+// Method: Syncopate summary page, "Experiments" (paper sec. 6.1 and Fig. 9):
+// RingAttention among the evaluated operators, with KV blocks passed between
+// ranks; the chunk plan makes the kernel wait for each block's ready flag
+// before it reads it ("Core method", paper sec. 5).  The per-block merge is the
+// usual online softmax: m' = max(m, max s), l' = l e^(m-m') + sum e^(s-m'),
+// O' = O e^(m-m') + sum e^(s-m') V.
+//
+// gfx950 design:
+//  * A workgroup (8 wave64s) owns up to 4 query heads that share one KV head
+//    (grouped-query attention) and 32 query rows per wave; for 32 query and 8
+//    KV heads that is 64 rows x 4 heads, so each K/V tile loaded into LDS is
+//    used by 256 query rows.
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of one query per
+//    32-key block, so the row max and row sum over keys are in-register
+//    reductions plus one swap between the two 32-lane halves.
+//  * O^T += V^T P^T keeps P in registers: the score accumulator's layout is
+//    already the MFMA B-operand layout once the 16 keys of each k-step are
+//    read in the order [0-3, 8-11, 4-7, 12-15]; V^T is written to LDS with
+//    its keys permuted the same way.  Each lane's O^T column is one query, so
+//    the rescale by e^(m-m') is a per-lane multiply.
+//  * exp2 with the scale folded into log2(e) units; probabilities go to bf16
+//    for the PV product, the running sum stays fp32.
+//  * KV tiles of 64 keys, double-buffered in LDS (64 KB), prefetched one tile
+//    ahead through registers; raw buffer loads return zero past a chunk's
+//    last key, and those keys are masked to -inf.
+#include <math.h>
+
+#include "device_common.hpp"
+#include "launch_args.hpp"
+
+namespace syncov {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;           // head dim
+constexpr int kKT = 64;           // keys per tile
+constexpr int kAttnThreads = 512; // 8 waves
+// A work item is HG query heads sharing one KV head (HG = min(heads_q /
+// heads_kv, 4)) times 32 * (8 / HG) query rows: 8 waves, one per (head, 32 rows).
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+
+// K tile rows are 256 bytes (16 slots): swizzle the slot with the row.
+__device__ __forceinline__ int kswz(int row, int slot) { return slot ^ (row & 15); }
+// V^T rows are 128 bytes (8 slots).
+__device__ __forceinline__ int vswz(int row, int slot) { return slot ^ ((row ^ (row >> 3)) & 7); }
+
+// Physical position (0..15) inside a 16-key k-step -> key offset.  Lane half h
+// holds keys {4h..4h+3, 8+4h..8+4h+3} of the step in the score accumulator.
+__device__ __forceinline__ int perm16(int phys) { return ((phys >> 3) << 2) + ((phys >> 2) & 1) * 8 + (phys & 3); }
+
+__global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
+  __shared__ u32x4_t Ks[2][kKT * 16];  // [key][16 slots of 8 d]
+  __shared__ u32x4_t Vt[2][kD * 8];    // [dv][8 slots of 8 permuted keys]
+  __shared__ int32_t s_ok;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int HG = a.heads_per_item, QS = 8 / HG, QB = 32 * QS;
+  const int hh = wave % HG, qs = wave / HG;
+  const int half = lane >> 5, col = lane & 31;
+  const uint32_t epoch = a.hdr[WS_EPOCH];
+  const int64_t Hq = a.heads_q, Hkv = a.heads_kv;
+  const int64_t krow = Hkv * kD;  // elements between consecutive keys of one head
+  const float c2 = a.scale * 1.4426950408889634f;  // scale in log2 units
+  const int group = static_cast<int>(Hq / Hkv);  // query heads per KV head
+  const int nqb = static_cast<int>((a.sq + QB - 1) / QB);
+  const int items = nqb * static_cast<int>(Hq / HG);
+
+  const int32_t slot0 = xcd_slot(blockIdx.x, gridDim.x, a.nxcd);
+  for (int item = slot0; item < items; item += gridDim.x) {
+    const int hg = item / nqb, qb = item - hg * nqb;  // head-group-major: one KV head's items adjacent
+    const int64_t h = static_cast<int64_t>(hg) * HG + hh;
+    const int g = static_cast<int>(h / group);  // KV head (uniform: HG divides the group or equals it)
+    const int64_t q = static_cast<int64_t>(qb) * QB + qs * 32 + col;  // this lane's query row
+    const bool qvalid = q < a.sq;
+
+    // Q^T as MFMA B operands: 8 k-steps of 16 dims, 8 dims per lane each.
+    bf16x8_t qf[8];
+    {
+      const __amdgpu_buffer_rsrc_t rq = attn_rsrc(a.q, a.sq * Hq * kD * 2);  // rows past sq read zero
+      const uint32_t base = static_cast<uint32_t>(((q * Hq + h) * kD + half * 8) * 2);
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds)
+        qf[ds] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t,
+                     __builtin_amdgcn_raw_buffer_load_b128(rq, base + ds * 32, 0, 0)));
+    }
+    // running state for query q, in log2 units: m2 = max t, l = sum 2^(t - m2)
+    float m2, l;
+    f32x16_t o[4];
+    if (a.init) {
+      m2 = -INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] = f32x16_t{};
+    } else {
+      m2 = qvalid ? a.m_state[h * a.sq + q] * 1.4426950408889634f : -INFINITY;
+      l = qvalid ? a.l_state[h * a.sq + q] : 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int dv = b * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          o[b][i] = qvalid ? a.o[(q * Hq + h) * kD + dv] : 0.f;
+        }
+    }
+
+    // tile cursor over the chunks in arrival order
+    int p = 0;
+    int64_t t0 = a.chunk_begin[a.arrival[0]];
+    u32x4_t rk[2];
+    uint32_t rv[8];
+    auto wait_chunk = [&](int pos) {
+      if (tid == 0) {
+        const bool ok = wait_flag(a.flags, a.arrival[pos], epoch, a.hdr, a.timeout_ticks);
+        if (ok) acquire_agent();
+        s_ok = ok;
+      }
+      __syncthreads();
+      const int ok = s_ok;
+      __syncthreads();
+      return ok;
+    };
+    // global -> registers for the tile [t, t + kKT) of chunk at position pos
+    auto load_tile = [&](int pos, int64_t t) {
+      const int64_t kend = a.chunk_begin[a.arrival[pos] + 1];
+      const int64_t bytes = (kend - t - 1) * krow * 2 + kD * 2;  // through the chunk's last key
+      const __amdgpu_buffer_rsrc_t rk_ = attn_rsrc(a.k + (t * Hkv + g) * kD, bytes);
+      const __amdgpu_buffer_rsrc_t rv_ = attn_rsrc(a.v + (t * Hkv + g) * kD, bytes);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {  // K: 64 keys x 16 slots = 1024 granules
+        const int gi = tid + i * kAttnThreads, key = gi >> 4, sl = gi & 15;
+        rk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    rk_, static_cast<uint32_t>((key * krow + sl * 8) * 2), 0, 0));
+      }
+      // V: unit = (8 permuted keys of a 16-key step half, 2 dims)
+      const int dp = tid & 63, kg = tid >> 6;  // dims 2dp, 2dp+1; physical key group kg (8 keys)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = (kg >> 1) * 16 + perm16((kg & 1) * 8 + j);
+        rv[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_, static_cast<uint32_t>((key * krow + dp * 2) * 2), 0, 0);
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int gi = tid + i * kAttnThreads, key = gi >> 4, sl = gi & 15;
+        Ks[buf][key * 16 + kswz(key, sl)] = rk[i];
+      }
+      const int dp = tid & 63, kg = tid >> 6;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        u32x4_t w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = rv[2 * j], hi = rv[2 * j + 1];
+          w[j] = e ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        const int dv = dp * 2 + e;
+        Vt[buf][dv * 8 + vswz(dv, kg)] = w;
+      }
+    };
+    auto advance = [&](int& pos, int64_t& t) {  // next tile; pos == C when done
+      t += kKT;
+      if (t >= a.chunk_begin[a.arrival[pos] + 1]) {
+        ++pos;
+        if (pos < a.num_chunks) t = a.chunk_begin[a.arrival[pos]];
+      }
+    };
+
+    bool alive = wait_chunk(0);
+    if (alive) {
+      load_tile(0, t0);
+      store_tile(0);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (alive && p < a.num_chunks) {
+      const int64_t kend = a.chunk_begin[a.arrival[p] + 1];
+      const int valid = static_cast<int>(kend - t0 < kKT ? kend - t0 : kKT);
+      int np = p;
+      int64_t nt = t0;
+      advance(np, nt);
+      const bool more = np < a.num_chunks;
+      if (more) {
+        if (np != p && !wait_chunk(np)) {  // next chunk never arrived
+          alive = false;
+          break;
+        }
+        load_tile(np, nt);
+      }
+
+      // S^T = K Q^T: two 32-key blocks
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) {
+          const int key = kb * 32 + col;
+          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Ks[buf][key * 16 + kswz(key, ds * 2 + half)]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kb], 0, 0, 0);
+        }
+      // online softmax for this lane's query over the tile's keys
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const float t = key < valid ? s[kb][i] * c2 : -INFINITY;
+          s[kb][i] = t;
+          mloc = fmaxf(mloc, t);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float mnew = fmaxf(m2, mloc);
+      const float alpha = mnew == -INFINITY ? 1.f : exp2f(m2 - mnew);
+      float lsum = 0.f;
+      bf16x8_t pf[4];  // P^T as B operands: k-steps of 16 keys
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = exp2f(s[kb][i] - mnew);
+          lsum += pv;
+          pf[kb * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
+        }
+      lsum += __shfl_xor(lsum, 32, 64);
+      l = l * alpha + lsum;
+      m2 = mnew;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] *= alpha;
+      // O^T += V^T P^T: 4 blocks of 32 dims x 4 k-steps of 16 keys
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int dv = b * 32 + col;
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, Vt[buf][dv * 8 + vswz(dv, ks * 2 + half)]);
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[b], 0, 0, 0);
+        }
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      p = np;
+      t0 = nt;
+    }
+    if (!alive) continue;  // a block never arrived: this work item's outputs are left untouched
+
+    // write back the state (lanes 0..31 and 32..63 hold the same query)
+    if (qvalid) {
+      const float ln2 = 0.6931471805599453f;
+      if (a.finalize) {
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int dv = b * 32 + 8 * i4 + 4 * half;
+            float4 v4 = make_float4(o[b][4 * i4] * inv, o[b][4 * i4 + 1] * inv, o[b][4 * i4 + 2] * inv,
+                                    o[b][4 * i4 + 3] * inv);
+            *reinterpret_cast<float4*>(a.o + (q * Hq + h) * kD + dv) = v4;
+          }
+        if (half == 0) {
+          if (a.lse) a.lse[h * a.sq + q] = m2 * ln2 + logf(l);
+          a.m_state[h * a.sq + q] = m2 * ln2;
+          a.l_state[h * a.sq + q] = l;
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int dv = b * 32 + 8 * i4 + 4 * half;
+            float4 v4 = make_float4(o[b][4 * i4], o[b][4 * i4 + 1], o[b][4 * i4 + 2], o[b][4 * i4 + 3]);
+            *reinterpret_cast<float4*>(a.o + (q * Hq + h) * kD + dv) = v4;
+          }
+        if (half == 0) {
+          a.m_state[h * a.sq + q] = m2 * ln2;
+          a.l_state[h * a.sq + q] = l;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_ring_attn(const AttnArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(ring_attn_step, dim3(grid), dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace syncov

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -35,6 +36,8 @@ hipError_t launch_begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters,
                              int32_t num_chunks, const int32_t* resident, int32_t preset_all, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s);
+hipError_t launch_ring_attn(const AttnArgs& a, int grid, hipStream_t s);
+constexpr int64_t kAttnHeadDim = 128;
 
 }  // namespace syncov
 
@@ -388,6 +391,84 @@ GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const 
   return g;
 }
 
+// Runs one call's copy-in (CU or SDMA backend, or none) beside the compute
+// kernel launched by `compute(stream, cus)`, joining both back to `cs`.
+// Chunks are staged from src[x] to dst[x] (ntensors tensors of rb[x]-byte
+// rows) in arrival order; resident chunks are skipped.
+template <typename Compute>
+int copy_in_and_compute(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs,
+                        void* copy, const char* const src[2], char* const dst[2], const int64_t rb[2], int ntensors,
+                        Compute compute) {
+  int rc = SYNC_OK;
+  const bool copy_only = cx.cfg.flags & SYNC_RUN_COPY_ONLY;
+  const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
+  if (cx.cfg.backend == SYNC_COPY_CU) {
+    MaskedPair* mp = nullptr;
+    if ((rc = masked_pair(d, cx.cfg.copy_cus, &mp))) return rc;
+    HIP_TRY(hipEventRecord(d.ev_fork, cs));
+    if (!compute_only) {
+      CopyArgs ca{};
+      for (int x = 0; x < ntensors; ++x) {
+        ca.src[x] = src[x];
+        ca.dst[x] = dst[x];
+        ca.row_bytes[x] = rb[x];
+      }
+      ca.ntensors = ntensors;
+      ca.num_chunks = pl.num_chunks;
+      ca.chunk_begin = cx.tab->chunk_begin;
+      ca.arrival = cx.tab->arrival;
+      ca.resident = cx.tab->resident;
+      ca.out_flags = cx.ws.flags;
+      ca.parts = cx.ws.parts;
+      ca.xparts = cx.ws.xparts;
+      ca.hdr = cx.ws.hdr;
+      ca.timeout_ticks = cx.timeout_ticks;
+      ca.streaming = cx.cfg.copy_streaming;
+      HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
+      if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
+      HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * cx.cfg.copy_wg_per_cu, mp->copy));
+      if (tm) {
+        HIP_TRY(hipEventRecord(tm->c1, mp->copy));
+        tm->has_copy = true;
+      }
+      HIP_TRY(hipEventRecord(d.ev_copy, mp->copy));
+    }
+    if (!copy_only) {
+      HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
+      if ((rc = compute(mp->gemm, mp->gemm_cus))) return rc;
+      HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
+      HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
+    }
+    if (!compute_only) HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
+    return SYNC_OK;
+  }
+
+  if (compute_only) return compute(cs, d.num_cus);
+  // SDMA: the chunk data moves on the SDMA engine and a one-lane kernel raises
+  // each flag; the compute kernel runs on a CU-masked stream that leaves one CU
+  // per XCD to the copy stream for those flag kernels.
+  MaskedPair* mp = nullptr;
+  if ((rc = masked_pair(d, d.num_xcds, &mp))) return rc;
+  hipStream_t ss = copy ? static_cast<hipStream_t>(copy) : mp->copy;
+  HIP_TRY(hipEventRecord(d.ev_fork, cs));
+  HIP_TRY(hipStreamWaitEvent(ss, d.ev_fork, 0));
+  if (tm) HIP_TRY(hipEventRecord(tm->c0, ss));
+  if ((rc = enqueue_sdma_copy_in(pl, cx, src, dst, rb, ntensors, ss))) return rc;
+  if (tm) {
+    HIP_TRY(hipEventRecord(tm->c1, ss));
+    tm->has_copy = true;
+  }
+  HIP_TRY(hipEventRecord(d.ev_copy, ss));
+  if (!copy_only) {
+    HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
+    if ((rc = compute(mp->gemm, mp->gemm_cus))) return rc;
+    HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
+    HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
+  }
+  HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
+  return SYNC_OK;
+}
+
 }  // namespace
 
 // ---- C ABI ---------------------------------------------------------------------
@@ -515,71 +596,8 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
   const char* src[2] = {static_cast<const char*>(a_peer), nullptr};
   char* dst[2] = {static_cast<char*>(a_local), nullptr};
   const int64_t rb[2] = {pl.desc.k * 2, 0};
-
-  if (cx.cfg.backend == SYNC_COPY_CU) {
-    MaskedPair* mp = nullptr;
-    if ((rc = masked_pair(d, cx.cfg.copy_cus, &mp))) return rc;
-    HIP_TRY(hipEventRecord(d.ev_fork, cs));
-    if (!(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY)) {
-      CopyArgs ca{};
-      ca.src[0] = src[0];
-      ca.dst[0] = dst[0];
-      ca.row_bytes[0] = rb[0];
-      ca.ntensors = 1;
-      ca.num_chunks = pl.num_chunks;
-      ca.chunk_begin = cx.tab->chunk_begin;
-      ca.arrival = cx.tab->arrival;
-      ca.resident = cx.tab->resident;
-      ca.out_flags = cx.ws.flags;
-      ca.parts = cx.ws.parts;
-      ca.xparts = cx.ws.xparts;
-      ca.hdr = cx.ws.hdr;
-      ca.timeout_ticks = cx.timeout_ticks;
-      ca.streaming = cx.cfg.copy_streaming;
-      HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
-      if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
-      HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * cx.cfg.copy_wg_per_cu, mp->copy));
-      if (tm) {
-        HIP_TRY(hipEventRecord(tm->c1, mp->copy));
-        tm->has_copy = true;
-      }
-      HIP_TRY(hipEventRecord(d.ev_copy, mp->copy));
-    }
-    if (!copy_only) {
-      HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
-      if ((rc = gemm_on(mp->gemm, mp->gemm_cus * gemm_wg_per_cu(pl)))) return rc;
-      HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
-      HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
-    }
-    if (!(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY)) HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
-    return SYNC_OK;
-  }
-
-  if (compute_only) return gemm_on(cs, d.num_cus * gemm_wg_per_cu(pl));
-  // SDMA: the chunk data moves on the SDMA engine, but the HIP runtime runs
-  // each 4-byte flag copy as a small blit kernel, which needs a free CU while
-  // the persistent GEMM spins.  So the GEMM runs on a CU-masked stream that
-  // leaves one CU per XCD to the copy stream.
-  MaskedPair* mp = nullptr;
-  if ((rc = masked_pair(d, d.num_xcds, &mp))) return rc;
-  hipStream_t ss = copy ? static_cast<hipStream_t>(copy) : mp->copy;
-  HIP_TRY(hipEventRecord(d.ev_fork, cs));
-  HIP_TRY(hipStreamWaitEvent(ss, d.ev_fork, 0));
-  if (tm) HIP_TRY(hipEventRecord(tm->c0, ss));
-  if ((rc = enqueue_sdma_copy_in(pl, cx, src, dst, rb, 1, ss))) return rc;
-  if (tm) {
-    HIP_TRY(hipEventRecord(tm->c1, ss));
-    tm->has_copy = true;
-  }
-  HIP_TRY(hipEventRecord(d.ev_copy, ss));
-  if (!copy_only) {
-    HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
-    if ((rc = gemm_on(mp->gemm, mp->gemm_cus * gemm_wg_per_cu(pl)))) return rc;
-    HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
-    HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
-  }
-  HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
-  return SYNC_OK;
+  return copy_in_and_compute(pl, cx, d, tm, cs, copy, src, dst, rb, 1,
+                             [&](hipStream_t st, int cus) { return gemm_on(st, cus * gemm_wg_per_cu(pl)); });
 }
 
 int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c, int32_t c_dtype,
@@ -659,9 +677,69 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
 int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q, const void* k_peer,
                         const void* v_peer, void* k_local, void* v_local, float* o, float* m_state, float* l_state,
                         float* lse, float scale, int32_t flags, void* ws, void* compute, void* copy) {
-  (void)plan; (void)cfg; (void)q; (void)k_peer; (void)v_peer; (void)k_local; (void)v_local; (void)o;
-  (void)m_state; (void)l_state; (void)lse; (void)scale; (void)flags; (void)ws; (void)compute; (void)copy;
-  return fail(SYNC_EUNSUPPORTED, "ring-attention step not built yet");
+  CallCtx cx;
+  int rc = prepare(plan, cfg, ws, SYNC_OP_RING_ATTN, cx);
+  if (rc) return rc;
+  const Plan& pl = plan->plan;
+  const auto& dsc = pl.desc;
+  if (dsc.k != kAttnHeadDim) return fail(SYNC_EUNSUPPORTED, "head dim (k) must be 128");
+  const int group = dsc.heads_q / dsc.heads_kv;
+  if (!(group == 1 || group == 2 || group % 4 == 0))
+    return fail(SYNC_EUNSUPPORTED, "heads_q / heads_kv must be 1, 2 or a multiple of 4");
+  if (flags & ~(SYNC_ATTN_INIT | SYNC_ATTN_FINALIZE)) return fail(SYNC_EINVAL, "unknown attention flags");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SYNC_EINVAL, "scale must be positive and finite");
+  const bool need_peer = cx.cfg.backend != SYNC_COPY_PRESET && !(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
+  if (!q || !k_local || !v_local || !o || !m_state || !l_state || (need_peer && (!k_peer || !v_peer)))
+    return fail(SYNC_EINVAL, "NULL operand");
+  if (!aligned16(q) || !aligned16(k_local) || !aligned16(v_local) || !aligned16(o) ||
+      (k_peer && !aligned16(k_peer)) || (v_peer && !aligned16(v_peer)))
+    return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
+  if (dsc.m * dsc.heads_q * dsc.k * 2 >= (int64_t(1) << 31))
+    return fail(SYNC_EUNSUPPORTED, "query tensor too large for 32-bit buffer offsets");
+  DeviceState& d = *cx.dev;
+  std::lock_guard<std::mutex> lk(d.mu);
+  hipStream_t cs = static_cast<hipStream_t>(compute);
+  const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
+  DeviceState::Timed* tm = nullptr;
+  if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
+  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, cx.ws.xparts, pl.num_chunks,
+                            cx.tab->resident, compute_only ? 1 : 0, cs));
+  AttnArgs at{};
+  at.q = static_cast<const uint16_t*>(q);
+  at.k = static_cast<const uint16_t*>(k_local);
+  at.v = static_cast<const uint16_t*>(v_local);
+  at.o = o;
+  at.m_state = m_state;
+  at.l_state = l_state;
+  at.lse = lse;
+  at.sq = dsc.m;
+  at.heads_q = dsc.heads_q;
+  at.heads_kv = dsc.heads_kv;
+  at.heads_per_item = std::min(group, 4);
+  at.scale = scale;
+  at.init = (flags & SYNC_ATTN_INIT) ? 1 : 0;
+  at.finalize = (flags & SYNC_ATTN_FINALIZE) ? 1 : 0;
+  at.chunk_begin = cx.tab->chunk_begin;
+  at.arrival = cx.tab->arrival;
+  at.num_chunks = pl.num_chunks;
+  at.flags = cx.ws.flags;
+  at.hdr = cx.ws.hdr;
+  at.timeout_ticks = cx.timeout_ticks;
+  at.nxcd = d.num_xcds;
+  auto attn_on = [&](hipStream_t st, int cus) -> int {
+    if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
+    HIP_TRY(launch_ring_attn(at, cus, st));
+    if (tm) {
+      HIP_TRY(hipEventRecord(tm->k1, st));
+      tm->has_kernel = true;
+    }
+    return SYNC_OK;
+  };
+  const int64_t row = static_cast<int64_t>(dsc.heads_kv) * dsc.k * 2;  // bytes per token of K or V
+  const char* src[2] = {static_cast<const char*>(k_peer), static_cast<const char*>(v_peer)};
+  char* dst[2] = {static_cast<char*>(k_local), static_cast<char*>(v_local)};
+  const int64_t rb[2] = {row, row};
+  return copy_in_and_compute(pl, cx, d, tm, cs, copy, src, dst, rb, 2, attn_on);
 }
 
 int sync_get_device_info(sync_device_info* out) {

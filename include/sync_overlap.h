@@ -231,9 +231,15 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
  *   q bf16 [m][heads_q][k]; k_*, v_* bf16 [world*n][heads_kv][k];
  *   o fp32 [m][heads_q][k]; m_state, l_state fp32 [heads_q][m];
  *   lse fp32 [heads_q][m] or NULL (written when FINALIZE).
+ *   m_state is in natural-log units (max of scale * q.k); l_state is the sum
+ *   of exp(score - m); o holds the unnormalised sum unless FINALIZE.
  *   flags: SYNC_ATTN_INIT starts from m=-inf, l=0, O=0 (else reads the
- *   state); SYNC_ATTN_FINALIZE writes O/l to o and m + ln l to lse.
- * Kernel constraints: k (head dim) == 128, tile_m == 128. */
+ *   state); SYNC_ATTN_FINALIZE writes O/l to o and m + ln l to lse (and the
+ *   final m, l to the state).  Non-causal, no masking; scale > 0.
+ * Kernel constraints (else EUNSUPPORTED): k (head dim) == 128;
+ *   heads_q / heads_kv is 1, 2 or a multiple of 4.  The kernel groups the query
+ *   heads of one KV head into its work items, so tile_m / tile_order of the
+ *   plan do not change the result (every item needs every block). */
 enum { SYNC_ATTN_INIT = 1, SYNC_ATTN_FINALIZE = 2 };
 int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q,
                         const void* k_peer, const void* v_peer, void* k_local, void* v_local,
