@@ -74,5 +74,6 @@ def test_wrong_op_for_plan():
 def test_workspace_size_scales_with_chunks():
     p1 = A.sync_plan(A.make_desc(1, 64, 8, 64, 4, split=1, tile_m=2, tile_n=2))
     p2 = A.sync_plan(A.make_desc(1, 4096, 8, 64, 4, split=256, tile_m=2, tile_n=2))
-    assert A.sync_workspace_size(p1) == 256 + 4 * 256
-    assert A.sync_workspace_size(p2) == 256 + 4 * 4096
+    # header + four uint32[C] arrays + uint32[C][16], each padded to 256 bytes
+    assert A.sync_workspace_size(p1) == 256 + 4 * 256 + 256
+    assert A.sync_workspace_size(p2) == 256 + 4 * 4096 + 1024 * 64
