@@ -54,6 +54,89 @@ __device__ __forceinline__ u32x2_t buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32
 // distinct banks, and so do the 8 slots of one row.
 __device__ __forceinline__ int swz(int row, int slot) { return slot ^ ((row ^ (row >> 3)) & 7); }
 
+// Epilogue.  Accumulator element e of a 32x32 block sits at row
+// 8*(e/4) + 4*(lane/32) + e%4, column lane%32.  Each wave writes one 32-row
+// strip at a time into its own LDS region (row-major, padded pitch), then
+// reads it back 16 bytes per lane and stores whole rows with buffer stores
+// (rows past M fall outside num_records and are dropped).
+template <int TM, int TN, int CT>
+__device__ __forceinline__ void store_tile_c(const GemmArgs& a, const f32x16_t (&acc)[TM / 64][TN / 64], char* lds,
+                                             int64_t m0, int64_t n0, int rows_valid, int cols_valid, int wave,
+                                             int lane) {
+  constexpr int WM = TM / 2, WN = TN / 2, MI = WM / 32, NI = WN / 32;
+  constexpr int ES = CT == 0 ? 4 : 2;
+  constexpr int SP = WN + 32 / ES;   // staged strip pitch (elements), +32 B
+  constexpr int LPR = WN * ES / 16;  // lanes per staged row
+  constexpr int RPI = 64 / LPR;      // rows per store instruction
+  const int wm = wave >> 1, wn = wave & 1;
+  char* const stage = lds + wave * 32 * SP * ES;
+  const int rr = lane / LPR, rc = (lane % LPR) * (16 / ES);
+  const bool col_ok = wn * WN + rc < cols_valid;
+  const int64_t N = a.N;
+  const int row_bytes = static_cast<int>(N) * ES;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3), c = j * 32 + (lane & 31);
+        if constexpr (CT == 0)
+          *reinterpret_cast<float*>(stage + (r * SP + c) * ES) = acc[i][j][e];
+        else
+          *reinterpret_cast<uint16_t*>(stage + (r * SP + c) * ES) = f32_to_bf16_rne(acc[i][j][e]);
+      }
+    __syncthreads();
+    const int strip = wm * WM + i * 32;  // first tile row of this strip
+    const int rows_left = rows_valid - strip;
+    const __amdgpu_buffer_rsrc_t cs =
+        make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
+                  rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + rr;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (r * SP + rc) * ES);
+      if (col_ok)
+        __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
+    }
+    __syncthreads();
+  }
+}
+
+// GEMM-RS completion of tile t: every wave's C stores have reached the L2;
+// then one agent-scope release (a write-back of this XCD's L2, covering all
+// four waves) before the tile is counted toward each chunk it wrote; the last
+// tile of a chunk raises the chunk's done flag.
+__device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, uint32_t epoch, int tid) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0) {
+    release_agent();
+    for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) {
+      const int32_t c = a.dep_idx[e];
+      const uint32_t old = add_acq_rel_agent(a.counters + c, 1u);
+      if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) st_release_agent(a.flags + c, epoch);
+    }
+  }
+}
+
+// AG: lane 0 waits for every chunk tile t reads, then one acquire.  Returns
+// false (uniformly) when a wait gave up, so the tile is skipped.
+__device__ __forceinline__ bool wait_tile_chunks(const GemmArgs& a, int32_t t, uint32_t epoch, int tid,
+                                                 int32_t* s_skip) {
+  if (tid == 0) {
+    bool ok = true;
+    for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e)
+      ok = wait_flag(a.flags, a.dep_idx[e], epoch, a.hdr, a.timeout_ticks);
+    if (ok) acquire_agent();
+    *s_skip = ok ? 0 : 1;
+  }
+  __syncthreads();
+  const int skip = *s_skip;
+  __syncthreads();
+  return !skip;
+}
+
 template <int TM, int TN, int BL, int CT, bool RS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
   constexpr int WM = TM / 2, WN = TN / 2;
@@ -92,17 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     const int cols_valid = static_cast<int>((N - n0) < TN ? (N - n0) : TN);
 
     if constexpr (!RS) {
-      if (tid == 0) {
-        bool ok = true;
-        for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e)
-          ok = wait_flag(a.flags, a.dep_idx[e], epoch, a.hdr, a.timeout_ticks);
-        if (ok) acquire_agent();
-        s_skip = ok ? 0 : 1;
-      }
-      __syncthreads();
-      const int skip = s_skip;
-      __syncthreads();
-      if (skip) continue;  // a chunk never arrived: this tile of C is left untouched
+      if (!wait_tile_chunks(a, t, epoch, tid, &s_skip)) continue;  // a chunk never arrived: tile left untouched
     }
 
     const uint16_t* const a_tile = a.A + m0 * K;
@@ -223,67 +296,269 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
       __syncthreads();
     }
 
-    // Epilogue.  Accumulator element e of a 32x32 block sits at row
-    // 8*(e/4) + 4*(lane/32) + e%4, column lane%32.  Each wave writes one
-    // 32-row strip at a time into its own LDS region (row-major, padded
-    // pitch), then reads it back 16 bytes per lane and stores whole rows.
-    {
-      char* const stage = reinterpret_cast<char*>(smem) + wave * 32 * SP * ES;
-      constexpr int LPR = WN * ES / 16;  // lanes per staged row
-      constexpr int RPI = 64 / LPR;      // rows per store instruction
-      const int rr = lane / LPR, rc = (lane % LPR) * (16 / ES);
-      const bool col_ok = wn * WN + rc < cols_valid;
-      const int row_bytes = static_cast<int>(N) * ES;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3), c = j * 32 + (lane & 31);
-            if constexpr (CT == 0)
-              *reinterpret_cast<float*>(stage + (r * SP + c) * ES) = acc[i][j][e];
-            else
-              *reinterpret_cast<uint16_t*>(stage + (r * SP + c) * ES) = f32_to_bf16_rne(acc[i][j][e]);
-          }
-        __syncthreads();
-        const int strip = wm * WM + i * 32;  // first tile row of this strip
-        const int rows_left = rows_valid - strip;
-        const __amdgpu_buffer_rsrc_t cs =
-            make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
-                      rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
-#pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
-          const int r = it * RPI + rr;
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (r * SP + rc) * ES);
-          if (col_ok)
-            __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
-        }
-        __syncthreads();
-      }
-    }
+    store_tile_c<TM, TN, CT>(a, acc, reinterpret_cast<char*>(smem), m0, n0, rows_valid, cols_valid, wave, lane);
+    if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
+  }
+}
 
-    if constexpr (RS) {
-      // every wave's C stores have reached the L2; then one agent-scope release
-      // (a write-back of this XCD's L2, covering all four waves) before counting
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __syncthreads();
-      if (tid == 0) {
-        release_agent();
-        for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) {
-          const int32_t c = a.dep_idx[e];
-          const uint32_t old = add_acq_rel_agent(a.counters + c, 1u);
-          if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) st_release_agent(a.flags + c, epoch);
-        }
-      }
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for B stored [n][k] (both operands k-contiguous).
+//  * K advances TK at a time through an NS-stage LDS ring.  Loads go straight
+//    from HBM to LDS (buffer_load ... lds, 16 bytes per lane): no staging
+//    registers, no ds_write pass.  A wave's load fills 1 KB of LDS, lane l at
+//    byte 16*l; the 16-byte-slot swizzle is applied by choosing which global
+//    slot each lane fetches.
+//  * The prologue fills every slot; right after the barrier that publishes
+//    stage kt+1 (which also proves every wave is done with stage kt), the load
+//    of stage kt+NS goes into stage kt's slot, so a load has NS-1 stages of
+//    MFMA work to land in.
+//  * Two register sets of fragments (one k16 step each) alternate: the MFMAs
+//    of one step are interleaved with the LDS reads of the next step (for the
+//    last step of a stage, the first step of the next stage, read after that
+//    stage's barrier), so LDS latency hides behind the MFMA pipe.
+//  * Fragment reads are inline asm: the compiler's wait insertion cannot tell
+//    them apart from the in-flight LDS-DMA writes and would put vmcnt(0) in
+//    front of each; the kernel waits explicitly instead (lgkmcnt before use,
+//    vmcnt + raw barrier per stage).
+// ---------------------------------------------------------------------------
+
+// s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// s_waitcnt with lgkmcnt = n and the other counters unconstrained.
+template <int n>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(n >= 0 && n < 16, "lgkmcnt");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (n << 8) | (3 << 14));
+}
+
+// (The LDS-address-space casts and the asm are device-only: a host pass that
+// sees them drops the kernel's host stub, so they sit behind the device guard.)
+__device__ __forceinline__ bf16x8_t lds_read_b128(uint32_t addr) {
+  bf16x8_t r{};
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+#endif
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+#else
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+#endif
+}
+
+// 16 bytes per lane from buffer offset voff straight into LDS at lds + 16*lane
+// (lds wave-uniform).
+__device__ __forceinline__ void dma_load_16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16, voff, 0, 0, 0);
+#endif
+}
+
+// Slot swizzle for rows of SLOTS 16-byte slots.  A fragment read has lanes
+// 0..15 (and 16..31) on 16 consecutive rows at one logical slot; the XOR term
+// spreads them over distinct 16-byte bank groups whether the LDS serves 8 or
+// 16 lanes of a 128-bit read per cycle.  It uses row bits 0..3 only, so a
+// fragment's 32-aligned base row does not change it.
+template <int SLOTS>
+__device__ __forceinline__ int rswz(int row, int slot) {
+  if constexpr (SLOTS == 4)
+    return slot ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
+  else
+    return slot ^ ((row & 7) ^ ((row >> 3) & 1));
+}
+
+template <int TM, int TN, int CT, bool RS, int TK, int NS>
+__global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
+  constexpr int WM = TM / 2, WN = TN / 2;
+  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int ROWB = TK * 2;                      // bytes per LDS row
+  constexpr int SLOTS = ROWB / 16;
+  constexpr int RPL = 1024 / ROWB;                  // rows per 1 KB wave load
+  constexpr int KS = TK / 16;                       // k16 steps per stage
+  constexpr int A_BYTES = TM * ROWB, B_BYTES = TN * ROWB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_LD = A_BYTES / 1024 / 4;          // 1 KB wave loads per wave per stage
+  constexpr int B_LD = B_BYTES / 1024 / 4;
+  constexpr int LPW = A_LD + B_LD;                  // loads per wave per stage
+  constexpr int NFRAG = MI + NI;                    // 16-byte reads per k16 step: A frags, then B frags
+  static_assert(TM % 64 == 0 && TN % 64 == 0 && A_LD >= 1 && B_LD >= 1, "tile");
+  static_assert((SLOTS == 4 || SLOTS == 8) && KS % 2 == 0, "stage depth");
+  static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring");
+  static_assert(NFRAG <= MI * NI, "one read per MFMA slot");
+  constexpr int ES = CT == 0 ? 4 : 2;
+  static_assert(4 * 32 * (WN + 32 / ES) * ES <= NS * STAGE, "epilogue staging must fit the LDS ring");
+
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  __shared__ int32_t s_skip;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t epoch = a.hdr[WS_EPOCH];
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const int nk = static_cast<int>(K / TK);
+
+  // per-lane global offsets (bytes, relative to the tile's first row at k0)
+  uint32_t a_off[A_LD], b_off[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int row = (wave * A_LD + i) * RPL + lane / SLOTS;
+    a_off[i] = static_cast<uint32_t>((row * K + rswz<SLOTS>(row, lane % SLOTS) * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int row = (wave * B_LD + i) * RPL + lane / SLOTS;
+    b_off[i] = static_cast<uint32_t>((row * K + rswz<SLOTS>(row, lane % SLOTS) * 8) * 2);
+  }
+  // per-lane LDS offset of a fragment read for k16 step kk (rows are 32-aligned,
+  // so the swizzle depends only on the lane's row within the block)
+  const int frow = lane & 31;
+  int frag_off[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) frag_off[kk] = frow * ROWB + rswz<SLOTS>(frow, kk * 2 + (lane >> 5)) * 16;
+
+  const int32_t slot0 = xcd_slot(blockIdx.x, gridDim.x, a.nxcd);
+  for (int32_t p = slot0; p < a.num_tiles; p += gridDim.x) {
+    const int32_t t = a.order[p];
+    const int32_t ti = t / a.tiles_n, tj = t - ti * a.tiles_n;
+    const int64_t m0 = static_cast<int64_t>(ti) * TM, n0 = static_cast<int64_t>(tj) * TN;
+    const int rows_valid = static_cast<int>((M - m0) < TM ? (M - m0) : TM);
+    const int cols_valid = static_cast<int>((N - n0) < TN ? (N - n0) : TN);
+    if constexpr (!RS) {
+      if (!wait_tile_chunks(a, t, epoch, tid, &s_skip)) continue;  // a chunk never arrived: tile left untouched
     }
+    const uint16_t* const a_tile = a.A + m0 * K;
+    const uint16_t* const b_tile = a.B + n0 * K;
+
+    auto issue = [&](int kt) {  // loads of k-step kt into slot kt % NS
+      char* st = smem + (kt % NS) * STAGE;
+      const int64_t k0 = static_cast<int64_t>(kt) * TK;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + k0, static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + k0, static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2);
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) dma_load_16(ra, st + (wave * A_LD + i) * 1024, a_off[i]);
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) dma_load_16(rb, st + A_BYTES + (wave * B_LD + i) * 1024, b_off[i]);
+    };
+    // stage kt is in LDS for every wave; the loads of later stages (at most
+    // NS - 2 of them) may still be in flight
+    auto landed = [&](int kt) {
+      const int later = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
+      if constexpr (NS >= 4) {
+        if (later >= 2) {
+          wait_vmcnt<2 * LPW>();
+        } else if (later == 1) {
+          wait_vmcnt<LPW>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      } else if constexpr (NS == 3) {
+        if (later >= 1)
+          wait_vmcnt<LPW>();
+        else
+          wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    f32x16_t acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = f32x16_t{};
+
+    __syncthreads();  // the previous tile's epilogue is done with the LDS
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (s < nk) issue(s);
+
+    const uint32_t ring = lds_addr(smem);
+    auto read_frag = [&](uint32_t st, int kk, int f) -> bf16x8_t {
+      const uint32_t off = st + frag_off[kk];
+      return f < MI ? lds_read_b128(off + (wm * WM + f * 32) * ROWB)
+                    : lds_read_b128(off + A_BYTES + (wn * WN + (f - MI) * 32) * ROWB);
+    };
+    // MFMAs on one fragment set, interleaved with the reads of the next set.
+    // The reads are unconditional: a read whose result the compiler might
+    // discard would let it emit select/copy code on registers that an
+    // in-flight asm read is still going to write.
+    auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk) {
+#pragma unroll
+      for (int x = 0; x < MI * NI; ++x) {
+        const int i = x / NI, j = x % NI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], cur[MI + j], acc[i][j], 0, 0, 0);
+        if (x < NFRAG) nxt[x] = read_frag(nst, nkk, x);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_lgkmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    bf16x8_t fp[NFRAG], fq[NFRAG];
+    landed(0);
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) fp[f] = read_frag(ring, 0, f);
+    wait_lgkmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint32_t st = ring + (kt % NS) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KS - 1; kk += 2) {
+        mma(fp, fq, st, kk + 1);
+        if (kk + 2 < KS) mma(fq, fp, st, kk + 2);
+      }
+      // last k16 step of the stage: its MFMAs read fq; the next stage's first
+      // step is read into fp once that stage has landed (after the last
+      // stage, a read of an idle slot whose result goes unused)
+      if (kt + 1 < nk) {
+        landed(kt + 1);
+        if (kt + NS < nk) issue(kt + NS);  // into stage kt's slot, free now
+      }
+      mma(fq, fp, ring + ((kt + 1) % NS) * STAGE, 0);
+    }
+    __syncthreads();  // every wave is done reading the ring before the epilogue reuses it
+    store_tile_c<TM, TN, CT>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane);
+    if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
   }
 }
 
 // Host-side launcher: picks the template instance; hipErrorInvalidValue for a
 // variant that does not exist.
+// K per stage and ring depth of the direct-to-LDS GEMM, per tile: 64-deep
+// stages read whole 128-byte lines per row; the ring takes what the LDS
+// holds at the tile's workgroups per CU (128x128 runs two per CU).
+template <int TM, int TN> struct DmaShape { static constexpr int TK = 64, NS = 2; };
+template <> struct DmaShape<256, 128> { static constexpr int TK = 64, NS = 3; };
+
 hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid,
                        hipStream_t stream) {
+#define SYNC_GEMM_DMA_CASE(TM_, TN_, CT_)                                                                \
+  if (tm == TM_ && tn == TN_ && b_layout == 1 && c_dtype == CT_) {                                       \
+    constexpr int TK_ = DmaShape<TM_, TN_>::TK, NS_ = DmaShape<TM_, TN_>::NS;                            \
+    if (rs)                                                                                              \
+      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, true, TK_, NS_>), dim3(grid), dim3(kThreads), 0, stream, a); \
+    else                                                                                                 \
+      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, false, TK_, NS_>), dim3(grid), dim3(kThreads), 0, stream, a); \
+    return hipGetLastError();                                                                            \
+  }
+  SYNC_GEMM_DMA_CASE(256, 256, 0)
+  SYNC_GEMM_DMA_CASE(256, 256, 1)
+  SYNC_GEMM_DMA_CASE(256, 128, 0)
+  SYNC_GEMM_DMA_CASE(256, 128, 1)
+  SYNC_GEMM_DMA_CASE(128, 128, 0)
+  SYNC_GEMM_DMA_CASE(128, 128, 1)
+#undef SYNC_GEMM_DMA_CASE
 #define SYNC_GEMM_CASE(TM_, TN_, BL_, CT_)                                                               \
   if (tm == TM_ && tn == TN_ && b_layout == BL_ && c_dtype == CT_) {                                     \
     if (rs)                                                                                              \

@@ -167,24 +167,28 @@ SDMA_LIMIT = ("the HIP runtime does not start the next SDMA copy while the persi
               "later chunks land only after the GEMM exits), so full-size SDMA overlap times out")
 
 
-def test_full_size_exact_small_integers():
-    a, b = inputs.gemm_operands(M2, N2, K2, 1.0, integer=True)
-    out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), split=2, backend=A.SYNC_COPY_CU, copy_cus=32)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_full_size_exact_small_integers(layout):
+    a, b = inputs.gemm_operands(M2, N2, K2, 1.0, integer=True, b_layout=layout)
+    out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), split=2, backend=A.SYNC_COPY_CU, copy_cus=32,
+                    layout=layout)
     assert np.all(out == np.round(out))  # every element an exact integer
     rows, cols = _samples(M2, N2, 4000)
-    exact = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols)
+    exact = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout=layout)
     assert np.array_equal(out[rows, cols].astype(np.float64), exact)
 
 
 @pytest.mark.parametrize("backend,cus,split", [
     pytest.param(A.SYNC_COPY_SDMA, 0, 1, marks=pytest.mark.skip(reason=SDMA_LIMIT)), (A.SYNC_COPY_CU, 32, 4),
                                               (A.SYNC_COPY_CU, 16, 2), (A.SYNC_COPY_PRESET, 0, 1)])
-def test_full_size_normal(backend, cus, split):
-    a, b = inputs.gemm_operands(M2, N2, K2, 64.0)
-    out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), split=split, backend=backend, copy_cus=cus)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_full_size_normal(backend, cus, split, layout):
+    a, b = inputs.gemm_operands(M2, N2, K2, 64.0, b_layout=layout)
+    out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), split=split, backend=backend, copy_cus=cus,
+                    layout=layout)
     assert np.isfinite(out).all()
     rows, cols = _samples(M2, N2, 20000, seed=1)
-    ref = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols)
+    ref = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout=layout)
     shard = rows // (M2 // W2)
     for s in range(W2):
         sel = shard == s

@@ -71,11 +71,12 @@ def check_staging(cn, st, tabs):
 
 
 @pytest.mark.parametrize("order", [A.SYNC_ORDER_ROW_MAJOR, A.SYNC_ORDER_CHUNK_MAJOR, A.SYNC_ORDER_SWIZZLED])
-def test_tiny_rs(order):
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_tiny_rs(order, layout):
     m, n, k, W = 1024, 512, 256, 4
-    a, b = inputs.gemm_operands(m, n, k, 16.0)
-    ref = oracle.gemm_f64(a, b, m, n, k)
-    cn, st, tabs = run_rs(m, n, k, W, a, b, order=order)
+    a, b = inputs.gemm_operands(m, n, k, 16.0, b_layout=layout)
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout=layout)
+    cn, st, tabs = run_rs(m, n, k, W, a, b, order=order, layout=A.SYNC_B_NK if layout == "nk" else A.SYNC_B_KN)
     assert shard_frobenius(cn.astype(np.float64), ref, W) <= 1e-3
     check_staging(cn, st, tabs)
     assert list(tabs["arrival"]) == [3, 2, 1, 0]  # ring send order of rank 0, own chunk last
@@ -117,12 +118,14 @@ def test_full_size_rs_exact_integers():
     check_staging(cn, st, tabs)
 
 
-def test_full_size_rs_normal():
-    a, b = inputs.gemm_operands(M3, N3, K3, 64.0)
-    cn, st, tabs = run_rs(M3, N3, K3, W3, a, b, tile=(256, 256), copy_cus=32)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_full_size_rs_normal(layout):
+    a, b = inputs.gemm_operands(M3, N3, K3, 64.0, b_layout=layout)
+    cn, st, tabs = run_rs(M3, N3, K3, W3, a, b, tile=(256, 256), copy_cus=32,
+                          layout=A.SYNC_B_NK if layout == "nk" else A.SYNC_B_KN)
     rng = np.random.default_rng(4)
     rows, cols = rng.integers(0, M3, 20000), rng.integers(0, N3, 20000)
-    ref = oracle.gemm_f64_sampled(a, b, M3, N3, K3, rows, cols)
+    ref = oracle.gemm_f64_sampled(a, b, M3, N3, K3, rows, cols, b_layout=layout)
     for s in range(W3):
         sel = rows // (M3 // W3) == s
         assert np.linalg.norm(cn[rows[sel], cols[sel]] - ref[sel]) / np.linalg.norm(ref[sel]) <= 1e-3
