@@ -26,7 +26,7 @@ SYNC_ORDER_ROW_MAJOR, SYNC_ORDER_CHUNK_MAJOR, SYNC_ORDER_SWIZZLED = 0, 1, 2
 SYNC_B_KN, SYNC_B_NK = 0, 1
 SYNC_DTYPE_F32, SYNC_DTYPE_BF16 = 0, 1
 SYNC_COPY_PRESET, SYNC_COPY_SDMA, SYNC_COPY_CU, SYNC_COPY_HOST_GATED = 0, 1, 2, 3
-SYNC_RUN_COPY_ONLY, SYNC_RUN_COMPUTE_ONLY, SYNC_RUN_TIMED = 1, 2, 4
+SYNC_RUN_COPY_ONLY, SYNC_RUN_COMPUTE_ONLY, SYNC_RUN_TIMED, SYNC_RUN_WITHHOLD = 1, 2, 4, 8
 SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 
 EXPORTED_SYMBOLS = (
@@ -73,8 +73,8 @@ class sync_plan_tables(ctypes.Structure):
 
 class sync_copy_cfg(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("copy_cus", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
-                ("host_gates", ctypes.c_void_p), ("flags", ctypes.c_int32), ("copy_wg_per_cu", ctypes.c_int32),
-                ("copy_streaming", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("host_gates", ctypes.c_void_p), ("flags", ctypes.c_int32), ("copy_streaming", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class sync_timing(ctypes.Structure):
@@ -209,10 +209,10 @@ def sync_plan_export(plan: Plan) -> dict:
 
 
 def make_cfg(backend: int = SYNC_COPY_SDMA, copy_cus: int = 0, timeout_ns: int = 0, host_gates=None,
-             flags: int = 0, copy_wg_per_cu: int = 0, copy_streaming: int = 0) -> sync_copy_cfg:
+             flags: int = 0, copy_streaming: int = 0) -> sync_copy_cfg:
     c = sync_copy_cfg()
     c.backend, c.copy_cus, c.timeout_ns, c.flags = backend, copy_cus, timeout_ns, flags
-    c.copy_wg_per_cu, c.copy_streaming = copy_wg_per_cu, copy_streaming
+    c.copy_streaming = copy_streaming
     c.host_gates = _ptr(host_gates)
     return c
 

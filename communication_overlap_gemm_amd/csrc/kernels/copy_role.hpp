@@ -1,0 +1,144 @@
+// Copy role: the workgroups of a call's launch that move chunks instead of
+// computing.
+//
+// The Syncopate summary page ("Core method", paper sec. 5.2, Fig. 7) lowers a
+// chunk plan to load/store on dedicated SMs among other backends, signalling
+// through global-memory flags; the review page's Fig. 5 caption shows that
+// communication on specialised SMs beside the compute.  The Entwine abstract
+// pairs a tile-reordered GEMM with SM-based fine-grained communication and
+// sizes the SM share against compute slowdown.
+//
+// Here the copy agent is not a kernel of its own: the first `count`
+// workgroups of the compute kernel's grid take this role, so a call is one
+// launch on one stream.  The dispatcher places workgroup b on XCD b % 8 and
+// issues workgroups in order, so with a multiple of 8 of them they are
+// spread evenly over the XCDs and resident before any compute workgroup.
+//   copy-in  (AG, attention): for each chunk in arrival order, every
+//            workgroup copies its slice of the chunk's rows from the peer
+//            region to the local buffer; the chunk's flag is raised once all
+//            slices are visible device-wide.
+//   copy-out (RS): for each chunk in send order, every workgroup waits for
+//            done[c] (raised by the GEMM role), copies its slice of the
+//            chunk's rows of C into the staging slot, and sent[c] is raised
+//            the same way.
+// All workgroups walk the same order, so chunks complete one after another at
+// the role's full bandwidth.
+#pragma once
+
+#include "device_common.hpp"
+#include "launch_args.hpp"
+
+namespace syncov {
+
+typedef uint32_t copy_u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kCopyUnroll = 8;  // 16-byte loads in flight per thread
+
+// Copies bytes [lo, hi) of src to dst (16-byte granules; both 16-byte
+// aligned), kCopyUnroll loads in flight per thread.  STREAM selects
+// non-temporal accesses.
+template <int THREADS, bool STREAM>
+__device__ __forceinline__ void copy_range(const char* __restrict__ src, char* __restrict__ dst, int64_t lo,
+                                           int64_t hi) {
+  const copy_u32x4_t* s = reinterpret_cast<const copy_u32x4_t*>(src);
+  copy_u32x4_t* d = reinterpret_cast<copy_u32x4_t*>(dst);
+  int64_t g = lo / 16 + threadIdx.x;
+  const int64_t gend = hi / 16;
+  constexpr int64_t step = THREADS;
+  auto ld = [](const copy_u32x4_t* p) { return STREAM ? __builtin_nontemporal_load(p) : *p; };
+  auto st = [](copy_u32x4_t v, copy_u32x4_t* p) {
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(v, p);
+    else
+      *p = v;
+  };
+  for (; g + (kCopyUnroll - 1) * step < gend; g += kCopyUnroll * step) {
+    copy_u32x4_t v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = ld(s + g + u * step);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) st(v[u], d + g + u * step);
+  }
+  for (; g < gend; g += step) st(ld(s + g), d + g);
+}
+
+// Publication.  A chunk is complete when every copy workgroup's stores of it
+// are visible device-wide.  Each workgroup first drains its stores into its
+// XCD's L2 (workgroup-scope release = wait for the stores), then counts
+// itself in a per-(chunk, XCD) counter; the last workgroup of each XCD writes
+// that L2 back with one agent-scope release (which covers the other
+// workgroups' lines in the same L2) and adds the XCD's workgroups to the
+// chunk's total; whoever completes the total raises the flag.  One L2
+// writeback per XCD per chunk instead of one per workgroup.  A census at the
+// start tells each workgroup how many copy workgroups share its XCD.
+// `rank` in [0, count) is this workgroup's index among the copy workgroups.
+template <int THREADS>
+__device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32_t epoch) {
+  __shared__ int32_t s_ok;
+  __shared__ uint32_t s_mine;
+  const int64_t G = count, b = rank;
+  const int xcc = xcc_id();
+  if (threadIdx.x == 0) {
+    add_acq_rel_agent(a.hdr + WS_CENSUS + xcc, 1u);
+    add_acq_rel_agent(a.hdr + WS_CENSUS_TOTAL, 1u);
+    // the copy workgroups are the first of the grid, all resident at once, so
+    // the census completes; the wait is still bounded
+    const uint64_t t0 = wall_clock64();
+    bool ok = true;
+    while (ld_relaxed_agent(a.hdr + WS_CENSUS_TOTAL) < static_cast<uint32_t>(G)) {
+      __builtin_amdgcn_s_sleep(1);
+      if (wall_clock64() - t0 > a.timeout_ticks) {
+        record_timeout(a.hdr, -1);
+        ok = false;
+        break;
+      }
+    }
+    s_mine = ok ? ld_relaxed_agent(a.hdr + WS_CENSUS + xcc) : 0u;
+  }
+  __syncthreads();
+  const uint32_t mine = s_mine;
+  if (mine == 0) return;
+  for (int32_t p = 0; p < a.num_chunks; ++p) {
+    const int32_t c = a.arrival[p];
+    if (!a.copy_out && a.resident[c]) continue;
+    if (a.copy_out) {
+      if (threadIdx.x == 0) {
+        const bool ok = wait_flag(a.wait_flags, c, epoch, a.hdr, a.timeout_ticks);
+        if (ok) acquire_agent();
+        s_ok = ok;
+      }
+      __syncthreads();
+      const int ok = s_ok;
+      __syncthreads();
+      if (!ok) continue;  // chunk never completed: nothing to send
+    }
+    const int64_t r0 = a.chunk_begin[c], r1 = a.chunk_begin[c + 1];
+    const int64_t drow = a.copy_out ? a.slot_row[p] : r0;
+    for (int x = 0; x < a.ntensors; ++x) {
+      const int64_t bytes = (r1 - r0) * a.row_bytes[x];
+      const int64_t granules = bytes / 16;
+      const int64_t lo = granules * b / G * 16, hi = granules * (b + 1) / G * 16;
+      if (a.streaming)
+        copy_range<THREADS, true>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
+      else
+        copy_range<THREADS, false>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores have reached the L2
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t* const xp = a.xparts + c * kMaxXcd + xcc;
+      const uint32_t old = add_acq_rel_agent(xp, 1u);
+      if (old + 1u == mine) {
+        st_relaxed_agent(xp, 0u);  // every workgroup of this XCD has counted: ready for the next call
+        release_agent();  // write this XCD's L2 back: every workgroup of this XCD has stored
+        const uint32_t done = add_acq_rel_agent(a.parts + c, mine);
+        if (done + mine == static_cast<uint32_t>(G)) {
+          st_relaxed_agent(a.parts + c, 0u);
+          st_release_agent(a.out_flags + c, epoch);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace syncov

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch_args.hpp"
+
 namespace syncov {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -27,12 +29,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // Workspace header words (uint32 index).  The flag and counter arrays follow
 // at offsets the host computes from the plan's chunk count.
 enum : int {
-  WS_EPOCH = 0,      // epoch of the current call (bumped by the begin kernel)
-  WS_ERR_CODE = 1,   // 0 = fine, else ERR_* below
-  WS_ERR_CHUNK = 2,  // chunk whose wait expired first
-  WS_TICKET = 3,     // reserved for dynamic tile tickets
-  WS_CENSUS_TOTAL = 4,  // copy agent: workgroups that have started
-  WS_CENSUS = 16,       // copy agent: workgroups started per XCD (16 slots)
+  WS_EPOCH = 0,         // epoch of the last completed call
+  WS_ERR_CODE = 1,      // 0 = fine, else ERR_* below (sticky until re-initialisation)
+  WS_ERR_CHUNK = 2,     // chunk whose wait expired first
+  WS_EXIT = 3,          // workgroups of the running call that have finished
+  WS_CENSUS_TOTAL = 4,  // copy role: workgroups that have started
+  WS_CENSUS = 16,       // copy role: workgroups started per XCD (16 slots)
   WS_HEADER_WORDS = 64
 };
 constexpr int kMaxXcd = 16;
@@ -43,6 +45,10 @@ enum : uint32_t { ERR_TIMEOUT = 1u };
 
 __device__ __forceinline__ uint32_t ld_relaxed_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_relaxed_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void st_release_agent(uint32_t* p, uint32_t v) {
@@ -95,6 +101,41 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// ---- one launch per call --------------------------------------------------
+// Every call is one kernel launch on the caller's stream.  Its epoch is one
+// past the epoch of the last completed call on this workspace; the last
+// workgroup of the grid to finish stores it, after every workgroup has read
+// the old value (each reads it before it counts itself out).  Flags are
+// compared against the epoch, so they are never cleared; per-chunk counters
+// are cleared by the workgroup that completes them.  A recorded error is
+// sticky: waits give up at once until the workspace is initialised again, and
+// the last workgroup clears the counters that a failed call left behind.
+__device__ __forceinline__ uint32_t call_epoch(const uint32_t* hdr) {
+  const uint32_t e = __hip_atomic_load(hdr + WS_EPOCH, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  return e == 0u ? 1u : e;
+}
+
+// Last action of every workgroup (all threads).
+__device__ __forceinline__ void end_call(uint32_t* hdr, uint32_t epoch, const CounterArrays& ca) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = add_acq_rel_agent(hdr + WS_EXIT, 1u);
+    if (old + 1u == gridDim.x) {
+      st_relaxed_agent(hdr + WS_CENSUS_TOTAL, 0u);
+      for (int x = 0; x < kMaxXcd; ++x) st_relaxed_agent(hdr + WS_CENSUS + x, 0u);
+      if (ld_relaxed_agent(hdr + WS_ERR_CODE) != 0u) {
+        for (int32_t c = 0; c < ca.num_chunks; ++c) {
+          st_relaxed_agent(ca.counters + c, 0u);
+          st_relaxed_agent(ca.parts + c, 0u);
+          for (int x = 0; x < kMaxXcd; ++x) st_relaxed_agent(ca.xparts + c * kMaxXcd + x, 0u);
+        }
+      }
+      st_relaxed_agent(hdr + WS_EXIT, 0u);
+      st_release_agent(hdr + WS_EPOCH, epoch);
+    }
+  }
 }
 
 // Persistent-kernel slot of workgroup `b` out of `g`: workgroups are handed to

@@ -23,6 +23,7 @@
 //    writes C with 16-byte buffer stores, rows past M dropped by the hardware.
 //  * One workgroup per CU walks the plan's tile order with a static stride;
 //    slots are remapped so that each XCD takes consecutive tiles of the order.
+#include "copy_role.hpp"
 #include "device_common.hpp"
 #include "launch_args.hpp"
 
@@ -114,21 +115,30 @@ __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, ui
     release_agent();
     for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) {
       const int32_t c = a.dep_idx[e];
-      const uint32_t old = add_acq_rel_agent(a.counters + c, 1u);
-      if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) st_release_agent(a.flags + c, epoch);
+      const uint32_t old = add_acq_rel_agent(a.cnt.counters + c, 1u);
+      if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) {
+        st_relaxed_agent(a.cnt.counters + c, 0u);  // every tile of c has counted: ready for the next call
+        st_release_agent(a.flags + c, epoch);
+      }
     }
   }
 }
 
-// AG: lane 0 waits for every chunk tile t reads, then one acquire.  Returns
-// false (uniformly) when a wait gave up, so the tile is skipped.
+// AG: lane 0 waits for every chunk tile t reads that was not in place before
+// the call, then one acquire.  Returns false (uniformly) when a wait gave up,
+// so the tile is skipped.
 __device__ __forceinline__ bool wait_tile_chunks(const GemmArgs& a, int32_t t, uint32_t epoch, int tid,
                                                  int32_t* s_skip) {
+  if (!a.wait_chunks) return true;
   if (tid == 0) {
-    bool ok = true;
-    for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e)
-      ok = wait_flag(a.flags, a.dep_idx[e], epoch, a.hdr, a.timeout_ticks);
-    if (ok) acquire_agent();
+    bool ok = true, waited = false;
+    for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e) {
+      const int32_t c = a.dep_idx[e];
+      if (a.resident[c]) continue;
+      ok = wait_flag(a.flags, c, epoch, a.hdr, a.timeout_ticks);
+      waited = true;
+    }
+    if (ok && waited) acquire_agent();
     *s_skip = ok ? 0 : 1;
   }
   __syncthreads();
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t epoch = a.hdr[WS_EPOCH];
+  const uint32_t epoch = call_epoch(a.hdr);
   const int64_t M = a.M, N = a.N, K = a.K;
   const int nk = static_cast<int>(K / kTK);
 
@@ -166,8 +176,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
   u32x4_t rbn[BL == 1 ? B_LD_NK : 1];
   u32x2_t rbk[BL == 0 ? B_UNITS : 1][8];
 
-  const int32_t slot0 = xcd_slot(blockIdx.x, gridDim.x, a.nxcd);
-  for (int32_t p = slot0; p < a.num_tiles; p += gridDim.x) {
+  if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
+    copy_role<kThreads>(a.copy, blockIdx.x, a.copy_blocks, epoch);
+    end_call(a.hdr, epoch, a.cnt);
+    return;
+  }
+  const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
+  const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
+  for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];
     const int32_t ti = t / a.tiles_n, tj = t - ti * a.tiles_n;
     const int64_t m0 = static_cast<int64_t>(ti) * TM, n0 = static_cast<int64_t>(tj) * TN;
@@ -299,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     store_tile_c<TM, TN, CT>(a, acc, reinterpret_cast<char*>(smem), m0, n0, rows_valid, cols_valid, wave, lane);
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
   }
+  end_call(a.hdr, epoch, a.cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -402,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t epoch = a.hdr[WS_EPOCH];
+  const uint32_t epoch = call_epoch(a.hdr);
   const int64_t M = a.M, N = a.N, K = a.K;
   const int nk = static_cast<int>(K / TK);
 
@@ -425,8 +442,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) frag_off[kk] = frow * ROWB + rswz<SLOTS>(frow, kk * 2 + (lane >> 5)) * 16;
 
-  const int32_t slot0 = xcd_slot(blockIdx.x, gridDim.x, a.nxcd);
-  for (int32_t p = slot0; p < a.num_tiles; p += gridDim.x) {
+  if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
+    copy_role<kThreads>(a.copy, blockIdx.x, a.copy_blocks, epoch);
+    end_call(a.hdr, epoch, a.cnt);
+    return;
+  }
+  const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
+  const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
+  for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];
     const int32_t ti = t / a.tiles_n, tj = t - ti * a.tiles_n;
     const int64_t m0 = static_cast<int64_t>(ti) * TM, n0 = static_cast<int64_t>(tj) * TN;
@@ -531,6 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
     store_tile_c<TM, TN, CT>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane);
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
   }
+  end_call(a.hdr, epoch, a.cnt);
 }
 
 // Host-side launcher: picks the template instance; hipErrorInvalidValue for a

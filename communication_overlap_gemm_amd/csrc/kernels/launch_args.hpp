@@ -5,25 +5,16 @@
 
 namespace syncov {
 
-// Persistent GEMM (gemm_persistent.hip).
-struct GemmArgs {
-  const uint16_t* A;  // bf16 [M][K]
-  const uint16_t* B;  // bf16 [K][N] (KN) or [N][K] (NK)
-  void* C;            // [M][N] fp32 or bf16
-  int64_t M, N, K;
-  const int32_t* order;  // tile traversal, num_tiles entries
-  int32_t num_tiles, tiles_n;
-  const int64_t* dep_ptr;  // tile -> chunks CSR
-  const int32_t* dep_idx;
-  const int32_t* tiles_in;  // RS: tiles per chunk
-  uint32_t* flags;          // AG: ready flags; RS: done flags
-  uint32_t* counters;       // RS: stored-tile counters (zeroed by the begin kernel)
-  uint32_t* hdr;            // workspace header
-  uint64_t timeout_ticks;   // wall-clock ticks allowed per wait
-  int32_t nxcd;             // XCDs (for the workgroup -> slot remap)
+// Per-chunk counter arrays of the workspace (cleared by the workgroup that
+// completes them; after a failed call, by the call's last workgroup).
+struct CounterArrays {
+  uint32_t* counters;  // GEMM-RS: tiles stored per chunk
+  uint32_t* parts;     // copy role: XCDs finished per chunk
+  uint32_t* xparts;    // copy role: workgroups finished per (chunk, XCD), C x 16
+  int32_t num_chunks;
 };
 
-// Copy agent (copy_agent.hip).
+// Copy role (copy_role.hpp): chunk copy-in or copy-out.
 struct CopyArgs {
   const char* src[2];  // up to two tensors per chunk (attention: K and V)
   char* dst[2];
@@ -36,7 +27,7 @@ struct CopyArgs {
   const int64_t* slot_row;     // copy-out: first staging row of each position (C+1)
   uint32_t* out_flags;         // raised per chunk when its copy is complete
   const uint32_t* wait_flags;  // copy-out: done flags to wait for
-  uint32_t* parts;             // per-chunk count of finished workgroups
+  uint32_t* parts;             // per-chunk count of finished XCD groups
   uint32_t* xparts;            // per (chunk, XCD) count of finished workgroups, C x 16
   uint32_t* hdr;
   uint64_t timeout_ticks;
@@ -44,10 +35,33 @@ struct CopyArgs {
   int32_t streaming;  // non-temporal loads and stores
 };
 
-// Ring-attention step (ring_attn.hip).
+// Persistent GEMM (gemm_persistent.hip).  Workgroups [0, copy_blocks) of the
+// grid run the copy role with `copy`; the others compute tiles.
+struct GemmArgs {
+  const uint16_t* A;  // bf16 [M][K]
+  const uint16_t* B;  // bf16 [K][N] (KN) or [N][K] (NK)
+  void* C;            // [M][N] fp32 or bf16
+  int64_t M, N, K;
+  const int32_t* order;  // tile traversal, num_tiles entries
+  int32_t num_tiles, tiles_n;
+  const int64_t* dep_ptr;  // tile -> chunks CSR
+  const int32_t* dep_idx;
+  const int32_t* tiles_in;  // RS: tiles per chunk
+  const int32_t* resident;  // AG: chunks in place before the call (never waited for)
+  uint32_t* flags;          // AG: ready flags; RS: done flags
+  uint32_t* hdr;            // workspace header
+  CounterArrays cnt;
+  uint64_t timeout_ticks;   // wall-clock ticks allowed per wait
+  int32_t nxcd;             // XCDs (for the workgroup -> slot remap)
+  int32_t wait_chunks;      // AG: 0 = every chunk is in place (compute-only)
+  int32_t copy_blocks;
+  CopyArgs copy;
+};
+
+// Ring-attention step (ring_attn.hip).  Same role split as GemmArgs.
 struct AttnArgs {
   const uint16_t* q;  // bf16 [sq][heads_q][128]
-  const uint16_t* k;  // bf16 [world*n][heads_kv][128] (local copy, filled by the copy agent)
+  const uint16_t* k;  // bf16 [world*n][heads_kv][128] (local copy, filled by the copy role)
   const uint16_t* v;
   float* o;           // [sq][heads_q][128]
   float* m_state;     // [heads_q][sq]
@@ -59,11 +73,16 @@ struct AttnArgs {
   int32_t init, finalize;
   const int64_t* chunk_begin;  // key-row bounds of the KV chunks
   const int32_t* arrival;
+  const int32_t* resident;
   int32_t num_chunks;
   const uint32_t* flags;
   uint32_t* hdr;
+  CounterArrays cnt;
   uint64_t timeout_ticks;
   int32_t nxcd;
+  int32_t wait_chunks;
+  int32_t copy_blocks;
+  CopyArgs copy;
 };
 
 }  // namespace syncov

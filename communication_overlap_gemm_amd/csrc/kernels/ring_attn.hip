@@ -30,6 +30,7 @@
 //    last key, and those keys are masked to -inf.
 #include <math.h>
 
+#include "copy_role.hpp"
 #include "device_common.hpp"
 #include "launch_args.hpp"
 
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
   const int HG = a.heads_per_item, QS = 8 / HG, QB = 32 * QS;
   const int hh = wave % HG, qs = wave / HG;
   const int half = lane >> 5, col = lane & 31;
-  const uint32_t epoch = a.hdr[WS_EPOCH];
+  const uint32_t epoch = call_epoch(a.hdr);
   const int64_t Hq = a.heads_q, Hkv = a.heads_kv;
   const int64_t krow = Hkv * kD;  // elements between consecutive keys of one head
   const float c2 = a.scale * 1.4426950408889634f;  // scale in log2 units
@@ -75,8 +76,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
   const int nqb = static_cast<int>((a.sq + QB - 1) / QB);
   const int items = nqb * static_cast<int>(Hq / HG);
 
-  const int32_t slot0 = xcd_slot(blockIdx.x, gridDim.x, a.nxcd);
-  for (int item = slot0; item < items; item += gridDim.x) {
+  if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
+    copy_role<kAttnThreads>(a.copy, blockIdx.x, a.copy_blocks, epoch);
+    end_call(a.hdr, epoch, a.cnt);
+    return;
+  }
+  const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
+  const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
+  for (int item = slot0; item < items; item += gn) {
     const int hg = item / nqb, qb = item - hg * nqb;  // head-group-major: one KV head's items adjacent
     const int64_t h = static_cast<int64_t>(hg) * HG + hh;
     const int g = static_cast<int>(h / group);  // KV head (uniform: HG divides the group or equals it)
@@ -119,8 +126,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
     u32x4_t rk[2];
     uint32_t rv[8];
     auto wait_chunk = [&](int pos) {
+      const int32_t c = a.arrival[pos];
+      if (!a.wait_chunks || a.resident[c]) return 1;  // in place before the call
       if (tid == 0) {
-        const bool ok = wait_flag(a.flags, a.arrival[pos], epoch, a.hdr, a.timeout_ticks);
+        const bool ok = wait_flag(a.flags, c, epoch, a.hdr, a.timeout_ticks);
         if (ok) acquire_agent();
         s_ok = ok;
       }
@@ -289,6 +298,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
       }
     }
   }
+  end_call(a.hdr, epoch, a.cnt);
 }
 
 hipError_t launch_ring_attn(const AttnArgs& a, int grid, hipStream_t s) {

@@ -30,10 +30,6 @@ namespace syncov {
 
 hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid, hipStream_t s);
 bool gemm_variant_exists(int tm, int tn);
-hipError_t launch_copy_agent(const CopyArgs& a, int grid, hipStream_t s);
-int copy_agent_max_wg_per_cu();
-hipError_t launch_begin_call(uint32_t* hdr, uint32_t* flags, uint32_t* counters, uint32_t* parts, uint32_t* xparts,
-                             int32_t num_chunks, const int32_t* resident, int32_t preset_all, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s);
 hipError_t launch_ring_attn(const AttnArgs& a, int grid, hipStream_t s);
@@ -62,10 +58,6 @@ int hip_fail(hipError_t e, const char* what) {
     hipError_t _e = (expr);                       \
     if (_e != hipSuccess) return hip_fail(_e, #expr); \
   } while (0)
-
-// Default copy-agent workgroups per dedicated CU (measured fastest: more
-// workgroups add per-chunk synchronisation without adding bandwidth).
-constexpr int kCopyWgPerCu = 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -301,14 +293,15 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   sync_copy_cfg cfg{};
   cfg.backend = SYNC_COPY_SDMA;
   if (cfg_in) cfg = *cfg_in;
-  if (cfg.reserved) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
-  if (cfg.copy_wg_per_cu < 0 || cfg.copy_wg_per_cu > 16) return fail(SYNC_EINVAL, "copy_wg_per_cu must be in [0, 16]");
-  if (cfg.copy_wg_per_cu == 0) cfg.copy_wg_per_cu = kCopyWgPerCu;
-  cfg.copy_wg_per_cu = std::min(cfg.copy_wg_per_cu, copy_agent_max_wg_per_cu());  // whole grid resident
+  if (cfg.reserved[0] || cfg.reserved[1]) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
+  if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_HOST_GATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
-  if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED))
+  if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD))
     return fail(SYNC_EINVAL, "unknown cfg.flags bits");
+  if ((cfg.flags & SYNC_RUN_WITHHOLD) &&
+      (cfg.backend != SYNC_COPY_CU || op == SYNC_OP_GEMM_RS || (cfg.flags & (SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY))))
+    return fail(SYNC_EINVAL, "WITHHOLD needs the CU backend, an AG or attention plan, and no other run mode");
   if ((cfg.flags & SYNC_RUN_COPY_ONLY) && (cfg.flags & SYNC_RUN_COMPUTE_ONLY))
     return fail(SYNC_EINVAL, "COPY_ONLY and COMPUTE_ONLY are exclusive");
   if ((cfg.flags & SYNC_RUN_COPY_ONLY) && cfg.backend == SYNC_COPY_PRESET)
@@ -330,15 +323,15 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
 }
 
 // Enqueues, on `s`, SDMA copies of every non-resident chunk in arrival order,
-// each followed by a one-lane kernel that raises the chunk's flag (stream
-// order puts it after the copy has landed).  HOST_GATED first makes the stream
-// wait for the chunk's host word.
+// each followed (when `publish`) by a one-lane kernel that raises the chunk's
+// flag (stream order puts it after the copy has landed).  HOST_GATED first
+// makes the stream wait for the chunk's host word.
 // Measured limitation of this path under the HIP runtime: once the persistent
 // GEMM is running, the runtime does not start the next SDMA copy on the copy
 // stream until the GEMM exits, so only chunks copied before the GEMM starts
 // overlap; later ones time out.  The CU backend does not have this limit.
 int enqueue_sdma_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2], char* const dst[2],
-                         const int64_t row_bytes[2], int ntensors, hipStream_t s) {
+                         const int64_t row_bytes[2], int ntensors, bool publish, hipStream_t s) {
   for (int32_t p = 0; p < pl.num_chunks; ++p) {
     const int32_t c = pl.arrival[p];
     if (pl.resident[c]) continue;
@@ -349,7 +342,7 @@ int enqueue_sdma_copy_in(const Plan& pl, const CallCtx& cx, const char* const sr
     for (int x = 0; x < ntensors; ++x)
       HIP_TRY(hipMemcpyAsync(dst[x] + r0 * row_bytes[x], src[x] + r0 * row_bytes[x],
                              static_cast<size_t>((r1 - r0) * row_bytes[x]), hipMemcpyDeviceToDeviceNoCU, s));
-    HIP_TRY(launch_publish_flag(cx.ws.hdr, cx.ws.flags, c, s));
+    if (publish) HIP_TRY(launch_publish_flag(cx.ws.hdr, cx.ws.flags, c, s));
   }
   return SYNC_OK;
 }
@@ -367,7 +360,11 @@ int check_gemm_shape(const Plan& pl) {
   return SYNC_OK;
 }
 
+// Compute workgroups per CU (the kernel's occupancy; copy workgroups of the
+// same launch take CUs at the same rate).
 int gemm_wg_per_cu(const Plan& pl) { return (pl.desc.tile_m == 128 && pl.desc.tile_n == 128) ? 2 : 1; }
+
+CounterArrays counter_arrays(const CallCtx& cx, int32_t C) { return CounterArrays{cx.ws.counters, cx.ws.parts, cx.ws.xparts, C}; }
 
 GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const void* B, void* C) {
   GemmArgs g{};
@@ -383,85 +380,124 @@ GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const 
   g.dep_ptr = cx.tab->dep_ptr;
   g.dep_idx = cx.tab->dep_idx;
   g.tiles_in = cx.tab->tiles_in;
+  g.resident = cx.tab->resident;
   g.flags = cx.ws.flags;
-  g.counters = cx.ws.counters;
   g.hdr = cx.ws.hdr;
+  g.cnt = counter_arrays(cx, pl.num_chunks);
   g.timeout_ticks = cx.timeout_ticks;
   g.nxcd = cx.dev->num_xcds;
+  g.wait_chunks = 1;
+  g.copy_blocks = 0;
   return g;
 }
 
-// Runs one call's copy-in (CU or SDMA backend, or none) beside the compute
-// kernel launched by `compute(stream, cus)`, joining both back to `cs`.
-// Chunks are staged from src[x] to dst[x] (ntensors tensors of rb[x]-byte
-// rows) in arrival order; resident chunks are skipped.
-template <typename Compute>
-int copy_in_and_compute(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs,
-                        void* copy, const char* const src[2], char* const dst[2], const int64_t rb[2], int ntensors,
-                        Compute compute) {
-  int rc = SYNC_OK;
-  const bool copy_only = cx.cfg.flags & SYNC_RUN_COPY_ONLY;
-  const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
-  if (cx.cfg.backend == SYNC_COPY_CU) {
-    MaskedPair* mp = nullptr;
-    if ((rc = masked_pair(d, cx.cfg.copy_cus, &mp))) return rc;
-    HIP_TRY(hipEventRecord(d.ev_fork, cs));
-    if (!compute_only) {
-      CopyArgs ca{};
-      for (int x = 0; x < ntensors; ++x) {
-        ca.src[x] = src[x];
-        ca.dst[x] = dst[x];
-        ca.row_bytes[x] = rb[x];
-      }
-      ca.ntensors = ntensors;
-      ca.num_chunks = pl.num_chunks;
-      ca.chunk_begin = cx.tab->chunk_begin;
-      ca.arrival = cx.tab->arrival;
-      ca.resident = cx.tab->resident;
-      ca.out_flags = cx.ws.flags;
-      ca.parts = cx.ws.parts;
-      ca.xparts = cx.ws.xparts;
-      ca.hdr = cx.ws.hdr;
-      ca.timeout_ticks = cx.timeout_ticks;
-      ca.streaming = cx.cfg.copy_streaming;
-      HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
-      if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
-      HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * cx.cfg.copy_wg_per_cu, mp->copy));
-      if (tm) {
-        HIP_TRY(hipEventRecord(tm->c1, mp->copy));
-        tm->has_copy = true;
-      }
-      HIP_TRY(hipEventRecord(d.ev_copy, mp->copy));
-    }
-    if (!copy_only) {
-      HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
-      if ((rc = compute(mp->gemm, mp->gemm_cus))) return rc;
-      HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
-      HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
-    }
-    if (!compute_only) HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
-    return SYNC_OK;
+// Copy role arguments: copy-in stages chunks from src[x] to dst[x] at the same
+// rows (ntensors tensors of rb[x]-byte rows) and raises the ready flags.
+CopyArgs make_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2], char* const dst[2],
+                      const int64_t rb[2], int ntensors) {
+  CopyArgs ca{};
+  for (int x = 0; x < ntensors; ++x) {
+    ca.src[x] = src[x];
+    ca.dst[x] = dst[x];
+    ca.row_bytes[x] = rb[x];
   }
+  ca.ntensors = ntensors;
+  ca.num_chunks = pl.num_chunks;
+  ca.chunk_begin = cx.tab->chunk_begin;
+  ca.arrival = cx.tab->arrival;
+  ca.resident = cx.tab->resident;
+  ca.slot_row = cx.tab->slot_row;
+  ca.out_flags = cx.ws.flags;
+  ca.parts = cx.ws.parts;
+  ca.xparts = cx.ws.xparts;
+  ca.hdr = cx.ws.hdr;
+  ca.timeout_ticks = cx.timeout_ticks;
+  ca.streaming = cx.cfg.copy_streaming;
+  return ca;
+}
 
-  if (compute_only) return compute(cs, d.num_cus);
-  // SDMA: the chunk data moves on the SDMA engine and a one-lane kernel raises
-  // each flag; the compute kernel runs on a CU-masked stream that leaves one CU
-  // per XCD to the copy stream for those flag kernels.
+// How one call's launch is split between roles.
+struct Roles {
+  int grid = 0;         // workgroups of the launch (0: no compute launch)
+  int copy_blocks = 0;  // leading workgroups that run the copy role
+  int wait = 1;         // compute waits for non-resident chunks
+  bool sdma = false;    // copy-in on the SDMA engine beside the launch
+};
+
+// CU backend: one launch, copy_cus * wpc copy workgroups first, then one
+// compute workgroup per remaining CU slot.  PRESET: compute alone, nothing to
+// wait for.  SDMA / HOST_GATED: compute on the CUs the masked GEMM stream
+// allows, copies on the SDMA engine.
+Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
+  Roles r;
+  const bool copy_only = cx.cfg.flags & SYNC_RUN_COPY_ONLY;
+  const bool compute_only = cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY;
+  switch (cx.cfg.backend) {
+    case SYNC_COPY_PRESET:
+      r.grid = d.num_cus * wpc;
+      r.wait = 0;
+      break;
+    case SYNC_COPY_CU:
+      if (copy_only) {
+        r.grid = r.copy_blocks = cx.cfg.copy_cus * wpc;
+      } else if (cx.cfg.flags & SYNC_RUN_WITHHOLD) {
+        r.grid = (d.num_cus - cx.cfg.copy_cus) * wpc;  // waits, but nobody copies
+      } else if (compute_only) {
+        r.grid = (d.num_cus - cx.cfg.copy_cus) * wpc;
+        r.wait = 0;
+      } else {
+        r.grid = d.num_cus * wpc;
+        r.copy_blocks = cx.cfg.copy_cus * wpc;
+      }
+      break;
+    default:  // SDMA, HOST_GATED
+      if (compute_only) {
+        r.grid = d.num_cus * wpc;
+        r.wait = 0;
+      } else {
+        r.sdma = true;
+        r.grid = copy_only ? 0 : (d.num_cus - d.num_xcds) * wpc;
+      }
+      break;
+  }
+  return r;
+}
+
+// Enqueues one call: `launch(stream, roles)` puts the compute kernel (with its
+// copy workgroups, if any) on a stream; SDMA copy-in goes to the library's
+// copy stream with the compute kernel on the masked GEMM stream, both joined
+// back to `cs`.
+template <typename Launch>
+int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs, void* copy,
+             const Roles& r, const char* const src[2], char* const dst[2], const int64_t rb[2], int ntensors,
+             Launch launch) {
+  auto timed = [&](hipStream_t st) -> int {
+    if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
+    int rc = launch(st, r);
+    if (rc) return rc;
+    if (tm) {
+      HIP_TRY(hipEventRecord(tm->k1, st));
+      tm->has_kernel = true;
+    }
+    return SYNC_OK;
+  };
+  if (!r.sdma) return timed(cs);
   MaskedPair* mp = nullptr;
-  if ((rc = masked_pair(d, d.num_xcds, &mp))) return rc;
+  int rc = masked_pair(d, d.num_xcds, &mp);
+  if (rc) return rc;
   hipStream_t ss = copy ? static_cast<hipStream_t>(copy) : mp->copy;
   HIP_TRY(hipEventRecord(d.ev_fork, cs));
   HIP_TRY(hipStreamWaitEvent(ss, d.ev_fork, 0));
   if (tm) HIP_TRY(hipEventRecord(tm->c0, ss));
-  if ((rc = enqueue_sdma_copy_in(pl, cx, src, dst, rb, ntensors, ss))) return rc;
+  if ((rc = enqueue_sdma_copy_in(pl, cx, src, dst, rb, ntensors, r.grid > 0, ss))) return rc;
   if (tm) {
     HIP_TRY(hipEventRecord(tm->c1, ss));
     tm->has_copy = true;
   }
   HIP_TRY(hipEventRecord(d.ev_copy, ss));
-  if (!copy_only) {
+  if (r.grid > 0) {
     HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
-    if ((rc = compute(mp->gemm, mp->gemm_cus))) return rc;
+    if ((rc = timed(mp->gemm))) return rc;
     HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
     HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
   }
@@ -575,34 +611,26 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
     return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
   DeviceState& d = *cx.dev;
   std::lock_guard<std::mutex> lk(d.mu);
-  hipStream_t cs = static_cast<hipStream_t>(compute);
-  const bool copy_only = cx.cfg.flags & SYNC_RUN_COPY_ONLY;
-  const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
-  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, cx.ws.xparts, pl.num_chunks,
-                            cx.tab->resident,
-                            compute_only ? 1 : 0, cs));
-  GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
-  auto gemm_on = [&](hipStream_t st, int grid) -> int {
-    if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
-    HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, false, grid, st));
-    if (tm) {
-      HIP_TRY(hipEventRecord(tm->k1, st));
-      tm->has_kernel = true;
-    }
-    return SYNC_OK;
-  };
   const char* src[2] = {static_cast<const char*>(a_peer), nullptr};
   char* dst[2] = {static_cast<char*>(a_local), nullptr};
   const int64_t rb[2] = {pl.desc.k * 2, 0};
-  return copy_in_and_compute(pl, cx, d, tm, cs, copy, src, dst, rb, 1,
-                             [&](hipStream_t st, int cus) { return gemm_on(st, cus * gemm_wg_per_cu(pl)); });
+  GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
+  g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
+  const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, src, dst, rb, 1,
+                  [&](hipStream_t st, const Roles& rr) -> int {
+                    g.copy_blocks = rr.copy_blocks;
+                    g.wait_chunks = rr.wait;
+                    HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, false, rr.grid,
+                                        st));
+                    return SYNC_OK;
+                  });
 }
 
 int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c, int32_t c_dtype,
                  void* staging, void* ws, void* compute, void* copy) {
-  (void)copy;
   CallCtx cx;
   int rc = prepare(plan, cfg, ws, SYNC_OP_GEMM_RS, cx);
   if (rc) return rc;
@@ -618,60 +646,28 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
     return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
   DeviceState& d = *cx.dev;
   std::lock_guard<std::mutex> lk(d.mu);
-  hipStream_t cs = static_cast<hipStream_t>(compute);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
-  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, cx.ws.xparts, pl.num_chunks, nullptr,
-                            0, cs));
   GemmArgs g = make_gemm_args(pl, cx, a, b, c);
-  auto gemm_on = [&](hipStream_t st, int grid) -> int {
-    if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
-    HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, true, grid, st));
-    if (tm) {
-      HIP_TRY(hipEventRecord(tm->k1, st));
-      tm->has_kernel = true;
-    }
-    return SYNC_OK;
-  };
-  if (compute_only && cx.cfg.backend == SYNC_COPY_PRESET) return gemm_on(cs, d.num_cus * gemm_wg_per_cu(pl));
-  MaskedPair* mp = nullptr;
-  if ((rc = masked_pair(d, cx.cfg.copy_cus, &mp))) return rc;
-  HIP_TRY(hipEventRecord(d.ev_fork, cs));
-  HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
-  if ((rc = gemm_on(mp->gemm, mp->gemm_cus * gemm_wg_per_cu(pl)))) return rc;
-  HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
-  if (!compute_only) {
-    CopyArgs ca{};
+  {
+    // copy-out: rows of C, in send order, into the packed staging slots
     const int64_t es = c_dtype == SYNC_DTYPE_F32 ? 4 : 2;
-    ca.src[0] = static_cast<const char*>(c);
-    ca.dst[0] = static_cast<char*>(staging);
-    ca.row_bytes[0] = pl.desc.n * es;
-    ca.ntensors = 1;
-    ca.num_chunks = pl.num_chunks;
-    ca.chunk_begin = cx.tab->chunk_begin;
-    ca.arrival = cx.tab->arrival;
-    ca.resident = cx.tab->resident;
-    ca.slot_row = cx.tab->slot_row;
-    ca.out_flags = cx.ws.sent;
-    ca.wait_flags = cx.ws.flags;
-    ca.parts = cx.ws.parts;
-    ca.xparts = cx.ws.xparts;
-    ca.hdr = cx.ws.hdr;
-    ca.timeout_ticks = cx.timeout_ticks;
-    ca.copy_out = 1;
-    ca.streaming = cx.cfg.copy_streaming;
-    HIP_TRY(hipStreamWaitEvent(mp->copy, d.ev_fork, 0));
-    if (tm) HIP_TRY(hipEventRecord(tm->c0, mp->copy));
-    HIP_TRY(launch_copy_agent(ca, cx.cfg.copy_cus * cx.cfg.copy_wg_per_cu, mp->copy));
-    if (tm) {
-      HIP_TRY(hipEventRecord(tm->c1, mp->copy));
-      tm->has_copy = true;
-    }
-    HIP_TRY(hipEventRecord(d.ev_copy, mp->copy));
-    HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
+    const char* src[2] = {static_cast<const char*>(c), nullptr};
+    char* dst[2] = {static_cast<char*>(staging), nullptr};
+    const int64_t rb[2] = {pl.desc.n * es, 0};
+    g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
+    g.copy.copy_out = 1;
+    g.copy.out_flags = cx.ws.sent;
+    g.copy.wait_flags = cx.ws.flags;
   }
-  HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
-  return SYNC_OK;
+  const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, nullptr, nullptr, nullptr, 0,
+                  [&](hipStream_t st, const Roles& rr) -> int {
+                    g.copy_blocks = rr.copy_blocks;
+                    HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, true, rr.grid,
+                                        st));
+                    return SYNC_OK;
+                  });
 }
 
 int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q, const void* k_peer,
@@ -698,12 +694,12 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
     return fail(SYNC_EUNSUPPORTED, "query tensor too large for 32-bit buffer offsets");
   DeviceState& d = *cx.dev;
   std::lock_guard<std::mutex> lk(d.mu);
-  hipStream_t cs = static_cast<hipStream_t>(compute);
-  const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
-  HIP_TRY(launch_begin_call(cx.ws.hdr, cx.ws.flags, cx.ws.counters, cx.ws.parts, cx.ws.xparts, pl.num_chunks,
-                            cx.tab->resident, compute_only ? 1 : 0, cs));
+  const int64_t row = static_cast<int64_t>(dsc.heads_kv) * dsc.k * 2;  // bytes per token of K or V
+  const char* src[2] = {static_cast<const char*>(k_peer), static_cast<const char*>(v_peer)};
+  char* dst[2] = {static_cast<char*>(k_local), static_cast<char*>(v_local)};
+  const int64_t rb[2] = {row, row};
   AttnArgs at{};
   at.q = static_cast<const uint16_t*>(q);
   at.k = static_cast<const uint16_t*>(k_local);
@@ -721,25 +717,22 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   at.finalize = (flags & SYNC_ATTN_FINALIZE) ? 1 : 0;
   at.chunk_begin = cx.tab->chunk_begin;
   at.arrival = cx.tab->arrival;
+  at.resident = cx.tab->resident;
   at.num_chunks = pl.num_chunks;
   at.flags = cx.ws.flags;
   at.hdr = cx.ws.hdr;
+  at.cnt = counter_arrays(cx, pl.num_chunks);
   at.timeout_ticks = cx.timeout_ticks;
   at.nxcd = d.num_xcds;
-  auto attn_on = [&](hipStream_t st, int cus) -> int {
-    if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
-    HIP_TRY(launch_ring_attn(at, cus, st));
-    if (tm) {
-      HIP_TRY(hipEventRecord(tm->k1, st));
-      tm->has_kernel = true;
-    }
-    return SYNC_OK;
-  };
-  const int64_t row = static_cast<int64_t>(dsc.heads_kv) * dsc.k * 2;  // bytes per token of K or V
-  const char* src[2] = {static_cast<const char*>(k_peer), static_cast<const char*>(v_peer)};
-  char* dst[2] = {static_cast<char*>(k_local), static_cast<char*>(v_local)};
-  const int64_t rb[2] = {row, row};
-  return copy_in_and_compute(pl, cx, d, tm, cs, copy, src, dst, rb, 2, attn_on);
+  at.copy = make_copy_in(pl, cx, src, dst, rb, 2);
+  const Roles r = roles_for(cx, d, 1);
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, src, dst, rb, 2,
+                  [&](hipStream_t st, const Roles& rr) -> int {
+                    at.copy_blocks = rr.copy_blocks;
+                    at.wait_chunks = rr.wait;
+                    HIP_TRY(launch_ring_attn(at, rr.grid, st));
+                    return SYNC_OK;
+                  });
 }
 
 int sync_get_device_info(sync_device_info* out) {

@@ -147,15 +147,19 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
 /* Backends [SYN-S "Core method", paper sec. 5.2, Fig. 7: the same plan lowers
  * to a copy engine or to load/store on dedicated SMs, both signalling through
  * global-memory flags]:
- *   PRESET      no copy; every chunk is marked ready before the kernel
- *               (compute-only; the caller provides the whole input)
+ *   PRESET      no copy; every chunk is taken as present (compute-only; the
+ *               caller provides the whole input)
  *   SDMA        per chunk, an SDMA-engine copy then a one-lane flag kernel, on
- *               the library's copy stream (masked to one CU per XCD; the GEMM
- *               runs on the other CUs).  Known limit: under the HIP runtime the
- *               next SDMA copy does not start while the persistent GEMM runs,
- *               so chunks not copied before the GEMM starts time out.
- *   CU          one copy kernel on `copy_cus` dedicated CUs (CU-masked
- *               stream); the GEMM runs on the remaining CUs
+ *               the library's copy stream (masked to one CU per XCD; the
+ *               compute kernel runs on the other CUs).  Known limit: under the
+ *               HIP runtime the next SDMA copy does not start while the
+ *               persistent GEMM runs, so chunks not copied before the GEMM
+ *               starts time out.
+ *   CU          the call is ONE kernel launch on `compute`: its first
+ *               copy_cus x (compute workgroups per CU) workgroups copy, the
+ *               rest compute; `copy` is unused.  Copy workgroups are spread
+ *               evenly over the XCDs and are resident before any compute
+ *               workgroup.
  *   HOST_GATED  as SDMA, but chunk c's copy first waits until the host word
  *               host_gates[c] becomes non-zero (tests: delayed or withheld
  *               chunks) */
@@ -163,32 +167,42 @@ enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOS
 
 /* mode bits for sync_copy_cfg.flags */
 enum {
-  SYNC_RUN_COPY_ONLY = 1,    /* run only the copy agent (copy-only timing) */
-  SYNC_RUN_COMPUTE_ONLY = 2, /* with CU backend: run only the GEMM on its CU share, flags preset */
-  SYNC_RUN_TIMED = 4         /* record device events around the copy agent and the compute kernel,
-                                on the streams they run on; read with sync_read_timings() */
+  SYNC_RUN_COPY_ONLY = 1,    /* run only the copy (copy-only timing); AG and attention */
+  SYNC_RUN_COMPUTE_ONLY = 2, /* run only the compute kernel, with the workgroups the CU split
+                                leaves it (CU backend) or all CUs, every chunk taken as present */
+  SYNC_RUN_TIMED = 4,        /* record device events around the call's kernel launch and the
+                                SDMA copies, on the streams they run on; read with
+                                sync_read_timings() */
+  SYNC_RUN_WITHHOLD = 8      /* CU backend, AG and attention (failure-path tests): no chunk is
+                                copied or flagged, so the compute kernel's waits for the
+                                non-resident chunks expire after timeout_ns and the call
+                                reports SYNC_ETIMEOUT through sync_workspace_status */
 };
 
 typedef struct {
   int32_t backend;          /* SYNC_COPY_* */
-  int32_t copy_cus;         /* CU backend: dedicated copy CUs, 8..128, multiple of 8 */
+  int32_t copy_cus;         /* CU backend: CUs given to the copy role, 8..128, multiple of 8 */
   uint64_t timeout_ns;      /* bound on every device-side wait; 0 = 2 s */
   const uint32_t* host_gates; /* HOST_GATED: pinned host words (hipHostMalloc), one per chunk */
   int32_t flags;            /* SYNC_RUN_* bits */
-  int32_t copy_wg_per_cu;   /* CU backend: copy workgroups per dedicated CU; 0 = 1; clamped to
-                                what fits on a CU at once */
-  int32_t copy_streaming;   /* CU backend: 1 = non-temporal loads/stores in the copy agent; 0 = plain */
-  int32_t reserved;         /* must be zero */
+  int32_t copy_streaming;   /* CU backend: 1 = non-temporal loads/stores in the copy role; 0 = plain */
+  int32_t reserved[2];      /* must be zero */
 } sync_copy_cfg;
 
 /* ---- workspace ---------------------------------------------------------- */
 /* Device scratch for flags, counters, the epoch and the error word.  Owned by
- * the caller, at least sync_workspace_size() bytes, 256-byte aligned; one
- * workspace must not be used by two calls that may overlap in time. */
+ * the caller, at least sync_workspace_size() bytes, 256-byte aligned.  Calls
+ * on one workspace must be ordered (one stream, or joined streams); two calls
+ * that may overlap in time race on it. */
 size_t sync_workspace_size(sync_plan_t plan);
 
-/* Zeroes the workspace with a fill kernel on `stream` (call once after
- * allocation).  Later calls bump a device-side epoch instead of clearing. */
+/* Zeroes the workspace with a fill kernel on `stream`.  Call once after
+ * allocation, and again after a call reported a device-side timeout (the
+ * error word is sticky: later waits give up at once).  Between calls nothing
+ * is cleared: each call's kernel takes the next epoch from the workspace and
+ * its last workgroup stores it, so a call is exactly one launch on the
+ * compute stream with the CU backend, and replaying a captured call is
+ * valid. */
 int sync_workspace_init(sync_plan_t plan, void* ws, void* stream);
 
 /* Synchronises `stream`, then reads the workspace error word.  Returns
@@ -214,10 +228,10 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
 /* GEMM-RS share [SYN-S "Experiments": GEMM-RS; ENT: tiles reordered so output
  * for communication is produced at a steady pace; SM-based fine-grained
  * communication].  The GEMM visits tiles in send order; when the last tile of
- * chunk c is stored it raises done[c]; the copy agent (CU backend: dedicated
- * CUs; SDMA: not supported, EUNSUPPORTED) waits for done[c] in send order and
- * copies the chunk's rows of c into `staging`, slot p = chunk arrival[p]
- * (slots packed back to back in send order).
+ * chunk c is stored it raises done[c]; the copy workgroups (CU backend; SDMA:
+ * not supported, EUNSUPPORTED) wait for done[c] in send order and copy the
+ * chunk's rows of c into `staging`, slot p = chunk arrival[p] (slots packed
+ * back to back in send order).
  *   a bf16 [m][k]; b bf16 as in sync_ag_gemm; c and staging [m][n] c_dtype.
  * PRESET: the GEMM alone (done flags raised, no copy-out). */
 int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
@@ -248,9 +262,10 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
 
 /* Durations of the most recent SYNC_RUN_TIMED calls on the current device
  * (a ring of 1024), oldest first; waits for those events.  kernel_ms is the
- * compute kernel (GEMM or attention) from just before its launch to just
- * after it, on its own stream; copy_ms spans the copy agent's work (0 if none).
- * Reading empties the ring.  *count = records written to out (<= max). */
+ * call's kernel launch (GEMM or attention; with the CU backend its copy
+ * workgroups are part of it) from just before the launch to just after it, on
+ * the stream it runs on; copy_ms spans the SDMA copies (0 if none).  Reading
+ * empties the ring.  *count = records written to out (<= max). */
 typedef struct {
   float kernel_ms;
   float copy_ms;

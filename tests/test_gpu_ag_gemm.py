@@ -194,3 +194,92 @@ def test_full_size_normal(backend, cus, split, layout):
         sel = shard == s
         num = np.linalg.norm(out[rows[sel], cols[sel]] - ref[sel])
         assert num / np.linalg.norm(ref[sel]) <= 1e-3
+
+
+# ---- one launch per call: failure path and replay ---------------------------
+
+def test_withheld_chunks_time_out_and_error_is_sticky():
+    """Chunks that never arrive: the waits expire (2 ms), the call reports the
+    timeout with a chunk that was withheld, tiles needing only the resident
+    shard are still computed and the others are left untouched; the error
+    stays until the workspace is initialised again, after which a normal call
+    is exact."""
+    m, n, k, world = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 32.0)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, tile_m=128, tile_n=128))
+    tabs = A.sync_plan_export(plan)
+    resident = [c for c in range(tabs["num_chunks"]) if tabs["resident"][c]]
+    assert resident == [0]
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    a_local = torch.zeros_like(a_peer)
+    a_local[0:256] = a_peer[0:256]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    withhold = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, timeout_ns=2_000_000, flags=A.SYNC_RUN_WITHHOLD)
+    print("[ag] withheld chunks, 2 ms limit", flush=True)
+    A.sync_ag_gemm(plan, withhold, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_ETIMEOUT and chunk in (1, 2, 3)
+    out = c.cpu().numpy()
+    assert np.isnan(out[256:]).all()
+    check_f32(out[:256], ref[:256], 1)
+    # sticky: the next call gives up at once and reports the same error
+    A.sync_ag_gemm(plan, A.make_cfg(A.SYNC_COPY_CU, copy_cus=8), a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s,
+                   None)
+    assert A.sync_workspace_status(ws, s)[0] == A.SYNC_ETIMEOUT
+    A.sync_workspace_init(plan, ws, s)
+    c.fill_(float("nan"))
+    A.sync_ag_gemm(plan, A.make_cfg(A.SYNC_COPY_CU, copy_cus=8), a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s,
+                   None)
+    assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
+    check_f32(c.cpu().numpy(), ref, world)
+
+
+def test_captured_call_replays():
+    """A CU-backend call is one kernel launch that takes its epoch from the
+    workspace, so a captured call can be replayed: each replay (with eager
+    work and synchronisation between replays, and different peer data) must
+    equal the eager result for that data."""
+    m = n = k = 1024
+    world = 4
+    data = [inputs.gemm_operands(m, n, k, 32.0, seed_a=inputs.SEED_A + 7 * x)[0] for x in range(3)]
+    _, b = inputs.gemm_operands(m, n, k, 32.0)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, split=2, tile_m=128, tile_n=128))
+    cfg = A.make_cfg(A.SYNC_COPY_CU, copy_cus=16)
+    b_d = dev_bits(b)
+    a_peer = dev_bits(data[0])
+    a_local = torch.zeros_like(a_peer)
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    eager = []
+    for x in range(3):  # eager results, one per dataset
+        a_peer.copy_(dev_bits(data[x]))
+        a_local.zero_()
+        a_local[0:256] = a_peer[0:256]
+        A.sync_ag_gemm(plan, cfg, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+        assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
+        eager.append(c.clone())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(s)
+    with torch.cuda.stream(side):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            A.sync_ag_gemm(plan, cfg, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, side, None)
+    s.wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        x = rep % 3
+        print(f"[ag] graph replay {rep} dataset {x}", flush=True)
+        a_peer.copy_(dev_bits(data[x]))
+        a_local.zero_()
+        a_local[0:256] = a_peer[0:256]
+        c.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
+        assert torch.equal(c, eager[x]), f"replay {rep} differs from the eager call"

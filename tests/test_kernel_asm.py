@@ -43,8 +43,10 @@ def test_check_catches_conditional_reads(tmp_path):
     for old, new in edits:
         assert old in bad, "kernel text changed: update the planted variant"
         bad = bad.replace(old, new)
-    for name in ("device_common.hpp", "launch_args.hpp"):
-        shutil.copy(os.path.join(os.path.dirname(asm_check.KERNEL), name), tmp_path / name)
+    kdir = os.path.dirname(asm_check.KERNEL)
+    for name in os.listdir(kdir):
+        if name.endswith(".hpp"):
+            shutil.copy(os.path.join(kdir, name), tmp_path / name)
     path = tmp_path / "gemm_persistent.hip"
     path.write_text(bad)
     _, found = asm_check.hazards(asm_check.device_assembly(str(path)))
