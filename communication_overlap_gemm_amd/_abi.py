@@ -26,13 +26,13 @@ SYNC_ORDER_ROW_MAJOR, SYNC_ORDER_CHUNK_MAJOR, SYNC_ORDER_SWIZZLED = 0, 1, 2
 SYNC_B_KN, SYNC_B_NK = 0, 1
 SYNC_DTYPE_F32, SYNC_DTYPE_BF16 = 0, 1
 SYNC_COPY_PRESET, SYNC_COPY_SDMA, SYNC_COPY_CU, SYNC_COPY_HOST_GATED = 0, 1, 2, 3
-SYNC_RUN_COPY_ONLY, SYNC_RUN_COMPUTE_ONLY, SYNC_RUN_TIMED, SYNC_RUN_WITHHOLD = 1, 2, 4, 8
+SYNC_RUN_COPY_ONLY, SYNC_RUN_COMPUTE_ONLY, SYNC_RUN_TIMED, SYNC_RUN_WITHHOLD, SYNC_RUN_TRACE = 1, 2, 4, 8, 16
 SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 
 EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
     "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_gemm_rs", "sync_ring_attn_step",
-    "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings",
+    "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
 )
 
 
@@ -74,7 +74,12 @@ class sync_plan_tables(ctypes.Structure):
 class sync_copy_cfg(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("copy_cus", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
                 ("host_gates", ctypes.c_void_p), ("flags", ctypes.c_int32), ("copy_streaming", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("withhold_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class sync_trace(ctypes.Structure):
+    _fields_ = [("tile_wait_begin", _P64), ("tile_wait_end", _P64), ("tile_end", _P64), ("tile_xcc", _P32),
+                ("tile_slot", _P32), ("chunk_ready", _P64), ("chunk_sent", _P64)]
 
 
 class sync_timing(ctypes.Structure):
@@ -112,6 +117,7 @@ def lib():
                                           i32, vp, vp, vp]),
             "sync_get_device_info": (i32, [ctypes.POINTER(sync_device_info)]),
             "sync_read_timings": (i32, [i32, ctypes.POINTER(sync_timing), ctypes.POINTER(i32)]),
+            "sync_trace_export": (i32, [vp, vp, vp, ctypes.POINTER(sync_trace)]),
             "sync_last_error": (ctypes.c_char_p, []),
             "sync_shutdown": (None, []),
         }
@@ -209,10 +215,10 @@ def sync_plan_export(plan: Plan) -> dict:
 
 
 def make_cfg(backend: int = SYNC_COPY_SDMA, copy_cus: int = 0, timeout_ns: int = 0, host_gates=None,
-             flags: int = 0, copy_streaming: int = 0) -> sync_copy_cfg:
+             flags: int = 0, copy_streaming: int = 0, withhold_chunk: int = -1) -> sync_copy_cfg:
     c = sync_copy_cfg()
     c.backend, c.copy_cus, c.timeout_ns, c.flags = backend, copy_cus, timeout_ns, flags
-    c.copy_streaming = copy_streaming
+    c.copy_streaming, c.withhold_chunk = copy_streaming, withhold_chunk
     c.host_gates = _ptr(host_gates)
     return c
 
@@ -223,6 +229,21 @@ def sync_workspace_size(plan: Plan) -> int:
 
 def sync_workspace_init(plan: Plan, ws, stream=None) -> None:
     _check(lib().sync_workspace_init(plan.handle, _ptr(ws), _stream(stream)))
+
+
+def sync_trace_export(plan: Plan, ws, stream=None) -> dict:
+    """Trace of the last SYNC_RUN_TRACE GEMM call: numpy arrays in ns (-1 = not recorded)."""
+    info = sync_plan_info()
+    _check(lib().sync_plan_get_info(plan.handle, ctypes.byref(info)))
+    T, C = info.num_tiles, info.num_chunks
+    out = {"tile_wait_begin": np.zeros(T, np.int64), "tile_wait_end": np.zeros(T, np.int64),
+           "tile_end": np.zeros(T, np.int64), "tile_xcc": np.zeros(T, np.int32), "tile_slot": np.zeros(T, np.int32),
+           "chunk_ready": np.zeros(C, np.int64), "chunk_sent": np.zeros(C, np.int64)}
+    t = sync_trace()
+    for name, arr in out.items():
+        setattr(t, name, arr.ctypes.data_as(_P64 if arr.dtype == np.int64 else _P32))
+    _check(lib().sync_trace_export(plan.handle, _ptr(ws), _stream(stream), ctypes.byref(t)))
+    return out
 
 
 def sync_workspace_status(ws, stream=None):

@@ -100,7 +100,7 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
   if (mine == 0) return;
   for (int32_t p = 0; p < a.num_chunks; ++p) {
     const int32_t c = a.arrival[p];
-    if (!a.copy_out && a.resident[c]) continue;
+    if (!a.copy_out && (a.resident[c] || a.skip_chunk == c || a.skip_chunk == -1)) continue;
     if (a.copy_out) {
       if (threadIdx.x == 0) {
         const bool ok = wait_flag(a.wait_flags, c, epoch, a.hdr, a.timeout_ticks);
@@ -134,6 +134,7 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
         const uint32_t done = add_acq_rel_agent(a.parts + c, mine);
         if (done + mine == static_cast<uint32_t>(G)) {
           st_relaxed_agent(a.parts + c, 0u);
+          if (a.trace_chunks) a.trace_chunks[2 * c + (a.copy_out ? 1 : 0)] = wall_clock64();
           st_release_agent(a.out_flags + c, epoch);
         }
       }

@@ -118,6 +118,7 @@ __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, ui
       const uint32_t old = add_acq_rel_agent(a.cnt.counters + c, 1u);
       if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) {
         st_relaxed_agent(a.cnt.counters + c, 0u);  // every tile of c has counted: ready for the next call
+        if (a.trace_chunks) a.trace_chunks[2 * c] = wall_clock64();
         st_release_agent(a.flags + c, epoch);
       }
     }
@@ -190,9 +191,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     const int rows_valid = static_cast<int>((M - m0) < TM ? (M - m0) : TM);
     const int cols_valid = static_cast<int>((N - n0) < TN ? (N - n0) : TN);
 
+    if (a.trace_tiles && tid == 0) {
+      a.trace_tiles[4 * t] = wall_clock64();
+      a.trace_tiles[4 * t + 3] = (static_cast<uint64_t>(xcc_id()) << 32) | static_cast<uint32_t>(p);
+    }
     if constexpr (!RS) {
       if (!wait_tile_chunks(a, t, epoch, tid, &s_skip)) continue;  // a chunk never arrived: tile left untouched
     }
+    if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 1] = wall_clock64();
 
     const uint16_t* const a_tile = a.A + m0 * K;
     auto load_a = [&](int64_t k0) {
@@ -314,6 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
 
     store_tile_c<TM, TN, CT>(a, acc, reinterpret_cast<char*>(smem), m0, n0, rows_valid, cols_valid, wave, lane);
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
+    if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
   }
   end_call(a.hdr, epoch, a.cnt);
 }
@@ -455,9 +462,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
     const int64_t m0 = static_cast<int64_t>(ti) * TM, n0 = static_cast<int64_t>(tj) * TN;
     const int rows_valid = static_cast<int>((M - m0) < TM ? (M - m0) : TM);
     const int cols_valid = static_cast<int>((N - n0) < TN ? (N - n0) : TN);
+    if (a.trace_tiles && tid == 0) {
+      a.trace_tiles[4 * t] = wall_clock64();
+      a.trace_tiles[4 * t + 3] = (static_cast<uint64_t>(xcc_id()) << 32) | static_cast<uint32_t>(p);
+    }
     if constexpr (!RS) {
       if (!wait_tile_chunks(a, t, epoch, tid, &s_skip)) continue;  // a chunk never arrived: tile left untouched
     }
+    if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 1] = wall_clock64();
     const uint16_t* const a_tile = a.A + m0 * K;
     const uint16_t* const b_tile = a.B + n0 * K;
 
@@ -553,6 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
     __syncthreads();  // every wave is done reading the ring before the epilogue reuses it
     store_tile_c<TM, TN, CT>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane);
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
+    if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
   }
   end_call(a.hdr, epoch, a.cnt);
 }

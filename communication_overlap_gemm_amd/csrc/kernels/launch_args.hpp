@@ -32,7 +32,9 @@ struct CopyArgs {
   uint32_t* hdr;
   uint64_t timeout_ticks;
   int32_t copy_out;
-  int32_t streaming;  // non-temporal loads and stores
+  int32_t streaming;   // non-temporal loads and stores
+  int32_t skip_chunk;  // copy-in: chunk left out (failure-path tests); -1 = all, -2 = none
+  uint64_t* trace_chunks;  // SYNC_RUN_TRACE: per chunk {ready, sent} wall-clock stamps, or null
 };
 
 // Persistent GEMM (gemm_persistent.hip).  Workgroups [0, copy_blocks) of the
@@ -55,6 +57,8 @@ struct GemmArgs {
   int32_t nxcd;             // XCDs (for the workgroup -> slot remap)
   int32_t wait_chunks;      // AG: 0 = every chunk is in place (compute-only)
   int32_t copy_blocks;
+  uint64_t* trace_tiles;    // SYNC_RUN_TRACE: per tile {wait begin, wait end, end, xcc<<32 | slot}, or null
+  uint64_t* trace_chunks;   // SYNC_RUN_TRACE: per chunk {ready/done, sent}, or null
   CopyArgs copy;
 };
 

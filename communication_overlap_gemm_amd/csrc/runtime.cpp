@@ -257,15 +257,23 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
 
 // Workspace layout: 256-byte header, then four uint32[C] arrays, each padded
 // to 256 bytes: flags (ready / done), counters (GEMM tiles stored per chunk),
-// parts (copy workgroups finished per chunk), sent (copy-out done); then
-// xparts, uint32[C][16] (copy workgroups finished per chunk and XCD).
+// parts (copy XCD groups finished per chunk), sent (copy-out done); then
+// xparts, uint32[C][16] (copy workgroups finished per chunk and XCD); then the
+// trace: uint64[T][4] per tile and uint64[C][2] per chunk (SYNC_RUN_TRACE).
 struct WsView {
   uint32_t *hdr, *flags, *counters, *parts, *sent, *xparts;
+  uint64_t *trace_tiles, *trace_chunks;
 };
 
 int64_t ws_array_bytes(int32_t C) { return align_up(static_cast<int64_t>(C) * 4, 256); }
 
-WsView ws_view(void* ws, int32_t C) {
+int64_t ws_trace_offset(int32_t C) { return 256 + 4 * ws_array_bytes(C) + align_up(static_cast<int64_t>(C) * 4 * kMaxXcd, 256); }
+
+int64_t ws_total_bytes(int32_t C, int32_t T) {
+  return ws_trace_offset(C) + align_up(static_cast<int64_t>(T) * 32, 256) + align_up(static_cast<int64_t>(C) * 16, 256);
+}
+
+WsView ws_view(void* ws, int32_t C, int32_t T) {
   char* b = static_cast<char*>(ws);
   const int64_t a = ws_array_bytes(C);
   WsView v;
@@ -275,6 +283,9 @@ WsView ws_view(void* ws, int32_t C) {
   v.parts = reinterpret_cast<uint32_t*>(b + 256 + 2 * a);
   v.sent = reinterpret_cast<uint32_t*>(b + 256 + 3 * a);
   v.xparts = reinterpret_cast<uint32_t*>(b + 256 + 4 * a);
+  const int64_t t0 = ws_trace_offset(C);
+  v.trace_tiles = reinterpret_cast<uint64_t*>(b + t0);
+  v.trace_chunks = reinterpret_cast<uint64_t*>(b + t0 + align_up(static_cast<int64_t>(T) * 32, 256));
   return v;
 }
 
@@ -293,12 +304,15 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   sync_copy_cfg cfg{};
   cfg.backend = SYNC_COPY_SDMA;
   if (cfg_in) cfg = *cfg_in;
-  if (cfg.reserved[0] || cfg.reserved[1]) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
+  if (cfg.reserved) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_HOST_GATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
-  if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD))
+  if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
     return fail(SYNC_EINVAL, "unknown cfg.flags bits");
+  if ((cfg.flags & SYNC_RUN_TRACE) && op == SYNC_OP_RING_ATTN) return fail(SYNC_EINVAL, "TRACE is for GEMM calls");
+  if ((cfg.flags & SYNC_RUN_WITHHOLD) && (cfg.withhold_chunk < -1 || cfg.withhold_chunk >= plan->plan.num_chunks))
+    return fail(SYNC_EINVAL, "withhold_chunk must be -1 or a chunk id");
   if ((cfg.flags & SYNC_RUN_WITHHOLD) &&
       (cfg.backend != SYNC_COPY_CU || op == SYNC_OP_GEMM_RS || (cfg.flags & (SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY))))
     return fail(SYNC_EINVAL, "WITHHOLD needs the CU backend, an AG or attention plan, and no other run mode");
@@ -314,7 +328,7 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   }
   rc = device_tables(plan, cx.dev->device, &cx.tab);
   if (rc) return rc;
-  cx.ws = ws_view(ws, plan->plan.num_chunks);
+  cx.ws = ws_view(ws, plan->plan.num_chunks, plan->plan.num_tiles);
   cx.cfg = cfg;
   const uint64_t ns = cfg.timeout_ns ? cfg.timeout_ns : 2000000000ull;
   cx.timeout_ticks = ns / 1000000ull * static_cast<uint64_t>(cx.dev->wall_khz) +
@@ -388,6 +402,8 @@ GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const 
   g.nxcd = cx.dev->num_xcds;
   g.wait_chunks = 1;
   g.copy_blocks = 0;
+  g.trace_tiles = (cx.cfg.flags & SYNC_RUN_TRACE) ? cx.ws.trace_tiles : nullptr;
+  g.trace_chunks = (cx.cfg.flags & SYNC_RUN_TRACE) ? cx.ws.trace_chunks : nullptr;
   return g;
 }
 
@@ -413,6 +429,8 @@ CopyArgs make_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2
   ca.hdr = cx.ws.hdr;
   ca.timeout_ticks = cx.timeout_ticks;
   ca.streaming = cx.cfg.copy_streaming;
+  ca.skip_chunk = (cx.cfg.flags & SYNC_RUN_WITHHOLD) ? cx.cfg.withhold_chunk : -2;
+  ca.trace_chunks = (cx.cfg.flags & SYNC_RUN_TRACE) ? cx.ws.trace_chunks : nullptr;
   return ca;
 }
 
@@ -440,8 +458,6 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
     case SYNC_COPY_CU:
       if (copy_only) {
         r.grid = r.copy_blocks = cx.cfg.copy_cus * wpc;
-      } else if (cx.cfg.flags & SYNC_RUN_WITHHOLD) {
-        r.grid = (d.num_cus - cx.cfg.copy_cus) * wpc;  // waits, but nobody copies
       } else if (compute_only) {
         r.grid = (d.num_cus - cx.cfg.copy_cus) * wpc;
         r.wait = 0;
@@ -481,6 +497,10 @@ int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm
     }
     return SYNC_OK;
   };
+  if (cx.cfg.flags & SYNC_RUN_TRACE) {  // stamps start at zero: "nothing recorded"
+    const int64_t words = (ws_total_bytes(pl.num_chunks, pl.num_tiles) - ws_trace_offset(pl.num_chunks)) / 4;
+    HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(cx.ws.trace_tiles), words, 0u, cs));
+  }
   if (!r.sdma) return timed(cs);
   MaskedPair* mp = nullptr;
   int rc = masked_pair(d, d.num_xcds, &mp);
@@ -571,8 +591,7 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out) {
 
 size_t sync_workspace_size(sync_plan_t plan) {
   if (!plan) return 0;
-  const int32_t C = plan->plan.num_chunks;
-  return static_cast<size_t>(256 + 4 * ws_array_bytes(C) + align_up(static_cast<int64_t>(C) * 4 * kMaxXcd, 256));
+  return static_cast<size_t>(ws_total_bytes(plan->plan.num_chunks, plan->plan.num_tiles));
 }
 
 int sync_workspace_init(sync_plan_t plan, void* ws, void* stream) {
@@ -582,6 +601,44 @@ int sync_workspace_init(sync_plan_t plan, void* ws, void* stream) {
   if (rc) return rc;
   HIP_TRY(launch_fill_u32(static_cast<uint32_t*>(ws), static_cast<int64_t>(sync_workspace_size(plan) / 4), 0u,
                           static_cast<hipStream_t>(stream)));
+  return SYNC_OK;
+}
+
+int sync_trace_export(sync_plan_t plan, const void* ws, void* stream, sync_trace* out) {
+  if (!plan || !ws || !out) return fail(SYNC_EINVAL, "plan, ws and out must be non-NULL");
+  DeviceState* d = nullptr;
+  int rc = current_device_state(&d);
+  if (rc) return rc;
+  const int32_t C = plan->plan.num_chunks, T = plan->plan.num_tiles;
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  const int64_t off = ws_trace_offset(C);
+  const int64_t chunk_off = align_up(static_cast<int64_t>(T) * 32, 256);
+  std::vector<uint64_t> tiles(static_cast<size_t>(T) * 4), chunks(static_cast<size_t>(C) * 2);
+  const char* b = static_cast<const char*>(ws);
+  if (T) HIP_TRY(hipMemcpy(tiles.data(), b + off, tiles.size() * 8, hipMemcpyDeviceToHost));
+  if (C) HIP_TRY(hipMemcpy(chunks.data(), b + off + chunk_off, chunks.size() * 8, hipMemcpyDeviceToHost));
+  uint64_t t0 = ~0ull;
+  for (int32_t t = 0; t < T; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (tiles[4 * t + i]) t0 = std::min(t0, tiles[4 * t + i]);
+  for (uint64_t v : chunks)
+    if (v) t0 = std::min(t0, v);
+  const double ns_per_tick = 1e6 / static_cast<double>(d->wall_khz);
+  auto ns = [&](uint64_t v) -> int64_t {
+    return v ? static_cast<int64_t>(std::llround(static_cast<double>(v - t0) * ns_per_tick)) : -1;
+  };
+  for (int32_t t = 0; t < T; ++t) {
+    const uint64_t* r = &tiles[4 * static_cast<size_t>(t)];
+    if (out->tile_wait_begin) out->tile_wait_begin[t] = ns(r[0]);
+    if (out->tile_wait_end) out->tile_wait_end[t] = ns(r[1]);
+    if (out->tile_end) out->tile_end[t] = ns(r[2]);
+    if (out->tile_xcc) out->tile_xcc[t] = r[0] ? static_cast<int32_t>(r[3] >> 32) : -1;
+    if (out->tile_slot) out->tile_slot[t] = r[0] ? static_cast<int32_t>(r[3] & 0xffffffffu) : -1;
+  }
+  for (int32_t c = 0; c < C; ++c) {
+    if (out->chunk_ready) out->chunk_ready[c] = ns(chunks[2 * c]);
+    if (out->chunk_sent) out->chunk_sent[c] = ns(chunks[2 * c + 1]);
+  }
   return SYNC_OK;
 }
 

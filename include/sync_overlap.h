@@ -173,10 +173,13 @@ enum {
   SYNC_RUN_TIMED = 4,        /* record device events around the call's kernel launch and the
                                 SDMA copies, on the streams they run on; read with
                                 sync_read_timings() */
-  SYNC_RUN_WITHHOLD = 8      /* CU backend, AG and attention (failure-path tests): no chunk is
-                                copied or flagged, so the compute kernel's waits for the
-                                non-resident chunks expire after timeout_ns and the call
-                                reports SYNC_ETIMEOUT through sync_workspace_status */
+  SYNC_RUN_WITHHOLD = 8,     /* CU backend, AG and attention (failure-path tests): chunk
+                                cfg.withhold_chunk (-1: every non-resident chunk) is neither
+                                copied nor flagged, so the waits for it expire after timeout_ns,
+                                exactly the tiles that read it stay unwritten, and the call
+                                reports SYNC_ETIMEOUT naming it through sync_workspace_status */
+  SYNC_RUN_TRACE = 16        /* GEMM calls: record per-tile and per-chunk device wall-clock
+                                stamps in the workspace; read with sync_trace_export() */
 };
 
 typedef struct {
@@ -186,7 +189,8 @@ typedef struct {
   const uint32_t* host_gates; /* HOST_GATED: pinned host words (hipHostMalloc), one per chunk */
   int32_t flags;            /* SYNC_RUN_* bits */
   int32_t copy_streaming;   /* CU backend: 1 = non-temporal loads/stores in the copy role; 0 = plain */
-  int32_t reserved[2];      /* must be zero */
+  int32_t withhold_chunk;   /* SYNC_RUN_WITHHOLD only: the chunk left out, or -1 for all */
+  int32_t reserved;         /* must be zero */
 } sync_copy_cfg;
 
 /* ---- workspace ---------------------------------------------------------- */
@@ -204,6 +208,30 @@ size_t sync_workspace_size(sync_plan_t plan);
  * compute stream with the CU backend, and replaying a captured call is
  * valid. */
 int sync_workspace_init(sync_plan_t plan, void* ws, void* stream);
+
+/* Trace of the last SYNC_RUN_TRACE GEMM call on a workspace (waits for
+ * `stream`).  Caller-owned arrays, any of which may be NULL; times in ns of the
+ * device wall clock, relative to the earliest stamp of the call; -1 where
+ * nothing was recorded (a tile that was skipped, a resident chunk, or a chunk
+ * copied by SDMA).
+ *   tile_wait_begin[T], tile_wait_end[T], tile_end[T]: when the workgroup took
+ *     tile t, when its chunk waits were over (compute starts), and when its
+ *     stores (and RS completion) were issued;
+ *   tile_xcc[T]: XCD that ran the tile; tile_slot[T]: position p in the
+ *     traversal at which it was taken (order[p] == t);
+ *   chunk_ready[C]: AG: the copy role raised the chunk's ready flag; RS: the
+ *     GEMM raised the chunk's done flag;  chunk_sent[C]: RS copy-out done. */
+typedef struct {
+  int64_t* tile_wait_begin;
+  int64_t* tile_wait_end;
+  int64_t* tile_end;
+  int32_t* tile_xcc;
+  int32_t* tile_slot;
+  int64_t* chunk_ready;
+  int64_t* chunk_sent;
+} sync_trace;
+
+int sync_trace_export(sync_plan_t plan, const void* ws, void* stream, sync_trace* out);
 
 /* Synchronises `stream`, then reads the workspace error word.  Returns
  * SYNC_OK, or SYNC_ETIMEOUT with *err_chunk (may be NULL) = the chunk whose

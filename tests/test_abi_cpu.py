@@ -74,6 +74,21 @@ def test_wrong_op_for_plan():
 def test_workspace_size_scales_with_chunks():
     p1 = A.sync_plan(A.make_desc(1, 64, 8, 64, 4, split=1, tile_m=2, tile_n=2))
     p2 = A.sync_plan(A.make_desc(1, 4096, 8, 64, 4, split=256, tile_m=2, tile_n=2))
-    # header + four uint32[C] arrays + uint32[C][16], each padded to 256 bytes
-    assert A.sync_workspace_size(p1) == 256 + 4 * 256 + 256
-    assert A.sync_workspace_size(p2) == 256 + 4 * 4096 + 1024 * 64
+    # header + four uint32[C] arrays + uint32[C][16], then the trace: uint64[T][4] and
+    # uint64[C][2]; each array padded to 256 bytes
+    assert A.sync_workspace_size(p1) == 256 + 4 * 256 + 256 + 128 * 32 + 256
+    assert A.sync_workspace_size(p2) == 256 + 4 * 4096 + 1024 * 64 + 8192 * 32 + 1024 * 16
+
+
+def test_withhold_and_trace_validation():
+    p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 64, 8, 64, 4, split=1, tile_m=128, tile_n=128))
+    bad = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, flags=A.SYNC_RUN_WITHHOLD, withhold_chunk=9)
+    rc = A.lib().sync_ag_gemm(p.handle, ctypes.byref(bad), None, None, None, None, 0, 256, None, None)
+    assert rc == A.SYNC_EINVAL and "withhold_chunk" in A.sync_last_error()
+    sdma = A.make_cfg(A.SYNC_COPY_SDMA, flags=A.SYNC_RUN_WITHHOLD, withhold_chunk=1)
+    rc = A.lib().sync_ag_gemm(p.handle, ctypes.byref(sdma), None, None, None, None, 0, 256, None, None)
+    assert rc == A.SYNC_EINVAL and "WITHHOLD" in A.sync_last_error()
+    pa = A.sync_plan(A.make_desc(A.SYNC_OP_RING_ATTN, 64, 16, 128, 4, heads_q=4, heads_kv=1))
+    tr = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, flags=A.SYNC_RUN_TRACE)
+    rc = A.lib().sync_ring_attn_step(pa.handle, ctypes.byref(tr), *([None] * 9), 1.0, 0, 256, None, None)
+    assert rc == A.SYNC_EINVAL and "TRACE" in A.sync_last_error()

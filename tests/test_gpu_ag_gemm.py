@@ -283,3 +283,80 @@ def test_captured_call_replays():
         torch.cuda.synchronize()
         assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
         assert torch.equal(c, eager[x]), f"replay {rep} differs from the eager call"
+
+
+def test_withholding_one_chunk_leaves_exactly_its_tiles():
+    """Withhold one copied chunk: exactly the tiles that read it stay unwritten
+    (still NaN), every other tile is correct, and the timeout names that chunk."""
+    m, n, k, world, split = 1024, 512, 256, 4, 2
+    a, b = inputs.gemm_operands(m, n, k, 32.0)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, split=split, tile_m=128, tile_n=128))
+    tabs = A.sync_plan_export(plan)
+    victim = int(tabs["arrival"][3])
+    assert not tabs["resident"][victim]
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    a_local = torch.zeros_like(a_peer)
+    for ch in range(tabs["num_chunks"]):
+        if tabs["resident"][ch]:
+            r0, r1 = tabs["chunk_begin"][ch], tabs["chunk_begin"][ch + 1]
+            a_local[r0:r1] = a_peer[r0:r1]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    cfg = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, timeout_ns=2_000_000, flags=A.SYNC_RUN_WITHHOLD,
+                     withhold_chunk=victim)
+    print(f"[ag] withhold chunk {victim}", flush=True)
+    A.sync_ag_gemm(plan, cfg, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_ETIMEOUT and chunk == victim
+    out = c.cpu().numpy()
+    skipped = set(tabs["inv_idx"][tabs["inv_ptr"][victim]:tabs["inv_ptr"][victim + 1]].tolist())
+    tn = tabs["tiles_n"]
+    for t in range(tabs["num_tiles"]):
+        i, j = divmod(t, tn)
+        blk = out[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+        if t in skipped:
+            assert np.isnan(blk).all(), f"tile {t} reads the withheld chunk but was written"
+        else:
+            r = ref[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            assert np.isfinite(blk).all() and np.linalg.norm(blk - r) <= 1e-3 * np.linalg.norm(r), f"tile {t}"
+
+
+@pytest.mark.parametrize("order", [A.SYNC_ORDER_ROW_MAJOR, A.SYNC_ORDER_CHUNK_MAJOR])
+def test_trace_tiles_start_after_their_chunks(order):
+    """Device trace of one call: slot p ran tile order[p]; every tile's compute
+    began after the copy role released each chunk it reads (one device wall
+    clock for all XCDs); stamps are ordered within each tile."""
+    m, n, k, world, split = 2048, 1024, 512, 4, 2
+    a, b = inputs.gemm_operands(m, n, k, 32.0)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, split=split, tile_m=128, tile_n=128,
+                                   tile_order=order))
+    tabs = A.sync_plan_export(plan)
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    a_local = torch.zeros_like(a_peer)
+    for ch in range(tabs["num_chunks"]):
+        if tabs["resident"][ch]:
+            r0, r1 = tabs["chunk_begin"][ch], tabs["chunk_begin"][ch + 1]
+            a_local[r0:r1] = a_peer[r0:r1]
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    cfg = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, flags=A.SYNC_RUN_TRACE)
+    A.sync_ag_gemm(plan, cfg, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+    assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
+    tr = A.sync_trace_export(plan, ws, s)
+    T = tabs["num_tiles"]
+    assert (tr["tile_slot"] >= 0).all()
+    assert np.array_equal(tabs["tile_order"][tr["tile_slot"]], np.arange(T))
+    assert (tr["tile_wait_begin"] <= tr["tile_wait_end"]).all() and (tr["tile_wait_end"] <= tr["tile_end"]).all()
+    assert set(tr["tile_xcc"].tolist()) <= set(range(16))
+    for ch in range(tabs["num_chunks"]):
+        assert (tr["chunk_ready"][ch] < 0) == bool(tabs["resident"][ch])
+    worst = 0
+    for t in range(T):
+        deps = tabs["dep_idx"][tabs["dep_ptr"][t]:tabs["dep_ptr"][t + 1]]
+        ready = [tr["chunk_ready"][ch] for ch in deps if not tabs["resident"][ch]]
+        if ready:
+            worst = min(worst, tr["tile_wait_end"][t] - max(ready))
+    assert worst >= 0, f"a tile started {-worst} ns before a chunk it reads was released"

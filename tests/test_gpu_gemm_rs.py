@@ -133,3 +133,28 @@ def test_full_size_rs_normal(layout):
         sel = rows // (M3 // W3) == s
         assert np.linalg.norm(cn[rows[sel], cols[sel]] - ref[sel]) / np.linalg.norm(ref[sel]) <= 1e-3
     check_staging(cn, st, tabs)
+
+
+def test_trace_done_and_sent_order():
+    """Device trace of an RS call: chunk c's done flag is raised after every
+    tile of c started computing, its copy-out after that, and the copy-out
+    walks the send order."""
+    m, n, k, W = 2048, 1024, 512, 4
+    a, b = inputs.gemm_operands(m, n, k, 16.0)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, split=2, tile_m=128, tile_n=128))
+    tabs = A.sync_plan_export(plan)
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+    staging = torch.empty_like(c)
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, flags=A.SYNC_RUN_TRACE), dev_bits(a), dev_bits(b),
+                   c, A.SYNC_DTYPE_F32, staging, ws, s, None)
+    assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
+    tr = A.sync_trace_export(plan, ws, s)
+    assert (tr["chunk_ready"] >= 0).all() and (tr["chunk_sent"] >= 0).all()
+    assert (tr["chunk_sent"] >= tr["chunk_ready"]).all()
+    sent_in_order = tr["chunk_sent"][tabs["arrival"]]
+    assert (np.diff(sent_in_order) >= 0).all()
+    for ch in range(tabs["num_chunks"]):
+        tiles = tabs["inv_idx"][tabs["inv_ptr"][ch]:tabs["inv_ptr"][ch + 1]]
+        assert tr["chunk_ready"][ch] >= tr["tile_wait_end"][tiles].max()
