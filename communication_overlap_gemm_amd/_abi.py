@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
     "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_gemm_rs", "sync_ring_attn_step",
     "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
+    "sync_autotune", "sync_tune_workspace_size", "sync_tune_forget",
 )
 
 
@@ -82,6 +83,25 @@ class sync_trace(ctypes.Structure):
                 ("tile_slot", _P32), ("chunk_ready", _P64), ("chunk_sent", _P64)]
 
 
+class sync_tune_space(ctypes.Structure):
+    _fields_ = [("splits", _P32), ("n_splits", ctypes.c_int32), ("tiles", _P32), ("n_tiles", ctypes.c_int32),
+                ("orders", _P32), ("n_orders", ctypes.c_int32), ("copy_cus", _P32), ("n_copy_cus", ctypes.c_int32),
+                ("warmup", ctypes.c_int32), ("iters", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
+                ("force", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class sync_tune_buffers(ctypes.Structure):
+    _fields_ = [("a_peer", ctypes.c_void_p), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
+                ("staging", ctypes.c_void_p), ("c_dtype", ctypes.c_int32), ("ws", ctypes.c_void_p),
+                ("stream", ctypes.c_void_p)]
+
+
+class sync_tune_result(ctypes.Structure):
+    _fields_ = [("split", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_order", ctypes.c_int32), ("copy_cus", ctypes.c_int32), ("best_ms", ctypes.c_float),
+                ("candidates_run", ctypes.c_int32), ("candidates_skipped", ctypes.c_int32)]
+
+
 class sync_timing(ctypes.Structure):
     _fields_ = [("kernel_ms", ctypes.c_float), ("copy_ms", ctypes.c_float)]
 
@@ -118,6 +138,11 @@ def lib():
             "sync_get_device_info": (i32, [ctypes.POINTER(sync_device_info)]),
             "sync_read_timings": (i32, [i32, ctypes.POINTER(sync_timing), ctypes.POINTER(i32)]),
             "sync_trace_export": (i32, [vp, vp, vp, ctypes.POINTER(sync_trace)]),
+            "sync_tune_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(sync_plan_desc),
+                                                           ctypes.POINTER(sync_tune_space)]),
+            "sync_autotune": (i32, [ctypes.POINTER(sync_plan_desc), ctypes.POINTER(sync_tune_space),
+                                    ctypes.POINTER(sync_tune_buffers), ctypes.POINTER(sync_tune_result)]),
+            "sync_tune_forget": (None, []),
             "sync_last_error": (ctypes.c_char_p, []),
             "sync_shutdown": (None, []),
         }
@@ -244,6 +269,42 @@ def sync_trace_export(plan: Plan, ws, stream=None) -> dict:
         setattr(t, name, arr.ctypes.data_as(_P64 if arr.dtype == np.int64 else _P32))
     _check(lib().sync_trace_export(plan.handle, _ptr(ws), _stream(stream), ctypes.byref(t)))
     return out
+
+
+def make_tune_space(splits=(1, 2, 4), tiles=((256, 256), (256, 128), (128, 128)),
+                    orders=(SYNC_ORDER_CHUNK_MAJOR,), copy_cus=(16, 32), warmup: int = 0, iters: int = 0,
+                    timeout_ns: int = 0, force: int = 0):
+    """A sync_tune_space plus the arrays it points into (keep the tuple alive while it is used)."""
+    arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.int32).reshape(-1))
+            for x in (splits, tiles, orders, copy_cus)]
+    sp = sync_tune_space()
+    sp.splits, sp.tiles, sp.orders, sp.copy_cus = (a.ctypes.data_as(_P32) for a in arrs)
+    sp.n_splits, sp.n_tiles, sp.n_orders, sp.n_copy_cus = len(arrs[0]), len(arrs[1]) // 2, len(arrs[2]), len(arrs[3])
+    sp.warmup, sp.iters, sp.timeout_ns, sp.force = warmup, iters, timeout_ns, force
+    return sp, arrs
+
+
+def sync_tune_workspace_size(base: sync_plan_desc, space) -> int:
+    sp = space[0] if isinstance(space, tuple) else space
+    return int(lib().sync_tune_workspace_size(ctypes.byref(base), ctypes.byref(sp)))
+
+
+def sync_autotune(base: sync_plan_desc, space, *, a, b, c, ws, c_dtype: int = SYNC_DTYPE_F32, a_peer=None,
+                  staging=None, stream=None) -> dict:
+    """Runs the autotuner (AG: a is a_local, a_peer the peer region; RS: a, staging)."""
+    sp = space[0] if isinstance(space, tuple) else space
+    bufs = sync_tune_buffers()
+    bufs.a_peer, bufs.a, bufs.b, bufs.c, bufs.staging = (_ptr(x) for x in (a_peer, a, b, c, staging))
+    bufs.c_dtype, bufs.ws, bufs.stream = c_dtype, _ptr(ws), _stream(stream)
+    r = sync_tune_result()
+    _check(lib().sync_autotune(ctypes.byref(base), ctypes.byref(sp), ctypes.byref(bufs), ctypes.byref(r)))
+    return {"split": r.split, "tile_m": r.tile_m, "tile_n": r.tile_n, "tile_order": r.tile_order,
+            "copy_cus": r.copy_cus, "best_ms": r.best_ms, "candidates_run": r.candidates_run,
+            "candidates_skipped": r.candidates_skipped}
+
+
+def sync_tune_forget() -> None:
+    lib().sync_tune_forget()
 
 
 def sync_workspace_status(ws, stream=None):

@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsync_overlap.so")
 ARCH = os.environ.get("SYNC_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["kernels/gemm_persistent.hip", "kernels/workspace.hip", "kernels/ring_attn.hip", "runtime.cpp"]
+HIP_SOURCES = ["kernels/gemm_persistent.hip", "kernels/workspace.hip", "kernels/ring_attn.hip", "runtime.cpp",
+               "autotune.cpp"]
 CXX_SOURCES = ["planner.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]

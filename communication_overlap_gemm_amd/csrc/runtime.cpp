@@ -48,6 +48,15 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+}  // namespace
+
+namespace syncov {
+// Sets the thread's last-error message (other translation units of the library).
+int set_error(int code, const std::string& msg) { return fail(code, msg); }
+}  // namespace syncov
+
+namespace {
+
 int hip_fail(hipError_t e, const char* what) {
   g_err = std::string(what) + ": " + hipGetErrorString(e);
   return SYNC_EHIP;

@@ -288,6 +288,62 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
                         float* o, float* m_state, float* l_state, float* lse, float scale,
                         int32_t flags, void* ws, void* compute, void* copy);
 
+/* ---- autotuner ------------------------------------------------------------ */
+/* Picks the fastest overlapped configuration of a GEMM call (AG or RS) by
+ * running it [spec: an autotuner over chunk size, split factor, tile
+ * shape, tile order, copy backend and copy-CU count; SYN-S "Core method":
+ * plans are tuned per workload and the pages leave the tuning cost out].
+ * Every candidate in the cross product of the space's lists is planned from
+ * `base` (its split, tile_m/tile_n, tile_order replaced), run `warmup` times
+ * and then timed over `iters` calls with device events on `bufs->stream`.
+ * Candidates the kernels do not support, or whose calls time out (each call
+ * is bounded by timeout_ns, default 100 ms here), are skipped.  The copy-CU
+ * list applies to the CU backend only; SDMA and HOST_GATED are not tuned.
+ * Results are cached per (device, op, shape, base fields, c_dtype, space) for
+ * the life of the process, and in the text file named by the environment
+ * variable SYNC_TUNE_CACHE when it is set (read on first use, appended after
+ * each tuning); a cached result returns at once with candidates_run = 0
+ * unless `force` is set.  The caller's buffers are overwritten by the runs
+ * (c, staging, the non-resident rows of a_local, the workspace). */
+typedef struct {
+  const int32_t* splits;    int32_t n_splits;   /* split factors */
+  const int32_t* tiles;     int32_t n_tiles;    /* n_tiles pairs (tile_m, tile_n) */
+  const int32_t* orders;    int32_t n_orders;   /* SYNC_ORDER_* */
+  const int32_t* copy_cus;  int32_t n_copy_cus; /* CU backend copy-CU counts */
+  int32_t warmup, iters;   /* per candidate; 0 = 3 and 10 */
+  uint64_t timeout_ns;     /* per-call device wait bound while tuning; 0 = 100 ms */
+  int32_t force;           /* 1 = ignore cached results */
+  int32_t reserved;        /* must be zero */
+} sync_tune_space;
+
+typedef struct {
+  const void* a_peer;  /* AG: bf16 [m][k] peer region; RS: unused */
+  void* a;             /* AG: a_local (resident shard filled); RS: a */
+  const void* b;
+  void* c;
+  void* staging;       /* RS only */
+  int32_t c_dtype;     /* SYNC_DTYPE_* */
+  void* ws;            /* >= sync_tune_workspace_size() bytes, 256-byte aligned */
+  void* stream;        /* compute stream */
+} sync_tune_buffers;
+
+typedef struct {
+  int32_t split, tile_m, tile_n, tile_order, copy_cus;
+  float best_ms;            /* mean call time of the winner */
+  int32_t candidates_run;   /* 0 when served from the cache */
+  int32_t candidates_skipped;
+} sync_tune_result;
+
+/* Workspace bytes that fit every candidate of the space (0 on bad input). */
+size_t sync_tune_workspace_size(const sync_plan_desc* base, const sync_tune_space* space);
+
+int sync_autotune(const sync_plan_desc* base, const sync_tune_space* space, const sync_tune_buffers* bufs,
+                  sync_tune_result* out);
+
+/* Drops the in-process cache of tuning results (the cache file, if any, is
+ * kept and read again on the next sync_autotune). */
+void sync_tune_forget(void);
+
 /* Durations of the most recent SYNC_RUN_TIMED calls on the current device
  * (a ring of 1024), oldest first; waits for those events.  kernel_ms is the
  * call's kernel launch (GEMM or attention; with the CU backend its copy
