@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 M, N, K, WORLD = 8192, 1792, 4096, 8
 DIVISOR = 64.0
 
-BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64)}
+BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64), "colocated": (4, 0)}
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
 PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk"}
@@ -144,6 +144,7 @@ def main():
     t_copy, recs_p = timed_loop(A.make_cfg(backend, cus, flags=A.SYNC_RUN_COPY_ONLY), args.steps, args.warmup)
     # CU backend: the copy-only launch is the copy role alone; SDMA: the copies' span
     copy_only_ms = float(np.mean([r[1] if backend == A.SYNC_COPY_SDMA else r[0] for r in recs_p]))
+    # (co-located: the copy-only launch is every workgroup copying, none computing)
 
     flops = 2.0 * M * N * K
     value = flops / t_ovl / 1e12
@@ -151,7 +152,8 @@ def main():
     copied = sum(int(tabs["chunk_begin"][c + 1] - tabs["chunk_begin"][c]) for c in range(tabs["num_chunks"])
                  if not tabs["resident"][c]) * K * 2
     kname = ("gemm_dma" if args.layout == "nk" else "gemm_persistent") + \
-        f"<{tm},{tn},{args.c_dtype},AG>" + (f" with {cus} copy workgroups" if backend == A.SYNC_COPY_CU else "")
+        f"<{tm},{tn},{args.c_dtype},AG>" + (f" with {cus} copy workgroups" if backend == A.SYNC_COPY_CU else
+                                              " with co-located copy" if backend == A.SYNC_COPY_COLOCATED else "")
     line = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -47,23 +47,37 @@ def device_assembly(source: str = KERNEL) -> str:
             return f.read()
 
 
-def hazards(asm: str, kernel_prefix: str = "_ZN6syncov8gemm_dma") -> tuple[int, list[str]]:
-    """(kernels scanned, hazard descriptions) for kernels whose symbol starts with kernel_prefix."""
-    found: list[str] = []
-    kernels = 0
-    kern = None
-    pending: set[int] = set()
-    in_asm = False
-    for ln, line in enumerate(asm.split("\n"), 1):
+def _kernels(asm: str, kernel_prefix: str):
+    """(name, [lines]) of every kernel whose symbol starts with kernel_prefix."""
+    out, cur, name = [], None, None
+    for line in asm.split("\n"):
         m = re.match(rf"^({kernel_prefix}\w*):", line)
         if m:
-            kern, pending, kernels = m.group(1), set(), kernels + 1
+            name, cur = m.group(1), []
             continue
-        if kern is None:
+        if cur is None:
             continue
         if line.startswith(".Lfunc_end"):
-            kern = None
+            out.append((name, cur))
+            cur = None
             continue
+        cur.append(line)
+    return out
+
+
+def _blocks(lines: list[str]):
+    """Basic blocks [label, [(line index, instruction, is_asm)], successor labels].
+    A block ends at a label, a branch or a terminator; it falls through to the
+    next block unless it ends in an unconditional branch or a terminator."""
+    blocks: list = []
+    in_asm = False
+    counter = 0
+
+    def new_block(label):
+        blocks.append([label, [], []])
+
+    new_block("<entry>")
+    for i, line in enumerate(lines):
         t = line.strip()
         if t.startswith(";;#ASMSTART"):
             in_asm = True
@@ -71,22 +85,76 @@ def hazards(asm: str, kernel_prefix: str = "_ZN6syncov8gemm_dma") -> tuple[int, 
         if t.startswith(";;#ASMEND"):
             in_asm = False
             continue
-        if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
+        m = re.match(r"^(\.L\w+):", t)
+        if m:
+            new_block(m.group(1))
             continue
+        if not t or t.startswith(";") or t.startswith("."):
+            continue
+        blocks[-1][1].append((i, t, in_asm))
+        bm = re.match(r"^s_(c?branch\w*)\s+(\.L\w+)", t)
+        if bm or re.match(r"^(s_endpgm|s_setpc|s_trap)", t):
+            if bm:
+                blocks[-1][2].append(bm.group(2))
+            counter += 1
+            new_block(f"<after {counter}>")
+    for k, blk in enumerate(blocks[:-1]):
+        last = blk[1][-1][1] if blk[1] else ""
+        if not _ends_block(last):
+            blk[2].append(blocks[k + 1][0])  # fall through
+    return blocks
+
+
+def _ends_block(instr: str) -> bool:
+    """Unconditional transfer: no fall-through."""
+    return bool(re.match(r"^(s_branch\s|s_endpgm|s_setpc|s_trap)", instr))
+
+
+def _transfer(block, pending: frozenset, report=None, name=""):
+    pend = set(pending)
+    for i, t, is_asm in block[1]:
         if t.startswith("s_waitcnt"):
             if "lgkmcnt(0)" in t:
-                pending = set()
+                pend = set()
             continue
-        if in_asm and t.startswith("ds_read_b128"):
+        if is_asm and t.startswith("ds_read_b128"):
             dst, addr = t.split(None, 1)[1].split(",", 1)
-            if _regs(addr) & pending:
-                found.append(f"{kern}:{ln}: address register still pending: {t}")
-            pending |= _regs(dst)
+            if report is not None and _regs(addr) & pend:
+                report.append(f"{name}:{i}: address register still pending: {t}")
+            pend |= _regs(dst)
             continue
-        hit = _regs(t) & pending
-        if hit:
-            found.append(f"{kern}:{ln}: {t} touches {sorted(hit)}")
-    return kernels, found
+        hit = _regs(t) & pend
+        if hit and report is not None:
+            report.append(f"{name}:{i}: {t} touches {sorted(hit)}")
+    return frozenset(pend)
+
+
+def hazards(asm: str, kernel_prefix: str = "_ZN6syncov8gemm_dma") -> tuple[int, list[str]]:
+    """(kernels scanned, hazard descriptions) for kernels whose symbol starts with
+    kernel_prefix.  Pending fragment registers are propagated along the
+    control-flow graph (branches and fall-through) to a fixpoint, so a read
+    whose wait sits in another block is followed through the branch."""
+    found: list[str] = []
+    kernels = _kernels(asm, kernel_prefix)
+    for name, lines in kernels:
+        blocks = _blocks(lines)
+        index = {b[0]: k for k, b in enumerate(blocks)}
+        entry = [frozenset() for _ in blocks]
+        work = list(range(len(blocks)))
+        while work:
+            k = work.pop()
+            out = _transfer(blocks[k], entry[k])
+            for succ in blocks[k][2]:
+                j = index.get(succ)
+                if j is None:
+                    continue
+                merged = entry[j] | out
+                if merged != entry[j]:
+                    entry[j] = merged
+                    work.append(j)
+        for k, blk in enumerate(blocks):
+            _transfer(blk, entry[k], found, name)
+    return len(kernels), found
 
 
 def main() -> int:

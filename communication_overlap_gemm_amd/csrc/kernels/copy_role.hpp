@@ -32,7 +32,7 @@ namespace syncov {
 
 typedef uint32_t copy_u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kCopyUnroll = 8;  // 16-byte loads in flight per thread
+constexpr int kCopyUnroll = 16;  // 16-byte loads in flight per thread
 
 // Copies bytes [lo, hi) of src to dst (16-byte granules; both 16-byte
 // aligned), kCopyUnroll loads in flight per thread.  STREAM selects
@@ -59,7 +59,15 @@ __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* _
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) st(v[u], d + g + u * step);
   }
-  for (; g < gend; g += step) st(ld(s + g), d + g);
+  if (g < gend) {  // the remainder, still with every load in flight before the stores
+    copy_u32x4_t v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (g + u * step < gend) v[u] = ld(s + g + u * step);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (g + u * step < gend) st(v[u], d + g + u * step);
+  }
 }
 
 // Publication.  A chunk is complete when every copy workgroup's stores of it
@@ -72,7 +80,10 @@ __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* _
 // writeback per XCD per chunk instead of one per workgroup.  A census at the
 // start tells each workgroup how many copy workgroups share its XCD.
 // `rank` in [0, count) is this workgroup's index among the copy workgroups.
-template <int THREADS>
+// BATCH: copy this workgroup's slice of every chunk, then publish them all
+// with one completion round (co-located copy: nothing computes until its own
+// share is copied, so per-chunk publication would only add latency).
+template <int THREADS, bool BATCH = false>
 __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32_t epoch) {
   __shared__ int32_t s_ok;
   __shared__ uint32_t s_mine;
@@ -98,9 +109,46 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
   __syncthreads();
   const uint32_t mine = s_mine;
   if (mine == 0) return;
+  auto skipped = [&](int32_t c) { return !a.copy_out && (a.resident[c] || a.skip_chunk == c || a.skip_chunk == -1); };
+  if constexpr (BATCH) {
+    int32_t first = -1;  // the batch counts in the slots of its first copied chunk
+    for (int32_t p = 0; p < a.num_chunks; ++p) {
+      const int32_t c = a.arrival[p];
+      if (skipped(c)) continue;
+      if (first < 0) first = c;
+      const int64_t r0 = a.chunk_begin[c], r1 = a.chunk_begin[c + 1];
+      for (int x = 0; x < a.ntensors; ++x) {
+        const int64_t granules = (r1 - r0) * a.row_bytes[x] / 16;
+        const int64_t lo = granules * b / G * 16, hi = granules * (b + 1) / G * 16;
+        copy_range<THREADS, false>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + r0 * a.row_bytes[x], lo, hi);
+      }
+    }
+    if (first < 0) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t* const xp = a.xparts + first * kMaxXcd + xcc;
+      if (add_acq_rel_agent(xp, 1u) + 1u == mine) {
+        st_relaxed_agent(xp, 0u);
+        release_agent();
+        const uint32_t done = add_acq_rel_agent(a.parts + first, mine);
+        if (done + mine == static_cast<uint32_t>(G)) {
+          st_relaxed_agent(a.parts + first, 0u);
+          const uint64_t now = wall_clock64();
+          for (int32_t p = 0; p < a.num_chunks; ++p) {
+            const int32_t c = a.arrival[p];
+            if (skipped(c)) continue;
+            if (a.trace_chunks) a.trace_chunks[2 * c] = now;
+            st_release_agent(a.out_flags + c, epoch);
+          }
+        }
+      }
+    }
+    return;
+  }
   for (int32_t p = 0; p < a.num_chunks; ++p) {
     const int32_t c = a.arrival[p];
-    if (!a.copy_out && (a.resident[c] || a.skip_chunk == c || a.skip_chunk == -1)) continue;
+    if (skipped(c)) continue;
     if (a.copy_out) {
       if (threadIdx.x == 0) {
         const bool ok = wait_flag(a.wait_flags, c, epoch, a.hdr, a.timeout_ticks);

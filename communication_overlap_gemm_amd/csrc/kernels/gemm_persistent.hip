@@ -60,17 +60,21 @@ __device__ __forceinline__ int swz(int row, int slot) { return slot ^ ((row ^ (r
 // strip at a time into its own LDS region (row-major, padded pitch), then
 // reads it back 16 bytes per lane and stores whole rows with buffer stores
 // (rows past M fall outside num_records and are dropped).
-template <int TM, int TN, int CT>
-__device__ __forceinline__ void store_tile_c(const GemmArgs& a, const f32x16_t (&acc)[TM / 64][TN / 64], char* lds,
+// WGM x WGN waves, each owning a (TM/WGM) x (TN/WGN) block; RPP staged rows
+// per pass (32, or 16 when the LDS ring cannot hold every wave's 32-row strip).
+template <int TM, int TN, int CT, int WGM, int WGN, int RPP>
+__device__ __forceinline__ void store_tile_w(const GemmArgs& a,
+                                             const f32x16_t (&acc)[TM / WGM / 32][TN / WGN / 32], char* lds,
                                              int64_t m0, int64_t n0, int rows_valid, int cols_valid, int wave,
                                              int lane) {
-  constexpr int WM = TM / 2, WN = TN / 2, MI = WM / 32, NI = WN / 32;
+  constexpr int WM = TM / WGM, WN = TN / WGN, MI = WM / 32, NI = WN / 32;
   constexpr int ES = CT == 0 ? 4 : 2;
   constexpr int SP = WN + 32 / ES;   // staged strip pitch (elements), +32 B
   constexpr int LPR = WN * ES / 16;  // lanes per staged row
   constexpr int RPI = 64 / LPR;      // rows per store instruction
-  const int wm = wave >> 1, wn = wave & 1;
-  char* const stage = lds + wave * 32 * SP * ES;
+  static_assert(RPP == 32 || RPP == 16, "rows per pass");
+  const int wm = wave / WGN, wn = wave % WGN;
+  char* const stage = lds + wave * RPP * SP * ES;
   const int rr = lane / LPR, rc = (lane % LPR) * (16 / ES);
   const bool col_ok = wn * WN + rc < cols_valid;
   const int64_t N = a.N;
@@ -78,30 +82,42 @@ __device__ __forceinline__ void store_tile_c(const GemmArgs& a, const f32x16_t (
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+    for (int h = 0; h < 32 / RPP; ++h) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3), c = j * 32 + (lane & 31);
-        if constexpr (CT == 0)
-          *reinterpret_cast<float*>(stage + (r * SP + c) * ES) = acc[i][j][e];
-        else
-          *reinterpret_cast<uint16_t*>(stage + (r * SP + c) * ES) = f32_to_bf16_rne(acc[i][j][e]);
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3) - h * RPP, c = j * 32 + (lane & 31);
+          if (RPP == 32 || (e >> 3) == h) {  // accumulator rows 0-15 hold e < 8, rows 16-31 e >= 8
+            if constexpr (CT == 0)
+              *reinterpret_cast<float*>(stage + (r * SP + c) * ES) = acc[i][j][e];
+            else
+              *reinterpret_cast<uint16_t*>(stage + (r * SP + c) * ES) = f32_to_bf16_rne(acc[i][j][e]);
+          }
+        }
+      __syncthreads();
+      const int strip = wm * WM + i * 32 + h * RPP;  // first tile row of this pass
+      const int rows_left = rows_valid - strip;
+      const __amdgpu_buffer_rsrc_t cs =
+          make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
+                    rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
+#pragma unroll
+      for (int it = 0; it < RPP / RPI; ++it) {
+        const int r = it * RPI + rr;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (r * SP + rc) * ES);
+        if (col_ok)
+          __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
       }
-    __syncthreads();
-    const int strip = wm * WM + i * 32;  // first tile row of this strip
-    const int rows_left = rows_valid - strip;
-    const __amdgpu_buffer_rsrc_t cs =
-        make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
-                  rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int r = it * RPI + rr;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (r * SP + rc) * ES);
-      if (col_ok)
-        __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
+      __syncthreads();
     }
-    __syncthreads();
   }
+}
+
+template <int TM, int TN, int CT>
+__device__ __forceinline__ void store_tile_c(const GemmArgs& a, const f32x16_t (&acc)[TM / 64][TN / 64], char* lds,
+                                             int64_t m0, int64_t n0, int rows_valid, int cols_valid, int wave,
+                                             int lane) {
+  store_tile_w<TM, TN, CT, 2, 2, 32>(a, acc, lds, m0, n0, rows_valid, cols_valid, wave, lane);
 }
 
 // GEMM-RS completion of tile t: every wave's C stores have reached the L2;
@@ -183,6 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     return;
   }
   const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
+  if (a.colocated) copy_role<kThreads, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];
@@ -399,9 +416,10 @@ __device__ __forceinline__ int rswz(int row, int slot) {
     return slot ^ ((row & 7) ^ ((row >> 3) & 1));
 }
 
-template <int TM, int TN, int CT, bool RS, int TK, int NS>
-__global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
-  constexpr int WM = TM / 2, WN = TN / 2;
+template <int TM, int TN, int CT, bool RS, int TK, int NS, int WGM, int WGN, bool SPREAD_LOADS = false>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
+  constexpr int NW = WGM * WGN, THREADS = 64 * NW;  // waves, as a WGM x WGN grid over the tile
+  constexpr int WM = TM / WGM, WN = TN / WGN;
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int ROWB = TK * 2;                      // bytes per LDS row
   constexpr int SLOTS = ROWB / 16;
@@ -409,23 +427,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
   constexpr int KS = TK / 16;                       // k16 steps per stage
   constexpr int A_BYTES = TM * ROWB, B_BYTES = TN * ROWB;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LD = A_BYTES / 1024 / 4;          // 1 KB wave loads per wave per stage
-  constexpr int B_LD = B_BYTES / 1024 / 4;
+  constexpr int A_LD = A_BYTES / 1024 / NW;         // 1 KB wave loads per wave per stage
+  constexpr int B_LD = B_BYTES / 1024 / NW;
   constexpr int LPW = A_LD + B_LD;                  // loads per wave per stage
   constexpr int NFRAG = MI + NI;                    // 16-byte reads per k16 step: A frags, then B frags
-  static_assert(TM % 64 == 0 && TN % 64 == 0 && A_LD >= 1 && B_LD >= 1, "tile");
+  constexpr bool SPREAD = SPREAD_LOADS && NS >= 3;  // stage loads interleaved with the MFMAs (see the main loop)
+  constexpr int PER = (LPW + KS - 1) / KS;          // SPREAD: loads per k16 step
+  constexpr int GAP = (MI * NI) / PER > 0 ? (MI * NI) / PER : 1;  // SPREAD: MFMAs between loads
+  static_assert(!SPREAD || (LPW % KS == 0 && PER <= MI * NI), "spread loads over the k16 steps");
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && A_LD >= 1 && B_LD >= 1 && A_LD * NW * 1024 == A_BYTES &&
+                B_LD * NW * 1024 == B_BYTES, "tile");
   static_assert((SLOTS == 4 || SLOTS == 8) && KS % 2 == 0, "stage depth");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring");
   static_assert(NFRAG <= MI * NI, "one read per MFMA slot");
   constexpr int ES = CT == 0 ? 4 : 2;
-  static_assert(4 * 32 * (WN + 32 / ES) * ES <= NS * STAGE, "epilogue staging must fit the LDS ring");
+  constexpr int RPP = NW * 32 * (WN + 32 / ES) * ES <= NS * STAGE ? 32 : 16;  // epilogue rows per pass
+  static_assert(NW * RPP * (WN + 32 / ES) * ES <= NS * STAGE, "epilogue staging must fit the LDS ring");
 
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
   __shared__ int32_t s_skip;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const uint32_t epoch = call_epoch(a.hdr);
   const int64_t M = a.M, N = a.N, K = a.K;
   const int nk = static_cast<int>(K / TK);
@@ -450,11 +474,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
   for (int kk = 0; kk < KS; ++kk) frag_off[kk] = frow * ROWB + rswz<SLOTS>(frow, kk * 2 + (lane >> 5)) * 16;
 
   if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
-    copy_role<kThreads>(a.copy, blockIdx.x, a.copy_blocks, epoch);
+    copy_role<THREADS>(a.copy, blockIdx.x, a.copy_blocks, epoch);
     end_call(a.hdr, epoch, a.cnt);
     return;
   }
   const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
+  if (a.colocated) copy_role<THREADS, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];
@@ -515,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
 
     __syncthreads();  // the previous tile's epilogue is done with the LDS
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < (SPREAD ? NS - 1 : NS); ++s)
       if (s < nk) issue(s);
 
     const uint32_t ring = lds_addr(smem);
@@ -524,46 +549,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
       return f < MI ? lds_read_b128(off + (wm * WM + f * 32) * ROWB)
                     : lds_read_b128(off + A_BYTES + (wn * WN + (f - MI) * 32) * ROWB);
     };
-    // MFMAs on one fragment set, interleaved with the reads of the next set.
-    // The reads are unconditional: a read whose result the compiler might
-    // discard would let it emit select/copy code on registers that an
-    // in-flight asm read is still going to write.
-    auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk) {
+    // One of the LPW 1 KB loads of stage `stage` (A loads first, then B).  A
+    // stage past the last one gets a zero-length buffer (nothing is read; its
+    // slot is free), so the load needs no branch.
+    auto dma_one = [&](int stage, int idx) {
+      char* st = smem + (stage % NS) * STAGE;
+      const int64_t k0 = static_cast<int64_t>(stage < nk ? stage : 0) * TK;
+      if (idx < A_LD) {
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(a_tile + k0, stage < nk ? static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2 : 0);
+        dma_load_16(ra, st + (wave * A_LD + idx) * 1024, a_off[idx]);
+      } else {
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(b_tile + k0, stage < nk ? static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2 : 0);
+        dma_load_16(rb, st + A_BYTES + (wave * B_LD + idx - A_LD) * 1024, b_off[idx - A_LD]);
+      }
+    };
+    // MFMAs on one fragment set, interleaved with the reads of the next set
+    // and (SPREAD) with part `part` of stage `dstage`'s loads.  The reads are
+    // unconditional: a read whose result the compiler might discard would let
+    // it emit select/copy code on registers that an in-flight asm read is
+    // still going to write.
+    auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk, int dstage, int part) {
 #pragma unroll
       for (int x = 0; x < MI * NI; ++x) {
         const int i = x / NI, j = x % NI;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], cur[MI + j], acc[i][j], 0, 0, 0);
         if (x < NFRAG) nxt[x] = read_frag(nst, nkk, x);
+        if constexpr (SPREAD) {
+          if (x % GAP == GAP - 1 && x / GAP < PER) dma_one(dstage, part * PER + x / GAP);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_lgkmcnt<0>();
       __builtin_amdgcn_sched_barrier(0);
     };
 
+    if constexpr (SPREAD) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) dma_one(NS - 1, i);  // part 0 of stage NS - 1 (zero-length past the end)
+    }
     bf16x8_t fp[NFRAG], fq[NFRAG];
     landed(0);
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) fp[f] = read_frag(ring, 0, f);
     wait_lgkmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
+    // SPREAD: the loads of stage kt + NS (into stage kt's slot, free once
+    // stage kt + 1 has landed) are spread over the last k16 step of stage kt
+    // (part 0) and the first KS - 1 steps of stage kt + 1 (parts 1..KS-1), one
+    // load every GAP MFMAs, so no wave stalls on a burst of loads.
+    // Loads of stages past the last are zero-length (see dma_one).  With
+    // SPREAD the prologue issued part 0 of stage NS - 1, so every stage's
+    // first steps carry parts 1.. of stage kt - 1 + NS.
     for (int kt = 0; kt < nk; ++kt) {
       const uint32_t st = ring + (kt % NS) * STAGE;
 #pragma unroll
       for (int kk = 0; kk < KS - 1; kk += 2) {
-        mma(fp, fq, st, kk + 1);
-        if (kk + 2 < KS) mma(fq, fp, st, kk + 2);
+        mma(fp, fq, st, kk + 1, kt - 1 + NS, kk + 1);
+        if (kk + 2 < KS) mma(fq, fp, st, kk + 2, kt - 1 + NS, kk + 2);
       }
       // last k16 step of the stage: its MFMAs read fq; the next stage's first
       // step is read into fp once that stage has landed (after the last
       // stage, a read of an idle slot whose result goes unused)
       if (kt + 1 < nk) {
         landed(kt + 1);
-        if (kt + NS < nk) issue(kt + NS);  // into stage kt's slot, free now
+        if constexpr (!SPREAD) {
+          if (kt + NS < nk) issue(kt + NS);  // into stage kt's slot, free now
+        }
       }
-      mma(fq, fp, ring + ((kt + 1) % NS) * STAGE, 0);
+      mma(fq, fp, ring + ((kt + 1) % NS) * STAGE, 0, kt + NS, 0);
     }
+    if constexpr (SPREAD) wait_vmcnt<0>();  // zero-length loads of the last steps have landed too
     __syncthreads();  // every wave is done reading the ring before the epilogue reuses it
-    store_tile_c<TM, TN, CT>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane);
+    store_tile_w<TM, TN, CT, WGM, WGN, RPP>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane);
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
     if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
   }
@@ -572,21 +631,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma(GemmArgs a) {
 
 // Host-side launcher: picks the template instance; hipErrorInvalidValue for a
 // variant that does not exist.
-// K per stage and ring depth of the direct-to-LDS GEMM, per tile: 64-deep
-// stages read whole 128-byte lines per row; the ring takes what the LDS
-// holds at the tile's workgroups per CU (128x128 runs two per CU).
-template <int TM, int TN> struct DmaShape { static constexpr int TK = 64, NS = 2; };
-template <> struct DmaShape<256, 128> { static constexpr int TK = 64, NS = 3; };
+// K per stage, ring depth and wave grid of the direct-to-LDS GEMM, per tile:
+// 64-deep stages read whole 128-byte lines per row; the ring takes what the
+// LDS holds at the tile's workgroups per CU (128x128 runs two per CU); the
+// 256x256 tile runs eight waves, two per SIMD, so that one wave's waits are
+// covered by the other's MFMAs (measured 124 us against 137 us with four
+// waves on 8192x1792x4096).  Spreading the stage loads between the MFMAs
+// (SpreadLoads) needs a ring of three or more slots and measured slower on
+// this tile (TK=32, four slots: 132 us), so it is off.
+template <int TM, int TN> struct DmaShape { static constexpr int TK = 64, NS = 2, WGM = 2, WGN = 2; };
+template <> struct DmaShape<256, 128> { static constexpr int TK = 64, NS = 3, WGM = 2, WGN = 2; };
+template <> struct DmaShape<256, 256> { static constexpr int TK = 64, NS = 2, WGM = 2, WGN = 4; };
 
 hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid,
                        hipStream_t stream) {
 #define SYNC_GEMM_DMA_CASE(TM_, TN_, CT_)                                                                \
   if (tm == TM_ && tn == TN_ && b_layout == 1 && c_dtype == CT_) {                                       \
-    constexpr int TK_ = DmaShape<TM_, TN_>::TK, NS_ = DmaShape<TM_, TN_>::NS;                            \
+    using S_ = DmaShape<TM_, TN_>;                                                                       \
+    const dim3 block(64 * S_::WGM * S_::WGN);                                                           \
     if (rs)                                                                                              \
-      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, true, TK_, NS_>), dim3(grid), dim3(kThreads), 0, stream, a); \
+      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, true, S_::TK, S_::NS, S_::WGM, S_::WGN>), dim3(grid), block, 0, \
+                         stream, a);                                                                     \
     else                                                                                                 \
-      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, false, TK_, NS_>), dim3(grid), dim3(kThreads), 0, stream, a); \
+      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, false, S_::TK, S_::NS, S_::WGM, S_::WGN>), dim3(grid), block, 0, \
+                         stream, a);                                                                     \
     return hipGetLastError();                                                                            \
   }
   SYNC_GEMM_DMA_CASE(256, 256, 0)

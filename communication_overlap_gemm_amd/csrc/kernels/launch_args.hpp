@@ -57,6 +57,7 @@ struct GemmArgs {
   int32_t nxcd;             // XCDs (for the workgroup -> slot remap)
   int32_t wait_chunks;      // AG: 0 = every chunk is in place (compute-only)
   int32_t copy_blocks;
+  int32_t colocated;        // AG: every compute workgroup first copies its share of each chunk
   uint64_t* trace_tiles;    // SYNC_RUN_TRACE: per tile {wait begin, wait end, end, xcc<<32 | slot}, or null
   uint64_t* trace_chunks;   // SYNC_RUN_TRACE: per chunk {ready/done, sent}, or null
   CopyArgs copy;
@@ -86,6 +87,7 @@ struct AttnArgs {
   int32_t nxcd;
   int32_t wait_chunks;
   int32_t copy_blocks;
+  int32_t colocated;
   CopyArgs copy;
 };
 

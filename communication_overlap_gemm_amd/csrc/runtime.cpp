@@ -315,7 +315,9 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   if (cfg_in) cfg = *cfg_in;
   if (cfg.reserved) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
-  if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_HOST_GATED) return fail(SYNC_EINVAL, "bad backend");
+  if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
+  if (cfg.backend == SYNC_COPY_COLOCATED && op == SYNC_OP_GEMM_RS)
+    return fail(SYNC_EUNSUPPORTED, "GEMM-RS copy-out runs on dedicated CUs (CU backend) or not at all (PRESET)");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
     return fail(SYNC_EINVAL, "unknown cfg.flags bits");
@@ -448,6 +450,8 @@ struct Roles {
   int grid = 0;         // workgroups of the launch (0: no compute launch)
   int copy_blocks = 0;  // leading workgroups that run the copy role
   int wait = 1;         // compute waits for non-resident chunks
+  int colocated = 0;    // every compute workgroup copies its share first
+  bool no_compute = false;  // co-located copy-only: the copy phase alone
   bool sdma = false;    // copy-in on the SDMA engine beside the launch
 };
 
@@ -474,6 +478,16 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
         r.grid = d.num_cus * wpc;
         r.copy_blocks = cx.cfg.copy_cus * wpc;
       }
+      break;
+    case SYNC_COPY_COLOCATED:
+      r.grid = d.num_cus * wpc;
+      if (copy_only) {
+        r.colocated = 1;  // the copy phase of every workgroup, no tiles after it
+        r.no_compute = true;
+      } else if (compute_only)
+        r.wait = 0;
+      else
+        r.colocated = 1;
       break;
     default:  // SDMA, HOST_GATED
       if (compute_only) {
@@ -689,6 +703,8 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     g.copy_blocks = rr.copy_blocks;
                     g.wait_chunks = rr.wait;
+                    g.colocated = rr.colocated;
+                    if (rr.no_compute) g.num_tiles = 0;
                     HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, false, rr.grid,
                                         st));
                     return SYNC_OK;
@@ -796,6 +812,8 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
                   [&](hipStream_t st, const Roles& rr) -> int {
                     at.copy_blocks = rr.copy_blocks;
                     at.wait_chunks = rr.wait;
+                    at.colocated = rr.colocated;
+                    if (rr.no_compute) at.sq = 0;
                     HIP_TRY(launch_ring_attn(at, rr.grid, st));
                     return SYNC_OK;
                   });

@@ -162,8 +162,13 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *               workgroup.
  *   HOST_GATED  as SDMA, but chunk c's copy first waits until the host word
  *               host_gates[c] becomes non-zero (tests: delayed or withheld
- *               chunks) */
-enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOST_GATED = 3 };
+ *               chunks)
+ *   COLOCATED   AG and attention: one launch on `compute` in which every
+ *               compute workgroup first copies its share of each chunk, in
+ *               arrival order (the flags are raised as chunks complete), and
+ *               then computes; no CUs are set aside [SYN-S Fig. 7: load/store
+ *               by the compute SMs themselves]. */
+enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOST_GATED = 3, SYNC_COPY_COLOCATED = 4 };
 
 /* mode bits for sync_copy_cfg.flags */
 enum {

@@ -76,13 +76,23 @@ def test_tiny_sdma_orders(tiny, order):
     assert np.array_equal(a_local, a)  # every peer chunk was staged in
 
 
+@pytest.mark.parametrize("split,tile", [(1, (128, 128)), (3, (256, 128)), (8, (256, 256))])
+def test_tiny_colocated_stages_everything(tiny, split, tile):
+    """Co-located backend: the compute workgroups themselves stage every peer
+    chunk, then compute."""
+    m, n, k, a, b, ref = tiny
+    out, a_local = run_ag(m, n, k, 4, a, b, split=split, tile=tile, backend=A.SYNC_COPY_COLOCATED)
+    check_f32(out, ref, 4)
+    assert np.array_equal(a_local, a)
+
+
 def test_tiny_bitwise_invariant_across_plans(tiny):
     m, n, k, a, b, ref = tiny
     base, _ = run_ag(m, n, k, 4, a, b, backend=A.SYNC_COPY_PRESET)
     check_f32(base, ref, 4)
     for kw in (dict(order=A.SYNC_ORDER_ROW_MAJOR), dict(order=A.SYNC_ORDER_SWIZZLED, split=3),
                dict(split=2, backend=A.SYNC_COPY_CU, copy_cus=8), dict(backend=A.SYNC_COPY_CU, copy_cus=32),
-               dict(split=64)):
+               dict(split=64), dict(split=4, backend=A.SYNC_COPY_COLOCATED)):
         out, _ = run_ag(m, n, k, 4, a, b, **kw)
         assert np.array_equal(out.view(np.uint32), base.view(np.uint32)), kw
 
@@ -180,7 +190,7 @@ def test_full_size_exact_small_integers(layout):
 
 @pytest.mark.parametrize("backend,cus,split", [
     pytest.param(A.SYNC_COPY_SDMA, 0, 1, marks=pytest.mark.skip(reason=SDMA_LIMIT)), (A.SYNC_COPY_CU, 32, 4),
-                                              (A.SYNC_COPY_CU, 16, 2), (A.SYNC_COPY_PRESET, 0, 1)])
+    (A.SYNC_COPY_CU, 16, 2), (A.SYNC_COPY_PRESET, 0, 1), (A.SYNC_COPY_COLOCATED, 0, 1)])
 @pytest.mark.parametrize("layout", ["kn", "nk"])
 def test_full_size_normal(backend, cus, split, layout):
     a, b = inputs.gemm_operands(M2, N2, K2, 64.0, b_layout=layout)

@@ -68,7 +68,7 @@ def check(o, lse, ref_o, ref_lse):
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (8, 4), (16, 2)])
-@pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_PRESET, 0), (A.SYNC_COPY_CU, 8)])
+@pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_PRESET, 0), (A.SYNC_COPY_CU, 8), (A.SYNC_COPY_COLOCATED, 0)])
 def test_small_heads_and_backends(hq, hkv, backend, cus):
     sq, W, n = 256, 4, 128
     q, k, v = inputs.attention_operands(sq, hq, W * n, hkv, D)

@@ -2,9 +2,9 @@
 
 The direct-to-LDS GEMM issues its fragment reads as inline asm and waits for
 them explicitly; the check fails if any compiler-generated instruction touches
-a fragment register while its LDS read may still be in flight.  A kernel
-variant with a runtime-conditional read (which makes the compiler emit select
-code on those registers) is planted to show that the check catches the
+a fragment register while its LDS read may still be in flight, following
+branches through the control-flow graph.  A kernel variant that uses a
+fragment before its wait is planted to show that the check catches the
 hazard.
 """
 import os
@@ -29,25 +29,25 @@ def test_no_pending_fragment_register_is_touched(asm):
     assert not found, "\n".join(found[:20])
 
 
-def test_check_catches_conditional_reads(tmp_path):
+def test_check_catches_a_use_before_the_wait(tmp_path):
+    """Plant an instruction that reads a just-requested fragment register
+    before the lgkmcnt wait (a VALU use of nxt[0]); the check must flag it."""
     with open(asm_check.KERNEL) as f:
         src = f.read()
-    edits = [
-        ("if (x < NFRAG) nxt[x] = read_frag(nst, nkk, x);",
-         "if (x < NFRAG && (nkk != 0 || live)) nxt[x] = read_frag(nst, nkk, x);"),
-        ("auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk) {",
-         "auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk, bool live = true) {"),
-        ("mma(fq, fp, ring + ((kt + 1) % NS) * STAGE, 0);", "mma(fq, fp, ring + ((kt + 1) % NS) * STAGE, 0, kt + 1 < nk);"),
-    ]
-    bad = src
-    for old, new in edits:
-        assert old in bad, "kernel text changed: update the planted variant"
-        bad = bad.replace(old, new)
+    old = """      wait_lgkmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+    };"""
+    new = """      acc[0][0][0] += static_cast<float>(nxt[0][0]);
+      wait_lgkmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+    };"""
+    assert src.count(old) == 1, "kernel text changed: update the planted variant"
+    bad = src.replace(old, new)
     kdir = os.path.dirname(asm_check.KERNEL)
     for name in os.listdir(kdir):
         if name.endswith(".hpp"):
             shutil.copy(os.path.join(kdir, name), tmp_path / name)
     path = tmp_path / "gemm_persistent.hip"
     path.write_text(bad)
-    _, found = asm_check.hazards(asm_check.device_assembly(str(path)))
-    assert found
+    n, found = asm_check.hazards(asm_check.device_assembly(str(path)))
+    assert n >= 12 and len(found) >= n  # at least one per kernel
