@@ -71,44 +71,19 @@ __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* _
 }
 
 // Publication.  A chunk is complete when every copy workgroup's stores of it
-// are visible device-wide.  Each workgroup first drains its stores into its
-// XCD's L2 (workgroup-scope release = wait for the stores), then counts
-// itself in a per-(chunk, XCD) counter; the last workgroup of each XCD writes
-// that L2 back with one agent-scope release (which covers the other
-// workgroups' lines in the same L2) and adds the XCD's workgroups to the
-// chunk's total; whoever completes the total raises the flag.  One L2
-// writeback per XCD per chunk instead of one per workgroup.  A census at the
-// start tells each workgroup how many copy workgroups share its XCD.
-// `rank` in [0, count) is this workgroup's index among the copy workgroups.
+// are visible device-wide.  Each workgroup drains its stores into its XCD's L2
+// (workgroup-scope release = wait for the stores), writes that L2 back with an
+// agent-scope release, and counts itself in the chunk's counting tree; the
+// workgroup that completes the count raises the flag.  No workgroup waits for
+// another.  `rank` in [0, count) is this workgroup's index among the copy
+// workgroups.
 // BATCH: copy this workgroup's slice of every chunk, then publish them all
 // with one completion round (co-located copy: nothing computes until its own
 // share is copied, so per-chunk publication would only add latency).
 template <int THREADS, bool BATCH = false>
 __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32_t epoch) {
   __shared__ int32_t s_ok;
-  __shared__ uint32_t s_mine;
   const int64_t G = count, b = rank;
-  const int xcc = xcc_id();
-  if (threadIdx.x == 0) {
-    add_acq_rel_agent(a.hdr + WS_CENSUS + xcc, 1u);
-    add_acq_rel_agent(a.hdr + WS_CENSUS_TOTAL, 1u);
-    // the copy workgroups are the first of the grid, all resident at once, so
-    // the census completes; the wait is still bounded
-    const uint64_t t0 = wall_clock64();
-    bool ok = true;
-    while (ld_relaxed_agent(a.hdr + WS_CENSUS_TOTAL) < static_cast<uint32_t>(G)) {
-      __builtin_amdgcn_s_sleep(1);
-      if (wall_clock64() - t0 > a.timeout_ticks) {
-        record_timeout(a.hdr, -1);
-        ok = false;
-        break;
-      }
-    }
-    s_mine = ok ? ld_relaxed_agent(a.hdr + WS_CENSUS + xcc) : 0u;
-  }
-  __syncthreads();
-  const uint32_t mine = s_mine;
-  if (mine == 0) return;
   auto skipped = [&](int32_t c) { return !a.copy_out && (a.resident[c] || a.skip_chunk == c || a.skip_chunk == -1); };
   if constexpr (BATCH) {
     int32_t first = -1;  // the batch counts in the slots of its first copied chunk
@@ -127,20 +102,14 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (threadIdx.x == 0) {
-      uint32_t* const xp = a.xparts + first * kMaxXcd + xcc;
-      if (add_acq_rel_agent(xp, 1u) + 1u == mine) {
-        st_relaxed_agent(xp, 0u);
-        release_agent();
-        const uint32_t done = add_acq_rel_agent(a.parts + first, mine);
-        if (done + mine == static_cast<uint32_t>(G)) {
-          st_relaxed_agent(a.parts + first, 0u);
-          const uint64_t now = wall_clock64();
-          for (int32_t p = 0; p < a.num_chunks; ++p) {
-            const int32_t c = a.arrival[p];
-            if (skipped(c)) continue;
-            if (a.trace_chunks) a.trace_chunks[2 * c] = now;
-            st_release_agent(a.out_flags + c, epoch);
-          }
+      release_agent();
+      if (tree_count(a.xparts + first * kMaxXcd, a.parts + first, rank, count)) {
+        const uint64_t now = wall_clock64();
+        for (int32_t p = 0; p < a.num_chunks; ++p) {
+          const int32_t c = a.arrival[p];
+          if (skipped(c)) continue;
+          if (a.trace_chunks) a.trace_chunks[2 * c] = now;
+          st_release_agent(a.out_flags + c, epoch);
         }
       }
     }
@@ -174,17 +143,10 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores have reached the L2
     __syncthreads();
     if (threadIdx.x == 0) {
-      uint32_t* const xp = a.xparts + c * kMaxXcd + xcc;
-      const uint32_t old = add_acq_rel_agent(xp, 1u);
-      if (old + 1u == mine) {
-        st_relaxed_agent(xp, 0u);  // every workgroup of this XCD has counted: ready for the next call
-        release_agent();  // write this XCD's L2 back: every workgroup of this XCD has stored
-        const uint32_t done = add_acq_rel_agent(a.parts + c, mine);
-        if (done + mine == static_cast<uint32_t>(G)) {
-          st_relaxed_agent(a.parts + c, 0u);
-          if (a.trace_chunks) a.trace_chunks[2 * c + (a.copy_out ? 1 : 0)] = wall_clock64();
-          st_release_agent(a.out_flags + c, epoch);
-        }
+      release_agent();  // write this XCD's L2 back
+      if (tree_count(a.xparts + c * kMaxXcd, a.parts + c, rank, count)) {
+        if (a.trace_chunks) a.trace_chunks[2 * c + (a.copy_out ? 1 : 0)] = wall_clock64();
+        st_release_agent(a.out_flags + c, epoch);
       }
     }
   }

@@ -29,12 +29,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // Workspace header words (uint32 index).  The flag and counter arrays follow
 // at offsets the host computes from the plan's chunk count.
 enum : int {
-  WS_EPOCH = 0,         // epoch of the last completed call
-  WS_ERR_CODE = 1,      // 0 = fine, else ERR_* below (sticky until re-initialisation)
-  WS_ERR_CHUNK = 2,     // chunk whose wait expired first
-  WS_EXIT = 3,          // workgroups of the running call that have finished
-  WS_CENSUS_TOTAL = 4,  // copy role: workgroups that have started
-  WS_CENSUS = 16,       // copy role: workgroups started per XCD (16 slots)
+  WS_EPOCH = 0,       // epoch of the last completed call
+  WS_ERR_CODE = 1,    // 0 = fine, else ERR_* below (sticky until re-initialisation)
+  WS_ERR_CHUNK = 2,   // chunk whose wait expired first
+  WS_EXIT = 3,        // finished groups of workgroups of the running call (tree level 2)
+  WS_EXIT_GROUP = 16, // finished workgroups per group of kTreeFan (tree level 1, 16 slots)
   WS_HEADER_WORDS = 64
 };
 constexpr int kMaxXcd = 16;
@@ -76,12 +75,27 @@ __device__ __forceinline__ void record_timeout(uint32_t* hdr, int32_t chunk) {
 // the wall-clock limit passes or another wait has already recorded an error
 // (so that every waiter on a withheld chunk gives up promptly).  No acquire
 // here: the caller performs one after all its waits succeed.
+// Polls back off exponentially (64 to 1024 cycles between loads): many
+// waiters on one flag would otherwise flood its memory channel and slow the
+// producers' stores and counters on it.
+__device__ __forceinline__ void backoff_sleep(int& n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_sleep(1); break;
+    case 1: __builtin_amdgcn_s_sleep(2); break;
+    case 2: __builtin_amdgcn_s_sleep(4); break;
+    case 3: __builtin_amdgcn_s_sleep(8); break;
+    default: __builtin_amdgcn_s_sleep(16); break;
+  }
+  if (n < 4) ++n;
+}
+
 __device__ __forceinline__ bool wait_flag(const uint32_t* flags, int32_t c, uint32_t epoch, uint32_t* hdr,
                                           uint64_t timeout_ticks) {
   if (epoch_reached(ld_relaxed_agent(flags + c), epoch)) return true;
   const uint64_t t0 = wall_clock64();
+  int b = 0;
   for (;;) {
-    __builtin_amdgcn_s_sleep(2);
+    backoff_sleep(b);
     if (epoch_reached(ld_relaxed_agent(flags + c), epoch)) return true;
     if (ld_relaxed_agent(hdr + WS_ERR_CODE) != 0) return false;
     if (wall_clock64() - t0 > timeout_ticks) {
@@ -103,6 +117,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Counting tree.  Many workgroups incrementing one word serialise on it; a
+// two-level tree keyed by the caller's rank (groups of `fan` workgroups, sizes
+// known from the count alone) keeps at most `fan` atomics on any word (16 for
+// up to 256 workgroups).  One lane per workgroup calls it after its own
+// release; it returns true for exactly one caller, the one that completes the
+// count, after clearing the words for the next use.  level1 holds up to 16
+// words.
+__device__ __forceinline__ bool tree_count(uint32_t* level1, uint32_t* level2, int32_t rank, int32_t count) {
+  const int32_t fan = count > 256 ? (count + 15) / 16 : 16;
+  const int32_t g = rank / fan, groups = (count + fan - 1) / fan;
+  const uint32_t in_group = static_cast<uint32_t>(count - g * fan < fan ? count - g * fan : fan);
+  if (add_acq_rel_agent(level1 + g, 1u) + 1u != in_group) return false;
+  st_relaxed_agent(level1 + g, 0u);
+  if (add_acq_rel_agent(level2, 1u) + 1u != static_cast<uint32_t>(groups)) return false;
+  st_relaxed_agent(level2, 0u);
+  return true;
+}
+
 // ---- one launch per call --------------------------------------------------
 // Every call is one kernel launch on the caller's stream.  Its epoch is one
 // past the epoch of the last completed call on this workspace; the last
@@ -121,10 +153,7 @@ __device__ __forceinline__ uint32_t call_epoch(const uint32_t* hdr) {
 __device__ __forceinline__ void end_call(uint32_t* hdr, uint32_t epoch, const CounterArrays& ca) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = add_acq_rel_agent(hdr + WS_EXIT, 1u);
-    if (old + 1u == gridDim.x) {
-      st_relaxed_agent(hdr + WS_CENSUS_TOTAL, 0u);
-      for (int x = 0; x < kMaxXcd; ++x) st_relaxed_agent(hdr + WS_CENSUS + x, 0u);
+    if (tree_count(hdr + WS_EXIT_GROUP, hdr + WS_EXIT, blockIdx.x, gridDim.x)) {
       if (ld_relaxed_agent(hdr + WS_ERR_CODE) != 0u) {
         for (int32_t c = 0; c < ca.num_chunks; ++c) {
           st_relaxed_agent(ca.counters + c, 0u);
@@ -132,7 +161,6 @@ __device__ __forceinline__ void end_call(uint32_t* hdr, uint32_t epoch, const Co
           for (int x = 0; x < kMaxXcd; ++x) st_relaxed_agent(ca.xparts + c * kMaxXcd + x, 0u);
         }
       }
-      st_relaxed_agent(hdr + WS_EXIT, 0u);
       st_release_agent(hdr + WS_EPOCH, epoch);
     }
   }
