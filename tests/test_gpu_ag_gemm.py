@@ -133,10 +133,27 @@ def test_tiny_bf16_output(tiny):
 def test_ragged_shapes(m, n, k, world, split, tile, layout):
     a, b = inputs.gemm_operands(m, n, k, 16.0, b_layout=layout)
     ref = oracle.gemm_f64(a, b, m, n, k, b_layout=layout)
-    for backend, cus in ((A.SYNC_COPY_SDMA, 0), (A.SYNC_COPY_CU, 16)):
-        out, _ = run_ag(m, n, k, world, a, b, layout=layout, split=split, tile=tile, backend=backend,
-                        copy_cus=cus, rank=world - 1)
+    for backend, cus in ((A.SYNC_COPY_SDMA, 0), (A.SYNC_COPY_CU, 16), (A.SYNC_COPY_COLOCATED, 0)):
+        out, a_local = run_ag(m, n, k, world, a, b, layout=layout, split=split, tile=tile, backend=backend,
+                              copy_cus=cus, rank=world - 1)
         check_f32(out, ref, world)
+        assert np.array_equal(a_local, a)
+
+
+@pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_CU, 32), (A.SYNC_COPY_COLOCATED, 0)])
+@pytest.mark.parametrize("split", [1, 8])
+def test_more_copy_workgroups_than_granules(backend, cus, split):
+    """Chunks of 2 rows x 128 B (16 granules of 16 B) against 64 or 256 copy
+    workgroups: most workgroups have an empty slice of most chunks and must
+    still count toward every chunk's completion exactly once."""
+    m, n, k, world = 64, 64, 64, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    for rep in range(3):  # repeated calls: the counters must come back to zero each time
+        out, a_local = run_ag(m, n, k, world, a, b, split=split, tile=(128, 128), backend=backend, copy_cus=cus,
+                              rank=1)
+        assert np.array_equal(out.astype(np.float64), ref)
+        assert np.array_equal(a_local, a)
 
 
 def test_epoch_alternating_payloads():
