@@ -34,7 +34,8 @@ DIVISOR = 64.0
 BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64), "colocated": (4, 0)}
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
-PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk"}
+PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk",
+            "teams": 1}
 
 
 def profiled_traffic(args):
@@ -73,6 +74,9 @@ def parse():
     p.add_argument("--order", default="chunk_major", choices=["row_major", "chunk_major", "swizzled"])
     p.add_argument("--c-dtype", default="f32", choices=["f32", "bf16"])
     p.add_argument("--layout", default="nk", choices=["nk", "kn"], help="B stored [n][k] or [k][n]")
+    p.add_argument("--teams", type=int, default=1,
+                   help="copied chunks in flight at once (1: one after another, as along a ring; 7: all, as "
+                        "pulls from every peer over a full mesh)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return p.parse_args()
@@ -123,7 +127,8 @@ def main():
             A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c_out, c_dtype, ws, stream, None)
         torch.cuda.synchronize()
         A.sync_read_timings(0)  # drop warm-up records
-        cfg_t = A.make_cfg(cfg.backend, cfg.copy_cus, cfg.timeout_ns, None, cfg.flags | A.SYNC_RUN_TIMED)
+        cfg_t = A.make_cfg(cfg.backend, cfg.copy_cus, cfg.timeout_ns, None, cfg.flags | A.SYNC_RUN_TIMED,
+                           copy_teams=cfg.copy_teams)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
@@ -137,11 +142,12 @@ def main():
         return wall, recs
 
     # overlapped (the metric), compute-only on the full chip, copy-only
-    t_ovl, recs = timed_loop(A.make_cfg(backend, cus), args.steps, args.warmup)
+    t_ovl, recs = timed_loop(A.make_cfg(backend, cus, copy_teams=args.teams), args.steps, args.warmup)
     k_ms = float(np.mean([r[0] for r in recs]))
     t_comp, recs_c = timed_loop(A.make_cfg(A.SYNC_COPY_PRESET), args.steps, args.warmup)
     k_comp_ms = float(np.mean([r[0] for r in recs_c]))
-    t_copy, recs_p = timed_loop(A.make_cfg(backend, cus, flags=A.SYNC_RUN_COPY_ONLY), args.steps, args.warmup)
+    t_copy, recs_p = timed_loop(A.make_cfg(backend, cus, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=args.teams),
+                                args.steps, args.warmup)
     # CU backend: the copy-only launch is the copy role alone; SDMA: the copies' span
     copy_only_ms = float(np.mean([r[1] if backend == A.SYNC_COPY_SDMA else r[0] for r in recs_p]))
     # (co-located: the copy-only launch is every workgroup copying, none computing)
@@ -171,7 +177,8 @@ def main():
             "workload": "AG-GEMM share, Llama-3-8B FFN up-projection at TP=8: A 8192x4096 bf16 gathered from "
                         "8 row chunks (N(0,1)/64), B 4096x1792 bf16, C 8192x1792 " + args.c_dtype,
             "m": M, "n": N, "k": K, "world": WORLD, "split": args.split, "tile": args.tile,
-            "tile_order": args.order, "copy_backend": args.backend, "b_layout": args.layout,
+            "tile_order": args.order, "copy_backend": args.backend, "copy_teams": args.teams,
+            "b_layout": args.layout,
         },
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "overlap": {

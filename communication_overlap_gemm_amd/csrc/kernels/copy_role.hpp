@@ -115,9 +115,18 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
     }
     return;
   }
+  // Teams (copy-in): the workgroups split into `teams` teams by rank; team t
+  // copies every teams-th copied chunk (in arrival order) from the t-th on,
+  // so up to `teams` chunks are in flight at once and one team's drain and
+  // publication overlap the others' copying.
+  const int32_t teams = (!a.copy_out && a.teams > 1 && a.teams <= count) ? a.teams : 1;
+  const int32_t team = rank % teams, trank = rank / teams;
+  const int32_t tcount = count / teams + (team < count % teams ? 1 : 0);
+  int32_t seq = -1;  // index of the chunk among the copied ones
   for (int32_t p = 0; p < a.num_chunks; ++p) {
     const int32_t c = a.arrival[p];
     if (skipped(c)) continue;
+    if (++seq % teams != team) continue;
     if (a.copy_out) {
       if (threadIdx.x == 0) {
         const bool ok = wait_flag(a.wait_flags, c, epoch, a.hdr, a.timeout_ticks);
@@ -134,7 +143,7 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
     for (int x = 0; x < a.ntensors; ++x) {
       const int64_t bytes = (r1 - r0) * a.row_bytes[x];
       const int64_t granules = bytes / 16;
-      const int64_t lo = granules * b / G * 16, hi = granules * (b + 1) / G * 16;
+      const int64_t lo = granules * trank / tcount * 16, hi = granules * (trank + 1) / tcount * 16;
       if (a.streaming)
         copy_range<THREADS, true>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
       else
@@ -144,7 +153,7 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
     __syncthreads();
     if (threadIdx.x == 0) {
       release_agent();  // write this XCD's L2 back
-      if (tree_count(a.xparts + c * kMaxXcd, a.parts + c, rank, count)) {
+      if (tree_count(a.xparts + c * kMaxXcd, a.parts + c, trank, tcount)) {
         if (a.trace_chunks) a.trace_chunks[2 * c + (a.copy_out ? 1 : 0)] = wall_clock64();
         st_release_agent(a.out_flags + c, epoch);
       }

@@ -34,6 +34,7 @@ struct CopyArgs {
   int32_t copy_out;
   int32_t streaming;   // non-temporal loads and stores
   int32_t skip_chunk;  // copy-in: chunk left out (failure-path tests); -1 = all, -2 = none
+  int32_t teams;       // copy-in: chunks in flight at once (1 = one after another)
   uint64_t* trace_chunks;  // SYNC_RUN_TRACE: per chunk {ready, sent} wall-clock stamps, or null
 };
 

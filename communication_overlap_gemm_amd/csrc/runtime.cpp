@@ -313,7 +313,9 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   sync_copy_cfg cfg{};
   cfg.backend = SYNC_COPY_SDMA;
   if (cfg_in) cfg = *cfg_in;
-  if (cfg.reserved) return fail(SYNC_EINVAL, "sync_copy_cfg.reserved must be zero");
+  if (cfg.copy_teams < 0 || cfg.copy_teams > plan->plan.num_chunks)
+    return fail(SYNC_EINVAL, "copy_teams must be in [0, number of chunks]");
+  if (cfg.copy_teams == 0) cfg.copy_teams = 1;
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_COLOCATED && op == SYNC_OP_GEMM_RS)
@@ -441,6 +443,7 @@ CopyArgs make_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2
   ca.timeout_ticks = cx.timeout_ticks;
   ca.streaming = cx.cfg.copy_streaming;
   ca.skip_chunk = (cx.cfg.flags & SYNC_RUN_WITHHOLD) ? cx.cfg.withhold_chunk : -2;
+  ca.teams = cx.cfg.copy_teams;
   ca.trace_chunks = (cx.cfg.flags & SYNC_RUN_TRACE) ? cx.ws.trace_chunks : nullptr;
   return ca;
 }

@@ -22,7 +22,7 @@ LAYOUT = {"kn": A.SYNC_B_KN, "nk": A.SYNC_B_NK}
 
 
 def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
-           backend=A.SYNC_COPY_SDMA, copy_cus=0, c_dtype=A.SYNC_DTYPE_F32, rank=0, poison=True, flags=0):
+           backend=A.SYNC_COPY_SDMA, copy_cus=0, c_dtype=A.SYNC_DTYPE_F32, rank=0, poison=True, flags=0, teams=0):
     print(f"[ag] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
           f"cus={copy_cus} dtype={c_dtype} layout={layout}", flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, rank=rank, split=split, tile_m=tile[0],
@@ -43,7 +43,7 @@ def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128)
     else:
         c = bf16_poison((m, n))
     ws = workspace(plan)
-    cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags)
+    cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags, copy_teams=teams)
     s = torch.cuda.current_stream()
     A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
@@ -92,7 +92,9 @@ def test_tiny_bitwise_invariant_across_plans(tiny):
     check_f32(base, ref, 4)
     for kw in (dict(order=A.SYNC_ORDER_ROW_MAJOR), dict(order=A.SYNC_ORDER_SWIZZLED, split=3),
                dict(split=2, backend=A.SYNC_COPY_CU, copy_cus=8), dict(backend=A.SYNC_COPY_CU, copy_cus=32),
-               dict(split=64), dict(split=4, backend=A.SYNC_COPY_COLOCATED)):
+               dict(split=64), dict(split=4, backend=A.SYNC_COPY_COLOCATED),
+               dict(split=3, backend=A.SYNC_COPY_CU, copy_cus=16, teams=9), dict(split=8, backend=A.SYNC_COPY_CU,
+                                                                                  copy_cus=24, teams=5)):
         out, _ = run_ag(m, n, k, 4, a, b, **kw)
         assert np.array_equal(out.view(np.uint32), base.view(np.uint32)), kw
 
@@ -140,9 +142,10 @@ def test_ragged_shapes(m, n, k, world, split, tile, layout):
         assert np.array_equal(a_local, a)
 
 
-@pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_CU, 32), (A.SYNC_COPY_COLOCATED, 0)])
+@pytest.mark.parametrize("backend,cus,teams", [(A.SYNC_COPY_CU, 32, 1), (A.SYNC_COPY_CU, 32, 3),
+                                               (A.SYNC_COPY_COLOCATED, 0, 1)])
 @pytest.mark.parametrize("split", [1, 8])
-def test_more_copy_workgroups_than_granules(backend, cus, split):
+def test_more_copy_workgroups_than_granules(backend, cus, teams, split):
     """Chunks of 2 rows x 128 B (16 granules of 16 B) against 64 or 256 copy
     workgroups: most workgroups have an empty slice of most chunks and must
     still count toward every chunk's completion exactly once."""
@@ -151,7 +154,7 @@ def test_more_copy_workgroups_than_granules(backend, cus, split):
     ref = oracle.gemm_f64(a, b, m, n, k)
     for rep in range(3):  # repeated calls: the counters must come back to zero each time
         out, a_local = run_ag(m, n, k, world, a, b, split=split, tile=(128, 128), backend=backend, copy_cus=cus,
-                              rank=1)
+                              rank=1, teams=teams)
         assert np.array_equal(out.astype(np.float64), ref)
         assert np.array_equal(a_local, a)
 
@@ -198,7 +201,7 @@ SDMA_LIMIT = ("the HIP runtime does not start the next SDMA copy while the persi
 def test_full_size_exact_small_integers(layout):
     a, b = inputs.gemm_operands(M2, N2, K2, 1.0, integer=True, b_layout=layout)
     out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), split=2, backend=A.SYNC_COPY_CU, copy_cus=32,
-                    layout=layout)
+                    layout=layout, teams=7)
     assert np.all(out == np.round(out))  # every element an exact integer
     rows, cols = _samples(M2, N2, 4000)
     exact = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout=layout)
