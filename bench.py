@@ -78,6 +78,7 @@ def parse():
                    help="copied chunks in flight at once (1: one after another, as along a ring; 7: all, as "
                         "pulls from every peer over a full mesh)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-other-rows", action="store_true", help="skip the RS, 70B-like AG and attention rows")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return p.parse_args()
 
@@ -202,9 +203,144 @@ def main():
             "flops_per_launch": flops,
         },
     }
+    if not args.no_other_rows:
+        del a_peer, a_local, b, c_out
+        line["other_rows"] = other_rows()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a_bits, b_bits, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def _time_calls(fn, steps, warmup):
+    """Mean seconds per call of fn() on the current stream (device events), after warm-up."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e-3
+
+
+def _ws(plan, torch, A):
+    n = A.sync_workspace_size(plan)
+    raw = torch.zeros(n // 4 + 64, dtype=torch.int32, device="cuda:0")
+    ws = raw[((-raw.data_ptr()) % 256) // 4:]
+    A.sync_workspace_init(plan, ws, torch.cuda.current_stream())
+    return ws
+
+
+def other_rows(steps=5, warmup=2):
+    """The other rows of the hot path on their configurations (one line each in
+    the output): GEMM-RS share (Llama-3-8B down-projection), AG-GEMM share
+    (70B-like FFN), ring-attention local step (Qwen-like GQA)."""
+    import numpy as np
+    import torch
+
+    from communication_overlap_gemm_amd import _abi as A
+    from communication_overlap_gemm_amd import inputs
+
+    dev = torch.device("cuda:0")
+    s = torch.cuda.current_stream()
+    out = {}
+
+    def check(ws):
+        rc, ch = A.sync_workspace_status(ws, s)
+        if rc != A.SYNC_OK:
+            raise SystemExit(f"device wait timed out on chunk {ch}")
+
+    # GEMM-RS: A 8192x1792, B 1792x4096 (stored [n][k]), C fp32, copy-out on 32 CUs in send order
+    m, n, k, w = 8192, 4096, 1792, 8
+    a_bits, b_bits = inputs.gemm_operands(m, n, k, 64.0, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, w, b_layout=A.SYNC_B_NK))
+    a = torch.from_numpy(a_bits.view(np.int16)).to(dev)
+    b = torch.from_numpy(b_bits.view(np.int16)).to(dev)
+    c = torch.empty((m, n), dtype=torch.float32, device=dev)
+    st = torch.empty_like(c)
+    ws = _ws(plan, torch, A)
+    t = {}
+    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_CU, 32)),
+                      ("overlapped_8_teams", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=8)),
+                      ("compute_only", A.make_cfg(A.SYNC_COPY_PRESET))):
+        t[name] = _time_calls(lambda: A.sync_gemm_rs(plan, cfg, a, b, c, A.SYNC_DTYPE_F32, st, ws, s, None), steps,
+                              warmup)
+        check(ws)
+    flops = 2.0 * m * n * k
+    hbm = (m * k + k * n) * 2 + m * n * 4 * 3  # A, B, C written, C read and staging written by the copy-out
+    out["gemm_rs_llama8b_down"] = {
+        "workload": "GEMM-RS share: A 8192x1792 bf16, B 1792x4096 bf16, C 8192x4096 fp32 in 8 row chunks, copy-out "
+                    "to staging in send order on 32 CUs", "tflops": round(flops / t["overlapped"] / 1e12, 1),
+        "t_overlap_us": round(t["overlapped"] * 1e6, 1), "t_compute_only_us": round(t["compute_only"] * 1e6, 1),
+        "t_overlap_8_teams_us": round(t["overlapped_8_teams"] * 1e6, 1),
+        "ratio_to_compute_only": round(t["overlapped"] / t["compute_only"], 4),
+        "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "hbm_bound_us": round(hbm / 8e12 * 1e6, 1), "frac_hbm_roofline": round(hbm / 8e12 / t["overlapped"], 4)}
+    del a, b, c, st
+
+    # AG-GEMM 70B-like: A 16384x8192 (8 shards of 2048 rows, split 4: 8 MiB chunks), B 8192x3584, C fp32
+    m, n, k = 16384, 3584, 8192
+    a_bits, b_bits = inputs.gemm_operands(m, n, k, 90.0, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, w, split=4, b_layout=A.SYNC_B_NK))
+    tabs = A.sync_plan_export(plan)
+    ap = torch.from_numpy(a_bits.view(np.int16)).to(dev)
+    b = torch.from_numpy(b_bits.view(np.int16)).to(dev)
+    al = torch.zeros_like(ap)
+    r = m // w
+    al[:r] = ap[:r]
+    c = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = _ws(plan, torch, A)
+    t = {}
+    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7)),
+                      ("compute_only", A.make_cfg(A.SYNC_COPY_PRESET)),
+                      ("copy_only", A.make_cfg(A.SYNC_COPY_CU, 32, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=7))):
+        t[name] = _time_calls(lambda: A.sync_ag_gemm(plan, cfg, ap, al, b, c, A.SYNC_DTYPE_F32, ws, s, None), steps,
+                              warmup)
+        check(ws)
+    flops = 2.0 * m * n * k
+    out["ag_gemm_70b_like"] = {
+        "workload": "AG-GEMM share: A 16384x8192 bf16 from 8 shards x 4 chunks (8 MiB), B 8192x3584 bf16, C fp32, "
+                    "32 copy CUs in 7 teams", "chunks": int(tabs["num_chunks"]),
+        "tflops": round(flops / t["overlapped"] / 1e12, 1), "t_overlap_us": round(t["overlapped"] * 1e6, 1),
+        "t_compute_only_us": round(t["compute_only"] * 1e6, 1), "t_copy_only_us": round(t["copy_only"] * 1e6, 1),
+        "ratio": round(t["overlapped"] / max(t["compute_only"], t["copy_only"]), 4),
+        "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del ap, b, al, c
+
+    # Ring attention: Q 4096x32x128, K/V 8 blocks of 4096 tokens x 8 heads x 128, non-causal
+    sq, hq, hkv, d, nb = 4096, 32, 8, 128, 4096
+    q_bits, k_bits, v_bits = inputs.attention_operands(sq, hq, w * nb, hkv, d)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_RING_ATTN, sq, nb, d, w, tile_m=128, tile_n=1, heads_q=hq, heads_kv=hkv))
+    q = torch.from_numpy(q_bits.view(np.int16)).to(dev)
+    kp = torch.from_numpy(k_bits.view(np.int16)).to(dev)
+    vp = torch.from_numpy(v_bits.view(np.int16)).to(dev)
+    kl, vl = torch.zeros_like(kp), torch.zeros_like(vp)
+    kl[:nb], vl[:nb] = kp[:nb], vp[:nb]
+    o = torch.empty((sq, hq, d), dtype=torch.float32, device=dev)
+    ms, ls, lse = (torch.empty((hq, sq), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = _ws(plan, torch, A)
+    t = {}
+    fl = A.SYNC_ATTN_INIT | A.SYNC_ATTN_FINALIZE
+    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_COLOCATED)),
+                      ("overlapped_32_copy_cus", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7)),
+                      ("compute_only", A.make_cfg(A.SYNC_COPY_PRESET))):
+        t[name] = _time_calls(lambda: A.sync_ring_attn_step(plan, cfg, q, kp, vp, kl, vl, o, ms, ls, lse,
+                                                            1.0 / d ** 0.5, fl, ws, s, None), steps, warmup)
+        check(ws)
+    flops = 4.0 * sq * (w * nb) * hq * d
+    out["ring_attention_qwen_like"] = {
+        "workload": "Ring-attention local step: Q 4096x32x128 bf16, K/V 8 blocks of 4096x8x128 bf16, fp32 (m, l, O), "
+                    "co-located copy (every workgroup pulls its share of K and V, then computes)",
+        "tflops": round(flops / t["overlapped"] / 1e12, 1), "t_overlap_us": round(t["overlapped"] * 1e6, 1),
+        "t_overlap_32_copy_cus_us": round(t["overlapped_32_copy_cus"] * 1e6, 1),
+        "t_compute_only_us": round(t["compute_only"] * 1e6, 1),
+        "ratio": round(t["overlapped"] / t["compute_only"], 4),
+        "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
 
 
 def cpu_baseline(a_bits, b_bits, target_s):

@@ -115,11 +115,11 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
     }
     return;
   }
-  // Teams (copy-in): the workgroups split into `teams` teams by rank; team t
-  // copies every teams-th copied chunk (in arrival order) from the t-th on,
-  // so up to `teams` chunks are in flight at once and one team's drain and
+  // Teams: the workgroups split into `teams` teams by rank; team t copies
+  // every teams-th copied chunk (in arrival / send order) from the t-th on, so
+  // up to `teams` chunks are in flight at once and one team's drain, waits and
   // publication overlap the others' copying.
-  const int32_t teams = (!a.copy_out && a.teams > 1 && a.teams <= count) ? a.teams : 1;
+  const int32_t teams = (a.teams > 1 && a.teams <= count) ? a.teams : 1;
   const int32_t team = rank % teams, trank = rank / teams;
   const int32_t tcount = count / teams + (team < count % teams ? 1 : 0);
   int32_t seq = -1;  // index of the chunk among the copied ones

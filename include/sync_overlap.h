@@ -195,9 +195,10 @@ typedef struct {
   int32_t flags;            /* SYNC_RUN_* bits */
   int32_t copy_streaming;   /* CU backend: 1 = non-temporal loads/stores in the copy role; 0 = plain */
   int32_t withhold_chunk;   /* SYNC_RUN_WITHHOLD only: the chunk left out, or -1 for all */
-  int32_t copy_teams;       /* CU backend copy-in: chunks in flight at once; the copy workgroups
-                               split into this many teams, team t taking every copy_teams-th
-                               copied chunk from the t-th.  0 or 1 = one chunk after another
+  int32_t copy_teams;       /* CU backend: chunks in flight at once; the copy workgroups split
+                               into this many teams, team t taking every copy_teams-th copied
+                               chunk from the t-th (copy-out: in send order, each team waiting
+                               for its chunk's done flag).  0 or 1 = one chunk after another
                                (ring arrival); the number of copied chunks = all at once (pulls
                                from every peer in parallel, as over a full xGMI mesh). */
 } sync_copy_cfg;

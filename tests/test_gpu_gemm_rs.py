@@ -32,7 +32,7 @@ def ws_arrays(ws, num_chunks):
 
 
 def run_rs(m, n, k, world, a_bits, b_bits, split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
-           backend=A.SYNC_COPY_CU, copy_cus=16, c_dtype=A.SYNC_DTYPE_F32, rank=0, layout=A.SYNC_B_KN):
+           backend=A.SYNC_COPY_CU, copy_cus=16, c_dtype=A.SYNC_DTYPE_F32, rank=0, layout=A.SYNC_B_KN, teams=0):
     print(f"[rs] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
           f"cus={copy_cus} dtype={c_dtype}", flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, world, rank=rank, split=split, tile_m=tile[0],
@@ -48,7 +48,8 @@ def run_rs(m, n, k, world, a_bits, b_bits, split=1, tile=(128, 128), order=A.SYN
         staging = bf16_poison((m, n))
     ws = workspace(plan)
     s = torch.cuda.current_stream()
-    A.sync_gemm_rs(plan, A.make_cfg(backend, copy_cus=copy_cus), a, b, c, c_dtype, staging, ws, s, None)
+    A.sync_gemm_rs(plan, A.make_cfg(backend, copy_cus=copy_cus, copy_teams=teams), a, b, c, c_dtype, staging, ws, s,
+                   None)
     rc, chunk = A.sync_workspace_status(ws, s)
     assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
     torch.cuda.synchronize()
@@ -158,3 +159,16 @@ def test_trace_done_and_sent_order():
     for ch in range(tabs["num_chunks"]):
         tiles = tabs["inv_idx"][tabs["inv_ptr"][ch]:tabs["inv_ptr"][ch + 1]]
         assert tr["chunk_ready"][ch] >= tr["tile_wait_end"][tiles].max()
+
+
+@pytest.mark.parametrize("teams,split", [(3, 1), (4, 1), (5, 2)])
+def test_rs_copy_out_teams(teams, split):
+    """Copy-out in teams (several chunks in flight): staging still holds every
+    chunk's rows in its send slot, bitwise, and the counters come back to zero."""
+    m, n, k, W = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    for rep in range(2):
+        cn, st, tabs = run_rs(m, n, k, W, a, b, split=split, teams=teams, copy_cus=16)
+        assert np.array_equal(cn.astype(np.float64), ref)
+        check_staging(cn, st, tabs)
