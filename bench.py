@@ -1,9 +1,11 @@
 """Benchmark: AG-GEMM share, Llama-3-8B FFN up-projection at TP=8, on one MI355X.
 
 One step = one sync_ag_gemm call, which is one kernel launch: its first
-workgroups (the copy role, on `copy_cus` CUs) stage the 7 peer chunks of A
-(8192 x 4096 bf16, 8 shards of 1024 rows, N(0,1)/64) from the peer HBM region
-while the other workgroups run the persistent MFMA GEMM of the gathered A
+workgroups (the copy role, on 32 CUs) stage the 7 peer chunks of A
+(8192 x 4096 bf16, 8 shards of 1024 rows, N(0,1)/64) from the peer HBM region,
+all 7 at once in 7 teams (as pulls from every peer over a full xGMI mesh; --teams 1
+copies them one after another, as along a ring), while the other workgroups
+run the persistent MFMA GEMM of the gathered A
 with B (4096 x 1792 bf16, stored [n][k] like a linear layer's weight by
 default) into C (8192 x 1792 fp32), each tile waiting on the chunks it reads.
 Inputs are resident in HBM before the timed region.
@@ -35,7 +37,7 @@ BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
 PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk",
-            "teams": 1}
+            "teams": 7}
 
 
 def profiled_traffic(args):
@@ -74,7 +76,7 @@ def parse():
     p.add_argument("--order", default="chunk_major", choices=["row_major", "chunk_major", "swizzled"])
     p.add_argument("--c-dtype", default="f32", choices=["f32", "bf16"])
     p.add_argument("--layout", default="nk", choices=["nk", "kn"], help="B stored [n][k] or [k][n]")
-    p.add_argument("--teams", type=int, default=1,
+    p.add_argument("--teams", type=int, default=7,
                    help="copied chunks in flight at once (1: one after another, as along a ring; 7: all, as "
                         "pulls from every peer over a full mesh)")
     p.add_argument("--no-cpu-baseline", action="store_true")
