@@ -81,6 +81,9 @@ def parse():
                         "pulls from every peer over a full mesh)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-rows", action="store_true", help="skip the RS, 70B-like AG and attention rows")
+    p.add_argument("--tune", action="store_true",
+                   help="run the autotuner over split {1,2,4} x tile {256x256, 256x128} x copy CUs {16, 32} first and "
+                        "bench its choice")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return p.parse_args()
 
@@ -99,6 +102,12 @@ def main():
     from communication_overlap_gemm_amd import inputs
 
     dev = torch.device("cuda:0")
+    tuned = None
+    if args.tune:
+        tuned = tune(args)
+        args.split, args.tile, args.backend = tuned["split"], f'{tuned["tile_m"]}x{tuned["tile_n"]}', \
+            f'cu{tuned["copy_cus"]}'
+        BACKENDS.setdefault(args.backend, (2, tuned["copy_cus"]))
     tm, tn = (int(x) for x in args.tile.split("x"))
     order = {"row_major": A.SYNC_ORDER_ROW_MAJOR, "chunk_major": A.SYNC_ORDER_CHUNK_MAJOR,
              "swizzled": A.SYNC_ORDER_SWIZZLED}[args.order]
@@ -205,12 +214,40 @@ def main():
             "flops_per_launch": flops,
         },
     }
+    if tuned is not None:
+        line["autotune"] = tuned
     if not args.no_other_rows:
         del a_peer, a_local, b, c_out
         line["other_rows"] = other_rows()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a_bits, b_bits, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def tune(args):
+    """sync_autotune on the headline workload (chunk-major order, copy teams as given)."""
+    import numpy as np
+    import torch
+
+    from communication_overlap_gemm_amd import _abi as A
+    from communication_overlap_gemm_amd import inputs
+
+    dev = torch.device("cuda:0")
+    b_layout = A.SYNC_B_NK if args.layout == "nk" else A.SYNC_B_KN
+    base = A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, b_layout=b_layout)
+    space = A.make_tune_space(splits=(1, 2, 4), tiles=((256, 256), (256, 128)), orders=(A.SYNC_ORDER_CHUNK_MAJOR,),
+                              copy_cus=(16, 32), warmup=2, iters=5)
+    a_bits, b_bits = inputs.gemm_operands(M, N, K, DIVISOR, b_layout=args.layout)
+    a_peer = torch.from_numpy(a_bits.view(np.int16)).to(dev)
+    b = torch.from_numpy(b_bits.view(np.int16)).to(dev)
+    a_local = torch.zeros_like(a_peer)
+    a_local[:M // WORLD] = a_peer[:M // WORLD]
+    c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    nb = A.sync_tune_workspace_size(base, space)
+    raw = torch.zeros(nb // 4 + 64, dtype=torch.int32, device=dev)
+    ws = raw[((-raw.data_ptr()) % 256) // 4:]
+    return A.sync_autotune(base, space, a=a_local, a_peer=a_peer, b=b, c=c, ws=ws,
+                           stream=torch.cuda.current_stream())
 
 
 def _time_calls(fn, steps, warmup):

@@ -390,3 +390,25 @@ def test_trace_tiles_start_after_their_chunks(order):
         if ready:
             worst = min(worst, tr["tile_wait_end"][t] - max(ready))
     assert worst >= 0, f"a tile started {-worst} ns before a chunk it reads was released"
+
+
+# ---- AG-GEMM share at the 70B-like FFN size --------------------------------------
+M4, N4, K4, W4 = 16384, 3584, 8192, 8
+
+
+@pytest.mark.parametrize("split,teams", [(4, 7), (16, 1)])
+def test_full_size_70b_like(split, teams):
+    """A 16384x8192 from 8 shards (2048 rows) in 32 or 128 chunks, B 8192x3584
+    stored [n][k], N(0,1)/90: sampled outputs against the oracle, per shard."""
+    a, b = inputs.gemm_operands(M4, N4, K4, 90.0, b_layout="nk")
+    out, a_local = run_ag(M4, N4, K4, W4, a, b, tile=(256, 256), split=split, backend=A.SYNC_COPY_CU, copy_cus=32,
+                          layout="nk", teams=teams, poison=False)
+    assert np.array_equal(a_local, a)
+    rows, cols = _samples(M4, N4, 12000, seed=4)
+    ref = oracle.gemm_f64_sampled(a, b, M4, N4, K4, rows, cols, b_layout="nk")
+    got = out[rows, cols].astype(np.float64)
+    assert np.isfinite(got).all()
+    shard = rows // (M4 // W4)
+    for s in range(W4):
+        sel = shard == s
+        assert np.linalg.norm(got[sel] - ref[sel]) <= 1e-3 * np.linalg.norm(ref[sel]), s
