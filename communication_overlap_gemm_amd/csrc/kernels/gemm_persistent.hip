@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     return;
   }
   const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
-  if (a.colocated) copy_role<kThreads, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
+  if (!RS && a.colocated) copy_role<kThreads, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];
@@ -339,6 +339,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
     if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
   }
+  // co-located GEMM-RS: every workgroup joins the copy-out once its tiles are
+  // stored, chunk by chunk in send order (the first chunks are done first)
+  if (RS && a.colocated) copy_role<kThreads>(a.copy, gb, gn, epoch);
   end_call(a.hdr, epoch, a.cnt);
 }
 
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
     return;
   }
   const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
-  if (a.colocated) copy_role<THREADS, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
+  if (!RS && a.colocated) copy_role<THREADS, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];
@@ -626,6 +629,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
     if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
   }
+  // co-located GEMM-RS: every workgroup joins the copy-out once its tiles are
+  // stored, chunk by chunk in send order (the first chunks are done first)
+  if (RS && a.colocated) copy_role<THREADS>(a.copy, gb, gn, epoch);
   end_call(a.hdr, epoch, a.cnt);
 }
 

@@ -318,8 +318,6 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   if (cfg.copy_teams == 0) cfg.copy_teams = 1;
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
-  if (cfg.backend == SYNC_COPY_COLOCATED && op == SYNC_OP_GEMM_RS)
-    return fail(SYNC_EUNSUPPORTED, "GEMM-RS copy-out runs on dedicated CUs (CU backend) or not at all (PRESET)");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
     return fail(SYNC_EINVAL, "unknown cfg.flags bits");
@@ -723,7 +721,7 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
   if ((rc = check_gemm_shape(pl))) return rc;
   if (c_dtype != SYNC_DTYPE_F32 && c_dtype != SYNC_DTYPE_BF16) return fail(SYNC_EINVAL, "bad c_dtype");
   if (cx.cfg.backend == SYNC_COPY_SDMA || cx.cfg.backend == SYNC_COPY_HOST_GATED)
-    return fail(SYNC_EUNSUPPORTED, "GEMM-RS copy-out runs on dedicated CUs (CU backend) or not at all (PRESET)");
+    return fail(SYNC_EUNSUPPORTED, "GEMM-RS copy-out runs on CUs (CU or COLOCATED backend) or not at all (PRESET)");
   const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
   if (cx.cfg.flags & SYNC_RUN_COPY_ONLY) return fail(SYNC_EINVAL, "COPY_ONLY is not defined for GEMM-RS");
   if (!a || !b || !c || (!compute_only && !staging)) return fail(SYNC_EINVAL, "NULL operand");
@@ -749,6 +747,7 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
   return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, nullptr, nullptr, nullptr, 0,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     g.copy_blocks = rr.copy_blocks;
+                    g.colocated = rr.colocated;
                     HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, true, rr.grid,
                                         st));
                     return SYNC_OK;

@@ -163,11 +163,12 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *   HOST_GATED  as SDMA, but chunk c's copy first waits until the host word
  *               host_gates[c] becomes non-zero (tests: delayed or withheld
  *               chunks)
- *   COLOCATED   AG and attention: one launch on `compute` in which every
- *               compute workgroup first copies its share of each chunk, in
- *               arrival order (the flags are raised as chunks complete), and
- *               then computes; no CUs are set aside [SYN-S Fig. 7: load/store
- *               by the compute SMs themselves]. */
+ *   COLOCATED   one launch on `compute` whose compute workgroups also copy; no
+ *               CUs are set aside [SYN-S Fig. 7: load/store by the compute SMs
+ *               themselves].  AG and attention: every workgroup first copies
+ *               its share of each chunk and then computes.  GEMM-RS: every
+ *               workgroup stores its tiles and then joins the copy-out, chunk
+ *               by chunk in send order. */
 enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOST_GATED = 3, SYNC_COPY_COLOCATED = 4 };
 
 /* mode bits for sync_copy_cfg.flags */
@@ -266,8 +267,8 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
 /* GEMM-RS share [SYN-S "Experiments": GEMM-RS; ENT: tiles reordered so output
  * for communication is produced at a steady pace; SM-based fine-grained
  * communication].  The GEMM visits tiles in send order; when the last tile of
- * chunk c is stored it raises done[c]; the copy workgroups (CU backend; SDMA:
- * not supported, EUNSUPPORTED) wait for done[c] in send order and copy the
+ * chunk c is stored it raises done[c]; the copy workgroups (CU or COLOCATED
+ * backend; SDMA: not supported, EUNSUPPORTED) wait for done[c] in send order and copy the
  * chunk's rows of c into `staging`, slot p = chunk arrival[p] (slots packed
  * back to back in send order).
  *   a bf16 [m][k]; b bf16 as in sync_ag_gemm; c and staging [m][n] c_dtype.

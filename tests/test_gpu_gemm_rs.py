@@ -172,3 +172,30 @@ def test_rs_copy_out_teams(teams, split):
         cn, st, tabs = run_rs(m, n, k, W, a, b, split=split, teams=teams, copy_cus=16)
         assert np.array_equal(cn.astype(np.float64), ref)
         check_staging(cn, st, tabs)
+
+
+@pytest.mark.parametrize("m,n,k,W,split,tile", [(1024, 512, 256, 4, 1, (128, 128)), (1000, 520, 320, 4, 3, (128, 128)),
+                                                 (968, 264, 192, 2, 5, (256, 128)), (1024, 512, 256, 4, 2, (256, 256))])
+def test_rs_colocated(m, n, k, W, split, tile):
+    """Co-located GEMM-RS: every workgroup stores its tiles, then joins the
+    copy-out in send order.  Exact for integer operands; staging bitwise."""
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    for teams in (0, W * split):  # one chunk after another; every chunk in its own team
+        cn, st, tabs = run_rs(m, n, k, W, a, b, split=split, tile=tile, backend=A.SYNC_COPY_COLOCATED, copy_cus=0,
+                              teams=teams)
+        assert np.array_equal(cn.astype(np.float64), ref)
+        check_staging(cn, st, tabs)
+
+
+def test_full_size_rs_colocated_exact():
+    m, n, k, W = 8192, 4096, 1792, 8
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    cn, st, tabs = run_rs(m, n, k, W, a, b, tile=(256, 256), backend=A.SYNC_COPY_COLOCATED, copy_cus=0,
+                          layout=A.SYNC_B_NK, teams=8)
+    assert np.all(cn == np.round(cn))
+    check_staging(cn, st, tabs)
+    rows = np.random.default_rng(3).integers(0, m, 3000)
+    cols = np.random.default_rng(4).integers(0, n, 3000)
+    exact = oracle.gemm_f64_sampled(a, b, m, n, k, rows, cols, b_layout="nk")
+    assert np.array_equal(cn[rows, cols].astype(np.float64), exact)
