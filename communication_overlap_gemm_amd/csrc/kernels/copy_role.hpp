@@ -86,18 +86,27 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
   const int64_t G = count, b = rank;
   auto skipped = [&](int32_t c) { return !a.copy_out && (a.resident[c] || a.skip_chunk == c || a.skip_chunk == -1); };
   if constexpr (BATCH) {
+    // Published all at once, so the copied rows are split evenly in row
+    // order, not chunk by chunk: each workgroup copies one contiguous share
+    // of the concatenated copied granules (one or two large ranges).
     int32_t first = -1;  // the batch counts in the slots of its first copied chunk
-    for (int32_t p = 0; p < a.num_chunks; ++p) {
-      const int32_t c = a.arrival[p];
-      if (skipped(c)) continue;
-      if (first < 0) first = c;
-      const int64_t r0 = a.chunk_begin[c], r1 = a.chunk_begin[c + 1];
-      for (int x = 0; x < a.ntensors; ++x) {
-        const int64_t granules = (r1 - r0) * a.row_bytes[x] / 16;
-        const int64_t lo = granules * b / G * 16, hi = granules * (b + 1) / G * 16;
-        copy_range<THREADS, false>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + r0 * a.row_bytes[x], lo, hi);
+    int64_t total = 0;
+    for (int x = 0; x < a.ntensors; ++x)
+      for (int32_t c = 0; c < a.num_chunks; ++c)
+        if (!skipped(c)) total += (a.chunk_begin[c + 1] - a.chunk_begin[c]) * a.row_bytes[x] / 16;
+    const int64_t lo = total * b / G, hi = total * (b + 1) / G;
+    int64_t pos = 0;
+    for (int x = 0; x < a.ntensors; ++x)
+      for (int32_t c = 0; c < a.num_chunks; ++c) {
+        if (skipped(c)) continue;
+        if (first < 0) first = c;  // the lowest copied chunk id: the same for every workgroup
+        const int64_t r0 = a.chunk_begin[c], n = (a.chunk_begin[c + 1] - r0) * a.row_bytes[x] / 16;
+        const int64_t a0 = lo > pos ? lo : pos, a1 = hi < pos + n ? hi : pos + n;
+        if (a0 < a1)
+          copy_range<THREADS, false>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + r0 * a.row_bytes[x], (a0 - pos) * 16,
+                                     (a1 - pos) * 16);
+        pos += n;
       }
-    }
     if (first < 0) return;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();

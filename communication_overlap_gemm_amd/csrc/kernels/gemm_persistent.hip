@@ -199,7 +199,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
     return;
   }
   const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
-  if (!RS && a.colocated) copy_role<kThreads, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
+  if (!RS && a.colocated) {  // co-located: pull this workgroup's share first
+    if (a.copy.teams > 1)
+      copy_role<kThreads>(a.copy, gb, gn, epoch);
+    else
+      copy_role<kThreads, true>(a.copy, gb, gn, epoch);
+  }
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];
@@ -482,7 +487,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
     return;
   }
   const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
-  if (!RS && a.colocated) copy_role<THREADS, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every chunk first
+  if (!RS && a.colocated) {  // co-located: pull this workgroup's share first
+    if (a.copy.teams > 1)
+      copy_role<THREADS>(a.copy, gb, gn, epoch);  // teams: each chunk published as soon as its team is done
+    else
+      copy_role<THREADS, true>(a.copy, gb, gn, epoch);  // one publication for all chunks
+  }
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];

@@ -82,7 +82,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
     return;
   }
   const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
-  if (a.colocated) copy_role<kAttnThreads, true>(a.copy, gb, gn, epoch);  // co-located: pull this share of every block first
+  if (a.colocated) {  // co-located: pull this workgroup's share of every block first
+    if (a.copy.teams > 1)
+      copy_role<kAttnThreads>(a.copy, gb, gn, epoch);
+    else
+      copy_role<kAttnThreads, true>(a.copy, gb, gn, epoch);
+  }
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int item = slot0; item < items; item += gn) {
     const int hg = item / nqb, qb = item - hg * nqb;  // head-group-major: one KV head's items adjacent
