@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--teams", type=int, default=7,
                    help="copied chunks in flight at once (1: one after another, as along a ring; 7: all, as "
                         "pulls from every peer over a full mesh)")
+    p.add_argument("--kslices", type=int, default=4,
+                   help="K-slices per copied chunk (1: whole chunks; >1: slice 0 of every chunk first, tiles start "
+                        "on it and wait in-kernel for the later slices)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-rows", action="store_true", help="skip the RS, 70B-like AG and attention rows")
     p.add_argument("--tune", action="store_true",
@@ -140,7 +143,7 @@ def main():
         torch.cuda.synchronize()
         A.sync_read_timings(0)  # drop warm-up records
         cfg_t = A.make_cfg(cfg.backend, cfg.copy_cus, cfg.timeout_ns, None, cfg.flags | A.SYNC_RUN_TIMED,
-                           copy_teams=cfg.copy_teams)
+                           copy_teams=cfg.copy_teams, copy_kslices=cfg.copy_kslices)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
@@ -154,12 +157,13 @@ def main():
         return wall, recs
 
     # overlapped (the metric), compute-only on the full chip, copy-only
-    t_ovl, recs = timed_loop(A.make_cfg(backend, cus, copy_teams=args.teams), args.steps, args.warmup)
+    t_ovl, recs = timed_loop(A.make_cfg(backend, cus, copy_teams=args.teams, copy_kslices=args.kslices), args.steps,
+                             args.warmup)
     k_ms = float(np.mean([r[0] for r in recs]))
     t_comp, recs_c = timed_loop(A.make_cfg(A.SYNC_COPY_PRESET), args.steps, args.warmup)
     k_comp_ms = float(np.mean([r[0] for r in recs_c]))
-    t_copy, recs_p = timed_loop(A.make_cfg(backend, cus, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=args.teams),
-                                args.steps, args.warmup)
+    t_copy, recs_p = timed_loop(A.make_cfg(backend, cus, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=args.teams,
+                                           copy_kslices=args.kslices), args.steps, args.warmup)
     # CU backend: the copy-only launch is the copy role alone; SDMA: the copies' span
     copy_only_ms = float(np.mean([r[1] if backend == A.SYNC_COPY_SDMA else r[0] for r in recs_p]))
     # (co-located: the copy-only launch is every workgroup copying, none computing)
@@ -190,7 +194,7 @@ def main():
                         "8 row chunks (N(0,1)/64), B 4096x1792 bf16, C 8192x1792 " + args.c_dtype,
             "m": M, "n": N, "k": K, "world": WORLD, "split": args.split, "tile": args.tile,
             "tile_order": args.order, "copy_backend": args.backend, "copy_teams": args.teams,
-            "b_layout": args.layout,
+            "copy_kslices": args.kslices, "b_layout": args.layout,
         },
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "overlap": {

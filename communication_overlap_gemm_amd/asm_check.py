@@ -3,11 +3,12 @@
 The GEMM reads its MFMA fragments from LDS with inline-asm ds_read_b128 and
 waits for them itself (lgkmcnt), so the compiler believes each destination
 register holds its value as soon as the asm statement issues.  Any
-compiler-generated instruction that reads or writes such a register before
-the next lgkmcnt(0) wait would see or clobber a value the LDS has not yet
-returned.  This module compiles the kernel source to gfx950 assembly and
-reports every such instruction; the kernels are correct only if it reports
-none.
+compiler-generated instruction that reads or writes such a register before a
+wait that covers the read would see or clobber a value the LDS has not yet
+returned.  LDS operations of one wave complete in issue order, so
+lgkmcnt(N) covers a read once N or more LDS operations were issued after it.
+This module compiles the kernel source to gfx950 assembly and reports every
+such instruction; the kernels are correct only if it reports none.
 
     python -m communication_overlap_gemm_amd.asm_check   # exit status 1 on a hazard
 """
@@ -110,23 +111,40 @@ def _ends_block(instr: str) -> bool:
     return bool(re.match(r"^(s_branch\s|s_endpgm|s_setpc|s_trap)", instr))
 
 
+_LGKM = re.compile(r"lgkmcnt\((\d+)\)")
+_CAP = 16  # LDS operations issued after a read, counted up to this
+
+
 def _transfer(block, pending: frozenset, report=None, name=""):
-    pend = set(pending)
+    """pending: frozenset of (register, LDS operations issued since its read)."""
+    pend = dict()
+    for r, n in pending:  # a register pending along several paths keeps its smallest count
+        pend[r] = min(n, pend.get(r, _CAP))
     for i, t, is_asm in block[1]:
         if t.startswith("s_waitcnt"):
-            if "lgkmcnt(0)" in t:
-                pend = set()
+            m = _LGKM.search(t)
+            if m:
+                n = int(m.group(1))
+                pend = {r: c for r, c in pend.items() if c < n}
             continue
-        if is_asm and t.startswith("ds_read_b128"):
-            dst, addr = t.split(None, 1)[1].split(",", 1)
-            if report is not None and _regs(addr) & pend:
-                report.append(f"{name}:{i}: address register still pending: {t}")
-            pend |= _regs(dst)
+        if t.startswith("ds_"):
+            if is_asm and t.startswith("ds_read_b128"):
+                dst, addr = t.split(None, 1)[1].split(",", 1)
+                if report is not None and _regs(addr) & set(pend):
+                    report.append(f"{name}:{i}: address register still pending: {t}")
+            else:
+                dst = ""
+            hit = _regs(t) & set(pend) if not is_asm else set()
+            if hit and report is not None:
+                report.append(f"{name}:{i}: {t} touches {sorted(hit)}")
+            pend = {r: min(c + 1, _CAP) for r, c in pend.items()}
+            for r in _regs(dst):
+                pend[r] = 0
             continue
-        hit = _regs(t) & pend
+        hit = _regs(t) & set(pend)
         if hit and report is not None:
             report.append(f"{name}:{i}: {t} touches {sorted(hit)}")
-    return frozenset(pend)
+    return frozenset(pend.items())
 
 
 def hazards(asm: str, kernel_prefix: str = "_ZN6syncov8gemm_dma") -> tuple[int, list[str]]:

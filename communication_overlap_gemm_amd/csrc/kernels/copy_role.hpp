@@ -21,6 +21,10 @@
 //            done[c] (raised by the GEMM role), copies its slice of the
 //            chunk's rows of C into the staging slot, and sent[c] is raised
 //            the same way.
+//   K-sliced copy-in: the chunks move as column slices of their rows, slice 0
+//            of every chunk first, each slice with a ready flag of its own, so
+//            a tile can start on the first K-slice of its rows before the rest
+//            of them has landed.
 // All workgroups walk the same order, so chunks complete one after another at
 // the role's full bandwidth.
 #pragma once
@@ -67,6 +71,51 @@ __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* _
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
       if (g + u * step < gend) st(v[u], d + g + u * step);
+  }
+}
+
+// Copies granules [lo, hi) of a column block: the block is `rows` rows of
+// `seg` bytes (a multiple of 16) at byte column col of rows `pitch` bytes
+// apart in src and dst, its granules numbered row by row.  Same loads in
+// flight per thread as copy_range; each thread steps its (row, column) by the
+// block stride instead of dividing.
+template <int THREADS, bool STREAM>
+__device__ __forceinline__ void copy_block(const char* __restrict__ src, char* __restrict__ dst, int64_t pitch,
+                                           int64_t col, int64_t seg, int64_t lo, int64_t hi) {
+  const int64_t gpr = seg / 16;  // granules per row
+  int64_t g = lo + threadIdx.x;
+  if (g >= hi) return;
+  int64_t row = g / gpr, cg = g - row * gpr;
+  const int64_t drow = THREADS / gpr, dcg = THREADS - drow * gpr;  // one step of THREADS granules
+  auto ld = [](const char* p) {
+    const copy_u32x4_t* q = reinterpret_cast<const copy_u32x4_t*>(p);
+    return STREAM ? __builtin_nontemporal_load(q) : *q;
+  };
+  auto st = [](copy_u32x4_t v, char* p) {
+    copy_u32x4_t* q = reinterpret_cast<copy_u32x4_t*>(p);
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(v, q);
+    else
+      *q = v;
+  };
+  while (g < hi) {
+    copy_u32x4_t v[kCopyUnroll];
+    int64_t off[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      off[u] = row * pitch + col + cg * 16;
+      if (g + u * THREADS < hi) v[u] = ld(src + off[u]);
+      row += drow;
+      cg += dcg;
+      if (cg >= gpr) {
+        cg -= gpr;
+        ++row;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (g + u * THREADS < hi) st(v[u], dst + off[u]);
+    g += kCopyUnroll * THREADS;
   }
 }
 
@@ -118,6 +167,7 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
           const int32_t c = a.arrival[p];
           if (skipped(c)) continue;
           if (a.trace_chunks) a.trace_chunks[2 * c] = now;
+          for (int32_t h = 0; a.kslices > 1 && h < a.kslices; ++h) st_release_agent(a.slice_flags + c * kMaxSlices + h, epoch);
           st_release_agent(a.out_flags + c, epoch);
         }
       }
@@ -125,49 +175,81 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
     return;
   }
   // Teams: the workgroups split into `teams` teams by rank; team t copies
-  // every teams-th copied chunk (in arrival / send order) from the t-th on, so
-  // up to `teams` chunks are in flight at once and one team's drain, waits and
-  // publication overlap the others' copying.
+  // every teams-th copied item (in arrival / send order) from the t-th on, so
+  // up to `teams` items are in flight at once and one team's drain, waits and
+  // publication overlap the others' copying.  An item is a chunk, or with a
+  // K-sliced copy-in one column slice of a chunk, slice-major: slice 0 of
+  // every chunk in arrival order, then slice 1, ...
   const int32_t teams = (a.teams > 1 && a.teams <= count) ? a.teams : 1;
   const int32_t team = rank % teams, trank = rank / teams;
   const int32_t tcount = count / teams + (team < count % teams ? 1 : 0);
-  int32_t seq = -1;  // index of the chunk among the copied ones
-  for (int32_t p = 0; p < a.num_chunks; ++p) {
-    const int32_t c = a.arrival[p];
-    if (skipped(c)) continue;
-    if (++seq % teams != team) continue;
-    if (a.copy_out) {
+  const int32_t S = (!a.copy_out && a.kslices > 1) ? a.kslices : 1;
+  int32_t seq = -1;  // index of the item among the copied ones
+  for (int32_t h = 0; h < S; ++h)
+    for (int32_t p = 0; p < a.num_chunks; ++p) {
+      const int32_t c = a.arrival[p];
+      if (skipped(c)) continue;
+      if (++seq % teams != team) continue;
+      if (a.copy_out) {
+        if (threadIdx.x == 0) {
+          const bool ok = wait_flag(a.wait_flags, c, epoch, a.hdr, a.timeout_ticks);
+          if (ok) acquire_agent();
+          s_ok = ok;
+        }
+        __syncthreads();
+        const int ok = s_ok;
+        __syncthreads();
+        if (!ok) continue;  // chunk never completed: nothing to send
+      }
+      const int64_t r0 = a.chunk_begin[c], r1 = a.chunk_begin[c + 1];
+      const int64_t drow = a.copy_out ? a.slot_row[p] : r0;
+      for (int x = 0; x < a.ntensors; ++x) {
+        const int64_t rb = a.row_bytes[x];
+        if (S == 1) {
+          const int64_t granules = (r1 - r0) * rb / 16;
+          const int64_t lo = granules * trank / tcount * 16, hi = granules * (trank + 1) / tcount * 16;
+          if (a.streaming)
+            copy_range<THREADS, true>(a.src[x] + r0 * rb, a.dst[x] + drow * rb, lo, hi);
+          else
+            copy_range<THREADS, false>(a.src[x] + r0 * rb, a.dst[x] + drow * rb, lo, hi);
+        } else {
+          const int64_t lines = rb / 128;  // 128-byte columns per row
+          const int64_t col = h * lines / S * 128, seg = (h + 1) * lines / S * 128 - col;
+          const int64_t granules = (r1 - r0) * (seg / 16);
+          const int64_t lo = granules * trank / tcount, hi = granules * (trank + 1) / tcount;
+          if (a.streaming)
+            copy_block<THREADS, true>(a.src[x] + r0 * rb, a.dst[x] + r0 * rb, rb, col, seg, lo, hi);
+          else
+            copy_block<THREADS, false>(a.src[x] + r0 * rb, a.dst[x] + r0 * rb, rb, col, seg, lo, hi);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores have reached the L2
+      __syncthreads();
       if (threadIdx.x == 0) {
-        const bool ok = wait_flag(a.wait_flags, c, epoch, a.hdr, a.timeout_ticks);
-        if (ok) acquire_agent();
-        s_ok = ok;
-      }
-      __syncthreads();
-      const int ok = s_ok;
-      __syncthreads();
-      if (!ok) continue;  // chunk never completed: nothing to send
-    }
-    const int64_t r0 = a.chunk_begin[c], r1 = a.chunk_begin[c + 1];
-    const int64_t drow = a.copy_out ? a.slot_row[p] : r0;
-    for (int x = 0; x < a.ntensors; ++x) {
-      const int64_t bytes = (r1 - r0) * a.row_bytes[x];
-      const int64_t granules = bytes / 16;
-      const int64_t lo = granules * trank / tcount * 16, hi = granules * (trank + 1) / tcount * 16;
-      if (a.streaming)
-        copy_range<THREADS, true>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
-      else
-        copy_range<THREADS, false>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + drow * a.row_bytes[x], lo, hi);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores have reached the L2
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      release_agent();  // write this XCD's L2 back
-      if (tree_count(a.xparts + c * kMaxXcd, a.parts + c, trank, tcount)) {
-        if (a.trace_chunks) a.trace_chunks[2 * c + (a.copy_out ? 1 : 0)] = wall_clock64();
-        st_release_agent(a.out_flags + c, epoch);
+        release_agent();  // write this XCD's L2 back
+        if (S == 1) {
+          if (tree_count(a.xparts + c * kMaxXcd, a.parts + c, trank, tcount)) {
+            if (a.trace_chunks) a.trace_chunks[2 * c + (a.copy_out ? 1 : 0)] = wall_clock64();
+            st_release_agent(a.out_flags + c, epoch);
+          }
+        } else {
+          const int32_t sl = c * kMaxSlices + h;
+          if (tree_count(a.sxparts + sl * kMaxXcd, a.sparts + sl, trank, tcount)) {
+            st_release_agent(a.slice_flags + sl, epoch);
+            // the chunk is whole once all its slices are: the completer of
+            // the last one (counted with acquire-release, so it sees the
+            // others' publications) raises the chunk flag and clears the count
+            const uint32_t done =
+                __hip_atomic_fetch_add(a.parts + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+            if (done == static_cast<uint32_t>(S)) {
+              st_relaxed_agent(a.parts + c, 0u);
+              if (a.trace_chunks) a.trace_chunks[2 * c] = wall_clock64();
+              st_release_agent(a.out_flags + c, epoch);
+            }
+          }
+        }
       }
     }
-  }
 }
 
 }  // namespace syncov

@@ -159,6 +159,10 @@ __device__ __forceinline__ void end_call(uint32_t* hdr, uint32_t epoch, const Co
           st_relaxed_agent(ca.counters + c, 0u);
           st_relaxed_agent(ca.parts + c, 0u);
           for (int x = 0; x < kMaxXcd; ++x) st_relaxed_agent(ca.xparts + c * kMaxXcd + x, 0u);
+          for (int h = 0; h < kMaxSlices; ++h) {
+            st_relaxed_agent(ca.sparts + c * kMaxSlices + h, 0u);
+            for (int x = 0; x < kMaxXcd; ++x) st_relaxed_agent(ca.sxparts + (c * kMaxSlices + h) * kMaxXcd + x, 0u);
+          }
         }
       }
       st_release_agent(hdr + WS_EPOCH, epoch);

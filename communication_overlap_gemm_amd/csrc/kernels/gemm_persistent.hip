@@ -23,6 +23,8 @@
 //    writes C with 16-byte buffer stores, rows past M dropped by the hardware.
 //  * One workgroup per CU walks the plan's tile order with a static stride;
 //    slots are remapped so that each XCD takes consecutive tiles of the order.
+#include <utility>
+
 #include "copy_role.hpp"
 #include "device_common.hpp"
 #include "launch_args.hpp"
@@ -144,18 +146,30 @@ __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, ui
 // AG: lane 0 waits for every chunk tile t reads that was not in place before
 // the call, then one acquire.  Returns false (uniformly) when a wait gave up,
 // so the tile is skipped.
+// Thread 0 waits for flags[c * stride + slice] of every chunk c tile t reads
+// (resident chunks excepted), then makes their data visible to this CU.
+// False if one never arrived (timeout or an error of the call).
+__device__ __forceinline__ bool wait_tile_deps(const GemmArgs& a, int32_t t, uint32_t epoch, const uint32_t* flags,
+                                               int32_t stride, int32_t slice) {
+  bool ok = true, waited = false;
+  for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e) {
+    const int32_t c = a.dep_idx[e];
+    if (a.resident[c]) continue;
+    // reads flags[c * stride + slice]; a timeout names chunk c
+    ok = wait_flag(flags + c * (stride - 1) + slice, c, epoch, a.hdr, a.timeout_ticks);
+    waited = true;
+  }
+  if (ok && waited) acquire_agent();
+  return ok;
+}
+
+// Tile start: every chunk of tile t (with a K-sliced copy, their slice 0).
 __device__ __forceinline__ bool wait_tile_chunks(const GemmArgs& a, int32_t t, uint32_t epoch, int tid,
                                                  int32_t* s_skip) {
   if (!a.wait_chunks) return true;
   if (tid == 0) {
-    bool ok = true, waited = false;
-    for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e) {
-      const int32_t c = a.dep_idx[e];
-      if (a.resident[c]) continue;
-      ok = wait_flag(a.flags, c, epoch, a.hdr, a.timeout_ticks);
-      waited = true;
-    }
-    if (ok && waited) acquire_agent();
+    const bool ok = a.kslices > 1 ? wait_tile_deps(a, t, epoch, a.slice_flags, kMaxSlices, 0)
+                                  : wait_tile_deps(a, t, epoch, a.flags, 1, 0);
     *s_skip = ok ? 0 : 1;
   }
   __syncthreads();
@@ -394,6 +408,23 @@ __device__ __forceinline__ bf16x8_t lds_read_b128(uint32_t addr) {
 #endif
   return r;
 }
+// The same with a constant byte offset in the instruction's 16-bit field.
+template <int OFF>
+__device__ __forceinline__ bf16x8_t lds_read_b128_at(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  bf16x8_t r{};
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "n"(OFF));
+#endif
+  return r;
+}
+
+// Calls f(std::integral_constant<int, X>{}) for X = 0 .. N-1 in order, so X
+// can name a template argument or an instruction's immediate.
+template <typename F, int... X>
+__device__ __forceinline__ void unroll_each(F&& f, std::integer_sequence<int, X...>) {
+  (f(std::integral_constant<int, X>{}), ...);
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -424,7 +455,14 @@ __device__ __forceinline__ int rswz(int row, int slot) {
     return slot ^ ((row & 7) ^ ((row >> 3) & 1));
 }
 
-template <int TM, int TN, int CT, bool RS, int TK, int NS, int WGM, int WGN, bool SPREAD_LOADS = false>
+// FEED: how a stage reaches the LDS.  0: direct-to-LDS loads, all issued
+// right after the barrier that frees the slot; F > 0: direct-to-LDS loads
+// spread over the first F k16 steps after that barrier, between the MFMAs;
+// kFeedReg: through registers (global loads one stage ahead, written to the
+// free slot with ds_write between the MFMAs).
+constexpr int kFeedReg = -1;
+
+template <int TM, int TN, int CT, bool RS, int TK, int NS, int WGM, int WGN, int FEED>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
   constexpr int NW = WGM * WGN, THREADS = 64 * NW;  // waves, as a WGM x WGN grid over the tile
   constexpr int WM = TM / WGM, WN = TN / WGN;
@@ -439,15 +477,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
   constexpr int B_LD = B_BYTES / 1024 / NW;
   constexpr int LPW = A_LD + B_LD;                  // loads per wave per stage
   constexpr int NFRAG = MI + NI;                    // 16-byte reads per k16 step: A frags, then B frags
-  constexpr bool SPREAD = SPREAD_LOADS && NS >= 3;  // stage loads interleaved with the MFMAs (see the main loop)
-  constexpr int PER = (LPW + KS - 1) / KS;          // SPREAD: loads per k16 step
-  constexpr int GAP = (MI * NI) / PER > 0 ? (MI * NI) / PER : 1;  // SPREAD: MFMAs between loads
-  static_assert(!SPREAD || (LPW % KS == 0 && PER <= MI * NI), "spread loads over the k16 steps");
   static_assert(WM % 32 == 0 && WN % 32 == 0 && A_LD >= 1 && B_LD >= 1 && A_LD * NW * 1024 == A_BYTES &&
                 B_LD * NW * 1024 == B_BYTES, "tile");
   static_assert((SLOTS == 4 || SLOTS == 8) && KS % 2 == 0, "stage depth");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring");
   static_assert(NFRAG <= MI * NI, "one read per MFMA slot");
+  constexpr bool REG = FEED == kFeedReg, SPREAD = FEED > 0;
+  constexpr int PPW = LPW / KS;  // REG: staged loads written (and refetched) per k16 step
+  static_assert(!REG || (NS == 2 && LPW % KS == 0 && NFRAG + PPW <= MI * NI && SLOTS == 8 && A_LD == B_LD &&
+                         A_LD % 2 == 0),
+                "register staging");
+  constexpr int LPG = SPREAD ? LPW / FEED : 1;          // SPREAD: loads per k16 step
+  constexpr int GAP = SPREAD ? MI * NI / LPG : 1;       // SPREAD: MFMAs between loads
+  static_assert(FEED >= kFeedReg && (!SPREAD || (NS == 2 && FEED <= KS && LPW % FEED == 0 && LPG <= MI * NI &&
+                                                 MI * NI % LPG == 0)),
+                "spread feed");
   constexpr int ES = CT == 0 ? 4 : 2;
   constexpr int RPP = NW * 32 * (WN + 32 / ES) * ES <= NS * STAGE ? 32 : 16;  // epilogue rows per pass
   static_assert(NW * RPP * (WN + 32 / ES) * ES <= NS * STAGE, "epilogue staging must fit the LDS ring");
@@ -474,12 +518,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
     const int row = (wave * B_LD + i) * RPL + lane / SLOTS;
     b_off[i] = static_cast<uint32_t>((row * K + rswz<SLOTS>(row, lane % SLOTS) * 8) * 2);
   }
+  // REG: A and B rows are indexed alike, and with 8 slots per row the swizzle
+  // depends only on bit 3 of the row, i.e. on the parity of the load index:
+  // load i's lane offset is reg_off[i % 2] from a buffer that starts
+  // (i - i % 2) * RPL rows further (in the base, not the scalar offset, which
+  // the range check of a raw buffer leaves out)
+  uint32_t reg_off[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = (wave * A_LD + p) * RPL + lane / SLOTS;  // swizzled as the direct-to-LDS loads
+    reg_off[p] = static_cast<uint32_t>(((p * RPL + lane / SLOTS) * K + rswz<SLOTS>(row, lane % SLOTS) * 8) * 2);
+  }
   // per-lane LDS offset of a fragment read for k16 step kk (rows are 32-aligned,
   // so the swizzle depends only on the lane's row within the block)
+  // plus the wave's first A row; its B rows sit a wave-uniform distance
+  // further (b_delta), and the fragment's row block is the read's immediate
   const int frow = lane & 31;
-  int frag_off[KS];
+  uint32_t frag_off[KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) frag_off[kk] = frow * ROWB + rswz<SLOTS>(frow, kk * 2 + (lane >> 5)) * 16;
+  for (int kk = 0; kk < KS; ++kk)
+    frag_off[kk] = (wm * WM + frow) * ROWB + rswz<SLOTS>(frow, kk * 2 + (lane >> 5)) * 16;
+  const uint32_t b_delta = static_cast<uint32_t>(A_BYTES + (wn * WN - wm * WM) * ROWB);
 
   if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
     copy_role<THREADS>(a.copy, blockIdx.x, a.copy_blocks, epoch);
@@ -545,6 +604,41 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
+    // REG: load `i` of stage kt (A loads first, then B) goes through a
+    // register; a stage past the last is a zero-length buffer (no access, the
+    // register reads zero), so the loads need no branch
+    u32x4_t rv[REG ? LPW : 1];
+    auto fetch = [&](int kt, int i) {
+      const bool live = kt < nk;
+      const int64_t k0 = static_cast<int64_t>(live ? kt : 0) * TK;
+      const int li = i < A_LD ? i : i - A_LD;
+      const int64_t r0 = static_cast<int64_t>(wave * A_LD + li - li % 2) * RPL;  // the buffer's first row
+      const __amdgpu_buffer_rsrc_t r =
+          i < A_LD ? make_rsrc(a_tile + r0 * K + k0, live ? (rows_valid - r0) * K * 2 - k0 * 2 : 0)
+                   : make_rsrc(b_tile + r0 * K + k0, live ? (cols_valid - r0) * K * 2 - k0 * 2 : 0);
+      rv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, reg_off[li % 2], 0, 0));
+    };
+    // REG: register `i` into stage kt's slot, at the place its direct-to-LDS
+    // load would have written (lane l's 16 bytes at 16 l of the wave's 1 KB)
+    auto put = [&](int kt, int i) {
+      char* const st = smem + (kt % NS) * STAGE;
+      char* const dst = i < A_LD ? st + (wave * A_LD + i) * 1024 : st + A_BYTES + (wave * B_LD + i - A_LD) * 1024;
+      *reinterpret_cast<u32x4_t*>(dst + lane * 16) = rv[i];
+    };
+    // SPREAD: direct-to-LDS load `i` of stage kt; past the last stage a
+    // zero-length buffer (nothing is read; zeros land in the free slot)
+    auto dma_one = [&](int kt, int i) {
+      char* const st = smem + (kt % NS) * STAGE;
+      const bool live = kt < nk;
+      const int64_t k0 = static_cast<int64_t>(live ? kt : 0) * TK;
+      if (i < A_LD)
+        dma_load_16(make_rsrc(a_tile + k0, live ? static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2 : 0),
+                    st + (wave * A_LD + i) * 1024, a_off[i]);
+      else
+        dma_load_16(make_rsrc(b_tile + k0, live ? static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2 : 0),
+                    st + A_BYTES + (wave * B_LD + i - A_LD) * 1024, b_off[i - A_LD]);
+    };
+
     f32x16_t acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -552,89 +646,139 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
       for (int j = 0; j < NI; ++j) acc[i][j] = f32x16_t{};
 
     __syncthreads();  // the previous tile's epilogue is done with the LDS
+    if constexpr (REG) {
+      // stage 0 into its slot, stage 1 into the registers, then the first part
+      // of stage 1 into its slot with stage 2's loads behind it (the rest of
+      // stage 1 is written during stage 0's first k16 steps)
 #pragma unroll
-    for (int s = 0; s < (SPREAD ? NS - 1 : NS); ++s)
-      if (s < nk) issue(s);
+      for (int i = 0; i < LPW; ++i) fetch(0, i);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) put(0, i);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) fetch(1, i);
+#pragma unroll
+      for (int i = 0; i < PPW; ++i) {
+        put(1, i);
+        fetch(2, i);
+      }
+    } else if constexpr (SPREAD) {
+      // stage 0, then the first part of stage 1 (its other parts go out
+      // during stage 0's first k16 steps)
+      if (0 < nk) issue(0);
+#pragma unroll
+      for (int i = 0; i < LPG; ++i) dma_one(1, i);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        if (s < nk) issue(s);
+    }
 
     const uint32_t ring = lds_addr(smem);
-    auto read_frag = [&](uint32_t st, int kk, int f) -> bf16x8_t {
-      const uint32_t off = st + frag_off[kk];
-      return f < MI ? lds_read_b128(off + (wm * WM + f * 32) * ROWB)
-                    : lds_read_b128(off + A_BYTES + (wn * WN + (f - MI) * 32) * ROWB);
+    // fragment F (A blocks first, then B) of one k16 step from per-lane bases
+    auto read_frag = [&](uint32_t abase, uint32_t bbase, auto fc) -> bf16x8_t {
+      constexpr int F = decltype(fc)::value;
+      if constexpr (F < MI)
+        return lds_read_b128_at<F * 32 * ROWB>(abase);
+      else
+        return lds_read_b128_at<(F - MI) * 32 * ROWB>(bbase);
     };
-    // One of the LPW 1 KB loads of stage `stage` (A loads first, then B).  A
-    // stage past the last one gets a zero-length buffer (nothing is read; its
-    // slot is free), so the load needs no branch.
-    auto dma_one = [&](int stage, int idx) {
-      char* st = smem + (stage % NS) * STAGE;
-      const int64_t k0 = static_cast<int64_t>(stage < nk ? stage : 0) * TK;
-      if (idx < A_LD) {
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(a_tile + k0, stage < nk ? static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2 : 0);
-        dma_load_16(ra, st + (wave * A_LD + idx) * 1024, a_off[idx]);
-      } else {
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(b_tile + k0, stage < nk ? static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2 : 0);
-        dma_load_16(rb, st + A_BYTES + (wave * B_LD + idx - A_LD) * 1024, b_off[idx - A_LD]);
-      }
-    };
-    // MFMAs on one fragment set, interleaved with the reads of the next set
-    // and (SPREAD) with part `part` of stage `dstage`'s loads.  The reads are
-    // unconditional: a read whose result the compiler might discard would let
-    // it emit select/copy code on registers that an in-flight asm read is
-    // still going to write.
-    auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk, int dstage, int part) {
-#pragma unroll
-      for (int x = 0; x < MI * NI; ++x) {
-        const int i = x / NI, j = x % NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], cur[MI + j], acc[i][j], 0, 0, 0);
-        if (x < NFRAG) nxt[x] = read_frag(nst, nkk, x);
-        if constexpr (SPREAD) {
-          if (x % GAP == GAP - 1 && x / GAP < PER) dma_one(dstage, part * PER + x / GAP);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      wait_lgkmcnt<0>();
+    // MFMAs on one fragment set, interleaved with the reads of the next set.
+    // The reads are unconditional: a read whose result the compiler might
+    // discard would let it emit select/copy code on registers that an
+    // in-flight asm read is still going to write.
+    // REG: after the reads, part `part` of the staged registers is written
+    // into stage pst's slot and refetched with stage pst + 1; the wait then
+    // leaves those PPW writes in flight (LDS operations complete in order, so
+    // the reads before them have landed).  SPREAD: part `part` (< FEED) of
+    // stage pst's direct-to-LDS loads, one every GAP MFMAs.
+    auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk, int pst, int part) {
+      const uint32_t abase = nst + frag_off[nkk], bbase = abase + b_delta;
+      unroll_each(
+          [&](auto xc) {
+            constexpr int x = decltype(xc)::value, i = x / NI, j = x % NI;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], cur[MI + j], acc[i][j], 0, 0, 0);
+            if constexpr (x < NFRAG) nxt[x] = read_frag(abase, bbase, xc);
+            if constexpr (REG && x >= NFRAG && x < NFRAG + PPW) {
+              put(pst, part * PPW + x - NFRAG);
+              fetch(pst + 1, part * PPW + x - NFRAG);
+            }
+            if constexpr (SPREAD && x % GAP == 0) {
+              if (part < FEED) dma_one(pst, part * LPG + x / GAP);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          },
+          std::make_integer_sequence<int, MI * NI>{});
+      if constexpr (REG)
+        wait_lgkmcnt<PPW>();
+      else
+        wait_lgkmcnt<0>();
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    if constexpr (SPREAD) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) dma_one(NS - 1, i);  // part 0 of stage NS - 1 (zero-length past the end)
-    }
+    // K-sliced copy: the first loads of stage s go out right after the
+    // barrier that ends stage s - LEAD, so thread 0 waits for slice h of the
+    // tile's chunks just before the barrier that precedes the first loads of
+    // slice h (its first stage is h * nk / kslices; slice 0 was waited for at
+    // the tile start, and every slice spans more stages than the prologue
+    // loads).  A slice that never arrives leaves the tile unstored (s_skip),
+    // as at the start.
+    constexpr int LEAD = REG ? 3 : (SPREAD ? 2 : NS);
+    const bool sliced = !RS && a.wait_chunks && a.kslices > 1;
+    int next_h = 1, next_stage = sliced ? nk / a.kslices : nk + LEAD;
+    auto wait_slice = [&](int kt) {
+      if (kt + LEAD == next_stage) {
+        if (tid == 0 && !wait_tile_deps(a, t, epoch, a.slice_flags, kMaxSlices, next_h)) s_skip = 1;
+        ++next_h;
+        next_stage = next_h < a.kslices ? next_h * nk / a.kslices : nk + LEAD;
+      }
+    };
+
     bf16x8_t fp[NFRAG], fq[NFRAG];
-    landed(0);
-#pragma unroll
-    for (int f = 0; f < NFRAG; ++f) fp[f] = read_frag(ring, 0, f);
+    if constexpr (REG) {
+      wait_lgkmcnt<0>();
+      __builtin_amdgcn_s_barrier();  // stage 0 is in its slot for every wave
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      landed(0);
+    }
+    unroll_each([&](auto fc) { fp[decltype(fc)::value] = read_frag(ring + frag_off[0], ring + frag_off[0] + b_delta, fc); },
+                std::make_integer_sequence<int, NFRAG>{});
     wait_lgkmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
-    // SPREAD: the loads of stage kt + NS (into stage kt's slot, free once
-    // stage kt + 1 has landed) are spread over the last k16 step of stage kt
-    // (part 0) and the first KS - 1 steps of stage kt + 1 (parts 1..KS-1), one
-    // load every GAP MFMAs, so no wave stalls on a burst of loads.
-    // Loads of stages past the last are zero-length (see dma_one).  With
-    // SPREAD the prologue issued part 0 of stage NS - 1, so every stage's
-    // first steps carry parts 1.. of stage kt - 1 + NS.
     for (int kt = 0; kt < nk; ++kt) {
       const uint32_t st = ring + (kt % NS) * STAGE;
+      // REG: these steps write parts 1.. of stage kt + 1 into its slot
 #pragma unroll
       for (int kk = 0; kk < KS - 1; kk += 2) {
-        mma(fp, fq, st, kk + 1, kt - 1 + NS, kk + 1);
-        if (kk + 2 < KS) mma(fq, fp, st, kk + 2, kt - 1 + NS, kk + 2);
+        mma(fp, fq, st, kk + 1, kt + 1, kk + 1);
+        if (kk + 2 < KS) mma(fq, fp, st, kk + 2, kt + 1, kk + 2);
       }
       // last k16 step of the stage: its MFMAs read fq; the next stage's first
       // step is read into fp once that stage has landed (after the last
       // stage, a read of an idle slot whose result goes unused)
-      if (kt + 1 < nk) {
+      wait_slice(kt);
+      if constexpr (REG) {
+        // every wave has written stage kt + 1 and read its last fragments of
+        // stage kt: the one slot becomes readable, the other writable (part 0
+        // of stage kt + 2 goes in during the last step)
+        wait_lgkmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (SPREAD) {
+        // the same after the last stage too: the zero-length loads that follow
+        // write into a slot other waves may still be reading until then
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (kt + 1 < nk) {
         landed(kt + 1);
-        if constexpr (!SPREAD) {
-          if (kt + NS < nk) issue(kt + NS);  // into stage kt's slot, free now
-        }
+        if (kt + NS < nk) issue(kt + NS);  // into stage kt's slot, free now
       }
-      mma(fq, fp, ring + ((kt + 1) % NS) * STAGE, 0, kt + NS, 0);
+      mma(fq, fp, ring + ((kt + 1) % NS) * STAGE, 0, kt + 2, 0);
     }
-    if constexpr (SPREAD) wait_vmcnt<0>();  // zero-length loads of the last steps have landed too
+    if constexpr (SPREAD) wait_vmcnt<0>();  // the zero-length loads after the last stage have landed
     __syncthreads();  // every wave is done reading the ring before the epilogue reuses it
+    if (sliced && s_skip) continue;  // a slice never arrived: tile left untouched
     store_tile_w<TM, TN, CT, WGM, WGN, RPP>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane);
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
     if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
@@ -652,12 +796,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
 // LDS holds at the tile's workgroups per CU (128x128 runs two per CU); the
 // 256x256 tile runs eight waves, two per SIMD, so that one wave's waits are
 // covered by the other's MFMAs (measured 124 us against 137 us with four
-// waves on 8192x1792x4096).  Spreading the stage loads between the MFMAs
-// (SpreadLoads) needs a ring of three or more slots and measured slower on
-// this tile (TK=32, four slots: 132 us), so it is off.
-template <int TM, int TN> struct DmaShape { static constexpr int TK = 64, NS = 2, WGM = 2, WGN = 2; };
-template <> struct DmaShape<256, 128> { static constexpr int TK = 64, NS = 3, WGM = 2, WGN = 2; };
-template <> struct DmaShape<256, 256> { static constexpr int TK = 64, NS = 2, WGM = 2, WGN = 4; };
+// waves on 8192x1792x4096).
+template <int TM, int TN> struct DmaShape { static constexpr int TK = 64, NS = 2, WGM = 2, WGN = 2, FEED = 0; };
+template <> struct DmaShape<256, 128> { static constexpr int TK = 64, NS = 3, WGM = 2, WGN = 2, FEED = 0; };
+template <> struct DmaShape<256, 256> { static constexpr int TK = 64, NS = 2, WGM = 2, WGN = 4, FEED = 0; };
 
 hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid,
                        hipStream_t stream) {
@@ -666,10 +808,10 @@ hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dt
     using S_ = DmaShape<TM_, TN_>;                                                                       \
     const dim3 block(64 * S_::WGM * S_::WGN);                                                           \
     if (rs)                                                                                              \
-      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, true, S_::TK, S_::NS, S_::WGM, S_::WGN>), dim3(grid), block, 0, \
+      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, true, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>), dim3(grid), block, 0, \
                          stream, a);                                                                     \
     else                                                                                                 \
-      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, false, S_::TK, S_::NS, S_::WGM, S_::WGN>), dim3(grid), block, 0, \
+      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, false, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>), dim3(grid), block, 0, \
                          stream, a);                                                                     \
     return hipGetLastError();                                                                            \
   }

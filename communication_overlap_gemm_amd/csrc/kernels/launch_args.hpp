@@ -5,12 +5,16 @@
 
 namespace syncov {
 
+constexpr int kMaxSlices = 8;  // K-slices per chunk (copy_kslices) the workspace holds
+
 // Per-chunk counter arrays of the workspace (cleared by the workgroup that
 // completes them; after a failed call, by the call's last workgroup).
 struct CounterArrays {
   uint32_t* counters;  // GEMM-RS: tiles stored per chunk
-  uint32_t* parts;     // copy role: XCDs finished per chunk
+  uint32_t* parts;     // copy role: XCDs finished per chunk (K-sliced copy: slices finished)
   uint32_t* xparts;    // copy role: workgroups finished per (chunk, XCD), C x 16
+  uint32_t* sparts;    // K-sliced copy: XCDs finished per (chunk, slice), C x kMaxSlices
+  uint32_t* sxparts;   // K-sliced copy: workgroups finished per (chunk, slice, XCD), C x kMaxSlices x 16
   int32_t num_chunks;
 };
 
@@ -36,6 +40,16 @@ struct CopyArgs {
   int32_t skip_chunk;  // copy-in: chunk left out (failure-path tests); -1 = all, -2 = none
   int32_t teams;       // copy-in: chunks in flight at once (1 = one after another)
   uint64_t* trace_chunks;  // SYNC_RUN_TRACE: per chunk {ready, sent} wall-clock stamps, or null
+  // copy-in K-slices: with kslices > 1 every chunk moves as kslices column
+  // blocks of its rows, slice by slice across all chunks (slice 0 of every
+  // chunk first); slice h of chunk c raises slice_flags[c * kMaxSlices + h]
+  // and the last of a chunk's slices raises out_flags[c].  Slice h holds the
+  // 128-byte row columns [h * R / kslices, (h + 1) * R / kslices) of each
+  // tensor, R = row_bytes / 128.
+  int32_t kslices;
+  uint32_t* slice_flags;
+  uint32_t* sparts;
+  uint32_t* sxparts;
 };
 
 // Persistent GEMM (gemm_persistent.hip).  Workgroups [0, copy_blocks) of the
@@ -61,6 +75,11 @@ struct GemmArgs {
   int32_t colocated;        // AG: every compute workgroup first copies its share of each chunk
   uint64_t* trace_tiles;    // SYNC_RUN_TRACE: per tile {wait begin, wait end, end, xcc<<32 | slot}, or null
   uint64_t* trace_chunks;   // SYNC_RUN_TRACE: per chunk {ready/done, sent}, or null
+  // AG with a K-sliced copy (kslices > 1): a tile waits for slice 0 of its
+  // chunks before its first loads and for slice h before the loads of the
+  // first K-step of slice h (slice_flags as in CopyArgs)
+  int32_t kslices;
+  const uint32_t* slice_flags;
   CopyArgs copy;
 };
 

@@ -268,15 +268,22 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
 // to 256 bytes: flags (ready / done), counters (GEMM tiles stored per chunk),
 // parts (copy XCD groups finished per chunk), sent (copy-out done); then
 // xparts, uint32[C][16] (copy workgroups finished per chunk and XCD); then the
+// K-sliced copy's sflags and sparts, uint32[C][8] each (ready flag and XCD
+// groups finished per chunk slice), and sxparts, uint32[C][8][16]; then the
 // trace: uint64[T][4] per tile and uint64[C][2] per chunk (SYNC_RUN_TRACE).
 struct WsView {
-  uint32_t *hdr, *flags, *counters, *parts, *sent, *xparts;
+  uint32_t *hdr, *flags, *counters, *parts, *sent, *xparts, *sflags, *sparts, *sxparts;
   uint64_t *trace_tiles, *trace_chunks;
 };
 
 int64_t ws_array_bytes(int32_t C) { return align_up(static_cast<int64_t>(C) * 4, 256); }
+int64_t ws_xparts_bytes(int32_t C) { return align_up(static_cast<int64_t>(C) * 4 * kMaxXcd, 256); }
+int64_t ws_slice_bytes(int32_t C) { return align_up(static_cast<int64_t>(C) * 4 * kMaxSlices, 256); }
 
-int64_t ws_trace_offset(int32_t C) { return 256 + 4 * ws_array_bytes(C) + align_up(static_cast<int64_t>(C) * 4 * kMaxXcd, 256); }
+int64_t ws_trace_offset(int32_t C) {
+  return 256 + 4 * ws_array_bytes(C) + ws_xparts_bytes(C) + 2 * ws_slice_bytes(C) +
+         align_up(static_cast<int64_t>(C) * 4 * kMaxSlices * kMaxXcd, 256);
+}
 
 int64_t ws_total_bytes(int32_t C, int32_t T) {
   return ws_trace_offset(C) + align_up(static_cast<int64_t>(T) * 32, 256) + align_up(static_cast<int64_t>(C) * 16, 256);
@@ -292,6 +299,10 @@ WsView ws_view(void* ws, int32_t C, int32_t T) {
   v.parts = reinterpret_cast<uint32_t*>(b + 256 + 2 * a);
   v.sent = reinterpret_cast<uint32_t*>(b + 256 + 3 * a);
   v.xparts = reinterpret_cast<uint32_t*>(b + 256 + 4 * a);
+  const int64_t s0 = 256 + 4 * a + ws_xparts_bytes(C);
+  v.sflags = reinterpret_cast<uint32_t*>(b + s0);
+  v.sparts = reinterpret_cast<uint32_t*>(b + s0 + ws_slice_bytes(C));
+  v.sxparts = reinterpret_cast<uint32_t*>(b + s0 + 2 * ws_slice_bytes(C));
   const int64_t t0 = ws_trace_offset(C);
   v.trace_tiles = reinterpret_cast<uint64_t*>(b + t0);
   v.trace_chunks = reinterpret_cast<uint64_t*>(b + t0 + align_up(static_cast<int64_t>(T) * 32, 256));
@@ -316,6 +327,17 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   if (cfg.copy_teams < 0 || cfg.copy_teams > plan->plan.num_chunks)
     return fail(SYNC_EINVAL, "copy_teams must be in [0, number of chunks]");
   if (cfg.copy_teams == 0) cfg.copy_teams = 1;
+  if (cfg.copy_kslices < 0 || cfg.copy_kslices > kMaxSlices) return fail(SYNC_EINVAL, "copy_kslices must be in [0, 8]");
+  if (cfg.copy_kslices == 0) cfg.copy_kslices = 1;
+  if (cfg.copy_kslices > 1) {
+    const sync_plan_desc& d = plan->plan.desc;
+    if (op != SYNC_OP_AG_GEMM || d.b_layout != SYNC_B_NK)
+      return fail(SYNC_EINVAL, "copy_kslices > 1 is for AG-GEMM with B stored [n][k]");
+    if (cfg.backend == SYNC_COPY_SDMA || cfg.backend == SYNC_COPY_HOST_GATED)
+      return fail(SYNC_EINVAL, "copy_kslices > 1 needs the CU, COLOCATED or PRESET backend");
+    if (d.k / 64 < 4 * static_cast<int64_t>(cfg.copy_kslices))
+      return fail(SYNC_EINVAL, "copy_kslices > 1 needs K/64 >= 4 x copy_kslices");
+  }
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
@@ -389,7 +411,9 @@ int check_gemm_shape(const Plan& pl) {
 // same launch take CUs at the same rate).
 int gemm_wg_per_cu(const Plan& pl) { return (pl.desc.tile_m == 128 && pl.desc.tile_n == 128) ? 2 : 1; }
 
-CounterArrays counter_arrays(const CallCtx& cx, int32_t C) { return CounterArrays{cx.ws.counters, cx.ws.parts, cx.ws.xparts, C}; }
+CounterArrays counter_arrays(const CallCtx& cx, int32_t C) {
+  return CounterArrays{cx.ws.counters, cx.ws.parts, cx.ws.xparts, cx.ws.sparts, cx.ws.sxparts, C};
+}
 
 GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const void* B, void* C) {
   GemmArgs g{};
@@ -415,6 +439,8 @@ GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const 
   g.copy_blocks = 0;
   g.trace_tiles = (cx.cfg.flags & SYNC_RUN_TRACE) ? cx.ws.trace_tiles : nullptr;
   g.trace_chunks = (cx.cfg.flags & SYNC_RUN_TRACE) ? cx.ws.trace_chunks : nullptr;
+  g.kslices = cx.cfg.copy_kslices;
+  g.slice_flags = cx.ws.sflags;
   return g;
 }
 
@@ -443,6 +469,10 @@ CopyArgs make_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2
   ca.skip_chunk = (cx.cfg.flags & SYNC_RUN_WITHHOLD) ? cx.cfg.withhold_chunk : -2;
   ca.teams = cx.cfg.copy_teams;
   ca.trace_chunks = (cx.cfg.flags & SYNC_RUN_TRACE) ? cx.ws.trace_chunks : nullptr;
+  ca.kslices = cx.cfg.copy_kslices;  // > 1 only for AG-GEMM (checked by prepare)
+  ca.slice_flags = cx.ws.sflags;
+  ca.sparts = cx.ws.sparts;
+  ca.sxparts = cx.ws.sxparts;
   return ca;
 }
 

@@ -202,6 +202,14 @@ typedef struct {
                                for its chunk's done flag).  0 or 1 = one chunk after another
                                (ring arrival); the number of copied chunks = all at once (pulls
                                from every peer in parallel, as over a full xGMI mesh). */
+  int32_t copy_kslices;     /* AG-GEMM with B [n][k] and the CU or COLOCATED backend: every chunk
+                               moves as this many column blocks (K-slices) of its rows, slice 0
+                               of every chunk first, each slice with its own ready flag; a tile
+                               starts on slice 0 of its rows and waits in-kernel for slice h
+                               just before it loads that K range, so tiles of late chunks start
+                               early.  The chunk plan, dependency table and tile order are
+                               unchanged.  0 or 1 = whole chunks; at most 8, with K/64 at least
+                               4 x copy_kslices.  Other ops and backends: 0 or 1. */
 } sync_copy_cfg;
 
 /* ---- workspace ---------------------------------------------------------- */

@@ -74,10 +74,12 @@ def test_wrong_op_for_plan():
 def test_workspace_size_scales_with_chunks():
     p1 = A.sync_plan(A.make_desc(1, 64, 8, 64, 4, split=1, tile_m=2, tile_n=2))
     p2 = A.sync_plan(A.make_desc(1, 4096, 8, 64, 4, split=256, tile_m=2, tile_n=2))
-    # header + four uint32[C] arrays + uint32[C][16], then the trace: uint64[T][4] and
+    # header + four uint32[C] arrays + uint32[C][16], the K-sliced copy's two
+    # uint32[C][8] and uint32[C][8][16], then the trace: uint64[T][4] and
     # uint64[C][2]; each array padded to 256 bytes
-    assert A.sync_workspace_size(p1) == 256 + 4 * 256 + 256 + 128 * 32 + 256
-    assert A.sync_workspace_size(p2) == 256 + 4 * 4096 + 1024 * 64 + 8192 * 32 + 1024 * 16
+    assert A.sync_workspace_size(p1) == 256 + 4 * 256 + 256 + 2 * 256 + 2048 + 128 * 32 + 256
+    assert A.sync_workspace_size(p2) == (256 + 4 * 4096 + 1024 * 64 + 2 * 1024 * 32 + 1024 * 512 + 8192 * 32
+                                         + 1024 * 16)
 
 
 def test_withhold_and_trace_validation():
@@ -92,3 +94,25 @@ def test_withhold_and_trace_validation():
     tr = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, flags=A.SYNC_RUN_TRACE)
     rc = A.lib().sync_ring_attn_step(pa.handle, ctypes.byref(tr), *([None] * 9), 1.0, 0, 256, None, None)
     assert rc == A.SYNC_EINVAL and "TRACE" in A.sync_last_error()
+
+
+def test_kslices_validation():
+    """copy_kslices is checked before any device work: range, op, B layout,
+    backend, and at least four 64-deep K steps per slice."""
+    def rc_of(plan, cfg):
+        return A.lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg), None, None, None, None, 0, 256, None, None)
+    nk = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    assert rc_of(nk, A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=9)) == A.SYNC_EINVAL
+    assert "[0, 8]" in A.sync_last_error()
+    assert rc_of(nk, A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=-1)) == A.SYNC_EINVAL
+    assert rc_of(nk, A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=5)) == A.SYNC_EINVAL  # 1024/64 = 16 < 20
+    assert "K/64" in A.sync_last_error()
+    assert rc_of(nk, A.make_cfg(A.SYNC_COPY_SDMA, copy_kslices=2)) == A.SYNC_EINVAL
+    assert "COLOCATED" in A.sync_last_error()
+    kn = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_KN))
+    assert rc_of(kn, A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2)) == A.SYNC_EINVAL
+    assert "[n][k]" in A.sync_last_error()
+    rs = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    rc = A.lib().sync_gemm_rs(rs.handle, ctypes.byref(A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2)), None, None,
+                              None, 0, None, 256, None, None)
+    assert rc == A.SYNC_EINVAL and "AG-GEMM" in A.sync_last_error()

@@ -22,9 +22,10 @@ LAYOUT = {"kn": A.SYNC_B_KN, "nk": A.SYNC_B_NK}
 
 
 def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
-           backend=A.SYNC_COPY_SDMA, copy_cus=0, c_dtype=A.SYNC_DTYPE_F32, rank=0, poison=True, flags=0, teams=0):
+           backend=A.SYNC_COPY_SDMA, copy_cus=0, c_dtype=A.SYNC_DTYPE_F32, rank=0, poison=True, flags=0, teams=0,
+           kslices=0):
     print(f"[ag] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
-          f"cus={copy_cus} dtype={c_dtype} layout={layout}", flush=True)
+          f"cus={copy_cus} dtype={c_dtype} layout={layout} teams={teams} kslices={kslices}", flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, rank=rank, split=split, tile_m=tile[0],
                                    tile_n=tile[1], tile_order=order, b_layout=LAYOUT[layout]))
     tabs = A.sync_plan_export(plan)
@@ -43,7 +44,7 @@ def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128)
     else:
         c = bf16_poison((m, n))
     ws = workspace(plan)
-    cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags, copy_teams=teams)
+    cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags, copy_teams=teams, copy_kslices=kslices)
     s = torch.cuda.current_stream()
     A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
@@ -412,3 +413,81 @@ def test_full_size_70b_like(split, teams):
     for s in range(W4):
         sel = shard == s
         assert np.linalg.norm(got[sel] - ref[sel]) <= 1e-3 * np.linalg.norm(ref[sel]), s
+
+
+# ---- K-sliced copy-in: chunks move as column slices, tiles start on slice 0 --
+
+@pytest.mark.parametrize("backend,cus,teams,kslices,tile", [
+    (A.SYNC_COPY_CU, 8, 1, 2, (256, 256)), (A.SYNC_COPY_CU, 16, 3, 4, (256, 128)),
+    (A.SYNC_COPY_CU, 8, 5, 3, (128, 128)), (A.SYNC_COPY_COLOCATED, 0, 3, 4, (256, 256)),
+    (A.SYNC_COPY_COLOCATED, 0, 1, 2, (256, 256))])
+def test_kslices_parity(backend, cus, teams, kslices, tile):
+    """K = 1152 (18 K-steps: uneven slices); the output matches the oracle and
+    is bitwise the compute-only output (the copy protocol changes only when
+    a K-step's operands are known to be in place)."""
+    m, n, k, world, split = 2048, 768, 1152, 4, 2
+    a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    out, a_local = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=backend,
+                          copy_cus=cus, teams=teams, kslices=kslices)
+    check_f32(out, ref, world)
+    assert np.array_equal(a_local, a)  # every slice of every chunk was staged
+    base, _ = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=A.SYNC_COPY_PRESET)
+    assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
+
+
+def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles():
+    """A withheld chunk under a K-sliced copy: none of its slices land, the
+    tiles that read it stay unwritten, the others are correct, and the timeout
+    names the chunk (not a slice)."""
+    m, n, k, world, split = 1024, 512, 512, 4, 2
+    a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, split=split, tile_m=128, tile_n=128,
+                                   b_layout=A.SYNC_B_NK))
+    tabs = A.sync_plan_export(plan)
+    victim = int(tabs["arrival"][4])
+    assert not tabs["resident"][victim]
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    a_local = torch.zeros_like(a_peer)
+    for ch in range(tabs["num_chunks"]):
+        if tabs["resident"][ch]:
+            r0, r1 = tabs["chunk_begin"][ch], tabs["chunk_begin"][ch + 1]
+            a_local[r0:r1] = a_peer[r0:r1]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    cfg = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, timeout_ns=2_000_000, flags=A.SYNC_RUN_WITHHOLD,
+                     withhold_chunk=victim, copy_teams=3, copy_kslices=2)
+    print(f"[ag] kslices=2 withhold chunk {victim}", flush=True)
+    A.sync_ag_gemm(plan, cfg, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_ETIMEOUT and chunk == victim
+    out = c.cpu().numpy()
+    skipped = set(tabs["inv_idx"][tabs["inv_ptr"][victim]:tabs["inv_ptr"][victim + 1]].tolist())
+    tn = tabs["tiles_n"]
+    for t in range(tabs["num_tiles"]):
+        i, j = divmod(t, tn)
+        blk = out[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+        if t in skipped:
+            assert np.isnan(blk).all(), f"tile {t} reads the withheld chunk but was written"
+        else:
+            r = ref[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            assert np.isfinite(blk).all() and np.linalg.norm(blk - r) <= 1e-3 * np.linalg.norm(r), f"tile {t}"
+
+
+@pytest.mark.parametrize("backend,cus,teams,kslices", [(A.SYNC_COPY_CU, 32, 7, 4), (A.SYNC_COPY_CU, 32, 7, 8),
+                                                       (A.SYNC_COPY_COLOCATED, 0, 7, 4)])
+def test_full_size_kslices(backend, cus, teams, kslices):
+    """The Llama-3-8B up-projection share with a K-sliced copy: sampled parity
+    against the oracle per row shard."""
+    a, b = inputs.gemm_operands(M2, N2, K2, 64.0, b_layout="nk")
+    out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), backend=backend, copy_cus=cus, layout="nk",
+                    teams=teams, kslices=kslices)
+    assert np.isfinite(out).all()
+    rows, cols = _samples(M2, N2, 20000, seed=3)
+    ref = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout="nk")
+    shard = rows // (M2 // W2)
+    for s in range(W2):
+        sel = shard == s
+        assert np.linalg.norm(out[rows[sel], cols[sel]] - ref[sel]) / np.linalg.norm(ref[sel]) <= 1e-3
