@@ -37,7 +37,7 @@ BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
 PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk",
-            "teams": 7}
+            "teams": 7, "kslices": 4}
 
 
 def profiled_traffic(args):
