@@ -33,11 +33,12 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 M, N, K, WORLD = 8192, 1792, 4096, 8
 DIVISOR = 64.0
 
+STORE_POLICIES = {"plain": 0, "stream": 1, "wt": 2}
 BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64), "colocated": (4, 0)}
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
 PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk",
-            "teams": 7, "kslices": 4}
+            "teams": 7, "kslices": 4, "copy_store": "plain"}
 
 
 def profiled_traffic(args):
@@ -82,6 +83,8 @@ def parse():
     p.add_argument("--kslices", type=int, default=4,
                    help="K-slices per copied chunk (1: whole chunks; >1: slice 0 of every chunk first, tiles start "
                         "on it and wait in-kernel for the later slices)")
+    p.add_argument("--copy-store", default="plain", choices=sorted(STORE_POLICIES),
+                   help="store policy of the copy role: plain, non-temporal (stream) or write-through (wt)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-rows", action="store_true", help="skip the RS, 70B-like AG and attention rows")
     p.add_argument("--tune", action="store_true",
@@ -143,6 +146,7 @@ def main():
         torch.cuda.synchronize()
         A.sync_read_timings(0)  # drop warm-up records
         cfg_t = A.make_cfg(cfg.backend, cfg.copy_cus, cfg.timeout_ns, None, cfg.flags | A.SYNC_RUN_TIMED,
+                           copy_streaming=cfg.copy_streaming,
                            copy_teams=cfg.copy_teams, copy_kslices=cfg.copy_kslices)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -157,12 +161,15 @@ def main():
         return wall, recs
 
     # overlapped (the metric), compute-only on the full chip, copy-only
-    t_ovl, recs = timed_loop(A.make_cfg(backend, cus, copy_teams=args.teams, copy_kslices=args.kslices), args.steps,
+    pol = STORE_POLICIES[args.copy_store]
+    t_ovl, recs = timed_loop(A.make_cfg(backend, cus, copy_teams=args.teams, copy_kslices=args.kslices,
+                                        copy_streaming=pol), args.steps,
                              args.warmup)
     k_ms = float(np.mean([r[0] for r in recs]))
     t_comp, recs_c = timed_loop(A.make_cfg(A.SYNC_COPY_PRESET), args.steps, args.warmup)
     k_comp_ms = float(np.mean([r[0] for r in recs_c]))
     t_copy, recs_p = timed_loop(A.make_cfg(backend, cus, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=args.teams,
+                                           copy_streaming=pol,
                                            copy_kslices=args.kslices), args.steps, args.warmup)
     # CU backend: the copy-only launch is the copy role alone; SDMA: the copies' span
     copy_only_ms = float(np.mean([r[1] if backend == A.SYNC_COPY_SDMA else r[0] for r in recs_p]))
@@ -194,7 +201,7 @@ def main():
                         "8 row chunks (N(0,1)/64), B 4096x1792 bf16, C 8192x1792 " + args.c_dtype,
             "m": M, "n": N, "k": K, "world": WORLD, "split": args.split, "tile": args.tile,
             "tile_order": args.order, "copy_backend": args.backend, "copy_teams": args.teams,
-            "copy_kslices": args.kslices, "b_layout": args.layout,
+            "copy_kslices": args.kslices, "copy_store": args.copy_store, "b_layout": args.layout,
         },
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "overlap": {
@@ -222,7 +229,7 @@ def main():
         line["autotune"] = tuned
     if not args.no_other_rows:
         del a_peer, a_local, b, c_out
-        line["other_rows"] = other_rows()
+        line["other_rows"] = other_rows(pol=pol)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a_bits, b_bits, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -278,7 +285,7 @@ def _ws(plan, torch, A):
     return ws
 
 
-def other_rows(steps=5, warmup=2):
+def other_rows(steps=5, warmup=2, pol=0):
     """The other rows of the hot path on their configurations (one line each in
     the output): GEMM-RS share (Llama-3-8B down-projection), AG-GEMM share
     (70B-like FFN), ring-attention local step (Qwen-like GQA)."""
@@ -307,8 +314,8 @@ def other_rows(steps=5, warmup=2):
     st = torch.empty_like(c)
     ws = _ws(plan, torch, A)
     t = {}
-    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_COLOCATED, copy_teams=8)),
-                      ("overlapped_32_copy_cus", A.make_cfg(A.SYNC_COPY_CU, 32)),
+    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_COLOCATED, copy_teams=8, copy_streaming=pol)),
+                      ("overlapped_32_copy_cus", A.make_cfg(A.SYNC_COPY_CU, 32, copy_streaming=pol)),
                       ("compute_only", A.make_cfg(A.SYNC_COPY_PRESET))):
         t[name] = _time_calls(lambda: A.sync_gemm_rs(plan, cfg, a, b, c, A.SYNC_DTYPE_F32, st, ws, s, None), steps,
                               warmup)
@@ -339,9 +346,10 @@ def other_rows(steps=5, warmup=2):
     c = torch.empty((m, n), dtype=torch.float32, device=dev)
     ws = _ws(plan, torch, A)
     t = {}
-    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7)),
+    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7, copy_streaming=pol)),
                       ("compute_only", A.make_cfg(A.SYNC_COPY_PRESET)),
-                      ("copy_only", A.make_cfg(A.SYNC_COPY_CU, 32, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=7))):
+                      ("copy_only", A.make_cfg(A.SYNC_COPY_CU, 32, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=7,
+                                                copy_streaming=pol))):
         t[name] = _time_calls(lambda: A.sync_ag_gemm(plan, cfg, ap, al, b, c, A.SYNC_DTYPE_F32, ws, s, None), steps,
                               warmup)
         check(ws)
@@ -369,8 +377,8 @@ def other_rows(steps=5, warmup=2):
     ws = _ws(plan, torch, A)
     t = {}
     fl = A.SYNC_ATTN_INIT | A.SYNC_ATTN_FINALIZE
-    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_COLOCATED)),
-                      ("overlapped_32_copy_cus", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7)),
+    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_COLOCATED, copy_streaming=pol)),
+                      ("overlapped_32_copy_cus", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7, copy_streaming=pol)),
                       ("compute_only", A.make_cfg(A.SYNC_COPY_PRESET))):
         t[name] = _time_calls(lambda: A.sync_ring_attn_step(plan, cfg, q, kp, vp, kl, vl, o, ms, ls, lse,
                                                             1.0 / d ** 0.5, fl, ws, s, None), steps, warmup)

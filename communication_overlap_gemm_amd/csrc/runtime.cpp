@@ -338,7 +338,7 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
     if (d.k / 64 < 4 * static_cast<int64_t>(cfg.copy_kslices))
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs K/64 >= 4 x copy_kslices");
   }
-  if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
+  if (cfg.copy_streaming < 0 || cfg.copy_streaming > 2) return fail(SYNC_EINVAL, "copy_streaming must be 0, 1 or 2");
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
@@ -353,6 +353,14 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
     return fail(SYNC_EINVAL, "COPY_ONLY and COMPUTE_ONLY are exclusive");
   if ((cfg.flags & SYNC_RUN_COPY_ONLY) && cfg.backend == SYNC_COPY_PRESET)
     return fail(SYNC_EINVAL, "COPY_ONLY needs a copy backend");
+  if (cfg.copy_streaming == 2) {  // write-through stores address a chunk with 32-bit buffer offsets
+    const sync_plan_desc& d = plan->plan.desc;
+    const int64_t rb = op == SYNC_OP_GEMM_RS ? d.n * 4 : op == SYNC_OP_RING_ATTN ? int64_t(d.heads_kv) * d.k * 2 : d.k * 2;
+    int64_t rows = 0;
+    for (int32_t c = 0; c < plan->plan.num_chunks; ++c)
+      rows = std::max<int64_t>(rows, plan->plan.chunk_begin[c + 1] - plan->plan.chunk_begin[c]);
+    if (rows * rb >= (int64_t(1) << 31)) return fail(SYNC_EUNSUPPORTED, "copy_streaming 2 needs chunks below 2 GiB");
+  }
   int rc = current_device_state(&cx.dev);
   if (rc) return rc;
   if (cfg.backend == SYNC_COPY_CU) {

@@ -23,9 +23,10 @@ LAYOUT = {"kn": A.SYNC_B_KN, "nk": A.SYNC_B_NK}
 
 def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
            backend=A.SYNC_COPY_SDMA, copy_cus=0, c_dtype=A.SYNC_DTYPE_F32, rank=0, poison=True, flags=0, teams=0,
-           kslices=0):
+           kslices=0, streaming=0):
     print(f"[ag] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
-          f"cus={copy_cus} dtype={c_dtype} layout={layout} teams={teams} kslices={kslices}", flush=True)
+          f"cus={copy_cus} dtype={c_dtype} layout={layout} teams={teams} kslices={kslices} streaming={streaming}",
+          flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, rank=rank, split=split, tile_m=tile[0],
                                    tile_n=tile[1], tile_order=order, b_layout=LAYOUT[layout]))
     tabs = A.sync_plan_export(plan)
@@ -44,7 +45,8 @@ def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128)
     else:
         c = bf16_poison((m, n))
     ws = workspace(plan)
-    cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags, copy_teams=teams, copy_kslices=kslices)
+    cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags, copy_teams=teams, copy_kslices=kslices,
+                     copy_streaming=streaming)
     s = torch.cuda.current_stream()
     A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
@@ -491,3 +493,35 @@ def test_full_size_kslices(backend, cus, teams, kslices):
     for s in range(W2):
         sel = shard == s
         assert np.linalg.norm(out[rows[sel], cols[sel]] - ref[sel]) / np.linalg.norm(ref[sel]) <= 1e-3
+
+
+# ---- store policy of the copy role: plain, non-temporal, write-through -----
+
+@pytest.mark.parametrize("streaming", [1, 2])
+@pytest.mark.parametrize("backend,cus,teams,kslices", [(A.SYNC_COPY_CU, 16, 1, 0), (A.SYNC_COPY_CU, 16, 3, 4),
+                                                       (A.SYNC_COPY_COLOCATED, 0, 0, 0)])
+def test_copy_store_policies(streaming, backend, cus, teams, kslices):
+    """Non-temporal and write-through stores stage the same bytes and give an
+    output bitwise equal to the compute-only one (exact small integers)."""
+    m, n, k, world, split = 2048, 768, 1152, 4, 2
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    out, a_local = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=(256, 256), backend=backend,
+                          copy_cus=cus, teams=teams, kslices=kslices, streaming=streaming)
+    assert np.array_equal(a_local, a)
+    assert np.array_equal(out.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("streaming", [1, 2])
+def test_full_size_write_through_copy(streaming):
+    """The Llama-3-8B up-projection share with the bench's copy (32 copy CUs in
+    7 teams, 4 K-slices) under each non-default store policy: exact for
+    small-integer operands on sampled outputs, every copied row staged."""
+    a, b = inputs.gemm_operands(M2, N2, K2, 1.0, integer=True, b_layout="nk")
+    out, a_local = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), backend=A.SYNC_COPY_CU, copy_cus=32, layout="nk",
+                          teams=7, kslices=4, streaming=streaming)
+    assert np.array_equal(a_local, a)
+    rows, cols = _samples(M2, N2, 4000, seed=5)
+    exact = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout="nk")
+    assert np.array_equal(out[rows, cols].astype(np.float64), exact)
+

@@ -32,9 +32,10 @@ def ws_arrays(ws, num_chunks):
 
 
 def run_rs(m, n, k, world, a_bits, b_bits, split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
-           backend=A.SYNC_COPY_CU, copy_cus=16, c_dtype=A.SYNC_DTYPE_F32, rank=0, layout=A.SYNC_B_KN, teams=0):
+           backend=A.SYNC_COPY_CU, copy_cus=16, c_dtype=A.SYNC_DTYPE_F32, rank=0, layout=A.SYNC_B_KN, teams=0,
+           streaming=0):
     print(f"[rs] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
-          f"cus={copy_cus} dtype={c_dtype}", flush=True)
+          f"cus={copy_cus} dtype={c_dtype} teams={teams} streaming={streaming}", flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, world, rank=rank, split=split, tile_m=tile[0],
                                    tile_n=tile[1], tile_order=order, b_layout=layout))
     tabs = A.sync_plan_export(plan)
@@ -48,8 +49,8 @@ def run_rs(m, n, k, world, a_bits, b_bits, split=1, tile=(128, 128), order=A.SYN
         staging = bf16_poison((m, n))
     ws = workspace(plan)
     s = torch.cuda.current_stream()
-    A.sync_gemm_rs(plan, A.make_cfg(backend, copy_cus=copy_cus, copy_teams=teams), a, b, c, c_dtype, staging, ws, s,
-                   None)
+    A.sync_gemm_rs(plan, A.make_cfg(backend, copy_cus=copy_cus, copy_teams=teams, copy_streaming=streaming), a, b, c,
+                   c_dtype, staging, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
     assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
     torch.cuda.synchronize()
@@ -199,3 +200,17 @@ def test_full_size_rs_colocated_exact():
     cols = np.random.default_rng(4).integers(0, n, 3000)
     exact = oracle.gemm_f64_sampled(a, b, m, n, k, rows, cols, b_layout="nk")
     assert np.array_equal(cn[rows, cols].astype(np.float64), exact)
+
+
+@pytest.mark.parametrize("streaming", [1, 2])
+@pytest.mark.parametrize("backend,cus,teams", [(A.SYNC_COPY_CU, 16, 0), (A.SYNC_COPY_CU, 16, 4),
+                                               (A.SYNC_COPY_COLOCATED, 0, 4)])
+def test_rs_copy_store_policies(streaming, backend, cus, teams):
+    """Copy-out under non-temporal and write-through stores: exact C and every
+    chunk bitwise in its send slot."""
+    m, n, k, W = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    cn, st, tabs = run_rs(m, n, k, W, a, b, split=1, backend=backend, copy_cus=cus, teams=teams, streaming=streaming)
+    assert np.array_equal(cn.astype(np.float64), ref)
+    check_staging(cn, st, tabs)

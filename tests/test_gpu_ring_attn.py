@@ -25,9 +25,9 @@ TOL = 2e-3
 
 
 def run_attn(sq, hq, hkv, world, n, q_bits, k_bits, v_bits, split=1, backend=A.SYNC_COPY_CU, cus=16,
-             flags=A.SYNC_ATTN_INIT | A.SYNC_ATTN_FINALIZE, scale=1 / math.sqrt(D), rank=0, state=None):
+             flags=A.SYNC_ATTN_INIT | A.SYNC_ATTN_FINALIZE, scale=1 / math.sqrt(D), rank=0, state=None, streaming=0):
     print(f"[attn] sq={sq} hq={hq} hkv={hkv} W={world} n={n} split={split} backend={backend} cus={cus} "
-          f"flags={flags}", flush=True)
+          f"flags={flags} streaming={streaming}", flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_RING_ATTN, sq, n, D, world, rank=rank, split=split, tile_m=128,
                                    tile_n=1, heads_q=hq, heads_kv=hkv))
     tabs = A.sync_plan_export(plan)
@@ -51,7 +51,7 @@ def run_attn(sq, hq, hkv, world, n, q_bits, k_bits, v_bits, split=1, backend=A.S
     lse = torch.full((hq, sq), float("nan"), dtype=torch.float32, device="cuda:0")
     ws = workspace(plan)
     s = torch.cuda.current_stream()
-    A.sync_ring_attn_step(plan, A.make_cfg(backend, copy_cus=cus), q, k_peer, v_peer, k_local, v_local, o, m, l,
+    A.sync_ring_attn_step(plan, A.make_cfg(backend, copy_cus=cus, copy_streaming=streaming), q, k_peer, v_peer, k_local, v_local, o, m, l,
                           lse, scale, flags, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
     assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
@@ -120,3 +120,15 @@ def test_full_size_sampled():
     assert np.isfinite(on).all()
     assert np.max(np.abs(on[qi, hi] - ref_o)) <= TOL
     assert np.max(np.abs(ln_[hi, qi] - ref_lse)) <= TOL
+
+
+@pytest.mark.parametrize("streaming", [1, 2])
+@pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_CU, 8), (A.SYNC_COPY_COLOCATED, 0)])
+def test_copy_store_policies(streaming, backend, cus):
+    """K and V staged with non-temporal or write-through stores: same result
+    as the plain copy, within the attention bar of the oracle."""
+    sq, hq, hkv, W, n = 256, 8, 2, 4, 128
+    q, kk, vv = inputs.attention_operands(sq, hq, W * n, hkv, D)
+    ref_o, ref_lse = oracle.attention_f64(q, kk, vv, 1 / math.sqrt(D))
+    o, _, _, lse = run_attn(sq, hq, hkv, W, n, q, kk, vv, backend=backend, cus=cus, streaming=streaming)
+    check(o, lse, ref_o, ref_lse)
