@@ -33,7 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 M, N, K, WORLD = 8192, 1792, 4096, 8
 DIVISOR = 64.0
 
-STORE_POLICIES = {"plain": 0, "stream": 1, "wt": 2}
+STORE_POLICIES = {"plain": 0, "stream": 1}
 BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64), "colocated": (4, 0)}
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
@@ -84,7 +84,7 @@ def parse():
                    help="K-slices per copied chunk (1: whole chunks; >1: slice 0 of every chunk first, tiles start "
                         "on it and wait in-kernel for the later slices)")
     p.add_argument("--copy-store", default="plain", choices=sorted(STORE_POLICIES),
-                   help="store policy of the copy role: plain, non-temporal (stream) or write-through (wt)")
+                   help="loads and stores of the copy role: plain or non-temporal (stream)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-rows", action="store_true", help="skip the RS, 70B-like AG and attention rows")
     p.add_argument("--tune", action="store_true",

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libsync_overlap.so")
 ARCH = os.environ.get("SYNC_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["kernels/gemm_persistent.hip", "kernels/workspace.hip", "kernels/ring_attn.hip", "runtime.cpp",
-               "autotune.cpp"]
+               "autotune.cpp", "sdma_engine.cpp"]
 CXX_SOURCES = ["planner.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
@@ -52,7 +52,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), sources))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-Wl,--no-undefined"]
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + \
+        [f"-L{rocm_lib}", "-lhsa-runtime64", "-Wl,--no-undefined"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

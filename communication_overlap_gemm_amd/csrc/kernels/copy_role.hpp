@@ -38,60 +38,39 @@ typedef uint32_t copy_u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCopyUnroll = 16;  // 16-byte loads in flight per thread
 
-// Store policy of the copy role (CopyArgs::streaming).
-//   kPolPlain:        ordinary loads and stores (write-back in the L2).
-//   kPolStream:       non-temporal loads and stores.
-//   kPolWriteThrough: ordinary loads; stores carry agent scope (sc1), so the
-//                     L2 writes them through instead of holding them dirty.
-//                     The publication still writes the L2 back, but finds
-//                     little there to write.
-enum : int { kPolPlain = 0, kPolStream = 1, kPolWriteThrough = 2 };
-
-// 16-byte store at byte offset off (< 2^31) from base under policy POL.
-template <int POL>
-__device__ __forceinline__ void copy_store(char* base, int64_t off, copy_u32x4_t v) {
-  if constexpr (POL == kPolWriteThrough) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), 0x7fffffff,
-                                                                       0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(copy_u32x4_t, v), r, static_cast<uint32_t>(off), 0,
-                                           16 /* sc1 */);
-  } else if constexpr (POL == kPolStream) {
-    __builtin_nontemporal_store(v, reinterpret_cast<copy_u32x4_t*>(base + off));
-  } else {
-    *reinterpret_cast<copy_u32x4_t*>(base + off) = v;
-  }
-}
-template <int POL>
-__device__ __forceinline__ copy_u32x4_t copy_load(const char* p) {
-  const copy_u32x4_t* q = reinterpret_cast<const copy_u32x4_t*>(p);
-  if constexpr (POL == kPolStream) return __builtin_nontemporal_load(q);
-  return *q;
-}
-
 // Copies bytes [lo, hi) of src to dst (16-byte granules; both 16-byte
-// aligned; hi < 2^31), kCopyUnroll loads in flight per thread, stores under
-// policy POL.
-template <int THREADS, int POL>
+// aligned), kCopyUnroll loads in flight per thread.  STREAM selects
+// non-temporal accesses.
+template <int THREADS, bool STREAM>
 __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* __restrict__ dst, int64_t lo,
                                            int64_t hi) {
+  const copy_u32x4_t* s = reinterpret_cast<const copy_u32x4_t*>(src);
+  copy_u32x4_t* d = reinterpret_cast<copy_u32x4_t*>(dst);
   int64_t g = lo / 16 + threadIdx.x;
   const int64_t gend = hi / 16;
   constexpr int64_t step = THREADS;
+  auto ld = [](const copy_u32x4_t* p) { return STREAM ? __builtin_nontemporal_load(p) : *p; };
+  auto st = [](copy_u32x4_t v, copy_u32x4_t* p) {
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(v, p);
+    else
+      *p = v;
+  };
   for (; g + (kCopyUnroll - 1) * step < gend; g += kCopyUnroll * step) {
     copy_u32x4_t v[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) v[u] = copy_load<POL>(src + (g + u * step) * 16);
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = ld(s + g + u * step);
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) copy_store<POL>(dst, (g + u * step) * 16, v[u]);
+    for (int u = 0; u < kCopyUnroll; ++u) st(v[u], d + g + u * step);
   }
   if (g < gend) {  // the remainder, still with every load in flight before the stores
     copy_u32x4_t v[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
-      if (g + u * step < gend) v[u] = copy_load<POL>(src + (g + u * step) * 16);
+      if (g + u * step < gend) v[u] = ld(s + g + u * step);
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
-      if (g + u * step < gend) copy_store<POL>(dst, (g + u * step) * 16, v[u]);
+      if (g + u * step < gend) st(v[u], d + g + u * step);
   }
 }
 
@@ -100,7 +79,7 @@ __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* _
 // apart in src and dst, its granules numbered row by row.  Same loads in
 // flight per thread as copy_range; each thread steps its (row, column) by the
 // block stride instead of dividing.
-template <int THREADS, int POL>
+template <int THREADS, bool STREAM>
 __device__ __forceinline__ void copy_block(const char* __restrict__ src, char* __restrict__ dst, int64_t pitch,
                                            int64_t col, int64_t seg, int64_t lo, int64_t hi) {
   const int64_t gpr = seg / 16;  // granules per row
@@ -108,13 +87,24 @@ __device__ __forceinline__ void copy_block(const char* __restrict__ src, char* _
   if (g >= hi) return;
   int64_t row = g / gpr, cg = g - row * gpr;
   const int64_t drow = THREADS / gpr, dcg = THREADS - drow * gpr;  // one step of THREADS granules
+  auto ld = [](const char* p) {
+    const copy_u32x4_t* q = reinterpret_cast<const copy_u32x4_t*>(p);
+    return STREAM ? __builtin_nontemporal_load(q) : *q;
+  };
+  auto st = [](copy_u32x4_t v, char* p) {
+    copy_u32x4_t* q = reinterpret_cast<copy_u32x4_t*>(p);
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(v, q);
+    else
+      *q = v;
+  };
   while (g < hi) {
     copy_u32x4_t v[kCopyUnroll];
     int64_t off[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
       off[u] = row * pitch + col + cg * 16;
-      if (g + u * THREADS < hi) v[u] = copy_load<POL>(src + off[u]);
+      if (g + u * THREADS < hi) v[u] = ld(src + off[u]);
       row += drow;
       cg += dcg;
       if (cg >= gpr) {
@@ -124,30 +114,9 @@ __device__ __forceinline__ void copy_block(const char* __restrict__ src, char* _
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
-      if (g + u * THREADS < hi) copy_store<POL>(dst, off[u], v[u]);
+      if (g + u * THREADS < hi) st(v[u], dst + off[u]);
     g += kCopyUnroll * THREADS;
   }
-}
-
-// The same with the policy chosen at run time.
-template <int THREADS>
-__device__ __forceinline__ void copy_range_pol(int pol, const char* src, char* dst, int64_t lo, int64_t hi) {
-  if (pol == kPolWriteThrough)
-    copy_range<THREADS, kPolWriteThrough>(src, dst, lo, hi);
-  else if (pol == kPolStream)
-    copy_range<THREADS, kPolStream>(src, dst, lo, hi);
-  else
-    copy_range<THREADS, kPolPlain>(src, dst, lo, hi);
-}
-template <int THREADS>
-__device__ __forceinline__ void copy_block_pol(int pol, const char* src, char* dst, int64_t pitch, int64_t col,
-                                               int64_t seg, int64_t lo, int64_t hi) {
-  if (pol == kPolWriteThrough)
-    copy_block<THREADS, kPolWriteThrough>(src, dst, pitch, col, seg, lo, hi);
-  else if (pol == kPolStream)
-    copy_block<THREADS, kPolStream>(src, dst, pitch, col, seg, lo, hi);
-  else
-    copy_block<THREADS, kPolPlain>(src, dst, pitch, col, seg, lo, hi);
 }
 
 // Publication.  A chunk is complete when every copy workgroup's stores of it
@@ -183,8 +152,8 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
         const int64_t r0 = a.chunk_begin[c], n = (a.chunk_begin[c + 1] - r0) * a.row_bytes[x] / 16;
         const int64_t a0 = lo > pos ? lo : pos, a1 = hi < pos + n ? hi : pos + n;
         if (a0 < a1)
-          copy_range_pol<THREADS>(a.streaming, a.src[x] + r0 * a.row_bytes[x], a.dst[x] + r0 * a.row_bytes[x],
-                                  (a0 - pos) * 16, (a1 - pos) * 16);
+          copy_range<THREADS, false>(a.src[x] + r0 * a.row_bytes[x], a.dst[x] + r0 * a.row_bytes[x], (a0 - pos) * 16,
+                                     (a1 - pos) * 16);
         pos += n;
       }
     if (first < 0) return;
@@ -239,13 +208,19 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
         if (S == 1) {
           const int64_t granules = (r1 - r0) * rb / 16;
           const int64_t lo = granules * trank / tcount * 16, hi = granules * (trank + 1) / tcount * 16;
-          copy_range_pol<THREADS>(a.streaming, a.src[x] + r0 * rb, a.dst[x] + drow * rb, lo, hi);
+          if (a.streaming)
+            copy_range<THREADS, true>(a.src[x] + r0 * rb, a.dst[x] + drow * rb, lo, hi);
+          else
+            copy_range<THREADS, false>(a.src[x] + r0 * rb, a.dst[x] + drow * rb, lo, hi);
         } else {
           const int64_t lines = rb / 128;  // 128-byte columns per row
           const int64_t col = h * lines / S * 128, seg = (h + 1) * lines / S * 128 - col;
           const int64_t granules = (r1 - r0) * (seg / 16);
           const int64_t lo = granules * trank / tcount, hi = granules * (trank + 1) / tcount;
-          copy_block_pol<THREADS>(a.streaming, a.src[x] + r0 * rb, a.dst[x] + r0 * rb, rb, col, seg, lo, hi);
+          if (a.streaming)
+            copy_block<THREADS, true>(a.src[x] + r0 * rb, a.dst[x] + r0 * rb, rb, col, seg, lo, hi);
+          else
+            copy_block<THREADS, false>(a.src[x] + r0 * rb, a.dst[x] + r0 * rb, rb, col, seg, lo, hi);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores have reached the L2

@@ -33,6 +33,7 @@ enum : int {
   WS_ERR_CODE = 1,    // 0 = fine, else ERR_* below (sticky until re-initialisation)
   WS_ERR_CHUNK = 2,   // chunk whose wait expired first
   WS_EXIT = 3,        // finished groups of workgroups of the running call (tree level 2)
+  WS_SDMA_EPOCH = 8,  // SDMA backend: the running call's epoch, copied into each chunk flag by the engine
   WS_EXIT_GROUP = 16, // finished workgroups per group of kTreeFan (tree level 1, 16 slots)
   WS_HEADER_WORDS = 64
 };

@@ -1,5 +1,6 @@
-// Small kernels around the workspace: initialisation and the flag raised
-// after each SDMA copy.
+// Small kernels around the workspace: initialisation, the gate and join of
+// the SDMA backend, and the flag raised after each stream-ordered copy of the
+// host-gated test backend.
 #include "device_common.hpp"
 
 namespace syncov {
@@ -17,6 +18,43 @@ __global__ __launch_bounds__(256) void fill_u32(uint32_t* p, int64_t n, uint32_t
 // cannot finish (and advance the stored epoch) before every such flag is up.
 __global__ __launch_bounds__(64) void publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c) {
   if (threadIdx.x == 0) st_release_agent(flags + c, call_epoch(hdr));
+}
+
+// SDMA backend, first kernel of a call on the caller's stream: fixes the
+// call's epoch in the workspace word that the engines copy into the chunk
+// flags, writes it past the L2 (the engines read memory, not an XCD's L2),
+// then opens the gate signal that every SDMA copy of the call waits for.
+__global__ __launch_bounds__(64) void sdma_gate(uint32_t* hdr, int64_t* gate) {
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(hdr + WS_SDMA_EPOCH, call_epoch(hdr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(gate, int64_t(0), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+// SDMA backend, copy-only: ends the call once every copied chunk's flag is up
+// (bounded waits; a timeout is recorded like any other), then stores the
+// call's epoch as the compute kernel's last workgroup would.
+__global__ __launch_bounds__(64) void sdma_join(uint32_t* hdr, const uint32_t* flags, const int32_t* arrival,
+                                                const int32_t* resident, int32_t num_chunks, uint64_t timeout_ticks) {
+  if (threadIdx.x == 0) {
+    const uint32_t e = call_epoch(hdr);
+    for (int32_t p = 0; p < num_chunks; ++p) {
+      const int32_t c = arrival[p];
+      if (!resident[c] && !wait_flag(flags, c, e, hdr, timeout_ticks)) break;
+    }
+    st_release_agent(hdr + WS_EPOCH, e);
+  }
+}
+
+hipError_t launch_sdma_gate(uint32_t* hdr, int64_t* gate, hipStream_t s) {
+  hipLaunchKernelGGL(sdma_gate, dim3(1), dim3(64), 0, s, hdr, gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_sdma_join(uint32_t* hdr, const uint32_t* flags, const int32_t* arrival, const int32_t* resident,
+                            int32_t num_chunks, uint64_t timeout_ticks, hipStream_t s) {
+  hipLaunchKernelGGL(sdma_join, dim3(1), dim3(64), 0, s, hdr, flags, arrival, resident, num_chunks, timeout_ticks);
+  return hipGetLastError();
 }
 
 hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s) {

@@ -24,6 +24,7 @@
 #include "kernels/device_common.hpp"
 #include "kernels/launch_args.hpp"
 #include "planner.hpp"
+#include "sdma_engine.hpp"
 #include "sync_overlap.h"
 
 namespace syncov {
@@ -32,6 +33,9 @@ hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dt
 bool gemm_variant_exists(int tm, int tn);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s);
+hipError_t launch_sdma_gate(uint32_t* hdr, int64_t* gate, hipStream_t s);
+hipError_t launch_sdma_join(uint32_t* hdr, const uint32_t* flags, const int32_t* arrival, const int32_t* resident,
+                            int32_t num_chunks, uint64_t timeout_ticks, hipStream_t s);
 hipError_t launch_ring_attn(const AttnArgs& a, int grid, hipStream_t s);
 constexpr int64_t kAttnHeadDim = 128;
 
@@ -338,7 +342,7 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
     if (d.k / 64 < 4 * static_cast<int64_t>(cfg.copy_kslices))
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs K/64 >= 4 x copy_kslices");
   }
-  if (cfg.copy_streaming < 0 || cfg.copy_streaming > 2) return fail(SYNC_EINVAL, "copy_streaming must be 0, 1 or 2");
+  if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
@@ -353,14 +357,6 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
     return fail(SYNC_EINVAL, "COPY_ONLY and COMPUTE_ONLY are exclusive");
   if ((cfg.flags & SYNC_RUN_COPY_ONLY) && cfg.backend == SYNC_COPY_PRESET)
     return fail(SYNC_EINVAL, "COPY_ONLY needs a copy backend");
-  if (cfg.copy_streaming == 2) {  // write-through stores address a chunk with 32-bit buffer offsets
-    const sync_plan_desc& d = plan->plan.desc;
-    const int64_t rb = op == SYNC_OP_GEMM_RS ? d.n * 4 : op == SYNC_OP_RING_ATTN ? int64_t(d.heads_kv) * d.k * 2 : d.k * 2;
-    int64_t rows = 0;
-    for (int32_t c = 0; c < plan->plan.num_chunks; ++c)
-      rows = std::max<int64_t>(rows, plan->plan.chunk_begin[c + 1] - plan->plan.chunk_begin[c]);
-    if (rows * rb >= (int64_t(1) << 31)) return fail(SYNC_EUNSUPPORTED, "copy_streaming 2 needs chunks below 2 GiB");
-  }
   int rc = current_device_state(&cx.dev);
   if (rc) return rc;
   if (cfg.backend == SYNC_COPY_CU) {
@@ -491,13 +487,15 @@ struct Roles {
   int wait = 1;         // compute waits for non-resident chunks
   int colocated = 0;    // every compute workgroup copies its share first
   bool no_compute = false;  // co-located copy-only: the copy phase alone
-  bool sdma = false;    // copy-in on the SDMA engine beside the launch
+  bool sdma = false;    // HOST_GATED: stream-ordered SDMA copies on the library's streams
+  bool engines = false; // SDMA: copies queued on the SDMA engines through HSA, gated by the call
 };
 
 // CU backend: one launch, copy_cus * wpc copy workgroups first, then one
 // compute workgroup per remaining CU slot.  PRESET: compute alone, nothing to
-// wait for.  SDMA / HOST_GATED: compute on the CUs the masked GEMM stream
-// allows, copies on the SDMA engine.
+// wait for.  SDMA: compute on every CU, copies on the SDMA engines.
+// HOST_GATED: compute on the CUs the masked GEMM stream allows, copies on
+// the copy stream.
 Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
   Roles r;
   const bool copy_only = cx.cfg.flags & SYNC_RUN_COPY_ONLY;
@@ -528,7 +526,14 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
       else
         r.colocated = 1;
       break;
-    default:  // SDMA, HOST_GATED
+    case SYNC_COPY_SDMA:
+      r.grid = copy_only ? 0 : d.num_cus * wpc;
+      if (compute_only)
+        r.wait = 0;
+      else
+        r.engines = true;
+      break;
+    default:  // HOST_GATED
       if (compute_only) {
         r.grid = d.num_cus * wpc;
         r.wait = 0;
@@ -539,6 +544,53 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
       break;
   }
   return r;
+}
+
+// SDMA backend: reserve the call's signals; on the caller's stream the gate
+// kernel; every copied chunk queued on the SDMA engines (each copy waits for
+// the gate, so launch and queueing may happen in either order); then the
+// compute kernel (copy-only: the join kernel).  If queueing fails, the join
+// kernel ends the call instead, the missing chunks' waits timing out.
+template <typename Launch>
+int run_engines(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs, const Roles& r,
+                const char* const src[2], char* const dst[2], const int64_t rb[2], int ntensors, Launch launch) {
+  int32_t copied = 0;
+  for (int32_t c = 0; c < pl.num_chunks; ++c) copied += pl.resident[c] ? 0 : 1;
+  SdmaCall call;
+  int rc = sdma_begin(d.device, copied, ntensors, &call);
+  if (rc) return rc;
+  SdmaJob job{};
+  for (int x = 0; x < ntensors; ++x) {
+    job.src[x] = src[x];
+    job.dst[x] = dst[x];
+    job.row_bytes[x] = rb[x];
+  }
+  job.ntensors = ntensors;
+  job.num_chunks = pl.num_chunks;
+  job.chunk_begin = pl.chunk_begin.data();
+  job.arrival = pl.arrival.data();
+  job.resident = pl.resident.data();
+  job.flags = cx.ws.flags;
+  job.epoch_word = cx.ws.hdr + WS_SDMA_EPOCH;
+  job.engines = cx.cfg.copy_teams;
+  if (tm) {
+    HIP_TRY(hipEventRecord(tm->k0, cs));
+    HIP_TRY(hipEventRecord(tm->c0, cs));
+  }
+  HIP_TRY(launch_sdma_gate(cx.ws.hdr, call.gate_value, cs));
+  const int queued = sdma_submit(d.device, call, job);
+  if (r.grid > 0 && queued == SYNC_OK) {
+    if ((rc = launch(cs, r))) return rc;
+  } else {
+    HIP_TRY(launch_sdma_join(cx.ws.hdr, cx.ws.flags, cx.tab->arrival, cx.tab->resident, pl.num_chunks,
+                             cx.timeout_ticks, cs));
+  }
+  if (tm) {
+    HIP_TRY(hipEventRecord(tm->k1, cs));
+    HIP_TRY(hipEventRecord(tm->c1, cs));
+    tm->has_kernel = tm->has_copy = true;
+  }
+  return queued;
 }
 
 // Enqueues one call: `launch(stream, roles)` puts the compute kernel (with its
@@ -563,6 +615,7 @@ int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm
     const int64_t words = (ws_total_bytes(pl.num_chunks, pl.num_tiles) - ws_trace_offset(pl.num_chunks)) / 4;
     HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(cx.ws.trace_tiles), words, 0u, cs));
   }
+  if (r.engines) return run_engines(pl, cx, d, tm, cs, r, src, dst, rb, ntensors, launch);
   if (!r.sdma) return timed(cs);
   MaskedPair* mp = nullptr;
   int rc = masked_pair(d, d.num_xcds, &mp);
@@ -661,6 +714,8 @@ int sync_workspace_init(sync_plan_t plan, void* ws, void* stream) {
   DeviceState* d = nullptr;
   int rc = current_device_state(&d);
   if (rc) return rc;
+  // SDMA flag copies of earlier calls must not land after the fill
+  if ((rc = sdma_quiesce_all(d->device))) return rc;
   HIP_TRY(launch_fill_u32(static_cast<uint32_t*>(ws), static_cast<int64_t>(sync_workspace_size(plan) / 4), 0u,
                           static_cast<hipStream_t>(stream)));
   return SYNC_OK;

@@ -1,0 +1,41 @@
+// SDMA copy agent driven through HSA (sdma_engine.cpp).
+#pragma once
+
+#include <stdint.h>
+
+namespace syncov {
+
+// One call's copies: every non-resident chunk, in arrival order, each tensor
+// row block [chunk_begin[c], chunk_begin[c+1]) from src to dst, then flags[c]
+// set to the 32-bit word at epoch_word.  Chunk i of the copied ones goes to
+// engine i % engines (of those available).
+struct SdmaJob {
+  const char* src[2];
+  char* dst[2];
+  int64_t row_bytes[2];
+  int32_t ntensors;
+  int32_t num_chunks;
+  const int64_t* chunk_begin;  // host tables
+  const int32_t* arrival;
+  const int32_t* resident;
+  uint32_t* flags;             // device
+  const uint32_t* epoch_word;  // device word the gate kernel fills with the call's epoch
+  int32_t engines;
+};
+
+struct SdmaCall {
+  int record = 0;
+  int64_t* gate_value = nullptr;  // the gate kernel stores 0 here to start the copies
+};
+
+// Reserves a call record on HIP device dev (waiting, bounded, for its previous
+// call's copies to complete) and arms its signals.
+int sdma_begin(int dev, int32_t copied_chunks, int32_t ntensors, SdmaCall* out);
+// Queues the copies and flag writes of a call reserved with sdma_begin.
+int sdma_submit(int dev, const SdmaCall& call, const SdmaJob& job);
+// Waits for every queued SDMA copy of device dev to complete.
+int sdma_quiesce_all(int dev);
+// Number of SDMA engines available for device-to-device copies on dev.
+int sdma_engine_count(int dev, int* out);
+
+}  // namespace syncov

@@ -194,10 +194,8 @@ typedef struct {
   uint64_t timeout_ns;      /* bound on every device-side wait; 0 = 2 s */
   const uint32_t* host_gates; /* HOST_GATED: pinned host words (hipHostMalloc), one per chunk */
   int32_t flags;            /* SYNC_RUN_* bits */
-  int32_t copy_streaming;   /* CU and COLOCATED backends, store policy of the copy role:
-                               0 = plain loads and stores; 1 = non-temporal loads and stores;
-                               2 = write-through stores (agent scope), so that the L2 holds no
-                               dirty copy data when a chunk is published */
+  int32_t copy_streaming;   /* CU and COLOCATED backends: 1 = non-temporal loads/stores in the copy
+                               role; 0 = plain */
   int32_t withhold_chunk;   /* SYNC_RUN_WITHHOLD only: the chunk left out, or -1 for all */
   int32_t copy_teams;       /* CU backend: chunks in flight at once; the copy workgroups split
                                into this many teams, team t taking every copy_teams-th copied

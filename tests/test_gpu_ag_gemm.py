@@ -196,8 +196,6 @@ def _samples(m, n, count, seed=0):
     return rows, cols
 
 
-SDMA_LIMIT = ("the HIP runtime does not start the next SDMA copy while the persistent GEMM runs (measured: "
-              "later chunks land only after the GEMM exits), so full-size SDMA overlap times out")
 
 
 @pytest.mark.parametrize("layout", ["kn", "nk"])
@@ -212,7 +210,7 @@ def test_full_size_exact_small_integers(layout):
 
 
 @pytest.mark.parametrize("backend,cus,split", [
-    pytest.param(A.SYNC_COPY_SDMA, 0, 1, marks=pytest.mark.skip(reason=SDMA_LIMIT)), (A.SYNC_COPY_CU, 32, 4),
+    (A.SYNC_COPY_SDMA, 0, 1), (A.SYNC_COPY_CU, 32, 4),
     (A.SYNC_COPY_CU, 16, 2), (A.SYNC_COPY_PRESET, 0, 1), (A.SYNC_COPY_COLOCATED, 0, 1)])
 @pytest.mark.parametrize("layout", ["kn", "nk"])
 def test_full_size_normal(backend, cus, split, layout):
@@ -495,14 +493,14 @@ def test_full_size_kslices(backend, cus, teams, kslices):
         assert np.linalg.norm(out[rows[sel], cols[sel]] - ref[sel]) / np.linalg.norm(ref[sel]) <= 1e-3
 
 
-# ---- store policy of the copy role: plain, non-temporal, write-through -----
+# ---- non-temporal loads and stores in the copy role -------------------------
 
-@pytest.mark.parametrize("streaming", [1, 2])
+@pytest.mark.parametrize("streaming", [1])
 @pytest.mark.parametrize("backend,cus,teams,kslices", [(A.SYNC_COPY_CU, 16, 1, 0), (A.SYNC_COPY_CU, 16, 3, 4),
                                                        (A.SYNC_COPY_COLOCATED, 0, 0, 0)])
 def test_copy_store_policies(streaming, backend, cus, teams, kslices):
-    """Non-temporal and write-through stores stage the same bytes and give an
-    output bitwise equal to the compute-only one (exact small integers)."""
+    """Non-temporal copies stage the same bytes and give the exact output
+    (small integers)."""
     m, n, k, world, split = 2048, 768, 1152, 4, 2
     a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
     ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
@@ -512,11 +510,11 @@ def test_copy_store_policies(streaming, backend, cus, teams, kslices):
     assert np.array_equal(out.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("streaming", [1, 2])
-def test_full_size_write_through_copy(streaming):
+@pytest.mark.parametrize("streaming", [1])
+def test_full_size_streaming_copy(streaming):
     """The Llama-3-8B up-projection share with the bench's copy (32 copy CUs in
-    7 teams, 4 K-slices) under each non-default store policy: exact for
-    small-integer operands on sampled outputs, every copied row staged."""
+    7 teams, 4 K-slices) with non-temporal copies: exact for small-integer
+    operands on sampled outputs, every copied row staged."""
     a, b = inputs.gemm_operands(M2, N2, K2, 1.0, integer=True, b_layout="nk")
     out, a_local = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), backend=A.SYNC_COPY_CU, copy_cus=32, layout="nk",
                           teams=7, kslices=4, streaming=streaming)
@@ -525,3 +523,66 @@ def test_full_size_write_through_copy(streaming):
     exact = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout="nk")
     assert np.array_equal(out[rows, cols].astype(np.float64), exact)
 
+
+# ---- SDMA engines driven through HSA: repeated calls, several engines -------
+
+@pytest.mark.parametrize("engines", [1, 7])
+def test_full_size_sdma_repeated_calls(engines):
+    """Back-to-back SDMA calls at the Llama-3-8B up-projection size, the peer
+    region alternating between two datasets: every call's chunks land while
+    its GEMM runs, and a tile that trusted a flag of the previous call would
+    read the other dataset."""
+    a1, b = inputs.gemm_operands(M2, N2, K2, 1.0, integer=True, b_layout="nk")
+    a2, _ = inputs.gemm_operands(M2, N2, K2, 1.0, integer=True, b_layout="nk",
+                                 seed_a=inputs.SEED_A + inputs.ALT_SEED_OFFSET)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, M2, N2, K2, W2, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    peers = [dev_bits(a1), dev_bits(a2)]
+    b_d = dev_bits(b)
+    a_local = bf16_poison((M2, K2))
+    c = torch.empty((M2, N2), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    rows, cols = _samples(M2, N2, 3000, seed=9)
+    exact = [oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout="nk") for a in (a1, a2)]
+    cfg = A.make_cfg(A.SYNC_COPY_SDMA, copy_teams=engines)
+    for it in range(4):
+        x = it % 2
+        print(f"[ag] SDMA full size, {engines} engine(s), call {it}", flush=True)
+        a_local[:M2 // W2] = peers[x][:M2 // W2]
+        c.fill_(float("nan"))
+        A.sync_ag_gemm(plan, cfg, peers[x], a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+        rc, chunk = A.sync_workspace_status(ws, s)
+        assert rc == A.SYNC_OK, f"call {it}: device wait timed out on chunk {chunk}"
+        assert np.array_equal(c[rows, cols].cpu().numpy().astype(np.float64), exact[x]), f"call {it}"
+    assert np.array_equal(host_bits(a_local), a2)
+    # five calls with no host sync in between, then one check
+    a_local[:M2 // W2] = peers[0][:M2 // W2]
+    for it in range(5):
+        A.sync_ag_gemm(plan, cfg, peers[0], a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    assert np.array_equal(c[rows, cols].cpu().numpy().astype(np.float64), exact[0])
+
+
+def test_sdma_copy_only_advances_the_epoch():
+    """SDMA copy-only: the join kernel ends each call once every chunk flag is
+    up; the rows are staged and the stored epoch advances once per call."""
+    m, n, k, world, split = 1024, 256, 512, 4, 3
+    a, _ = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, split=split, tile_m=128, tile_n=128,
+                                   b_layout=A.SYNC_B_NK))
+    a_peer = dev_bits(a)
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    b_d = torch.zeros((n, k), dtype=torch.int16, device="cuda:0")
+    c = torch.zeros((m, n), dtype=torch.float32, device="cuda:0")
+    for it in range(3):
+        a_local = bf16_poison((m, k))
+        a_local[: m // world] = a_peer[: m // world]
+        print(f"[ag] SDMA copy-only call {it}", flush=True)
+        A.sync_ag_gemm(plan, A.make_cfg(A.SYNC_COPY_SDMA, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=2), a_peer, a_local,
+                       b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+        rc, chunk = A.sync_workspace_status(ws, s)
+        assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+        assert np.array_equal(host_bits(a_local), a)
+        assert int(ws[0].item()) == it + 1

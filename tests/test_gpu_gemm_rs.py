@@ -202,12 +202,12 @@ def test_full_size_rs_colocated_exact():
     assert np.array_equal(cn[rows, cols].astype(np.float64), exact)
 
 
-@pytest.mark.parametrize("streaming", [1, 2])
+@pytest.mark.parametrize("streaming", [1])
 @pytest.mark.parametrize("backend,cus,teams", [(A.SYNC_COPY_CU, 16, 0), (A.SYNC_COPY_CU, 16, 4),
                                                (A.SYNC_COPY_COLOCATED, 0, 4)])
 def test_rs_copy_store_policies(streaming, backend, cus, teams):
-    """Copy-out under non-temporal and write-through stores: exact C and every
-    chunk bitwise in its send slot."""
+    """Copy-out with non-temporal loads and stores: exact C and every chunk
+    bitwise in its send slot."""
     m, n, k, W = 1024, 512, 256, 4
     a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True)
     ref = oracle.gemm_f64(a, b, m, n, k)

@@ -25,7 +25,8 @@ TOL = 2e-3
 
 
 def run_attn(sq, hq, hkv, world, n, q_bits, k_bits, v_bits, split=1, backend=A.SYNC_COPY_CU, cus=16,
-             flags=A.SYNC_ATTN_INIT | A.SYNC_ATTN_FINALIZE, scale=1 / math.sqrt(D), rank=0, state=None, streaming=0):
+             flags=A.SYNC_ATTN_INIT | A.SYNC_ATTN_FINALIZE, scale=1 / math.sqrt(D), rank=0, state=None, streaming=0,
+             teams=0):
     print(f"[attn] sq={sq} hq={hq} hkv={hkv} W={world} n={n} split={split} backend={backend} cus={cus} "
           f"flags={flags} streaming={streaming}", flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_RING_ATTN, sq, n, D, world, rank=rank, split=split, tile_m=128,
@@ -51,7 +52,8 @@ def run_attn(sq, hq, hkv, world, n, q_bits, k_bits, v_bits, split=1, backend=A.S
     lse = torch.full((hq, sq), float("nan"), dtype=torch.float32, device="cuda:0")
     ws = workspace(plan)
     s = torch.cuda.current_stream()
-    A.sync_ring_attn_step(plan, A.make_cfg(backend, copy_cus=cus, copy_streaming=streaming), q, k_peer, v_peer, k_local, v_local, o, m, l,
+    cfg = A.make_cfg(backend, copy_cus=cus, copy_streaming=streaming, copy_teams=teams)
+    A.sync_ring_attn_step(plan, cfg, q, k_peer, v_peer, k_local, v_local, o, m, l,
                           lse, scale, flags, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
     assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
@@ -68,7 +70,8 @@ def check(o, lse, ref_o, ref_lse):
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (8, 4), (16, 2)])
-@pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_PRESET, 0), (A.SYNC_COPY_CU, 8), (A.SYNC_COPY_COLOCATED, 0)])
+@pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_PRESET, 0), (A.SYNC_COPY_CU, 8), (A.SYNC_COPY_COLOCATED, 0),
+                                         (A.SYNC_COPY_SDMA, 0)])
 def test_small_heads_and_backends(hq, hkv, backend, cus):
     sq, W, n = 256, 4, 128
     q, k, v = inputs.attention_operands(sq, hq, W * n, hkv, D)
@@ -108,10 +111,11 @@ def test_chained_steps_carry_state():
 
 
 # ---- Qwen-like GQA ring step: Q 4096 x 32 x 128, 8 KV blocks of 4096 x 8 x 128 ----
-def test_full_size_sampled():
+@pytest.mark.parametrize("backend,cus,teams", [(A.SYNC_COPY_CU, 32, 0), (A.SYNC_COPY_SDMA, 0, 7)])
+def test_full_size_sampled(backend, cus, teams):
     sq, hq, hkv, W, n = 4096, 32, 8, 8, 4096
     q, k, v = inputs.attention_operands(sq, hq, W * n, hkv, D)
-    o, _, _, lse = run_attn(sq, hq, hkv, W, n, q, k, v, cus=32)
+    o, _, _, lse = run_attn(sq, hq, hkv, W, n, q, k, v, backend=backend, cus=cus, teams=teams)
     rng = np.random.default_rng(5)
     qi = np.concatenate([rng.integers(0, sq, 600), [0, sq - 1]])
     hi = np.concatenate([rng.integers(0, hq, 600), [0, hq - 1]])
@@ -122,11 +126,11 @@ def test_full_size_sampled():
     assert np.max(np.abs(ln_[hi, qi] - ref_lse)) <= TOL
 
 
-@pytest.mark.parametrize("streaming", [1, 2])
+@pytest.mark.parametrize("streaming", [1])
 @pytest.mark.parametrize("backend,cus", [(A.SYNC_COPY_CU, 8), (A.SYNC_COPY_COLOCATED, 0)])
 def test_copy_store_policies(streaming, backend, cus):
-    """K and V staged with non-temporal or write-through stores: same result
-    as the plain copy, within the attention bar of the oracle."""
+    """K and V staged with non-temporal loads and stores: within the
+    attention bar of the oracle."""
     sq, hq, hkv, W, n = 256, 8, 2, 4, 128
     q, kk, vv = inputs.attention_operands(sq, hq, W * n, hkv, D)
     ref_o, ref_lse = oracle.attention_f64(q, kk, vv, 1 / math.sqrt(D))

@@ -57,3 +57,33 @@ def test_check_catches_a_use_before_the_wait(tmp_path):
     # the compiler may place a wait of its own ahead of the planted use in an
     # instance (then that use is no hazard); nearly every instance must flag it
     assert n >= 12 and len(flagged) >= n - 2, (n, sorted(flagged))
+
+
+def _resources(asm):
+    """name -> (total VGPRs incl. AGPRs, LDS bytes) of every kernel in the assembly."""
+    import re
+    out = {}
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S):
+        body = m.group(2)
+        vgpr = int(re.search(r"\.amdhsa_next_free_vgpr\s+(\d+)", body).group(1))
+        lds = int(re.search(r"\.amdhsa_group_segment_fixed_size\s+(\d+)", body).group(1))
+        out[m.group(1)] = (vgpr, lds)
+    return out
+
+
+def test_occupancy_the_launcher_assumes(asm):
+    """128x128 tiles run two workgroups of four waves per CU (two waves per
+    SIMD); the co-located backend needs every workgroup of the grid resident
+    at once, so those kernels must stay within 256 VGPRs per wave and half the
+    LDS.  Eight-wave 256x256 kernels must also fit two waves per SIMD."""
+    res = _resources(asm)
+    assert res
+    checked = 0
+    for name, (vgpr, lds) in res.items():
+        if "ILi128ELi128E" in name:  # gemm_dma / gemm_persistent <128, 128, ...>
+            assert vgpr <= 256 and 2 * lds <= 160 * 1024, (name, vgpr, lds)
+            checked += 1
+        if "gemm_dmaILi256ELi256E" in name:
+            assert vgpr <= 256, (name, vgpr)
+            checked += 1
+    assert checked >= 12, checked
