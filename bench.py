@@ -175,6 +175,24 @@ def main():
     copy_only_ms = float(np.mean([r[1] if backend == A.SYNC_COPY_SDMA else r[0] for r in recs_p]))
     # (co-located: the copy-only launch is every workgroup copying, none computing)
 
+    # copy-backend sweep on the same workload (a few timed calls each): SDMA on
+    # one engine (as one ring link) and on seven (as pulls from seven peers),
+    # 8/16/32 dedicated copy CUs (7 teams, 4 K-slices), co-located copy
+    sweep = {}
+    if not args.no_other_rows:
+        for sname, (sb, scus, steams, sks) in (("sdma_1_engine", (A.SYNC_COPY_SDMA, 0, 1, 1)),
+                                                ("sdma_7_engines", (A.SYNC_COPY_SDMA, 0, 7, 1)),
+                                                ("cu8", (A.SYNC_COPY_CU, 8, 7, 4)),
+                                                ("cu16", (A.SYNC_COPY_CU, 16, 7, 4)),
+                                                ("cu32", (A.SYNC_COPY_CU, 32, 7, 4)),
+                                                ("colocated", (A.SYNC_COPY_COLOCATED, 0, 0, 1))):
+            t_o, _ = timed_loop(A.make_cfg(sb, scus, copy_teams=steams, copy_kslices=sks), 10, 3)
+            t_c, _ = timed_loop(A.make_cfg(sb, scus, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=steams,
+                                           copy_kslices=sks), 10, 3)
+            sweep[sname] = {"t_overlap_us": round(t_o * 1e6, 1), "t_copy_only_us": round(t_c * 1e6, 1),
+                            "tflops": round(2.0 * M * N * K / t_o / 1e12, 1),
+                            "ratio": round(t_o / max(t_comp, t_c), 4)}
+
     flops = 2.0 * M * N * K
     value = flops / t_ovl / 1e12
     achieved = flops / (k_ms * 1e-3) / 1e12
@@ -227,6 +245,8 @@ def main():
     }
     if tuned is not None:
         line["autotune"] = tuned
+    if sweep:
+        line["copy_backend_sweep"] = sweep
     if not args.no_other_rows:
         del a_peer, a_local, b, c_out
         line["other_rows"] = other_rows(pol=pol)

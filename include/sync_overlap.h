@@ -149,20 +149,26 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  * global-memory flags]:
  *   PRESET      no copy; every chunk is taken as present (compute-only; the
  *               caller provides the whole input)
- *   SDMA        per chunk, an SDMA-engine copy then a one-lane flag kernel, on
- *               the library's copy stream (masked to one CU per XCD; the
- *               compute kernel runs on the other CUs).  Known limit: under the
- *               HIP runtime the next SDMA copy does not start while the
- *               persistent GEMM runs, so chunks not copied before the GEMM
- *               starts time out.
+ *   SDMA        the chunks move on the SDMA engines, queued through HSA
+ *               (hsa_amd_memory_async_copy_on_engine; copy_teams engines, 1
+ *               if 0).  On `compute` a one-workgroup gate kernel fixes the
+ *               call's epoch and opens the call's gate signal, which every
+ *               copy waits for; after each chunk's data copy the same engine
+ *               copies the epoch into the chunk's ready flag; the compute
+ *               kernel follows on `compute`, on every CU (copy-only: a join
+ *               kernel that waits for every flag).  `copy` is unused.  The
+ *               host may wait (bounded) for the copies of the call made 16
+ *               calls earlier on the device before queueing new ones.
  *   CU          the call is ONE kernel launch on `compute`: its first
  *               copy_cus x (compute workgroups per CU) workgroups copy, the
  *               rest compute; `copy` is unused.  Copy workgroups are spread
  *               evenly over the XCDs and are resident before any compute
  *               workgroup.
- *   HOST_GATED  as SDMA, but chunk c's copy first waits until the host word
- *               host_gates[c] becomes non-zero (tests: delayed or withheld
- *               chunks)
+ *   HOST_GATED  (tests: delayed or withheld chunks) per chunk, a runtime copy
+ *               that first waits until the host word host_gates[c] becomes
+ *               non-zero, then a one-lane flag kernel, on `copy` or the
+ *               library's copy stream (masked to one CU per XCD; the compute
+ *               kernel runs on the other CUs)
  *   COLOCATED   one launch on `compute` whose compute workgroups also copy; no
  *               CUs are set aside [SYN-S Fig. 7: load/store by the compute SMs
  *               themselves].  AG and attention: every workgroup first copies
@@ -177,7 +183,7 @@ enum {
   SYNC_RUN_COMPUTE_ONLY = 2, /* run only the compute kernel, with the workgroups the CU split
                                 leaves it (CU backend) or all CUs, every chunk taken as present */
   SYNC_RUN_TIMED = 4,        /* record device events around the call's kernel launch and the
-                                SDMA copies, on the streams they run on; read with
+                                runtime copies (HOST_GATED), on the streams they run on; read with
                                 sync_read_timings() */
   SYNC_RUN_WITHHOLD = 8,     /* CU backend, AG and attention (failure-path tests): chunk
                                 cfg.withhold_chunk (-1: every non-resident chunk) is neither
@@ -197,7 +203,8 @@ typedef struct {
   int32_t copy_streaming;   /* CU and COLOCATED backends: 1 = non-temporal loads/stores in the copy
                                role; 0 = plain */
   int32_t withhold_chunk;   /* SYNC_RUN_WITHHOLD only: the chunk left out, or -1 for all */
-  int32_t copy_teams;       /* CU backend: chunks in flight at once; the copy workgroups split
+  int32_t copy_teams;       /* SDMA backend: engines used (copied chunk i goes to engine i mod
+                               copy_teams).  CU backend: chunks in flight at once; the copy workgroups split
                                into this many teams, team t taking every copy_teams-th copied
                                chunk from the t-th (copy-out: in send order, each team waiting
                                for its chunk's done flag).  0 or 1 = one chunk after another
@@ -226,7 +233,9 @@ size_t sync_workspace_size(sync_plan_t plan);
  * is cleared: each call's kernel takes the next epoch from the workspace and
  * its last workgroup stores it, so a call is exactly one launch on the
  * compute stream with the CU backend, and replaying a captured call is
- * valid. */
+ * valid.  First waits on the host (bounded; SYNC_ETIMEOUT) until every SDMA
+ * copy queued on this device has completed, so that no flag write of an
+ * earlier call lands after the fill. */
 int sync_workspace_init(sync_plan_t plan, void* ws, void* stream);
 
 /* Trace of the last SYNC_RUN_TRACE GEMM call on a workspace (waits for
@@ -368,7 +377,9 @@ void sync_tune_forget(void);
  * (a ring of 1024), oldest first; waits for those events.  kernel_ms is the
  * call's kernel launch (GEMM or attention; with the CU backend its copy
  * workgroups are part of it) from just before the launch to just after it, on
- * the stream it runs on; copy_ms spans the SDMA copies (0 if none).  Reading
+ * the stream it runs on (SDMA: from before the gate kernel to after the
+ * compute or join kernel); copy_ms spans the copies (HOST_GATED: the runtime
+ * copies; SDMA: the same span as kernel_ms; 0 if none).  Reading
  * empties the ring.  *count = records written to out (<= max). */
 typedef struct {
   float kernel_ms;
