@@ -146,7 +146,7 @@ def main():
         torch.cuda.synchronize()
         A.sync_read_timings(0)  # drop warm-up records
         cfg_t = A.make_cfg(cfg.backend, cfg.copy_cus, cfg.timeout_ns, None, cfg.flags | A.SYNC_RUN_TIMED,
-                           copy_streaming=cfg.copy_streaming,
+                           copy_streaming=cfg.copy_streaming, copy_link_gbps=cfg.copy_link_gbps,
                            copy_teams=cfg.copy_teams, copy_kslices=cfg.copy_kslices)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -177,18 +177,22 @@ def main():
 
     # copy-backend sweep on the same workload (a few timed calls each): SDMA on
     # one engine (as one ring link) and on seven (as pulls from seven peers),
-    # 8/16/32 dedicated copy CUs (7 teams, 4 K-slices), co-located copy
+    # 8/16/32 dedicated copy CUs (7 teams, 4 K-slices), co-located copy, and
+    # 32 copy CUs paced as xGMI links of 153 GB/s: one link carrying every
+    # chunk (ring) or seven links at once (mesh)
     sweep = {}
     if not args.no_other_rows:
-        for sname, (sb, scus, steams, sks) in (("sdma_1_engine", (A.SYNC_COPY_SDMA, 0, 1, 1)),
-                                                ("sdma_7_engines", (A.SYNC_COPY_SDMA, 0, 7, 1)),
-                                                ("cu8", (A.SYNC_COPY_CU, 8, 7, 4)),
-                                                ("cu16", (A.SYNC_COPY_CU, 16, 7, 4)),
-                                                ("cu32", (A.SYNC_COPY_CU, 32, 7, 4)),
-                                                ("colocated", (A.SYNC_COPY_COLOCATED, 0, 0, 1))):
-            t_o, _ = timed_loop(A.make_cfg(sb, scus, copy_teams=steams, copy_kslices=sks), 10, 3)
+        for sname, (sb, scus, steams, sks, gbps) in (("sdma_1_engine", (A.SYNC_COPY_SDMA, 0, 1, 1, 0.0)),
+                                                      ("sdma_7_engines", (A.SYNC_COPY_SDMA, 0, 7, 1, 0.0)),
+                                                      ("cu8", (A.SYNC_COPY_CU, 8, 7, 4, 0.0)),
+                                                      ("cu16", (A.SYNC_COPY_CU, 16, 7, 4, 0.0)),
+                                                      ("cu32", (A.SYNC_COPY_CU, 32, 7, 4, 0.0)),
+                                                      ("colocated", (A.SYNC_COPY_COLOCATED, 0, 0, 1, 0.0)),
+                                                      ("cu32_xgmi_ring_153", (A.SYNC_COPY_CU, 32, 1, 4, 153.0)),
+                                                      ("cu32_xgmi_mesh_153", (A.SYNC_COPY_CU, 32, 7, 4, 153.0))):
+            t_o, _ = timed_loop(A.make_cfg(sb, scus, copy_teams=steams, copy_kslices=sks, copy_link_gbps=gbps), 10, 3)
             t_c, _ = timed_loop(A.make_cfg(sb, scus, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=steams,
-                                           copy_kslices=sks), 10, 3)
+                                           copy_kslices=sks, copy_link_gbps=gbps), 10, 3)
             sweep[sname] = {"t_overlap_us": round(t_o * 1e6, 1), "t_copy_only_us": round(t_c * 1e6, 1),
                             "tflops": round(2.0 * M * N * K / t_o / 1e12, 1),
                             "ratio": round(t_o / max(t_comp, t_c), 4)}

@@ -185,6 +185,7 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
   const int32_t tcount = count / teams + (team < count % teams ? 1 : 0);
   const int32_t S = (!a.copy_out && a.kslices > 1) ? a.kslices : 1;
   int32_t seq = -1;  // index of the item among the copied ones
+  uint64_t link_free = 0;  // thread 0, paced copies: when this team's link is next free
   for (int32_t h = 0; h < S; ++h)
     for (int32_t p = 0; p < a.num_chunks; ++p) {
       const int32_t c = a.arrival[p];
@@ -203,6 +204,15 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
       }
       const int64_t r0 = a.chunk_begin[c], r1 = a.chunk_begin[c + 1];
       const int64_t drow = a.copy_out ? a.slot_row[p] : r0;
+      if (a.pace_q16 && threadIdx.x == 0) {  // the item holds the link from when both are ready
+        int64_t bytes = 0;
+        for (int x = 0; x < a.ntensors; ++x) {
+          const int64_t lines = a.row_bytes[x] / 128;
+          bytes += (r1 - r0) * (S == 1 ? a.row_bytes[x] : ((h + 1) * lines / S - h * lines / S) * 128);
+        }
+        const uint64_t now = wall_clock64();
+        link_free = (link_free > now ? link_free : now) + ((static_cast<uint64_t>(bytes) * a.pace_q16) >> 36);
+      }
       for (int x = 0; x < a.ntensors; ++x) {
         const int64_t rb = a.row_bytes[x];
         if (S == 1) {
@@ -226,6 +236,10 @@ __device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores have reached the L2
       __syncthreads();
       if (threadIdx.x == 0) {
+        if (a.pace_q16) {  // paced: the item is delivered when its link time has passed
+          int n = 0;
+          while (wall_clock64() < link_free) backoff_sleep(n);
+        }
         release_agent();  // write this XCD's L2 back
         if (S == 1) {
           if (tree_count(a.xparts + c * kMaxXcd, a.parts + c, trank, tcount)) {

@@ -47,6 +47,11 @@ struct CopyArgs {
   // 128-byte row columns [h * R / kslices, (h + 1) * R / kslices) of each
   // tensor, R = row_bytes / 128.
   int32_t kslices;
+  // Link pacing (0 = none): each team stands for one link; an item occupies
+  // its team's link for bytes * pace_q16 / 2^36 wall-clock ticks (pace_q16 =
+  // ticks per MiB in 16.16 fixed point), starting when both the link is free
+  // and the item may start, and is published only when that time has passed.
+  uint64_t pace_q16;
   uint32_t* slice_flags;
   uint32_t* sparts;
   uint32_t* sxparts;

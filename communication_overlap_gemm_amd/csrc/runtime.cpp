@@ -343,6 +343,11 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs K/64 >= 4 x copy_kslices");
   }
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
+  if (cfg.copy_link_gbps != 0.f) {
+    if (!(cfg.copy_link_gbps >= 1.f && cfg.copy_link_gbps <= 10000.f))
+      return fail(SYNC_EINVAL, "copy_link_gbps must be 0 or in [1, 10000]");
+    if (cfg.backend != SYNC_COPY_CU) return fail(SYNC_EINVAL, "copy_link_gbps paces the CU backend's copy teams");
+  }
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
@@ -477,6 +482,12 @@ CopyArgs make_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2
   ca.slice_flags = cx.ws.sflags;
   ca.sparts = cx.ws.sparts;
   ca.sxparts = cx.ws.sxparts;
+  if (cx.cfg.copy_link_gbps > 0.f) {  // wall-clock ticks per MiB at the link rate, 16.16 fixed point
+    const double ticks_per_mib = static_cast<double>(cx.dev->wall_khz) * 1e3 * 1048576.0 /
+                                 (static_cast<double>(cx.cfg.copy_link_gbps) * 1e9);
+    ca.pace_q16 = static_cast<uint64_t>(ticks_per_mib * 65536.0 + 0.5);
+    if (!ca.pace_q16) ca.pace_q16 = 1;
+  }
   return ca;
 }
 

@@ -218,6 +218,13 @@ typedef struct {
                                early.  The chunk plan, dependency table and tile order are
                                unchanged.  0 or 1 = whole chunks; at most 8, with K/64 at least
                                4 x copy_kslices.  Other ops and backends: 0 or 1. */
+  float copy_link_gbps;     /* CU backend: 0 = copy at the copy workgroups' own speed; else each
+                               copy team stands for one link of this many GB/s (1e9 B/s, in
+                               [1, 10000]) and delivers an item (chunk or K-slice; RS: a chunk of
+                               C) no earlier than the link, free from its previous item and from
+                               the moment the item may start, has carried its bytes (e.g. 153
+                               for one xGMI link of an MI355X node: copy_teams = 1 paces a ring,
+                               7 teams seven links at once) */
 } sync_copy_cfg;
 
 /* ---- workspace ---------------------------------------------------------- */

@@ -116,3 +116,15 @@ def test_kslices_validation():
     rc = A.lib().sync_gemm_rs(rs.handle, ctypes.byref(A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2)), None, None,
                               None, 0, None, 256, None, None)
     assert rc == A.SYNC_EINVAL and "AG-GEMM" in A.sync_last_error()
+
+
+def test_link_pacing_validation():
+    """copy_link_gbps: 0 or within [1, 10000], and only for the CU backend."""
+    def rc_of(plan, cfg):
+        return A.lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg), None, None, None, None, 0, 256, None, None)
+    p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    for bad in (0.5, -3.0, 20000.0, float("nan")):
+        assert rc_of(p, A.make_cfg(A.SYNC_COPY_CU, 8, copy_link_gbps=bad)) == A.SYNC_EINVAL
+        assert "copy_link_gbps" in A.sync_last_error()
+    assert rc_of(p, A.make_cfg(A.SYNC_COPY_COLOCATED, copy_link_gbps=100.0)) == A.SYNC_EINVAL
+    assert "CU backend" in A.sync_last_error()

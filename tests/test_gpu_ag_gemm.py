@@ -586,3 +586,45 @@ def test_sdma_copy_only_advances_the_epoch():
         assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
         assert np.array_equal(host_bits(a_local), a)
         assert int(ws[0].item()) == it + 1
+
+
+# ---- copy teams paced at a link rate (one team = one link) -------------------
+
+def _paced_call(plan, tabs, a, b, m, n, k, world, flags, teams, kslices, gbps):
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    a_local = bf16_poison((m, k))
+    for ch in range(tabs["num_chunks"]):
+        if tabs["resident"][ch]:
+            r0, r1 = tabs["chunk_begin"][ch], tabs["chunk_begin"][ch + 1]
+            a_local[r0:r1] = a_peer[r0:r1]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    A.sync_read_timings(0)
+    cfg = A.make_cfg(A.SYNC_COPY_CU, copy_cus=16, flags=flags | A.SYNC_RUN_TIMED, copy_teams=teams,
+                     copy_kslices=kslices, copy_link_gbps=gbps)
+    print(f"[ag] paced {gbps} GB/s, teams={teams}, kslices={kslices}, flags={flags}", flush=True)
+    A.sync_ag_gemm(plan, cfg, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    (kernel_ms, _), = A.sync_read_timings(16)
+    return c.cpu().numpy(), host_bits(a_local), kernel_ms
+
+
+@pytest.mark.parametrize("teams,kslices", [(1, 0), (3, 0), (1, 2), (3, 4)])
+def test_paced_copy_is_exact_and_no_faster_than_its_links(teams, kslices):
+    """Three copied chunks of 1 MiB each, every team paced at 10 GB/s: the
+    output stays exact and the staged rows complete, and the copy-only call
+    lasts at least the busiest link's time (1 team: 3 MiB; 3 teams: 1 MiB)."""
+    m, n, k, world, gbps = 2048, 512, 1024, 4, 10.0
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, tile_m=128, tile_n=128, b_layout=A.SYNC_B_NK))
+    tabs = A.sync_plan_export(plan)
+    out, a_local, _ = _paced_call(plan, tabs, a, b, m, n, k, world, 0, teams, kslices, gbps)
+    assert np.array_equal(out.astype(np.float64), ref)
+    assert np.array_equal(a_local, a)
+    _, a_local, ms = _paced_call(plan, tabs, a, b, m, n, k, world, A.SYNC_RUN_COPY_ONLY, teams, kslices, gbps)
+    assert np.array_equal(a_local, a)
+    busiest = (3 if teams == 1 else 1) * (m // world) * k * 2
+    assert ms * 1e-3 >= 0.95 * busiest / (gbps * 1e9), (ms, busiest)

@@ -214,3 +214,26 @@ def test_rs_copy_store_policies(streaming, backend, cus, teams):
     cn, st, tabs = run_rs(m, n, k, W, a, b, split=1, backend=backend, copy_cus=cus, teams=teams, streaming=streaming)
     assert np.array_equal(cn.astype(np.float64), ref)
     check_staging(cn, st, tabs)
+
+
+@pytest.mark.parametrize("teams", [0, 4])
+def test_rs_paced_copy_out(teams):
+    """Copy-out paced at 20 GB/s per team: exact C and every chunk bitwise in
+    its send slot."""
+    m, n, k, W = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, tile_m=128, tile_n=128))
+    tabs = A.sync_plan_export(plan)
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    st = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    print(f"[rs] paced copy-out, teams={teams}", flush=True)
+    A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_CU, copy_cus=16, copy_teams=teams, copy_link_gbps=20.0),
+                   dev_bits(a), dev_bits(b), c, A.SYNC_DTYPE_F32, st, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    cn = c.cpu().numpy()
+    assert np.array_equal(cn.astype(np.float64), ref)
+    check_staging(cn, st.cpu().numpy(), tabs)
