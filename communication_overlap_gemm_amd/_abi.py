@@ -26,6 +26,7 @@ SYNC_ORDER_ROW_MAJOR, SYNC_ORDER_CHUNK_MAJOR, SYNC_ORDER_SWIZZLED = 0, 1, 2
 SYNC_B_KN, SYNC_B_NK = 0, 1
 SYNC_DTYPE_F32, SYNC_DTYPE_BF16 = 0, 1
 SYNC_COPY_PRESET, SYNC_COPY_SDMA, SYNC_COPY_CU, SYNC_COPY_HOST_GATED, SYNC_COPY_COLOCATED = 0, 1, 2, 3, 4
+SYNC_COPY_EPILOGUE = 5
 SYNC_RUN_COPY_ONLY, SYNC_RUN_COMPUTE_ONLY, SYNC_RUN_TIMED, SYNC_RUN_WITHHOLD, SYNC_RUN_TRACE = 1, 2, 4, 8, 16
 SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 

@@ -64,11 +64,13 @@ __device__ __forceinline__ int swz(int row, int slot) { return slot ^ ((row ^ (r
 // (rows past M fall outside num_records and are dropped).
 // WGM x WGN waves, each owning a (TM/WGM) x (TN/WGN) block; RPP staged rows
 // per pass (32, or 16 when the LDS ring cannot hold every wave's 32-row strip).
-template <int TM, int TN, int CT, int WGM, int WGN, int RPP>
+// PUSH (GEMM-RS instances): with push_row0 >= 0 the tile's rows also go to
+// staging from row push_row0 on (its send slot; the tile lies in one chunk).
+template <int TM, int TN, int CT, int WGM, int WGN, int RPP, bool PUSH = false>
 __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
                                              const f32x16_t (&acc)[TM / WGM / 32][TN / WGN / 32], char* lds,
                                              int64_t m0, int64_t n0, int rows_valid, int cols_valid, int wave,
-                                             int lane) {
+                                             int lane, int64_t push_row0 = -1) {
   constexpr int WM = TM / WGM, WN = TN / WGN, MI = WM / 32, NI = WN / 32;
   constexpr int ES = CT == 0 ? 4 : 2;
   constexpr int SP = WN + 32 / ES;   // staged strip pitch (elements), +32 B
@@ -103,23 +105,31 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
       const __amdgpu_buffer_rsrc_t cs =
           make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
                     rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
+      const bool push = PUSH && push_row0 >= 0;
+      [[maybe_unused]] const __amdgpu_buffer_rsrc_t ss =
+          make_rsrc(static_cast<char*>(push ? a.staging : a.C) + ((push_row0 + strip) * N + n0 + wn * WN) * ES,
+                    push && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
 #pragma unroll
       for (int it = 0; it < RPP / RPI; ++it) {
         const int r = it * RPI + rr;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (r * SP + rc) * ES);
-        if (col_ok)
+        if (col_ok) {
           __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
+          if constexpr (PUSH) {
+            if (push) __builtin_amdgcn_raw_buffer_store_b128(v, ss, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
+          }
+        }
       }
       __syncthreads();
     }
   }
 }
 
-template <int TM, int TN, int CT>
+template <int TM, int TN, int CT, bool PUSH = false>
 __device__ __forceinline__ void store_tile_c(const GemmArgs& a, const f32x16_t (&acc)[TM / 64][TN / 64], char* lds,
                                              int64_t m0, int64_t n0, int rows_valid, int cols_valid, int wave,
-                                             int lane) {
-  store_tile_w<TM, TN, CT, 2, 2, 32>(a, acc, lds, m0, n0, rows_valid, cols_valid, wave, lane);
+                                             int lane, int64_t push_row0 = -1) {
+  store_tile_w<TM, TN, CT, 2, 2, 32, PUSH>(a, acc, lds, m0, n0, rows_valid, cols_valid, wave, lane, push_row0);
 }
 
 // GEMM-RS completion of tile t: every wave's C stores have reached the L2;
@@ -138,6 +148,10 @@ __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, ui
         st_relaxed_agent(a.cnt.counters + c, 0u);  // every tile of c has counted: ready for the next call
         if (a.trace_chunks) a.trace_chunks[2 * c] = wall_clock64();
         st_release_agent(a.flags + c, epoch);
+        if (a.push_rows) {  // the tiles also wrote the chunk into its send slot
+          if (a.trace_chunks) a.trace_chunks[2 * c + 1] = wall_clock64();
+          st_release_agent(a.sent + c, epoch);
+        }
       }
     }
   }
@@ -779,7 +793,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
     if constexpr (SPREAD) wait_vmcnt<0>();  // the zero-length loads after the last stage have landed
     __syncthreads();  // every wave is done reading the ring before the epilogue reuses it
     if (sliced && s_skip) continue;  // a slice never arrived: tile left untouched
-    store_tile_w<TM, TN, CT, WGM, WGN, RPP>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane);
+    store_tile_w<TM, TN, CT, WGM, WGN, RPP, RS>(a, acc, smem, m0, n0, rows_valid, cols_valid, wave, lane,
+                                                RS && a.push_rows ? a.push_rows[t] : -1);
     if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
     if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
   }

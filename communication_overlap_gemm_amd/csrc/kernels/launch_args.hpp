@@ -85,6 +85,13 @@ struct GemmArgs {
   // first K-step of slice h (slice_flags as in CopyArgs)
   int32_t kslices;
   const uint32_t* slice_flags;
+  // GEMM-RS with the epilogue backend (push_rows non-null): the epilogue also
+  // stores tile t's rows into `staging` from row push_rows[t] on (its send
+  // slot; every tile lies in one chunk), and the tile that completes chunk c
+  // raises sent[c] with done[c]
+  const int32_t* push_rows;
+  void* staging;
+  uint32_t* sent;
   CopyArgs copy;
 };
 

@@ -212,12 +212,14 @@ struct DeviceTables {
   int32_t* arrival = nullptr;
   int32_t* resident = nullptr;
   int64_t* slot_row = nullptr;
+  int32_t* push_rows = nullptr;  // GEMM-RS: staging row of each tile's first row (tiles in one chunk)
   void* block = nullptr;  // one allocation holding all of the above
 };
 
 struct sync_plan_s {
   Plan plan;
-  std::vector<int64_t> slot_row;  // staging row of each send position (C+1)
+  std::vector<int64_t> slot_row;   // staging row of each send position (C+1)
+  std::vector<int32_t> push_rows;  // GEMM-RS, every tile in one chunk: staging row of each tile's first row (T)
   std::mutex mu;
   std::map<int, DeviceTables> dev;
 };
@@ -243,7 +245,7 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   auto sz = [](size_t n, size_t e) { return align_up(static_cast<int64_t>(n * e), 256); };
   const int64_t total = sz(pl.tile_order.size(), 4) + sz(pl.dep_ptr.size(), 8) + sz(pl.dep_idx.size(), 4) +
                         sz(pl.tiles_in.size(), 4) + sz(pl.chunk_begin.size(), 8) + sz(pl.arrival.size(), 4) +
-                        sz(pl.resident.size(), 4) + sz(p->slot_row.size(), 8) + 256;
+                        sz(pl.resident.size(), 4) + sz(p->slot_row.size(), 8) + sz(p->push_rows.size(), 4) + 256;
   std::vector<char> host(static_cast<size_t>(total), 0);
   void* block = nullptr;
   HIP_TRY(hipMalloc(&block, static_cast<size_t>(total)));
@@ -259,6 +261,7 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   put(cur, host, pl.arrival, &t.arrival, base);
   put(cur, host, pl.resident, &t.resident, base);
   put(cur, host, p->slot_row, &t.slot_row, base);
+  if (!p->push_rows.empty()) put(cur, host, p->push_rows, &t.push_rows, base);
   hipError_t e = hipMemcpy(block, host.data(), static_cast<size_t>(total), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(block);
@@ -348,7 +351,9 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
       return fail(SYNC_EINVAL, "copy_link_gbps must be 0 or in [1, 10000]");
     if (cfg.backend != SYNC_COPY_CU) return fail(SYNC_EINVAL, "copy_link_gbps paces the CU backend's copy teams");
   }
-  if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_COLOCATED) return fail(SYNC_EINVAL, "bad backend");
+  if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_EPILOGUE) return fail(SYNC_EINVAL, "bad backend");
+  if (cfg.backend == SYNC_COPY_EPILOGUE && op != SYNC_OP_GEMM_RS)
+    return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend sends GEMM-RS output; AG and attention copy in");
   if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
     return fail(SYNC_EINVAL, "unknown cfg.flags bits");
@@ -500,6 +505,7 @@ struct Roles {
   bool no_compute = false;  // co-located copy-only: the copy phase alone
   bool sdma = false;    // HOST_GATED: stream-ordered SDMA copies on the library's streams
   bool engines = false; // SDMA: copies queued on the SDMA engines through HSA, gated by the call
+  bool push = false;    // EPILOGUE: the RS epilogue stores every tile into its send slot too
 };
 
 // CU backend: one launch, copy_cus * wpc copy workgroups first, then one
@@ -536,6 +542,11 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
         r.wait = 0;
       else
         r.colocated = 1;
+      break;
+    case SYNC_COPY_EPILOGUE:
+      r.grid = d.num_cus * wpc;
+      r.wait = 0;
+      r.push = !compute_only;
       break;
     case SYNC_COPY_SDMA:
       r.grid = copy_only ? 0 : d.num_cus * wpc;
@@ -667,6 +678,16 @@ int sync_plan(const sync_plan_desc* desc, sync_plan_t* out) {
   for (int32_t s = 0; s < pl.num_chunks; ++s) {
     const int32_t c = pl.arrival[s];
     p->slot_row[s + 1] = p->slot_row[s] + (pl.chunk_begin[c + 1] - pl.chunk_begin[c]);
+  }
+  bool one_chunk = pl.desc.op == SYNC_OP_GEMM_RS && pl.rows < (int64_t(1) << 31);
+  for (int32_t t = 0; one_chunk && t < pl.num_tiles; ++t) one_chunk = pl.dep_ptr[t + 1] - pl.dep_ptr[t] == 1;
+  if (one_chunk) {
+    p->push_rows.resize(static_cast<size_t>(pl.num_tiles));
+    for (int32_t t = 0; t < pl.num_tiles; ++t) {
+      const int32_t c = pl.dep_idx[pl.dep_ptr[t]];
+      const int64_t m0 = static_cast<int64_t>(t / pl.tiles_n) * pl.desc.tile_m;
+      p->push_rows[t] = static_cast<int32_t>(p->slot_row[pl.chunk_pos[c]] + (m0 - pl.chunk_begin[c]));
+    }
   }
   *out = p.release();
   return SYNC_OK;
@@ -848,6 +869,19 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
     g.copy.wait_flags = cx.ws.flags;
   }
   const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  if (r.push) {
+    const int64_t es = c_dtype == SYNC_DTYPE_F32 ? 4 : 2;
+    if (pl.desc.m * pl.desc.n * es >= (int64_t(1) << 31))
+      return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend needs m x n x element size below 2 GiB");
+    if (pl.desc.b_layout != SYNC_B_NK)
+      return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend is built for B stored [n][k]");
+    if (!cx.tab->push_rows)
+      return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend needs every tile inside one chunk (chunk rows a "
+                                     "multiple of tile_m)");
+    g.push_rows = cx.tab->push_rows;
+    g.staging = staging;
+    g.sent = cx.ws.sent;
+  }
   return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, nullptr, nullptr, nullptr, 0,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     g.copy_blocks = rr.copy_blocks;

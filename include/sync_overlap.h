@@ -174,8 +174,18 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *               themselves].  AG and attention: every workgroup first copies
  *               its share of each chunk and then computes.  GEMM-RS: every
  *               workgroup stores its tiles and then joins the copy-out, chunk
- *               by chunk in send order. */
-enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOST_GATED = 3, SYNC_COPY_COLOCATED = 4 };
+ *               by chunk in send order.
+ *   EPILOGUE    GEMM-RS only: no copy pass at all; the epilogue of every tile
+ *               stores it both into C and, row by row, into its chunk's send
+ *               slot in `staging`, and the tile that completes chunk c raises
+ *               sent[c] with done[c] [SYN-S Fig. 7: communication by the
+ *               compute SMs' own stores; Entwine abstract: output handed to
+ *               communication as the tiles produce it].  Needs B stored
+ *               [n][k], every tile inside one chunk (chunk bounds on tile
+ *               rows) and m x n x (element size) below 2 GiB, else
+ *               EUNSUPPORTED. */
+enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOST_GATED = 3, SYNC_COPY_COLOCATED = 4,
+       SYNC_COPY_EPILOGUE = 5 };
 
 /* mode bits for sync_copy_cfg.flags */
 enum {

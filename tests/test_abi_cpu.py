@@ -128,3 +128,10 @@ def test_link_pacing_validation():
         assert "copy_link_gbps" in A.sync_last_error()
     assert rc_of(p, A.make_cfg(A.SYNC_COPY_COLOCATED, copy_link_gbps=100.0)) == A.SYNC_EINVAL
     assert "CU backend" in A.sync_last_error()
+
+
+def test_epilogue_backend_is_for_gemm_rs():
+    p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    rc = A.lib().sync_ag_gemm(p.handle, ctypes.byref(A.make_cfg(A.SYNC_COPY_EPILOGUE)), None, None, None, None, 0,
+                              256, None, None)
+    assert rc == A.SYNC_EUNSUPPORTED and "EPILOGUE" in A.sync_last_error()

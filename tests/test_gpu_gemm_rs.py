@@ -237,3 +237,52 @@ def test_rs_paced_copy_out(teams):
     cn = c.cpu().numpy()
     assert np.array_equal(cn.astype(np.float64), ref)
     check_staging(cn, st.cpu().numpy(), tabs)
+
+
+# ---- EPILOGUE backend: every tile stores itself into its send slot ----------
+
+@pytest.mark.parametrize("m,n,k,W,split,tile,rank", [(1024, 512, 256, 4, 1, (128, 128), 0),
+                                                      (1024, 512, 256, 4, 2, (128, 128), 3),
+                                                      (2048, 768, 320, 4, 1, (256, 256), 1),
+                                                      (1024, 520, 320, 4, 1, (256, 128), 2)])
+def test_rs_epilogue_push(m, n, k, W, split, tile, rank):
+    """No copy pass: C exact for small integers, every chunk bitwise in its
+    send slot, done and sent flags raised, counters back to zero (a ragged
+    last tile column included)."""
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    for rep in range(2):
+        cn, st, tabs = run_rs(m, n, k, W, a, b, split=split, tile=tile, backend=A.SYNC_COPY_EPILOGUE, copy_cus=0,
+                              rank=rank, layout=A.SYNC_B_NK)
+        assert np.array_equal(cn.astype(np.float64), ref)
+        check_staging(cn, st, tabs)
+
+
+def test_rs_epilogue_needs_tiles_inside_chunks():
+    """A 256-row tile over 128-row chunks straddles two chunks: EUNSUPPORTED."""
+    m, n, k, W = 1024, 512, 256, 4
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, split=2, tile_m=256, tile_n=256,
+                                   b_layout=A.SYNC_B_NK))
+    ws = workspace(plan)
+    t = torch.zeros((m, n), dtype=torch.float32, device="cuda:0")
+    ab = torch.zeros((m, k), dtype=torch.int16, device="cuda:0")
+    bb = torch.zeros((n, k), dtype=torch.int16, device="cuda:0")
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), ab, bb, t, A.SYNC_DTYPE_F32, t.clone(), ws,
+                       torch.cuda.current_stream(), None)
+    assert ei.value.code == A.SYNC_EUNSUPPORTED and "one chunk" in ei.value.message
+
+
+def test_full_size_rs_epilogue_exact():
+    """The Llama-3-8B down-projection share with the epilogue backend: exact
+    for small integers on samples, staging bitwise."""
+    m, n, k, W = 8192, 4096, 1792, 8
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    cn, st, tabs = run_rs(m, n, k, W, a, b, tile=(256, 256), backend=A.SYNC_COPY_EPILOGUE, copy_cus=0,
+                          layout=A.SYNC_B_NK)
+    assert np.all(cn == np.round(cn))
+    check_staging(cn, st, tabs)
+    rows = np.random.default_rng(13).integers(0, m, 3000)
+    cols = np.random.default_rng(14).integers(0, n, 3000)
+    exact = oracle.gemm_f64_sampled(a, b, m, n, k, rows, cols, b_layout="nk")
+    assert np.array_equal(cn[rows, cols].astype(np.float64), exact)
