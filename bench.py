@@ -345,6 +345,13 @@ def other_rows(steps=5, warmup=2, pol=0):
         t[name] = _time_calls(lambda: A.sync_gemm_rs(plan, cfg, a, b, c, A.SYNC_DTYPE_F32, st, ws, s, None), steps,
                               warmup)
         check(ws)
+    # the same with its reduce-scatter step: each send slot = own tile + incoming partial sums
+    part = torch.from_numpy(inputs.partials_f32(m, n)).to(dev)
+    t["overlapped_reduce_step"] = _time_calls(
+        lambda: A.sync_gemm_rs_reduce(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), a, b, c, part, st, ws, s, None), steps,
+        warmup)
+    check(ws)
+    del part
     flops = 2.0 * m * n * k
     hbm = (m * k + k * n) * 2 + m * n * 4 * 2  # A, B, then C and staging each written once
     out["gemm_rs_llama8b_down"] = {
@@ -354,6 +361,7 @@ def other_rows(steps=5, warmup=2, pol=0):
         "tflops": round(flops / t["overlapped"] / 1e12, 1),
         "t_overlap_us": round(t["overlapped"] * 1e6, 1), "t_compute_only_us": round(t["compute_only"] * 1e6, 1),
         "t_overlap_colocated_us": round(t["overlapped_colocated"] * 1e6, 1),
+        "t_overlap_with_reduce_step_us": round(t["overlapped_reduce_step"] * 1e6, 1),
         "t_overlap_32_copy_cus_us": round(t["overlapped_32_copy_cus"] * 1e6, 1),
         "ratio_to_compute_only": round(t["overlapped"] / t["compute_only"], 4),
         "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -32,7 +32,8 @@ SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 
 EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
-    "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_gemm_rs", "sync_ring_attn_step",
+    "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_gemm_rs", "sync_gemm_rs_reduce",
+    "sync_ring_attn_step",
     "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
     "sync_autotune", "sync_tune_workspace_size", "sync_tune_forget",
 )
@@ -135,6 +136,7 @@ def lib():
             "sync_workspace_status": (i32, [vp, vp, ctypes.POINTER(i32)]),
             "sync_ag_gemm": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, i32, vp, vp, vp]),
             "sync_gemm_rs": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, i32, vp, vp, vp, vp]),
+            "sync_gemm_rs_reduce": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp]),
             "sync_ring_attn_step": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                           i32, vp, vp, vp]),
             "sync_get_device_info": (i32, [ctypes.POINTER(sync_device_info)]),
@@ -330,6 +332,13 @@ def sync_gemm_rs(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, c_dtype: int
                  copy=None) -> None:
     _check(lib().sync_gemm_rs(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a), _ptr(b),
                               _ptr(c), c_dtype, _ptr(staging), _ptr(ws), _stream(compute), _stream(copy)))
+
+
+def sync_gemm_rs_reduce(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, partials, staging, ws, compute=None,
+                        copy=None) -> None:
+    _check(lib().sync_gemm_rs_reduce(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a), _ptr(b),
+                                     _ptr(c), _ptr(partials), _ptr(staging), _ptr(ws), _stream(compute),
+                                     _stream(copy)))
 
 
 def sync_ring_attn_step(plan: Plan, cfg: Optional[sync_copy_cfg], q, k_peer, v_peer, k_local, v_local, o, m_state,

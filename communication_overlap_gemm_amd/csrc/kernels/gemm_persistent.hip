@@ -64,6 +64,14 @@ __device__ __forceinline__ int swz(int row, int slot) { return slot ^ ((row ^ (r
 // (rows past M fall outside num_records and are dropped).
 // WGM x WGN waves, each owning a (TM/WGM) x (TN/WGN) block; RPP staged rows
 // per pass (32, or 16 when the LDS ring cannot hold every wave's 32-row strip).
+// 16 bytes of fp32 C plus 16 bytes of incoming fp32 partials, element-wise.
+__device__ __forceinline__ u32x4_t add_partials(u32x4_t c, u32x4_t p) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(__uint_as_float(c[i]) + __uint_as_float(p[i]));
+  return r;
+}
+
 // PUSH (GEMM-RS instances): with push_row0 >= 0 the tile's rows also go to
 // staging from row push_row0 on (its send slot; the tile lies in one chunk).
 template <int TM, int TN, int CT, int WGM, int WGN, int RPP, bool PUSH = false>
@@ -109,6 +117,12 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
       [[maybe_unused]] const __amdgpu_buffer_rsrc_t ss =
           make_rsrc(static_cast<char*>(push ? a.staging : a.C) + ((push_row0 + strip) * N + n0 + wn * WN) * ES,
                     push && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
+      // the incoming partials at the same rows and columns as C (none: zero
+      // records); fp32 C only
+      const bool reduce = CT == 0 && push && a.partials;
+      [[maybe_unused]] const __amdgpu_buffer_rsrc_t ps =
+          make_rsrc(static_cast<const char*>(reduce ? a.partials : a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
+                    reduce && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
 #pragma unroll
       for (int it = 0; it < RPP / RPI; ++it) {
         const int r = it * RPI + rr;
@@ -116,7 +130,14 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
         if (col_ok) {
           __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
           if constexpr (PUSH) {
-            if (push) __builtin_amdgcn_raw_buffer_store_b128(v, ss, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
+            if (push) {
+              const uint32_t off = static_cast<uint32_t>(r * row_bytes + rc * ES);
+              u32x4_t w = v;
+              if constexpr (CT == 0) {
+                if (reduce) w = add_partials(v, buf_load_b128(ps, off));
+              }
+              __builtin_amdgcn_raw_buffer_store_b128(w, ss, off, 0, 0);
+            }
           }
         }
       }

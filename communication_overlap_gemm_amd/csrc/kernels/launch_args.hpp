@@ -92,6 +92,10 @@ struct GemmArgs {
   const int32_t* push_rows;
   void* staging;
   uint32_t* sent;
+  // reduce-scatter step (non-null with push_rows; fp32 C): [M][N] fp32, the
+  // partial sums arriving from the ring predecessor; a send slot receives
+  // the tile plus these rows
+  const void* partials;
   CopyArgs copy;
 };
 

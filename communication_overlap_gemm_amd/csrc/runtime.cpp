@@ -837,11 +837,19 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
                   });
 }
 
-int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c, int32_t c_dtype,
-                 void* staging, void* ws, void* compute, void* copy) {
+// GEMM-RS share; `partials` (fp32 [m][n], or null) makes the send the
+// reduce-scatter step: slot data = tile + the incoming partial sums.
+static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
+                        int32_t c_dtype, const void* partials, void* staging, void* ws, void* compute, void* copy) {
   CallCtx cx;
   int rc = prepare(plan, cfg, ws, SYNC_OP_GEMM_RS, cx);
   if (rc) return rc;
+  if (partials) {
+    if (cx.cfg.backend != SYNC_COPY_EPILOGUE || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY))
+      return fail(SYNC_EUNSUPPORTED, "the reduce-scatter step runs in the EPILOGUE backend's stores");
+    if (c_dtype != SYNC_DTYPE_F32) return fail(SYNC_EUNSUPPORTED, "the reduce-scatter step needs fp32 C");
+    if (!aligned16(partials)) return fail(SYNC_EINVAL, "partials must be 16-byte aligned");
+  }
   const Plan& pl = plan->plan;
   if ((rc = check_gemm_shape(pl))) return rc;
   if (c_dtype != SYNC_DTYPE_F32 && c_dtype != SYNC_DTYPE_BF16) return fail(SYNC_EINVAL, "bad c_dtype");
@@ -881,6 +889,7 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
     g.push_rows = cx.tab->push_rows;
     g.staging = staging;
     g.sent = cx.ws.sent;
+    g.partials = partials;
   }
   return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, nullptr, nullptr, nullptr, 0,
                   [&](hipStream_t st, const Roles& rr) -> int {
@@ -890,6 +899,17 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
                                         st));
                     return SYNC_OK;
                   });
+}
+
+int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c, int32_t c_dtype,
+                 void* staging, void* ws, void* compute, void* copy) {
+  return gemm_rs_impl(plan, cfg, a, b, c, c_dtype, nullptr, staging, ws, compute, copy);
+}
+
+int sync_gemm_rs_reduce(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
+                        const float* partials, void* staging, void* ws, void* compute, void* copy) {
+  if (!partials) return fail(SYNC_EINVAL, "partials is NULL");
+  return gemm_rs_impl(plan, cfg, a, b, c, SYNC_DTYPE_F32, partials, staging, ws, compute, copy);
 }
 
 int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q, const void* k_peer,

@@ -14,6 +14,7 @@ from __future__ import annotations
 import numpy as np
 
 SEED_A, SEED_B, SEED_Q, SEED_K, SEED_V = 1, 2, 3, 4, 5
+SEED_P = 6
 ALT_SEED_OFFSET = 100
 
 
@@ -75,3 +76,12 @@ def attention_operands(sq: int, hq: int, skv: int, hkv: int, d: int,
     k = normal_bf16(seed_k, (skv, hkv, d))
     v = normal_bf16(seed_v, (skv, hkv, d))
     return q, k, v
+
+
+def partials_f32(m: int, n: int, seed: int = SEED_P, integer: bool = False) -> np.ndarray:
+    """[m, n] float32 stand-in for the partial sums a rank receives in a ring
+    reduce-scatter: small integers in [-8, 8] (exact sums) or N(0,1)/8."""
+    rng = np.random.default_rng(seed)
+    if integer:
+        return rng.integers(-8, 9, size=(m, n)).astype(np.float32)
+    return (rng.standard_normal((m, n), dtype=np.float32) / np.float32(8.0)).astype(np.float32)

@@ -311,6 +311,19 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
 int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
                  int32_t c_dtype, void* staging, void* ws, void* compute, void* copy);
 
+/* GEMM-RS share with its reduce-scatter step [SYN-S "Experiments", paper
+ * sec. 6.1: GEMM-RS; in a ring reduce-scatter each rank adds its own partial
+ * result to the partial sum it receives and forwards the total].  As
+ * sync_gemm_rs with the EPILOGUE backend and fp32 C, plus
+ *   partials fp32 [m][n]: the partial sums arriving from the ring predecessor,
+ *            at C's row positions (read-only);
+ * staging slot p then holds C + partials over the rows of chunk arrival[p]
+ * (fp32 add of the stored C value and the partial), written by the epilogue of
+ * each tile; C holds this rank's own product as before.  Other backends,
+ * bf16 C or COMPUTE_ONLY: EUNSUPPORTED; partials NULL: EINVAL. */
+int sync_gemm_rs_reduce(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
+                        const float* partials, void* staging, void* ws, void* compute, void* copy);
+
 /* Ring-attention local step [SYN-S "Experiments", paper sec. 6.1 and Fig. 9:
  * RingAttention].  KV blocks (chunks of K and V token rows) are staged from
  * k_peer/v_peer into k_local/v_local in arrival order; each (query tile, head)

@@ -151,3 +151,14 @@ def rs_staging_expected(r_full, plan: PlanTables):
         slots.append((c, b, e))
         parts.append(r_full[b:e])
     return slots, np.concatenate(parts, axis=0)
+
+
+def rs_reduce_staging_expected(r_full, partials, plan: PlanTables):
+    """The reduce-scatter step of the share (Syncopate summary page,
+    "Experiments", paper sec. 6.1: GEMM-RS; a ring reduce-scatter forwards the
+    sum of the rank's own partial result and the partial sum it received):
+    staging slot p holds, over the rows of chunk arrival[p], R + P in fp64,
+    where P is the received partial sum.  Same slot order as
+    rs_staging_expected."""
+    total = np.asarray(r_full, dtype=np.float64) + np.asarray(partials, dtype=np.float64)
+    return rs_staging_expected(total, plan)

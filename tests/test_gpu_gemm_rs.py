@@ -286,3 +286,89 @@ def test_full_size_rs_epilogue_exact():
     cols = np.random.default_rng(14).integers(0, n, 3000)
     exact = oracle.gemm_f64_sampled(a, b, m, n, k, rows, cols, b_layout="nk")
     assert np.array_equal(cn[rows, cols].astype(np.float64), exact)
+
+
+# ---- the reduce-scatter step: send slot = own tile + incoming partial sums ---
+
+def _run_rs_reduce(m, n, k, W, a, b, p, split=1, tile=(128, 128), rank=0):
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, rank=rank, split=split, tile_m=tile[0],
+                                   tile_n=tile[1], b_layout=A.SYNC_B_NK))
+    tabs = A.sync_plan_export(plan)
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    st = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    pd = torch.from_numpy(p).to("cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    print(f"[rs-reduce] m={m} n={n} k={k} W={W} split={split} tile={tile} rank={rank}", flush=True)
+    A.sync_gemm_rs_reduce(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), dev_bits(a), dev_bits(b), c, pd, st, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    hdr, flags, counters, parts, sent = ws_arrays(ws, tabs["num_chunks"])
+    assert np.all(flags == hdr[0]) and np.all(sent == hdr[0]) and not counters.any()
+    return c.cpu().numpy(), st.cpu().numpy(), plan
+
+
+@pytest.mark.parametrize("m,n,k,W,split,tile,rank", [(1024, 512, 256, 4, 1, (128, 128), 0),
+                                                      (1024, 520, 320, 4, 2, (128, 128), 3),
+                                                      (2048, 768, 320, 4, 1, (256, 256), 1)])
+def test_rs_reduce_step_exact(m, n, k, W, split, tile, rank):
+    """Small-integer operands and partials: C = R and every send slot = R + P
+    over its chunk's rows, exactly, in the oracle's slot order."""
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    p = inputs.partials_f32(m, n, integer=True)
+    r = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    cn, st, _ = _run_rs_reduce(m, n, k, W, a, b, p, split, tile, rank)
+    assert np.array_equal(cn.astype(np.float64), r)
+    ptab = oracle.plan_ref(oracle.PlanDesc(op=oracle.OP_GEMM_RS, m=m, n=n, k=k, world=W, rank=rank, split=split,
+                                           tile_m=tile[0], tile_n=tile[1]))
+    _, want = oracle.rs_reduce_staging_expected(r, p, ptab)
+    assert np.array_equal(st.astype(np.float64), want)
+
+
+def test_rs_reduce_step_normal_data():
+    """N(0,1)/64 operands, N(0,1)/8 partials: every slot within the fp32 bar
+    of the fp64 oracle's R + P (relative Frobenius <= 1e-3 per slot)."""
+    m, n, k, W = 1024, 512, 1024, 4
+    a, b = inputs.gemm_operands(m, n, k, 64.0, b_layout="nk")
+    p = inputs.partials_f32(m, n)
+    r = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    _, st, _ = _run_rs_reduce(m, n, k, W, a, b, p)
+    ptab = oracle.plan_ref(oracle.PlanDesc(op=oracle.OP_GEMM_RS, m=m, n=n, k=k, world=W))
+    slots, want = oracle.rs_reduce_staging_expected(r, p, ptab)
+    row = 0
+    for c, b0, e in slots:
+        got, ref = st[row:row + e - b0].astype(np.float64), want[row:row + e - b0]
+        assert np.linalg.norm(got - ref) <= 1e-3 * np.linalg.norm(ref), c
+        row += e - b0
+
+
+def test_full_size_rs_reduce_step():
+    """The Llama-3-8B down-projection share with its reduce-scatter step:
+    sampled C exact against the oracle for small integers, and every send slot
+    the fp32 sum of the stored C and the partials, bitwise."""
+    m, n, k, W = 8192, 4096, 1792, 8
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    p = inputs.partials_f32(m, n, integer=True)
+    cn, st, plan = _run_rs_reduce(m, n, k, W, a, b, p, tile=(256, 256))
+    tabs = A.sync_plan_export(plan)
+    check_staging((cn + p).astype(np.float32), st, tabs)
+    rows = np.random.default_rng(15).integers(0, m, 3000)
+    cols = np.random.default_rng(16).integers(0, n, 3000)
+    exact = oracle.gemm_f64_sampled(a, b, m, n, k, rows, cols, b_layout="nk")
+    assert np.array_equal(cn[rows, cols].astype(np.float64), exact)
+
+
+def test_rs_reduce_step_validation():
+    m, n, k, W = 1024, 512, 256, 4
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, b_layout=A.SYNC_B_NK))
+    ws = workspace(plan)
+    t = torch.zeros((m, n), dtype=torch.float32, device="cuda:0")
+    ab = torch.zeros((m, k), dtype=torch.int16, device="cuda:0")
+    bb = torch.zeros((n, k), dtype=torch.int16, device="cuda:0")
+    s = torch.cuda.current_stream()
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_gemm_rs_reduce(plan, A.make_cfg(A.SYNC_COPY_CU, 16), ab, bb, t, t.clone(), t.clone(), ws, s, None)
+    assert ei.value.code == A.SYNC_EUNSUPPORTED
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_gemm_rs_reduce(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), ab, bb, t, None, t.clone(), ws, s, None)
+    assert ei.value.code == A.SYNC_EINVAL
