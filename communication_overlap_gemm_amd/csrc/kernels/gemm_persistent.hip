@@ -95,6 +95,24 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int h = 0; h < 32 / RPP; ++h) {
+      const int strip = wm * WM + i * 32 + h * RPP;  // first tile row of this pass
+      const int rows_left = rows_valid - strip;
+      const bool push = PUSH && push_row0 >= 0;
+      // reduce-scatter step (fp32 C): this pass's incoming partials are loaded
+      // first, so that their latency overlaps the staging through LDS (rows
+      // past M lie outside the resource and read as zero)
+      const bool reduce = CT == 0 && push && a.partials;
+      [[maybe_unused]] const __amdgpu_buffer_rsrc_t ps =
+          make_rsrc(static_cast<const char*>(reduce ? a.partials : a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
+                    reduce && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
+      [[maybe_unused]] u32x4_t pv[PUSH && CT == 0 ? RPP / RPI : 1];
+      if constexpr (PUSH && CT == 0) {
+        if (reduce && col_ok) {
+#pragma unroll
+          for (int it = 0; it < RPP / RPI; ++it)
+            pv[it] = buf_load_b128(ps, static_cast<uint32_t>((it * RPI + rr) * row_bytes + rc * ES));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NI; ++j)
 #pragma unroll
@@ -108,21 +126,12 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
           }
         }
       __syncthreads();
-      const int strip = wm * WM + i * 32 + h * RPP;  // first tile row of this pass
-      const int rows_left = rows_valid - strip;
       const __amdgpu_buffer_rsrc_t cs =
           make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
                     rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
-      const bool push = PUSH && push_row0 >= 0;
       [[maybe_unused]] const __amdgpu_buffer_rsrc_t ss =
           make_rsrc(static_cast<char*>(push ? a.staging : a.C) + ((push_row0 + strip) * N + n0 + wn * WN) * ES,
                     push && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
-      // the incoming partials at the same rows and columns as C (none: zero
-      // records); fp32 C only
-      const bool reduce = CT == 0 && push && a.partials;
-      [[maybe_unused]] const __amdgpu_buffer_rsrc_t ps =
-          make_rsrc(static_cast<const char*>(reduce ? a.partials : a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
-                    reduce && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
 #pragma unroll
       for (int it = 0; it < RPP / RPI; ++it) {
         const int r = it * RPI + rr;
@@ -134,7 +143,7 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
               const uint32_t off = static_cast<uint32_t>(r * row_bytes + rc * ES);
               u32x4_t w = v;
               if constexpr (CT == 0) {
-                if (reduce) w = add_partials(v, buf_load_b128(ps, off));
+                if (reduce) w = add_partials(v, pv[it]);
               }
               __builtin_amdgcn_raw_buffer_store_b128(w, ss, off, 0, 0);
             }
