@@ -90,7 +90,8 @@ class sync_tune_space(ctypes.Structure):
     _fields_ = [("splits", _P32), ("n_splits", ctypes.c_int32), ("tiles", _P32), ("n_tiles", ctypes.c_int32),
                 ("orders", _P32), ("n_orders", ctypes.c_int32), ("copy_cus", _P32), ("n_copy_cus", ctypes.c_int32),
                 ("warmup", ctypes.c_int32), ("iters", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
-                ("force", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("force", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("agents", ctypes.c_void_p), ("n_agents", ctypes.c_int32)]
 
 
 class sync_tune_buffers(ctypes.Structure):
@@ -102,7 +103,8 @@ class sync_tune_buffers(ctypes.Structure):
 class sync_tune_result(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_order", ctypes.c_int32), ("copy_cus", ctypes.c_int32), ("best_ms", ctypes.c_float),
-                ("candidates_run", ctypes.c_int32), ("candidates_skipped", ctypes.c_int32)]
+                ("candidates_run", ctypes.c_int32), ("candidates_skipped", ctypes.c_int32),
+                ("backend", ctypes.c_int32), ("agent", ctypes.c_int32)]
 
 
 class sync_timing(ctypes.Structure):
@@ -279,14 +281,19 @@ def sync_trace_export(plan: Plan, ws, stream=None) -> dict:
 
 def make_tune_space(splits=(1, 2, 4), tiles=((256, 256), (256, 128), (128, 128)),
                     orders=(SYNC_ORDER_CHUNK_MAJOR,), copy_cus=(16, 32), warmup: int = 0, iters: int = 0,
-                    timeout_ns: int = 0, force: int = 0):
-    """A sync_tune_space plus the arrays it points into (keep the tuple alive while it is used)."""
+                    timeout_ns: int = 0, force: int = 0, agents=()):
+    """A sync_tune_space plus the arrays it points into (keep the tuple alive while it is used).
+    agents: sync_copy_cfg entries (make_cfg) to try instead of the copy_cus list."""
     arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.int32).reshape(-1))
             for x in (splits, tiles, orders, copy_cus)]
     sp = sync_tune_space()
     sp.splits, sp.tiles, sp.orders, sp.copy_cus = (a.ctypes.data_as(_P32) for a in arrs)
     sp.n_splits, sp.n_tiles, sp.n_orders, sp.n_copy_cus = len(arrs[0]), len(arrs[1]) // 2, len(arrs[2]), len(arrs[3])
     sp.warmup, sp.iters, sp.timeout_ns, sp.force = warmup, iters, timeout_ns, force
+    if agents:
+        ag = (sync_copy_cfg * len(agents))(*agents)
+        arrs.append(ag)
+        sp.agents, sp.n_agents = ctypes.cast(ag, ctypes.c_void_p), len(agents)
     return sp, arrs
 
 
@@ -306,7 +313,7 @@ def sync_autotune(base: sync_plan_desc, space, *, a, b, c, ws, c_dtype: int = SY
     _check(lib().sync_autotune(ctypes.byref(base), ctypes.byref(sp), ctypes.byref(bufs), ctypes.byref(r)))
     return {"split": r.split, "tile_m": r.tile_m, "tile_n": r.tile_n, "tile_order": r.tile_order,
             "copy_cus": r.copy_cus, "best_ms": r.best_ms, "candidates_run": r.candidates_run,
-            "candidates_skipped": r.candidates_skipped}
+            "candidates_skipped": r.candidates_skipped, "backend": r.backend, "agent": r.agent}
 
 
 def sync_tune_forget() -> None:

@@ -38,7 +38,8 @@ const char* cache_path() {
   return (p && *p) ? p : nullptr;
 }
 
-// Cache file: one line per result, "key<TAB>split tile_m tile_n order copy_cus best_ms".
+// Cache file: one line per result,
+// "key<TAB>split tile_m tile_n order copy_cus best_ms backend agent".
 void load_file_locked() {
   const char* path = cache_path();
   if (!path || g_file_loaded == path) return;
@@ -50,7 +51,8 @@ void load_file_locked() {
     if (tab == std::string::npos) continue;
     sync_tune_result r{};
     std::istringstream in(line.substr(tab + 1));
-    if (in >> r.split >> r.tile_m >> r.tile_n >> r.tile_order >> r.copy_cus >> r.best_ms) g_cache[line.substr(0, tab)] = r;
+    if (in >> r.split >> r.tile_m >> r.tile_n >> r.tile_order >> r.copy_cus >> r.best_ms >> r.backend >> r.agent)
+      g_cache[line.substr(0, tab)] = r;
   }
 }
 
@@ -59,7 +61,7 @@ void append_file_locked(const std::string& key, const sync_tune_result& r) {
   if (!path) return;
   std::ofstream f(path, std::ios::app);
   f << key << '\t' << r.split << ' ' << r.tile_m << ' ' << r.tile_n << ' ' << r.tile_order << ' ' << r.copy_cus << ' '
-    << r.best_ms << '\n';
+    << r.best_ms << ' ' << r.backend << ' ' << r.agent << '\n';
 }
 
 std::string list_str(const int32_t* v, int32_t n) {
@@ -77,6 +79,15 @@ std::string cache_key(const sync_plan_desc& b, const sync_tune_space& sp, int32_
     << b.b_layout << " g" << b.group_m << " C" << c_dtype << " S[" << list_str(sp.splits, sp.n_splits) << "] T["
     << list_str(sp.tiles, 2 * sp.n_tiles) << "] O[" << list_str(sp.orders, sp.n_orders) << "] U["
     << list_str(sp.copy_cus, sp.n_copy_cus) << "]";
+  if (sp.n_agents > 0) {
+    k << " A[";
+    for (int32_t i = 0; i < sp.n_agents; ++i) {
+      const sync_copy_cfg& c = sp.agents[i];
+      k << (i ? ";" : "") << c.backend << ',' << c.copy_cus << ',' << c.copy_teams << ',' << c.copy_kslices << ','
+        << c.copy_streaming << ',' << c.copy_link_gbps;
+    }
+    k << "]";
+  }
   if (b.pattern == SYNC_PAT_EXPLICIT && b.explicit_order) k << " E[" << list_str(b.explicit_order, b.world) << "]";
   return k.str();
 }
@@ -86,9 +97,20 @@ int check_space(const sync_plan_desc* base, const sync_tune_space* sp) {
   if (base->op != SYNC_OP_AG_GEMM && base->op != SYNC_OP_GEMM_RS)
     return set_error(SYNC_EINVAL, "the autotuner covers the GEMM ops (AG, RS)");
   if (sp->reserved) return set_error(SYNC_EINVAL, "sync_tune_space.reserved must be zero");
-  if (!sp->splits || sp->n_splits < 1 || !sp->tiles || sp->n_tiles < 1 || !sp->orders || sp->n_orders < 1 ||
-      !sp->copy_cus || sp->n_copy_cus < 1)
+  if (!sp->splits || sp->n_splits < 1 || !sp->tiles || sp->n_tiles < 1 || !sp->orders || sp->n_orders < 1)
     return set_error(SYNC_EINVAL, "every list of the space needs at least one entry");
+  if (sp->n_agents < 0 || (sp->n_agents > 0 && !sp->agents))
+    return set_error(SYNC_EINVAL, "agents must hold n_agents copy configurations");
+  if (sp->n_agents == 0 && (!sp->copy_cus || sp->n_copy_cus < 1))
+    return set_error(SYNC_EINVAL, "the space needs copy-CU counts or a list of copy agents");
+  for (int32_t i = 0; i < sp->n_agents; ++i) {
+    const sync_copy_cfg& c = sp->agents[i];
+    if (c.flags || c.host_gates)
+      return set_error(SYNC_EINVAL, "tuned copy agents take no run-mode flags and no host gates");
+    if (c.backend != SYNC_COPY_SDMA && c.backend != SYNC_COPY_CU && c.backend != SYNC_COPY_COLOCATED &&
+        c.backend != SYNC_COPY_EPILOGUE)
+      return set_error(SYNC_EINVAL, "tuned copy agents are SDMA, CU, COLOCATED or EPILOGUE");
+  }
   if (sp->warmup < 0 || sp->iters < 0) return set_error(SYNC_EINVAL, "warmup and iters must be >= 0");
   return SYNC_OK;
 }
@@ -157,14 +179,19 @@ int sync_autotune(const sync_plan_desc* base, const sync_tune_space* space, cons
   for_each_candidate(*base, sp, [&](const sync_plan_desc& d) {
     if (hard) return;
     sync_plan_t p = nullptr;
+    const int32_t n_cfg = sp.n_agents > 0 ? sp.n_agents : sp.n_copy_cus;
     if (sync_plan(&d, &p) != SYNC_OK) {
-      skipped += sp.n_copy_cus;
+      skipped += n_cfg;
       return;
     }
-    for (int32_t u = 0; u < sp.n_copy_cus && !hard; ++u) {
+    for (int32_t u = 0; u < n_cfg && !hard; ++u) {
       sync_copy_cfg cfg{};
-      cfg.backend = SYNC_COPY_CU;
-      cfg.copy_cus = sp.copy_cus[u];
+      if (sp.n_agents > 0) {
+        cfg = sp.agents[u];
+      } else {
+        cfg.backend = SYNC_COPY_CU;
+        cfg.copy_cus = sp.copy_cus[u];
+      }
       cfg.timeout_ns = sp.timeout_ns ? sp.timeout_ns : 100000000ull;
       auto call = [&]() -> int {
         if (d.op == SYNC_OP_AG_GEMM)
@@ -217,6 +244,8 @@ int sync_autotune(const sync_plan_desc* base, const sync_tune_space* space, cons
         best.tile_n = d.tile_n;
         best.tile_order = d.tile_order;
         best.copy_cus = cfg.copy_cus;
+        best.backend = cfg.backend;
+        best.agent = sp.n_agents > 0 ? u : -1;
         best.best_ms = ms;
       }
     }

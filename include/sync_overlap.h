@@ -356,8 +356,13 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
  * `base` (its split, tile_m/tile_n, tile_order replaced), run `warmup` times
  * and then timed over `iters` calls with device events on `bufs->stream`.
  * Candidates the kernels do not support, or whose calls time out (each call
- * is bounded by timeout_ns, default 100 ms here), are skipped.  The copy-CU
- * list applies to the CU backend only; SDMA and HOST_GATED are not tuned.
+ * is bounded by timeout_ns, default 100 ms here), are skipped.  The copy side
+ * of a candidate is either each entry of `agents` (copy configurations: SDMA
+ * with its engine count in copy_teams, CU with copy_cus / copy_teams /
+ * copy_kslices / copy_link_gbps, COLOCATED, or EPILOGUE for GEMM-RS; no flags
+ * or host gates), or, with n_agents = 0, the CU backend at each count of the
+ * copy_cus list.  Candidates an agent does not support (e.g. EPILOGUE for
+ * AG) are skipped.
  * Results are cached per (device, op, shape, base fields, c_dtype, space) for
  * the life of the process, and in the text file named by the environment
  * variable SYNC_TUNE_CACHE when it is set (read on first use, appended after
@@ -373,6 +378,7 @@ typedef struct {
   uint64_t timeout_ns;     /* per-call device wait bound while tuning; 0 = 100 ms */
   int32_t force;           /* 1 = ignore cached results */
   int32_t reserved;        /* must be zero */
+  const sync_copy_cfg* agents; int32_t n_agents; /* copy agents to try; 0 = the copy_cus list */
 } sync_tune_space;
 
 typedef struct {
@@ -391,6 +397,8 @@ typedef struct {
   float best_ms;            /* mean call time of the winner */
   int32_t candidates_run;   /* 0 when served from the cache */
   int32_t candidates_skipped;
+  int32_t backend;          /* SYNC_COPY_* of the winner */
+  int32_t agent;            /* index of the winner in agents, -1 when from the copy_cus list */
 } sync_tune_result;
 
 /* Workspace bytes that fit every candidate of the space (0 on bad input). */

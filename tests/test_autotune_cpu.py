@@ -32,7 +32,8 @@ def test_empty_list_is_rejected(field):
     bufs = A.sync_tune_buffers()
     bufs.ws = 256
     rc = A.lib().sync_autotune(ctypes.byref(base()), ctypes.byref(sp), ctypes.byref(bufs), ctypes.byref(res))
-    assert rc == A.SYNC_EINVAL and "at least one entry" in A.sync_last_error()
+    msg = "copy-CU counts or a list of copy agents" if field == "copy_cus" else "at least one entry"
+    assert rc == A.SYNC_EINVAL and msg in A.sync_last_error()
 
 
 def test_attention_is_not_tuned():
@@ -50,3 +51,18 @@ def test_unaligned_workspace_is_rejected():
     bufs.ws = 257
     rc = A.lib().sync_autotune(ctypes.byref(base()), ctypes.byref(sp), ctypes.byref(bufs), ctypes.byref(res))
     assert rc == A.SYNC_EINVAL and "256-byte" in A.sync_last_error()
+
+
+def test_copy_agents_replace_the_copy_cu_list():
+    """With agents the copy_cus list may be empty; agents take no run flags,
+    no host gates, and only the SDMA, CU, COLOCATED or EPILOGUE backends."""
+    ok = (A.make_cfg(A.SYNC_COPY_SDMA, copy_teams=7), A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7, copy_kslices=4))
+    sp = A.make_tune_space(splits=(1,), tiles=((256, 256),), copy_cus=(), agents=ok)
+    assert A.sync_tune_workspace_size(base(), sp) > 0
+    for bad in (A.make_cfg(A.SYNC_COPY_HOST_GATED), A.make_cfg(A.SYNC_COPY_PRESET),
+                A.make_cfg(A.SYNC_COPY_CU, 16, flags=A.SYNC_RUN_TIMED)):
+        sp, keep = A.make_tune_space(splits=(1,), tiles=((256, 256),), copy_cus=(), agents=(bad,))
+        res, bufs = A.sync_tune_result(), A.sync_tune_buffers()
+        bufs.ws = 256
+        rc = A.lib().sync_autotune(ctypes.byref(base()), ctypes.byref(sp), ctypes.byref(bufs), ctypes.byref(res))
+        assert rc == A.SYNC_EINVAL and "agents" in A.sync_last_error()

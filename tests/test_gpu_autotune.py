@@ -97,3 +97,45 @@ def test_cache_file_survives_forgetting(tmp_path, monkeypatch):
         assert abs(r2["best_ms"] - r1["best_ms"]) <= 1e-3 * r1["best_ms"] + 1e-6
     finally:
         A.sync_tune_forget()
+
+
+@pytest.mark.parametrize("op", [A.SYNC_OP_AG_GEMM, A.SYNC_OP_GEMM_RS])
+def test_autotune_over_copy_agents(op):
+    """The copy backend as a tuning dimension: SDMA engines, dedicated copy CUs
+    with K-slices, co-located copy, and the RS epilogue backend.  Agents a
+    plan cannot use (EPILOGUE for AG; K-slices for RS) are skipped, the winner
+    is one of the agents, and running it alone is exact."""
+    m, n, k, world = 2048, 1024, 512, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    exact = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    base = A.make_desc(op, m, n, k, world, b_layout=A.SYNC_B_NK)
+    agents = (A.make_cfg(A.SYNC_COPY_SDMA, copy_teams=3), A.make_cfg(A.SYNC_COPY_CU, 16, copy_teams=3, copy_kslices=2),
+              A.make_cfg(A.SYNC_COPY_COLOCATED, copy_teams=4), A.make_cfg(A.SYNC_COPY_EPILOGUE))
+    tiles = ((256, 128), (128, 128))
+    space = A.make_tune_space(splits=(1, 2), tiles=tiles, copy_cus=(), agents=agents, warmup=1, iters=3, force=1)
+    ws = aligned_ws(A.sync_tune_workspace_size(base, space))
+    a_d, b_d = dev_bits(a), dev_bits(b)
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+    s = torch.cuda.current_stream()
+    print(f"[tune] agents, op={op}", flush=True)
+    if op == A.SYNC_OP_AG_GEMM:
+        a_local = torch.zeros_like(a_d)
+        a_local[0:m // world] = a_d[0:m // world]
+        r = A.sync_autotune(base, space, a=a_local, a_peer=a_d, b=b_d, c=c, ws=ws, stream=s)
+        usable = (0, 1, 2)  # SDMA, CU, COLOCATED; EPILOGUE sends RS output only
+    else:
+        staging = torch.empty_like(c)
+        r = A.sync_autotune(base, space, a=a_d, b=b_d, c=c, staging=staging, ws=ws, stream=s)
+        usable = (2, 3)     # COLOCATED, EPILOGUE; SDMA cannot copy out, K-slices are for AG
+    assert r["candidates_run"] == 4 * len(usable) and r["candidates_skipped"] == 4 * (4 - len(usable))
+    assert r["agent"] in usable and r["backend"] == agents[r["agent"]].backend and r["best_ms"] > 0
+    plan = A.sync_plan(A.make_desc(op, m, n, k, world, split=r["split"], tile_m=r["tile_m"], tile_n=r["tile_n"],
+                                   tile_order=r["tile_order"], b_layout=A.SYNC_B_NK))
+    A.sync_workspace_init(plan, ws, s)
+    c.fill_(float("nan"))
+    if op == A.SYNC_OP_AG_GEMM:
+        A.sync_ag_gemm(plan, agents[r["agent"]], a_d, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+    else:
+        A.sync_gemm_rs(plan, agents[r["agent"]], a_d, b_d, c, A.SYNC_DTYPE_F32, staging, ws, s, None)
+    assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
+    assert np.array_equal(c.cpu().numpy().astype(np.float64), exact)
