@@ -140,7 +140,7 @@ def main():
 
     backend, cus = BACKENDS[args.backend]
 
-    def timed_loop(cfg, steps, warmup):
+    def timed_loop(cfg, steps, warmup, plan=plan, ws=ws):
         for _ in range(warmup):
             A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c_out, c_dtype, ws, stream, None)
         torch.cuda.synchronize()
@@ -251,6 +251,26 @@ def main():
         line["autotune"] = tuned
     if sweep:
         line["copy_backend_sweep"] = sweep
+    if not args.no_other_rows:
+        # split factor (sub-chunks per peer shard: chunks of 8, 4 and 2 MiB)
+        split_sweep = {}
+        for sp in (1, 2, 4):
+            pl = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, split=sp, tile_m=tm, tile_n=tn,
+                                         tile_order=order, b_layout=b_layout))
+            w_raw = torch.zeros(A.sync_workspace_size(pl) // 4 + 64, dtype=torch.int32, device=dev)
+            w = w_raw[((-w_raw.data_ptr()) % 256) // 4:]
+            A.sync_workspace_init(pl, w, stream)
+            for sname, (sb, scus, steams, sks) in (("cu32", (A.SYNC_COPY_CU, 32, 7, 4)),
+                                                    ("sdma_7_engines", (A.SYNC_COPY_SDMA, 0, 7, 1))):
+                t_o, _ = timed_loop(A.make_cfg(sb, scus, copy_teams=steams, copy_kslices=sks), 10, 3, pl, w)
+                t_c, _ = timed_loop(A.make_cfg(sb, scus, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=steams,
+                                               copy_kslices=sks), 10, 3, pl, w)
+                split_sweep[f"split{sp}_{sname}"] = {"chunk_mib": round(8.0 / sp, 2),
+                                                     "t_overlap_us": round(t_o * 1e6, 1),
+                                                     "t_copy_only_us": round(t_c * 1e6, 1),
+                                                     "ratio": round(t_o / max(t_comp, t_c), 4)}
+            del w_raw
+        line["split_sweep"] = split_sweep
     if not args.no_other_rows:
         del a_peer, a_local, b, c_out
         line["other_rows"] = other_rows(pol=pol)
