@@ -1022,6 +1022,7 @@ int sync_read_timings(int32_t max, sync_timing* out, int32_t* count) {
 const char* sync_last_error(void) { return g_err.c_str(); }
 
 void sync_shutdown(void) {
+  sdma_release_all();
   std::lock_guard<std::mutex> lk(g_devices_mu);
   int cur = 0;
   const bool have = hipGetDevice(&cur) == hipSuccess;

@@ -231,6 +231,24 @@ int sdma_submit(int dev, const SdmaCall& call, const SdmaJob& job) {
   return SYNC_OK;
 }
 
+void sdma_release_all() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& kv : g_engines) {
+    Engines& e = *kv.second;
+    if (!e.ready) continue;
+    std::lock_guard<std::mutex> lk2(e.mu);
+    for (Record& r : e.rec) {
+      (void)quiesce(r);  // bounded; a record still busy after the bound is released anyway
+      if (r.gate.handle) (void)hsa_signal_destroy(r.gate);
+      if (r.done.handle) (void)hsa_signal_destroy(r.done);
+      for (hsa_signal_t s : r.chunk) (void)hsa_signal_destroy(s);
+      r = Record{};
+    }
+    (void)hsa_shut_down();  // the reference taken when the engines were first used
+  }
+  g_engines.clear();
+}
+
 int sdma_quiesce_all(int dev) {
   std::lock_guard<std::mutex> lk(g_mu);
   auto it = g_engines.find(dev);

@@ -35,6 +35,9 @@ int sdma_begin(int dev, int32_t copied_chunks, int32_t ntensors, SdmaCall* out);
 int sdma_submit(int dev, const SdmaCall& call, const SdmaJob& job);
 // Waits for every queued SDMA copy of device dev to complete.
 int sdma_quiesce_all(int dev);
+// Waits (bounded) for every queued SDMA copy, then destroys the signals and
+// drops the HSA reference of every device's engine state.
+void sdma_release_all();
 // Number of SDMA engines available for device-to-device copies on dev.
 int sdma_engine_count(int dev, int* out);
 

@@ -441,7 +441,9 @@ int sync_get_device_info(sync_device_info* out);
 /* Thread-local message for the last failing call on this thread. */
 const char* sync_last_error(void);
 
-/* Destroys the library's streams and events on every device. */
+/* Destroys the library's streams, events and SDMA signals on every device
+ * (first waiting, bounded, for queued SDMA copies).  Only when no call is in
+ * flight; the next call re-creates what it needs. */
 void sync_shutdown(void);
 
 #ifdef __cplusplus

@@ -628,3 +628,17 @@ def test_paced_copy_is_exact_and_no_faster_than_its_links(teams, kslices):
     assert np.array_equal(a_local, a)
     busiest = (3 if teams == 1 else 1) * (m // world) * k * 2
     assert ms * 1e-3 >= 0.95 * busiest / (gbps * 1e9), (ms, busiest)
+
+
+def test_shutdown_then_calls_again():
+    """sync_shutdown releases the library's streams, events and SDMA signals;
+    the next SDMA and CU calls re-create what they need and stay exact."""
+    m, n, k, world = 1024, 512, 512, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    for backend, cus in ((A.SYNC_COPY_SDMA, 0), (A.SYNC_COPY_CU, 16), (A.SYNC_COPY_SDMA, 0)):
+        out, a_local = run_ag(m, n, k, world, a, b, layout="nk", tile=(128, 128), backend=backend, copy_cus=cus,
+                              teams=2)
+        assert np.array_equal(out.astype(np.float64), ref) and np.array_equal(a_local, a)
+        torch.cuda.synchronize()
+        A.sync_shutdown()
