@@ -371,7 +371,15 @@ def other_rows(steps=5, warmup=2, pol=0):
         lambda: A.sync_gemm_rs_reduce(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), a, b, c, part, st, ws, s, None), steps,
         warmup)
     check(ws)
-    del part
+    # GEMM-AR share: that reduce-scatter step, then the all-gather of the reduced chunks (every
+    # workgroup joins it once its tiles are stored)
+    peer = torch.from_numpy(inputs.partials_f32(m, n, seed=inputs.SEED_P + inputs.ALT_SEED_OFFSET)).to(dev)
+    out_ar = torch.empty_like(c)
+    t["gemm_ar"] = _time_calls(
+        lambda: A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), a, b, c, part, peer, out_ar, st, ws, s, None),
+        steps, warmup)
+    check(ws)
+    del part, peer, out_ar
     flops = 2.0 * m * n * k
     hbm = (m * k + k * n) * 2 + m * n * 4 * 2  # A, B, then C and staging each written once
     out["gemm_rs_llama8b_down"] = {
@@ -382,6 +390,7 @@ def other_rows(steps=5, warmup=2, pol=0):
         "t_overlap_us": round(t["overlapped"] * 1e6, 1), "t_compute_only_us": round(t["compute_only"] * 1e6, 1),
         "t_overlap_colocated_us": round(t["overlapped_colocated"] * 1e6, 1),
         "t_overlap_with_reduce_step_us": round(t["overlapped_reduce_step"] * 1e6, 1),
+        "t_gemm_ar_share_us": round(t["gemm_ar"] * 1e6, 1),
         "t_overlap_32_copy_cus_us": round(t["overlapped_32_copy_cus"] * 1e6, 1),
         "ratio_to_compute_only": round(t["overlapped"] / t["compute_only"], 4),
         "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4),

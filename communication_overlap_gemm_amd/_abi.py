@@ -32,7 +32,7 @@ SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 
 EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
-    "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_gemm_rs", "sync_gemm_rs_reduce",
+    "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_gemm_rs", "sync_gemm_rs_reduce", "sync_gemm_ar",
     "sync_ring_attn_step",
     "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
     "sync_autotune", "sync_tune_workspace_size", "sync_tune_forget",
@@ -139,6 +139,7 @@ def lib():
             "sync_ag_gemm": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, i32, vp, vp, vp]),
             "sync_gemm_rs": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, i32, vp, vp, vp, vp]),
             "sync_gemm_rs_reduce": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp]),
+            "sync_gemm_ar": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "sync_ring_attn_step": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                           i32, vp, vp, vp]),
             "sync_get_device_info": (i32, [ctypes.POINTER(sync_device_info)]),
@@ -346,6 +347,13 @@ def sync_gemm_rs_reduce(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, parti
     _check(lib().sync_gemm_rs_reduce(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a), _ptr(b),
                                      _ptr(c), _ptr(partials), _ptr(staging), _ptr(ws), _stream(compute),
                                      _stream(copy)))
+
+
+def sync_gemm_ar(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, partials, reduced_peer, out, staging, ws,
+                 compute=None, copy=None) -> None:
+    _check(lib().sync_gemm_ar(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a), _ptr(b), _ptr(c),
+                              _ptr(partials), _ptr(reduced_peer), _ptr(out), _ptr(staging), _ptr(ws),
+                              _stream(compute), _stream(copy)))
 
 
 def sync_ring_attn_step(plan: Plan, cfg: Optional[sync_copy_cfg], q, k_peer, v_peer, k_local, v_local, o, m_state,

@@ -187,6 +187,35 @@ __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, ui
   }
 }
 
+// GEMM-AR share, all-gather half: workgroups walk the items in ring
+// all-gather order (dedicated copy workgroups from the start, compute
+// workgroups once their tiles are stored); for each, thread 0 waits until the
+// item's gate chunk is done (the rank's own chunk with the same sub-chunk
+// index: in a ring all-reduce the all-gather of a sub-chunk follows the end
+// of its reduce-scatter on every rank), then the workgroup copies share
+// `rank` of `count` of the item's rows.  Nothing is published per item: the
+// call's end covers them.
+template <int THREADS>
+__device__ void ar_gather(const GemmArgs& a, int32_t rank, int32_t count, uint32_t epoch) {
+  __shared__ int32_t s_ok;
+  for (int32_t i = 0; i < a.ar_count; ++i) {
+    const int64_t* it = a.ar_items + 5 * i;
+    if (threadIdx.x == 0) {
+      const bool ok = wait_flag(a.flags, static_cast<int32_t>(it[4]), epoch, a.hdr, a.timeout_ticks);
+      if (ok) acquire_agent();
+      s_ok = ok;
+    }
+    __syncthreads();
+    const int ok = s_ok;
+    __syncthreads();
+    if (!ok) return;  // the call failed: the error is recorded
+    const int64_t granules = it[3] * a.ar_row_bytes / 16;
+    const int64_t lo = granules * rank / count * 16, hi = granules * (rank + 1) / count * 16;
+    const char* const src = it[0] ? a.ar_src[1] : a.ar_src[0];
+    copy_range<THREADS, false>(src + it[1] * a.ar_row_bytes, a.ar_out + it[2] * a.ar_row_bytes, lo, hi);
+  }
+}
+
 // AG: lane 0 waits for every chunk tile t reads that was not in place before
 // the call, then one acquire.  Returns false (uniformly) when a wait gave up,
 // so the tile is skipped.
@@ -585,6 +614,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
   const uint32_t b_delta = static_cast<uint32_t>(A_BYTES + (wn * WN - wm * WM) * ROWB);
 
   if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
+    if constexpr (RS && CT == 0) {  // GEMM-AR is fp32 only
+      if (a.ar_count) {  // every workgroup of the launch takes a share of each item
+        ar_gather<THREADS>(a, blockIdx.x, gridDim.x, epoch);
+        end_call(a.hdr, epoch, a.cnt);
+        return;
+      }
+    }
     copy_role<THREADS>(a.copy, blockIdx.x, a.copy_blocks, epoch);
     end_call(a.hdr, epoch, a.cnt);
     return;
@@ -831,6 +867,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
   // co-located GEMM-RS: every workgroup joins the copy-out once its tiles are
   // stored, chunk by chunk in send order (the first chunks are done first)
   if (RS && a.colocated) copy_role<THREADS>(a.copy, gb, gn, epoch);
+  // GEMM-AR: every compute workgroup joins the all-gather once its tiles are stored
+  if constexpr (RS && CT == 0) {
+    if (a.ar_count) ar_gather<THREADS>(a, blockIdx.x, gridDim.x, epoch);
+  }
   end_call(a.hdr, epoch, a.cnt);
 }
 

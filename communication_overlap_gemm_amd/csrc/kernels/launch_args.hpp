@@ -96,6 +96,15 @@ struct GemmArgs {
   // partial sums arriving from the ring predecessor; a send slot receives
   // the tile plus these rows
   const void* partials;
+  // GEMM-AR share (ar_count > 0; RS instances): the copy workgroups gather the
+  // all-reduced rows into ar_out instead of copying out.  Item i is
+  // ar_items[5 i .. 5 i + 4] = {source (0: staging, 1: ar_peer), source row,
+  // destination row, rows, gate chunk}; it waits until the gate chunk is done.
+  const int64_t* ar_items;
+  int32_t ar_count;
+  const char* ar_src[2];
+  char* ar_out;
+  int64_t ar_row_bytes;
   CopyArgs copy;
 };
 

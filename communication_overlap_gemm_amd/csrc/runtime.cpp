@@ -213,6 +213,7 @@ struct DeviceTables {
   int32_t* resident = nullptr;
   int64_t* slot_row = nullptr;
   int32_t* push_rows = nullptr;  // GEMM-RS: staging row of each tile's first row (tiles in one chunk)
+  int64_t* ar_items = nullptr;   // GEMM-RS plans: the all-gather items of a GEMM-AR share
   void* block = nullptr;  // one allocation holding all of the above
 };
 
@@ -220,6 +221,7 @@ struct sync_plan_s {
   Plan plan;
   std::vector<int64_t> slot_row;   // staging row of each send position (C+1)
   std::vector<int32_t> push_rows;  // GEMM-RS, every tile in one chunk: staging row of each tile's first row (T)
+  std::vector<int64_t> ar_items;   // GEMM-RS: GEMM-AR all-gather items, 5 per item (see GemmArgs)
   std::mutex mu;
   std::map<int, DeviceTables> dev;
 };
@@ -245,7 +247,8 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   auto sz = [](size_t n, size_t e) { return align_up(static_cast<int64_t>(n * e), 256); };
   const int64_t total = sz(pl.tile_order.size(), 4) + sz(pl.dep_ptr.size(), 8) + sz(pl.dep_idx.size(), 4) +
                         sz(pl.tiles_in.size(), 4) + sz(pl.chunk_begin.size(), 8) + sz(pl.arrival.size(), 4) +
-                        sz(pl.resident.size(), 4) + sz(p->slot_row.size(), 8) + sz(p->push_rows.size(), 4) + 256;
+                        sz(pl.resident.size(), 4) + sz(p->slot_row.size(), 8) + sz(p->push_rows.size(), 4) +
+                        sz(p->ar_items.size(), 8) + 256;
   std::vector<char> host(static_cast<size_t>(total), 0);
   void* block = nullptr;
   HIP_TRY(hipMalloc(&block, static_cast<size_t>(total)));
@@ -262,6 +265,7 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   put(cur, host, pl.resident, &t.resident, base);
   put(cur, host, p->slot_row, &t.slot_row, base);
   if (!p->push_rows.empty()) put(cur, host, p->push_rows, &t.push_rows, base);
+  if (!p->ar_items.empty()) put(cur, host, p->ar_items, &t.ar_items, base);
   hipError_t e = hipMemcpy(block, host.data(), static_cast<size_t>(total), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(block);
@@ -679,6 +683,22 @@ int sync_plan(const sync_plan_desc* desc, sync_plan_t* out) {
     const int32_t c = pl.arrival[s];
     p->slot_row[s + 1] = p->slot_row[s] + (pl.chunk_begin[c + 1] - pl.chunk_begin[c]);
   }
+  if (pl.desc.op == SYNC_OP_GEMM_RS) {
+    // GEMM-AR all-gather order: ring step k brings shard (r - d k) mod W (k = 0:
+    // this rank's own, fully reduced in its staging slots), sub-chunks in
+    // order; sub-chunk q of every shard waits for this rank's own sub-chunk q
+    const auto& d = pl.desc;
+    const int32_t W = d.world, S = pl.num_chunks / W;
+    for (int32_t kstep = 0; kstep < W; ++kstep) {
+      const int32_t w = static_cast<int32_t>((((d.rank - d.ring_dir * kstep) % W) + W) % W);
+      for (int32_t q = 0; q < S; ++q) {
+        const int32_t c = w * S + q, own = d.rank * S + q;
+        const int64_t r0 = pl.chunk_begin[c], rows = pl.chunk_begin[c + 1] - r0;
+        const int64_t item[5] = {kstep == 0 ? 0 : 1, kstep == 0 ? p->slot_row[pl.chunk_pos[c]] : r0, r0, rows, own};
+        p->ar_items.insert(p->ar_items.end(), item, item + 5);
+      }
+    }
+  }
   bool one_chunk = pl.desc.op == SYNC_OP_GEMM_RS && pl.rows < (int64_t(1) << 31);
   for (int32_t t = 0; one_chunk && t < pl.num_tiles; ++t) one_chunk = pl.dep_ptr[t + 1] - pl.dep_ptr[t] == 1;
   if (one_chunk) {
@@ -840,10 +860,21 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
 // GEMM-RS share; `partials` (fp32 [m][n], or null) makes the send the
 // reduce-scatter step: slot data = tile + the incoming partial sums.
 static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
-                        int32_t c_dtype, const void* partials, void* staging, void* ws, void* compute, void* copy) {
+                        int32_t c_dtype, const void* partials, void* staging, void* ws, void* compute, void* copy,
+                        const void* ar_peer = nullptr, void* ar_out = nullptr) {
   CallCtx cx;
   int rc = prepare(plan, cfg, ws, SYNC_OP_GEMM_RS, cx);
   if (rc) return rc;
+  const bool ar = ar_out != nullptr;
+  if (ar) {
+    if (cx.cfg.flags & (SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TRACE))
+      return fail(SYNC_EUNSUPPORTED, "GEMM-AR calls take no COMPUTE_ONLY or TRACE mode");
+    if (cx.cfg.copy_cus < 0 || cx.cfg.copy_cus % cx.dev->num_xcds || cx.cfg.copy_cus > cx.dev->num_cus / 2)
+      return fail(SYNC_EINVAL, "GEMM-AR: copy_cus (CUs set aside for the all-gather) must be 0 or a multiple of "
+                               "the XCD count, at most half the CUs");
+    if (!ar_peer || !aligned16(ar_peer) || !aligned16(ar_out))
+      return fail(SYNC_EINVAL, "GEMM-AR: reduced_peer and out must be non-NULL and 16-byte aligned");
+  }
   if (partials) {
     if (cx.cfg.backend != SYNC_COPY_EPILOGUE || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY))
       return fail(SYNC_EUNSUPPORTED, "the reduce-scatter step runs in the EPILOGUE backend's stores");
@@ -891,7 +922,17 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
     g.sent = cx.ws.sent;
     g.partials = partials;
   }
-  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, nullptr, nullptr, nullptr, 0,
+  Roles rar = r;
+  if (ar) {  // the all-gather runs on copy_cus dedicated CUs of the same launch
+    rar.copy_blocks = cx.cfg.copy_cus * gemm_wg_per_cu(pl);
+    g.ar_items = cx.tab->ar_items;
+    g.ar_count = pl.num_chunks;
+    g.ar_src[0] = static_cast<const char*>(staging);
+    g.ar_src[1] = static_cast<const char*>(ar_peer);
+    g.ar_out = static_cast<char*>(ar_out);
+    g.ar_row_bytes = pl.desc.n * 4;
+  }
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, rar, nullptr, nullptr, nullptr, 0,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     g.copy_blocks = rr.copy_blocks;
                     g.colocated = rr.colocated;
@@ -910,6 +951,13 @@ int sync_gemm_rs_reduce(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
                         const float* partials, void* staging, void* ws, void* compute, void* copy) {
   if (!partials) return fail(SYNC_EINVAL, "partials is NULL");
   return gemm_rs_impl(plan, cfg, a, b, c, SYNC_DTYPE_F32, partials, staging, ws, compute, copy);
+}
+
+int sync_gemm_ar(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
+                 const float* partials, const float* reduced_peer, float* out, void* staging, void* ws, void* compute,
+                 void* copy) {
+  if (!partials || !out) return fail(SYNC_EINVAL, "partials and out must be non-NULL");
+  return gemm_rs_impl(plan, cfg, a, b, c, SYNC_DTYPE_F32, partials, staging, ws, compute, copy, reduced_peer, out);
 }
 
 int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q, const void* k_peer,

@@ -324,6 +324,27 @@ int sync_gemm_rs(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
 int sync_gemm_rs_reduce(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
                         const float* partials, void* staging, void* ws, void* compute, void* copy);
 
+/* GEMM-AR share [SYN-S "Experiments", paper sec. 6.1 and Fig. 11: GEMM-AR;
+ * a ring all-reduce is a reduce-scatter followed by an all-gather]: the
+ * reduce-scatter half exactly as sync_gemm_rs_reduce (EPILOGUE backend, fp32
+ * C; C, partials and staging as there), and in the same launch the
+ * all-gather half: cfg->copy_cus CUs set aside for it from the start (0, or a
+ * multiple of the XCD count up to half the CUs), and every compute
+ * workgroup joins it once its tiles are stored:
+ *   reduced_peer fp32 [m][n]: the fully reduced rows the peers send back in
+ *                the all-gather, at their natural rows (read-only; the rows of
+ *                this rank's own chunks are not read);
+ *   out          fp32 [m][n]: the all-reduced result: this rank's own chunks
+ *                from their staging slots (own tile + partials), every other
+ *                chunk from reduced_peer.
+ * The all-gather takes the chunks in ring order (this rank's own first, then
+ * shard (rank - ring_dir k) mod world at step k), and sub-chunk q of every
+ * shard waits in-kernel until this rank's own sub-chunk q is done, as the
+ * all-gather of a sub-chunk follows its reduce-scatter on every rank. */
+int sync_gemm_ar(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
+                 const float* partials, const float* reduced_peer, float* out, void* staging, void* ws,
+                 void* compute, void* copy);
+
 /* Ring-attention local step [SYN-S "Experiments", paper sec. 6.1 and Fig. 9:
  * RingAttention].  KV blocks (chunks of K and V token rows) are staged from
  * k_peer/v_peer into k_local/v_local in arrival order; each (query tile, head)

@@ -162,3 +162,18 @@ def rs_reduce_staging_expected(r_full, partials, plan: PlanTables):
     rs_staging_expected."""
     total = np.asarray(r_full, dtype=np.float64) + np.asarray(partials, dtype=np.float64)
     return rs_staging_expected(total, plan)
+
+
+def ar_share_expected(r_full, partials, reduced_peer, plan: PlanTables, world: int, rank: int):
+    """The GEMM-AR share's output (Syncopate summary page, "Experiments",
+    paper sec. 6.1, Fig. 11: GEMM-AR; an all-reduce is a reduce-scatter then
+    an all-gather): the rows of this rank's own shard hold R + P, where P is
+    the partial sum received in the reduce-scatter (the reduce-scatter ends
+    there); every other row holds what the all-gather brings, reduced_peer.
+    fp64."""
+    out = np.array(reduced_peer, dtype=np.float64, copy=True)
+    per = plan.num_chunks // world
+    for c in range(rank * per, (rank + 1) * per):
+        b, e = plan.chunk_begin[c], plan.chunk_begin[c + 1]
+        out[b:e] = np.asarray(r_full[b:e], dtype=np.float64) + np.asarray(partials[b:e], dtype=np.float64)
+    return out

@@ -372,3 +372,73 @@ def test_rs_reduce_step_validation():
     with pytest.raises(A.SyncError) as ei:
         A.sync_gemm_rs_reduce(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), ab, bb, t, None, t.clone(), ws, s, None)
     assert ei.value.code == A.SYNC_EINVAL
+
+
+# ---- GEMM-AR share: reduce-scatter step, then the all-gather in the same launch
+
+def _run_ar(m, n, k, W, a, b, p, peer, split=1, tile=(128, 128), rank=0, cus=16):
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, rank=rank, split=split, tile_m=tile[0],
+                                   tile_n=tile[1], b_layout=A.SYNC_B_NK))
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    st = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    out = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    pd, peer_d = torch.from_numpy(p).to("cuda:0"), torch.from_numpy(peer).to("cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    print(f"[ar] m={m} n={n} k={k} W={W} split={split} tile={tile} rank={rank} cus={cus}", flush=True)
+    A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE, copy_cus=cus), dev_bits(a), dev_bits(b), c, pd, peer_d, out,
+                   st, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    return c.cpu().numpy(), st.cpu().numpy(), out.cpu().numpy(), plan
+
+
+@pytest.mark.parametrize("m,n,k,W,split,tile,rank,cus", [(1024, 512, 256, 4, 1, (128, 128), 0, 16),
+                                                          (1024, 520, 320, 4, 2, (128, 128), 3, 0),
+                                                          (2048, 768, 320, 4, 1, (256, 256), 1, 8)])
+def test_ar_share_exact(m, n, k, W, split, tile, rank, cus):
+    """Small integers: C = R, send slots = R + P, and the all-reduced output
+    equals the oracle's (own shard R + P, every other row what the peers sent)."""
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    p = inputs.partials_f32(m, n, integer=True)
+    peer = inputs.partials_f32(m, n, seed=inputs.SEED_P + inputs.ALT_SEED_OFFSET, integer=True)
+    r = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    for rep in range(2):
+        cn, st, out, _ = _run_ar(m, n, k, W, a, b, p, peer, split, tile, rank, cus)
+        assert np.array_equal(cn.astype(np.float64), r)
+        ptab = oracle.plan_ref(oracle.PlanDesc(op=oracle.OP_GEMM_RS, m=m, n=n, k=k, world=W, rank=rank, split=split,
+                                               tile_m=tile[0], tile_n=tile[1]))
+        _, want_st = oracle.rs_reduce_staging_expected(r, p, ptab)
+        assert np.array_equal(st.astype(np.float64), want_st)
+        assert np.array_equal(out.astype(np.float64), oracle.ar_share_expected(r, p, peer, ptab, W, rank))
+
+
+def test_full_size_ar_share():
+    """The Llama-3-8B down-projection shape as a GEMM-AR share: other rows
+    bitwise what the peers sent, own rows the fp32 sum of C and P, C exact on
+    samples for small integers."""
+    m, n, k, W = 8192, 4096, 1792, 8
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    p = inputs.partials_f32(m, n, integer=True)
+    peer = inputs.partials_f32(m, n, seed=inputs.SEED_P + inputs.ALT_SEED_OFFSET)
+    cn, _, out, _ = _run_ar(m, n, k, W, a, b, p, peer, tile=(256, 256), cus=0)
+    own = m // W
+    assert np.array_equal(out[own:].view(np.uint32), peer[own:].view(np.uint32))
+    assert np.array_equal(out[:own].view(np.uint32), (cn[:own] + p[:own]).astype(np.float32).view(np.uint32))
+    rows = np.random.default_rng(17).integers(0, m, 3000)
+    cols = np.random.default_rng(18).integers(0, n, 3000)
+    exact = oracle.gemm_f64_sampled(a, b, m, n, k, rows, cols, b_layout="nk")
+    assert np.array_equal(cn[rows, cols].astype(np.float64), exact)
+
+
+def test_ar_share_rejects_bad_copy_cus():
+    m, n, k, W = 1024, 512, 256, 4
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, b_layout=A.SYNC_B_NK))
+    ws = workspace(plan)
+    t = torch.zeros((m, n), dtype=torch.float32, device="cuda:0")
+    ab = torch.zeros((m, k), dtype=torch.int16, device="cuda:0")
+    bb = torch.zeros((n, k), dtype=torch.int16, device="cuda:0")
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE, 12), ab, bb, t, t.clone(), t.clone(), t.clone(),
+                       t.clone(), ws, torch.cuda.current_stream(), None)
+    assert ei.value.code == A.SYNC_EINVAL and "copy_cus" in ei.value.message

@@ -51,3 +51,26 @@ def test_reduce_step_invariants(m, world, split, rank, d):
         row += e - b
     assert row == m and np.all(seen == 1)                  # every row sent exactly once
     assert slots[-1][0] in range(rank * split, (rank + 1) * split)  # the rank's own chunks go last
+
+
+def test_ar_share_hand_worked():
+    """W = 2: the own shard's rows end the reduce-scatter as R + P; the other
+    rows come from the all-gather."""
+    plan = _plan(4, 2)
+    r = np.array([[1.0], [2.0], [3.0], [4.0]])
+    p = np.array([[10.0], [20.0], [30.0], [40.0]])
+    peer = np.array([[100.0], [200.0], [300.0], [400.0]])
+    assert oracle.ar_share_expected(r, p, peer, plan, 2, 0).ravel().tolist() == [11.0, 22.0, 300.0, 400.0]
+    plan1 = _plan(4, 2, rank=1)
+    assert oracle.ar_share_expected(r, p, peer, plan1, 2, 1).ravel().tolist() == [100.0, 200.0, 33.0, 44.0]
+
+
+def test_ar_share_with_split_keeps_every_own_sub_chunk():
+    m, world, split, rank = 48, 4, 3, 2
+    plan = _plan(m, world, split, rank)
+    rng = np.random.default_rng(3)
+    r, p, peer = rng.standard_normal((m, 2)), rng.standard_normal((m, 2)), rng.standard_normal((m, 2))
+    out = oracle.ar_share_expected(r, p, peer, plan, world, rank)
+    own = np.zeros(m, dtype=bool)
+    own[rank * m // world:(rank + 1) * m // world] = True
+    assert np.array_equal(out[own], r[own] + p[own]) and np.array_equal(out[~own], peer[~own])
