@@ -332,7 +332,8 @@ def _ws(plan, torch, A):
 def other_rows(steps=5, warmup=2, pol=0):
     """The other rows of the hot path on their configurations (one line each in
     the output): GEMM-RS share (Llama-3-8B down-projection), AG-GEMM share
-    (70B-like FFN), ring-attention local step (Qwen-like GQA)."""
+    (70B-like FFN), A2A-GEMM receive side (MoE-like uneven token blocks),
+    ring-attention local step (Qwen-like GQA)."""
     import numpy as np
     import torch
 
@@ -421,6 +422,39 @@ def other_rows(steps=5, warmup=2, pol=0):
     out["ag_gemm_70b_like"] = {
         "workload": "AG-GEMM share: A 16384x8192 bf16 from 8 shards x 4 chunks (8 MiB), B 8192x3584 bf16, C fp32, "
                     "32 copy CUs in 7 teams", "chunks": int(tabs["num_chunks"]),
+        "tflops": round(flops / t["overlapped"] / 1e12, 1), "t_overlap_us": round(t["overlapped"] * 1e6, 1),
+        "t_compute_only_us": round(t["compute_only"] * 1e6, 1), "t_copy_only_us": round(t["copy_only"] * 1e6, 1),
+        "ratio": round(t["overlapped"] / max(t["compute_only"], t["copy_only"]), 4),
+        "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del ap, b, al, c
+
+    # A2A-GEMM receive side, MoE-like: 8 peers send uneven token blocks (seeded Dirichlet(2) routing skew,
+    # 8192 tokens in all) of d_model 4096 to this rank's expert, up-projection to 1792, C fp32
+    m, n, k = 8192, 1792, 4096
+    rng = np.random.default_rng(21)
+    rows = np.maximum(1, np.floor(rng.dirichlet(np.full(w, 2.0)) * m).astype(np.int64))
+    rows[-1] += m - rows.sum()
+    rows = [int(x) for x in rows]
+    a_bits, b_bits = inputs.gemm_operands(m, n, k, 64.0, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, w, b_layout=A.SYNC_B_NK, shard_rows=rows))
+    ap = torch.from_numpy(a_bits.view(np.int16)).to(dev)
+    b = torch.from_numpy(b_bits.view(np.int16)).to(dev)
+    al = torch.zeros_like(ap)
+    al[:rows[0]] = ap[:rows[0]]
+    c = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = _ws(plan, torch, A)
+    t = {}
+    for name, cfg in (("overlapped", A.make_cfg(A.SYNC_COPY_CU, 32, copy_teams=7, copy_kslices=4)),
+                      ("compute_only", A.make_cfg(A.SYNC_COPY_PRESET)),
+                      ("copy_only", A.make_cfg(A.SYNC_COPY_CU, 32, flags=A.SYNC_RUN_COPY_ONLY, copy_teams=7,
+                                               copy_kslices=4))):
+        t[name] = _time_calls(lambda: A.sync_ag_gemm(plan, cfg, ap, al, b, c, A.SYNC_DTYPE_F32, ws, s, None), steps,
+                              warmup)
+        check(ws)
+    flops = 2.0 * m * n * k
+    out["a2a_gemm_moe_like"] = {
+        "workload": "A2A-GEMM receive side: 8 peers send uneven token blocks " + str(rows) + " (8192 tokens, "
+                    "d 4096, bf16), GEMM with B 4096x1792, C fp32; 32 copy CUs in 7 teams, 4 K-slices",
         "tflops": round(flops / t["overlapped"] / 1e12, 1), "t_overlap_us": round(t["overlapped"] * 1e6, 1),
         "t_compute_only_us": round(t["compute_only"] * 1e6, 1), "t_copy_only_us": round(t["copy_only"] * 1e6, 1),
         "ratio": round(t["overlapped"] / max(t["compute_only"], t["copy_only"]), 4),

@@ -55,7 +55,7 @@ class sync_plan_desc(ctypes.Structure):
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_order", ctypes.c_int32),
         ("group_m", ctypes.c_int32), ("local_resident", ctypes.c_int32),
         ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("b_layout", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("shard_rows", ctypes.POINTER(ctypes.c_int64)), ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -204,7 +204,8 @@ class Plan:
 def make_desc(op: int, m: int, n: int, k: int, world: int, rank: int = 0, ring_dir: int = 1,
               pattern: int = SYNC_PAT_RING, explicit_order: Optional[Sequence[int]] = None, split: int = 1,
               tile_m: int = 256, tile_n: int = 256, tile_order: int = SYNC_ORDER_CHUNK_MAJOR, group_m: int = 0,
-              local_resident: int = 1, heads_q: int = 0, heads_kv: int = 0, b_layout: int = SYNC_B_KN):
+              local_resident: int = 1, heads_q: int = 0, heads_kv: int = 0, b_layout: int = SYNC_B_KN,
+              shard_rows: Optional[Sequence[int]] = None):
     d = sync_plan_desc()
     d.op, d.m, d.n, d.k, d.world, d.rank, d.ring_dir = op, m, n, k, world, rank, ring_dir
     d.pattern, d.split, d.tile_m, d.tile_n, d.tile_order = pattern, split, tile_m, tile_n, tile_order
@@ -213,6 +214,10 @@ def make_desc(op: int, m: int, n: int, k: int, world: int, rank: int = 0, ring_d
         arr = (ctypes.c_int32 * len(explicit_order))(*explicit_order)
         d.explicit_order = ctypes.cast(arr, _P32)
         d._keep = arr  # keep alive until sync_plan() has read it
+    if shard_rows is not None:
+        rows = (ctypes.c_int64 * len(shard_rows))(*shard_rows)
+        d.shard_rows = ctypes.cast(rows, _P64)
+        d._keep_rows = rows
     return d
 
 

@@ -32,22 +32,39 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
   if (d.tile_m < 1) { err = "tile_m must be positive"; return false; }
   if (d.tile_order < SYNC_ORDER_ROW_MAJOR || d.tile_order > SYNC_ORDER_SWIZZLED) { err = "bad tile_order"; return false; }
   if (d.group_m < 0) { err = "group_m must be >= 0"; return false; }
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
     if (d.reserved[i]) { err = "reserved fields must be zero"; return false; }
+  p.desc.shard_rows = nullptr;
   const int32_t W = d.world, s = d.split;
   const int64_t G = d.group_m > 0 ? d.group_m : 4;
 
+  std::vector<int64_t> rows_of(W), base(W + 1, 0);  // rows of each shard and their prefix sums
   if (attn) {
     if (d.heads_q < 1 || d.heads_kv < 1 || d.heads_q % d.heads_kv) { err = "heads_q must be a positive multiple of heads_kv"; return false; }
+    if (d.shard_rows) { err = "shard_rows is for the GEMM ops"; return false; }
     p.shard_rows = d.n;
     p.rows = static_cast<int64_t>(W) * d.n;
+    std::fill(rows_of.begin(), rows_of.end(), p.shard_rows);
   } else {
     if (d.tile_n < 1) { err = "tile_n must be positive"; return false; }
-    if (d.m % W) { err = "m must be divisible by world"; return false; }
     if (d.b_layout != SYNC_B_KN && d.b_layout != SYNC_B_NK) { err = "bad b_layout"; return false; }
-    p.shard_rows = d.m / W;
+    if (d.shard_rows) {
+      int64_t total = 0;
+      for (int32_t w = 0; w < W; ++w) {
+        if (d.shard_rows[w] < 1) { err = "shard_rows must be positive"; return false; }
+        rows_of[w] = d.shard_rows[w];
+        total += rows_of[w];
+      }
+      if (total != d.m) { err = "shard_rows must sum to m"; return false; }
+      p.shard_rows = *std::min_element(rows_of.begin(), rows_of.end());
+    } else {
+      if (d.m % W) { err = "m must be divisible by world"; return false; }
+      p.shard_rows = d.m / W;
+      std::fill(rows_of.begin(), rows_of.end(), p.shard_rows);
+    }
     p.rows = d.m;
   }
+  for (int32_t w = 0; w < W; ++w) base[w + 1] = base[w] + rows_of[w];
   if (s < 1 || s > p.shard_rows) { err = "split must be in [1, rows per shard]"; return false; }
 
   // shard consumed (AG, attention) or sent (RS) at each ring step
@@ -81,7 +98,7 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
   for (int32_t w = 0; w < W; ++w)
     for (int32_t q = 0; q < s; ++q) {
       const int32_t c = w * s + q;
-      p.chunk_begin[c] = static_cast<int64_t>(w) * p.shard_rows + (static_cast<int64_t>(q) * p.shard_rows) / s;
+      p.chunk_begin[c] = base[w] + (static_cast<int64_t>(q) * rows_of[w]) / s;
       p.chunk_pos[c] = step_of[w] * s + q;
       p.resident[c] = (!rs && d.local_resident && w == d.rank) ? 1 : 0;
     }

@@ -23,7 +23,7 @@ struct Plan {
   sync_plan_desc desc{};
   std::vector<int32_t> explicit_order;
   int64_t rows = 0;        // rows of the chunked tensor (m, or world*n for attention)
-  int64_t shard_rows = 0;  // R
+  int64_t shard_rows = 0;  // R (uneven shards: the smallest shard's rows)
   int32_t num_chunks = 0, num_tiles = 0, tiles_m = 0, tiles_n = 0;
   std::vector<int64_t> chunk_begin;  // C+1
   std::vector<int32_t> chunk_pos, arrival, resident, tiles_in;  // C

@@ -99,7 +99,12 @@ typedef struct {
   int32_t local_resident; /* 1: the rank's own shard is already in place (AG, attention) */
   int32_t heads_q, heads_kv; /* RING_ATTN only; heads_q % heads_kv == 0 */
   int32_t b_layout;       /* SYNC_B_KN or SYNC_B_NK (GEMM ops) */
-  int32_t reserved[4];    /* must be zero */
+  const int64_t* shard_rows; /* host, GEMM ops, read only during sync_plan(): NULL = m / world rows
+                                per shard; else world positive row counts summing to m, shard w
+                                holding rows [sum of the counts before w, + shard_rows[w]) (an
+                                all-to-all's receive side: peer w sends shard_rows[w] tokens) and
+                                split <= the smallest count */
+  int32_t reserved[2];    /* must be zero */
 } sync_plan_desc;
 
 typedef struct sync_plan_s* sync_plan_t;

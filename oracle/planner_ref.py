@@ -22,6 +22,9 @@ Reading, in the order the planner applies it:
   R = M / W rows per shard (attention: M := W * n tokens, R = n); s = split.
   chunk c = w*s + q  (shard w, sub-chunk q):
       begin(c) = w*R + floor(q*R/s),  end(c) = w*R + floor((q+1)*R/s)
+  Uneven shards (an all-to-all's receive side, GEMM ops only): shard w has
+  R_w rows (given, summing to M) and starts at B_w = R_0 + ... + R_(w-1);
+      begin(c) = B_w + floor(q*R_w/s),  with s <= min R_w
   ring step -> shard:
       AG, attention:  shard_at(k) = (r - d*k) mod W        (k = 0 is local)
       RS:             shard_at(k) = (r - d*(k+1)) mod W    (own chunk last)
@@ -71,6 +74,7 @@ class PlanDesc:
     local_resident: int = 1
     heads_q: int = 0
     heads_kv: int = 0
+    shard_rows: Optional[List[int]] = None
 
 
 @dataclass
@@ -113,17 +117,27 @@ def plan_ref(desc: PlanDesc) -> PlanTables:
     if d.op == OP_RING_ATTN:
         if d.heads_q < 1 or d.heads_kv < 1 or d.heads_q % d.heads_kv:
             raise PlanError("heads")
+        if d.shard_rows is not None:
+            raise PlanError("shard_rows")
         R = d.n                       # tokens per KV block
         M_rows = W * d.n              # rows of the chunked (KV) tensor
+        rows_of = [R] * W
     else:
         if d.tile_n < 1:
             raise PlanError("tile_n")
-        if d.m % W:
-            raise PlanError("m % world")
-        R = d.m // W
+        if d.shard_rows is not None:
+            rows_of = list(d.shard_rows)
+            if len(rows_of) != W or min(rows_of) < 1 or sum(rows_of) != d.m:
+                raise PlanError("shard_rows")
+        else:
+            if d.m % W:
+                raise PlanError("m % world")
+            rows_of = [d.m // W] * W
+        R = min(rows_of)
         M_rows = d.m
     if not (1 <= s <= R):
         raise PlanError("split")
+    shard_base = [sum(rows_of[:w]) for w in range(W)]
 
     # ring step -> shard
     if d.pattern == PAT_RING:
@@ -146,7 +160,7 @@ def plan_ref(desc: PlanDesc) -> PlanTables:
     chunk_begin = []
     for w in range(W):
         for q in range(s):
-            chunk_begin.append(w * R + (q * R) // s)
+            chunk_begin.append(shard_base[w] + (q * rows_of[w]) // s)
     chunk_begin.append(M_rows)
     chunk_pos = [kpos[c // s] * s + (c % s) for c in range(C)]
     arrival = [0] * C

@@ -642,3 +642,50 @@ def test_shutdown_then_calls_again():
         assert np.array_equal(out.astype(np.float64), ref) and np.array_equal(a_local, a)
         torch.cuda.synchronize()
         A.sync_shutdown()
+
+
+# ---- uneven shards: the receive side of an all-to-all (A2A-GEMM) ------------
+
+def _a2a_rows(total, world, seed):
+    """Seeded uneven token counts per peer (MoE-like routing skew), summing to total."""
+    rng = np.random.default_rng(seed)
+    w = rng.dirichlet(np.full(world, 2.0))
+    rows = np.maximum(1, np.floor(w * total).astype(np.int64))
+    rows[-1] += total - rows.sum()
+    assert rows.min() >= 1 and rows.sum() == total
+    return [int(x) for x in rows]
+
+
+@pytest.mark.parametrize("backend,cus,teams,kslices,split,tile", [
+    (A.SYNC_COPY_CU, 16, 3, 0, 1, (128, 128)), (A.SYNC_COPY_CU, 32, 7, 4, 1, (256, 256)),
+    (A.SYNC_COPY_SDMA, 0, 3, 0, 2, (256, 128)), (A.SYNC_COPY_COLOCATED, 0, 0, 0, 1, (256, 256))])
+def test_a2a_gemm_uneven_shards_exact(backend, cus, teams, kslices, split, tile):
+    """Peers send uneven token blocks (tiles straddle shard boundaries): exact
+    for small integers, every received row staged."""
+    world, n, k = 8, 768, 1024
+    rows = _a2a_rows(2040, world, seed=21)
+    m = sum(rows)
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, split=split, tile_m=tile[0], tile_n=tile[1],
+                                   b_layout=A.SYNC_B_NK, shard_rows=rows))
+    tabs = A.sync_plan_export(plan)
+    ptab = oracle.plan_ref(oracle.PlanDesc(op=oracle.OP_AG_GEMM, m=m, n=n, k=k, world=world, split=split,
+                                           tile_m=tile[0], tile_n=tile[1], shard_rows=rows))
+    assert list(tabs["chunk_begin"]) == list(ptab.chunk_begin)
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    a_local = bf16_poison((m, k))
+    a_local[:rows[0]] = a_peer[:rows[0]]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    print(f"[a2a] rows={rows} backend={backend} cus={cus} teams={teams} kslices={kslices} split={split} tile={tile}",
+          flush=True)
+    for rep in range(2):
+        c.fill_(float("nan"))
+        A.sync_ag_gemm(plan, A.make_cfg(backend, copy_cus=cus, copy_teams=teams, copy_kslices=kslices), a_peer, a_local,
+                       b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
+        rc, chunk = A.sync_workspace_status(ws, s)
+        assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+        assert np.array_equal(host_bits(a_local), a)
+        assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)

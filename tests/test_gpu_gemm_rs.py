@@ -442,3 +442,26 @@ def test_ar_share_rejects_bad_copy_cus():
         A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE, 12), ab, bb, t, t.clone(), t.clone(), t.clone(),
                        t.clone(), ws, torch.cuda.current_stream(), None)
     assert ei.value.code == A.SYNC_EINVAL and "copy_cus" in ei.value.message
+
+
+def test_rs_uneven_shards_copy_out():
+    """GEMM-RS over uneven row blocks (an all-to-all's send side): exact C and
+    every block bitwise in its send slot."""
+    m, n, k, W = 1000, 512, 256, 4
+    rows = [100, 400, 150, 350]
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True)
+    ref = oracle.gemm_f64(a, b, m, n, k)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, tile_m=128, tile_n=128, shard_rows=rows))
+    tabs = A.sync_plan_export(plan)
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    st = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    print(f"[rs] uneven shards {rows}", flush=True)
+    A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_CU, copy_cus=16, copy_teams=4), dev_bits(a), dev_bits(b), c,
+                   A.SYNC_DTYPE_F32, st, ws, s, None)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    cn = c.cpu().numpy()
+    assert np.array_equal(cn.astype(np.float64), ref)
+    check_staging(cn, st.cpu().numpy(), tabs)

@@ -175,3 +175,20 @@ def test_rejects_invalid(bad):
 def test_attention_requires_grouped_heads():
     with pytest.raises(P.PlanError):
         P.plan_ref(P.PlanDesc(op=P.OP_RING_ATTN, m=4, n=4, k=8, world=2, tile_m=2, heads_q=3, heads_kv=2))
+
+
+def test_uneven_shards_hand_worked():
+    """Three peers send 3, 1 and 4 rows (W = 3, rank 0, split 1, one-row tiles):
+    shards start at 0, 3 and 4; the ring brings shard 0 (local), then 2, then 1."""
+    t = P.plan_ref(P.PlanDesc(op=P.OP_AG_GEMM, m=8, n=2, k=2, world=3, rank=0, tile_m=1, tile_n=2,
+                              shard_rows=[3, 1, 4]))
+    assert list(t.chunk_begin) == [0, 3, 4, 8]
+    assert list(t.arrival) == [0, 2, 1]
+    assert list(t.resident) == [1, 0, 0]
+    # one-row tiles: rows 0-2 read chunk 0, row 3 chunk 1, rows 4-7 chunk 2
+    assert [t.dep_idx[t.dep_ptr[i]] for i in range(8)] == [0, 0, 0, 1, 2, 2, 2, 2]
+    t2 = P.plan_ref(P.PlanDesc(op=P.OP_AG_GEMM, m=8, n=2, k=2, world=3, split=2, tile_m=4, tile_n=2,
+                               shard_rows=[3, 2, 3]))
+    assert list(t2.chunk_begin) == [0, 1, 3, 4, 5, 6, 8]     # floor(q * R_w / 2) inside each shard
+    # a 4-row tile over rows 4-7 meets chunks 3 (row 4), 4 (row 5) and 5 (rows 6-7)
+    assert list(t2.dep_idx[t2.dep_ptr[1]:t2.dep_ptr[2]]) == [3, 4, 5]

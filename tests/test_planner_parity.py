@@ -75,3 +75,38 @@ def test_explicit_order_bit_exact():
     for perm in itertools.permutations(range(4)):
         _same(*_both(op=1, m=12, n=4, k=64, world=4, rank=1, pattern=1, explicit_order=list(perm), split=3,
                       tile_m=2, tile_n=2, tile_order=2, group_m=3))
+
+
+def _uneven():
+    rng = np.random.default_rng(11)
+    for op in (P.OP_AG_GEMM, P.OP_GEMM_RS):
+        for W in (1, 2, 3, 5):
+            for _ in range(6):
+                rows = [int(x) for x in rng.integers(1, 9, size=W)]
+                for s in range(1, min(3, min(rows)) + 1):
+                    for tm, order, d in itertools.product((1, 3), (0, 1, 2), (1, -1)):
+                        yield dict(op=op, m=sum(rows), n=5, k=3, world=W, rank=int(rng.integers(0, W)), ring_dir=d,
+                                   split=s, tile_m=tm, tile_n=2, tile_order=order, group_m=2, shard_rows=rows)
+
+
+def test_uneven_shards_bit_exact():
+    """Uneven shards (an all-to-all's receive side): both planners agree bit
+    for bit on random per-shard row counts."""
+    n = 0
+    for kw in _uneven():
+        _same(*_both(**kw))
+        n += 1
+    assert n > 300
+
+
+def test_uneven_shards_rejected_alike():
+    for bad in (dict(shard_rows=[3, 0, 5]), dict(shard_rows=[3, 3, 3]), dict(shard_rows=[2, 2, 4], split=3)):
+        kw = dict(op=P.OP_AG_GEMM, m=8, n=4, k=4, world=3, tile_m=2, tile_n=2)
+        kw.update(bad)
+        with pytest.raises(P.PlanError):
+            P.plan_ref(P.PlanDesc(**kw))
+        with pytest.raises(A.SyncError):
+            A.sync_plan(A.make_desc(**kw))
+    with pytest.raises(A.SyncError):
+        A.sync_plan(A.make_desc(P.OP_RING_ATTN, 4, 4, 128, 2, tile_m=4, tile_n=1, heads_q=2, heads_kv=1,
+                                shard_rows=[2, 2]))
