@@ -375,9 +375,9 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
 
 /* ---- autotuner ------------------------------------------------------------ */
 /* Picks the fastest overlapped configuration of a GEMM call (AG or RS) by
- * running it [spec: an autotuner over chunk size, split factor, tile
- * shape, tile order, copy backend and copy-CU count; SYN-S "Core method":
- * plans are tuned per workload and the pages leave the tuning cost out].
+ * running it over split factor (chunk size), tile shape, tile order and copy
+ * agent (backend, copy-CU count, ...) [SYN-S "Core method": plans are tuned
+ * per workload, and the pages leave the tuning cost out].
  * Every candidate in the cross product of the space's lists is planned from
  * `base` (its split, tile_m/tile_n, tile_order replaced), run `warmup` times
  * and then timed over `iters` calls with device events on `bufs->stream`.
