@@ -11,8 +11,8 @@
  *   [SYN-R] the pith.science review page of that paper: captions of Fig. 3-7.
  *   [ENT]   "Entwine" abstract (arXiv 2609.11562, arxivdaily page).
  *
- * The pages state the problem as "a local tile kernel plus a chunk schedule"
- * [SYN-A]: the caller describes the chunk plan with sync_plan(); the tile
+ * The pages pose the problem as a chunk schedule given together with a local
+ * tile kernel [SYN-A]: the caller describes the chunk plan with sync_plan(); the tile
  * kernel is this library's persistent bf16 MFMA GEMM (or the ring-attention
  * step), whose tile traversal the plan reorders [SYN-S, Fig. 6] and whose
  * tiles wait in-kernel on per-chunk ready flags (AG) or raise per-chunk done
