@@ -366,6 +366,11 @@ def other_rows(steps=5, warmup=2, pol=0):
         t[name] = _time_calls(lambda: A.sync_gemm_rs(plan, cfg, a, b, c, A.SYNC_DTYPE_F32, st, ws, s, None), steps,
                               warmup)
         check(ws)
+    # epilogue backend with C left unwritten: the send slots are the only output
+    t["send_only"] = _time_calls(
+        lambda: A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), a, b, None, A.SYNC_DTYPE_F32, st, ws, s, None),
+        steps, warmup)
+    check(ws)
     # the same with its reduce-scatter step: each send slot = own tile + incoming partial sums
     part = torch.from_numpy(inputs.partials_f32(m, n)).to(dev)
     t["overlapped_reduce_step"] = _time_calls(
@@ -390,6 +395,7 @@ def other_rows(steps=5, warmup=2, pol=0):
         "tflops": round(flops / t["overlapped"] / 1e12, 1),
         "t_overlap_us": round(t["overlapped"] * 1e6, 1), "t_compute_only_us": round(t["compute_only"] * 1e6, 1),
         "t_overlap_colocated_us": round(t["overlapped_colocated"] * 1e6, 1),
+        "t_overlap_send_slots_only_us": round(t["send_only"] * 1e6, 1),
         "t_overlap_with_reduce_step_us": round(t["overlapped_reduce_step"] * 1e6, 1),
         "t_gemm_ar_share_us": round(t["gemm_ar"] * 1e6, 1),
         "t_overlap_32_copy_cus_us": round(t["overlapped_32_copy_cus"] * 1e6, 1),

@@ -126,9 +126,12 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
           }
         }
       __syncthreads();
+      // RS with a send slot may leave C unwritten (C null): its stores then
+      // fall outside a zero-record resource and are dropped
+      const bool c_out = !PUSH || a.C != nullptr;
       const __amdgpu_buffer_rsrc_t cs =
-          make_rsrc(static_cast<char*>(a.C) + ((m0 + strip) * N + n0 + wn * WN) * ES,
-                    rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
+          make_rsrc(static_cast<char*>(c_out ? a.C : a.staging) + ((m0 + strip) * N + n0 + wn * WN) * ES,
+                    c_out && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);
       [[maybe_unused]] const __amdgpu_buffer_rsrc_t ss =
           make_rsrc(static_cast<char*>(push ? a.staging : a.C) + ((push_row0 + strip) * N + n0 + wn * WN) * ES,
                     push && rows_left > 0 ? static_cast<int64_t>(rows_left) * row_bytes : 0);

@@ -888,7 +888,9 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
     return fail(SYNC_EUNSUPPORTED, "GEMM-RS copy-out runs on CUs (CU or COLOCATED backend) or not at all (PRESET)");
   const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
   if (cx.cfg.flags & SYNC_RUN_COPY_ONLY) return fail(SYNC_EINVAL, "COPY_ONLY is not defined for GEMM-RS");
-  if (!a || !b || !c || (!compute_only && !staging)) return fail(SYNC_EINVAL, "NULL operand");
+  // the EPILOGUE backend's tiles go straight to their send slots, so C is optional there
+  const bool c_optional = cx.cfg.backend == SYNC_COPY_EPILOGUE && !compute_only;
+  if (!a || !b || (!c && !c_optional) || (!compute_only && !staging)) return fail(SYNC_EINVAL, "NULL operand");
   if (!aligned16(a) || !aligned16(b) || !aligned16(c) || (staging && !aligned16(staging)))
     return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
   DeviceState& d = *cx.dev;

@@ -185,7 +185,8 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *               slot in `staging`, and the tile that completes chunk c raises
  *               sent[c] with done[c] [SYN-S Fig. 7: communication by the
  *               compute SMs' own stores; Entwine abstract: output handed to
- *               communication as the tiles produce it].  Needs B stored
+ *               communication as the tiles produce it].  C may be NULL
+ *               here: the send slots are then the only output.  Needs B stored
  *               [n][k], every tile inside one chunk (chunk bounds on tile
  *               rows) and m x n x (element size) below 2 GiB, else
  *               EUNSUPPORTED. */

@@ -465,3 +465,35 @@ def test_rs_uneven_shards_copy_out():
     cn = c.cpu().numpy()
     assert np.array_equal(cn.astype(np.float64), ref)
     check_staging(cn, st.cpu().numpy(), tabs)
+
+
+@pytest.mark.parametrize("reduce", [False, True])
+def test_epilogue_send_without_c(reduce):
+    """Epilogue backend with C = NULL: the send slots (plain or with the
+    reduce-scatter step) are the only output and match the oracle exactly;
+    other backends still need C."""
+    m, n, k, W = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    p = inputs.partials_f32(m, n, integer=True)
+    r = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, tile_m=128, tile_n=128, b_layout=A.SYNC_B_NK))
+    ptab = oracle.plan_ref(oracle.PlanDesc(op=oracle.OP_GEMM_RS, m=m, n=n, k=k, world=W, tile_m=128, tile_n=128))
+    st = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    print(f"[rs] epilogue send without C, reduce={reduce}", flush=True)
+    if reduce:
+        A.sync_gemm_rs_reduce(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), dev_bits(a), dev_bits(b), None,
+                              torch.from_numpy(p).to("cuda:0"), st, ws, s, None)
+        _, want = oracle.rs_reduce_staging_expected(r, p, ptab)
+    else:
+        A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), dev_bits(a), dev_bits(b), None, A.SYNC_DTYPE_F32, st,
+                       ws, s, None)
+        _, want = oracle.rs_staging_expected(r, ptab)
+    rc, chunk = A.sync_workspace_status(ws, s)
+    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    assert np.array_equal(st.cpu().numpy().astype(np.float64), want)
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_CU, 16), dev_bits(a), dev_bits(b), None, A.SYNC_DTYPE_F32, st, ws,
+                       s, None)
+    assert ei.value.code == A.SYNC_EINVAL
