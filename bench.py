@@ -385,6 +385,10 @@ def other_rows(steps=5, warmup=2, pol=0):
         lambda: A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), a, b, c, part, peer, out_ar, st, ws, s, None),
         steps, warmup)
     check(ws)
+    t["gemm_ar_no_c"] = _time_calls(
+        lambda: A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE), a, b, None, part, peer, out_ar, st, ws, s, None),
+        steps, warmup)
+    check(ws)
     del part, peer, out_ar
     flops = 2.0 * m * n * k
     hbm = (m * k + k * n) * 2 + m * n * 4 * 2  # A, B, then C and staging each written once
@@ -398,6 +402,7 @@ def other_rows(steps=5, warmup=2, pol=0):
         "t_overlap_send_slots_only_us": round(t["send_only"] * 1e6, 1),
         "t_overlap_with_reduce_step_us": round(t["overlapped_reduce_step"] * 1e6, 1),
         "t_gemm_ar_share_us": round(t["gemm_ar"] * 1e6, 1),
+        "t_gemm_ar_share_without_c_us": round(t["gemm_ar_no_c"] * 1e6, 1),
         "t_overlap_32_copy_cus_us": round(t["overlapped_32_copy_cus"] * 1e6, 1),
         "ratio_to_compute_only": round(t["overlapped"] / t["compute_only"], 4),
         "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4),

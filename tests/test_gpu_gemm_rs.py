@@ -376,7 +376,7 @@ def test_rs_reduce_step_validation():
 
 # ---- GEMM-AR share: reduce-scatter step, then the all-gather in the same launch
 
-def _run_ar(m, n, k, W, a, b, p, peer, split=1, tile=(128, 128), rank=0, cus=16):
+def _run_ar(m, n, k, W, a, b, p, peer, split=1, tile=(128, 128), rank=0, cus=16, with_c=True):
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, m, n, k, W, rank=rank, split=split, tile_m=tile[0],
                                    tile_n=tile[1], b_layout=A.SYNC_B_NK))
     c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
@@ -386,8 +386,8 @@ def _run_ar(m, n, k, W, a, b, p, peer, split=1, tile=(128, 128), rank=0, cus=16)
     ws = workspace(plan)
     s = torch.cuda.current_stream()
     print(f"[ar] m={m} n={n} k={k} W={W} split={split} tile={tile} rank={rank} cus={cus}", flush=True)
-    A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE, copy_cus=cus), dev_bits(a), dev_bits(b), c, pd, peer_d, out,
-                   st, ws, s, None)
+    A.sync_gemm_ar(plan, A.make_cfg(A.SYNC_COPY_EPILOGUE, copy_cus=cus), dev_bits(a), dev_bits(b),
+                   c if with_c else None, pd, peer_d, out, st, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
     assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
     return c.cpu().numpy(), st.cpu().numpy(), out.cpu().numpy(), plan
@@ -497,3 +497,18 @@ def test_epilogue_send_without_c(reduce):
         A.sync_gemm_rs(plan, A.make_cfg(A.SYNC_COPY_CU, 16), dev_bits(a), dev_bits(b), None, A.SYNC_DTYPE_F32, st, ws,
                        s, None)
     assert ei.value.code == A.SYNC_EINVAL
+
+
+def test_ar_share_without_c():
+    """GEMM-AR share with C = NULL: the reduce step takes the tile from the
+    epilogue, so the all-reduced output is exact without C in memory."""
+    m, n, k, W = 1024, 512, 256, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    p = inputs.partials_f32(m, n, integer=True)
+    peer = inputs.partials_f32(m, n, seed=inputs.SEED_P + inputs.ALT_SEED_OFFSET, integer=True)
+    r = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    cn, _, out, _ = _run_ar(m, n, k, W, a, b, p, peer, rank=2, cus=0, with_c=False)
+    assert np.isnan(cn).all()  # never written
+    ptab = oracle.plan_ref(oracle.PlanDesc(op=oracle.OP_GEMM_RS, m=m, n=n, k=k, world=W, rank=2, tile_m=128,
+                                           tile_n=128))
+    assert np.array_equal(out.astype(np.float64), oracle.ar_share_expected(r, p, peer, ptab, W, 2))
