@@ -34,6 +34,9 @@ M, N, K, WORLD = 8192, 1792, 4096, 8
 DIVISOR = 64.0
 
 STORE_POLICIES = {"plain": 0, "stream": 1}
+# copy agents the autotuner tries: (label, bench backend, copy teams, K-slices)
+TUNE_AGENTS = (("sdma_7_engines", "sdma", 7, 1), ("cu16", "cu16", 7, 4), ("cu32", "cu32", 7, 4),
+               ("colocated", "colocated", 0, 1))
 BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64), "colocated": (4, 0)}
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
@@ -88,8 +91,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-rows", action="store_true", help="skip the RS, 70B-like AG and attention rows")
     p.add_argument("--tune", action="store_true",
-                   help="run the autotuner over split {1,2,4} x tile {256x256, 256x128} x copy CUs {16, 32} first and "
-                        "bench its choice")
+                   help="run the autotuner over split {1,2,4} x tile {256x256, 256x128} x copy agent (SDMA on 7 "
+                        "engines, 16 or 32 copy CUs with 4 K-slices, co-located) first and bench its choice")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return p.parse_args()
 
@@ -111,9 +114,8 @@ def main():
     tuned = None
     if args.tune:
         tuned = tune(args)
-        args.split, args.tile, args.backend = tuned["split"], f'{tuned["tile_m"]}x{tuned["tile_n"]}', \
-            f'cu{tuned["copy_cus"]}'
-        BACKENDS.setdefault(args.backend, (2, tuned["copy_cus"]))
+        args.split, args.tile = tuned["split"], f'{tuned["tile_m"]}x{tuned["tile_n"]}'
+        args.backend, args.teams, args.kslices = TUNE_AGENTS[tuned["agent"]][1:]
     tm, tn = (int(x) for x in args.tile.split("x"))
     order = {"row_major": A.SYNC_ORDER_ROW_MAJOR, "chunk_major": A.SYNC_ORDER_CHUNK_MAJOR,
              "swizzled": A.SYNC_ORDER_SWIZZLED}[args.order]
@@ -290,8 +292,10 @@ def tune(args):
     dev = torch.device("cuda:0")
     b_layout = A.SYNC_B_NK if args.layout == "nk" else A.SYNC_B_KN
     base = A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, b_layout=b_layout)
+    agents = [A.make_cfg(BACKENDS[be][0], BACKENDS[be][1], copy_teams=teams, copy_kslices=ks)
+              for _, be, teams, ks in TUNE_AGENTS]
     space = A.make_tune_space(splits=(1, 2, 4), tiles=((256, 256), (256, 128)), orders=(A.SYNC_ORDER_CHUNK_MAJOR,),
-                              copy_cus=(16, 32), warmup=2, iters=5)
+                              copy_cus=(), agents=agents, warmup=2, iters=5)
     a_bits, b_bits = inputs.gemm_operands(M, N, K, DIVISOR, b_layout=args.layout)
     a_peer = torch.from_numpy(a_bits.view(np.int16)).to(dev)
     b = torch.from_numpy(b_bits.view(np.int16)).to(dev)
