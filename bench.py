@@ -37,7 +37,8 @@ STORE_POLICIES = {"plain": 0, "stream": 1}
 # copy agents the autotuner tries: (label, bench backend, copy teams, K-slices)
 TUNE_AGENTS = (("sdma_7_engines", "sdma", 7, 1), ("cu16", "cu16", 7, 4), ("cu32", "cu32", 7, 4),
                ("colocated", "colocated", 0, 1))
-BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu32": (2, 32), "cu64": (2, 64), "colocated": (4, 0)}
+BACKENDS = {"sdma": (1, 0), "cu8": (2, 8), "cu16": (2, 16), "cu24": (2, 24), "cu32": (2, 32), "cu40": (2, 40),
+            "cu64": (2, 64), "colocated": (4, 0)}
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
 PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk",
