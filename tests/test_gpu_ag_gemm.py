@@ -23,7 +23,7 @@ LAYOUT = {"kn": A.SYNC_B_KN, "nk": A.SYNC_B_NK}
 
 def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
            backend=A.SYNC_COPY_SDMA, copy_cus=0, c_dtype=A.SYNC_DTYPE_F32, rank=0, poison=True, flags=0, teams=0,
-           kslices=0, streaming=0):
+           kslices=0, streaming=0, calls=1):
     print(f"[ag] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
           f"cus={copy_cus} dtype={c_dtype} layout={layout} teams={teams} kslices={kslices} streaming={streaming}",
           flush=True)
@@ -48,9 +48,16 @@ def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128)
     cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags, copy_teams=teams, copy_kslices=kslices,
                      copy_streaming=streaming)
     s = torch.cuda.current_stream()
-    A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, s, None)
-    rc, chunk = A.sync_workspace_status(ws, s)
-    assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+    for call in range(calls):  # calls > 1: the same workspace again, copied rows and C poisoned in between
+        if call:
+            c.copy_(torch.full_like(c, float("nan")) if c_dtype == A.SYNC_DTYPE_F32 else bf16_poison((m, n)))
+            for ch in range(tabs["num_chunks"]):
+                if not tabs["resident"][ch]:
+                    r0, r1 = tabs["chunk_begin"][ch], tabs["chunk_begin"][ch + 1]
+                    a_local[r0:r1] = bf16_poison((r1 - r0, k))
+        A.sync_ag_gemm(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, s, None)
+        rc, chunk = A.sync_workspace_status(ws, s)
+        assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk} (call {call})"
     torch.cuda.synchronize()
     out = c.cpu().numpy() if c_dtype == A.SYNC_DTYPE_F32 else inputs.bf16_bits_to_f32(host_bits(c))
     return out, host_bits(a_local)
@@ -433,6 +440,25 @@ def test_kslices_parity(backend, cus, teams, kslices, tile):
     check_f32(out, ref, world)
     assert np.array_equal(a_local, a)  # every slice of every chunk was staged
     base, _ = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=A.SYNC_COPY_PRESET)
+    assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
+
+
+@pytest.mark.parametrize("cus,teams,kslices,tile,rank", [
+    (8, 1, 2, (256, 256), 0), (32, 7, 4, (256, 256), 1), (16, 3, 4, (256, 128), 2), (8, 5, 3, (128, 128), 3)])
+def test_kslices_repeated_calls(cus, teams, kslices, tile, rank):
+    """Three K-sliced calls on one workspace, the copied rows and C poisoned
+    before each: the slice and chunk counters each call leaves cleared let the
+    next one stage every slice again and match the oracle, bitwise the
+    compute-only output."""
+    m, n, k, world, split = 2048, 768, 1152, 4, 2
+    a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    out, a_local = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=A.SYNC_COPY_CU,
+                          copy_cus=cus, teams=teams, kslices=kslices, rank=rank, calls=3)
+    check_f32(out, ref, world)
+    assert np.array_equal(a_local, a)
+    base, _ = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=A.SYNC_COPY_PRESET,
+                     rank=rank)
     assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
 
 
