@@ -39,6 +39,12 @@ def test_library_exports_symbol(name):
     (dict(b_layout=3), "b_layout"),
     (dict(pattern=1, explicit_order=[0, 1, 1, 2]), "permutation"),
     (dict(pattern=1), "explicit_order"),
+    (dict(m=0), "positive"),              # empty problems are rejected, not run as no-ops
+    (dict(n=0), "positive"),
+    (dict(k=0), "positive"),
+    (dict(n=-8), "positive"),
+    (dict(world=0), "world"),
+    (dict(tile_m=0), "tile_m"),
 ])
 def test_plan_rejects(bad, msg):
     kw = dict(op=1, m=8, n=8, k=64, world=4, tile_m=2, tile_n=2)

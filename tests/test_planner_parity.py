@@ -100,7 +100,8 @@ def test_uneven_shards_bit_exact():
 
 
 def test_uneven_shards_rejected_alike():
-    for bad in (dict(shard_rows=[3, 0, 5]), dict(shard_rows=[3, 3, 3]), dict(shard_rows=[2, 2, 4], split=3)):
+    for bad in (dict(shard_rows=[3, 0, 5]), dict(shard_rows=[3, 3, 3]), dict(shard_rows=[2, 2, 4], split=3),
+                dict(m=0, shard_rows=None), dict(k=0), dict(n=0), dict(world=0, shard_rows=None)):
         kw = dict(op=P.OP_AG_GEMM, m=8, n=4, k=4, world=3, tile_m=2, tile_n=2)
         kw.update(bad)
         with pytest.raises(P.PlanError):
