@@ -130,7 +130,7 @@ __device__ __forceinline__ void copy_block(const char* __restrict__ src, char* _
 // with one completion round (co-located copy: nothing computes until its own
 // share is copied, so per-chunk publication would only add latency).
 template <int THREADS, bool BATCH = false>
-__device__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32_t epoch) {
+__device__ __forceinline__ void copy_role(const CopyArgs& a, int32_t rank, int32_t count, uint32_t epoch) {
   __shared__ int32_t s_ok;
   const int64_t G = count, b = rank;
   auto skipped = [&](int32_t c) { return !a.copy_out && (a.resident[c] || a.skip_chunk == c || a.skip_chunk == -1); };

@@ -87,3 +87,19 @@ def test_occupancy_the_launcher_assumes(asm):
             assert vgpr <= 256, (name, vgpr)
             checked += 1
     assert checked >= 12, checked
+
+
+def test_no_scratch_in_the_nk_kernels(asm):
+    """Every gemm_dma instance (B stored [n][k]: the one kernel for that layout,
+    AG and RS, fp32 and bf16 C, all three tiles) keeps its state in registers:
+    no private segment.  An out-of-line copy role once left the bf16-C
+    256x256 instances with 588 bytes of scratch and 15 % slower."""
+    import re
+    checked = 0
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S):
+        if "gemm_dma" not in m.group(1):
+            continue
+        scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", m.group(2)).group(1))
+        assert scratch == 0, (m.group(1), scratch)
+        checked += 1
+    assert checked == 12, checked
