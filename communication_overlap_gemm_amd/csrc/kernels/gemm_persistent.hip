@@ -148,7 +148,10 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
               if constexpr (CT == 0) {
                 if (reduce) w = add_partials(v, pv[it]);
               }
-              __builtin_amdgcn_raw_buffer_store_b128(w, ss, off, 0, 0);
+              // the send slot is not read again by this launch's GEMM: a
+              // non-temporal store (cache policy NT) keeps it from displacing
+              // the A and B lines the other tiles still read from L2
+              __builtin_amdgcn_raw_buffer_store_b128(w, ss, off, 0, 2);
             }
           }
         }
