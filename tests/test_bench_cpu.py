@@ -1,0 +1,44 @@
+"""bench.py's host-side contract (no GPU): one GPU only, the profiled
+configuration is the default one, and the profile-derived HBM traffic is
+reported only for that configuration."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _args(*argv):
+    old = sys.argv
+    sys.argv = ["bench.py", *argv]
+    try:
+        return bench.parse()
+    finally:
+        sys.argv = old
+
+
+@pytest.mark.parametrize("n", ["2", "8"])
+def test_more_than_one_gpu_exits_with_a_message(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", n], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_profiled_configuration_is_the_default():
+    args = _args()
+    for k, v in bench.PROFILED.items():
+        assert getattr(args, k) == v, k
+
+
+def test_traffic_only_for_the_profiled_configuration():
+    t = bench.profiled_traffic(_args())
+    assert t is None or (isinstance(t, int) and t > 0)  # None once the kernel sources change
+    for argv in (["--tile", "256x128"], ["--split", "2"], ["--backend", "cu16"], ["--kslices", "2"],
+                 ["--c-dtype", "bf16"], ["--layout", "kn"], ["--teams", "1"], ["--copy-store", "stream"]):
+        assert bench.profiled_traffic(_args(*argv)) is None, argv
