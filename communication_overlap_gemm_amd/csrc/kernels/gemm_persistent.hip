@@ -218,7 +218,7 @@ __device__ void ar_gather(const GemmArgs& a, int32_t rank, int32_t count, uint32
     const int64_t granules = it[3] * a.ar_row_bytes / 16;
     const int64_t lo = granules * rank / count * 16, hi = granules * (rank + 1) / count * 16;
     const char* const src = it[0] ? a.ar_src[1] : a.ar_src[0];
-    copy_range<THREADS, false>(src + it[1] * a.ar_row_bytes, a.ar_out + it[2] * a.ar_row_bytes, lo, hi);
+    copy_range<THREADS, true>(src + it[1] * a.ar_row_bytes, a.ar_out + it[2] * a.ar_row_bytes, lo, hi);
   }
 }
 
