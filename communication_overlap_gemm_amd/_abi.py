@@ -178,6 +178,32 @@ def _ptr(x) -> Optional[int]:
     raise TypeError(f"cannot take a device pointer from {type(x).__name__}")
 
 
+def _arg(x, name: str, elem: int, count: int) -> Optional[int]:
+    """Device address of x.  A tensor is also checked against what the call
+    will touch: on a GPU, contiguous, `elem`-byte elements and at least `count`
+    of them (these are size checks only; nothing is computed)."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr") and hasattr(x, "is_contiguous"):
+        if not getattr(x, "is_cuda", False):
+            raise SyncError(SYNC_EINVAL, f"{name} must be a device tensor")
+        if not x.is_contiguous():
+            raise SyncError(SYNC_EINVAL, f"{name} must be contiguous")
+        if x.element_size() != elem:
+            raise SyncError(SYNC_EINVAL, f"{name} must have {elem}-byte elements, not {x.element_size()}")
+        if x.numel() < count:
+            raise SyncError(SYNC_EINVAL, f"{name} holds {x.numel()} elements; the plan needs {count}")
+        return int(x.data_ptr())
+    return _ptr(x)
+
+
+def _ws_arg(plan, ws) -> Optional[int]:
+    if ws is None or isinstance(ws, int) or not hasattr(ws, "element_size"):
+        return _ptr(ws)
+    need = int(lib().sync_workspace_size(plan.handle))
+    return _arg(ws, "ws", ws.element_size(), (need + ws.element_size() - 1) // ws.element_size())
+
+
 def _stream(s) -> Optional[int]:
     if s is None:
         return None
@@ -335,37 +361,59 @@ def sync_workspace_status(ws, stream=None):
     return rc, ch.value
 
 
+def _c_elem(c_dtype: int) -> int:
+    return 4 if c_dtype == SYNC_DTYPE_F32 else 2
+
+
 def sync_ag_gemm(plan: Plan, cfg: Optional[sync_copy_cfg], a_peer, a_local, b, c, c_dtype: int, ws,
                  compute=None, copy=None) -> None:
-    _check(lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a_peer),
-                              _ptr(a_local), _ptr(b), _ptr(c), c_dtype, _ptr(ws), _stream(compute), _stream(copy)))
+    m, n, k = plan.desc.m, plan.desc.n, plan.desc.k
+    _check(lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg) if cfg is not None else None,
+                              _arg(a_peer, "a_peer", 2, m * k), _arg(a_local, "a_local", 2, m * k),
+                              _arg(b, "b", 2, k * n), _arg(c, "c", _c_elem(c_dtype), m * n), c_dtype,
+                              _ws_arg(plan, ws), _stream(compute), _stream(copy)))
 
 
 def sync_gemm_rs(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, c_dtype: int, staging, ws, compute=None,
                  copy=None) -> None:
-    _check(lib().sync_gemm_rs(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a), _ptr(b),
-                              _ptr(c), c_dtype, _ptr(staging), _ptr(ws), _stream(compute), _stream(copy)))
+    m, n, k = plan.desc.m, plan.desc.n, plan.desc.k
+    e = _c_elem(c_dtype)
+    _check(lib().sync_gemm_rs(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _arg(a, "a", 2, m * k),
+                              _arg(b, "b", 2, k * n), _arg(c, "c", e, m * n), c_dtype,
+                              _arg(staging, "staging", e, m * n), _ws_arg(plan, ws), _stream(compute),
+                              _stream(copy)))
 
 
 def sync_gemm_rs_reduce(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, partials, staging, ws, compute=None,
                         copy=None) -> None:
-    _check(lib().sync_gemm_rs_reduce(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a), _ptr(b),
-                                     _ptr(c), _ptr(partials), _ptr(staging), _ptr(ws), _stream(compute),
-                                     _stream(copy)))
+    m, n, k = plan.desc.m, plan.desc.n, plan.desc.k
+    _check(lib().sync_gemm_rs_reduce(plan.handle, ctypes.byref(cfg) if cfg is not None else None,
+                                     _arg(a, "a", 2, m * k), _arg(b, "b", 2, k * n), _arg(c, "c", 4, m * n),
+                                     _arg(partials, "partials", 4, m * n), _arg(staging, "staging", 4, m * n),
+                                     _ws_arg(plan, ws), _stream(compute), _stream(copy)))
 
 
 def sync_gemm_ar(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, partials, reduced_peer, out, staging, ws,
                  compute=None, copy=None) -> None:
-    _check(lib().sync_gemm_ar(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(a), _ptr(b), _ptr(c),
-                              _ptr(partials), _ptr(reduced_peer), _ptr(out), _ptr(staging), _ptr(ws),
-                              _stream(compute), _stream(copy)))
+    m, n, k = plan.desc.m, plan.desc.n, plan.desc.k
+    _check(lib().sync_gemm_ar(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _arg(a, "a", 2, m * k),
+                              _arg(b, "b", 2, k * n), _arg(c, "c", 4, m * n), _arg(partials, "partials", 4, m * n),
+                              _arg(reduced_peer, "reduced_peer", 4, m * n), _arg(out, "out", 4, m * n),
+                              _arg(staging, "staging", 4, m * n), _ws_arg(plan, ws), _stream(compute),
+                              _stream(copy)))
 
 
 def sync_ring_attn_step(plan: Plan, cfg: Optional[sync_copy_cfg], q, k_peer, v_peer, k_local, v_local, o, m_state,
                         l_state, lse, scale: float, flags: int, ws, compute=None, copy=None) -> None:
-    _check(lib().sync_ring_attn_step(plan.handle, ctypes.byref(cfg) if cfg is not None else None, _ptr(q),
-                                     _ptr(k_peer), _ptr(v_peer), _ptr(k_local), _ptr(v_local), _ptr(o),
-                                     _ptr(m_state), _ptr(l_state), _ptr(lse), float(scale), flags, _ptr(ws),
+    d = plan.desc
+    sq, d_head, hq, hkv = d.m, d.k, d.heads_q, d.heads_kv
+    kv = d.world * d.n * hkv * d_head
+    _check(lib().sync_ring_attn_step(plan.handle, ctypes.byref(cfg) if cfg is not None else None,
+                                     _arg(q, "q", 2, sq * hq * d_head), _arg(k_peer, "k_peer", 2, kv),
+                                     _arg(v_peer, "v_peer", 2, kv), _arg(k_local, "k_local", 2, kv),
+                                     _arg(v_local, "v_local", 2, kv), _arg(o, "o", 4, sq * hq * d_head),
+                                     _arg(m_state, "m_state", 4, hq * sq), _arg(l_state, "l_state", 4, hq * sq),
+                                     _arg(lse, "lse", 4, hq * sq), float(scale), flags, _ws_arg(plan, ws),
                                      _stream(compute), _stream(copy)))
 
 

@@ -257,8 +257,15 @@ __device__ __forceinline__ bool wait_tile_chunks(const GemmArgs& a, int32_t t, u
   return !skip;
 }
 
+// Workgroups per CU a tile shape is launched with: 128x128 runs two per CU
+// (its LDS ring and registers fit twice), larger tiles one.  The kernels
+// declare it in their launch bounds, so the compiler holds each instance to
+// that register budget; the runtime checks the resulting occupancy before a
+// launch whose workgroups must all be resident at once.
+template <int TM, int TN> constexpr int kWgPerCu = (TM == 128 && TN == 128) ? 2 : 1;
+
 template <int TM, int TN, int BL, int CT, bool RS>
-__global__ __launch_bounds__(kThreads, 1) void gemm_persistent(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, (kWgPerCu<TM, TN>)) void gemm_persistent(GemmArgs a) {
   constexpr int WM = TM / 2, WN = TN / 2;
   constexpr int MI = WM / 32, NI = WN / 32;
   constexpr int A_LD = TM / 32;                             // 16-byte A loads per thread per stage
@@ -542,7 +549,7 @@ __device__ __forceinline__ int rswz(int row, int slot) {
 constexpr int kFeedReg = -1;
 
 template <int TM, int TN, int CT, bool RS, int TK, int NS, int WGM, int WGN, int FEED>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma(GemmArgs a) {
+__global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(GemmArgs a) {
   constexpr int NW = WGM * WGN, THREADS = 64 * NW;  // waves, as a WGM x WGN grid over the tile
   constexpr int WM = TM / WGM, WN = TN / WGN;
   constexpr int MI = WM / 32, NI = WN / 32;
@@ -895,19 +902,23 @@ template <int TM, int TN> struct DmaShape { static constexpr int TK = 64, NS = 2
 template <> struct DmaShape<256, 128> { static constexpr int TK = 64, NS = 3, WGM = 2, WGN = 2, FEED = 0; };
 template <> struct DmaShape<256, 256> { static constexpr int TK = 64, NS = 2, WGM = 2, WGN = 4, FEED = 2; };
 
+// With max_per_cu non-null nothing is launched: *max_per_cu receives how many
+// workgroups of the chosen instance can be resident on one CU.
 hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid,
-                       hipStream_t stream) {
+                       hipStream_t stream, int* max_per_cu) {
+  auto go = [&](auto kernel, int threads) -> hipError_t {
+    if (max_per_cu)
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(max_per_cu, reinterpret_cast<const void*>(kernel), threads,
+                                                          0);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+  };
 #define SYNC_GEMM_DMA_CASE(TM_, TN_, CT_)                                                                \
   if (tm == TM_ && tn == TN_ && b_layout == 1 && c_dtype == CT_) {                                       \
     using S_ = DmaShape<TM_, TN_>;                                                                       \
-    const dim3 block(64 * S_::WGM * S_::WGN);                                                           \
-    if (rs)                                                                                              \
-      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, true, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>), dim3(grid), block, 0, \
-                         stream, a);                                                                     \
-    else                                                                                                 \
-      hipLaunchKernelGGL((gemm_dma<TM_, TN_, CT_, false, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>), dim3(grid), block, 0, \
-                         stream, a);                                                                     \
-    return hipGetLastError();                                                                            \
+    constexpr int threads_ = 64 * S_::WGM * S_::WGN;                                                     \
+    return rs ? go(gemm_dma<TM_, TN_, CT_, true, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>, threads_)  \
+              : go(gemm_dma<TM_, TN_, CT_, false, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>, threads_); \
   }
   SYNC_GEMM_DMA_CASE(256, 256, 0)
   SYNC_GEMM_DMA_CASE(256, 256, 1)
@@ -918,13 +929,8 @@ hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dt
 #undef SYNC_GEMM_DMA_CASE
 #define SYNC_GEMM_CASE(TM_, TN_, BL_, CT_)                                                               \
   if (tm == TM_ && tn == TN_ && b_layout == BL_ && c_dtype == CT_) {                                     \
-    if (rs)                                                                                              \
-      hipLaunchKernelGGL((gemm_persistent<TM_, TN_, BL_, CT_, true>), dim3(grid), dim3(kThreads), 0,     \
-                         stream, a);                                                                     \
-    else                                                                                                 \
-      hipLaunchKernelGGL((gemm_persistent<TM_, TN_, BL_, CT_, false>), dim3(grid), dim3(kThreads), 0,    \
-                         stream, a);                                                                     \
-    return hipGetLastError();                                                                            \
+    return rs ? go(gemm_persistent<TM_, TN_, BL_, CT_, true>, kThreads)                                  \
+              : go(gemm_persistent<TM_, TN_, BL_, CT_, false>, kThreads);                                \
   }
 #define SYNC_GEMM_TILES(BL_, CT_) \
   SYNC_GEMM_CASE(256, 256, BL_, CT_) SYNC_GEMM_CASE(256, 128, BL_, CT_) SYNC_GEMM_CASE(128, 128, BL_, CT_)
@@ -935,6 +941,11 @@ hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dt
 #undef SYNC_GEMM_TILES
 #undef SYNC_GEMM_CASE
   return hipErrorInvalidValue;
+}
+
+int gemm_wg_per_cu(int tm, int tn) {
+  if (tm == 128 && tn == 128) return kWgPerCu<128, 128>;
+  return 1;
 }
 
 bool gemm_variant_exists(int tm, int tn) {

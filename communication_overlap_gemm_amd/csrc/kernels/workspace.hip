@@ -1,6 +1,5 @@
-// Small kernels around the workspace: initialisation, the gate and join of
-// the SDMA backend, and the flag raised after each stream-ordered copy of the
-// host-gated test backend.
+// Small kernels around the workspace: initialisation, and the gate and join
+// of the SDMA backend.
 #include "device_common.hpp"
 
 namespace syncov {
@@ -11,13 +10,6 @@ __global__ __launch_bounds__(256) void fill_u32(uint32_t* p, int64_t n, uint32_t
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[i] = v;
-}
-
-// Raises flags[c] to the running call's epoch (one lane), after the stream's
-// preceding SDMA copy of chunk c has completed.  The call's compute kernel
-// cannot finish (and advance the stored epoch) before every such flag is up.
-__global__ __launch_bounds__(64) void publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c) {
-  if (threadIdx.x == 0) st_release_agent(flags + c, call_epoch(hdr));
 }
 
 // SDMA backend, first kernel of a call on the caller's stream: fixes the
@@ -54,11 +46,6 @@ hipError_t launch_sdma_gate(uint32_t* hdr, int64_t* gate, hipStream_t s) {
 hipError_t launch_sdma_join(uint32_t* hdr, const uint32_t* flags, const int32_t* arrival, const int32_t* resident,
                             int32_t num_chunks, uint64_t timeout_ticks, hipStream_t s) {
   hipLaunchKernelGGL(sdma_join, dim3(1), dim3(64), 0, s, hdr, flags, arrival, resident, num_chunks, timeout_ticks);
-  return hipGetLastError();
-}
-
-hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s) {
-  hipLaunchKernelGGL(publish_flag, dim3(1), dim3(64), 0, s, hdr, flags, c);
   return hipGetLastError();
 }
 

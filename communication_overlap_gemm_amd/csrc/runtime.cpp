@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <tuple>
 #include <memory>
 #include <mutex>
 #include <string>
@@ -29,10 +30,11 @@
 
 namespace syncov {
 
-hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dtype, bool rs, int grid, hipStream_t s,
+                       int* max_per_cu = nullptr);
+int gemm_wg_per_cu(int tm, int tn);
 bool gemm_variant_exists(int tm, int tn);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
-hipError_t launch_publish_flag(uint32_t* hdr, uint32_t* flags, int32_t c, hipStream_t s);
 hipError_t launch_sdma_gate(uint32_t* hdr, int64_t* gate, hipStream_t s);
 hipError_t launch_sdma_join(uint32_t* hdr, const uint32_t* flags, const int32_t* arrival, const int32_t* resident,
                             int32_t num_chunks, uint64_t timeout_ticks, hipStream_t s);
@@ -77,24 +79,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // ---- per-device state ----------------------------------------------------
-struct MaskedPair {
-  hipStream_t copy = nullptr, gemm = nullptr;
-  int gemm_cus = 0;
-};
-
-// The library owns exactly two streams per device, a copy stream masked to
-// the copy CUs and a GEMM stream masked to the rest, so that together with
-// the caller's stream it stays within the runtime's default of four hardware
-// queues: a copy stream that shared a hardware queue with the spinning GEMM
-// could never run.  The pair is rebuilt when the copy-CU count changes.
+// Per-device facts and the ring of timing events.  Every call runs on the
+// caller's stream: the library creates no streams.
 struct DeviceState {
   bool ready = false;
   int device = 0;
   int num_cus = 0, num_xcds = 1, clock_khz = 0;
   int64_t wall_khz = 100000;
   std::string arch;
-  MaskedPair pair;
-  int pair_copy_cus = -1;
   // SYNC_RUN_TIMED: ring of event quadruples (kernel start/end, copy start/end)
   struct Timed {
     hipEvent_t k0 = nullptr, k1 = nullptr, c0 = nullptr, c1 = nullptr;
@@ -102,7 +94,6 @@ struct DeviceState {
   };
   std::vector<Timed> ring;
   int64_t ring_head = 0, ring_count = 0;
-  hipEvent_t ev_fork = nullptr, ev_copy = nullptr, ev_gemm = nullptr;
   std::mutex mu;  // serialises launch sequences (the events and streams are shared)
 };
 
@@ -127,55 +118,9 @@ int current_device_state(DeviceState** out) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0) d.num_xcds = v;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) == hipSuccess && v > 0) d.wall_khz = v;
-    HIP_TRY(hipEventCreateWithFlags(&d.ev_fork, hipEventDisableTiming));
-    HIP_TRY(hipEventCreateWithFlags(&d.ev_copy, hipEventDisableTiming));
-    HIP_TRY(hipEventCreateWithFlags(&d.ev_gemm, hipEventDisableTiming));
     d.ready = true;
   }
   *out = &d;
-  return SYNC_OK;
-}
-
-// CU mask bits for the copy agent: `copy_cus` CUs spread evenly over the XCDs.
-// Logical CU i of the mask lives on XCD i % num_xcds (round-robin numbering),
-// so the first copy_cus bits give copy_cus / num_xcds CUs on every XCD.
-// SYNC_CU_MASK_LAYOUT=blocked switches to XCD-major numbering.
-std::vector<uint32_t> copy_mask_bits(int num_cus, int num_xcds, int copy_cus, bool complement) {
-  std::vector<char> is_copy(num_cus, 0);
-  const char* env = std::getenv("SYNC_CU_MASK_LAYOUT");
-  const bool blocked = env && std::strcmp(env, "blocked") == 0;
-  if (!blocked) {
-    for (int i = 0; i < copy_cus && i < num_cus; ++i) is_copy[i] = 1;
-  } else {
-    const int per_xcd = num_cus / num_xcds, take = copy_cus / num_xcds;
-    for (int x = 0; x < num_xcds; ++x)
-      for (int i = 0; i < take; ++i) is_copy[x * per_xcd + i] = 1;
-  }
-  std::vector<uint32_t> words((num_cus + 31) / 32, 0u);
-  for (int i = 0; i < num_cus; ++i)
-    if (is_copy[i] != complement) words[i / 32] |= 1u << (i % 32);
-  return words;
-}
-
-int masked_pair(DeviceState& d, int copy_cus, MaskedPair** out) {
-  if (d.pair_copy_cus != copy_cus) {
-    if (d.pair.copy) {
-      // pending work on the old streams still completes; release happens after it
-      (void)hipStreamDestroy(d.pair.copy);
-      (void)hipStreamDestroy(d.pair.gemm);
-      d.pair = MaskedPair{};
-      d.pair_copy_cus = -1;
-    }
-    MaskedPair mp;
-    auto cm = copy_mask_bits(d.num_cus, d.num_xcds, copy_cus, false);
-    auto gm = copy_mask_bits(d.num_cus, d.num_xcds, copy_cus, true);
-    HIP_TRY(hipExtStreamCreateWithCUMask(&mp.copy, static_cast<uint32_t>(cm.size()), cm.data()));
-    HIP_TRY(hipExtStreamCreateWithCUMask(&mp.gemm, static_cast<uint32_t>(gm.size()), gm.data()));
-    mp.gemm_cus = d.num_cus - copy_cus;
-    d.pair = mp;
-    d.pair_copy_cus = copy_cus;
-  }
-  *out = &d.pair;
   return SYNC_OK;
 }
 
@@ -344,7 +289,7 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
     const sync_plan_desc& d = plan->plan.desc;
     if (op != SYNC_OP_AG_GEMM || d.b_layout != SYNC_B_NK)
       return fail(SYNC_EINVAL, "copy_kslices > 1 is for AG-GEMM with B stored [n][k]");
-    if (cfg.backend == SYNC_COPY_SDMA || cfg.backend == SYNC_COPY_HOST_GATED)
+    if (cfg.backend == SYNC_COPY_SDMA)
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs the CU, COLOCATED or PRESET backend");
     if (d.k / 64 < 4 * static_cast<int64_t>(cfg.copy_kslices))
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs K/64 >= 4 x copy_kslices");
@@ -358,7 +303,9 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   if (cfg.backend < SYNC_COPY_PRESET || cfg.backend > SYNC_COPY_EPILOGUE) return fail(SYNC_EINVAL, "bad backend");
   if (cfg.backend == SYNC_COPY_EPILOGUE && op != SYNC_OP_GEMM_RS)
     return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend sends GEMM-RS output; AG and attention copy in");
-  if (cfg.backend == SYNC_COPY_HOST_GATED && !cfg.host_gates) return fail(SYNC_EINVAL, "HOST_GATED needs host_gates");
+  if (cfg.backend == SYNC_COPY_HOST_GATED)
+    return fail(SYNC_EUNSUPPORTED, "the HOST_GATED backend was withdrawn (stream-ordered runtime copies cannot start "
+                                   "while the persistent kernel runs); SYNC_RUN_WITHHOLD covers failure-path tests");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
     return fail(SYNC_EINVAL, "unknown cfg.flags bits");
   if ((cfg.flags & SYNC_RUN_TRACE) && op == SYNC_OP_RING_ATTN) return fail(SYNC_EINVAL, "TRACE is for GEMM calls");
@@ -387,31 +334,6 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   return SYNC_OK;
 }
 
-// Enqueues, on `s`, SDMA copies of every non-resident chunk in arrival order,
-// each followed (when `publish`) by a one-lane kernel that raises the chunk's
-// flag (stream order puts it after the copy has landed).  HOST_GATED first
-// makes the stream wait for the chunk's host word.
-// Measured limitation of this path under the HIP runtime: once the persistent
-// GEMM is running, the runtime does not start the next SDMA copy on the copy
-// stream until the GEMM exits, so only chunks copied before the GEMM starts
-// overlap; later ones time out.  The CU backend does not have this limit.
-int enqueue_sdma_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2], char* const dst[2],
-                         const int64_t row_bytes[2], int ntensors, bool publish, hipStream_t s) {
-  for (int32_t p = 0; p < pl.num_chunks; ++p) {
-    const int32_t c = pl.arrival[p];
-    if (pl.resident[c]) continue;
-    if (cx.cfg.backend == SYNC_COPY_HOST_GATED)
-      HIP_TRY(hipStreamWaitValue32(s, const_cast<uint32_t*>(cx.cfg.host_gates + c), 1u, hipStreamWaitValueGte,
-                                   0xffffffffu));
-    const int64_t r0 = pl.chunk_begin[c], r1 = pl.chunk_begin[c + 1];
-    for (int x = 0; x < ntensors; ++x)
-      HIP_TRY(hipMemcpyAsync(dst[x] + r0 * row_bytes[x], src[x] + r0 * row_bytes[x],
-                             static_cast<size_t>((r1 - r0) * row_bytes[x]), hipMemcpyDeviceToDeviceNoCU, s));
-    if (publish) HIP_TRY(launch_publish_flag(cx.ws.hdr, cx.ws.flags, c, s));
-  }
-  return SYNC_OK;
-}
-
 int check_gemm_shape(const Plan& pl) {
   const auto& d = pl.desc;
   if (d.k % 64) return fail(SYNC_EUNSUPPORTED, "k must be a multiple of 64");
@@ -427,7 +349,38 @@ int check_gemm_shape(const Plan& pl) {
 
 // Compute workgroups per CU (the kernel's occupancy; copy workgroups of the
 // same launch take CUs at the same rate).
-int gemm_wg_per_cu(const Plan& pl) { return (pl.desc.tile_m == 128 && pl.desc.tile_n == 128) ? 2 : 1; }
+int gemm_wg_per_cu(const Plan& pl) { return syncov::gemm_wg_per_cu(pl.desc.tile_m, pl.desc.tile_n); }
+
+// A launch of num_cus x wpc workgroups assumes every one of them is resident
+// at once: the co-located copy publishes every chunk once all workgroups have
+// copied, and co-located copy-out and the GEMM-AR all-gather wait for chunks
+// that other workgroups of the grid produce.  The instance's occupancy (from
+// its registers and LDS) is read once per device and variant; an instance
+// that fits fewer workgroups per CU is refused rather than left to time out.
+std::mutex g_occ_mu;
+std::map<std::tuple<int, int, int, int, int, int>, int> g_occ;
+
+int check_residency(const Plan& pl, int device, int c_dtype, bool rs) {
+  const auto key = std::make_tuple(device, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, rs ? 1 : 0);
+  int occ = -1;
+  {
+    std::lock_guard<std::mutex> lk(g_occ_mu);
+    auto it = g_occ.find(key);
+    if (it != g_occ.end()) occ = it->second;
+  }
+  if (occ < 0) {
+    GemmArgs none{};
+    HIP_TRY(launch_gemm(none, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, rs, 0, nullptr, &occ));
+    std::lock_guard<std::mutex> lk(g_occ_mu);
+    g_occ[key] = occ;
+  }
+  const int need = gemm_wg_per_cu(pl);
+  if (occ < need)
+    return fail(SYNC_EUNSUPPORTED, "the " + std::to_string(pl.desc.tile_m) + "x" + std::to_string(pl.desc.tile_n) +
+                                       " kernel fits " + std::to_string(occ) + " workgroup(s) per CU; its launch "
+                                       "needs " + std::to_string(need));
+  return SYNC_OK;
+}
 
 CounterArrays counter_arrays(const CallCtx& cx, int32_t C) {
   return CounterArrays{cx.ws.counters, cx.ws.parts, cx.ws.xparts, cx.ws.sparts, cx.ws.sxparts, C};
@@ -507,7 +460,6 @@ struct Roles {
   int wait = 1;         // compute waits for non-resident chunks
   int colocated = 0;    // every compute workgroup copies its share first
   bool no_compute = false;  // co-located copy-only: the copy phase alone
-  bool sdma = false;    // HOST_GATED: stream-ordered SDMA copies on the library's streams
   bool engines = false; // SDMA: copies queued on the SDMA engines through HSA, gated by the call
   bool push = false;    // EPILOGUE: the RS epilogue stores every tile into its send slot too
 };
@@ -515,8 +467,6 @@ struct Roles {
 // CU backend: one launch, copy_cus * wpc copy workgroups first, then one
 // compute workgroup per remaining CU slot.  PRESET: compute alone, nothing to
 // wait for.  SDMA: compute on every CU, copies on the SDMA engines.
-// HOST_GATED: compute on the CUs the masked GEMM stream allows, copies on
-// the copy stream.
 Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
   Roles r;
   const bool copy_only = cx.cfg.flags & SYNC_RUN_COPY_ONLY;
@@ -559,14 +509,7 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
       else
         r.engines = true;
       break;
-    default:  // HOST_GATED
-      if (compute_only) {
-        r.grid = d.num_cus * wpc;
-        r.wait = 0;
-      } else {
-        r.sdma = true;
-        r.grid = copy_only ? 0 : (d.num_cus - d.num_xcds) * wpc;
-      }
+    default:  // rejected by prepare()
       break;
   }
   return r;
@@ -619,12 +562,11 @@ int run_engines(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed*
   return queued;
 }
 
-// Enqueues one call: `launch(stream, roles)` puts the compute kernel (with its
-// copy workgroups, if any) on a stream; SDMA copy-in goes to the library's
-// copy stream with the compute kernel on the masked GEMM stream, both joined
-// back to `cs`.
+// Enqueues one call on the caller's stream `cs`: `launch(stream, roles)` puts
+// the compute kernel (with its copy workgroups, if any) there; the SDMA
+// backend adds its gate kernel and queues the copies on the engines.
 template <typename Launch>
-int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs, void* copy,
+int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs,
              const Roles& r, const char* const src[2], char* const dst[2], const int64_t rb[2], int ntensors,
              Launch launch) {
   auto timed = [&](hipStream_t st) -> int {
@@ -642,28 +584,7 @@ int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm
     HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(cx.ws.trace_tiles), words, 0u, cs));
   }
   if (r.engines) return run_engines(pl, cx, d, tm, cs, r, src, dst, rb, ntensors, launch);
-  if (!r.sdma) return timed(cs);
-  MaskedPair* mp = nullptr;
-  int rc = masked_pair(d, d.num_xcds, &mp);
-  if (rc) return rc;
-  hipStream_t ss = copy ? static_cast<hipStream_t>(copy) : mp->copy;
-  HIP_TRY(hipEventRecord(d.ev_fork, cs));
-  HIP_TRY(hipStreamWaitEvent(ss, d.ev_fork, 0));
-  if (tm) HIP_TRY(hipEventRecord(tm->c0, ss));
-  if ((rc = enqueue_sdma_copy_in(pl, cx, src, dst, rb, ntensors, r.grid > 0, ss))) return rc;
-  if (tm) {
-    HIP_TRY(hipEventRecord(tm->c1, ss));
-    tm->has_copy = true;
-  }
-  HIP_TRY(hipEventRecord(d.ev_copy, ss));
-  if (r.grid > 0) {
-    HIP_TRY(hipStreamWaitEvent(mp->gemm, d.ev_fork, 0));
-    if ((rc = timed(mp->gemm))) return rc;
-    HIP_TRY(hipEventRecord(d.ev_gemm, mp->gemm));
-    HIP_TRY(hipStreamWaitEvent(cs, d.ev_gemm, 0));
-  }
-  HIP_TRY(hipStreamWaitEvent(cs, d.ev_copy, 0));
-  return SYNC_OK;
+  return timed(cs);
 }
 
 }  // namespace
@@ -768,6 +689,8 @@ int sync_workspace_init(sync_plan_t plan, void* ws, void* stream) {
   if (rc) return rc;
   // SDMA flag copies of earlier calls must not land after the fill
   if ((rc = sdma_quiesce_all(d->device))) return rc;
+  DeviceTables* tab = nullptr;  // set-up: the plan's tables go to the device now, not on the first launch
+  if ((rc = device_tables(plan, d->device, &tab))) return rc;
   HIP_TRY(launch_fill_u32(static_cast<uint32_t*>(ws), static_cast<int64_t>(sync_workspace_size(plan) / 4), 0u,
                           static_cast<hipStream_t>(stream)));
   return SYNC_OK;
@@ -823,8 +746,8 @@ int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk) {
   return SYNC_OK;
 }
 
-int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local, const void* b, void* c,
-                 int32_t c_dtype, void* ws, void* compute, void* copy) {
+static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local, const void* b,
+                        void* c, int32_t c_dtype, void* ws, void* compute) {
   CallCtx cx;
   int rc = prepare(plan, cfg, ws, SYNC_OP_AG_GEMM, cx);
   if (rc) return rc;
@@ -836,6 +759,7 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
   if (!aligned16(a_local) || !aligned16(b) || !aligned16(c) || (a_peer && !aligned16(a_peer)))
     return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
   DeviceState& d = *cx.dev;
+  if ((rc = check_residency(pl, d.device, c_dtype, false))) return rc;
   std::lock_guard<std::mutex> lk(d.mu);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
@@ -845,7 +769,7 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
   GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
   g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
   const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
-  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, src, dst, rb, 1,
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), r, src, dst, rb, 1,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     g.copy_blocks = rr.copy_blocks;
                     g.wait_chunks = rr.wait;
@@ -855,6 +779,12 @@ int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer,
                                         st));
                     return SYNC_OK;
                   });
+}
+
+int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local, const void* b, void* c,
+                 int32_t c_dtype, void* ws, void* compute, void* copy) {
+  (void)copy;
+  return ag_gemm_impl(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, compute);
 }
 
 // GEMM-RS share; `partials` (fp32 [m][n], or null) makes the send the
@@ -884,7 +814,7 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   const Plan& pl = plan->plan;
   if ((rc = check_gemm_shape(pl))) return rc;
   if (c_dtype != SYNC_DTYPE_F32 && c_dtype != SYNC_DTYPE_BF16) return fail(SYNC_EINVAL, "bad c_dtype");
-  if (cx.cfg.backend == SYNC_COPY_SDMA || cx.cfg.backend == SYNC_COPY_HOST_GATED)
+  if (cx.cfg.backend == SYNC_COPY_SDMA)
     return fail(SYNC_EUNSUPPORTED, "GEMM-RS copy-out runs on CUs (CU or COLOCATED backend) or not at all (PRESET)");
   const bool compute_only = cx.cfg.backend == SYNC_COPY_PRESET || (cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
   if (cx.cfg.flags & SYNC_RUN_COPY_ONLY) return fail(SYNC_EINVAL, "COPY_ONLY is not defined for GEMM-RS");
@@ -894,6 +824,7 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   if (!aligned16(a) || !aligned16(b) || !aligned16(c) || (staging && !aligned16(staging)))
     return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
   DeviceState& d = *cx.dev;
+  if ((rc = check_residency(pl, d.device, c_dtype, true))) return rc;
   std::lock_guard<std::mutex> lk(d.mu);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
@@ -934,7 +865,7 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
     g.ar_out = static_cast<char*>(ar_out);
     g.ar_row_bytes = pl.desc.n * 4;
   }
-  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, rar, nullptr, nullptr, nullptr, 0,
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), rar, nullptr, nullptr, nullptr, 0,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     g.copy_blocks = rr.copy_blocks;
                     g.colocated = rr.colocated;
@@ -1018,7 +949,7 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   at.nxcd = d.num_xcds;
   at.copy = make_copy_in(pl, cx, src, dst, rb, 2);
   const Roles r = roles_for(cx, d, 1);
-  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), copy, r, src, dst, rb, 2,
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), r, src, dst, rb, 2,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     at.copy_blocks = rr.copy_blocks;
                     at.wait_chunks = rr.wait;
@@ -1080,16 +1011,9 @@ void sync_shutdown(void) {
     DeviceState& d = *kv.second;
     if (!d.ready) continue;
     (void)hipSetDevice(kv.first);
-    if (d.pair.copy) {
-      (void)hipStreamDestroy(d.pair.copy);
-      (void)hipStreamDestroy(d.pair.gemm);
-    }
     for (auto& t : d.ring)
       for (hipEvent_t e : {t.k0, t.k1, t.c0, t.c1})
         if (e) (void)hipEventDestroy(e);
-    (void)hipEventDestroy(d.ev_fork);
-    (void)hipEventDestroy(d.ev_copy);
-    (void)hipEventDestroy(d.ev_gemm);
   }
   g_devices.clear();
   if (have) (void)hipSetDevice(cur);

@@ -85,3 +85,19 @@ def partials_f32(m: int, n: int, seed: int = SEED_P, integer: bool = False) -> n
     if integer:
         return rng.integers(-8, 9, size=(m, n)).astype(np.float32)
     return (rng.standard_normal((m, n), dtype=np.float32) / np.float32(8.0)).astype(np.float32)
+
+
+SEED_ROUTING = 21
+
+
+def routed_token_counts(total: int, world: int, seed: int = SEED_ROUTING, alpha: float = 2.0) -> list:
+    """Uneven token counts per peer for an all-to-all (MoE-like routing skew):
+    a seeded Dirichlet(alpha) split of `total` tokens, each count at least 1,
+    the last absorbing the rounding so that they sum to `total`."""
+    rng = np.random.default_rng(seed)
+    w = rng.dirichlet(np.full(world, alpha))
+    rows = np.maximum(1, np.floor(w * total).astype(np.int64))
+    rows[-1] += total - rows.sum()
+    if rows.min() < 1 or rows.sum() != total:
+        raise ValueError("cannot split the tokens into positive counts")
+    return [int(x) for x in rows]

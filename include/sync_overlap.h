@@ -27,9 +27,10 @@
  *     must be 16-byte aligned.  Host pointers are marked "host".
  *   - Streams are hipStream_t passed as void*; NULL means the null stream.
  *   - Launch calls are stream-ordered and asynchronous: SYNC_OK means the work
- *     was enqueued on `compute` (which the call joins back to before
- *     returning).  Device-side failures (a wait that timed out) are read
- *     afterwards with sync_workspace_status().
+ *     was enqueued on `compute`.  Device-side failures (a wait that timed
+ *     out) are read afterwards with sync_workspace_status().  The `copy`
+ *     stream argument of the launch calls is reserved and unused: every
+ *     backend runs on `compute` (the SDMA backend also on the engines).
  *   - All matrices are row-major.  bf16 = IEEE bfloat16 bit patterns.
  */
 #ifndef SYNC_OVERLAP_H
@@ -169,11 +170,11 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *               rest compute; `copy` is unused.  Copy workgroups are spread
  *               evenly over the XCDs and are resident before any compute
  *               workgroup.
- *   HOST_GATED  (tests: delayed or withheld chunks) per chunk, a runtime copy
- *               that first waits until the host word host_gates[c] becomes
- *               non-zero, then a one-lane flag kernel, on `copy` or the
- *               library's copy stream (masked to one CU per XCD; the compute
- *               kernel runs on the other CUs)
+ *   HOST_GATED  withdrawn: every call returns EUNSUPPORTED.  (It queued
+ *               stream-ordered runtime copies beside the persistent kernel;
+ *               the runtime does not start such a copy while that kernel
+ *               runs.)  The value stays reserved.  Failure-path tests use
+ *               SYNC_RUN_WITHHOLD instead.
  *   COLOCATED   one launch on `compute` whose compute workgroups also copy; no
  *               CUs are set aside [SYN-S Fig. 7: load/store by the compute SMs
  *               themselves].  AG and attention: every workgroup first copies
@@ -198,9 +199,8 @@ enum {
   SYNC_RUN_COPY_ONLY = 1,    /* run only the copy (copy-only timing); AG and attention */
   SYNC_RUN_COMPUTE_ONLY = 2, /* run only the compute kernel, with the workgroups the CU split
                                 leaves it (CU backend) or all CUs, every chunk taken as present */
-  SYNC_RUN_TIMED = 4,        /* record device events around the call's kernel launch and the
-                                runtime copies (HOST_GATED), on the streams they run on; read with
-                                sync_read_timings() */
+  SYNC_RUN_TIMED = 4,        /* record device events around the call's kernel launch on the
+                                compute stream; read with sync_read_timings() */
   SYNC_RUN_WITHHOLD = 8,     /* CU backend, AG and attention (failure-path tests): chunk
                                 cfg.withhold_chunk (-1: every non-resident chunk) is neither
                                 copied nor flagged, so the waits for it expire after timeout_ns,
@@ -214,7 +214,7 @@ typedef struct {
   int32_t backend;          /* SYNC_COPY_* */
   int32_t copy_cus;         /* CU backend: CUs given to the copy role, 8..128, multiple of 8 */
   uint64_t timeout_ns;      /* bound on every device-side wait; 0 = 2 s */
-  const uint32_t* host_gates; /* HOST_GATED: pinned host words (hipHostMalloc), one per chunk */
+  const uint32_t* host_gates; /* reserved (the withdrawn HOST_GATED backend); ignored */
   int32_t flags;            /* SYNC_RUN_* bits */
   int32_t copy_streaming;   /* CU and COLOCATED backends: 1 = non-temporal loads/stores in the copy
                                role; 0 = plain */
@@ -250,7 +250,8 @@ typedef struct {
  * that may overlap in time race on it. */
 size_t sync_workspace_size(sync_plan_t plan);
 
-/* Zeroes the workspace with a fill kernel on `stream`.  Call once after
+/* Zeroes the workspace with a fill kernel on `stream` and puts the plan's
+ * tables on the current device if they are not there yet.  Call once after
  * allocation, and again after a call reported a device-side timeout (the
  * error word is sticky: later waits give up at once).  Between calls nothing
  * is cleared: each call's kernel takes the next epoch from the workspace and
@@ -443,8 +444,8 @@ void sync_tune_forget(void);
  * call's kernel launch (GEMM or attention; with the CU backend its copy
  * workgroups are part of it) from just before the launch to just after it, on
  * the stream it runs on (SDMA: from before the gate kernel to after the
- * compute or join kernel); copy_ms spans the copies (HOST_GATED: the runtime
- * copies; SDMA: the same span as kernel_ms; 0 if none).  Reading
+ * compute or join kernel); copy_ms spans the copies (SDMA: the same span as
+ * kernel_ms; 0 if none).  Reading
  * empties the ring.  *count = records written to out (<= max). */
 typedef struct {
   float kernel_ms;

@@ -34,11 +34,17 @@ _LIB = None
 
 
 def default_threads() -> int:
+    """Threads the oracle uses: every CPU this process may run on, unless
+    OMP_NUM_THREADS names a smaller share (a shared machine's CPU share for
+    one job)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 def _lib():

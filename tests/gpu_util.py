@@ -53,3 +53,23 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     ax = np.abs(x.astype(np.float32))
     e = np.floor(np.log2(np.maximum(ax, np.float32(2.0 ** -126))))
     return np.float32(2.0) ** (e - 7)
+
+
+def check_full_f32(out: np.ndarray, ref: np.ndarray, absab: np.ndarray, k: int, world: int) -> float:
+    """Whole-output parity of an fp32-accumulated product against the fp64
+    oracle R: every element within the worst-case bound of a K-term fp32 sum
+    in any order, |C - R| <= K 2^-24 (|A||B|) (plus one fp32 ulp of slack for
+    the final rounding), and the per-row-shard relative Frobenius error at
+    most 1e-3.  A stale, missing or misplaced tile fails the first check."""
+    assert out.shape == ref.shape
+    assert np.isfinite(out).all(), f"{(~np.isfinite(out)).sum()} non-finite outputs"
+    o = out.astype(np.float64)
+    bound = k * 2.0 ** -24 * absab + np.abs(ref) * 2.0 ** -23
+    bad = np.abs(o - ref) > bound
+    if bad.any():
+        idx = np.argwhere(bad)
+        raise AssertionError(f"{bad.sum()} outputs outside the fp32 accumulation bound; first {idx[:6].tolist()} "
+                             f"got {o[bad][:6]} want {ref[bad][:6]}")
+    err = shard_frobenius(o, ref, world)
+    assert err <= 1e-3, err
+    return err

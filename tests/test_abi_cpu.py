@@ -141,3 +141,53 @@ def test_epilogue_backend_is_for_gemm_rs():
     rc = A.lib().sync_ag_gemm(p.handle, ctypes.byref(A.make_cfg(A.SYNC_COPY_EPILOGUE)), None, None, None, None, 0,
                               256, None, None)
     assert rc == A.SYNC_EUNSUPPORTED and "EPILOGUE" in A.sync_last_error()
+
+
+def test_host_gated_backend_is_withdrawn():
+    """HOST_GATED is rejected before any device work, for every launch call."""
+    p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256))
+    cfg = A.make_cfg(A.SYNC_COPY_HOST_GATED)
+    rc = A.lib().sync_ag_gemm(p.handle, ctypes.byref(cfg), None, None, None, None, 0, 256, None, None)
+    assert rc == A.SYNC_EUNSUPPORTED and "withdrawn" in A.sync_last_error()
+    rs = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, 1024, 256, 1024, 4, tile_m=256, tile_n=256))
+    rc = A.lib().sync_gemm_rs(rs.handle, ctypes.byref(cfg), None, None, None, 0, None, 256, None, None)
+    assert rc == A.SYNC_EUNSUPPORTED and "withdrawn" in A.sync_last_error()
+
+
+def test_binding_checks_tensor_sizes():
+    """The binding refuses tensors that are not on a GPU, not contiguous, of
+    the wrong element size or too small for the plan, before the library sees
+    them (a short tensor would otherwise be read or written past its end)."""
+    torch = pytest.importorskip("torch")
+    p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 256, 128, 64, 4, tile_m=128, tile_n=128))
+    host = torch.zeros(256 * 64, dtype=torch.int16)
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_ag_gemm(p, None, host, 0x1000, 0x1000, 0x1000, A.SYNC_DTYPE_F32, 0x1000)
+    assert ei.value.code == A.SYNC_EINVAL and "device tensor" in ei.value.message
+
+    class FakeDev:  # the attributes the checks read, without a GPU
+        is_cuda = True
+
+        def __init__(self, n, elem, contiguous=True):
+            self.n, self.elem, self.contig = n, elem, contiguous
+
+        def data_ptr(self):
+            return 0x1000
+
+        def is_contiguous(self):
+            return self.contig
+
+        def element_size(self):
+            return self.elem
+
+        def numel(self):
+            return self.n
+
+    for bad, msg in ((FakeDev(256 * 64 - 1, 2), "elements"), (FakeDev(256 * 64, 4), "2-byte"),
+                     (FakeDev(256 * 64, 2, contiguous=False), "contiguous")):
+        with pytest.raises(A.SyncError) as ei:
+            A.sync_ag_gemm(p, None, None, bad, 0x1000, 0x1000, A.SYNC_DTYPE_F32, 0x1000)
+        assert ei.value.code == A.SYNC_EINVAL and msg in ei.value.message
+    with pytest.raises(A.SyncError) as ei:  # fp32 C needs 4-byte elements
+        A.sync_ag_gemm(p, None, None, 0x1000, 0x1000, FakeDev(256 * 128, 2), A.SYNC_DTYPE_F32, 0x1000)
+    assert "c must have 4-byte" in ei.value.message

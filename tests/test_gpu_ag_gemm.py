@@ -14,7 +14,8 @@ import oracle
 from communication_overlap_gemm_amd import _abi as A
 from communication_overlap_gemm_amd import inputs
 
-from gpu_util import bf16_poison, bf16_round, bf16_ulp, dev_bits, host_bits, shard_frobenius, workspace
+from gpu_util import (bf16_poison, bf16_round, bf16_ulp, check_full_f32, dev_bits, host_bits,
+                      shard_frobenius, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -216,22 +217,20 @@ def test_full_size_exact_small_integers(layout):
     assert np.array_equal(out[rows, cols].astype(np.float64), exact)
 
 
+def _b_for(b_kn, layout):
+    return b_kn if layout == "kn" else np.ascontiguousarray(b_kn.T)
+
+
 @pytest.mark.parametrize("backend,cus,split", [
     (A.SYNC_COPY_SDMA, 0, 1), (A.SYNC_COPY_CU, 32, 4),
     (A.SYNC_COPY_CU, 16, 2), (A.SYNC_COPY_PRESET, 0, 1), (A.SYNC_COPY_COLOCATED, 0, 1)])
 @pytest.mark.parametrize("layout", ["kn", "nk"])
-def test_full_size_normal(backend, cus, split, layout):
-    a, b = inputs.gemm_operands(M2, N2, K2, 64.0, b_layout=layout)
-    out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), split=split, backend=backend, copy_cus=cus,
-                    layout=layout)
-    assert np.isfinite(out).all()
-    rows, cols = _samples(M2, N2, 20000, seed=1)
-    ref = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout=layout)
-    shard = rows // (M2 // W2)
-    for s in range(W2):
-        sel = shard == s
-        num = np.linalg.norm(out[rows[sel], cols[sel]] - ref[sel])
-        assert num / np.linalg.norm(ref[sel]) <= 1e-3
+def test_full_size_normal(cfg2_data, backend, cus, split, layout):
+    """Every output element of the full-size share against the oracle."""
+    a, b_kn, ref, absab = cfg2_data
+    out, _ = run_ag(M2, N2, K2, W2, a, _b_for(b_kn, layout), tile=(256, 256), split=split, backend=backend,
+                    copy_cus=cus, layout=layout)
+    check_full_f32(out, ref, absab, K2, W2)
 
 
 # ---- one launch per call: failure path and replay ---------------------------
@@ -504,19 +503,13 @@ def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles():
 
 @pytest.mark.parametrize("backend,cus,teams,kslices", [(A.SYNC_COPY_CU, 32, 7, 4), (A.SYNC_COPY_CU, 32, 7, 8),
                                                        (A.SYNC_COPY_COLOCATED, 0, 7, 4)])
-def test_full_size_kslices(backend, cus, teams, kslices):
-    """The Llama-3-8B up-projection share with a K-sliced copy: sampled parity
-    against the oracle per row shard."""
-    a, b = inputs.gemm_operands(M2, N2, K2, 64.0, b_layout="nk")
-    out, _ = run_ag(M2, N2, K2, W2, a, b, tile=(256, 256), backend=backend, copy_cus=cus, layout="nk",
-                    teams=teams, kslices=kslices)
-    assert np.isfinite(out).all()
-    rows, cols = _samples(M2, N2, 20000, seed=3)
-    ref = oracle.gemm_f64_sampled(a, b, M2, N2, K2, rows, cols, b_layout="nk")
-    shard = rows // (M2 // W2)
-    for s in range(W2):
-        sel = shard == s
-        assert np.linalg.norm(out[rows[sel], cols[sel]] - ref[sel]) / np.linalg.norm(ref[sel]) <= 1e-3
+def test_full_size_kslices(cfg2_data, backend, cus, teams, kslices):
+    """The Llama-3-8B up-projection share with a K-sliced copy: every output
+    element against the oracle."""
+    a, b_kn, ref, absab = cfg2_data
+    out, _ = run_ag(M2, N2, K2, W2, a, _b_for(b_kn, "nk"), tile=(256, 256), backend=backend, copy_cus=cus,
+                    layout="nk", teams=teams, kslices=kslices)
+    check_full_f32(out, ref, absab, K2, W2)
 
 
 # ---- non-temporal loads and stores in the copy role -------------------------
@@ -672,16 +665,6 @@ def test_shutdown_then_calls_again():
 
 # ---- uneven shards: the receive side of an all-to-all (A2A-GEMM) ------------
 
-def _a2a_rows(total, world, seed):
-    """Seeded uneven token counts per peer (MoE-like routing skew), summing to total."""
-    rng = np.random.default_rng(seed)
-    w = rng.dirichlet(np.full(world, 2.0))
-    rows = np.maximum(1, np.floor(w * total).astype(np.int64))
-    rows[-1] += total - rows.sum()
-    assert rows.min() >= 1 and rows.sum() == total
-    return [int(x) for x in rows]
-
-
 @pytest.mark.parametrize("backend,cus,teams,kslices,split,tile", [
     (A.SYNC_COPY_CU, 16, 3, 0, 1, (128, 128)), (A.SYNC_COPY_CU, 32, 7, 4, 1, (256, 256)),
     (A.SYNC_COPY_SDMA, 0, 3, 0, 2, (256, 128)), (A.SYNC_COPY_COLOCATED, 0, 0, 0, 1, (256, 256))])
@@ -689,7 +672,7 @@ def test_a2a_gemm_uneven_shards_exact(backend, cus, teams, kslices, split, tile)
     """Peers send uneven token blocks (tiles straddle shard boundaries): exact
     for small integers, every received row staged."""
     world, n, k = 8, 768, 1024
-    rows = _a2a_rows(2040, world, seed=21)
+    rows = inputs.routed_token_counts(2040, world)
     m = sum(rows)
     a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
     ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
