@@ -32,7 +32,7 @@ SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 
 EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
-    "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_gemm_rs", "sync_gemm_rs_reduce", "sync_gemm_ar",
+    "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_ag_gemm_noalloc", "sync_gemm_rs", "sync_gemm_rs_reduce", "sync_gemm_ar",
     "sync_ring_attn_step",
     "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
     "sync_autotune", "sync_tune_workspace_size", "sync_tune_forget",
@@ -137,6 +137,7 @@ def lib():
             "sync_workspace_init": (i32, [vp, vp, vp]),
             "sync_workspace_status": (i32, [vp, vp, ctypes.POINTER(i32)]),
             "sync_ag_gemm": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, i32, vp, vp, vp]),
+            "sync_ag_gemm_noalloc": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, i32, vp]),
             "sync_gemm_rs": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, i32, vp, vp, vp, vp]),
             "sync_gemm_rs_reduce": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp]),
             "sync_gemm_ar": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -372,6 +373,14 @@ def sync_ag_gemm(plan: Plan, cfg: Optional[sync_copy_cfg], a_peer, a_local, b, c
                               _arg(a_peer, "a_peer", 2, m * k), _arg(a_local, "a_local", 2, m * k),
                               _arg(b, "b", 2, k * n), _arg(c, "c", _c_elem(c_dtype), m * n), c_dtype,
                               _ws_arg(plan, ws), _stream(compute), _stream(copy)))
+
+
+def sync_ag_gemm_noalloc(plan: Plan, cfg: sync_copy_cfg, a_peer, a_local, b, c, c_dtype: int, compute=None) -> None:
+    m, n, k = plan.desc.m, plan.desc.n, plan.desc.k
+    _check(lib().sync_ag_gemm_noalloc(plan.handle, ctypes.byref(cfg) if cfg is not None else None,
+                                      _arg(a_peer, "a_peer", 2, m * k), _arg(a_local, "a_local", 2, m * k),
+                                      _arg(b, "b", 2, k * n), _arg(c, "c", _c_elem(c_dtype), m * n), c_dtype,
+                                      _stream(compute)))
 
 
 def sync_gemm_rs(plan: Plan, cfg: Optional[sync_copy_cfg], a, b, c, c_dtype: int, staging, ws, compute=None,

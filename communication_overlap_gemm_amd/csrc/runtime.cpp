@@ -79,11 +79,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // ---- per-device state ----------------------------------------------------
+// Workspace of sync_ag_gemm_noalloc: a file-scope device array, so that the
+// call allocates nothing.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, once per device
+// (DeviceState::scratch), and only that address is passed to kernels.
+constexpr int64_t kScratchBytes = int64_t(1) << 20;
+__device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
+
 // Per-device facts and the ring of timing events.  Every call runs on the
 // caller's stream: the library creates no streams.
 struct DeviceState {
   bool ready = false;
   int device = 0;
+  void* scratch = nullptr;        // device address of `scratch` on this device
+  hipError_t scratch_err = hipSuccess;
   int num_cus = 0, num_xcds = 1, clock_khz = 0;
   int64_t wall_khz = 100000;
   std::string arch;
@@ -118,6 +128,9 @@ int current_device_state(DeviceState** out) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0) d.num_xcds = v;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) == hipSuccess && v > 0) d.wall_khz = v;
+    // this device is current: its own copy of the scratch array
+    d.scratch_err = hipGetSymbolAddress(&d.scratch, HIP_SYMBOL(scratch));
+    if (d.scratch_err != hipSuccess) d.scratch = nullptr;
     d.ready = true;
   }
   *out = &d;
@@ -220,6 +233,18 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   return SYNC_OK;
 }
 
+// The plan's tables on `dev` if an earlier call put them there; EINVAL
+// otherwise (for callers that may not allocate).
+int resident_tables(sync_plan_s* p, int dev, DeviceTables** out) {
+  std::lock_guard<std::mutex> lk(p->mu);
+  auto it = p->dev.find(dev);
+  if (it == p->dev.end())
+    return fail(SYNC_EINVAL, "the plan's tables are not on this device yet: call sync_workspace_init or a launch "
+                             "call with this plan on the device first");
+  *out = &it->second;
+  return SYNC_OK;
+}
+
 // Workspace layout: 256-byte header, then four uint32[C] arrays, each padded
 // to 256 bytes: flags (ready / done), counters (GEMM tiles stored per chunk),
 // parts (copy XCD groups finished per chunk), sent (copy-out done); then
@@ -273,10 +298,13 @@ struct CallCtx {
   uint64_t timeout_ticks = 0;
 };
 
-int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, CallCtx& cx) {
+// ws == nullptr with `noalloc`: the call runs on the device's static scratch
+// and must not allocate (the plan's tables must already be on the device).
+int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, CallCtx& cx, bool noalloc = false) {
   if (!plan) return fail(SYNC_EINVAL, "plan is NULL");
   if (plan->plan.desc.op != op) return fail(SYNC_EINVAL, "plan was built for a different op");
-  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(SYNC_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  if (!noalloc && (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)))
+    return fail(SYNC_EINVAL, "workspace must be non-NULL and 256-byte aligned");
   sync_copy_cfg cfg{};
   cfg.backend = SYNC_COPY_SDMA;
   if (cfg_in) cfg = *cfg_in;
@@ -324,8 +352,14 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
     if (cfg.copy_cus < cx.dev->num_xcds || cfg.copy_cus % cx.dev->num_xcds || cfg.copy_cus > cx.dev->num_cus / 2)
       return fail(SYNC_EINVAL, "copy_cus must be a multiple of the XCD count and at most half the CUs");
   }
-  rc = device_tables(plan, cx.dev->device, &cx.tab);
-  if (rc) return rc;
+  if (noalloc) {
+    if (!cx.dev->scratch)
+      return fail(SYNC_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(cx.dev->scratch_err));
+    ws = cx.dev->scratch;
+    if ((rc = resident_tables(plan, cx.dev->device, &cx.tab))) return rc;
+  } else if ((rc = device_tables(plan, cx.dev->device, &cx.tab))) {
+    return rc;
+  }
   cx.ws = ws_view(ws, plan->plan.num_chunks, plan->plan.num_tiles);
   cx.cfg = cfg;
   const uint64_t ns = cfg.timeout_ns ? cfg.timeout_ns : 2000000000ull;
@@ -735,7 +769,14 @@ int sync_trace_export(sync_plan_t plan, const void* ws, void* stream, sync_trace
 }
 
 int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk) {
-  if (!ws) return fail(SYNC_EINVAL, "workspace is NULL");
+  if (!ws) {  // the static scratch of sync_ag_gemm_noalloc on the current device
+    DeviceState* d = nullptr;
+    int rc = current_device_state(&d);
+    if (rc) return rc;
+    if (!d->scratch)
+      return fail(SYNC_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(d->scratch_err));
+    ws = d->scratch;
+  }
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
   uint32_t h[3] = {0, 0, 0};
   HIP_TRY(hipMemcpy(h, ws, sizeof h, hipMemcpyDeviceToHost));
@@ -747,12 +788,25 @@ int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk) {
 }
 
 static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local, const void* b,
-                        void* c, int32_t c_dtype, void* ws, void* compute) {
+                        void* c, int32_t c_dtype, void* ws, void* compute, bool noalloc) {
   CallCtx cx;
-  int rc = prepare(plan, cfg, ws, SYNC_OP_AG_GEMM, cx);
+  if (noalloc) {  // nothing that allocates: no SDMA signals, no timing events, no trace
+    const int32_t backend = cfg ? cfg->backend : SYNC_COPY_SDMA;
+    if (backend != SYNC_COPY_PRESET && backend != SYNC_COPY_CU && backend != SYNC_COPY_COLOCATED)
+      return fail(SYNC_EUNSUPPORTED, "sync_ag_gemm_noalloc runs the PRESET, CU and COLOCATED backends");
+    if (cfg->flags & (SYNC_RUN_TIMED | SYNC_RUN_TRACE))
+      return fail(SYNC_EUNSUPPORTED, "sync_ag_gemm_noalloc takes no TIMED or TRACE mode");
+  }
+  int rc = prepare(plan, cfg, ws, SYNC_OP_AG_GEMM, cx, noalloc);
   if (rc) return rc;
   const Plan& pl = plan->plan;
   if ((rc = check_gemm_shape(pl))) return rc;
+  if (noalloc) {
+    const int64_t need = ws_trace_offset(pl.num_chunks);
+    if (need > kScratchBytes)
+      return fail(SYNC_EINVAL, "the plan needs " + std::to_string(need) + " bytes of workspace; the static scratch "
+                               "holds " + std::to_string(kScratchBytes));
+  }
   if (c_dtype != SYNC_DTYPE_F32 && c_dtype != SYNC_DTYPE_BF16) return fail(SYNC_EINVAL, "bad c_dtype");
   const bool need_peer = cx.cfg.backend != SYNC_COPY_PRESET && !(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
   if (!a_local || !b || !c || (need_peer && !a_peer)) return fail(SYNC_EINVAL, "NULL operand");
@@ -763,6 +817,8 @@ static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   std::lock_guard<std::mutex> lk(d.mu);
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
+  if (noalloc)  // the scratch keeps the last call's contents: epoch, flags and counters start from zero
+    HIP_TRY(launch_fill_u32(cx.ws.hdr, ws_trace_offset(pl.num_chunks) / 4, 0u, static_cast<hipStream_t>(compute)));
   const char* src[2] = {static_cast<const char*>(a_peer), nullptr};
   char* dst[2] = {static_cast<char*>(a_local), nullptr};
   const int64_t rb[2] = {pl.desc.k * 2, 0};
@@ -784,7 +840,13 @@ static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
 int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local, const void* b, void* c,
                  int32_t c_dtype, void* ws, void* compute, void* copy) {
   (void)copy;
-  return ag_gemm_impl(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, compute);
+  return ag_gemm_impl(plan, cfg, a_peer, a_local, b, c, c_dtype, ws, compute, false);
+}
+
+int sync_ag_gemm_noalloc(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local,
+                         const void* b, void* c, int32_t c_dtype, void* compute) {
+  if (!cfg) return fail(SYNC_EINVAL, "sync_ag_gemm_noalloc needs a copy configuration");
+  return ag_gemm_impl(plan, cfg, a_peer, a_local, b, c, c_dtype, nullptr, compute, true);
 }
 
 // GEMM-RS share; `partials` (fp32 [m][n], or null) makes the send the

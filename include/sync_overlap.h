@@ -288,7 +288,8 @@ int sync_trace_export(sync_plan_t plan, const void* ws, void* stream, sync_trace
 
 /* Synchronises `stream`, then reads the workspace error word.  Returns
  * SYNC_OK, or SYNC_ETIMEOUT with *err_chunk (may be NULL) = the chunk whose
- * wait expired first. */
+ * wait expired first.  ws == NULL reads the static scratch of the current
+ * device (the last sync_ag_gemm_noalloc call there). */
 int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk);
 
 /* ---- launch calls --------------------------------------------------------- */
@@ -305,6 +306,31 @@ int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk);
  * (tile_m, tile_n) in {(256,256), (256,128), (128,128)}. */
 int sync_ag_gemm(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local,
                  const void* b, void* c, int32_t c_dtype, void* ws, void* compute, void* copy);
+
+/* AG-GEMM share for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same call as sync_ag_gemm (same arguments, kernels and result), except
+ * that its workspace is the library's static device scratch, a 1 MiB array
+ * that every GPU the library runs on holds until the process ends, and that
+ * it calls no hipMalloc, hipFree or other allocating routine:
+ *   - cfg must be non-NULL; backend PRESET, CU or COLOCATED (SDMA needs
+ *     signals: EUNSUPPORTED); no SYNC_RUN_TIMED or SYNC_RUN_TRACE
+ *     (EUNSUPPORTED); other cfg fields as for sync_ag_gemm.
+ *   - The plan's tables must already be on the device: any earlier
+ *     sync_workspace_init or launch call with this plan on the current device
+ *     put them there (else EINVAL).
+ *   - The plan's workspace (sync_workspace_size less its trace area) must fit
+ *     in 1 MiB (else EINVAL), e.g. up to ~1000 chunks.
+ *   - Each call first clears the part of the scratch it uses with a fill
+ *     kernel on `compute` (stream-ordered, so the call can be captured), then
+ *     launches as sync_ag_gemm does.  The scratch keeps the last call's
+ *     contents; sync_workspace_status(NULL, stream, &chunk) reads its error
+ *     word (a device-side timeout of the last call).
+ *   - Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *     in time on one GPU (other streams, other threads) race on it; order
+ *     them on one stream. */
+int sync_ag_gemm_noalloc(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local,
+                         const void* b, void* c, int32_t c_dtype, void* compute);
 
 /* GEMM-RS share [SYN-S "Experiments": GEMM-RS; ENT: tiles reordered so output
  * for communication is produced at a steady pace; SM-based fine-grained
