@@ -49,20 +49,23 @@ FLUSH_BYTES = 512 << 20       # written between cold-cache calls (twice the Infi
 CU, COLOC, SDMA, PRESET, EPI = (A.SYNC_COPY_CU, A.SYNC_COPY_COLOCATED, A.SYNC_COPY_SDMA, A.SYNC_COPY_PRESET,
                                 A.SYNC_COPY_EPILOGUE)
 HEADLINE = dict(split=1, tile=(256, 256), order="chunk_major", layout="nk", c_dtype="f32")
-HEADLINE_AGENT = dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4)
+HEADLINE_AGENT = dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=2, copy_lead_slice=1)
 BACKENDS = {"sdma": dict(backend=SDMA, copy_teams=7), "cu8": dict(backend=CU, copy_cus=8),
             "cu16": dict(backend=CU, copy_cus=16), "cu24": dict(backend=CU, copy_cus=24),
             "cu32": dict(backend=CU, copy_cus=32), "cu40": dict(backend=CU, copy_cus=40),
             "cu64": dict(backend=CU, copy_cus=64), "colocated": dict(backend=COLOC)}
 SWEEP_AGENTS = {
     "sdma_1_engine": dict(backend=SDMA, copy_teams=1), "sdma_7_engines": dict(backend=SDMA, copy_teams=7),
+    "cu32_4slices_no_lead": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4),
+    "cu32_4slices_lead2": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4, copy_lead_slice=2),
+    "cu32_2slices_no_lead": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=2),
     "cu8": dict(backend=CU, copy_cus=8, copy_teams=7, copy_kslices=4),
     "cu16": dict(backend=CU, copy_cus=16, copy_teams=7, copy_kslices=4),
     "cu32": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4),
     "colocated": dict(backend=COLOC),
     "cu32_xgmi_ring_153": dict(backend=CU, copy_cus=32, copy_teams=1, copy_kslices=4, copy_link_gbps=153.0),
     "cu32_xgmi_mesh_153": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4, copy_link_gbps=153.0)}
-SPLIT_SWEEP_AGENTS = {"cu32": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4),
+SPLIT_SWEEP_AGENTS = {"cu32": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=2, copy_lead_slice=1),
                       "sdma_7_engines": dict(backend=SDMA, copy_teams=7)}
 # GEMM-RS, Llama-3-8B down-projection
 RS_SHAPE = dict(m=8192, n=4096, k=1792, world=8, divisor=64.0)
@@ -90,27 +93,30 @@ ATTN_AGENTS = {"overlapped": dict(backend=COLOC), "overlapped_32_copy_cus": dict
 
 ORDERS = {"row_major": A.SYNC_ORDER_ROW_MAJOR, "chunk_major": A.SYNC_ORDER_CHUNK_MAJOR,
           "swizzled": A.SYNC_ORDER_SWIZZLED}
-TUNE_AGENTS = (("sdma_7_engines", "sdma", 7, 1), ("cu16", "cu16", 7, 4), ("cu32", "cu32", 7, 4),
-               ("colocated", "colocated", 0, 1))
+TUNE_AGENTS = (("sdma_7_engines", "sdma", 7, 1, 0), ("cu16", "cu16", 7, 4, 0), ("cu32", "cu32", 7, 4, 0),
+               ("cu32_lead", "cu32", 7, 2, 1), ("colocated", "colocated", 0, 1, 0))
 
 PROFILE = os.path.join(ROOT, "profiles", "gemm_dma_ag_llama8b_up.md")
 KERNEL_SOURCES = ["gemm_persistent.hip", "copy_role.hpp", "device_common.hpp", "launch_args.hpp"]
 PROFILED = {"tile": "256x256", "split": 1, "order": "chunk_major", "backend": "cu32", "c_dtype": "f32", "layout": "nk",
-            "teams": 7, "kslices": 4, "copy_store": "plain"}
+            "teams": 7, "kslices": 2, "lead": 1, "copy_store": "plain"}
 
 
 def cfg(flags=0, **kw):
     return A.make_cfg(flags=flags, **kw)
 
 
-def agent_for(name, teams, kslices):
+def agent_for(name, teams, kslices, lead=0):
     """Copy configuration of a command-line backend name: SDMA takes the engine
-    count (teams); the CU and co-located backends take teams and K-slices."""
+    count (teams); the CU and co-located backends take teams and K-slices; the
+    CU backend with K-slices also the lead slices its compute workgroups copy."""
     kw = dict(BACKENDS[name])
     if kw["backend"] in (CU, SDMA, COLOC):
         kw["copy_teams"] = teams
     if kw["backend"] in (CU, COLOC):
         kw["copy_kslices"] = kslices
+    if kw["backend"] == CU and kslices > 1:
+        kw["copy_lead_slice"] = lead
     return kw
 
 
@@ -153,9 +159,12 @@ def parse(argv=None):
     p.add_argument("--teams", type=int, default=7,
                    help="copied chunks in flight at once (1: one after another, as along a ring; 7: all, as "
                         "pulls from every peer over a full mesh)")
-    p.add_argument("--kslices", type=int, default=4,
+    p.add_argument("--kslices", type=int, default=2,
                    help="K-slices per copied chunk (1: whole chunks; >1: slice 0 of every chunk first, tiles start "
                         "on it and wait in-kernel for the later slices)")
+    p.add_argument("--lead", type=int, default=1,
+                   help="CU backend with K-slices: leading slices of each chunk copied by the compute workgroups "
+                        "whose first tile reads it (0: the copy workgroups move every slice)")
     p.add_argument("--copy-store", default="plain", choices=["plain", "stream"],
                    help="loads and stores of the copy role: plain or non-temporal (stream)")
     p.add_argument("--cache", default="cold", choices=["cold", "warm"],
@@ -249,7 +258,7 @@ def main(argv=None):
     if args.tune:
         tuned = tune(args)
         args.split, args.tile = tuned["split"], f'{tuned["tile_m"]}x{tuned["tile_n"]}'
-        args.backend, args.teams, args.kslices = TUNE_AGENTS[tuned["agent"]][1:]
+        args.backend, args.teams, args.kslices, args.lead = TUNE_AGENTS[tuned["agent"]][1:]
     tm, tn = (int(x) for x in args.tile.split("x"))
     order = ORDERS[args.order]
     c_dtype = A.SYNC_DTYPE_F32 if args.c_dtype == "f32" else A.SYNC_DTYPE_BF16
@@ -269,7 +278,7 @@ def main(argv=None):
     c_out = torch.empty((M, N), dtype=torch.float32 if c_dtype == A.SYNC_DTYPE_F32 else torch.int16, device=dev)
     ws = workspace(plan, torch)
 
-    agent = agent_for(args.backend, args.teams, args.kslices)
+    agent = agent_for(args.backend, args.teams, args.kslices, args.lead)
     agent["copy_streaming"] = 1 if args.copy_store == "stream" else 0
 
     def ag_call(c_cfg, pl=plan, w=ws):
@@ -324,7 +333,8 @@ def main(argv=None):
                         "8 row chunks (N(0,1)/64), B 4096x1792 bf16, C 8192x1792 " + args.c_dtype,
             "m": M, "n": N, "k": K, "world": WORLD, "split": args.split, "tile": args.tile,
             "tile_order": args.order, "copy_backend": args.backend, "copy_teams": args.teams,
-            "copy_kslices": args.kslices, "copy_store": args.copy_store, "b_layout": args.layout,
+            "copy_kslices": args.kslices, "copy_lead_slices": agent.get("copy_lead_slice", 0),
+            "copy_store": args.copy_store, "b_layout": args.layout,
             "cache": args.cache,
             "timing": "value = 2MNK / mean per-call duration; each call bracketed by device events on its launch "
                       "stream" + ("; 512 MiB written between calls, outside the events" if cold else
@@ -619,7 +629,7 @@ def tune(args):
     dev = torch.device("cuda:0")
     b_layout = A.SYNC_B_NK if args.layout == "nk" else A.SYNC_B_KN
     base = A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, b_layout=b_layout)
-    agents = [A.make_cfg(**agent_for(be, teams, ks)) for _, be, teams, ks in TUNE_AGENTS]
+    agents = [A.make_cfg(**agent_for(be, teams, ks, ld)) for _, be, teams, ks, ld in TUNE_AGENTS]
     space = A.make_tune_space(splits=(1, 2, 4), tiles=((256, 256), (256, 128)), orders=(A.SYNC_ORDER_CHUNK_MAJOR,),
                               copy_cus=(), agents=agents, warmup=2, iters=5)
     a_bits, b_bits = inputs.gemm_operands(M, N, K, DIVISOR, b_layout=args.layout)

@@ -78,7 +78,8 @@ class sync_copy_cfg(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("copy_cus", ctypes.c_int32), ("timeout_ns", ctypes.c_uint64),
                 ("host_gates", ctypes.c_void_p), ("flags", ctypes.c_int32), ("copy_streaming", ctypes.c_int32),
                 ("withhold_chunk", ctypes.c_int32), ("copy_teams", ctypes.c_int32),
-                ("copy_kslices", ctypes.c_int32), ("copy_link_gbps", ctypes.c_float)]
+                ("copy_kslices", ctypes.c_int32), ("copy_link_gbps", ctypes.c_float),
+                ("copy_lead_slice", ctypes.c_int32)]
 
 
 class sync_trace(ctypes.Structure):
@@ -280,11 +281,11 @@ def sync_plan_export(plan: Plan) -> dict:
 
 def make_cfg(backend: int = SYNC_COPY_SDMA, copy_cus: int = 0, timeout_ns: int = 0, host_gates=None,
              flags: int = 0, copy_streaming: int = 0, withhold_chunk: int = -1, copy_teams: int = 0,
-             copy_kslices: int = 0, copy_link_gbps: float = 0.0) -> sync_copy_cfg:
+             copy_kslices: int = 0, copy_link_gbps: float = 0.0, copy_lead_slice: int = 0) -> sync_copy_cfg:
     c = sync_copy_cfg()
     c.backend, c.copy_cus, c.timeout_ns, c.flags = backend, copy_cus, timeout_ns, flags
     c.copy_streaming, c.withhold_chunk, c.copy_teams = copy_streaming, withhold_chunk, copy_teams
-    c.copy_kslices, c.copy_link_gbps = copy_kslices, copy_link_gbps
+    c.copy_kslices, c.copy_link_gbps, c.copy_lead_slice = copy_kslices, copy_link_gbps, copy_lead_slice
     c.host_gates = _ptr(host_gates)
     return c
 

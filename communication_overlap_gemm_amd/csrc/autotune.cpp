@@ -84,7 +84,7 @@ std::string cache_key(const sync_plan_desc& b, const sync_tune_space& sp, int32_
     for (int32_t i = 0; i < sp.n_agents; ++i) {
       const sync_copy_cfg& c = sp.agents[i];
       k << (i ? ";" : "") << c.backend << ',' << c.copy_cus << ',' << c.copy_teams << ',' << c.copy_kslices << ','
-        << c.copy_streaming << ',' << c.copy_link_gbps;
+        << c.copy_streaming << ',' << c.copy_link_gbps << ',' << c.copy_lead_slice;
     }
     k << "]";
   }

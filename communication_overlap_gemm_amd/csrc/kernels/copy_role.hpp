@@ -119,6 +119,24 @@ __device__ __forceinline__ void copy_block(const char* __restrict__ src, char* _
   }
 }
 
+// Thread 0 of a workgroup that has copied (and released) its share of slice h
+// of chunk c, rank-th of `count`: the completer of the slice's count raises
+// the slice flag, and the completer of the chunk's last slice raises the chunk
+// flag (counted with acquire-release, so it sees the others' publications)
+// and clears the count.
+__device__ __forceinline__ void slice_done(const CopyArgs& a, int32_t c, int32_t h, int32_t S, int32_t rank,
+                                           int32_t count, uint32_t epoch) {
+  const int32_t sl = c * kMaxSlices + h;
+  if (!tree_count(a.sxparts + sl * kMaxXcd, a.sparts + sl, rank, count)) return;
+  st_release_agent(a.slice_flags + sl, epoch);
+  const uint32_t done = __hip_atomic_fetch_add(a.parts + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  if (done == static_cast<uint32_t>(S)) {
+    st_relaxed_agent(a.parts + c, 0u);
+    if (a.trace_chunks) a.trace_chunks[2 * c] = wall_clock64();
+    st_release_agent(a.out_flags + c, epoch);
+  }
+}
+
 // Publication.  A chunk is complete when every copy workgroup's stores of it
 // are visible device-wide.  Each workgroup drains its stores into its XCD's L2
 // (workgroup-scope release = wait for the stores), writes that L2 back with an
@@ -190,6 +208,7 @@ __device__ __forceinline__ void copy_role(const CopyArgs& a, int32_t rank, int32
     for (int32_t p = 0; p < a.num_chunks; ++p) {
       const int32_t c = a.arrival[p];
       if (skipped(c)) continue;
+      if (h < a.lead_slices && a.lead_count && a.lead_count[c] > 0) continue;  // the compute workgroups copy it
       if (++seq % teams != team) continue;
       if (a.copy_out) {
         if (threadIdx.x == 0) {
@@ -247,23 +266,40 @@ __device__ __forceinline__ void copy_role(const CopyArgs& a, int32_t rank, int32
             st_release_agent(a.out_flags + c, epoch);
           }
         } else {
-          const int32_t sl = c * kMaxSlices + h;
-          if (tree_count(a.sxparts + sl * kMaxXcd, a.sparts + sl, trank, tcount)) {
-            st_release_agent(a.slice_flags + sl, epoch);
-            // the chunk is whole once all its slices are: the completer of
-            // the last one (counted with acquire-release, so it sees the
-            // others' publications) raises the chunk flag and clears the count
-            const uint32_t done =
-                __hip_atomic_fetch_add(a.parts + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-            if (done == static_cast<uint32_t>(S)) {
-              st_relaxed_agent(a.parts + c, 0u);
-              if (a.trace_chunks) a.trace_chunks[2 * c] = wall_clock64();
-              st_release_agent(a.out_flags + c, epoch);
-            }
-          }
+          slice_done(a, c, h, S, trank, tcount, epoch);
         }
       }
     }
+}
+
+// Lead slices of a K-sliced copy-in, run by compute workgroup g before its
+// first tile: for each (chunk c, share rank) of its lead items, copy share
+// rank of lead_count[c] of the first lead_slices slices of chunk c's rows (the
+// first floor(L lines / S) 128-byte columns of each row, L = lead_slices),
+// then publish each of those slices with the other workgroups of the share
+// group.  The shares of one chunk are held by the workgroups whose first tile
+// reads it, which all start together.
+template <int THREADS>
+__device__ __forceinline__ void lead_slice(const CopyArgs& a, const int32_t* lead_ptr, const int32_t* lead_item,
+                                           int32_t g, uint32_t epoch) {
+  const int32_t S = a.kslices, L = a.lead_slices;
+  for (int32_t e = lead_ptr[g]; e < lead_ptr[g + 1]; ++e) {
+    const int32_t c = lead_item[2 * e], rank = lead_item[2 * e + 1], count = a.lead_count[c];
+    const int64_t r0 = a.chunk_begin[c], r1 = a.chunk_begin[c + 1], rb = a.row_bytes[0];
+    const int64_t seg = L * (rb / 128) / S * 128;  // slices [0, L): the columns before slice L's first
+    const int64_t granules = (r1 - r0) * (seg / 16);
+    const int64_t lo = granules * rank / count, hi = granules * (rank + 1) / count;
+    if (a.streaming)
+      copy_block<THREADS, true>(a.src[0] + r0 * rb, a.dst[0] + r0 * rb, rb, 0, seg, lo, hi);
+    else
+      copy_block<THREADS, false>(a.src[0] + r0 * rb, a.dst[0] + r0 * rb, rb, 0, seg, lo, hi);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      release_agent();  // write this XCD's L2 back
+      for (int32_t h = 0; h < L; ++h) slice_done(a, c, h, S, rank, count, epoch);
+    }
+  }
 }
 
 }  // namespace syncov

@@ -645,6 +645,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
     else
       copy_role<THREADS, true>(a.copy, gb, gn, epoch);  // one publication for all chunks
   }
+  if constexpr (!RS) {
+    if (a.lead_ptr) lead_slice<THREADS>(a.copy, a.lead_ptr, a.lead_item, gb, epoch);  // slice 0 of the first tile's chunk
+  }
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
   for (int32_t p = slot0; p < a.num_tiles; p += gn) {
     const int32_t t = a.order[p];

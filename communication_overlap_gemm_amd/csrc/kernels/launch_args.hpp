@@ -55,6 +55,12 @@ struct CopyArgs {
   uint32_t* slice_flags;
   uint32_t* sparts;
   uint32_t* sxparts;
+  // K-sliced copy-in with lead slices: chunks with lead_count[c] > 0 have
+  // their first lead_slices slices copied by compute workgroups (GemmArgs
+  // lead tables); the copy role leaves those items out.  Null: the copy role
+  // moves every item.
+  const int32_t* lead_count;
+  int32_t lead_slices;
 };
 
 // Persistent GEMM (gemm_persistent.hip).  Workgroups [0, copy_blocks) of the
@@ -105,6 +111,12 @@ struct GemmArgs {
   const char* ar_src[2];
   char* ar_out;
   int64_t ar_row_bytes;
+  // AG with a K-sliced copy and lead slices (lead_ptr non-null): compute
+  // workgroup g first copies share lead_item[2 e + 1] of copy.lead_count[c] of
+  // the lead slices of chunk c = lead_item[2 e], for e in [lead_ptr[g],
+  // lead_ptr[g + 1]), and publishes them with the others of that share group
+  const int32_t* lead_ptr;
+  const int32_t* lead_item;
   CopyArgs copy;
 };
 

@@ -175,6 +175,15 @@ struct DeviceTables {
   void* block = nullptr;  // one allocation holding all of the above
 };
 
+// Lead-slice tables of an AG plan for one launch shape (see GemmArgs):
+// lead_ptr[gn + 1], lead_item[2 x items], lead_count[C], one device block.
+struct LeadTables {
+  int32_t* lead_ptr = nullptr;
+  int32_t* lead_item = nullptr;
+  int32_t* lead_count = nullptr;
+  void* block = nullptr;
+};
+
 struct sync_plan_s {
   Plan plan;
   std::vector<int64_t> slot_row;   // staging row of each send position (C+1)
@@ -182,6 +191,8 @@ struct sync_plan_s {
   std::vector<int64_t> ar_items;   // GEMM-RS: GEMM-AR all-gather items, 5 per item (see GemmArgs)
   std::mutex mu;
   std::map<int, DeviceTables> dev;
+  // (device, compute workgroups, XCDs, withheld chunk) -> lead-slice tables
+  std::map<std::tuple<int, int, int, int>, LeadTables> lead;
 };
 
 namespace {
@@ -242,6 +253,62 @@ int resident_tables(sync_plan_s* p, int dev, DeviceTables** out) {
     return fail(SYNC_EINVAL, "the plan's tables are not on this device yet: call sync_workspace_init or a launch "
                              "call with this plan on the device first");
   *out = &it->second;
+  return SYNC_OK;
+}
+
+// Host twin of the kernels' xcd_slot: the traversal position compute
+// workgroup b of g takes first.
+int32_t first_slot(int32_t b, int32_t g, int32_t nxcd) {
+  if (nxcd <= 1 || g % nxcd) return b;
+  return (b % nxcd) * (g / nxcd) + b / nxcd;
+}
+
+// Lead-slice tables for a launch with gn compute workgroups: workgroup g's
+// first tile is order[first_slot(g)]; for every non-resident, non-withheld
+// chunk it reads, g takes the next share of that chunk's slice 0.  Built once
+// per (plan, device, gn, XCDs, withheld chunk) and kept with the plan.
+int lead_tables(sync_plan_s* p, int dev, int32_t gn, int32_t nxcd, int32_t withheld, LeadTables** out) {
+  std::lock_guard<std::mutex> lk(p->mu);
+  const auto key = std::make_tuple(dev, gn, nxcd, withheld);
+  auto it = p->lead.find(key);
+  if (it != p->lead.end()) {
+    *out = &it->second;
+    return SYNC_OK;
+  }
+  const Plan& pl = p->plan;
+  std::vector<int32_t> ptr(static_cast<size_t>(gn) + 1, 0), item, count(static_cast<size_t>(pl.num_chunks), 0);
+  for (int32_t g = 0; g < gn; ++g) {
+    const int32_t pos = first_slot(g, gn, nxcd);
+    if (pos < pl.num_tiles) {
+      const int32_t t = pl.tile_order[pos];
+      for (int64_t e = pl.dep_ptr[t]; e < pl.dep_ptr[t + 1]; ++e) {
+        const int32_t c = pl.dep_idx[e];
+        if (pl.resident[c] || c == withheld || withheld == -1) continue;
+        item.push_back(c);
+        item.push_back(count[c]++);
+      }
+    }
+    ptr[g + 1] = static_cast<int32_t>(item.size() / 2);
+  }
+  const int64_t n0 = align_up(static_cast<int64_t>(ptr.size()) * 4, 256);
+  const int64_t n1 = align_up(static_cast<int64_t>(std::max<size_t>(item.size(), 1)) * 4, 256);
+  const int64_t n2 = align_up(static_cast<int64_t>(count.size()) * 4, 256);
+  std::vector<char> host(static_cast<size_t>(n0 + n1 + n2), 0);
+  std::memcpy(host.data(), ptr.data(), ptr.size() * 4);
+  if (!item.empty()) std::memcpy(host.data() + n0, item.data(), item.size() * 4);
+  std::memcpy(host.data() + n0 + n1, count.data(), count.size() * 4);
+  LeadTables t;
+  HIP_TRY(hipMalloc(&t.block, host.size()));
+  hipError_t e = hipMemcpy(t.block, host.data(), host.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(t.block);
+    return hip_fail(e, "hipMemcpy(lead tables)");
+  }
+  char* b = static_cast<char*>(t.block);
+  t.lead_ptr = reinterpret_cast<int32_t*>(b);
+  t.lead_item = reinterpret_cast<int32_t*>(b + n0);
+  t.lead_count = reinterpret_cast<int32_t*>(b + n0 + n1);
+  *out = &p->lead.emplace(key, t).first->second;
   return SYNC_OK;
 }
 
@@ -323,6 +390,13 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs K/64 >= 4 x copy_kslices");
   }
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
+  if (cfg.copy_lead_slice < 0 || (cfg.copy_lead_slice > 0 && cfg.copy_lead_slice >= cfg.copy_kslices))
+    return fail(SYNC_EINVAL, "copy_lead_slice must be in [0, copy_kslices)");
+  if (cfg.copy_lead_slice &&
+      (op != SYNC_OP_AG_GEMM || cfg.backend != SYNC_COPY_CU || cfg.copy_link_gbps != 0.f ||
+       (cfg.flags & SYNC_RUN_COPY_ONLY)))
+    return fail(SYNC_EINVAL, "copy_lead_slice is for AG-GEMM with the CU backend, copy_kslices > 1, no pacing and "
+                             "no COPY_ONLY");
   if (cfg.copy_link_gbps != 0.f) {
     if (!(cfg.copy_link_gbps >= 1.f && cfg.copy_link_gbps <= 10000.f))
       return fail(SYNC_EINVAL, "copy_link_gbps must be 0 or in [1, 10000]");
@@ -676,6 +750,10 @@ void sync_plan_destroy(sync_plan_t plan) {
     if (have) (void)hipSetDevice(kv.first);
     (void)hipFree(kv.second.block);
   }
+  for (auto& kv : plan->lead) {
+    if (have) (void)hipSetDevice(std::get<0>(kv.first));
+    (void)hipFree(kv.second.block);
+  }
   if (have) (void)hipSetDevice(cur);
   delete plan;
 }
@@ -790,12 +868,13 @@ int sync_workspace_status(const void* ws, void* stream, int32_t* err_chunk) {
 static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a_local, const void* b,
                         void* c, int32_t c_dtype, void* ws, void* compute, bool noalloc) {
   CallCtx cx;
-  if (noalloc) {  // nothing that allocates: no SDMA signals, no timing events, no trace
+  if (noalloc) {  // nothing that allocates: no SDMA signals, no timing events, no trace, no lead tables
     const int32_t backend = cfg ? cfg->backend : SYNC_COPY_SDMA;
     if (backend != SYNC_COPY_PRESET && backend != SYNC_COPY_CU && backend != SYNC_COPY_COLOCATED)
       return fail(SYNC_EUNSUPPORTED, "sync_ag_gemm_noalloc runs the PRESET, CU and COLOCATED backends");
     if (cfg->flags & (SYNC_RUN_TIMED | SYNC_RUN_TRACE))
       return fail(SYNC_EUNSUPPORTED, "sync_ag_gemm_noalloc takes no TIMED or TRACE mode");
+    if (cfg->copy_lead_slice) return fail(SYNC_EUNSUPPORTED, "sync_ag_gemm_noalloc takes no copy_lead_slice");
   }
   int rc = prepare(plan, cfg, ws, SYNC_OP_AG_GEMM, cx, noalloc);
   if (rc) return rc;
@@ -825,6 +904,15 @@ static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
   g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
   const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  if (cx.cfg.copy_lead_slice && r.wait && r.grid > r.copy_blocks) {
+    const int32_t withheld = (cx.cfg.flags & SYNC_RUN_WITHHOLD) ? cx.cfg.withhold_chunk : -2;
+    LeadTables* lt = nullptr;
+    if ((rc = lead_tables(plan, d.device, r.grid - r.copy_blocks, d.num_xcds, withheld, &lt))) return rc;
+    g.lead_ptr = lt->lead_ptr;
+    g.lead_item = lt->lead_item;
+    g.copy.lead_count = lt->lead_count;
+    g.copy.lead_slices = cx.cfg.copy_lead_slice;
+  }
   return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), r, src, dst, rb, 1,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     g.copy_blocks = rr.copy_blocks;

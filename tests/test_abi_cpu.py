@@ -191,3 +191,19 @@ def test_binding_checks_tensor_sizes():
     with pytest.raises(A.SyncError) as ei:  # fp32 C needs 4-byte elements
         A.sync_ag_gemm(p, None, None, 0x1000, 0x1000, FakeDev(256 * 128, 2), A.SYNC_DTYPE_F32, 0x1000)
     assert "c must have 4-byte" in ei.value.message
+
+
+def test_lead_slice_validation():
+    """copy_lead_slice: in [0, copy_kslices), and only for AG-GEMM with the CU
+    backend, K-slices, no pacing and a compute part."""
+    def rc_of(plan, cfg):
+        return A.lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg), None, None, None, None, 0, 256, None, None)
+    p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    for bad in (A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=2),
+                A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=4, copy_lead_slice=-1),
+                A.make_cfg(A.SYNC_COPY_CU, 8, copy_lead_slice=1),
+                A.make_cfg(A.SYNC_COPY_COLOCATED, copy_kslices=2, copy_lead_slice=1),
+                A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=1, copy_link_gbps=100.0),
+                A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=1, flags=A.SYNC_RUN_COPY_ONLY)):
+        assert rc_of(p, bad) == A.SYNC_EINVAL
+        assert "copy_lead_slice" in A.sync_last_error()

@@ -39,6 +39,6 @@ def test_profiled_configuration_is_the_default():
 def test_traffic_only_for_the_profiled_configuration():
     t = bench.profiled_traffic(_args())
     assert t is None or (isinstance(t, int) and t > 0)  # None once the kernel sources change
-    for argv in (["--tile", "256x128"], ["--split", "2"], ["--backend", "cu16"], ["--kslices", "2"],
+    for argv in (["--tile", "256x128"], ["--split", "2"], ["--backend", "cu16"], ["--kslices", "4"], ["--lead", "0"],
                  ["--c-dtype", "bf16"], ["--layout", "kn"], ["--teams", "1"], ["--copy-store", "stream"]):
         assert bench.profiled_traffic(_args(*argv)) is None, argv

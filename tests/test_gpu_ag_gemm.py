@@ -24,10 +24,10 @@ LAYOUT = {"kn": A.SYNC_B_KN, "nk": A.SYNC_B_NK}
 
 def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128), order=A.SYNC_ORDER_CHUNK_MAJOR,
            backend=A.SYNC_COPY_SDMA, copy_cus=0, c_dtype=A.SYNC_DTYPE_F32, rank=0, poison=True, flags=0, teams=0,
-           kslices=0, streaming=0, calls=1):
+           kslices=0, streaming=0, calls=1, lead=0):
     print(f"[ag] m={m} n={n} k={k} W={world} split={split} tile={tile} order={order} backend={backend} "
-          f"cus={copy_cus} dtype={c_dtype} layout={layout} teams={teams} kslices={kslices} streaming={streaming}",
-          flush=True)
+          f"cus={copy_cus} dtype={c_dtype} layout={layout} teams={teams} kslices={kslices} streaming={streaming} "
+          f"lead={lead}", flush=True)
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, rank=rank, split=split, tile_m=tile[0],
                                    tile_n=tile[1], tile_order=order, b_layout=LAYOUT[layout]))
     tabs = A.sync_plan_export(plan)
@@ -47,7 +47,7 @@ def run_ag(m, n, k, world, a_bits, b_bits, layout="kn", split=1, tile=(128, 128)
         c = bf16_poison((m, n))
     ws = workspace(plan)
     cfg = A.make_cfg(backend, copy_cus=copy_cus, flags=flags, copy_teams=teams, copy_kslices=kslices,
-                     copy_streaming=streaming)
+                     copy_streaming=streaming, copy_lead_slice=lead)
     s = torch.cuda.current_stream()
     for call in range(calls):  # calls > 1: the same workspace again, copied rows and C poisoned in between
         if call:
@@ -423,11 +423,13 @@ def test_full_size_70b_like(split, teams):
 
 # ---- K-sliced copy-in: chunks move as column slices, tiles start on slice 0 --
 
-@pytest.mark.parametrize("backend,cus,teams,kslices,tile", [
-    (A.SYNC_COPY_CU, 8, 1, 2, (256, 256)), (A.SYNC_COPY_CU, 16, 3, 4, (256, 128)),
-    (A.SYNC_COPY_CU, 8, 5, 3, (128, 128)), (A.SYNC_COPY_COLOCATED, 0, 3, 4, (256, 256)),
-    (A.SYNC_COPY_COLOCATED, 0, 1, 2, (256, 256))])
-def test_kslices_parity(backend, cus, teams, kslices, tile):
+@pytest.mark.parametrize("backend,cus,teams,kslices,tile,lead", [
+    (A.SYNC_COPY_CU, 8, 1, 2, (256, 256), 0), (A.SYNC_COPY_CU, 16, 3, 4, (256, 128), 0),
+    (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 0), (A.SYNC_COPY_COLOCATED, 0, 3, 4, (256, 256), 0),
+    (A.SYNC_COPY_COLOCATED, 0, 1, 2, (256, 256), 0), (A.SYNC_COPY_CU, 8, 1, 2, (256, 256), 1),
+    (A.SYNC_COPY_CU, 16, 3, 4, (256, 128), 1), (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 1),
+    (A.SYNC_COPY_CU, 16, 3, 4, (256, 256), 2), (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 2)])
+def test_kslices_parity(backend, cus, teams, kslices, tile, lead):
     """K = 1152 (18 K-steps: uneven slices); the output matches the oracle and
     is bitwise the compute-only output (the copy protocol changes only when
     a K-step's operands are known to be in place)."""
@@ -435,16 +437,18 @@ def test_kslices_parity(backend, cus, teams, kslices, tile):
     a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
     ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
     out, a_local = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=backend,
-                          copy_cus=cus, teams=teams, kslices=kslices)
+                          copy_cus=cus, teams=teams, kslices=kslices, lead=lead)
     check_f32(out, ref, world)
     assert np.array_equal(a_local, a)  # every slice of every chunk was staged
     base, _ = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=A.SYNC_COPY_PRESET)
     assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
 
 
-@pytest.mark.parametrize("cus,teams,kslices,tile,rank", [
-    (8, 1, 2, (256, 256), 0), (32, 7, 4, (256, 256), 1), (16, 3, 4, (256, 128), 2), (8, 5, 3, (128, 128), 3)])
-def test_kslices_repeated_calls(cus, teams, kslices, tile, rank):
+@pytest.mark.parametrize("cus,teams,kslices,tile,rank,lead", [
+    (8, 1, 2, (256, 256), 0, 0), (32, 7, 4, (256, 256), 1, 0), (16, 3, 4, (256, 128), 2, 0),
+    (8, 5, 3, (128, 128), 3, 0), (32, 7, 4, (256, 256), 1, 1), (8, 5, 3, (128, 128), 3, 1),
+    (32, 7, 4, (256, 256), 2, 2)])
+def test_kslices_repeated_calls(cus, teams, kslices, tile, rank, lead):
     """Three K-sliced calls on one workspace, the copied rows and C poisoned
     before each: the slice and chunk counters each call leaves cleared let the
     next one stage every slice again and match the oracle, bitwise the
@@ -453,7 +457,7 @@ def test_kslices_repeated_calls(cus, teams, kslices, tile, rank):
     a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
     ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
     out, a_local = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=A.SYNC_COPY_CU,
-                          copy_cus=cus, teams=teams, kslices=kslices, rank=rank, calls=3)
+                          copy_cus=cus, teams=teams, kslices=kslices, rank=rank, calls=3, lead=lead)
     check_f32(out, ref, world)
     assert np.array_equal(a_local, a)
     base, _ = run_ag(m, n, k, world, a, b, layout="nk", split=split, tile=tile, backend=A.SYNC_COPY_PRESET,
@@ -461,10 +465,12 @@ def test_kslices_repeated_calls(cus, teams, kslices, tile, rank):
     assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
 
 
-def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles():
-    """A withheld chunk under a K-sliced copy: none of its slices land, the
-    tiles that read it stay unwritten, the others are correct, and the timeout
-    names the chunk (not a slice)."""
+@pytest.mark.parametrize("lead", [0, 1])
+def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles(lead):
+    """A withheld chunk under a K-sliced copy (with or without the lead slice
+    copied by the compute workgroups): none of its slices land, the tiles that
+    read it stay unwritten, the others are correct, and the timeout names the
+    chunk (not a slice)."""
     m, n, k, world, split = 1024, 512, 512, 4, 2
     a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
     ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
@@ -483,7 +489,7 @@ def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles():
     ws = workspace(plan)
     s = torch.cuda.current_stream()
     cfg = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, timeout_ns=2_000_000, flags=A.SYNC_RUN_WITHHOLD,
-                     withhold_chunk=victim, copy_teams=3, copy_kslices=2)
+                     withhold_chunk=victim, copy_teams=3, copy_kslices=2, copy_lead_slice=lead)
     print(f"[ag] kslices=2 withhold chunk {victim}", flush=True)
     A.sync_ag_gemm(plan, cfg, a_peer, a_local, b_d, c, A.SYNC_DTYPE_F32, ws, s, None)
     rc, chunk = A.sync_workspace_status(ws, s)
@@ -501,14 +507,17 @@ def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles():
             assert np.isfinite(blk).all() and np.linalg.norm(blk - r) <= 1e-3 * np.linalg.norm(r), f"tile {t}"
 
 
-@pytest.mark.parametrize("backend,cus,teams,kslices", [(A.SYNC_COPY_CU, 32, 7, 4), (A.SYNC_COPY_CU, 32, 7, 8),
-                                                       (A.SYNC_COPY_COLOCATED, 0, 7, 4)])
-def test_full_size_kslices(cfg2_data, backend, cus, teams, kslices):
+@pytest.mark.parametrize("backend,cus,teams,kslices,lead", [(A.SYNC_COPY_CU, 32, 7, 4, 0), (A.SYNC_COPY_CU, 32, 7, 8, 0),
+                                                            (A.SYNC_COPY_COLOCATED, 0, 7, 4, 0),
+                                                            (A.SYNC_COPY_CU, 32, 7, 4, 1), (A.SYNC_COPY_CU, 32, 7, 8, 1),
+                                                            (A.SYNC_COPY_CU, 32, 7, 4, 2), (A.SYNC_COPY_CU, 32, 7, 8, 3)])
+def test_full_size_kslices(cfg2_data, backend, cus, teams, kslices, lead):
     """The Llama-3-8B up-projection share with a K-sliced copy: every output
     element against the oracle."""
     a, b_kn, ref, absab = cfg2_data
-    out, _ = run_ag(M2, N2, K2, W2, a, _b_for(b_kn, "nk"), tile=(256, 256), backend=backend, copy_cus=cus,
-                    layout="nk", teams=teams, kslices=kslices)
+    out, a_local = run_ag(M2, N2, K2, W2, a, _b_for(b_kn, "nk"), tile=(256, 256), backend=backend, copy_cus=cus,
+                          layout="nk", teams=teams, kslices=kslices, lead=lead)
+    assert np.array_equal(a_local, a)
     check_full_f32(out, ref, absab, K2, W2)
 
 

@@ -33,7 +33,7 @@ M2, N2, K2, W2 = bench.M, bench.N, bench.K, bench.WORLD
 
 def _ag_kwargs(ag):
     return dict(backend=ag["backend"], copy_cus=ag.get("copy_cus", 0), teams=ag.get("copy_teams", 0),
-                kslices=ag.get("copy_kslices", 0))
+                kslices=ag.get("copy_kslices", 0), lead=ag.get("copy_lead_slice", 0))
 
 
 def _paced(ag):
