@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libsync_overlap.so")
 # ---- constants (mirror sync_overlap.h) ------------------------------------
 SYNC_OK, SYNC_EINVAL, SYNC_EUNSUPPORTED, SYNC_EHIP, SYNC_ETIMEOUT, SYNC_ENOMEM, SYNC_ENODEV = 0, -1, -2, -3, -4, -5, -6
 SYNC_OP_AG_GEMM, SYNC_OP_GEMM_RS, SYNC_OP_RING_ATTN = 1, 2, 3
-SYNC_PAT_RING, SYNC_PAT_EXPLICIT = 0, 1
+SYNC_PAT_RING, SYNC_PAT_EXPLICIT, SYNC_PAT_HIER_SWIZZLE, SYNC_PAT_MESH = 0, 1, 2, 3
 SYNC_ORDER_ROW_MAJOR, SYNC_ORDER_CHUNK_MAJOR, SYNC_ORDER_SWIZZLED = 0, 1, 2
 SYNC_B_KN, SYNC_B_NK = 0, 1
 SYNC_DTYPE_F32, SYNC_DTYPE_BF16 = 0, 1
@@ -55,7 +55,8 @@ class sync_plan_desc(ctypes.Structure):
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_order", ctypes.c_int32),
         ("group_m", ctypes.c_int32), ("local_resident", ctypes.c_int32),
         ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("b_layout", ctypes.c_int32),
-        ("shard_rows", ctypes.POINTER(ctypes.c_int64)), ("reserved", ctypes.c_int32 * 2),
+        ("shard_rows", ctypes.POINTER(ctypes.c_int64)), ("hier_group", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 
@@ -233,11 +234,12 @@ def make_desc(op: int, m: int, n: int, k: int, world: int, rank: int = 0, ring_d
               pattern: int = SYNC_PAT_RING, explicit_order: Optional[Sequence[int]] = None, split: int = 1,
               tile_m: int = 256, tile_n: int = 256, tile_order: int = SYNC_ORDER_CHUNK_MAJOR, group_m: int = 0,
               local_resident: int = 1, heads_q: int = 0, heads_kv: int = 0, b_layout: int = SYNC_B_KN,
-              shard_rows: Optional[Sequence[int]] = None):
+              shard_rows: Optional[Sequence[int]] = None, hier_group: int = 0):
     d = sync_plan_desc()
     d.op, d.m, d.n, d.k, d.world, d.rank, d.ring_dir = op, m, n, k, world, rank, ring_dir
     d.pattern, d.split, d.tile_m, d.tile_n, d.tile_order = pattern, split, tile_m, tile_n, tile_order
     d.group_m, d.local_resident, d.heads_q, d.heads_kv, d.b_layout = group_m, local_resident, heads_q, heads_kv, b_layout
+    d.hier_group = hier_group
     if explicit_order is not None:
         arr = (ctypes.c_int32 * len(explicit_order))(*explicit_order)
         d.explicit_order = ctypes.cast(arr, _P32)

@@ -76,7 +76,7 @@ std::string cache_key(const sync_plan_desc& b, const sync_tune_space& sp, int32_
   std::ostringstream k;
   k << di.arch << '/' << di.num_cus << " op" << b.op << " m" << b.m << " n" << b.n << " k" << b.k << " W" << b.world
     << " r" << b.rank << " d" << b.ring_dir << " pat" << b.pattern << " res" << b.local_resident << " B"
-    << b.b_layout << " g" << b.group_m << " C" << c_dtype << " S[" << list_str(sp.splits, sp.n_splits) << "] T["
+    << b.b_layout << " g" << b.group_m << " h" << b.hier_group << " C" << c_dtype << " S[" << list_str(sp.splits, sp.n_splits) << "] T["
     << list_str(sp.tiles, 2 * sp.n_tiles) << "] O[" << list_str(sp.orders, sp.n_orders) << "] U["
     << list_str(sp.copy_cus, sp.n_copy_cus) << "]";
   if (sp.n_agents > 0) {

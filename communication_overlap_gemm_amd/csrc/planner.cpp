@@ -32,8 +32,7 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
   if (d.tile_m < 1) { err = "tile_m must be positive"; return false; }
   if (d.tile_order < SYNC_ORDER_ROW_MAJOR || d.tile_order > SYNC_ORDER_SWIZZLED) { err = "bad tile_order"; return false; }
   if (d.group_m < 0) { err = "group_m must be >= 0"; return false; }
-  for (int i = 0; i < 2; ++i)
-    if (d.reserved[i]) { err = "reserved fields must be zero"; return false; }
+  if (d.reserved[0]) { err = "reserved fields must be zero"; return false; }
   p.desc.shard_rows = nullptr;
   const int32_t W = d.world, s = d.split;
   const int64_t G = d.group_m > 0 ? d.group_m : 4;
@@ -69,7 +68,11 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
 
   // shard consumed (AG, attention) or sent (RS) at each ring step
   std::vector<int32_t> step_shard(W);
-  if (d.pattern == SYNC_PAT_RING) {
+  if ((d.pattern == SYNC_PAT_HIER_SWIZZLE) != (d.hier_group != 0)) {
+    err = "hier_group is set exactly for the hierarchical swizzle pattern";
+    return false;
+  }
+  if (d.pattern == SYNC_PAT_RING || d.pattern == SYNC_PAT_MESH) {
     for (int32_t st = 0; st < W; ++st)
       step_shard[st] = wrap(static_cast<int64_t>(d.rank) - static_cast<int64_t>(d.ring_dir) * (rs ? st + 1 : st), W);
   } else if (d.pattern == SYNC_PAT_EXPLICIT) {
@@ -82,6 +85,18 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
       step_shard[st] = w;
     }
     p.explicit_order = step_shard;
+  } else if (d.pattern == SYNC_PAT_HIER_SWIZZLE) {
+    // groups of g consecutive ranks: own group first, then each group in
+    // turn; inside a group, start at this rank's local index (at every step
+    // the ranks of a group pull from distinct peers).  RS: reversed.
+    const int32_t g = d.hier_group;
+    if (g < 1 || W % g) { err = "hier_group must divide world"; return false; }
+    const int32_t groups = W / g, my_group = d.rank / g, my_local = d.rank % g;
+    for (int32_t a = 0; a < groups; ++a)
+      for (int32_t b = 0; b < g; ++b) {
+        const int32_t st = a * g + b, w = ((my_group + a) % groups) * g + (my_local + b) % g;
+        step_shard[rs ? W - 1 - st : st] = w;
+      }
   } else {
     err = "bad pattern";
     return false;
@@ -99,7 +114,9 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
     for (int32_t q = 0; q < s; ++q) {
       const int32_t c = w * s + q;
       p.chunk_begin[c] = base[w] + (static_cast<int64_t>(q) * rows_of[w]) / s;
-      p.chunk_pos[c] = step_of[w] * s + q;
+      // mesh: every peer's link runs at once, so sub-chunk q of every shard
+      // arrives before sub-chunk q + 1 of any (ties in ring step order)
+      p.chunk_pos[c] = d.pattern == SYNC_PAT_MESH ? q * W + step_of[w] : step_of[w] * s + q;
       p.resident[c] = (!rs && d.local_resident && w == d.rank) ? 1 : 0;
     }
   p.chunk_begin[C] = p.rows;

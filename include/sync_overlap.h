@@ -56,7 +56,7 @@ enum {
 
 /* ---- plan descriptor --------------------------------------------------- */
 enum { SYNC_OP_AG_GEMM = 1, SYNC_OP_GEMM_RS = 2, SYNC_OP_RING_ATTN = 3 };
-enum { SYNC_PAT_RING = 0, SYNC_PAT_EXPLICIT = 1 };
+enum { SYNC_PAT_RING = 0, SYNC_PAT_EXPLICIT = 1, SYNC_PAT_HIER_SWIZZLE = 2, SYNC_PAT_MESH = 3 };
 enum { SYNC_ORDER_ROW_MAJOR = 0, SYNC_ORDER_CHUNK_MAJOR = 1, SYNC_ORDER_SWIZZLED = 2 };
 enum { SYNC_B_KN = 0, SYNC_B_NK = 1 };      /* B as [k][n], or [n][k] (Linear weight) */
 enum { SYNC_DTYPE_F32 = 0, SYNC_DTYPE_BF16 = 1 };
@@ -78,6 +78,14 @@ enum { SYNC_DTYPE_F32 = 0, SYNC_DTYPE_BF16 = 1 };
  *   (step 0 is the local shard); RS: the shard sent at step s is
  *   (rank - d*(s+1)) mod world (own shard last).  EXPLICIT: explicit_order
  *   (host, `world` entries, a permutation) lists shards in that order.
+ *   HIER_SWIZZLE [SYN-S sec. 5.1 names hierarchical swizzles among the
+ *   patterns a plan expresses]: ranks form world / hier_group groups of
+ *   hier_group consecutive ranks; rank r = G*g + l takes at step a*g + b the
+ *   shard ((G + a) mod (world/g))*g + (l + b) mod g: its own group first,
+ *   then every group in turn, the ranks of a group pulling from distinct
+ *   peers at every step; RS sends in the reverse of that order (own shard
+ *   last).  MESH: the RING step order, but every peer's link runs at once:
+ *   sub-chunk q of every shard is at position q*world + step(shard).
  * Tiles: tile t = i*tiles_n + j covers C rows [i*tile_m, ..) and columns
  *   [j*tile_n, ..) (attention: work item t = i*heads_q + h).  A tile depends
  *   on every chunk its rows meet; its key is the last (AG) / first (RS)
@@ -105,7 +113,8 @@ typedef struct {
                                 holding rows [sum of the counts before w, + shard_rows[w]) (an
                                 all-to-all's receive side: peer w sends shard_rows[w] tokens) and
                                 split <= the smallest count */
-  int32_t reserved[2];    /* must be zero */
+  int32_t hier_group;     /* HIER_SWIZZLE: ranks per group, dividing world; other patterns: 0 */
+  int32_t reserved[1];    /* must be zero */
 } sync_plan_desc;
 
 typedef struct sync_plan_s* sync_plan_t;

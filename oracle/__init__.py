@@ -26,7 +26,7 @@ import numpy as np
 
 from .planner_ref import (  # noqa: F401
     OP_AG_GEMM, OP_GEMM_RS, OP_RING_ATTN, ORDER_CHUNK_MAJOR, ORDER_ROW_MAJOR, ORDER_SWIZZLED,
-    PAT_EXPLICIT, PAT_RING, PlanDesc, PlanError, PlanTables, plan_ref)
+    PAT_EXPLICIT, PAT_HIER_SWIZZLE, PAT_MESH, PAT_RING, PlanDesc, PlanError, PlanTables, plan_ref)
 from .attention import attention_online_f64  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -29,7 +29,17 @@ Reading, in the order the planner applies it:
       AG, attention:  shard_at(k) = (r - d*k) mod W        (k = 0 is local)
       RS:             shard_at(k) = (r - d*(k+1)) mod W    (own chunk last)
       explicit:       shard_at(k) = user order (a permutation)
-  pos(w*s+q) = kpos(w)*s + q with kpos = inverse of shard_at;
+      hierarchical swizzle (the summary page names the pattern, sec. 5.1, and
+      defines none; this is the reading): ranks form W/g groups of g
+      consecutive ranks; rank r = G_r*g + l_r takes at step k = a*g + b
+          AG, attention:  shard_at(k) = ((G_r + a) mod (W/g))*g + (l_r + b) mod g
+          RS:             shard_at(k) = the AG order reversed (own shard last)
+      so its own group comes first, every group in turn, and at each step the
+      ranks of a group pull from distinct peers (each (a, b) is a bijection of
+      ranks);
+      mesh: the ring's step order, but every peer's link runs at once, so
+      sub-chunk q of every shard arrives before sub-chunk q + 1 of any.
+  pos(w*s+q) = kpos(w)*s + q with kpos = inverse of shard_at (mesh: q*W + kpos(w));
   arrival[p] = the chunk whose pos is p;
   resident(c) = local_resident and w == r and op != RS.
   tiles: Tm = ceil(M/TM), Tn = ceil(N/TN), t = i*Tn + j, rows(i) = [i*TM, min((i+1)*TM, M))
@@ -46,7 +56,7 @@ from dataclasses import dataclass, field
 from typing import List, Optional
 
 OP_AG_GEMM, OP_GEMM_RS, OP_RING_ATTN = 1, 2, 3
-PAT_RING, PAT_EXPLICIT = 0, 1
+PAT_RING, PAT_EXPLICIT, PAT_HIER_SWIZZLE, PAT_MESH = 0, 1, 2, 3
 ORDER_ROW_MAJOR, ORDER_CHUNK_MAJOR, ORDER_SWIZZLED = 0, 1, 2
 DEFAULT_GROUP_M = 4
 
@@ -75,6 +85,7 @@ class PlanDesc:
     heads_q: int = 0
     heads_kv: int = 0
     shard_rows: Optional[List[int]] = None
+    hier_group: int = 0
 
 
 @dataclass
@@ -140,7 +151,9 @@ def plan_ref(desc: PlanDesc) -> PlanTables:
     shard_base = [sum(rows_of[:w]) for w in range(W)]
 
     # ring step -> shard
-    if d.pattern == PAT_RING:
+    if (d.pattern == PAT_HIER_SWIZZLE) != (d.hier_group != 0):
+        raise PlanError("hier_group is set exactly for the hierarchical swizzle")
+    if d.pattern in (PAT_RING, PAT_MESH):
         if d.op == OP_GEMM_RS:
             shard_at = [(r - d.ring_dir * (k + 1)) % W for k in range(W)]
         else:
@@ -150,6 +163,14 @@ def plan_ref(desc: PlanDesc) -> PlanTables:
         if sorted(order) != list(range(W)):
             raise PlanError("explicit order is not a permutation")
         shard_at = order
+    elif d.pattern == PAT_HIER_SWIZZLE:
+        g = d.hier_group
+        if g < 1 or W % g:
+            raise PlanError("hier_group must divide world")
+        groups, my_group, my_local = W // g, r // g, r % g
+        shard_at = [((my_group + a) % groups) * g + (my_local + b) % g for a in range(groups) for b in range(g)]
+        if d.op == OP_GEMM_RS:
+            shard_at = shard_at[::-1]
     else:
         raise PlanError("pattern")
     kpos = [0] * W
@@ -162,7 +183,10 @@ def plan_ref(desc: PlanDesc) -> PlanTables:
         for q in range(s):
             chunk_begin.append(shard_base[w] + (q * rows_of[w]) // s)
     chunk_begin.append(M_rows)
-    chunk_pos = [kpos[c // s] * s + (c % s) for c in range(C)]
+    if d.pattern == PAT_MESH:
+        chunk_pos = [(c % s) * W + kpos[c // s] for c in range(C)]
+    else:
+        chunk_pos = [kpos[c // s] * s + (c % s) for c in range(C)]
     arrival = [0] * C
     for c, p in enumerate(chunk_pos):
         arrival[p] = c

@@ -56,7 +56,7 @@ def test_plan_rejects(bad, msg):
 
 def test_reserved_must_be_zero():
     d = A.make_desc(1, 8, 8, 64, 4, tile_m=2, tile_n=2)
-    d.reserved[1] = 5
+    d.reserved[0] = 5
     with pytest.raises(A.SyncError):
         A.sync_plan(d)
 

@@ -1,5 +1,5 @@
 """Arrival and send patterns on the GPU: explicit pull orders, the reverse ring
-direction and a single rank, for AG-GEMM (copy CUs with K-slices, SDMA,
+direction, a single rank, the hierarchical swizzle and the mesh, for AG-GEMM (copy CUs with K-slices, SDMA,
 co-located), GEMM-RS (epilogue backend and copy-out) and the GEMM-AR share.
 
 The plan fixes when each chunk arrives or leaves (Syncopate summary page,
@@ -20,24 +20,37 @@ from gpu_util import bf16_poison, dev_bits, host_bits, workspace
 
 pytestmark = pytest.mark.gpu
 
-PATTERNS = [  # (world, rank, ring_dir, explicit order or None)
+PATTERNS = [  # (world, rank, ring_dir, order): an explicit order, None (ring), ("hier", g) or ("mesh",)
     (4, 2, 1, [2, 0, 3, 1]),   # explicit: own shard first, then a scattered pull order
     (4, 1, 1, [3, 2, 1, 0]),   # explicit: own shard in the middle of the order
     (4, 1, -1, None),          # ring towards rank - 1
     (1, 0, 1, None),           # one rank: nothing to copy or send
+    (8, 5, 1, ("hier", 4)),    # hierarchical swizzle: two groups of four
+    (8, 2, 1, ("hier", 2)),    # hierarchical swizzle: four groups of two
+    (8, 3, -1, ("mesh",)),     # every peer's link at once, sub-chunks interleaved
 ]
 
 
+def _pattern(order):
+    """(pattern, explicit order, hier_group) of a PATTERNS entry."""
+    if order is None:
+        return A.SYNC_PAT_RING, None, 0
+    if isinstance(order, tuple):
+        return (A.SYNC_PAT_HIER_SWIZZLE, None, order[1]) if order[0] == "hier" else (A.SYNC_PAT_MESH, None, 0)
+    return A.SYNC_PAT_EXPLICIT, order, 0
+
+
 def _desc(op, m, n, k, world, rank, d, order, **kw):
-    pat = A.SYNC_PAT_EXPLICIT if order else A.SYNC_PAT_RING
-    return A.make_desc(op, m, n, k, world, rank=rank, ring_dir=d, pattern=pat, explicit_order=order,
-                       b_layout=A.SYNC_B_NK, **kw)
+    pat, explicit, g = _pattern(order)
+    return A.make_desc(op, m, n, k, world, rank=rank, ring_dir=d, pattern=pat, explicit_order=explicit,
+                       hier_group=g, b_layout=A.SYNC_B_NK, **kw)
 
 
 def _ref_plan(op, m, n, k, world, rank, d, order, split=1, tile=(256, 256)):
-    return oracle.plan_ref(oracle.PlanDesc(op=op, m=m, n=n, k=k, world=world, rank=rank, ring_dir=d,
-                                           pattern=oracle.PAT_EXPLICIT if order else oracle.PAT_RING,
-                                           explicit_order=order, split=split, tile_m=tile[0], tile_n=tile[1]))
+    pat, explicit, g = _pattern(order)
+    return oracle.plan_ref(oracle.PlanDesc(op=op, m=m, n=n, k=k, world=world, rank=rank, ring_dir=d, pattern=pat,
+                                           explicit_order=explicit, hier_group=g, split=split, tile_m=tile[0],
+                                           tile_n=tile[1]))
 
 
 @pytest.mark.parametrize("world,rank,d,order", PATTERNS)
@@ -52,6 +65,7 @@ def test_ag_patterns(world, rank, d, order, backend, cus, teams, kslices):
     tabs = A.sync_plan_export(plan)
     ptab = _ref_plan(oracle.OP_AG_GEMM, m, n, k, world, rank, d, order, split)
     assert list(tabs["arrival"]) == list(ptab.arrival) and list(tabs["resident"]) == list(ptab.resident)
+    assert list(tabs["tile_order"]) == list(ptab.tile_order)
     a_peer, b_d = dev_bits(a), dev_bits(b)
     a_local = bf16_poison((m, k))
     for c in range(tabs["num_chunks"]):

@@ -192,3 +192,58 @@ def test_uneven_shards_hand_worked():
     assert list(t2.chunk_begin) == [0, 1, 3, 4, 5, 6, 8]     # floor(q * R_w / 2) inside each shard
     # a 4-row tile over rows 4-7 meets chunks 3 (row 4), 4 (row 5) and 5 (rows 6-7)
     assert list(t2.dep_idx[t2.dep_ptr[1]:t2.dep_ptr[2]]) == [3, 4, 5]
+
+
+# ---- hierarchical swizzle and mesh patterns -----------------------------------
+
+def _order(op, W, r, pattern, g=0, d=1, split=1):
+    t = P.plan_ref(P.PlanDesc(op=op, m=W * split * 2, n=4, k=4, world=W, rank=r, ring_dir=d, pattern=pattern,
+                              hier_group=g, split=split, tile_m=2, tile_n=2))
+    return t
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 6, 8, 12])
+def test_hier_swizzle_steps_are_conflict_free_and_group_first(W):
+    """For every group size g dividing W: each rank's order is a permutation
+    starting with its own shard and then its own group; at every step the
+    ranks pull from distinct shards (a bijection), and the RS send order is
+    the all-gather order reversed."""
+    for g in [x for x in range(1, W + 1) if W % x == 0]:
+        orders = [_order(P.OP_AG_GEMM, W, r, P.PAT_HIER_SWIZZLE, g).arrival for r in range(W)]
+        for r, o in enumerate(orders):
+            assert sorted(o) == list(range(W)) and o[0] == r
+            assert sorted(o[:g]) == list(range((r // g) * g, (r // g) * g + g))
+            assert _order(P.OP_GEMM_RS, W, r, P.PAT_HIER_SWIZZLE, g).arrival == o[::-1]
+        for k in range(W):
+            assert sorted(o[k] for o in orders) == list(range(W)), (g, k)
+
+
+@pytest.mark.parametrize("W", [1, 2, 4, 5, 8])
+def test_hier_swizzle_degenerates_to_the_reverse_ring(W):
+    """One group of all ranks, or groups of one rank: both are the ring
+    towards rank - 1 (rank r takes r, r+1, r+2, ...)."""
+    for r in range(W):
+        ring = _order(P.OP_AG_GEMM, W, r, P.PAT_RING, d=-1).arrival
+        assert _order(P.OP_AG_GEMM, W, r, P.PAT_HIER_SWIZZLE, W).arrival == ring
+        assert _order(P.OP_AG_GEMM, W, r, P.PAT_HIER_SWIZZLE, 1).arrival == ring
+
+
+@pytest.mark.parametrize("op", [P.OP_AG_GEMM, P.OP_GEMM_RS])
+def test_mesh_interleaves_sub_chunks(op):
+    """Mesh with split 1 is the ring; with split s the first W positions hold
+    sub-chunk 0 of every shard, in ring step order, then sub-chunk 1, ..."""
+    W, s = 5, 3
+    for r in range(W):
+        for d in (1, -1):
+            assert _order(op, W, r, P.PAT_MESH, d=d).chunk_pos == _order(op, W, r, P.PAT_RING, d=d).chunk_pos
+            ring = _order(op, W, r, P.PAT_RING, d=d, split=s)
+            mesh = _order(op, W, r, P.PAT_MESH, d=d, split=s)
+            steps = [ring.arrival[k * s] // s for k in range(W)]  # shards in ring step order
+            assert mesh.arrival == [steps[k] * s + q for q in range(s) for k in range(W)]
+
+
+def test_pattern_group_validation():
+    for kw in (dict(pattern=P.PAT_HIER_SWIZZLE, hier_group=3), dict(pattern=P.PAT_HIER_SWIZZLE, hier_group=0),
+               dict(pattern=P.PAT_RING, hier_group=2), dict(pattern=7)):
+        with pytest.raises(P.PlanError):
+            P.plan_ref(P.PlanDesc(op=P.OP_AG_GEMM, m=8, n=4, k=4, world=4, tile_m=2, tile_n=2, **kw))

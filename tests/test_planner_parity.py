@@ -71,6 +71,30 @@ def test_workload_plans_bit_exact(kw):
     _same(*_both(**kw))
 
 
+def test_hier_swizzle_and_mesh_bit_exact():
+    """The hierarchical-swizzle and mesh patterns: both planners agree bit
+    for bit over worlds, group sizes, ranks, directions, splits and orders."""
+    n = 0
+    for op in (P.OP_AG_GEMM, P.OP_GEMM_RS, P.OP_RING_ATTN):
+        for W in (1, 2, 4, 6, 8):
+            for r in sorted({0, W // 2, W - 1}):
+                for s, order in itertools.product((1, 3), (0, 1, 2)):
+                    attn = op == P.OP_RING_ATTN
+                    base = dict(op=op, m=W * 6 if not attn else 7, n=5 if not attn else 6, k=3 if not attn else 8,
+                                world=W, rank=r, split=s, tile_m=4, tile_n=1 if attn else 2, tile_order=order,
+                                group_m=2, **(dict(heads_q=4, heads_kv=2) if attn else {}))
+                    for g in [x for x in range(1, W + 1) if W % x == 0]:
+                        _same(*_both(pattern=P.PAT_HIER_SWIZZLE, hier_group=g, **base))
+                        n += 1
+                    for d in (1, -1):
+                        _same(*_both(pattern=P.PAT_MESH, ring_dir=d, **base))
+                        n += 1
+    assert n > 300
+    for bad in (dict(pattern=P.PAT_HIER_SWIZZLE, hier_group=3), dict(pattern=P.PAT_RING, hier_group=2)):
+        with pytest.raises(A.SyncError):
+            A.sync_plan(A.make_desc(P.OP_AG_GEMM, 8, 4, 4, 4, tile_m=2, tile_n=2, **bad))
+
+
 def test_explicit_order_bit_exact():
     for perm in itertools.permutations(range(4)):
         _same(*_both(op=1, m=12, n=4, k=64, world=4, rank=1, pattern=1, explicit_order=list(perm), split=3,
