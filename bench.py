@@ -364,6 +364,8 @@ def main(argv=None):
         line["split_sweep"] = split_sweep(series, torch, tm, tn, order, b_layout)
         line["trace_headline"] = trace_headline(plan, agent, a_peer, a_local, b, c_out, c_dtype, ws, stream, tabs)
         line["layout_kn_row"] = layout_kn_row(timer, torch, inputs, stream)
+        line["split_baseline"] = {"ag_llama8b_up": split_baseline_ag(timer, plan, a_peer, a_local, b, c_out, c_dtype, ws,
+                                                                     stream, torch, res["cold"]["overlapped"])}
         del a_peer, a_local, b, c_out
         torch.cuda.empty_cache()
         line["other_rows"] = other_rows(timer, torch, inputs, stream)
@@ -425,6 +427,26 @@ def trace_headline(plan, agent, a_peer, a_local, b, c_out, c_dtype, ws, stream, 
             "last_tile_end_us": round(float(tr["tile_end"].max()) / 1e3, 1)}
 
 
+SPLIT_AGENTS = {"runtime_copy_blit": dict(backend=CU), "runtime_copy_sdma": dict(backend=SDMA)}
+
+
+def split_baseline_ag(timer, plan, a_peer, a_local, b, c_out, c_dtype, ws, stream, torch, fused, steps=10, warmup=3):
+    """The kernel-level overlap baseline on the headline workload (per-chunk
+    runtime copies on a second stream, per-chunk GEMM launches joined by
+    events), cold cache, against the fused call: the fusion gain."""
+    x = torch.cuda.Stream()
+    out = {}
+    for name, ag in SPLIT_AGENTS.items():
+        st = timer.series(lambda: A.sync_gemm_split(plan, cfg(**ag), a_peer, a_local, b, c_out, c_dtype, None, ws,
+                                                    stream, x), steps, warmup, True)
+        check(ws, stream)
+        out[name] = {"t_us": us(st), "tflops": round(2.0 * M * N * K / st["median_s"] / 1e12, 1),
+                     "fusion_gain": round(st["median_s"] / fused["median_s"], 3)}
+    out["t_fused_us"] = us(fused)
+    out["workload"] = "the headline share split into 8 per-chunk copies and GEMM launches (7 copied)"
+    return out
+
+
 def layout_kn_row(timer, torch, inputs, stream, steps=10, warmup=3):
     """The headline workload with B stored [k][n] (the kernel for that layout), cold cache."""
     import numpy as np
@@ -477,6 +499,11 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
     part = torch.from_numpy(inputs.partials_f32(m, n)).to(dev)
     t["overlapped_reduce_step"] = t_of(lambda: A.sync_gemm_rs_reduce(plan, cfg(backend=EPI), a, b, c, part, st, ws,
                                                                      stream, None), ws)
+    # the kernel-level overlap baseline: per-chunk GEMM launches, each chunk copied out after its launch
+    x = torch.cuda.Stream()
+    for name, ag in SPLIT_AGENTS.items():
+        t["split_" + name] = t_of(lambda: A.sync_gemm_split(plan, cfg(**ag), None, a, b, c, A.SYNC_DTYPE_F32, st, ws,
+                                                            stream, x), ws)
     # emission cadence: done-flag times of one traced call, in send order
     A.sync_gemm_rs(plan, cfg(backend=EPI, flags=A.SYNC_RUN_TRACE), a, b, c, A.SYNC_DTYPE_F32, st, ws, stream, None)
     check(ws, stream)
@@ -511,6 +538,8 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
         "t_overlap_send_slots_only_us": round(t["send_only"] * 1e6, 1),
         "t_overlap_with_reduce_step_us": round(t["overlapped_reduce_step"] * 1e6, 1),
         "gemm_ar_share_by_split": ar,
+        "split_baseline": {nm: {"t_us": round(t["split_" + nm] * 1e6, 1),
+                                "fusion_gain": round(t["split_" + nm] / t["overlapped"], 3)} for nm in SPLIT_AGENTS},
         "ratio_to_compute_only": round(t["overlapped"] / t["compute_only"], 4),
         "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4),
         "hbm_bound_us": round(hbm / 8e12 * 1e6, 1), "frac_hbm_roofline": round(hbm / 8e12 / t["overlapped"], 4),

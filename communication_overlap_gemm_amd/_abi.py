@@ -33,7 +33,7 @@ SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
     "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_ag_gemm_noalloc", "sync_gemm_rs", "sync_gemm_rs_reduce", "sync_gemm_ar",
-    "sync_ring_attn_step",
+    "sync_ring_attn_step", "sync_gemm_split",
     "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
     "sync_autotune", "sync_tune_workspace_size", "sync_tune_forget",
 )
@@ -145,6 +145,7 @@ def lib():
             "sync_gemm_ar": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "sync_ring_attn_step": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                           i32, vp, vp, vp]),
+            "sync_gemm_split": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, i32, vp, vp, vp, vp]),
             "sync_get_device_info": (i32, [ctypes.POINTER(sync_device_info)]),
             "sync_read_timings": (i32, [i32, ctypes.POINTER(sync_timing), ctypes.POINTER(i32)]),
             "sync_trace_export": (i32, [vp, vp, vp, ctypes.POINTER(sync_trace)]),
@@ -427,6 +428,18 @@ def sync_ring_attn_step(plan: Plan, cfg: Optional[sync_copy_cfg], q, k_peer, v_p
                                      _arg(m_state, "m_state", 4, hq * sq), _arg(l_state, "l_state", 4, hq * sq),
                                      _arg(lse, "lse", 4, hq * sq), float(scale), flags, _ws_arg(plan, ws),
                                      _stream(compute), _stream(copy)))
+
+
+def sync_gemm_split(plan: Plan, cfg: Optional[sync_copy_cfg], a_peer, a, b, c, c_dtype: int, staging, ws, compute,
+                    copy) -> None:
+    """The kernel-level overlap baseline (per-chunk copies and GEMM launches
+    joined by events); `copy` is a second stream."""
+    m, n, k = plan.desc.m, plan.desc.n, plan.desc.k
+    e = _c_elem(c_dtype)
+    _check(lib().sync_gemm_split(plan.handle, ctypes.byref(cfg) if cfg is not None else None,
+                                 _arg(a_peer, "a_peer", 2, m * k), _arg(a, "a", 2, m * k), _arg(b, "b", 2, k * n),
+                                 _arg(c, "c", e, m * n), c_dtype, _arg(staging, "staging", e, m * n),
+                                 _ws_arg(plan, ws), _stream(compute), _stream(copy)))
 
 
 def sync_get_device_info() -> dict:

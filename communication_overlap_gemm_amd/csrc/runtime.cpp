@@ -19,6 +19,7 @@
 #include <tuple>
 #include <memory>
 #include <mutex>
+#include <numeric>
 #include <string>
 #include <vector>
 
@@ -104,6 +105,7 @@ struct DeviceState {
   };
   std::vector<Timed> ring;
   int64_t ring_head = 0, ring_count = 0;
+  std::vector<hipEvent_t> split_events;  // sync_gemm_split: one per chunk hand-over, plus the join
   std::mutex mu;  // serialises launch sequences (the events and streams are shared)
 };
 
@@ -172,6 +174,7 @@ struct DeviceTables {
   int64_t* slot_row = nullptr;
   int32_t* push_rows = nullptr;  // GEMM-RS: staging row of each tile's first row (tiles in one chunk)
   int64_t* ar_items = nullptr;   // GEMM-RS plans: the all-gather items of a GEMM-AR share
+  int32_t* ident = nullptr;      // 0 .. T-1: the traversal of one chunk's GEMM in sync_gemm_split
   void* block = nullptr;  // one allocation holding all of the above
 };
 
@@ -217,7 +220,7 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   const int64_t total = sz(pl.tile_order.size(), 4) + sz(pl.dep_ptr.size(), 8) + sz(pl.dep_idx.size(), 4) +
                         sz(pl.tiles_in.size(), 4) + sz(pl.chunk_begin.size(), 8) + sz(pl.arrival.size(), 4) +
                         sz(pl.resident.size(), 4) + sz(p->slot_row.size(), 8) + sz(p->push_rows.size(), 4) +
-                        sz(p->ar_items.size(), 8) + 256;
+                        sz(p->ar_items.size(), 8) + sz(pl.tile_order.size(), 4) + 256;
   std::vector<char> host(static_cast<size_t>(total), 0);
   void* block = nullptr;
   HIP_TRY(hipMalloc(&block, static_cast<size_t>(total)));
@@ -235,6 +238,9 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   put(cur, host, p->slot_row, &t.slot_row, base);
   if (!p->push_rows.empty()) put(cur, host, p->push_rows, &t.push_rows, base);
   if (!p->ar_items.empty()) put(cur, host, p->ar_items, &t.ar_items, base);
+  std::vector<int32_t> ident(pl.tile_order.size());
+  std::iota(ident.begin(), ident.end(), 0);
+  put(cur, host, ident, &t.ident, base);
   hipError_t e = hipMemcpy(block, host.data(), static_cast<size_t>(total), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(block);
@@ -392,11 +398,8 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
   if (cfg.copy_lead_slice < 0 || (cfg.copy_lead_slice > 0 && cfg.copy_lead_slice >= cfg.copy_kslices))
     return fail(SYNC_EINVAL, "copy_lead_slice must be in [0, copy_kslices)");
-  if (cfg.copy_lead_slice &&
-      (op != SYNC_OP_AG_GEMM || cfg.backend != SYNC_COPY_CU || cfg.copy_link_gbps != 0.f ||
-       (cfg.flags & SYNC_RUN_COPY_ONLY)))
-    return fail(SYNC_EINVAL, "copy_lead_slice is for AG-GEMM with the CU backend, copy_kslices > 1, no pacing and "
-                             "no COPY_ONLY");
+  if (cfg.copy_lead_slice && (op != SYNC_OP_AG_GEMM || cfg.backend != SYNC_COPY_CU || cfg.copy_link_gbps != 0.f))
+    return fail(SYNC_EINVAL, "copy_lead_slice is for AG-GEMM with the CU backend, copy_kslices > 1 and no pacing");
   if (cfg.copy_link_gbps != 0.f) {
     if (!(cfg.copy_link_gbps >= 1.f && cfg.copy_link_gbps <= 10000.f))
       return fail(SYNC_EINVAL, "copy_link_gbps must be 0 or in [1, 10000]");
@@ -1043,6 +1046,89 @@ int sync_gemm_ar(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, cons
   return gemm_rs_impl(plan, cfg, a, b, c, SYNC_DTYPE_F32, partials, staging, ws, compute, copy, reduced_peer, out);
 }
 
+// Kernel-level overlap baseline (Syncopate summary page, "Key observations",
+// observation 1, Fig. 2(a)-(b): the operator split into per-chunk kernels,
+// overlapped by streams).  Same GEMM kernel and K order as the fused calls;
+// the hand-over of every chunk is a runtime copy plus a pair of events.
+int sync_gemm_split(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a, const void* b, void* c,
+                    int32_t c_dtype, void* staging, void* ws, void* compute, void* copy) {
+  if (!plan) return fail(SYNC_EINVAL, "plan is NULL");
+  const Plan& pl = plan->plan;
+  const int32_t op = pl.desc.op;
+  if (op != SYNC_OP_AG_GEMM && op != SYNC_OP_GEMM_RS) return fail(SYNC_EINVAL, "sync_gemm_split takes a GEMM plan");
+  const int32_t backend = cfg ? cfg->backend : SYNC_COPY_CU;
+  if (backend != SYNC_COPY_CU && backend != SYNC_COPY_SDMA)
+    return fail(SYNC_EINVAL, "sync_gemm_split copies with the runtime: backend CU (blit kernels) or SDMA (engines)");
+  if (cfg && cfg->flags) return fail(SYNC_EINVAL, "sync_gemm_split takes no run-mode flags");
+  if (!copy) return fail(SYNC_EINVAL, "sync_gemm_split needs a copy stream");
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return fail(SYNC_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  int rc = check_gemm_shape(pl);
+  if (rc) return rc;
+  if (c_dtype != SYNC_DTYPE_F32 && c_dtype != SYNC_DTYPE_BF16) return fail(SYNC_EINVAL, "bad c_dtype");
+  const bool ag = op == SYNC_OP_AG_GEMM;
+  if (!a || !b || !c || (ag && !a_peer) || (!ag && !staging)) return fail(SYNC_EINVAL, "NULL operand");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c) || (a_peer && !aligned16(a_peer)) ||
+      (staging && !aligned16(staging)))
+    return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
+  DeviceState* dp = nullptr;
+  if ((rc = current_device_state(&dp))) return rc;
+  DeviceState& d = *dp;
+  if ((rc = check_residency(pl, d.device, c_dtype, false))) return rc;
+  DeviceTables* tab = nullptr;
+  if ((rc = device_tables(plan, d.device, &tab))) return rc;
+  std::lock_guard<std::mutex> lk(d.mu);
+  const int32_t C = pl.num_chunks;
+  while (static_cast<int32_t>(d.split_events.size()) < C + 1) {
+    hipEvent_t e = nullptr;
+    HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    d.split_events.push_back(e);
+  }
+  hipStream_t cs = static_cast<hipStream_t>(compute), xs = static_cast<hipStream_t>(copy);
+  const hipMemcpyKind kind = backend == SYNC_COPY_SDMA ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+  const int64_t K = pl.desc.k, N = pl.desc.n, es = c_dtype == SYNC_DTYPE_F32 ? 4 : 2;
+  const int32_t TM = pl.desc.tile_m, Tn = pl.tiles_n, full = d.num_cus * gemm_wg_per_cu(pl);
+  CallCtx cx;
+  cx.dev = &d;
+  cx.tab = tab;
+  cx.ws = ws_view(ws, C, pl.num_tiles);
+  cx.timeout_ticks = 2000ull * static_cast<uint64_t>(d.wall_khz);
+  // the GEMM over the rows of one chunk: every tile in place, the identity traversal
+  auto gemm_rows = [&](int64_t r0, int64_t r1) -> int {
+    GemmArgs g = make_gemm_args(pl, cx, static_cast<const uint16_t*>(a) + r0 * K, b,
+                                static_cast<char*>(c) + r0 * N * es);
+    g.M = r1 - r0;
+    g.order = tab->ident;
+    g.num_tiles = static_cast<int32_t>((r1 - r0 + TM - 1) / TM) * Tn;
+    g.wait_chunks = 0;
+    const int grid = std::min(full, g.num_tiles);
+    HIP_TRY(launch_gemm(g, pl.desc.tile_m, pl.desc.tile_n, pl.desc.b_layout, c_dtype, false, grid, cs));
+    return SYNC_OK;
+  };
+  for (int32_t p = 0; p < C; ++p) {
+    const int32_t ch = pl.arrival[p];
+    const int64_t r0 = pl.chunk_begin[ch], r1 = pl.chunk_begin[ch + 1];
+    if (ag) {  // copy in the chunk, then its GEMM once the copy has landed
+      if (!pl.resident[ch]) {
+        HIP_TRY(hipMemcpyAsync(static_cast<char*>(a) + r0 * K * 2, static_cast<const char*>(a_peer) + r0 * K * 2,
+                               static_cast<size_t>((r1 - r0) * K * 2), kind, xs));
+        HIP_TRY(hipEventRecord(d.split_events[p], xs));
+        HIP_TRY(hipStreamWaitEvent(cs, d.split_events[p], 0));
+      }
+      if ((rc = gemm_rows(r0, r1))) return rc;
+    } else {  // the chunk's GEMM, then its copy-out to send slot p
+      if ((rc = gemm_rows(r0, r1))) return rc;
+      HIP_TRY(hipEventRecord(d.split_events[p], cs));
+      HIP_TRY(hipStreamWaitEvent(xs, d.split_events[p], 0));
+      HIP_TRY(hipMemcpyAsync(static_cast<char*>(staging) + plan->slot_row[p] * N * es,
+                             static_cast<const char*>(c) + r0 * N * es, static_cast<size_t>((r1 - r0) * N * es), kind,
+                             xs));
+    }
+  }
+  HIP_TRY(hipEventRecord(d.split_events[C], xs));  // the call ends on `compute` once every copy has
+  HIP_TRY(hipStreamWaitEvent(cs, d.split_events[C], 0));
+  return SYNC_OK;
+}
+
 int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q, const void* k_peer,
                         const void* v_peer, void* k_local, void* v_local, float* o, float* m_state, float* l_state,
                         float* lse, float scale, int32_t flags, void* ws, void* compute, void* copy) {
@@ -1164,6 +1250,7 @@ void sync_shutdown(void) {
     for (auto& t : d.ring)
       for (hipEvent_t e : {t.k0, t.k1, t.c0, t.c1})
         if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : d.split_events) (void)hipEventDestroy(e);
   }
   g_devices.clear();
   if (have) (void)hipSetDevice(cur);

@@ -255,8 +255,8 @@ typedef struct {
                                workgroups whose first tile reads that chunk (each a share of its
                                rows, published together), before they start it; the copy
                                workgroups move the other slices, and every slice of chunks no
-                               first tile reads.  0 = the copy workgroups move every slice.  Not
-                               with COPY_ONLY (nothing computes) or pacing. */
+                               first tile reads.  0 = the copy workgroups move every slice, as
+                               with COPY_ONLY (nothing computes).  Not with pacing. */
 } sync_copy_cfg;
 
 /* ---- workspace ---------------------------------------------------------- */
@@ -393,6 +393,27 @@ int sync_gemm_rs_reduce(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
 int sync_gemm_ar(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a, const void* b, void* c,
                  const float* partials, const float* reduced_peer, float* out, void* staging, void* ws,
                  void* compute, void* copy);
+
+/* Kernel-level overlap baseline of a GEMM plan [SYN-S "Key observations",
+ * observation 1, Fig. 2(a)-(b); SYN-R Fig. 2 caption: the operator split into
+ * per-chunk kernels whose communication overlaps through streams, which the
+ * fused kernel is claimed to beat].  No fusion: for each chunk in the plan's
+ * order,
+ *   AG plan: a runtime copy of the chunk's rows from a_peer into a on `copy`
+ *            (resident chunks are not copied), an event, and on `compute`
+ *            after it a GEMM launch over those rows of a (every tile in
+ *            place, tiles in row-major order);
+ *   RS plan: a GEMM launch over the chunk's rows on `compute`, an event, and
+ *            on `copy` after it a runtime copy of those rows of c into send
+ *            slot p of `staging` (as sync_gemm_rs packs it); a_peer unused.
+ * Then `compute` waits for `copy`, so the call is complete when `compute` is.
+ * The GEMM kernel and its per-tile K order are those of the fused calls, so
+ * the result is bitwise the same.  cfg: NULL or backend CU (runtime copies
+ * on blit kernels) or SDMA (copies on the engines), no flags.  `copy` must
+ * be a stream other than `compute`; ws as for the other calls.  Operands as
+ * in sync_ag_gemm (a = a_local) or sync_gemm_rs. */
+int sync_gemm_split(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_peer, void* a, const void* b,
+                    void* c, int32_t c_dtype, void* staging, void* ws, void* compute, void* copy);
 
 /* Ring-attention local step [SYN-S "Experiments", paper sec. 6.1 and Fig. 9:
  * RingAttention].  KV blocks (chunks of K and V token rows) are staged from

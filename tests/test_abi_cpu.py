@@ -195,7 +195,7 @@ def test_binding_checks_tensor_sizes():
 
 def test_lead_slice_validation():
     """copy_lead_slice: in [0, copy_kslices), and only for AG-GEMM with the CU
-    backend, K-slices, no pacing and a compute part."""
+    backend, K-slices and no pacing."""
     def rc_of(plan, cfg):
         return A.lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg), None, None, None, None, 0, 256, None, None)
     p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
@@ -203,7 +203,22 @@ def test_lead_slice_validation():
                 A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=4, copy_lead_slice=-1),
                 A.make_cfg(A.SYNC_COPY_CU, 8, copy_lead_slice=1),
                 A.make_cfg(A.SYNC_COPY_COLOCATED, copy_kslices=2, copy_lead_slice=1),
-                A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=1, copy_link_gbps=100.0),
-                A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=1, flags=A.SYNC_RUN_COPY_ONLY)):
+                A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=1, copy_link_gbps=100.0)):
         assert rc_of(p, bad) == A.SYNC_EINVAL
         assert "copy_lead_slice" in A.sync_last_error()
+
+
+def test_split_baseline_validation():
+    """sync_gemm_split: a GEMM plan, a copy stream, a runtime-copy backend and
+    no run flags; checked before any device work."""
+    lib = A.lib()
+    ag = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256))
+    at = A.sync_plan(A.make_desc(A.SYNC_OP_RING_ATTN, 64, 16, 128, 4, heads_q=4, heads_kv=1))
+    args = (0x1000, 0x1000, 0x1000, 0x1000, 0, None, 256)
+    assert lib.sync_gemm_split(None, None, *args, None, 0x10) == A.SYNC_EINVAL
+    assert lib.sync_gemm_split(at.handle, None, *args, None, 0x10) == A.SYNC_EINVAL
+    assert "GEMM plan" in A.sync_last_error()
+    assert lib.sync_gemm_split(ag.handle, None, *args, None, None) == A.SYNC_EINVAL
+    assert "copy stream" in A.sync_last_error()
+    for bad in (A.make_cfg(A.SYNC_COPY_COLOCATED), A.make_cfg(A.SYNC_COPY_CU, 16, flags=A.SYNC_RUN_TIMED)):
+        assert lib.sync_gemm_split(ag.handle, ctypes.byref(bad), *args, None, 0x10) == A.SYNC_EINVAL

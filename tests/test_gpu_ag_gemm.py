@@ -707,3 +707,14 @@ def test_a2a_gemm_uneven_shards_exact(backend, cus, teams, kslices, split, tile)
         assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
         assert np.array_equal(host_bits(a_local), a)
         assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
+
+
+def test_lead_slices_copy_only_stages_everything():
+    """COPY_ONLY with lead slices: no compute workgroup runs, so the copy
+    workgroups move every slice; every peer row lands and C is untouched."""
+    m, n, k, world = 2048, 768, 1152, 4
+    a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="nk")
+    out, a_local = run_ag(m, n, k, world, a, b, layout="nk", split=2, tile=(256, 256), backend=A.SYNC_COPY_CU,
+                          copy_cus=16, teams=3, kslices=4, lead=2, flags=A.SYNC_RUN_COPY_ONLY)
+    assert np.array_equal(a_local, a)
+    assert np.isnan(out).all()
