@@ -3,8 +3,9 @@
 One step = one sync_ag_gemm call, which is one kernel launch: its first
 workgroups (the copy role, on 32 CUs) stage the 7 peer chunks of A
 (8192 x 4096 bf16, 8 shards of 1024 rows, N(0,1)/64) from the peer HBM region,
-all 7 at once in 7 teams (as pulls from every peer over a full xGMI mesh), in 4
-K-slices each, while the other workgroups run the persistent MFMA GEMM of the
+all 7 at once in 7 teams (as pulls from every peer over a full xGMI mesh), in 2
+K-slices each (the compute workgroups copy the first slice of the chunk their
+first tile reads), while the other workgroups run the persistent MFMA GEMM of the
 gathered A with B (4096 x 1792 bf16, stored [n][k] like a linear layer's
 weight) into C (8192 x 1792 fp32), each tile waiting on the chunks it reads.
 Inputs are resident in HBM before the timed region.
@@ -20,8 +21,9 @@ Printed: one JSON line with the metric (TFLOP/s of the overlapped call), the
 overlap efficiency (overlapped time / max(compute-only, copy-only)), the
 roofline of the dominant kernel (the call's launch), the other rows of the hot
 path (GEMM-RS, the 70B-like AG with its chunk-size and tile-order sweep, the
-MoE-like A2A, ring attention, the GEMM-AR split sweep, the split multi-kernel
-baseline), and the CPU oracle timed on the host on the same products.
+MoE-like A2A, ring attention, head-parallel attention, the GEMM-AR split
+sweep, the split multi-kernel baseline), and the CPU oracle timed on the host
+on the same products.
 """
 from __future__ import annotations
 
@@ -90,6 +92,13 @@ A2A_AGENTS = {"cu32_7teams_4slices": dict(backend=CU, copy_cus=32, copy_teams=7,
 ATTN_SHAPE = dict(sq=4096, hq=32, hkv=8, d=128, n=4096, world=8)
 ATTN_AGENTS = {"overlapped": dict(backend=COLOC), "overlapped_32_copy_cus": dict(backend=CU, copy_cus=32, copy_teams=7),
                "compute_only": dict(backend=PRESET)}
+
+# head-parallel attention share, Llama-3-8B-like (32 query / 8 KV heads): 8 ranks x 4096 tokens, one
+# rank's head group of 4 query heads and 1 KV head over all 32768 tokens
+HEAD_SHAPE = dict(world=8, n=4096, hq=4, hkv=1, d=128)
+HEAD_AGENTS = {"colocated": dict(backend=COLOC), "cu32_7teams": dict(backend=CU, copy_cus=32, copy_teams=7),
+               "sdma_7_engines": dict(backend=A.SYNC_COPY_SDMA, copy_teams=7), "compute_only": dict(backend=PRESET)}
+HEAD_COPY_ONLY = dict(backend=CU, copy_cus=32, copy_teams=7, flags=A.SYNC_RUN_COPY_ONLY)
 
 ORDERS = {"row_major": A.SYNC_ORDER_ROW_MAJOR, "chunk_major": A.SYNC_ORDER_CHUNK_MAJOR,
           "swizzled": A.SYNC_ORDER_SWIZZLED}
@@ -645,6 +654,36 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
         "t_compute_only_us": round(t["compute_only"] * 1e6, 1),
         "ratio": round(t["overlapped"] / t["compute_only"], 4),
         "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, kp, vp, kl, vl, o, ms, ls, lse
+
+    # Head-parallel share: Q, K, V of one head group arrive as 8 token blocks (7 from peers)
+    w, nb, hq, hkv, d = (HEAD_SHAPE[x] for x in ("world", "n", "hq", "hkv", "d"))
+    s = w * nb
+    q_bits, k_bits, v_bits = inputs.attention_operands(s, hq, s, hkv, d)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_HEAD_ATTN, s, nb, d, w, tile_m=32 * (8 // min(hq // hkv, 4)), tile_n=1,
+                                   heads_q=hq, heads_kv=hkv))
+    peers = [torch.from_numpy(x.view(np.int16)).to(dev) for x in (q_bits, k_bits, v_bits)]
+    local = [torch.zeros_like(x) for x in peers]
+    for lo, pe in zip(local, peers):
+        lo[:nb] = pe[:nb]  # rank 0's own block
+    o = torch.empty((s, hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((hq, s), dtype=torch.float32, device=dev)
+    ws = workspace(plan, torch)
+    t = {}
+    for name, ag in list(HEAD_AGENTS.items()) + [("copy_only", HEAD_COPY_ONLY)]:
+        t[name] = t_of(lambda: A.sync_head_attn(plan, cfg(**ag), *peers, *local, o, lse, 1.0 / d ** 0.5, ws, stream,
+                                                None), ws)
+    best = min((x for x in HEAD_AGENTS if x != "compute_only"), key=lambda x: t[x])
+    flops = 4.0 * s * s * hq * d
+    out["head_parallel_attention_llama8b_like"] = {
+        "workload": "Head-parallel attention share: 8 ranks x 4096 tokens; this rank's head group (4 query heads, "
+                    "1 KV head, d 128) of all 32768 tokens arrives as 8 token blocks of Q, K and V (7 copied), "
+                    "non-causal attention over all 32768 tokens, fp32 O and LSE",
+        "best_agent": best, "tflops": round(flops / t[best] / 1e12, 1), "t_overlap_us": round(t[best] * 1e6, 1),
+        "t_compute_only_us": round(t["compute_only"] * 1e6, 1), "t_copy_only_us": round(t["copy_only"] * 1e6, 1),
+        "ratio": round(t[best] / max(t["compute_only"], t["copy_only"]), 4),
+        "frac_mfma_peak": round(flops / t[best] / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "t_us_by_agent": {nm: round(t[nm] * 1e6, 1) for nm in t}}
     return out
 
 
@@ -750,6 +789,18 @@ def cpu_baseline_by_config(inputs):
                                          "gflops": round(4.0 * sq * w * nb * hq * d / full / 1e9, 2),
                                          "measured": f"{count} of {sq * hq} (query, head) rows ({dt:.2f} s), scaled "
                                                      f"by {sq * hq / count:.0f}"}
+    del q, kk, vv
+    w, nb, hq, hkv, d = (HEAD_SHAPE[x] for x in ("world", "n", "hq", "hkv", "d"))
+    s = w * nb
+    q, kk, vv = inputs.attention_operands(s, hq, s, hkv, d)
+    qi, hi = rng.integers(0, s, count), rng.integers(0, hq, count)
+    t0 = time.perf_counter()
+    oracle.attention_f64_sampled(q, kk, vv, 1.0 / d ** 0.5, qi, hi, threads=th)
+    dt = time.perf_counter() - t0
+    full = dt * s * hq / count
+    out["6_head_parallel_attention_llama8b_like"] = {
+        "seconds": round(full, 2), "gflops": round(4.0 * s * s * hq * d / full / 1e9, 2),
+        "measured": f"{count} of {s * hq} (query, head) rows ({dt:.2f} s), scaled by {s * hq / count:.0f}"}
     return out
 
 

@@ -8,5 +8,5 @@ the library is loaded on the first call and a missing build raises.
 from . import _abi  # noqa: F401
 from ._abi import (  # noqa: F401
     SyncError, make_tune_space, sync_ag_gemm, sync_autotune, sync_gemm_rs, sync_get_device_info, sync_last_error, sync_plan, sync_plan_export,
-    sync_plan_get_info, sync_read_timings, sync_ring_attn_step, sync_shutdown, sync_trace_export,
+    sync_head_attn, sync_plan_get_info, sync_read_timings, sync_ring_attn_step, sync_shutdown, sync_trace_export,
     sync_tune_workspace_size, sync_workspace_init, sync_workspace_size, sync_workspace_status)

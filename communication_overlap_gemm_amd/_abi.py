@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libsync_overlap.so")
 
 # ---- constants (mirror sync_overlap.h) ------------------------------------
 SYNC_OK, SYNC_EINVAL, SYNC_EUNSUPPORTED, SYNC_EHIP, SYNC_ETIMEOUT, SYNC_ENOMEM, SYNC_ENODEV = 0, -1, -2, -3, -4, -5, -6
-SYNC_OP_AG_GEMM, SYNC_OP_GEMM_RS, SYNC_OP_RING_ATTN = 1, 2, 3
+SYNC_OP_AG_GEMM, SYNC_OP_GEMM_RS, SYNC_OP_RING_ATTN, SYNC_OP_HEAD_ATTN = 1, 2, 3, 4
 SYNC_PAT_RING, SYNC_PAT_EXPLICIT, SYNC_PAT_HIER_SWIZZLE, SYNC_PAT_MESH = 0, 1, 2, 3
 SYNC_ORDER_ROW_MAJOR, SYNC_ORDER_CHUNK_MAJOR, SYNC_ORDER_SWIZZLED = 0, 1, 2
 SYNC_B_KN, SYNC_B_NK = 0, 1
@@ -33,7 +33,7 @@ SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
     "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_ag_gemm_noalloc", "sync_gemm_rs", "sync_gemm_rs_reduce", "sync_gemm_ar",
-    "sync_ring_attn_step", "sync_gemm_split",
+    "sync_ring_attn_step", "sync_head_attn", "sync_gemm_split",
     "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
     "sync_autotune", "sync_tune_workspace_size", "sync_tune_forget",
 )
@@ -145,6 +145,8 @@ def lib():
             "sync_gemm_ar": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "sync_ring_attn_step": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, f32,
                                           i32, vp, vp, vp]),
+            "sync_head_attn": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
+                                     vp, vp]),
             "sync_gemm_split": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, i32, vp, vp, vp, vp]),
             "sync_get_device_info": (i32, [ctypes.POINTER(sync_device_info)]),
             "sync_read_timings": (i32, [i32, ctypes.POINTER(sync_timing), ctypes.POINTER(i32)]),
@@ -428,6 +430,20 @@ def sync_ring_attn_step(plan: Plan, cfg: Optional[sync_copy_cfg], q, k_peer, v_p
                                      _arg(m_state, "m_state", 4, hq * sq), _arg(l_state, "l_state", 4, hq * sq),
                                      _arg(lse, "lse", 4, hq * sq), float(scale), flags, _ws_arg(plan, ws),
                                      _stream(compute), _stream(copy)))
+
+
+def sync_head_attn(plan: Plan, cfg: Optional[sync_copy_cfg], q_peer, k_peer, v_peer, q, k, v, o, lse,
+                   scale: float, ws, compute=None, copy=None) -> None:
+    """Head-parallel attention share: the all-to-all receive side of Q, K, V
+    (token block w from peer w) fused with attention over all world*n tokens."""
+    d = plan.desc
+    s, d_head, hq, hkv = d.m, d.k, d.heads_q, d.heads_kv
+    qn, kv = s * hq * d_head, s * hkv * d_head
+    _check(lib().sync_head_attn(plan.handle, ctypes.byref(cfg) if cfg is not None else None,
+                                _arg(q_peer, "q_peer", 2, qn), _arg(k_peer, "k_peer", 2, kv),
+                                _arg(v_peer, "v_peer", 2, kv), _arg(q, "q", 2, qn), _arg(k, "k", 2, kv),
+                                _arg(v, "v", 2, kv), _arg(o, "o", 4, qn), _arg(lse, "lse", 4, hq * s),
+                                float(scale), _ws_arg(plan, ws), _stream(compute), _stream(copy)))
 
 
 def sync_gemm_split(plan: Plan, cfg: Optional[sync_copy_cfg], a_peer, a, b, c, c_dtype: int, staging, ws, compute,

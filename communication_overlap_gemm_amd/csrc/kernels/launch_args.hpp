@@ -6,6 +6,7 @@
 namespace syncov {
 
 constexpr int kMaxSlices = 8;  // K-slices per chunk (copy_kslices) the workspace holds
+constexpr int kMaxCopyTensors = 3;  // tensors staged per chunk (head-parallel attention: Q, K and V)
 
 // Per-chunk counter arrays of the workspace (cleared by the workgroup that
 // completes them; after a failed call, by the call's last workgroup).
@@ -20,9 +21,9 @@ struct CounterArrays {
 
 // Copy role (copy_role.hpp): chunk copy-in or copy-out.
 struct CopyArgs {
-  const char* src[2];  // up to two tensors per chunk (attention: K and V)
-  char* dst[2];
-  int64_t row_bytes[2];
+  const char* src[kMaxCopyTensors];  // tensors per chunk (ring attention: K and V; head-parallel: Q, K, V)
+  char* dst[kMaxCopyTensors];
+  int64_t row_bytes[kMaxCopyTensors];
   int32_t ntensors;
   int32_t num_chunks;
   const int64_t* chunk_begin;  // C+1 row bounds
@@ -126,7 +127,7 @@ struct AttnArgs {
   const uint16_t* k;  // bf16 [world*n][heads_kv][128] (local copy, filled by the copy role)
   const uint16_t* v;
   float* o;           // [sq][heads_q][128]
-  float* m_state;     // [heads_q][sq]
+  float* m_state;     // [heads_q][sq] (null: not kept; only with init and finalize)
   float* l_state;
   float* lse;         // [heads_q][sq] or null
   int64_t sq;
@@ -137,6 +138,15 @@ struct AttnArgs {
   const int32_t* arrival;
   const int32_t* resident;
   int32_t num_chunks;
+  // Head-parallel attention: the queries arrive with the keys.  items[it] is
+  // the plan tile (i * heads_q + h, h the first head of the item's group,
+  // tile_m = the item's query rows) taken it-th; the item waits for the chunks
+  // dep_idx[dep_ptr[t] ..) holding its query rows before it reads them.  Null
+  // items: ring attention (queries resident, items head-group-major).
+  const int32_t* items;
+  int32_t num_items;
+  const int64_t* dep_ptr;
+  const int32_t* dep_idx;
   const uint32_t* flags;
   uint32_t* hdr;
   CounterArrays cnt;

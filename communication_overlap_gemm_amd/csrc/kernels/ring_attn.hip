@@ -28,6 +28,14 @@
 //  * KV tiles of 64 keys, double-buffered in LDS (64 KB), prefetched one tile
 //    ahead through registers; raw buffer loads return zero past a chunk's
 //    last key, and those keys are masked to -inf.
+//
+// The same kernel runs the head-parallel share (Syncopate summary page,
+// "Experiments", paper sec. 6.1 and Fig. 9, head-parallel attention; the
+// all-to-all scheme is DeepSpeed-Ulysses', in the review page's references):
+// after the all-to-all each rank holds every token of its head group, token
+// block w coming from peer w, queries included.  A work item then also waits
+// for the chunks holding its own query rows, and items are taken in the
+// plan's order (those whose queries land first go first).
 #include <math.h>
 
 #include "copy_role.hpp"
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
   const float c2 = a.scale * 1.4426950408889634f;  // scale in log2 units
   const int group = static_cast<int>(Hq / Hkv);  // query heads per KV head
   const int nqb = static_cast<int>((a.sq + QB - 1) / QB);
-  const int items = nqb * static_cast<int>(Hq / HG);
+  const int items = a.items ? a.num_items : nqb * static_cast<int>(Hq / HG);
 
   if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
     copy_role<kAttnThreads>(a.copy, blockIdx.x, a.copy_blocks, epoch);
@@ -88,9 +96,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
     else
       copy_role<kAttnThreads, true>(a.copy, gb, gn, epoch);
   }
+  // head-parallel attention: wait for the chunks holding plan tile t's query rows
+  auto wait_queries = [&](int t) {
+    if (!a.wait_chunks) return 1;
+    if (tid == 0) {
+      bool ok = true;
+      for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e) {
+        const int32_t c = a.dep_idx[e];
+        if (!a.resident[c]) ok = wait_flag(a.flags, c, epoch, a.hdr, a.timeout_ticks);
+      }
+      if (ok) acquire_agent();
+      s_ok = ok;
+    }
+    __syncthreads();
+    const int ok = s_ok;
+    __syncthreads();
+    return ok;
+  };
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
-  for (int item = slot0; item < items; item += gn) {
-    const int hg = item / nqb, qb = item - hg * nqb;  // head-group-major: one KV head's items adjacent
+  for (int it = slot0; it < items; it += gn) {
+    int hg, qb;
+    if (a.items) {  // plan tile t = qb * heads_q + (first head of the group)
+      const int t = a.items[it];
+      qb = t / static_cast<int>(Hq);
+      hg = (t - qb * static_cast<int>(Hq)) / HG;
+      if (!wait_queries(t)) continue;  // its queries never arrived: outputs left untouched
+    } else {
+      hg = it / nqb;  // head-group-major: one KV head's items adjacent
+      qb = it - hg * nqb;
+    }
     const int64_t h = static_cast<int64_t>(hg) * HG + hh;
     const int g = static_cast<int>(h / group);  // KV head (uniform: HG divides the group or equals it)
     const int64_t q = static_cast<int64_t>(qb) * QB + qs * 32 + col;  // this lane's query row
@@ -285,8 +319,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
           }
         if (half == 0) {
           if (a.lse) a.lse[h * a.sq + q] = m2 * ln2 + logf(l);
-          a.m_state[h * a.sq + q] = m2 * ln2;
-          a.l_state[h * a.sq + q] = l;
+          if (a.m_state) {
+            a.m_state[h * a.sq + q] = m2 * ln2;
+            a.l_state[h * a.sq + q] = l;
+          }
         }
       } else {
 #pragma unroll

@@ -22,9 +22,13 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
   p = Plan{};
   p.desc = d;
   p.desc.explicit_order = nullptr;
-  const bool attn = d.op == SYNC_OP_RING_ATTN;
+  const bool head = d.op == SYNC_OP_HEAD_ATTN;
+  const bool attn = d.op == SYNC_OP_RING_ATTN || head;
   const bool rs = d.op == SYNC_OP_GEMM_RS;
-  if (d.op != SYNC_OP_AG_GEMM && !rs && !attn) { err = "op must be AG_GEMM, GEMM_RS or RING_ATTN"; return false; }
+  if (d.op != SYNC_OP_AG_GEMM && !rs && !attn) {
+    err = "op must be AG_GEMM, GEMM_RS, RING_ATTN or HEAD_ATTN";
+    return false;
+  }
   if (d.world < 1) { err = "world must be >= 1"; return false; }
   if (d.rank < 0 || d.rank >= d.world) { err = "rank out of range"; return false; }
   if (d.ring_dir != 1 && d.ring_dir != -1) { err = "ring_dir must be +1 or -1"; return false; }
@@ -41,6 +45,10 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
   if (attn) {
     if (d.heads_q < 1 || d.heads_kv < 1 || d.heads_q % d.heads_kv) { err = "heads_q must be a positive multiple of heads_kv"; return false; }
     if (d.shard_rows) { err = "shard_rows is for the GEMM ops"; return false; }
+    if (head && d.m != static_cast<int64_t>(W) * d.n) {
+      err = "head-parallel attention: the queries are every token (m = world * n)";
+      return false;
+    }
     p.shard_rows = d.n;
     p.rows = static_cast<int64_t>(W) * d.n;
     std::fill(rows_of.begin(), rows_of.end(), p.shard_rows);
@@ -134,7 +142,7 @@ bool build_plan(const sync_plan_desc& d, Plan& p, std::string& err) {
   // chunks met by each tile row: a contiguous id range [lo, hi)
   std::vector<int32_t> row_lo(tm), row_hi(tm);
   for (int64_t i = 0; i < tm; ++i) {
-    if (attn) { row_lo[i] = 0; row_hi[i] = C; continue; }
+    if (attn && !head) { row_lo[i] = 0; row_hi[i] = C; continue; }  // ring: every KV block
     const int64_t r0 = i * d.tile_m, r1 = std::min<int64_t>(r0 + d.tile_m, d.m);
     // first chunk whose end is past r0; last chunk whose begin is before r1
     auto first = std::upper_bound(p.chunk_begin.begin() + 1, p.chunk_begin.end(), r0) - (p.chunk_begin.begin() + 1);

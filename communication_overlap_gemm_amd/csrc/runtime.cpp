@@ -175,6 +175,7 @@ struct DeviceTables {
   int32_t* push_rows = nullptr;  // GEMM-RS: staging row of each tile's first row (tiles in one chunk)
   int64_t* ar_items = nullptr;   // GEMM-RS plans: the all-gather items of a GEMM-AR share
   int32_t* ident = nullptr;      // 0 .. T-1: the traversal of one chunk's GEMM in sync_gemm_split
+  int32_t* head_items = nullptr; // HEAD_ATTN plans: the tiles that start a kernel work item, in order
   void* block = nullptr;  // one allocation holding all of the above
 };
 
@@ -192,6 +193,7 @@ struct sync_plan_s {
   std::vector<int64_t> slot_row;   // staging row of each send position (C+1)
   std::vector<int32_t> push_rows;  // GEMM-RS, every tile in one chunk: staging row of each tile's first row (T)
   std::vector<int64_t> ar_items;   // GEMM-RS: GEMM-AR all-gather items, 5 per item (see GemmArgs)
+  std::vector<int32_t> head_items; // HEAD_ATTN: tiles whose head starts a kernel work item, in traversal order
   std::mutex mu;
   std::map<int, DeviceTables> dev;
   // (device, compute workgroups, XCDs, withheld chunk) -> lead-slice tables
@@ -220,7 +222,8 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   const int64_t total = sz(pl.tile_order.size(), 4) + sz(pl.dep_ptr.size(), 8) + sz(pl.dep_idx.size(), 4) +
                         sz(pl.tiles_in.size(), 4) + sz(pl.chunk_begin.size(), 8) + sz(pl.arrival.size(), 4) +
                         sz(pl.resident.size(), 4) + sz(p->slot_row.size(), 8) + sz(p->push_rows.size(), 4) +
-                        sz(p->ar_items.size(), 8) + sz(pl.tile_order.size(), 4) + 256;
+                        sz(p->ar_items.size(), 8) + sz(pl.tile_order.size(), 4) + sz(p->head_items.size(), 4) +
+                        256;
   std::vector<char> host(static_cast<size_t>(total), 0);
   void* block = nullptr;
   HIP_TRY(hipMalloc(&block, static_cast<size_t>(total)));
@@ -241,6 +244,7 @@ int device_tables(sync_plan_s* p, int dev, DeviceTables** out) {
   std::vector<int32_t> ident(pl.tile_order.size());
   std::iota(ident.begin(), ident.end(), 0);
   put(cur, host, ident, &t.ident, base);
+  if (!p->head_items.empty()) put(cur, host, p->head_items, &t.head_items, base);
   hipError_t e = hipMemcpy(block, host.data(), static_cast<size_t>(total), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(block);
@@ -413,7 +417,8 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
                                    "while the persistent kernel runs); SYNC_RUN_WITHHOLD covers failure-path tests");
   if (cfg.flags & ~(SYNC_RUN_COPY_ONLY | SYNC_RUN_COMPUTE_ONLY | SYNC_RUN_TIMED | SYNC_RUN_WITHHOLD | SYNC_RUN_TRACE))
     return fail(SYNC_EINVAL, "unknown cfg.flags bits");
-  if ((cfg.flags & SYNC_RUN_TRACE) && op == SYNC_OP_RING_ATTN) return fail(SYNC_EINVAL, "TRACE is for GEMM calls");
+  if ((cfg.flags & SYNC_RUN_TRACE) && (op == SYNC_OP_RING_ATTN || op == SYNC_OP_HEAD_ATTN))
+    return fail(SYNC_EINVAL, "TRACE is for GEMM calls");
   if ((cfg.flags & SYNC_RUN_WITHHOLD) && (cfg.withhold_chunk < -1 || cfg.withhold_chunk >= plan->plan.num_chunks))
     return fail(SYNC_EINVAL, "withhold_chunk must be -1 or a chunk id");
   if ((cfg.flags & SYNC_RUN_WITHHOLD) &&
@@ -528,8 +533,8 @@ GemmArgs make_gemm_args(const Plan& pl, const CallCtx& cx, const void* A, const 
 
 // Copy role arguments: copy-in stages chunks from src[x] to dst[x] at the same
 // rows (ntensors tensors of rb[x]-byte rows) and raises the ready flags.
-CopyArgs make_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[2], char* const dst[2],
-                      const int64_t rb[2], int ntensors) {
+CopyArgs make_copy_in(const Plan& pl, const CallCtx& cx, const char* const src[kMaxCopyTensors],
+                      char* const dst[kMaxCopyTensors], const int64_t rb[kMaxCopyTensors], int ntensors) {
   CopyArgs ca{};
   for (int x = 0; x < ntensors; ++x) {
     ca.src[x] = src[x];
@@ -633,7 +638,8 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
 // kernel ends the call instead, the missing chunks' waits timing out.
 template <typename Launch>
 int run_engines(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs, const Roles& r,
-                const char* const src[2], char* const dst[2], const int64_t rb[2], int ntensors, Launch launch) {
+                const char* const src[kMaxCopyTensors], char* const dst[kMaxCopyTensors],
+                const int64_t rb[kMaxCopyTensors], int ntensors, Launch launch) {
   int32_t copied = 0;
   for (int32_t c = 0; c < pl.num_chunks; ++c) copied += pl.resident[c] ? 0 : 1;
   SdmaCall call;
@@ -678,8 +684,8 @@ int run_engines(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed*
 // backend adds its gate kernel and queues the copies on the engines.
 template <typename Launch>
 int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs,
-             const Roles& r, const char* const src[2], char* const dst[2], const int64_t rb[2], int ntensors,
-             Launch launch) {
+             const Roles& r, const char* const src[kMaxCopyTensors], char* const dst[kMaxCopyTensors],
+             const int64_t rb[kMaxCopyTensors], int ntensors, Launch launch) {
   auto timed = [&](hipStream_t st) -> int {
     if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
     int rc = launch(st, r);
@@ -730,6 +736,13 @@ int sync_plan(const sync_plan_desc* desc, sync_plan_t* out) {
         p->ar_items.insert(p->ar_items.end(), item, item + 5);
       }
     }
+  }
+  if (pl.desc.op == SYNC_OP_HEAD_ATTN) {
+    // the attention kernel's work item is a group of hg query heads sharing
+    // one KV head: the plan tiles of each group's first head stand for it
+    const int32_t group = pl.desc.heads_q / pl.desc.heads_kv, hg = std::min(group, 4);
+    for (int32_t t : pl.tile_order)
+      if ((t % pl.tiles_n) % hg == 0) p->head_items.push_back(t);
   }
   bool one_chunk = pl.desc.op == SYNC_OP_GEMM_RS && pl.rows < (int64_t(1) << 31);
   for (int32_t t = 0; one_chunk && t < pl.num_tiles; ++t) one_chunk = pl.dep_ptr[t + 1] - pl.dep_ptr[t] == 1;
@@ -901,9 +914,9 @@ static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
   if (noalloc)  // the scratch keeps the last call's contents: epoch, flags and counters start from zero
     HIP_TRY(launch_fill_u32(cx.ws.hdr, ws_trace_offset(pl.num_chunks) / 4, 0u, static_cast<hipStream_t>(compute)));
-  const char* src[2] = {static_cast<const char*>(a_peer), nullptr};
-  char* dst[2] = {static_cast<char*>(a_local), nullptr};
-  const int64_t rb[2] = {pl.desc.k * 2, 0};
+  const char* src[kMaxCopyTensors] = {static_cast<const char*>(a_peer)};
+  char* dst[kMaxCopyTensors] = {static_cast<char*>(a_local)};
+  const int64_t rb[kMaxCopyTensors] = {pl.desc.k * 2};
   GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
   g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
   const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
@@ -985,9 +998,9 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   {
     // copy-out: rows of C, in send order, into the packed staging slots
     const int64_t es = c_dtype == SYNC_DTYPE_F32 ? 4 : 2;
-    const char* src[2] = {static_cast<const char*>(c), nullptr};
-    char* dst[2] = {static_cast<char*>(staging), nullptr};
-    const int64_t rb[2] = {pl.desc.n * es, 0};
+    const char* src[kMaxCopyTensors] = {static_cast<const char*>(c)};
+    char* dst[kMaxCopyTensors] = {static_cast<char*>(staging)};
+    const int64_t rb[kMaxCopyTensors] = {pl.desc.n * es};
     g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
     g.copy.copy_out = 1;
     g.copy.out_flags = cx.ws.sent;
@@ -1156,9 +1169,9 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   DeviceState::Timed* tm = nullptr;
   if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
   const int64_t row = static_cast<int64_t>(dsc.heads_kv) * dsc.k * 2;  // bytes per token of K or V
-  const char* src[2] = {static_cast<const char*>(k_peer), static_cast<const char*>(v_peer)};
-  char* dst[2] = {static_cast<char*>(k_local), static_cast<char*>(v_local)};
-  const int64_t rb[2] = {row, row};
+  const char* src[kMaxCopyTensors] = {static_cast<const char*>(k_peer), static_cast<const char*>(v_peer)};
+  char* dst[kMaxCopyTensors] = {static_cast<char*>(k_local), static_cast<char*>(v_local)};
+  const int64_t rb[kMaxCopyTensors] = {row, row};
   AttnArgs at{};
   at.q = static_cast<const uint16_t*>(q);
   at.k = static_cast<const uint16_t*>(k_local);
@@ -1191,6 +1204,79 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
                     at.wait_chunks = rr.wait;
                     at.colocated = rr.colocated;
                     if (rr.no_compute) at.sq = 0;
+                    HIP_TRY(launch_ring_attn(at, rr.grid, st));
+                    return SYNC_OK;
+                  });
+}
+
+int sync_head_attn(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q_peer, const void* k_peer,
+                   const void* v_peer, void* q, void* k, void* v, float* o, float* lse, float scale, void* ws,
+                   void* compute, void* copy) {
+  CallCtx cx;
+  int rc = prepare(plan, cfg, ws, SYNC_OP_HEAD_ATTN, cx);
+  if (rc) return rc;
+  const Plan& pl = plan->plan;
+  const auto& dsc = pl.desc;
+  if (dsc.k != kAttnHeadDim) return fail(SYNC_EUNSUPPORTED, "head dim (k) must be 128");
+  const int group = dsc.heads_q / dsc.heads_kv;
+  if (!(group == 1 || group == 2 || group % 4 == 0))
+    return fail(SYNC_EUNSUPPORTED, "heads_q / heads_kv must be 1, 2 or a multiple of 4");
+  const int hg = std::min(group, 4), qb = 32 * (8 / hg);
+  if (dsc.tile_m != qb)
+    return fail(SYNC_EUNSUPPORTED, "tile_m must be the kernel's query block: " + std::to_string(qb) +
+                                       " rows for heads_q / heads_kv = " + std::to_string(group));
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SYNC_EINVAL, "scale must be positive and finite");
+  const bool need_peer = cx.cfg.backend != SYNC_COPY_PRESET && !(cx.cfg.flags & SYNC_RUN_COMPUTE_ONLY);
+  if (!q || !k || !v || !o || (need_peer && (!q_peer || !k_peer || !v_peer))) return fail(SYNC_EINVAL, "NULL operand");
+  for (const void* x : {q_peer, k_peer, v_peer, static_cast<const void*>(q), static_cast<const void*>(k),
+                        static_cast<const void*>(v), static_cast<const void*>(o)})
+    if (x && !aligned16(x)) return fail(SYNC_EINVAL, "operands must be 16-byte aligned");
+  if (dsc.m * dsc.heads_q * dsc.k * 2 >= (int64_t(1) << 31))
+    return fail(SYNC_EUNSUPPORTED, "query tensor too large for 32-bit buffer offsets");
+  DeviceState& d = *cx.dev;
+  std::lock_guard<std::mutex> lk(d.mu);
+  DeviceState::Timed* tm = nullptr;
+  if ((rc = timing_slot(d, cx.cfg.flags & SYNC_RUN_TIMED, &tm))) return rc;
+  const int64_t qrow = static_cast<int64_t>(dsc.heads_q) * dsc.k * 2;   // bytes per token of Q
+  const int64_t kvrow = static_cast<int64_t>(dsc.heads_kv) * dsc.k * 2;  // of K or V
+  const char* src[kMaxCopyTensors] = {static_cast<const char*>(q_peer), static_cast<const char*>(k_peer),
+                                      static_cast<const char*>(v_peer)};
+  char* dst[kMaxCopyTensors] = {static_cast<char*>(q), static_cast<char*>(k), static_cast<char*>(v)};
+  const int64_t rb[kMaxCopyTensors] = {qrow, kvrow, kvrow};
+  AttnArgs at{};
+  at.q = static_cast<const uint16_t*>(q);
+  at.k = static_cast<const uint16_t*>(k);
+  at.v = static_cast<const uint16_t*>(v);
+  at.o = o;
+  at.lse = lse;
+  at.sq = dsc.m;
+  at.heads_q = dsc.heads_q;
+  at.heads_kv = dsc.heads_kv;
+  at.heads_per_item = hg;
+  at.scale = scale;
+  at.init = 1;
+  at.finalize = 1;
+  at.chunk_begin = cx.tab->chunk_begin;
+  at.arrival = cx.tab->arrival;
+  at.resident = cx.tab->resident;
+  at.num_chunks = pl.num_chunks;
+  at.items = cx.tab->head_items;
+  at.num_items = static_cast<int32_t>(plan->head_items.size());
+  at.dep_ptr = cx.tab->dep_ptr;
+  at.dep_idx = cx.tab->dep_idx;
+  at.flags = cx.ws.flags;
+  at.hdr = cx.ws.hdr;
+  at.cnt = counter_arrays(cx, pl.num_chunks);
+  at.timeout_ticks = cx.timeout_ticks;
+  at.nxcd = d.num_xcds;
+  at.copy = make_copy_in(pl, cx, src, dst, rb, 3);
+  const Roles r = roles_for(cx, d, 1);
+  return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), r, src, dst, rb, 3,
+                  [&](hipStream_t st, const Roles& rr) -> int {
+                    at.copy_blocks = rr.copy_blocks;
+                    at.wait_chunks = rr.wait;
+                    at.colocated = rr.colocated;
+                    if (rr.no_compute) at.num_items = 0;
                     HIP_TRY(launch_ring_attn(at, rr.grid, st));
                     return SYNC_OK;
                   });

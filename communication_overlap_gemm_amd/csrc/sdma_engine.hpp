@@ -3,6 +3,8 @@
 
 #include <stdint.h>
 
+#include "kernels/launch_args.hpp"
+
 namespace syncov {
 
 // One call's copies: every non-resident chunk, in arrival order, each tensor
@@ -10,9 +12,9 @@ namespace syncov {
 // set to the 32-bit word at epoch_word.  Chunk i of the copied ones goes to
 // engine i % engines (of those available).
 struct SdmaJob {
-  const char* src[2];
-  char* dst[2];
-  int64_t row_bytes[2];
+  const char* src[kMaxCopyTensors];
+  char* dst[kMaxCopyTensors];
+  int64_t row_bytes[kMaxCopyTensors];
   int32_t ntensors;
   int32_t num_chunks;
   const int64_t* chunk_begin;  // host tables

@@ -55,7 +55,7 @@ enum {
 };
 
 /* ---- plan descriptor --------------------------------------------------- */
-enum { SYNC_OP_AG_GEMM = 1, SYNC_OP_GEMM_RS = 2, SYNC_OP_RING_ATTN = 3 };
+enum { SYNC_OP_AG_GEMM = 1, SYNC_OP_GEMM_RS = 2, SYNC_OP_RING_ATTN = 3, SYNC_OP_HEAD_ATTN = 4 };
 enum { SYNC_PAT_RING = 0, SYNC_PAT_EXPLICIT = 1, SYNC_PAT_HIER_SWIZZLE = 2, SYNC_PAT_MESH = 3 };
 enum { SYNC_ORDER_ROW_MAJOR = 0, SYNC_ORDER_CHUNK_MAJOR = 1, SYNC_ORDER_SWIZZLED = 2 };
 enum { SYNC_B_KN = 0, SYNC_B_NK = 1 };      /* B as [k][n], or [n][k] (Linear weight) */
@@ -73,6 +73,11 @@ enum { SYNC_DTYPE_F32 = 0, SYNC_DTYPE_BF16 = 1 };
  *   [w*R + floor(q*R/split), w*R + floor((q+1)*R/split)), R = m/world.
  * RING_ATTN: m = query rows Sq, n = tokens per KV block, k = head dim d;
  *   the chunked tensors are K and V ([world*n][heads_kv][d]).
+ * HEAD_ATTN (head-parallel attention, the receive side of the all-to-all
+ *   that turns sequence shards into head shards): n = tokens each peer
+ *   sends, m = world*n (every token is a query), k = head dim; heads_q and
+ *   heads_kv are this rank's head group.  The chunked tensors are Q, K and V
+ *   ([world*n][heads][d]); block w comes from peer w.
  * Ring order (pattern RING, direction d = ring_dir):
  *   AG / attention: the shard consumed at step s is (rank - d*s) mod world
  *   (step 0 is the local shard); RS: the shard sent at step s is
@@ -88,8 +93,9 @@ enum { SYNC_DTYPE_F32 = 0, SYNC_DTYPE_BF16 = 1 };
  *   sub-chunk q of every shard is at position q*world + step(shard).
  * Tiles: tile t = i*tiles_n + j covers C rows [i*tile_m, ..) and columns
  *   [j*tile_n, ..) (attention: work item t = i*heads_q + h).  A tile depends
- *   on every chunk its rows meet; its key is the last (AG) / first (RS)
- *   position among them.  Tile order [SYN-S, paper sec. 5.2, Fig. 6; ENT]:
+ *   on every chunk its rows meet (RING_ATTN: on every chunk; HEAD_ATTN: on
+ *   the chunks holding its query rows); its key is the last (AG, attention) /
+ *   first (RS) position among them.  Tile order [SYN-S, paper sec. 5.2, Fig. 6; ENT]:
  *   ROW_MAJOR (t ascending), CHUNK_MAJOR (key, i, j) or SWIZZLED
  *   (key, i / group_m, j, i).
  */
@@ -106,7 +112,7 @@ typedef struct {
   int32_t tile_order;     /* SYNC_ORDER_* */
   int32_t group_m;        /* SWIZZLED group height in tile rows; 0 = 4 */
   int32_t local_resident; /* 1: the rank's own shard is already in place (AG, attention) */
-  int32_t heads_q, heads_kv; /* RING_ATTN only; heads_q % heads_kv == 0 */
+  int32_t heads_q, heads_kv; /* attention ops only; heads_q % heads_kv == 0 */
   int32_t b_layout;       /* SYNC_B_KN or SYNC_B_NK (GEMM ops) */
   const int64_t* shard_rows; /* host, GEMM ops, read only during sync_plan(): NULL = m / world rows
                                 per shard; else world positive row counts summing to m, shard w
@@ -437,6 +443,38 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
                         const void* k_peer, const void* v_peer, void* k_local, void* v_local,
                         float* o, float* m_state, float* l_state, float* lse, float scale,
                         int32_t flags, void* ws, void* compute, void* copy);
+
+/* Head-parallel attention share [SYN-S "Experiments", paper sec. 6.1 and
+ * Fig. 9: head-parallel and sequence-parallel attention among the evaluated
+ * operators; the pages give no scheme, the one used is DeepSpeed-Ulysses', in
+ * SYN-R's references].  Before attention every rank holds a sequence shard of
+ * n tokens of all heads; an all-to-all turns it into a head shard: this rank
+ * receives, from every peer w, the n tokens [w*n, (w+1)*n) of its own head
+ * group.  This call is that receive side fused with the attention over all
+ * world*n tokens of the group: Q, K and V chunks (token blocks, in the plan's
+ * arrival order) are staged from q_peer/k_peer/v_peer into q/k/v, and each
+ * (query block, head group) work item starts once the chunks holding its
+ * queries are in place, then folds the KV chunks in as they land, with the
+ * same fp32 online softmax as sync_ring_attn_step.
+ *   plan: op HEAD_ATTN, m = world*n, heads_q / heads_kv = this rank's group.
+ *   q_* bf16 [world*n][heads_q][k]; k_*, v_* bf16 [world*n][heads_kv][k];
+ *   the *_peer tensors hold at rows [w*n, (w+1)*n) what peer w sends (on one
+ *   GPU: device buffers standing for the peers'); q, k, v are filled with
+ *   every non-resident chunk's rows (the resident one, this rank's own
+ *   block, must be in place already).
+ *   o fp32 [world*n][heads_q][k] = softmax(scale q.k^T) v per head (query
+ *   head h reads KV head h / (heads_q / heads_kv)); lse fp32 [heads_q][world*n]
+ *   (natural log of the softmax denominator) or NULL.
+ * Kernel constraints (else EUNSUPPORTED): k == 128; heads_q / heads_kv is 1,
+ *   2 or a multiple of 4; tile_m == 32 * 8 / min(heads_q / heads_kv, 4) (the
+ *   kernel's query block: 64, 128 or 256 rows); the plan's tile order is the
+ *   order work items are taken in.  cfg as for sync_ring_attn_step (backends
+ *   CU, COLOCATED, SDMA or PRESET; COPY_ONLY, COMPUTE_ONLY, TIMED, WITHHOLD).
+ *   A work item whose chunks never arrive leaves its outputs untouched and
+ *   the call returns ETIMEOUT. */
+int sync_head_attn(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q_peer, const void* k_peer,
+                   const void* v_peer, void* q, void* k, void* v, float* o, float* lse, float scale, void* ws,
+                   void* compute, void* copy);
 
 /* ---- autotuner ------------------------------------------------------------ */
 /* Picks the fastest overlapped configuration of a GEMM call (AG or RS) by

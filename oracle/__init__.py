@@ -10,6 +10,8 @@ Contents (each cites the passage it follows in its own header):
   gemm_ref.c     fp64 matrix product R = A . B (full and sampled)
   attn_ref.c     fp64 direct two-pass softmax attention (full and sampled)
   attention.py   fp64 blockwise online-softmax merge (to check the merge identity)
+  head_parallel.py the head-parallel attention share: the all-to-all's head
+                 group of each rank, and direct attention on it
   planner_ref.py reference chunk planner (chunk rows, ring positions, tile
                  dependencies, tile orders)
 Pins: tests/test_oracle_*.py check every function here against closed forms,
@@ -25,9 +27,10 @@ import os
 import numpy as np
 
 from .planner_ref import (  # noqa: F401
-    OP_AG_GEMM, OP_GEMM_RS, OP_RING_ATTN, ORDER_CHUNK_MAJOR, ORDER_ROW_MAJOR, ORDER_SWIZZLED,
+    OP_AG_GEMM, OP_GEMM_RS, OP_HEAD_ATTN, OP_RING_ATTN, ORDER_CHUNK_MAJOR, ORDER_ROW_MAJOR, ORDER_SWIZZLED,
     PAT_EXPLICIT, PAT_HIER_SWIZZLE, PAT_MESH, PAT_RING, PlanDesc, PlanError, PlanTables, plan_ref)
 from .attention import attention_online_f64  # noqa: F401
+from .head_parallel import head_group, head_parallel_attention_f64  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

@@ -44,6 +44,11 @@ Reading, in the order the planner applies it:
   resident(c) = local_resident and w == r and op != RS.
   tiles: Tm = ceil(M/TM), Tn = ceil(N/TN), t = i*Tn + j, rows(i) = [i*TM, min((i+1)*TM, M))
          attention: Tm = ceil(Sq/TM), Tn = Hq (work item t = i*Hq + h), deps = all chunks
+         head-parallel attention (the all-to-all receive side of sequence
+         parallelism: every rank holds all Sq = W*n tokens of its heads, token
+         block w from peer w; Q, K and V arrive together): Tm = ceil(Sq/TM),
+         Tn = Hq, deps = the chunks holding the item's query rows (its K and V
+         blocks are folded in as they land)
   deps(t) = {c : [begin(c), end(c)) meets rows(i)} ascending; inv = its transpose
   key(t)  = max pos over deps (AG, attention) / min pos over deps (RS)
   orders: ROW_MAJOR  t ascending
@@ -55,7 +60,7 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 from typing import List, Optional
 
-OP_AG_GEMM, OP_GEMM_RS, OP_RING_ATTN = 1, 2, 3
+OP_AG_GEMM, OP_GEMM_RS, OP_RING_ATTN, OP_HEAD_ATTN = 1, 2, 3, 4
 PAT_RING, PAT_EXPLICIT, PAT_HIER_SWIZZLE, PAT_MESH = 0, 1, 2, 3
 ORDER_ROW_MAJOR, ORDER_CHUNK_MAJOR, ORDER_SWIZZLED = 0, 1, 2
 DEFAULT_GROUP_M = 4
@@ -114,8 +119,9 @@ def _ceil_div(a: int, b: int) -> int:
 def plan_ref(desc: PlanDesc) -> PlanTables:
     """Build the chunk and tile tables for one descriptor (reading above)."""
     d = desc
-    if d.op not in (OP_AG_GEMM, OP_GEMM_RS, OP_RING_ATTN):
+    if d.op not in (OP_AG_GEMM, OP_GEMM_RS, OP_RING_ATTN, OP_HEAD_ATTN):
         raise PlanError("op")
+    attn = d.op in (OP_RING_ATTN, OP_HEAD_ATTN)
     if d.world < 1 or not (0 <= d.rank < d.world) or d.ring_dir not in (1, -1):
         raise PlanError("world/rank/ring_dir")
     if d.m < 1 or d.n < 1 or d.k < 1 or d.tile_m < 1:
@@ -125,11 +131,13 @@ def plan_ref(desc: PlanDesc) -> PlanTables:
     G = d.group_m if d.group_m > 0 else DEFAULT_GROUP_M
     W, r, s = d.world, d.rank, d.split
 
-    if d.op == OP_RING_ATTN:
+    if attn:
         if d.heads_q < 1 or d.heads_kv < 1 or d.heads_q % d.heads_kv:
             raise PlanError("heads")
         if d.shard_rows is not None:
             raise PlanError("shard_rows")
+        if d.op == OP_HEAD_ATTN and d.m != W * d.n:
+            raise PlanError("head-parallel attention: the queries are every token (m = world * n)")
         R = d.n                       # tokens per KV block
         M_rows = W * d.n              # rows of the chunked (KV) tensor
         rows_of = [R] * W
@@ -198,7 +206,8 @@ def plan_ref(desc: PlanDesc) -> PlanTables:
         Tm, Tn = _ceil_div(d.m, d.tile_m), d.heads_q
         deps_of_row = [list(range(C)) for _ in range(Tm)]
     else:
-        Tm, Tn = _ceil_div(d.m, d.tile_m), _ceil_div(d.n, d.tile_n)
+        Tm = _ceil_div(d.m, d.tile_m)
+        Tn = d.heads_q if d.op == OP_HEAD_ATTN else _ceil_div(d.n, d.tile_n)
         deps_of_row = []
         for i in range(Tm):
             lo, hi = i * d.tile_m, min((i + 1) * d.tile_m, d.m)

@@ -222,3 +222,22 @@ def test_split_baseline_validation():
     assert "copy stream" in A.sync_last_error()
     for bad in (A.make_cfg(A.SYNC_COPY_COLOCATED), A.make_cfg(A.SYNC_COPY_CU, 16, flags=A.SYNC_RUN_TIMED)):
         assert lib.sync_gemm_split(ag.handle, ctypes.byref(bad), *args, None, 0x10) == A.SYNC_EINVAL
+
+
+def test_head_attn_validation():
+    """sync_head_attn: a HEAD_ATTN plan whose queries are every token, no
+    trace mode; checked before any device work."""
+    lib = A.lib()
+    with pytest.raises(A.SyncError) as ei:
+        A.sync_plan(A.make_desc(A.SYNC_OP_HEAD_ATTN, 48, 16, 128, 4, tile_m=64, heads_q=4, heads_kv=1))
+    assert ei.value.code == A.SYNC_EINVAL and "every token" in ei.value.message
+    hp = A.sync_plan(A.make_desc(A.SYNC_OP_HEAD_ATTN, 64, 16, 128, 4, tile_m=64, heads_q=4, heads_kv=1))
+    at = A.sync_plan(A.make_desc(A.SYNC_OP_RING_ATTN, 64, 16, 128, 4, heads_q=4, heads_kv=1))
+    args = [0x1000] * 8
+    assert lib.sync_head_attn(at.handle, None, *args, 1.0, 256, None, None) == A.SYNC_EINVAL
+    assert "different op" in A.sync_last_error()
+    tr = A.make_cfg(A.SYNC_COPY_CU, copy_cus=8, flags=A.SYNC_RUN_TRACE)
+    assert lib.sync_head_attn(hp.handle, ctypes.byref(tr), *args, 1.0, 256, None, None) == A.SYNC_EINVAL
+    assert "TRACE" in A.sync_last_error()
+    info = A.sync_plan_get_info(hp)
+    assert info.num_chunks == 4 and info.num_tiles == 4

@@ -24,6 +24,7 @@ from communication_overlap_gemm_amd import inputs
 from gpu_util import check_full_f32, dev_bits, workspace
 from test_gpu_ag_gemm import _samples, run_ag
 from test_gpu_gemm_rs import check_staging, run_rs
+from test_gpu_head_attn import run_head
 from test_gpu_ring_attn import TOL, run_attn
 
 pytestmark = pytest.mark.gpu
@@ -268,3 +269,40 @@ def test_attention_row_agents(name):
     assert np.isfinite(on).all() and np.isfinite(ln_).all()
     assert np.max(np.abs(on[qi, hi] - ref_o)) <= TOL
     assert np.max(np.abs(ln_[hi, qi] - ref_lse)) <= TOL
+
+
+# ---- head-parallel attention row ----------------------------------------------------
+
+@pytest.mark.parametrize("name", sorted(bench.HEAD_AGENTS))
+def test_head_attention_row_agents(name):
+    """The Llama-3-8B-like head-parallel share (one rank's 4 query / 1 KV
+    heads over 8 x 4096 tokens, rank 0) with each agent the row times:
+    sampled (query, head) rows of O and LSE within 2e-3 of the oracle."""
+    ag = bench.HEAD_AGENTS[name]
+    w, n, hq, hkv, d = (bench.HEAD_SHAPE[x] for x in ("world", "n", "hq", "hkv", "d"))
+    s = w * n
+    q, k, v = inputs.attention_operands(s, hq, s, hkv, d)
+    rc, _, o, lse, _, _ = run_head(w, n, 0, q, k, v, backend=ag["backend"], cus=ag.get("copy_cus", 0),
+                                   teams=ag.get("copy_teams", 0))
+    assert rc == A.SYNC_OK
+    rng = np.random.default_rng(7)
+    qi = np.concatenate([rng.integers(0, s, 600), [0, n, s - 1]])
+    hi = np.concatenate([rng.integers(0, hq, 600), [0, 1, hq - 1]])
+    ref_o, ref_lse = oracle.attention_f64_sampled(q, k, v, 1 / math.sqrt(d), qi, hi)
+    on, ln_ = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(on).all() and np.isfinite(ln_).all()
+    assert np.max(np.abs(on[qi, hi] - ref_o)) <= TOL
+    assert np.max(np.abs(ln_[hi, qi] - ref_lse)) <= TOL
+
+
+def test_head_attention_row_copy_only():
+    """The row's copy-only agent stages Q, K and V bit for bit."""
+    ag = bench.HEAD_COPY_ONLY
+    w, n, hq, hkv, d = (bench.HEAD_SHAPE[x] for x in ("world", "n", "hq", "hkv", "d"))
+    s = w * n
+    q, k, v = inputs.attention_operands(s, hq, s, hkv, d)
+    rc, _, _, _, peers, local = run_head(w, n, 0, q, k, v, backend=ag["backend"], cus=ag["copy_cus"],
+                                         teams=ag["copy_teams"], flags=ag["flags"])
+    assert rc == A.SYNC_OK
+    for p, l in zip(peers, local):
+        assert torch.equal(p, l)

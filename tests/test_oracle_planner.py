@@ -89,7 +89,7 @@ def _check_invariants(desc, t):
         deps = t.dep_idx[t.dep_ptr[tile]:t.dep_ptr[tile + 1]]
         if desc.op == P.OP_RING_ATTN:
             want = list(range(C))
-        else:
+        else:  # GEMM ops and head-parallel attention: the chunks holding the tile's rows
             rows = range(i * desc.tile_m, min((i + 1) * desc.tile_m, desc.m))
             want = sorted({next(c for c in range(C) if t.chunk_begin[c] <= row < t.chunk_begin[c + 1])
                            for row in rows})
@@ -116,7 +116,7 @@ def _check_invariants(desc, t):
         assert t.resident[c] == int(own and desc.local_resident and desc.op != P.OP_GEMM_RS)
     # aligned case: one dependency per tile, equal tile counts per chunk
     if desc.op != P.OP_RING_ATTN:
-        R = desc.m // desc.world
+        R = desc.m // desc.world  # head-parallel attention: n tokens per peer
         if R % desc.split == 0 and (R // desc.split) % desc.tile_m == 0:
             assert all(t.dep_ptr[x + 1] - t.dep_ptr[x] == 1 for x in range(T))
             assert set(t.tiles_in) == {(R // desc.split // desc.tile_m) * t.tiles_n}
@@ -140,6 +140,10 @@ def _enumerate():
     for W, n, s, tm in itertools.product((1, 2, 3), (2, 3), (1, 2), (1, 3)):
         yield P.PlanDesc(op=P.OP_RING_ATTN, m=5, n=n, k=8, world=W, rank=W - 1, split=s, tile_m=tm,
                          tile_n=1, heads_q=4, heads_kv=2, tile_order=1)
+    for W, n, s, tm, order in itertools.product((1, 2, 3, 4), (2, 3, 5), (1, 2), (1, 2, 4), (0, 1, 2)):
+        for r in sorted({0, W - 1}):
+            yield P.PlanDesc(op=P.OP_HEAD_ATTN, m=W * n, n=n, k=8, world=W, rank=r, split=s, tile_m=tm,
+                             heads_q=2, heads_kv=1, tile_order=order, group_m=2)
 
 
 def test_invariants_brute_force_enumeration():
@@ -175,6 +179,34 @@ def test_rejects_invalid(bad):
 def test_attention_requires_grouped_heads():
     with pytest.raises(P.PlanError):
         P.plan_ref(P.PlanDesc(op=P.OP_RING_ATTN, m=4, n=4, k=8, world=2, tile_m=2, heads_q=3, heads_kv=2))
+    with pytest.raises(P.PlanError):
+        P.plan_ref(P.PlanDesc(op=P.OP_HEAD_ATTN, m=8, n=4, k=8, world=2, tile_m=2, heads_q=3, heads_kv=2))
+
+
+@pytest.mark.parametrize("m", [4, 7, 9])
+def test_head_parallel_queries_are_every_token(m):
+    """Head-parallel attention: after the all-to-all every token of the head
+    group is a query, so m must be world * n."""
+    with pytest.raises(P.PlanError):
+        P.plan_ref(P.PlanDesc(op=P.OP_HEAD_ATTN, m=m, n=4, k=8, world=2, tile_m=2, heads_q=2, heads_kv=1))
+
+
+def test_head_parallel_items_start_with_their_queries():
+    """Every tile's key is the position of the last chunk holding its query
+    rows, so in chunk-major order the tiles whose queries are resident come
+    first, and a tile's queries have all arrived by its key."""
+    for W in (2, 4, 8):
+        for r in range(W):
+            t = P.plan_ref(P.PlanDesc(op=P.OP_HEAD_ATTN, m=W * 8, n=8, k=8, world=W, rank=r, split=2, tile_m=4,
+                                      heads_q=4, heads_kv=1))
+            first = t.tile_order[:(8 // 4) * t.tiles_n]  # the own block's 2 tile rows x 4 heads
+            assert all(t.resident[c] for x in first for c in t.dep_idx[t.dep_ptr[x]:t.dep_ptr[x + 1]])
+            for x in t.tile_order:
+                ps = [t.chunk_pos[c] for c in t.dep_idx[t.dep_ptr[x]:t.dep_ptr[x + 1]]]
+                rows = range((x // t.tiles_n) * 4, (x // t.tiles_n) * 4 + 4)
+                assert all(any(t.chunk_begin[c] <= q < t.chunk_begin[c + 1] and t.chunk_pos[c] <= t.tile_key[x]
+                               for c in range(t.num_chunks)) for q in rows)
+                assert max(ps) == t.tile_key[x]
 
 
 def test_uneven_shards_hand_worked():

@@ -40,6 +40,9 @@ def _enumerate():
     for W, n, s, tm in itertools.product((1, 2, 3), (2, 3), (1, 2), (1, 3)):
         yield dict(op=P.OP_RING_ATTN, m=5, n=n, k=8, world=W, rank=0, split=s, tile_m=tm, tile_n=1,
                    heads_q=4, heads_kv=2, tile_order=1)
+    for W, n, s, tm, order in itertools.product((1, 2, 3, 4), (2, 5), (1, 2), (1, 3, 4), (0, 1, 2)):
+        yield dict(op=P.OP_HEAD_ATTN, m=W * n, n=n, k=8, world=W, rank=W // 2, split=s, tile_m=tm, tile_n=1,
+                   heads_q=4, heads_kv=1, tile_order=order, group_m=2)
 
 
 def test_enumeration_bit_exact():
@@ -63,6 +66,9 @@ WORKLOADS = [
       for s in (1, 4, 16, 64) for o in (0, 1, 2)],
     # ring-attention step: 4096 queries, 8 KV blocks of 4096 tokens, 32/8 heads
     dict(op=3, m=4096, n=4096, k=128, world=8, tile_m=128, tile_n=1, heads_q=32, heads_kv=8),
+    # head-parallel attention share: 8 peers x 4096 tokens, one rank's 4/1 heads, 64-row query blocks
+    *[dict(op=4, m=32768, n=4096, k=128, world=8, rank=3, split=s, tile_m=64, tile_n=1, heads_q=4, heads_kv=1,
+           tile_order=o) for s in (1, 4) for o in (0, 1, 2)],
 ]
 
 
@@ -75,12 +81,13 @@ def test_hier_swizzle_and_mesh_bit_exact():
     """The hierarchical-swizzle and mesh patterns: both planners agree bit
     for bit over worlds, group sizes, ranks, directions, splits and orders."""
     n = 0
-    for op in (P.OP_AG_GEMM, P.OP_GEMM_RS, P.OP_RING_ATTN):
+    for op in (P.OP_AG_GEMM, P.OP_GEMM_RS, P.OP_RING_ATTN, P.OP_HEAD_ATTN):
         for W in (1, 2, 4, 6, 8):
             for r in sorted({0, W // 2, W - 1}):
                 for s, order in itertools.product((1, 3), (0, 1, 2)):
-                    attn = op == P.OP_RING_ATTN
-                    base = dict(op=op, m=W * 6 if not attn else 7, n=5 if not attn else 6, k=3 if not attn else 8,
+                    attn = op in (P.OP_RING_ATTN, P.OP_HEAD_ATTN)
+                    m = W * 6 if op == P.OP_HEAD_ATTN else (7 if attn else W * 6)
+                    base = dict(op=op, m=m, n=6 if attn else 5, k=8 if attn else 3,
                                 world=W, rank=r, split=s, tile_m=4, tile_n=1 if attn else 2, tile_order=order,
                                 group_m=2, **(dict(heads_q=4, heads_kv=2) if attn else {}))
                     for g in [x for x in range(1, W + 1) if W % x == 0]:
