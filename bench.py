@@ -180,6 +180,9 @@ def parse(argv=None):
                    help="headline series: cold (512 MiB written between calls) or warm (back to back)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-rows", action="store_true", help="only the headline workload")
+    p.add_argument("--attention-only", action="store_true",
+                   help="time only the ring-attention and head-parallel attention rows (--steps/--warmup calls "
+                        "per agent) and print them as one JSON object (a profiling aid, not the bench line)")
     p.add_argument("--tune", action="store_true",
                    help="run the autotuner over split {1,2,4} x tile {256x256, 256x128} x copy agent (SDMA on 7 "
                         "engines, 16 or 32 copy CUs with 4 K-slices, co-located) first and bench its choice")
@@ -262,6 +265,9 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     timer = Timer(torch)
+    if args.attention_only:
+        print(json.dumps(attention_rows(timer, torch, inputs, stream, args.steps, args.warmup)), flush=True)
+        return
     cold = args.cache == "cold"
     tuned = None
     if args.tune:
@@ -627,6 +633,21 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
         "frac_mfma_peak": round(flops / t[best] / 1e12 / PEAK_BF16_TFLOPS, 4),
         "t_overlap_us_by_agent": {nm: round(t[nm] * 1e6, 1) for nm in A2A_AGENTS}}
     del ap, b, al, c
+    out.update(attention_rows(timer, torch, inputs, stream, steps, warmup))
+    return out
+
+
+def attention_rows(timer, torch, inputs, stream, steps=5, warmup=2):
+    """The ring-attention step and the head-parallel share, cold cache."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    out = {}
+
+    def t_of(fn, ws):
+        st = timer.series(fn, steps, warmup, True)
+        check(ws, stream)
+        return st["median_s"]
 
     # Ring attention: Q 4096x32x128, K/V 8 blocks of 4096 tokens x 8 heads x 128, non-causal
     sq, hq, hkv, d, nb, w = (ATTN_SHAPE[x] for x in ("sq", "hq", "hkv", "d", "n", "world"))

@@ -257,35 +257,48 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
           const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Ks[buf][key * 16 + kswz(key, ds * 2 + half)]);
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kb], 0, 0, 0);
         }
-      // online softmax for this lane's query over the tile's keys
-      float mloc = -INFINITY;
+      // online softmax for this lane's query over the tile's keys; keys past
+      // the chunk's last one (only on its last, partial tile) are masked
+      if (valid < kKT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (key >= valid) s[kb][i] = -INFINITY;
+          }
+      }
+      float mraw = s[0][0];  // tile max of the unscaled scores (scale > 0)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const float t = key < valid ? s[kb][i] * c2 : -INFINITY;
-          s[kb][i] = t;
-          mloc = fmaxf(mloc, t);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float mnew = fmaxf(m2, mloc);
-      const float alpha = mnew == -INFINITY ? 1.f : exp2f(m2 - mnew);
+        for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[kb][i]);
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+      // (l, O) are rescaled only on tiles where some query's max grows; for
+      // the others alpha would be exactly 1, so skipping it changes nothing.
+      // The max key of each query keeps probability exactly 1.
+      const float mt = mraw * c2;
+      if (__ballot(mt > m2)) {
+        const float mnew = fmaxf(m2, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);  // 0 on the first tile (m2 = -inf)
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o[b] *= alpha;
+        m2 = mnew;
+      }
+      const float nm = -m2;
       float lsum = 0.f;
       bf16x8_t pf[4];  // P^T as B operands: k-steps of 16 keys
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = exp2f(s[kb][i] - mnew);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, nm));  // masked keys: exp2(-inf) = 0
           lsum += pv;
           pf[kb * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(pv);
         }
       lsum += __shfl_xor(lsum, 32, 64);
-      l = l * alpha + lsum;
-      m2 = mnew;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) o[b] *= alpha;
+      l += lsum;
       // O^T += V^T P^T: 4 blocks of 32 dims x 4 k-steps of 16 keys
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
