@@ -25,7 +25,7 @@
 //    the rescale by e^(m-m') is a per-lane multiply.
 //  * exp2 with the scale folded into log2(e) units; probabilities go to bf16
 //    for the PV product, the running sum stays fp32.
-//  * KV tiles of 64 keys, double-buffered in LDS (64 KB), prefetched one tile
+//  * KV tiles of 64 keys, double-buffered in LDS (66 KB), prefetched one tile
 //    ahead through registers; raw buffer loads return zero past a chunk's
 //    last key, and those keys are masked to -inf.
 //
@@ -57,18 +57,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
 }
 
-// K tile rows are 256 bytes (16 slots): swizzle the slot with the row.
-__device__ __forceinline__ int kswz(int row, int slot) { return slot ^ (row & 15); }
-// V^T rows are 128 bytes (8 slots).
-__device__ __forceinline__ int vswz(int row, int slot) { return slot ^ ((row ^ (row >> 3)) & 7); }
+// LDS rows are padded by one 16-byte slot (K: 16 slots of 8 dims per key,
+// V^T: 8 slots of 8 keys per dim), so the 16 lanes of a 128-bit read, one row
+// each, start on 16 distinct 4-bank groups, and a lane's reads differ from
+// one another by immediate offsets only.
+constexpr int kKRow = 17, kVRow = 9;
+
+// Scheduling hint for a block of N MFMAs fed by N LDS reads: issue AHEAD
+// reads first, then alternate one MFMA and one read, so AHEAD reads stay in
+// flight instead of one read being waited for before each MFMA.
+template <int N, int AHEAD>
+__device__ __forceinline__ void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
 
 // Physical position (0..15) inside a 16-key k-step -> key offset.  Lane half h
 // holds keys {4h..4h+3, 8+4h..8+4h+3} of the step in the score accumulator.
 __device__ __forceinline__ int perm16(int phys) { return ((phys >> 3) << 2) + ((phys >> 2) & 1) * 8 + (phys & 3); }
 
 __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
-  __shared__ u32x4_t Ks[2][kKT * 16];  // [key][16 slots of 8 d]
-  __shared__ u32x4_t Vt[2][kD * 8];    // [dv][8 slots of 8 permuted keys]
+  __shared__ u32x4_t Ks[2][kKT * kKRow];  // [key][16 slots of 8 d + pad]
+  __shared__ u32x4_t Vt[2][kD * kVRow];   // [dv][8 slots of 8 permuted keys + pad]
   __shared__ int32_t s_ok;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -202,7 +217,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int gi = tid + i * kAttnThreads, key = gi >> 4, sl = gi & 15;
-        Ks[buf][key * 16 + kswz(key, sl)] = rk[i];
+        Ks[buf][key * kKRow + sl] = rk[i];
       }
       const int dp = tid & 63, kg = tid >> 6;
 #pragma unroll
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
           w[j] = e ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
         }
         const int dv = dp * 2 + e;
-        Vt[buf][dv * 8 + vswz(dv, kg)] = w;
+        Vt[buf][dv * kVRow + kg] = w;
       }
     };
     auto advance = [&](int& pos, int64_t& t) {  // next tile; pos == C when done
@@ -248,25 +263,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
       }
 
       // S^T = K Q^T: two 32-key blocks
+      // (the two 32-key blocks' chains alternate; all 16 K fragments are read first)
       f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+      {
+        bf16x8_t kf[8][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int ds = 0; ds < 8; ++ds)
 #pragma unroll
-        for (int ds = 0; ds < 8; ++ds) {
-          const int key = kb * 32 + col;
-          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Ks[buf][key * 16 + kswz(key, ds * 2 + half)]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kb], 0, 0, 0);
-        }
+          for (int kb = 0; kb < 2; ++kb)
+            kf[ds][kb] = __builtin_bit_cast(bf16x8_t, Ks[buf][(kb * 32 + col) * kKRow + ds * 2 + half]);
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kb], qf[ds], s[kb], 0, 0, 0);
+        sched_reads_ahead<16, 8>();
+      }
       // online softmax for this lane's query over the tile's keys; keys past
       // the chunk's last one (only on its last, partial tile) are masked
       if (valid < kKT) {
+        const int lim = valid - 4 * half;  // key - 4 * half is a constant per register
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= valid) s[kb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[kb][i] = -INFINITY;
       }
       float mraw = s[0][0];  // tile max of the unscaled scores (scale > 0)
 #pragma unroll
@@ -300,14 +321,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
       lsum += __shfl_xor(lsum, 32, 64);
       l += lsum;
       // O^T += V^T P^T: 4 blocks of 32 dims x 4 k-steps of 16 keys
+      {
+        bf16x8_t vf[4][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int dv = b * 32 + col;
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, Vt[buf][dv * 8 + vswz(dv, ks * 2 + half)]);
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[b], 0, 0, 0);
-        }
+          for (int b = 0; b < 4; ++b)
+            vf[ks][b] = __builtin_bit_cast(bf16x8_t, Vt[buf][(b * 32 + col) * kVRow + ks * 2 + half]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][b], pf[ks], o[b], 0, 0, 0);
+        sched_reads_ahead<16, 8>();
+      }
       if (more) store_tile(buf ^ 1);
       __syncthreads();
       buf ^= 1;
