@@ -430,7 +430,8 @@ int sync_gemm_split(sync_plan_t plan, const sync_copy_cfg* cfg, const void* a_pe
  *   o fp32 [m][heads_q][k]; m_state, l_state fp32 [heads_q][m];
  *   lse fp32 [heads_q][m] or NULL (written when FINALIZE).
  *   m_state is in natural-log units (max of scale * q.k); l_state is the sum
- *   of exp(score - m); o holds the unnormalised sum unless FINALIZE.
+ *   of exp(score - m); o holds the unnormalised sum unless FINALIZE.  The
+ *   probabilities multiplying V are rounded to bf16 (l sums them unrounded).
  *   flags: SYNC_ATTN_INIT starts from m=-inf, l=0, O=0 (else reads the
  *   state); SYNC_ATTN_FINALIZE writes O/l to o and m + ln l to lse (and the
  *   final m, l to the state).  Non-causal, no masking; scale > 0.
