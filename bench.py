@@ -189,6 +189,11 @@ def parse(argv=None):
     return p.parse_args(argv)
 
 
+def progress(msg):
+    """One line per finished row on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 # ---- timing ------------------------------------------------------------------
 class Timer:
     """Device-event timing of calls on the current stream (the stream every
@@ -311,6 +316,7 @@ def main(argv=None):
             "overlapped": series(cfg(**agent), args.steps, args.warmup, mode == "cold"),
             "compute_only": series(cfg(backend=PRESET), args.steps, args.warmup, mode == "cold"),
             "copy_only": series(cfg(flags=A.SYNC_RUN_COPY_ONLY, **agent), args.steps, args.warmup, mode == "cold")}
+    progress("headline series done")
     head = res[args.cache]
     flops = 2.0 * M * N * K
     t_ovl = head["overlapped"]["mean_s"]
@@ -366,7 +372,7 @@ def main(argv=None):
             "frac": round(value / PEAK_BF16_TFLOPS, 4),
             "traffic": profiled_traffic(args),
             "traffic_note": "FETCH_SIZE + WRITE_SIZE per launch: bytes between the L2s and the memory fabric "
-                            "(Infinity Cache hits included), warm series",
+                            "(Infinity Cache hits included), cold overlapped series, scaled by a copy-only calibration",
             "kernel": kname,
             "flops_per_launch": flops,
             "launch_mean_us": round(t_ovl * 1e6, 2),
@@ -376,18 +382,24 @@ def main(argv=None):
         line["autotune"] = tuned
     if not args.no_other_rows:
         line["copy_backend_sweep"] = backend_sweep(series, flops)
+        progress("copy backend sweep done")
         line["split_sweep"] = split_sweep(series, torch, tm, tn, order, b_layout)
+        progress("split sweep done")
         line["trace_headline"] = trace_headline(plan, agent, a_peer, a_local, b, c_out, c_dtype, ws, stream, tabs)
         line["layout_kn_row"] = layout_kn_row(timer, torch, inputs, stream)
         line["split_baseline"] = {"ag_llama8b_up": split_baseline_ag(timer, plan, a_peer, a_local, b, c_out, c_dtype, ws,
                                                                      stream, torch, res["cold"]["overlapped"])}
+        progress("trace, B-layout and split-baseline rows done")
         del a_peer, a_local, b, c_out
         torch.cuda.empty_cache()
         line["other_rows"] = other_rows(timer, torch, inputs, stream)
+        progress("other rows done")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a_bits, b_bits, args.layout)
+        progress("CPU baseline done")
         if not args.no_other_rows:
             line["cpu_baseline_by_config"] = cpu_baseline_by_config(inputs)
+            progress("CPU baseline by configuration done")
     print(json.dumps(line), flush=True)
 
 
@@ -563,6 +575,7 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
                              "gap_cv": round(float(gaps.std() / gaps.mean()), 3) if gaps.mean() > 0 else None}}
     del a, b, c, st
 
+    progress("GEMM-RS and GEMM-AR rows done")
     # AG-GEMM 70B-like: A 16384x8192 (8 shards of 2048 rows), B 8192x3584 stored [n][k], C fp32
     m, n, k, w = (AG70_SHAPE[x] for x in ("m", "n", "k", "world"))
     a_bits, b_bits = inputs.gemm_operands(m, n, k, AG70_SHAPE["divisor"], b_layout="nk")
@@ -605,6 +618,7 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
         "chunk_size_x_tile_order_sweep": {"agent": "colocated", "by_split_order": sweep}}
     del ap, b, al, c, wss, plans
 
+    progress("70B-like AG row done")
     # A2A-GEMM receive side, MoE-like: 8 peers send uneven token blocks to this rank's expert
     m, n, k, w = (A2A_SHAPE[x] for x in ("m", "n", "k", "world"))
     rows = inputs.routed_token_counts(m, w)
@@ -677,6 +691,7 @@ def attention_rows(timer, torch, inputs, stream, steps=5, warmup=2):
         "frac_mfma_peak": round(flops / t["overlapped"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del q, kp, vp, kl, vl, o, ms, ls, lse
 
+    progress("ring attention row done")
     # Head-parallel share: Q, K, V of one head group arrive as 8 token blocks (7 from peers)
     w, nb, hq, hkv, d = (HEAD_SHAPE[x] for x in ("world", "n", "hq", "hkv", "d"))
     s = w * nb
