@@ -106,7 +106,8 @@ class sync_tune_result(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_order", ctypes.c_int32), ("copy_cus", ctypes.c_int32), ("best_ms", ctypes.c_float),
                 ("candidates_run", ctypes.c_int32), ("candidates_skipped", ctypes.c_int32),
-                ("backend", ctypes.c_int32), ("agent", ctypes.c_int32)]
+                ("backend", ctypes.c_int32), ("agent", ctypes.c_int32), ("from_cache", ctypes.c_int32),
+                ("call_wall_ms", ctypes.c_float), ("search_wall_ms", ctypes.c_float)]
 
 
 class sync_timing(ctypes.Structure):
@@ -352,7 +353,8 @@ def sync_autotune(base: sync_plan_desc, space, *, a, b, c, ws, c_dtype: int = SY
     _check(lib().sync_autotune(ctypes.byref(base), ctypes.byref(sp), ctypes.byref(bufs), ctypes.byref(r)))
     return {"split": r.split, "tile_m": r.tile_m, "tile_n": r.tile_n, "tile_order": r.tile_order,
             "copy_cus": r.copy_cus, "best_ms": r.best_ms, "candidates_run": r.candidates_run,
-            "candidates_skipped": r.candidates_skipped, "backend": r.backend, "agent": r.agent}
+            "candidates_skipped": r.candidates_skipped, "backend": r.backend, "agent": r.agent,
+            "from_cache": r.from_cache, "call_wall_ms": r.call_wall_ms, "search_wall_ms": r.search_wall_ms}
 
 
 def sync_tune_forget() -> None:

@@ -10,6 +10,7 @@
 // are the knobs of the reordered GEMM (Entwine abstract).
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cstdio>
 #include <cstdlib>
 #include <fstream>
@@ -39,7 +40,7 @@ const char* cache_path() {
 }
 
 // Cache file: one line per result,
-// "key<TAB>split tile_m tile_n order copy_cus best_ms backend agent".
+// "key<TAB>split tile_m tile_n order copy_cus best_ms backend agent search_wall_ms".
 void load_file_locked() {
   const char* path = cache_path();
   if (!path || g_file_loaded == path) return;
@@ -51,8 +52,10 @@ void load_file_locked() {
     if (tab == std::string::npos) continue;
     sync_tune_result r{};
     std::istringstream in(line.substr(tab + 1));
-    if (in >> r.split >> r.tile_m >> r.tile_n >> r.tile_order >> r.copy_cus >> r.best_ms >> r.backend >> r.agent)
+    if (in >> r.split >> r.tile_m >> r.tile_n >> r.tile_order >> r.copy_cus >> r.best_ms >> r.backend >> r.agent) {
+      if (!(in >> r.search_wall_ms)) r.search_wall_ms = 0.f;  // lines written before the field existed
       g_cache[line.substr(0, tab)] = r;
+    }
   }
 }
 
@@ -61,7 +64,7 @@ void append_file_locked(const std::string& key, const sync_tune_result& r) {
   if (!path) return;
   std::ofstream f(path, std::ios::app);
   f << key << '\t' << r.split << ' ' << r.tile_m << ' ' << r.tile_n << ' ' << r.tile_order << ' ' << r.copy_cus << ' '
-    << r.best_ms << ' ' << r.backend << ' ' << r.agent << '\n';
+    << r.best_ms << ' ' << r.backend << ' ' << r.agent << ' ' << r.search_wall_ms << '\n';
 }
 
 std::string list_str(const int32_t* v, int32_t n) {
@@ -73,8 +76,10 @@ std::string list_str(const int32_t* v, int32_t n) {
 std::string cache_key(const sync_plan_desc& b, const sync_tune_space& sp, int32_t c_dtype) {
   sync_device_info di{};
   (void)sync_get_device_info(&di);
+  int hip_version = 0;
+  (void)hipRuntimeGetVersion(&hip_version);
   std::ostringstream k;
-  k << di.arch << '/' << di.num_cus << " op" << b.op << " m" << b.m << " n" << b.n << " k" << b.k << " W" << b.world
+  k << di.arch << '/' << di.num_cus << " hip" << hip_version << " op" << b.op << " m" << b.m << " n" << b.n << " k" << b.k << " W" << b.world
     << " r" << b.rank << " d" << b.ring_dir << " pat" << b.pattern << " res" << b.local_resident << " B"
     << b.b_layout << " g" << b.group_m << " h" << b.hier_group << " C" << c_dtype << " S[" << list_str(sp.splits, sp.n_splits) << "] T["
     << list_str(sp.tiles, 2 * sp.n_tiles) << "] O[" << list_str(sp.orders, sp.n_orders) << "] U["
@@ -155,6 +160,10 @@ int sync_autotune(const sync_plan_desc* base, const sync_tune_space* space, cons
   if (!bufs->ws || (reinterpret_cast<uintptr_t>(bufs->ws) & 255u))
     return set_error(SYNC_EINVAL, "workspace must be non-NULL and 256-byte aligned");
   const sync_tune_space& sp = *space;
+  const auto t_start = std::chrono::steady_clock::now();
+  auto wall_ms = [&]() {
+    return std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+  };
   const std::string key = cache_key(*base, sp, bufs->c_dtype);
   if (!sp.force) {
     std::lock_guard<std::mutex> lk(g_cache_mu);
@@ -164,6 +173,8 @@ int sync_autotune(const sync_plan_desc* base, const sync_tune_space* space, cons
       *out = it->second;
       out->candidates_run = 0;
       out->candidates_skipped = 0;
+      out->from_cache = 1;
+      out->call_wall_ms = wall_ms();
       return SYNC_OK;
     }
   }
@@ -257,6 +268,9 @@ int sync_autotune(const sync_plan_desc* base, const sync_tune_space* space, cons
   if (run == 0) return set_error(SYNC_EUNSUPPORTED, "no candidate of the space could run");
   best.candidates_run = run;
   best.candidates_skipped = skipped;
+  best.from_cache = 0;
+  best.search_wall_ms = wall_ms();
+  best.call_wall_ms = best.search_wall_ms;
   {
     std::lock_guard<std::mutex> lk(g_cache_mu);
     load_file_locked();

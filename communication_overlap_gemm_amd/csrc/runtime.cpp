@@ -114,7 +114,10 @@ std::map<int, std::unique_ptr<DeviceState>> g_devices;
 
 int current_device_state(DeviceState** out) {
   int dev = 0;
-  HIP_TRY(hipGetDevice(&dev));
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge == hipErrorNoDevice || ge == hipErrorInsufficientDriver)
+    return fail(SYNC_ENODEV, std::string("no HIP device: ") + hipGetErrorString(ge));
+  if (ge != hipSuccess) return hip_fail(ge, "hipGetDevice");
   std::lock_guard<std::mutex> lk(g_devices_mu);
   auto& slot = g_devices[dev];
   if (!slot) slot = std::make_unique<DeviceState>();

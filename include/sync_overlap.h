@@ -493,7 +493,7 @@ int sync_head_attn(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q_pee
  * or host gates), or, with n_agents = 0, the CU backend at each count of the
  * copy_cus list.  Candidates an agent does not support (e.g. EPILOGUE for
  * AG) are skipped.
- * Results are cached per (device, op, shape, base fields, c_dtype, space) for
+ * Results are cached per (device, HIP runtime version, op, shape, base fields, c_dtype, space) for
  * the life of the process, and in the text file named by the environment
  * variable SYNC_TUNE_CACHE when it is set (read on first use, appended after
  * each tuning); a cached result returns at once with candidates_run = 0
@@ -529,6 +529,9 @@ typedef struct {
   int32_t candidates_skipped;
   int32_t backend;          /* SYNC_COPY_* of the winner */
   int32_t agent;            /* index of the winner in agents, -1 when from the copy_cus list */
+  int32_t from_cache;       /* 1 when served from the cache (in-process or file) */
+  float call_wall_ms;       /* host wall time of this sync_autotune call */
+  float search_wall_ms;     /* host wall time the search that produced the result took (kept in the cache) */
 } sync_tune_result;
 
 /* Workspace bytes that fit every candidate of the space (0 on bad input). */

@@ -70,6 +70,10 @@ def test_autotune_picks_a_valid_exact_config(op):
         r2 = A.sync_autotune(base, space2, a=a_d, b=b_d, c=c, staging=staging, ws=ws, stream=s)
     assert r2["candidates_run"] == 0 and {k: r2[k] for k in ("split", "tile_m", "tile_n", "tile_order", "copy_cus")} \
         == {k: r[k] for k in ("split", "tile_m", "tile_n", "tile_order", "copy_cus")}
+    # tuning cost: the search's wall time is kept with the result; a cache hit costs little
+    assert r["from_cache"] == 0 and r["search_wall_ms"] > 0 and r["call_wall_ms"] == r["search_wall_ms"]
+    assert r2["from_cache"] == 1 and r2["search_wall_ms"] == r["search_wall_ms"]
+    assert 0 <= r2["call_wall_ms"] < r["search_wall_ms"]
 
 
 def test_cache_file_survives_forgetting(tmp_path, monkeypatch):
@@ -93,8 +97,9 @@ def test_cache_file_survives_forgetting(tmp_path, monkeypatch):
         assert cache.read_text().count("\n") == 1
         A.sync_tune_forget()
         r2 = A.sync_autotune(base, space, a=al, a_peer=a_d, b=b_d, c=c, ws=ws, stream=s)
-        assert r2["candidates_run"] == 0 and r2["split"] == r1["split"]
+        assert r2["candidates_run"] == 0 and r2["split"] == r1["split"] and r2["from_cache"] == 1
         assert abs(r2["best_ms"] - r1["best_ms"]) <= 1e-3 * r1["best_ms"] + 1e-6
+        assert abs(r2["search_wall_ms"] - r1["search_wall_ms"]) <= 1e-3 * r1["search_wall_ms"] + 1e-3
     finally:
         A.sync_tune_forget()
 
