@@ -716,7 +716,7 @@ def attention_rows(timer, torch, inputs, stream, steps=5, warmup=2):
     w, nb, hq, hkv, d = (HEAD_SHAPE[x] for x in ("world", "n", "hq", "hkv", "d"))
     s = w * nb
     q_bits, k_bits, v_bits = inputs.attention_operands(s, hq, s, hkv, d)
-    plan = A.sync_plan(A.make_desc(A.SYNC_OP_HEAD_ATTN, s, nb, d, w, tile_m=32 * (8 // min(hq // hkv, 4)), tile_n=1,
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_HEAD_ATTN, s, nb, d, w, tile_m=A.sync_attn_query_block(hq, hkv), tile_n=1,
                                    heads_q=hq, heads_kv=hkv))
     peers = [torch.from_numpy(x.view(np.int16)).to(dev) for x in (q_bits, k_bits, v_bits)]
     local = [torch.zeros_like(x) for x in peers]

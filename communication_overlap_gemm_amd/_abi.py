@@ -33,7 +33,7 @@ SYNC_ATTN_INIT, SYNC_ATTN_FINALIZE = 1, 2
 EXPORTED_SYMBOLS = (
     "sync_plan", "sync_plan_destroy", "sync_plan_get_info", "sync_plan_export", "sync_workspace_size",
     "sync_workspace_init", "sync_workspace_status", "sync_ag_gemm", "sync_ag_gemm_noalloc", "sync_gemm_rs", "sync_gemm_rs_reduce", "sync_gemm_ar",
-    "sync_ring_attn_step", "sync_head_attn", "sync_gemm_split",
+    "sync_ring_attn_step", "sync_head_attn", "sync_attn_query_block", "sync_gemm_split",
     "sync_get_device_info", "sync_last_error", "sync_shutdown", "sync_read_timings", "sync_trace_export",
     "sync_autotune", "sync_tune_workspace_size", "sync_tune_forget",
 )
@@ -148,6 +148,7 @@ def lib():
                                           i32, vp, vp, vp]),
             "sync_head_attn": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                      vp, vp]),
+            "sync_attn_query_block": (i32, [i32, i32]),
             "sync_gemm_split": (i32, [vp, ctypes.POINTER(sync_copy_cfg), vp, vp, vp, vp, i32, vp, vp, vp, vp]),
             "sync_get_device_info": (i32, [ctypes.POINTER(sync_device_info)]),
             "sync_read_timings": (i32, [i32, ctypes.POINTER(sync_timing), ctypes.POINTER(i32)]),
@@ -446,6 +447,11 @@ def sync_head_attn(plan: Plan, cfg: Optional[sync_copy_cfg], q_peer, k_peer, v_p
                                 _arg(v_peer, "v_peer", 2, kv), _arg(q, "q", 2, qn), _arg(k, "k", 2, kv),
                                 _arg(v, "v", 2, kv), _arg(o, "o", 4, qn), _arg(lse, "lse", 4, hq * s),
                                 float(scale), _ws_arg(plan, ws), _stream(compute), _stream(copy)))
+
+
+def sync_attn_query_block(heads_q: int, heads_kv: int) -> int:
+    """Query rows of one attention work item (the tile_m of a HEAD_ATTN plan); 0 if unsupported."""
+    return int(lib().sync_attn_query_block(heads_q, heads_kv))
 
 
 def sync_gemm_split(plan: Plan, cfg: Optional[sync_copy_cfg], a_peer, a, b, c, c_dtype: int, staging, ws, compute,

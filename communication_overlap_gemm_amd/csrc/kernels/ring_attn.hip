@@ -48,9 +48,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;           // head dim
 constexpr int kKT = 64;           // keys per tile
-constexpr int kAttnThreads = 512; // 8 waves
+constexpr int kAttnThreads = 512;  // 8 waves (4 waves in two workgroups per CU measured 13 % slower)
+constexpr int kAttnWgPerCu = 512 / kAttnThreads;
+constexpr int kKLoads = kKT * 16 / kAttnThreads;  // 16-byte K granules per thread per tile
+constexpr int kVUnits = kKT * kD / 16 / kAttnThreads;  // (8 keys, 2 dims) V units per thread per tile
 // A work item is HG query heads sharing one KV head (HG = min(heads_q /
-// heads_kv, 4)) times 32 * (8 / HG) query rows: 8 waves, one per (head, 32 rows).
+// heads_kv, 4)) times 32 * (waves / HG) query rows: one wave per (head, 32 rows).
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes));
@@ -81,14 +84,14 @@ __device__ __forceinline__ void sched_reads_ahead() {
 // holds keys {4h..4h+3, 8+4h..8+4h+3} of the step in the score accumulator.
 __device__ __forceinline__ int perm16(int phys) { return ((phys >> 3) << 2) + ((phys >> 2) & 1) * 8 + (phys & 3); }
 
-__global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(AttnArgs a) {
   __shared__ u32x4_t Ks[2][kKT * kKRow];  // [key][16 slots of 8 d + pad]
   __shared__ u32x4_t Vt[2][kD * kVRow];   // [dv][8 slots of 8 permuted keys + pad]
   __shared__ int32_t s_ok;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int HG = a.heads_per_item, QS = 8 / HG, QB = 32 * QS;
+  const int HG = a.heads_per_item, QS = (kAttnThreads / 64) / HG, QB = 32 * QS;
   const int hh = wave % HG, qs = wave / HG;
   const int half = lane >> 5, col = lane & 31;
   const uint32_t epoch = call_epoch(a.hdr);
@@ -178,8 +181,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
     // tile cursor over the chunks in arrival order
     int p = 0;
     int64_t t0 = a.chunk_begin[a.arrival[0]];
-    u32x4_t rk[2];
-    uint32_t rv[8];
+    u32x4_t rk[kKLoads];
+    uint32_t rv[kVUnits][8];
     auto wait_chunk = [&](int pos) {
       const int32_t c = a.arrival[pos];
       if (!a.wait_chunks || a.resident[c]) return 1;  // in place before the call
@@ -200,36 +203,42 @@ __global__ __launch_bounds__(kAttnThreads, 1) void ring_attn_step(AttnArgs a) {
       const __amdgpu_buffer_rsrc_t rk_ = attn_rsrc(a.k + (t * Hkv + g) * kD, bytes);
       const __amdgpu_buffer_rsrc_t rv_ = attn_rsrc(a.v + (t * Hkv + g) * kD, bytes);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {  // K: 64 keys x 16 slots = 1024 granules
+      for (int i = 0; i < kKLoads; ++i) {  // K: 64 keys x 16 slots = 1024 granules
         const int gi = tid + i * kAttnThreads, key = gi >> 4, sl = gi & 15;
         rk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                     rk_, static_cast<uint32_t>((key * krow + sl * 8) * 2), 0, 0));
       }
       // V: unit = (8 permuted keys of a 16-key step half, 2 dims)
-      const int dp = tid & 63, kg = tid >> 6;  // dims 2dp, 2dp+1; physical key group kg (8 keys)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = (kg >> 1) * 16 + perm16((kg & 1) * 8 + j);
-        rv[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_, static_cast<uint32_t>((key * krow + dp * 2) * 2), 0, 0);
+      for (int u = 0; u < kVUnits; ++u) {
+        const int un = tid + u * kAttnThreads, dp = un & 63, kg = un >> 6;  // dims 2dp, 2dp+1; key group kg
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = (kg >> 1) * 16 + perm16((kg & 1) * 8 + j);
+          rv[u][j] = __builtin_amdgcn_raw_buffer_load_b32(rv_, static_cast<uint32_t>((key * krow + dp * 2) * 2), 0, 0);
+        }
       }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < kKLoads; ++i) {
         const int gi = tid + i * kAttnThreads, key = gi >> 4, sl = gi & 15;
         Ks[buf][key * kKRow + sl] = rk[i];
       }
-      const int dp = tid & 63, kg = tid >> 6;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        u32x4_t w;
+      for (int u = 0; u < kVUnits; ++u) {
+        const int un = tid + u * kAttnThreads, dp = un & 63, kg = un >> 6;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = rv[2 * j], hi = rv[2 * j + 1];
-          w[j] = e ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        for (int e = 0; e < 2; ++e) {
+          u32x4_t w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = rv[u][2 * j], hi = rv[u][2 * j + 1];
+            w[j] = e ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+          }
+          const int dv = dp * 2 + e;
+          Vt[buf][dv * kVRow + kg] = w;
         }
-        const int dv = dp * 2 + e;
-        Vt[buf][dv * kVRow + kg] = w;
       }
     };
     auto advance = [&](int& pos, int64_t& t) {  // next tile; pos == C when done
@@ -387,5 +396,11 @@ hipError_t launch_ring_attn(const AttnArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(ring_attn_step, dim3(grid), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
+
+// Workgroups per CU the launch assumes (every one resident: the co-located
+// copy publishes once all have copied), and the query rows of a work item
+// with hg query heads per item.
+int attn_wg_per_cu() { return kAttnWgPerCu; }
+int attn_query_block(int hg) { return 32 * ((kAttnThreads / 64) / hg); }
 
 }  // namespace syncov

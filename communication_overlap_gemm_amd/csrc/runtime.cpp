@@ -40,6 +40,8 @@ hipError_t launch_sdma_gate(uint32_t* hdr, int64_t* gate, hipStream_t s);
 hipError_t launch_sdma_join(uint32_t* hdr, const uint32_t* flags, const int32_t* arrival, const int32_t* resident,
                             int32_t num_chunks, uint64_t timeout_ticks, hipStream_t s);
 hipError_t launch_ring_attn(const AttnArgs& a, int grid, hipStream_t s);
+int attn_wg_per_cu();
+int attn_query_block(int hg);
 constexpr int64_t kAttnHeadDim = 128;
 
 }  // namespace syncov
@@ -1200,7 +1202,7 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   at.timeout_ticks = cx.timeout_ticks;
   at.nxcd = d.num_xcds;
   at.copy = make_copy_in(pl, cx, src, dst, rb, 2);
-  const Roles r = roles_for(cx, d, 1);
+  const Roles r = roles_for(cx, d, attn_wg_per_cu());
   return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), r, src, dst, rb, 2,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     at.copy_blocks = rr.copy_blocks;
@@ -1224,7 +1226,7 @@ int sync_head_attn(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q_pee
   const int group = dsc.heads_q / dsc.heads_kv;
   if (!(group == 1 || group == 2 || group % 4 == 0))
     return fail(SYNC_EUNSUPPORTED, "heads_q / heads_kv must be 1, 2 or a multiple of 4");
-  const int hg = std::min(group, 4), qb = 32 * (8 / hg);
+  const int hg = std::min(group, 4), qb = attn_query_block(hg);
   if (dsc.tile_m != qb)
     return fail(SYNC_EUNSUPPORTED, "tile_m must be the kernel's query block: " + std::to_string(qb) +
                                        " rows for heads_q / heads_kv = " + std::to_string(group));
@@ -1273,7 +1275,7 @@ int sync_head_attn(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q_pee
   at.timeout_ticks = cx.timeout_ticks;
   at.nxcd = d.num_xcds;
   at.copy = make_copy_in(pl, cx, src, dst, rb, 3);
-  const Roles r = roles_for(cx, d, 1);
+  const Roles r = roles_for(cx, d, attn_wg_per_cu());
   return run_call(pl, cx, d, tm, static_cast<hipStream_t>(compute), r, src, dst, rb, 3,
                   [&](hipStream_t st, const Roles& rr) -> int {
                     at.copy_blocks = rr.copy_blocks;
@@ -1283,6 +1285,13 @@ int sync_head_attn(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q_pee
                     HIP_TRY(launch_ring_attn(at, rr.grid, st));
                     return SYNC_OK;
                   });
+}
+
+int32_t sync_attn_query_block(int32_t heads_q, int32_t heads_kv) {
+  if (heads_q < 1 || heads_kv < 1 || heads_q % heads_kv) return 0;
+  const int32_t group = heads_q / heads_kv;
+  if (!(group == 1 || group == 2 || group % 4 == 0)) return 0;
+  return attn_query_block(std::min(group, 4));
 }
 
 int sync_get_device_info(sync_device_info* out) {

@@ -467,8 +467,8 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
  *   head h reads KV head h / (heads_q / heads_kv)); lse fp32 [heads_q][world*n]
  *   (natural log of the softmax denominator) or NULL.
  * Kernel constraints (else EUNSUPPORTED): k == 128; heads_q / heads_kv is 1,
- *   2 or a multiple of 4; tile_m == 32 * 8 / min(heads_q / heads_kv, 4) (the
- *   kernel's query block: 64, 128 or 256 rows); the plan's tile order is the
+ *   2 or a multiple of 4; tile_m == sync_attn_query_block(heads_q, heads_kv)
+ *   (the query rows of one kernel work item); the plan's tile order is the
  *   order work items are taken in.  cfg as for sync_ring_attn_step (backends
  *   CU, COLOCATED, SDMA or PRESET; COPY_ONLY, COMPUTE_ONLY, TIMED, WITHHOLD).
  *   A work item whose chunks never arrive leaves its outputs untouched and
@@ -476,6 +476,11 @@ int sync_ring_attn_step(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
 int sync_head_attn(sync_plan_t plan, const sync_copy_cfg* cfg, const void* q_peer, const void* k_peer,
                    const void* v_peer, void* q, void* k, void* v, float* o, float* lse, float scale, void* ws,
                    void* compute, void* copy);
+
+/* Query rows of one work item of the attention kernel for this head
+ * grouping (the tile_m a HEAD_ATTN plan must use); 0 if the grouping has no
+ * kernel variant.  Needs no device. */
+int32_t sync_attn_query_block(int32_t heads_q, int32_t heads_kv);
 
 /* ---- autotuner ------------------------------------------------------------ */
 /* Picks the fastest overlapped configuration of a GEMM call (AG or RS) by

@@ -20,5 +20,7 @@ hipError_t launch_sdma_join(uint32_t*, const uint32_t*, const int32_t*, const in
   return hipErrorNoDevice;
 }
 hipError_t launch_ring_attn(const AttnArgs&, int, hipStream_t) { return hipErrorNoDevice; }
+int attn_wg_per_cu() { return 1; }
+int attn_query_block(int hg) { return 32 * (8 / hg); }
 
 }  // namespace syncov

@@ -241,3 +241,16 @@ def test_head_attn_validation():
     assert "TRACE" in A.sync_last_error()
     info = A.sync_plan_get_info(hp)
     assert info.num_chunks == 4 and info.num_tiles == 4
+
+
+def test_attn_query_block():
+    """The query rows of one attention work item: a multiple of 32 that
+    halves as the query heads per item double (up to 4), 0 for groupings the
+    kernel has no variant for.  Plans of op HEAD_ATTN must use it as tile_m."""
+    qb = A.sync_attn_query_block
+    base = qb(4, 1)
+    assert base > 0 and base % 32 == 0
+    assert qb(8, 2) == qb(16, 1) == qb(32, 8) == base
+    assert qb(2, 1) == qb(4, 2) == 2 * base and qb(1, 1) == qb(8, 8) == 4 * base
+    for hq, hkv in ((3, 1), (6, 1), (4, 3), (0, 1), (4, 0), (-4, 1)):
+        assert qb(hq, hkv) == 0

@@ -28,7 +28,7 @@ TOL = 2e-3
 
 def query_block(hq, hkv):
     """The kernel's query rows per work item (the plan's tile_m)."""
-    return 32 * (8 // min(hq // hkv, 4))
+    return A.sync_attn_query_block(hq, hkv)
 
 
 def run_head(world, n, rank, qg, kg, vg, split=1, backend=A.SYNC_COPY_CU, cus=16,
