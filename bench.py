@@ -61,8 +61,9 @@ BACKENDS = {"sdma": dict(backend=SDMA, copy_teams=7), "cu8": dict(backend=CU, co
             "cu64": dict(backend=CU, copy_cus=64), "colocated": dict(backend=COLOC)}
 SWEEP_AGENTS = {
     "sdma_1_engine": dict(backend=SDMA, copy_teams=1), "sdma_7_engines": dict(backend=SDMA, copy_teams=7),
-    "cu32_4slices_no_lead": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4),
     "cu32_4slices_lead2": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4, copy_lead_slice=2),
+    # every slice by the compute workgroups whose first tile reads the chunk: the per-tile co-located form
+    "cu32_2slices_lead_all": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=2, copy_lead_slice=2),
     "cu32_2slices_no_lead": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=2),
     "cu8": dict(backend=CU, copy_cus=8, copy_teams=7, copy_kslices=4),
     "cu16": dict(backend=CU, copy_cus=16, copy_teams=7, copy_kslices=4),

@@ -405,8 +405,8 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs K/64 >= 4 x copy_kslices");
   }
   if (cfg.copy_streaming != 0 && cfg.copy_streaming != 1) return fail(SYNC_EINVAL, "copy_streaming must be 0 or 1");
-  if (cfg.copy_lead_slice < 0 || (cfg.copy_lead_slice > 0 && cfg.copy_lead_slice >= cfg.copy_kslices))
-    return fail(SYNC_EINVAL, "copy_lead_slice must be in [0, copy_kslices)");
+  if (cfg.copy_lead_slice < 0 || (cfg.copy_lead_slice > 0 && (cfg.copy_kslices < 2 || cfg.copy_lead_slice > cfg.copy_kslices)))
+    return fail(SYNC_EINVAL, "copy_lead_slice must be 0, or in [1, copy_kslices] with copy_kslices > 1");
   if (cfg.copy_lead_slice && (op != SYNC_OP_AG_GEMM || cfg.backend != SYNC_COPY_CU || cfg.copy_link_gbps != 0.f))
     return fail(SYNC_EINVAL, "copy_lead_slice is for AG-GEMM with the CU backend, copy_kslices > 1 and no pacing");
   if (cfg.copy_link_gbps != 0.f) {

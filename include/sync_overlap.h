@@ -256,13 +256,15 @@ typedef struct {
                                the moment the item may start, has carried its bytes (e.g. 153
                                for one xGMI link of an MI355X node: copy_teams = 1 paces a ring,
                                7 teams seven links at once) */
-  int32_t copy_lead_slice;  /* AG-GEMM, CU backend, copy_kslices > 1: L in [1, copy_kslices) = the
+  int32_t copy_lead_slice;  /* AG-GEMM, CU backend, copy_kslices > 1: L in [1, copy_kslices] = the
                                first L K-slices of each copied chunk are copied by the compute
                                workgroups whose first tile reads that chunk (each a share of its
                                rows, published together), before they start it; the copy
                                workgroups move the other slices, and every slice of chunks no
-                               first tile reads.  0 = the copy workgroups move every slice, as
-                               with COPY_ONLY (nothing computes).  Not with pacing. */
+                               first tile reads.  L = copy_kslices: those workgroups copy the
+                               whole chunk, the per-tile co-located form.  0 = the copy
+                               workgroups move every slice, as with COPY_ONLY (nothing
+                               computes).  Not with pacing. */
 } sync_copy_cfg;
 
 /* ---- workspace ---------------------------------------------------------- */

@@ -194,12 +194,13 @@ def test_binding_checks_tensor_sizes():
 
 
 def test_lead_slice_validation():
-    """copy_lead_slice: in [0, copy_kslices), and only for AG-GEMM with the CU
-    backend, K-slices and no pacing."""
+    """copy_lead_slice: 0 or in [1, copy_kslices] with copy_kslices > 1, and
+    only for AG-GEMM with the CU backend and no pacing."""
     def rc_of(plan, cfg):
         return A.lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg), None, None, None, None, 0, 256, None, None)
     p = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
-    for bad in (A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=2),
+    for bad in (A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2, copy_lead_slice=3),
+                A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=1, copy_lead_slice=1),
                 A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=4, copy_lead_slice=-1),
                 A.make_cfg(A.SYNC_COPY_CU, 8, copy_lead_slice=1),
                 A.make_cfg(A.SYNC_COPY_COLOCATED, copy_kslices=2, copy_lead_slice=1),

@@ -428,7 +428,9 @@ def test_full_size_70b_like(split, teams):
     (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 0), (A.SYNC_COPY_COLOCATED, 0, 3, 4, (256, 256), 0),
     (A.SYNC_COPY_COLOCATED, 0, 1, 2, (256, 256), 0), (A.SYNC_COPY_CU, 8, 1, 2, (256, 256), 1),
     (A.SYNC_COPY_CU, 16, 3, 4, (256, 128), 1), (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 1),
-    (A.SYNC_COPY_CU, 16, 3, 4, (256, 256), 2), (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 2)])
+    (A.SYNC_COPY_CU, 16, 3, 4, (256, 256), 2), (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 2),
+    (A.SYNC_COPY_CU, 8, 1, 2, (256, 256), 2), (A.SYNC_COPY_CU, 16, 3, 4, (256, 128), 4),
+    (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 3)])
 def test_kslices_parity(backend, cus, teams, kslices, tile, lead):
     """K = 1152 (18 K-steps: uneven slices); the output matches the oracle and
     is bitwise the compute-only output (the copy protocol changes only when
@@ -447,7 +449,7 @@ def test_kslices_parity(backend, cus, teams, kslices, tile, lead):
 @pytest.mark.parametrize("cus,teams,kslices,tile,rank,lead", [
     (8, 1, 2, (256, 256), 0, 0), (32, 7, 4, (256, 256), 1, 0), (16, 3, 4, (256, 128), 2, 0),
     (8, 5, 3, (128, 128), 3, 0), (32, 7, 4, (256, 256), 1, 1), (8, 5, 3, (128, 128), 3, 1),
-    (32, 7, 4, (256, 256), 2, 2)])
+    (32, 7, 4, (256, 256), 2, 2), (32, 7, 2, (256, 256), 1, 2), (8, 5, 3, (128, 128), 3, 3)])
 def test_kslices_repeated_calls(cus, teams, kslices, tile, rank, lead):
     """Three K-sliced calls on one workspace, the copied rows and C poisoned
     before each: the slice and chunk counters each call leaves cleared let the
@@ -465,7 +467,7 @@ def test_kslices_repeated_calls(cus, teams, kslices, tile, rank, lead):
     assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
 
 
-@pytest.mark.parametrize("lead", [0, 1])
+@pytest.mark.parametrize("lead", [0, 1, 2])
 def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles(lead):
     """A withheld chunk under a K-sliced copy (with or without the lead slice
     copied by the compute workgroups): none of its slices land, the tiles that
@@ -510,7 +512,8 @@ def test_kslices_withholding_one_chunk_leaves_exactly_its_tiles(lead):
 @pytest.mark.parametrize("backend,cus,teams,kslices,lead", [(A.SYNC_COPY_CU, 32, 7, 4, 0), (A.SYNC_COPY_CU, 32, 7, 8, 0),
                                                             (A.SYNC_COPY_COLOCATED, 0, 7, 4, 0),
                                                             (A.SYNC_COPY_CU, 32, 7, 4, 1), (A.SYNC_COPY_CU, 32, 7, 8, 1),
-                                                            (A.SYNC_COPY_CU, 32, 7, 4, 2), (A.SYNC_COPY_CU, 32, 7, 8, 3)])
+                                                            (A.SYNC_COPY_CU, 32, 7, 4, 2), (A.SYNC_COPY_CU, 32, 7, 8, 3),
+                                                            (A.SYNC_COPY_CU, 32, 7, 2, 2), (A.SYNC_COPY_CU, 32, 7, 4, 4)])
 def test_full_size_kslices(cfg2_data, backend, cus, teams, kslices, lead):
     """The Llama-3-8B up-projection share with a K-sliced copy: every output
     element against the oracle."""
