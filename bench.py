@@ -495,12 +495,18 @@ def split_baseline_ag(timer, plan, a_peer, a_local, b, c_out, c_dtype, ws, strea
     return out
 
 
+KN_TILE = (128, 128)  # B [k][n]: the fastest tile of gemm_persistent (two workgroups per CU, no spills)
+KN_AGENTS = {"overlapped_cu32_7teams": dict(backend=CU, copy_cus=32, copy_teams=7),
+             "overlapped_colocated": dict(backend=COLOC), "compute_only": dict(backend=PRESET)}
+
+
 def layout_kn_row(timer, torch, inputs, stream, steps=10, warmup=3):
     """The headline workload with B stored [k][n] (the kernel for that layout), cold cache."""
     import numpy as np
 
     a_bits, b_bits = inputs.gemm_operands(M, N, K, DIVISOR, b_layout="kn")
-    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, tile_m=256, tile_n=256, b_layout=A.SYNC_B_KN))
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, tile_m=KN_TILE[0], tile_n=KN_TILE[1],
+                                   b_layout=A.SYNC_B_KN))
     ap = torch.from_numpy(a_bits.view(np.int16)).to("cuda:0")
     b = torch.from_numpy(b_bits.view(np.int16)).to("cuda:0")
     al = torch.zeros_like(ap)
@@ -508,13 +514,13 @@ def layout_kn_row(timer, torch, inputs, stream, steps=10, warmup=3):
     c = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
     ws = workspace(plan, torch)
     out = {}
-    for name, ag in (("overlapped_cu32_7teams", dict(backend=CU, copy_cus=32, copy_teams=7)),
-                     ("overlapped_colocated", dict(backend=COLOC)), ("compute_only", dict(backend=PRESET))):
+    for name, ag in KN_AGENTS.items():
         st = timer.series(lambda: A.sync_ag_gemm(plan, cfg(**ag), ap, al, b, c, A.SYNC_DTYPE_F32, ws, stream, None),
                           steps, warmup, True)
         check(ws, stream)
         out[name] = {"median_us": us(st), "tflops": round(2.0 * M * N * K / st["median_s"] / 1e12, 1)}
-    out["workload"] = "the headline share with B stored [k][n] (gemm_persistent<256,256>), fp32 C, cold cache"
+    out["workload"] = (f"the headline share with B stored [k][n] (gemm_persistent<{KN_TILE[0]},{KN_TILE[1]}>), "
+                       "fp32 C, cold cache")
     return out
 
 

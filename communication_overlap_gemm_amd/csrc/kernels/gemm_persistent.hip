@@ -937,10 +937,9 @@ hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dt
   }
 #define SYNC_GEMM_TILES(BL_, CT_) \
   SYNC_GEMM_CASE(256, 256, BL_, CT_) SYNC_GEMM_CASE(256, 128, BL_, CT_) SYNC_GEMM_CASE(128, 128, BL_, CT_)
+  // B [n][k] always runs gemm_dma (above); gemm_persistent serves B [k][n]
   SYNC_GEMM_TILES(0, 0)
   SYNC_GEMM_TILES(0, 1)
-  SYNC_GEMM_TILES(1, 0)
-  SYNC_GEMM_TILES(1, 1)
 #undef SYNC_GEMM_TILES
 #undef SYNC_GEMM_CASE
   return hipErrorInvalidValue;

@@ -81,12 +81,12 @@ def _run_ag_paced(a, b_nk, split, ag):
     return c.cpu().numpy(), a_local.cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("ag", [dict(backend=bench.CU, copy_cus=32, copy_teams=7), dict(backend=bench.COLOC),
-                                dict(backend=bench.PRESET)], ids=["cu32_7teams", "colocated", "compute_only"])
-def test_layout_kn_row(cfg2_data, ag):
-    """The headline share with B stored [k][n] (the bench's [k][n] row)."""
+@pytest.mark.parametrize("name", sorted(bench.KN_AGENTS))
+def test_layout_kn_row(cfg2_data, name):
+    """The headline share with B stored [k][n] (the bench's [k][n] row, its
+    tile and agents): every output element against the oracle."""
     a, b_kn, ref, absab = cfg2_data
-    out, _ = run_ag(M2, N2, K2, W2, a, b_kn, layout="kn", tile=(256, 256), **_ag_kwargs(ag))
+    out, _ = run_ag(M2, N2, K2, W2, a, b_kn, layout="kn", tile=bench.KN_TILE, **_ag_kwargs(bench.KN_AGENTS[name]))
     check_full_f32(out, ref, absab, K2, W2)
 
 
