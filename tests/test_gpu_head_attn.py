@@ -185,3 +185,64 @@ def test_full_size_sampled(backend, cus, teams):
     assert np.isfinite(on).all() and np.isfinite(ln_).all()
     assert np.max(np.abs(on[qi, hi] - ref_o)) <= TOL
     assert np.max(np.abs(ln_[hi, qi] - ref_lse)) <= TOL
+
+
+def test_captured_call_replays():
+    """A CU-backend head-parallel call is one kernel launch that takes its
+    epoch from the workspace, so a captured call can be replayed: each replay
+    (with eager work and synchronisation between replays, and different peer
+    data) equals the eager result for that data, bit for bit."""
+    W, n, rank, hq, hkv = 4, 128, 1, 8, 2
+    s_tok = W * n
+    datasets = [inputs.attention_operands(s_tok, hq, s_tok, hkv, D, seed_q=inputs.SEED_Q + 11 * x,
+                                          seed_k=inputs.SEED_K + 11 * x, seed_v=inputs.SEED_V + 11 * x)
+                for x in range(3)]
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_HEAD_ATTN, s_tok, n, D, W, rank=rank, split=2,
+                                   tile_m=query_block(hq, hkv), tile_n=1, heads_q=hq, heads_kv=hkv))
+    tabs = A.sync_plan_export(plan)
+    cfg = A.make_cfg(A.SYNC_COPY_CU, copy_cus=16, copy_teams=3)
+    peers = [dev_bits(x) for x in datasets[0]]
+    local = [torch.zeros_like(p) for p in peers]
+    o = torch.empty((s_tok, hq, D), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((hq, s_tok), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    st = torch.cuda.current_stream()
+    scale = 1 / math.sqrt(D)
+
+    def load(x):
+        for p, l, src in zip(peers, local, datasets[x]):
+            p.copy_(dev_bits(src))
+            l.fill_(0x7FC0)  # bf16 NaN: every non-resident row must be staged again
+            for c in range(tabs["num_chunks"]):
+                if tabs["resident"][c]:
+                    r0, r1 = tabs["chunk_begin"][c], tabs["chunk_begin"][c + 1]
+                    l[r0:r1] = p[r0:r1]
+
+    eager = []
+    for x in range(3):
+        load(x)
+        A.sync_head_attn(plan, cfg, *peers, *local, o, lse, scale, ws, st, None)
+        assert A.sync_workspace_status(ws, st)[0] == A.SYNC_OK
+        eager.append((o.clone(), lse.clone()))
+        ref_o, ref_lse = oracle.attention_f64(*datasets[x], scale)
+        check(o, lse, ref_o, ref_lse)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(st)
+    with torch.cuda.stream(side):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            A.sync_head_attn(plan, cfg, *peers, *local, o, lse, scale, ws, side, None)
+    st.wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        x = rep % 3
+        print(f"[head] graph replay {rep} dataset {x}", flush=True)
+        load(x)
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert A.sync_workspace_status(ws, st)[0] == A.SYNC_OK
+        assert torch.equal(o, eager[x][0]) and torch.equal(lse, eager[x][1]), f"replay {rep} differs"
