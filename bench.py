@@ -348,10 +348,9 @@ def main(argv=None):
                 "copy_GBps": round(2 * copied / t_p / 1e9, 1),
                 "series": {x: brief(r[x]) for x in r}}
 
-    kname = ("gemm_dma" if args.layout == "nk" else "gemm_persistent") + \
-        f"<{tm},{tn},{args.c_dtype},AG>" + (f" with {agent.get('copy_cus')} copy workgroups"
-                                             if agent["backend"] == CU else
-                                             " with co-located copy" if agent["backend"] == COLOC else "")
+    kname = f"gemm_dma<{tm},{tn},{args.c_dtype},AG,B {args.layout}>" + (
+        f" with {agent.get('copy_cus')} copy workgroups" if agent["backend"] == CU else
+        " with co-located copy" if agent["backend"] == COLOC else "")
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -495,9 +494,9 @@ def split_baseline_ag(timer, plan, a_peer, a_local, b, c_out, c_dtype, ws, strea
     return out
 
 
-KN_TILE = (128, 128)  # B [k][n]: the fastest tile of gemm_persistent (two workgroups per CU, no spills)
-KN_AGENTS = {"overlapped_cu32_7teams": dict(backend=CU, copy_cus=32, copy_teams=7),
-             "overlapped_colocated": dict(backend=COLOC), "compute_only": dict(backend=PRESET)}
+KN_TILE = HEADLINE["tile"]  # B [k][n] runs the headline's kernel, with transposing B reads
+KN_AGENTS = {"overlapped_headline_agent": HEADLINE_AGENT, "overlapped_colocated": dict(backend=COLOC),
+             "compute_only": dict(backend=PRESET)}
 
 
 def layout_kn_row(timer, torch, inputs, stream, steps=10, warmup=3):
@@ -519,7 +518,7 @@ def layout_kn_row(timer, torch, inputs, stream, steps=10, warmup=3):
                           steps, warmup, True)
         check(ws, stream)
         out[name] = {"median_us": us(st), "tflops": round(2.0 * M * N * K / st["median_s"] / 1e12, 1)}
-    out["workload"] = (f"the headline share with B stored [k][n] (gemm_persistent<{KN_TILE[0]},{KN_TILE[1]}>), "
+    out["workload"] = (f"the headline share with B stored [k][n] (gemm_dma<{KN_TILE[0]},{KN_TILE[1]}>), "
                        "fp32 C, cold cache")
     return out
 

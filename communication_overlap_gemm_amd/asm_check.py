@@ -1,7 +1,8 @@
 """Static check of the direct-to-LDS GEMM's device assembly.
 
-The GEMM reads its MFMA fragments from LDS with inline-asm ds_read_b128 and
-waits for them itself (lgkmcnt), so the compiler believes each destination
+The GEMM reads its MFMA fragments from LDS with inline-asm ds_read_b128 (and,
+for B stored [k][n], the transposing ds_read_b64_tr_b16) and waits for them
+itself (lgkmcnt), so the compiler believes each destination
 register holds its value as soon as the asm statement issues.  Any
 compiler-generated instruction that reads or writes such a register before a
 wait that covers the read would see or clobber a value the LDS has not yet
@@ -112,6 +113,7 @@ def _ends_block(instr: str) -> bool:
 
 
 _LGKM = re.compile(r"lgkmcnt\((\d+)\)")
+_ASM_READS = ("ds_read_b128", "ds_read_b64_tr_b16")  # the kernel's inline-asm fragment reads
 _CAP = 16  # LDS operations issued after a read, counted up to this
 
 
@@ -128,7 +130,7 @@ def _transfer(block, pending: frozenset, report=None, name=""):
                 pend = {r: c for r, c in pend.items() if c < n}
             continue
         if t.startswith("ds_"):
-            if is_asm and t.startswith("ds_read_b128"):
+            if is_asm and t.startswith(_ASM_READS):
                 dst, addr = t.split(None, 1)[1].split(",", 1)
                 if report is not None and _regs(addr) & set(pend):
                     report.append(f"{name}:{i}: address register still pending: {t}")

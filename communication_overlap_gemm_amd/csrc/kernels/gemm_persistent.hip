@@ -10,19 +10,23 @@
 // tiles are ordered so output is produced for communication at a steady pace.
 //
 // gfx950 design (not the pages' Hopper/Triton design):
-//  * 256 threads = 4 wave64s in a 2x2 grid; each wave owns a (TM/2)x(TN/2)
-//    block of C built from v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
-//  * K advances 64 at a time through a double-buffered LDS ring; one barrier
-//    per step; the next step's global loads are in flight during the MFMAs.
-//  * Operands are read with raw buffer loads from a per-tile base (32-bit
-//    offsets; reads past the end return zero, so ragged M/N need no branches).
-//  * A and B fragments are stored k-contiguous in LDS (B is transposed on the
-//    way in when it is [k][n]) with a 16-byte XOR swizzle, so every fragment
-//    is one ds_read_b128 and reads are free of bank conflicts.
-//  * The epilogue stages 32-row strips of the accumulators through LDS and
+//  * A grid of wave64s per workgroup (2x2, or 2x4 for 256x256 tiles: two
+//    waves per SIMD); each wave owns a block of C built from
+//    v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
+//  * K advances 64 at a time through a ring of LDS stages filled by
+//    direct-to-LDS buffer loads (no staging registers), one barrier per stage.
+//  * Operands are read from a per-tile buffer base (32-bit offsets; reads
+//    past the end return zero, so ragged M/N need no branches).
+//  * A (and B stored [n][k]) sit k-contiguous in LDS, one ds_read_b128 per
+//    fragment; B stored [k][n] sits as it is in memory and is turned into
+//    k-contiguous fragments by gfx950's transposing LDS reads.  16-byte XOR
+//    swizzles keep both kinds of read free of bank conflicts.
+//  * The epilogue stages row strips of the accumulators through LDS and
 //    writes C with 16-byte buffer stores, rows past M dropped by the hardware.
-//  * One workgroup per CU walks the plan's tile order with a static stride;
-//    slots are remapped so that each XCD takes consecutive tiles of the order.
+//  * One workgroup per CU (two for 128x128) walks the plan's tile order with
+//    a static stride; slots are remapped so that each XCD takes consecutive
+//    tiles of the order.
+#include <type_traits>
 #include <utility>
 
 #include "copy_role.hpp"
@@ -31,14 +35,9 @@
 
 namespace syncov {
 
-
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kTK = 64;          // K per LDS stage
-constexpr int kThreads = 256;    // 4 waves
-constexpr int kSlots = kTK / 8;  // 16-byte slots per LDS row
-constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any num_records used here
 
 // Raw buffer resource over [base, base + bytes); word 3 selects 32-bit data
 // format as gfx9 raw buffer accesses expect.
@@ -49,13 +48,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4_t buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-__device__ __forceinline__ u32x2_t buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
 
-// 16-byte slot swizzle: rows r..r+15 reading one logical slot land in
-// distinct banks, and so do the 8 slots of one row.
-__device__ __forceinline__ int swz(int row, int slot) { return slot ^ ((row ^ (row >> 3)) & 7); }
 
 // Epilogue.  Accumulator element e of a 32x32 block sits at row
 // 8*(e/4) + 4*(lane/32) + e%4, column lane%32.  Each wave writes one 32-row
@@ -161,13 +154,6 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
   }
 }
 
-template <int TM, int TN, int CT, bool PUSH = false>
-__device__ __forceinline__ void store_tile_c(const GemmArgs& a, const f32x16_t (&acc)[TM / 64][TN / 64], char* lds,
-                                             int64_t m0, int64_t n0, int rows_valid, int cols_valid, int wave,
-                                             int lane, int64_t push_row0 = -1) {
-  store_tile_w<TM, TN, CT, 2, 2, 32, PUSH>(a, acc, lds, m0, n0, rows_valid, cols_valid, wave, lane, push_row0);
-}
-
 // GEMM-RS completion of tile t: every wave's C stores have reached the L2;
 // then one agent-scope release (a write-back of this XCD's L2, covering all
 // four waves) before the tile is counted toward each chunk it wrote; the last
@@ -264,194 +250,8 @@ __device__ __forceinline__ bool wait_tile_chunks(const GemmArgs& a, int32_t t, u
 // launch whose workgroups must all be resident at once.
 template <int TM, int TN> constexpr int kWgPerCu = (TM == 128 && TN == 128) ? 2 : 1;
 
-template <int TM, int TN, int BL, int CT, bool RS>
-__global__ __launch_bounds__(kThreads, (kWgPerCu<TM, TN>)) void gemm_persistent(GemmArgs a) {
-  constexpr int WM = TM / 2, WN = TN / 2;
-  constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int A_LD = TM / 32;                             // 16-byte A loads per thread per stage
-  constexpr int B_LD_NK = TN / 32;                          // NK: 16-byte B loads per thread
-  constexpr int B_UNITS = (kTK / 8) * (TN / 4) / kThreads;  // KN: 8x4 blocks per thread
-  constexpr int ES = CT == 0 ? 4 : 2;                       // C element size
-  constexpr int SP = WN + 32 / ES;                          // staged strip pitch (elements), +32 B
-  static_assert(TM % 64 == 0 && TN % 128 == 0, "tile");
-  static_assert(B_UNITS >= 1, "tile too small for the KN loader");
-  static_assert(4 * 32 * SP * ES <= 2 * (TM + TN) * kSlots * 16, "epilogue staging must fit the LDS ring");
-
-  __shared__ u32x4_t smem[2 * (TM + TN) * kSlots];
-  __shared__ int32_t s_skip;
-  u32x4_t* const As0 = smem;
-  u32x4_t* const Bs0 = smem + 2 * TM * kSlots;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t epoch = call_epoch(a.hdr);
-  const int64_t M = a.M, N = a.N, K = a.K;
-  const int nk = static_cast<int>(K / kTK);
-
-  u32x4_t ra[A_LD];
-  u32x4_t rbn[BL == 1 ? B_LD_NK : 1];
-  u32x2_t rbk[BL == 0 ? B_UNITS : 1][8];
-
-  if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
-    copy_role<kThreads>(a.copy, blockIdx.x, a.copy_blocks, epoch);
-    end_call(a.hdr, epoch, a.cnt);
-    return;
-  }
-  const int32_t gb = blockIdx.x - a.copy_blocks, gn = gridDim.x - a.copy_blocks;
-  if (!RS && a.colocated) {  // co-located: pull this workgroup's share first
-    if (a.copy.teams > 1)
-      copy_role<kThreads>(a.copy, gb, gn, epoch);
-    else
-      copy_role<kThreads, true>(a.copy, gb, gn, epoch);
-  }
-  const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
-  for (int32_t p = slot0; p < a.num_tiles; p += gn) {
-    const int32_t t = a.order[p];
-    const int32_t ti = t / a.tiles_n, tj = t - ti * a.tiles_n;
-    const int64_t m0 = static_cast<int64_t>(ti) * TM, n0 = static_cast<int64_t>(tj) * TN;
-    const int rows_valid = static_cast<int>((M - m0) < TM ? (M - m0) : TM);
-    const int cols_valid = static_cast<int>((N - n0) < TN ? (N - n0) : TN);
-
-    if (a.trace_tiles && tid == 0) {
-      a.trace_tiles[4 * t] = wall_clock64();
-      a.trace_tiles[4 * t + 3] = (static_cast<uint64_t>(xcc_id()) << 32) | static_cast<uint32_t>(p);
-    }
-    if constexpr (!RS) {
-      if (!wait_tile_chunks(a, t, epoch, tid, &s_skip)) continue;  // a chunk never arrived: tile left untouched
-    }
-    if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 1] = wall_clock64();
-
-    const uint16_t* const a_tile = a.A + m0 * K;
-    auto load_a = [&](int64_t k0) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a_tile + k0, static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2);
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const int row = i * 32 + (tid >> 3), sl = tid & 7;
-        ra[i] = buf_load_b128(rs, static_cast<uint32_t>((row * K + sl * 8) * 2));
-      }
-    };
-    auto store_a = [&](int buf) {
-      u32x4_t* As = As0 + buf * TM * kSlots;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const int row = i * 32 + (tid >> 3), sl = tid & 7;
-        As[row * kSlots + swz(row, sl)] = ra[i];
-      }
-    };
-    auto load_b = [&](int64_t k0) {
-      if constexpr (BL == 1) {
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(a.B + n0 * K + k0, static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2);
-#pragma unroll
-        for (int i = 0; i < B_LD_NK; ++i) {
-          const int row = i * 32 + (tid >> 3), sl = tid & 7;
-          rbn[i] = buf_load_b128(rs, static_cast<uint32_t>((row * K + sl * 8) * 2));
-        }
-      } else {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.B + k0 * N + n0, (K - k0) * N * 2 - n0 * 2);
-#pragma unroll
-        for (int u = 0; u < B_UNITS; ++u) {
-          const int unit = tid + kThreads * u;
-          const int ng = unit % (TN / 4), kg = unit / (TN / 4);
-          const bool in = ng * 4 < cols_valid;
-          // the 8 k-rows differ by a wave-uniform stride: it goes in the scalar
-          // offset, the lane's column in the (range-checked) vector offset
-          const uint32_t voff = in ? static_cast<uint32_t>((kg * 8 * N + ng * 4) * 2) : kOutOfRange;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk)
-            rbk[u][kk] = buf_load_b64(rs, voff, static_cast<uint32_t>(kk * N * 2));
-        }
-      }
-    };
-    auto store_b = [&](int buf) {
-      u32x4_t* Bs = Bs0 + buf * TN * kSlots;
-      if constexpr (BL == 1) {
-#pragma unroll
-        for (int i = 0; i < B_LD_NK; ++i) {
-          const int row = i * 32 + (tid >> 3), sl = tid & 7;
-          Bs[row * kSlots + swz(row, sl)] = rbn[i];
-        }
-      } else {
-        // transpose 8 k-rows x 4 n-columns into 4 k-contiguous vectors
-#pragma unroll
-        for (int u = 0; u < B_UNITS; ++u) {
-          const int unit = tid + kThreads * u;
-          const int ng = unit % (TN / 4), kg = unit / (TN / 4);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            u32x4_t w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t lo = rbk[u][2 * j][v >> 1], hi = rbk[u][2 * j + 1][v >> 1];
-              w[j] = (v & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-            const int nl = ng * 4 + v;
-            Bs[nl * kSlots + swz(nl, kg)] = w;
-          }
-        }
-      }
-    };
-
-    f32x16_t acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) acc[i][j] = f32x16_t{};
-
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    store_b(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        load_a(static_cast<int64_t>(kt + 1) * kTK);
-        load_b(static_cast<int64_t>(kt + 1) * kTK);
-      }
-      const u32x4_t* As = As0 + cur * TM * kSlots;
-      const u32x4_t* Bs = Bs0 + cur * TN * kSlots;
-#pragma unroll
-      for (int kk = 0; kk < kTK / 16; ++kk) {
-        const int sl = kk * 2 + (lane >> 5);
-        bf16x8_t af[MI], bfv[NI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const int r = wm * WM + i * 32 + (lane & 31);
-          af[i] = __builtin_bit_cast(bf16x8_t, As[r * kSlots + swz(r, sl)]);
-        }
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const int r = wn * WN + j * 32 + (lane & 31);
-          bfv[j] = __builtin_bit_cast(bf16x8_t, Bs[r * kSlots + swz(r, sl)]);
-        }
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-        store_a(cur ^ 1);
-        store_b(cur ^ 1);
-      }
-      __syncthreads();
-    }
-
-    store_tile_c<TM, TN, CT>(a, acc, reinterpret_cast<char*>(smem), m0, n0, rows_valid, cols_valid, wave, lane);
-    if constexpr (RS) publish_rs_tile(a, t, epoch, tid);
-    if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 2] = wall_clock64();
-  }
-  // co-located GEMM-RS: every workgroup joins the copy-out once its tiles are
-  // stored, chunk by chunk in send order (the first chunks are done first)
-  if (RS && a.colocated) copy_role<kThreads>(a.copy, gb, gn, epoch);
-  end_call(a.hdr, epoch, a.cnt);
-}
-
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant for B stored [n][k] (both operands k-contiguous).
+// The GEMM kernel (gemm_dma), for B stored [n][k] or [k][n].
 //  * K advances TK at a time through an NS-stage LDS ring.  Loads go straight
 //    from HBM to LDS (buffer_load ... lds, 16 bytes per lane): no staging
 //    registers, no ds_write pass.  A wave's load fills 1 KB of LDS, lane l at
@@ -505,6 +305,22 @@ __device__ __forceinline__ bf16x8_t lds_read_b128_at(uint32_t base) {
   return r;
 }
 
+// gfx950's transposing LDS read of 16-bit elements, with a constant byte
+// offset.  Each lane names 8 bytes (four elements); within every group of 16
+// lanes, lane i receives element i % 4 of the lanes i / 4, i / 4 + 4,
+// i / 4 + 8 and i / 4 + 12 of its group, in that order.  When source lane r
+// points at row (r / 4) and columns 4 (r % 4) .. 4 (r % 4) + 3 of a row-major
+// 4 x 16 block, destination lane i therefore holds column i, rows 0..3.
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_tr16_at(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2_t r{};
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "n"(OFF));
+#endif
+  return r;
+}
+
 // Calls f(std::integral_constant<int, X>{}) for X = 0 .. N-1 in order, so X
 // can name a template argument or an instruction's immediate.
 template <typename F, int... X>
@@ -541,6 +357,20 @@ __device__ __forceinline__ int rswz(int row, int slot) {
     return slot ^ ((row & 7) ^ ((row >> 3) & 1));
 }
 
+// B stored [k][n] (BKN): a stage holds TK rows of TN columns, and 16-byte slot
+// s of row k sits at slot s ^ 4 kn_swz(k).  The swizzle term uses row bits 0,
+// 1 and (with 32 slots per row) 3: the rows that one transposing read touches
+// (four consecutive rows per 32 lanes, two such sets 8 rows apart) then fall
+// on distinct 64-byte bank groups, and within a k16 step the term depends only
+// on the lane, so every read of a fragment is one base plus an immediate.
+template <int TN>
+__device__ __forceinline__ int kn_swz(int k) {
+  if constexpr (TN >= 256)
+    return (k & 3) | (((k >> 3) & 1) << 2);
+  else
+    return k & 3;
+}
+
 // FEED: how a stage reaches the LDS.  0: direct-to-LDS loads, all issued
 // right after the barrier that frees the slot; F > 0: direct-to-LDS loads
 // spread over the first F k16 steps after that barrier, between the MFMAs;
@@ -548,7 +378,7 @@ __device__ __forceinline__ int rswz(int row, int slot) {
 // free slot with ds_write between the MFMAs).
 constexpr int kFeedReg = -1;
 
-template <int TM, int TN, int CT, bool RS, int TK, int NS, int WGM, int WGN, int FEED>
+template <int TM, int TN, int CT, bool RS, int TK, int NS, int WGM, int WGN, int FEED, bool BKN>
 __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(GemmArgs a) {
   constexpr int NW = WGM * WGN, THREADS = 64 * NW;  // waves, as a WGM x WGN grid over the tile
   constexpr int WM = TM / WGM, WN = TN / WGN;
@@ -558,19 +388,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
   constexpr int RPL = 1024 / ROWB;                  // rows per 1 KB wave load
   constexpr int KS = TK / 16;                       // k16 steps per stage
   constexpr int A_BYTES = TM * ROWB, B_BYTES = TN * ROWB;
+  constexpr int ROWB_B = BKN ? TN * 2 : ROWB;       // bytes per LDS row of B
+  constexpr int RPLB = 1024 / ROWB_B;               // rows of B per 1 KB wave load
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int A_LD = A_BYTES / 1024 / NW;         // 1 KB wave loads per wave per stage
   constexpr int B_LD = B_BYTES / 1024 / NW;
   constexpr int LPW = A_LD + B_LD;                  // loads per wave per stage
-  constexpr int NFRAG = MI + NI;                    // 16-byte reads per k16 step: A frags, then B frags
+  constexpr int NFRAG = MI + NI;                    // fragments per k16 step: A frags, then B frags
+  constexpr int NB = BKN ? 2 * NI : NI;             // B reads per k16 step (two transposing halves per fragment)
+  constexpr int NRD = MI + NB;                      // LDS reads per k16 step
   static_assert(WM % 32 == 0 && WN % 32 == 0 && A_LD >= 1 && B_LD >= 1 && A_LD * NW * 1024 == A_BYTES &&
                 B_LD * NW * 1024 == B_BYTES, "tile");
   static_assert((SLOTS == 4 || SLOTS == 8) && KS % 2 == 0, "stage depth");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring");
-  static_assert(NFRAG <= MI * NI, "one read per MFMA slot");
+  static_assert(NFRAG <= MI * NI && (!BKN || (WN == 64 && (TN == 128 || TN == 256))), "reads per MFMA slot");
   constexpr bool REG = FEED == kFeedReg, SPREAD = FEED > 0;
   constexpr int PPW = LPW / KS;  // REG: staged loads written (and refetched) per k16 step
-  static_assert(!REG || (NS == 2 && LPW % KS == 0 && NFRAG + PPW <= MI * NI && SLOTS == 8 && A_LD == B_LD &&
+  static_assert(!REG || (!BKN && NS == 2 && LPW % KS == 0 && NFRAG + PPW <= MI * NI && SLOTS == 8 && A_LD == B_LD &&
                          A_LD % 2 == 0),
                 "register staging");
   constexpr int LPG = SPREAD ? LPW / FEED : 1;          // SPREAD: loads per k16 step
@@ -601,8 +435,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int row = (wave * B_LD + i) * RPL + lane / SLOTS;
-    b_off[i] = static_cast<uint32_t>((row * K + rswz<SLOTS>(row, lane % SLOTS) * 8) * 2);
+    if constexpr (BKN) {  // row k of the stage, physical slot lane % (TN / 8)
+      const int k = (wave * B_LD + i) * RPLB + lane / (TN / 8);
+      b_off[i] = static_cast<uint32_t>((k * N + ((lane % (TN / 8)) ^ (4 * kn_swz<TN>(k))) * 8) * 2);
+    } else {
+      const int row = (wave * B_LD + i) * RPL + lane / SLOTS;
+      b_off[i] = static_cast<uint32_t>((row * K + rswz<SLOTS>(row, lane % SLOTS) * 8) * 2);
+    }
   }
   // REG: A and B rows are indexed alike, and with 8 slots per row the swizzle
   // depends only on bit 3 of the row, i.e. on the parity of the load index:
@@ -625,6 +464,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
   for (int kk = 0; kk < KS; ++kk)
     frag_off[kk] = (wm * WM + frow) * ROWB + rswz<SLOTS>(frow, kk * 2 + (lane >> 5)) * 16;
   const uint32_t b_delta = static_cast<uint32_t>(A_BYTES + (wn * WN - wm * WM) * ROWB);
+  // BKN: per-lane offset in a stage of fragment j's first transposing read at
+  // k16 step 0.  Lane group g = lane / 16 reads rows 8 (g / 2) + r / 4 (r =
+  // lane % 16) and columns 16 (g % 2) + 4 (r % 4) .. + 3 of the fragment's 32,
+  // so lane l receives column l % 32 at rows 8 (l / 32) .. + 3, the B-operand
+  // layout of the 32x32x16 MFMA; the second half is 4 rows further, the k16
+  // step 16 rows further (immediates).
+  uint32_t kn_off[BKN ? NI : 1];
+  if constexpr (BKN) {
+    const int g = lane >> 4, r = lane & 15, k = 8 * (g >> 1) + (r >> 2);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int n = wn * WN + 32 * j + 16 * (g & 1) + 4 * (r & 3);
+      kn_off[j] = static_cast<uint32_t>(A_BYTES + k * ROWB_B + (((n >> 3) ^ (4 * kn_swz<TN>(k))) << 4) + 8 * (r & 1));
+    }
+  }
 
   if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
     if constexpr (RS && CT == 0) {  // GEMM-AR is fp32 only
@@ -664,13 +518,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
     }
     if (a.trace_tiles && tid == 0) a.trace_tiles[4 * t + 1] = wall_clock64();
     const uint16_t* const a_tile = a.A + m0 * K;
-    const uint16_t* const b_tile = a.B + n0 * K;
+    const uint16_t* const b_tile = BKN ? a.B + n0 : a.B + n0 * K;
+    // B's buffer for the stage at k0: its rows (B [n][k]: the tile's columns
+    // from k0; B [k][n]: rows k0.. of B from column n0, to the end of B)
+    auto b_rsrc = [&](int64_t k0, bool live) {
+      if constexpr (BKN)
+        return make_rsrc(b_tile + k0 * N, live ? (K - k0) * N * 2 - n0 * 2 : 0);
+      else
+        return make_rsrc(b_tile + k0, live ? static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2 : 0);
+    };
 
     auto issue = [&](int kt) {  // loads of k-step kt into slot kt % NS
       char* st = smem + (kt % NS) * STAGE;
       const int64_t k0 = static_cast<int64_t>(kt) * TK;
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + k0, static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + k0, static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2);
+      const __amdgpu_buffer_rsrc_t rb = b_rsrc(k0, true);
 #pragma unroll
       for (int i = 0; i < A_LD; ++i) dma_load_16(ra, st + (wave * A_LD + i) * 1024, a_off[i]);
 #pragma unroll
@@ -731,8 +593,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
         dma_load_16(make_rsrc(a_tile + k0, live ? static_cast<int64_t>(rows_valid) * K * 2 - k0 * 2 : 0),
                     st + (wave * A_LD + i) * 1024, a_off[i]);
       else
-        dma_load_16(make_rsrc(b_tile + k0, live ? static_cast<int64_t>(cols_valid) * K * 2 - k0 * 2 : 0),
-                    st + A_BYTES + (wave * B_LD + i - A_LD) * 1024, b_off[i - A_LD]);
+        dma_load_16(b_rsrc(k0, live), st + A_BYTES + (wave * B_LD + i - A_LD) * 1024, b_off[i - A_LD]);
     };
 
     f32x16_t acc[MI][NI];
@@ -770,14 +631,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
     }
 
     const uint32_t ring = lds_addr(smem);
-    // fragment F (A blocks first, then B) of one k16 step from per-lane bases
-    auto read_frag = [&](uint32_t abase, uint32_t bbase, auto fc) -> bf16x8_t {
-      constexpr int F = decltype(fc)::value;
-      if constexpr (F < MI)
-        return lds_read_b128_at<F * 32 * ROWB>(abase);
-      else
-        return lds_read_b128_at<(F - MI) * 32 * ROWB>(bbase);
+    // One k16 step's fragments: A blocks, then B (BKN: two transposing halves
+    // per block, rows 0..3 and 4..7 of each lane's eight)
+    using BFrag = std::conditional_t<BKN, u32x2_t, bf16x8_t>;
+    struct Frags {
+      bf16x8_t a[MI];
+      BFrag b[NB];
     };
+    struct Bases {
+      uint32_t a, b, kn[BKN ? NI : 1];
+    };
+    auto bases = [&](uint32_t nst, int nkk) {
+      Bases q;
+      q.a = nst + frag_off[nkk];
+      q.b = q.a + b_delta;
+      if constexpr (BKN) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) q.kn[j] = nst + nkk * (16 * ROWB_B) + kn_off[j];
+      }
+      return q;
+    };
+    // read R of one k16 step (A first, then B) into f
+    auto read_one = [&](Frags& f, const Bases& q, auto rc) {
+      constexpr int R = decltype(rc)::value;
+      if constexpr (R < MI)
+        f.a[R] = lds_read_b128_at<R * 32 * ROWB>(q.a);
+      else if constexpr (BKN)
+        f.b[R - MI] = lds_read_tr16_at<((R - MI) % 2) * 4 * ROWB_B>(q.kn[(R - MI) / 2]);
+      else
+        f.b[R - MI] = lds_read_b128_at<(R - MI) * 32 * ROWB>(q.b);
+    };
+    // B operand of fragment j
+    auto b_op = [&](const Frags& f, auto jc) -> bf16x8_t {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (BKN)
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.b[2 * j], f.b[2 * j + 1], 0, 1, 2, 3));
+      else
+        return f.b[j];
+    };
+    // MFMA slot after which read R is issued: one read per slot while they
+    // fit, else spread evenly
+    constexpr auto read_slot = [](int r) { return NRD <= MI * NI ? r : r * (MI * NI) / NRD; };
     // MFMAs on one fragment set, interleaved with the reads of the next set.
     // The reads are unconditional: a read whose result the compiler might
     // discard would let it emit select/copy code on registers that an
@@ -787,13 +681,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
     // leaves those PPW writes in flight (LDS operations complete in order, so
     // the reads before them have landed).  SPREAD: part `part` (< FEED) of
     // stage pst's direct-to-LDS loads, one every GAP MFMAs.
-    auto mma = [&](bf16x8_t (&cur)[NFRAG], bf16x8_t (&nxt)[NFRAG], uint32_t nst, int nkk, int pst, int part) {
-      const uint32_t abase = nst + frag_off[nkk], bbase = abase + b_delta;
+    auto mma = [&](Frags& cur, Frags& nxt, uint32_t nst, int nkk, int pst, int part) {
+      const Bases q = bases(nst, nkk);
       unroll_each(
           [&](auto xc) {
             constexpr int x = decltype(xc)::value, i = x / NI, j = x % NI;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[i], cur[MI + j], acc[i][j], 0, 0, 0);
-            if constexpr (x < NFRAG) nxt[x] = read_frag(abase, bbase, xc);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[i], b_op(cur, std::integral_constant<int, j>{}),
+                                                                acc[i][j], 0, 0, 0);
+            unroll_each(
+                [&](auto rc) {
+                  if constexpr (read_slot(decltype(rc)::value) == x) read_one(nxt, q, rc);
+                },
+                std::make_integer_sequence<int, NRD>{});
             if constexpr (REG && x >= NFRAG && x < NFRAG + PPW) {
               put(pst, part * PPW + x - NFRAG);
               fetch(pst + 1, part * PPW + x - NFRAG);
@@ -829,7 +728,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
       }
     };
 
-    bf16x8_t fp[NFRAG], fq[NFRAG];
+    Frags fp, fq;
     if constexpr (REG) {
       wait_lgkmcnt<0>();
       __builtin_amdgcn_s_barrier();  // stage 0 is in its slot for every wave
@@ -837,8 +736,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
     } else {
       landed(0);
     }
-    unroll_each([&](auto fc) { fp[decltype(fc)::value] = read_frag(ring + frag_off[0], ring + frag_off[0] + b_delta, fc); },
-                std::make_integer_sequence<int, NFRAG>{});
+    {
+      const Bases q = bases(ring, 0);
+      unroll_each([&](auto rc) { read_one(fp, q, rc); }, std::make_integer_sequence<int, NRD>{});
+    }
     wait_lgkmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -916,32 +817,23 @@ hipError_t launch_gemm(const GemmArgs& a, int tm, int tn, int b_layout, int c_dt
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
     return hipGetLastError();
   };
-#define SYNC_GEMM_DMA_CASE(TM_, TN_, CT_)                                                                \
-  if (tm == TM_ && tn == TN_ && b_layout == 1 && c_dtype == CT_) {                                       \
-    using S_ = DmaShape<TM_, TN_>;                                                                       \
-    constexpr int threads_ = 64 * S_::WGM * S_::WGN;                                                     \
-    return rs ? go(gemm_dma<TM_, TN_, CT_, true, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>, threads_)  \
-              : go(gemm_dma<TM_, TN_, CT_, false, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED>, threads_); \
+#define SYNC_GEMM_DMA_CASE(TM_, TN_, BL_, CT_)                                                               \
+  if (tm == TM_ && tn == TN_ && b_layout == BL_ && c_dtype == CT_) {                                         \
+    using S_ = DmaShape<TM_, TN_>;                                                                           \
+    constexpr int threads_ = 64 * S_::WGM * S_::WGN;                                                         \
+    return rs ? go(gemm_dma<TM_, TN_, CT_, true, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED, BL_ == 0>,      \
+                   threads_)                                                                                 \
+              : go(gemm_dma<TM_, TN_, CT_, false, S_::TK, S_::NS, S_::WGM, S_::WGN, S_::FEED, BL_ == 0>,     \
+                   threads_);                                                                                \
   }
-  SYNC_GEMM_DMA_CASE(256, 256, 0)
-  SYNC_GEMM_DMA_CASE(256, 256, 1)
-  SYNC_GEMM_DMA_CASE(256, 128, 0)
-  SYNC_GEMM_DMA_CASE(256, 128, 1)
-  SYNC_GEMM_DMA_CASE(128, 128, 0)
-  SYNC_GEMM_DMA_CASE(128, 128, 1)
+#define SYNC_GEMM_DMA_TILES(BL_, CT_) \
+  SYNC_GEMM_DMA_CASE(256, 256, BL_, CT_) SYNC_GEMM_DMA_CASE(256, 128, BL_, CT_) SYNC_GEMM_DMA_CASE(128, 128, BL_, CT_)
+  SYNC_GEMM_DMA_TILES(1, 0)
+  SYNC_GEMM_DMA_TILES(1, 1)
+  SYNC_GEMM_DMA_TILES(0, 0)
+  SYNC_GEMM_DMA_TILES(0, 1)
+#undef SYNC_GEMM_DMA_TILES
 #undef SYNC_GEMM_DMA_CASE
-#define SYNC_GEMM_CASE(TM_, TN_, BL_, CT_)                                                               \
-  if (tm == TM_ && tn == TN_ && b_layout == BL_ && c_dtype == CT_) {                                     \
-    return rs ? go(gemm_persistent<TM_, TN_, BL_, CT_, true>, kThreads)                                  \
-              : go(gemm_persistent<TM_, TN_, BL_, CT_, false>, kThreads);                                \
-  }
-#define SYNC_GEMM_TILES(BL_, CT_) \
-  SYNC_GEMM_CASE(256, 256, BL_, CT_) SYNC_GEMM_CASE(256, 128, BL_, CT_) SYNC_GEMM_CASE(128, 128, BL_, CT_)
-  // B [n][k] always runs gemm_dma (above); gemm_persistent serves B [k][n]
-  SYNC_GEMM_TILES(0, 0)
-  SYNC_GEMM_TILES(0, 1)
-#undef SYNC_GEMM_TILES
-#undef SYNC_GEMM_CASE
   return hipErrorInvalidValue;
 }
 

@@ -397,8 +397,7 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   if (cfg.copy_kslices == 0) cfg.copy_kslices = 1;
   if (cfg.copy_kslices > 1) {
     const sync_plan_desc& d = plan->plan.desc;
-    if (op != SYNC_OP_AG_GEMM || d.b_layout != SYNC_B_NK)
-      return fail(SYNC_EINVAL, "copy_kslices > 1 is for AG-GEMM with B stored [n][k]");
+    if (op != SYNC_OP_AG_GEMM) return fail(SYNC_EINVAL, "copy_kslices > 1 is for AG-GEMM");
     if (cfg.backend == SYNC_COPY_SDMA)
       return fail(SYNC_EINVAL, "copy_kslices > 1 needs the CU, COLOCATED or PRESET backend");
     if (d.k / 64 < 4 * static_cast<int64_t>(cfg.copy_kslices))
@@ -1016,8 +1015,6 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
     const int64_t es = c_dtype == SYNC_DTYPE_F32 ? 4 : 2;
     if (pl.desc.m * pl.desc.n * es >= (int64_t(1) << 31))
       return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend needs m x n x element size below 2 GiB");
-    if (pl.desc.b_layout != SYNC_B_NK)
-      return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend is built for B stored [n][k]");
     if (!cx.tab->push_rows)
       return fail(SYNC_EUNSUPPORTED, "the EPILOGUE backend needs every tile inside one chunk (chunk rows a "
                                      "multiple of tile_m)");

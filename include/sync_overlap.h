@@ -202,10 +202,9 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *               sent[c] with done[c] [SYN-S Fig. 7: communication by the
  *               compute SMs' own stores; Entwine abstract: output handed to
  *               communication as the tiles produce it].  C may be NULL
- *               here: the send slots are then the only output.  Needs B stored
- *               [n][k], every tile inside one chunk (chunk bounds on tile
- *               rows) and m x n x (element size) below 2 GiB, else
- *               EUNSUPPORTED. */
+ *               here: the send slots are then the only output.  Needs every
+ *               tile inside one chunk (chunk bounds on tile rows) and
+ *               m x n x (element size) below 2 GiB, else EUNSUPPORTED. */
 enum { SYNC_COPY_PRESET = 0, SYNC_COPY_SDMA = 1, SYNC_COPY_CU = 2, SYNC_COPY_HOST_GATED = 3, SYNC_COPY_COLOCATED = 4,
        SYNC_COPY_EPILOGUE = 5 };
 
@@ -241,7 +240,7 @@ typedef struct {
                                for its chunk's done flag).  0 or 1 = one chunk after another
                                (ring arrival); the number of copied chunks = all at once (pulls
                                from every peer in parallel, as over a full xGMI mesh). */
-  int32_t copy_kslices;     /* AG-GEMM with B [n][k] and the CU or COLOCATED backend: every chunk
+  int32_t copy_kslices;     /* AG-GEMM with the CU or COLOCATED backend: every chunk
                                moves as this many column blocks (K-slices) of its rows, slice 0
                                of every chunk first, each slice with its own ready flag; a tile
                                starts on slice 0 of its rows and waits in-kernel for slice h

@@ -103,8 +103,8 @@ def test_withhold_and_trace_validation():
 
 
 def test_kslices_validation():
-    """copy_kslices is checked before any device work: range, op, B layout,
-    backend, and at least four 64-deep K steps per slice."""
+    """copy_kslices is checked before any device work: range, op, backend, and
+    at least four 64-deep K steps per slice."""
     def rc_of(plan, cfg):
         return A.lib().sync_ag_gemm(plan.handle, ctypes.byref(cfg), None, None, None, None, 0, 256, None, None)
     nk = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
@@ -115,9 +115,6 @@ def test_kslices_validation():
     assert "K/64" in A.sync_last_error()
     assert rc_of(nk, A.make_cfg(A.SYNC_COPY_SDMA, copy_kslices=2)) == A.SYNC_EINVAL
     assert "COLOCATED" in A.sync_last_error()
-    kn = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_KN))
-    assert rc_of(kn, A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2)) == A.SYNC_EINVAL
-    assert "[n][k]" in A.sync_last_error()
     rs = A.sync_plan(A.make_desc(A.SYNC_OP_GEMM_RS, 1024, 256, 1024, 4, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
     rc = A.lib().sync_gemm_rs(rs.handle, ctypes.byref(A.make_cfg(A.SYNC_COPY_CU, 8, copy_kslices=2)), None, None,
                               None, 0, None, 256, None, None)
