@@ -20,14 +20,15 @@
 //    reductions plus one swap between the two 32-lane halves.
 //  * O^T += V^T P^T keeps P in registers: the score accumulator's layout is
 //    already the MFMA B-operand layout once the 16 keys of each k-step are
-//    read in the order [0-3, 8-11, 4-7, 12-15]; V^T is written to LDS with
-//    its keys permuted the same way.  Each lane's O^T column is one query, so
-//    the rescale by e^(m-m') is a per-lane multiply.
+//    taken in the order [0-3, 8-11, 4-7, 12-15].  V stays in LDS as it is in
+//    memory (key-major), and gfx950's transposing LDS reads build the V^T
+//    fragments, 4 keys per read, in that same key order.  Each lane's O^T
+//    column is one query, so the rescale by e^(m-m') is a per-lane multiply.
 //  * exp2 with the scale folded into log2(e) units; probabilities go to bf16
 //    for the PV product, the running sum stays fp32.
 //  * KV tiles of 64 keys, double-buffered in LDS (66 KB), prefetched one tile
-//    ahead through registers; raw buffer loads return zero past a chunk's
-//    last key, and those keys are masked to -inf.
+//    ahead through registers with 16-byte loads; raw buffer loads return zero
+//    past a chunk's last key, and those keys are masked to -inf.
 //
 // The same kernel runs the head-parallel share (Syncopate summary page,
 // "Experiments", paper sec. 6.1 and Fig. 9, head-parallel attention; the
@@ -51,7 +52,7 @@ constexpr int kKT = 64;           // keys per tile
 constexpr int kAttnThreads = 512;  // 8 waves (4 waves in two workgroups per CU measured 13 % slower)
 constexpr int kAttnWgPerCu = 512 / kAttnThreads;
 constexpr int kKLoads = kKT * 16 / kAttnThreads;  // 16-byte K granules per thread per tile
-constexpr int kVUnits = kKT * kD / 16 / kAttnThreads;  // (8 keys, 2 dims) V units per thread per tile
+constexpr int kVLoads = kKT * 16 / kAttnThreads;  // 16-byte V granules per thread per tile
 // A work item is HG query heads sharing one KV head (HG = min(heads_q /
 // heads_kv, 4)) times 32 * (waves / HG) query rows: one wave per (head, 32 rows).
 
@@ -60,11 +61,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
 }
 
-// LDS rows are padded by one 16-byte slot (K: 16 slots of 8 dims per key,
-// V^T: 8 slots of 8 keys per dim), so the 16 lanes of a 128-bit read, one row
-// each, start on 16 distinct 4-bank groups, and a lane's reads differ from
-// one another by immediate offsets only.
-constexpr int kKRow = 17, kVRow = 9;
+// K rows are padded by one 16-byte slot (16 slots of 8 dims per key), so the
+// 16 lanes of a 128-bit read, one row each, start on 16 distinct 4-bank
+// groups, and a lane's reads differ from one another by immediate offsets
+// only.
+constexpr int kKRow = 17;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+// gfx950's transposing LDS read of 16-bit elements: within every group of 16
+// lanes, lane i receives element i % 4 of the 8 bytes named by lanes i / 4,
+// i / 4 + 4, i / 4 + 8 and i / 4 + 12, in that order.  When lane r of a group
+// names row r / 4, columns 4 (r % 4) .. + 3 of a row-major block, lane i
+// receives column i, rows 0..3.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+#else
+  return s16x4_t{};
+#endif
+}
+// V sits in LDS as it is in memory, [key][16 slots of 8 dims], with 16-byte
+// slot s of key k at slot s ^ 4 (k % 4): the 8 keys one transposing read of
+// the PV product touches (4 per 32 lanes) then fall on 4 distinct 64-byte
+// bank groups, twice.
+__device__ __forceinline__ int vswz(int key, int slot) { return slot ^ (4 * (key & 3)); }
 
 // Scheduling hint for a block of N MFMAs fed by N LDS reads: issue AHEAD
 // reads first, then alternate one MFMA and one read, so AHEAD reads stay in
@@ -80,13 +100,10 @@ __device__ __forceinline__ void sched_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
-// Physical position (0..15) inside a 16-key k-step -> key offset.  Lane half h
-// holds keys {4h..4h+3, 8+4h..8+4h+3} of the step in the score accumulator.
-__device__ __forceinline__ int perm16(int phys) { return ((phys >> 3) << 2) + ((phys >> 2) & 1) * 8 + (phys & 3); }
 
 __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(AttnArgs a) {
   __shared__ u32x4_t Ks[2][kKT * kKRow];  // [key][16 slots of 8 d + pad]
-  __shared__ u32x4_t Vt[2][kD * kVRow];   // [dv][8 slots of 8 permuted keys + pad]
+  __shared__ u32x4_t Vs[2][kKT * 16];     // [key][16 slots of 8 dims, swizzled]
   __shared__ int32_t s_ok;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -100,6 +117,18 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
   const float c2 = a.scale * 1.4426950408889634f;  // scale in log2 units
   const int group = static_cast<int>(Hq / Hkv);  // query heads per KV head
   const int nqb = static_cast<int>((a.sq + QB - 1) / QB);
+  // per-lane byte offset in a V tile of the first transposing read of dim
+  // block b: lane r of 16-lane group g names key 4 (g / 2) + r / 4 and dims
+  // 32 b + 16 (g % 2) + 4 (r % 4) .. + 3
+  int vrd[4];
+  {
+    const int g = lane >> 4, r = lane & 15, key = 4 * (g >> 1) + (r >> 2);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int dim = 32 * b + 16 * (g & 1) + 4 * (r & 3);
+      vrd[b] = key * 256 + vswz(key, dim >> 3) * 16 + (dim & 7) * 2;
+    }
+  }
   const int items = a.items ? a.num_items : nqb * static_cast<int>(Hq / HG);
 
   if (static_cast<int32_t>(blockIdx.x) < a.copy_blocks) {
@@ -181,8 +210,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
     // tile cursor over the chunks in arrival order
     int p = 0;
     int64_t t0 = a.chunk_begin[a.arrival[0]];
-    u32x4_t rk[kKLoads];
-    uint32_t rv[kVUnits][8];
+    u32x4_t rk[kKLoads], rv[kVLoads];
     auto wait_chunk = [&](int pos) {
       const int32_t c = a.arrival[pos];
       if (!a.wait_chunks || a.resident[c]) return 1;  // in place before the call
@@ -208,15 +236,11 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
         rk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                     rk_, static_cast<uint32_t>((key * krow + sl * 8) * 2), 0, 0));
       }
-      // V: unit = (8 permuted keys of a 16-key step half, 2 dims)
 #pragma unroll
-      for (int u = 0; u < kVUnits; ++u) {
-        const int un = tid + u * kAttnThreads, dp = un & 63, kg = un >> 6;  // dims 2dp, 2dp+1; key group kg
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = (kg >> 1) * 16 + perm16((kg & 1) * 8 + j);
-          rv[u][j] = __builtin_amdgcn_raw_buffer_load_b32(rv_, static_cast<uint32_t>((key * krow + dp * 2) * 2), 0, 0);
-        }
+      for (int i = 0; i < kVLoads; ++i) {  // V: the same granules
+        const int gi = tid + i * kAttnThreads, key = gi >> 4, sl = gi & 15;
+        rv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    rv_, static_cast<uint32_t>((key * krow + sl * 8) * 2), 0, 0));
       }
     };
     auto store_tile = [&](int buf) {
@@ -226,19 +250,9 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
         Ks[buf][key * kKRow + sl] = rk[i];
       }
 #pragma unroll
-      for (int u = 0; u < kVUnits; ++u) {
-        const int un = tid + u * kAttnThreads, dp = un & 63, kg = un >> 6;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          u32x4_t w;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = rv[u][2 * j], hi = rv[u][2 * j + 1];
-            w[j] = e ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-          }
-          const int dv = dp * 2 + e;
-          Vt[buf][dv * kVRow + kg] = w;
-        }
+      for (int i = 0; i < kVLoads; ++i) {
+        const int gi = tid + i * kAttnThreads, key = gi >> 4, sl = gi & 15;
+        Vs[buf][key * 16 + vswz(key, sl)] = rv[i];
       }
     };
     auto advance = [&](int& pos, int64_t& t) {  // next tile; pos == C when done
@@ -329,14 +343,20 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
         }
       lsum += __shfl_xor(lsum, 32, 64);
       l += lsum;
-      // O^T += V^T P^T: 4 blocks of 32 dims x 4 k-steps of 16 keys
+      // O^T += V^T P^T: 4 blocks of 32 dims x 4 k-steps of 16 keys.  A
+      // fragment's lane holds dim 32 b + lane % 32 at keys 4 h..4 h + 3 and
+      // 8 + 4 h..8 + 4 h + 3 of the k-step (h = lane / 32: the order P holds
+      // them in), two transposing reads of 4 keys each.
       {
         bf16x8_t vf[4][4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            vf[ks][b] = __builtin_bit_cast(bf16x8_t, Vt[buf][(b * 32 + col) * kVRow + ks * 2 + half]);
+          for (int b = 0; b < 4; ++b) {
+            const char* const p = reinterpret_cast<const char*>(Vs[buf]) + ks * 16 * 256 + vrd[b];
+            const s16x4_t lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * 256);
+            vf[ks][b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
