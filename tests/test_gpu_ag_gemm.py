@@ -446,6 +446,25 @@ def test_kslices_parity(backend, cus, teams, kslices, tile, lead):
     assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
 
 
+@pytest.mark.parametrize("backend,cus,teams,kslices,tile,lead,n", [
+    (A.SYNC_COPY_CU, 8, 1, 2, (256, 256), 1, 768), (A.SYNC_COPY_CU, 16, 3, 4, (256, 128), 2, 768),
+    (A.SYNC_COPY_COLOCATED, 0, 3, 4, (256, 256), 0, 768), (A.SYNC_COPY_CU, 8, 5, 3, (128, 128), 3, 768),
+    (A.SYNC_COPY_CU, 32, 7, 2, (256, 256), 1, 520), (A.SYNC_COPY_CU, 16, 3, 3, (256, 128), 0, 520)])
+def test_kslices_parity_b_kn(backend, cus, teams, kslices, tile, lead, n):
+    """The K-sliced copy with B stored [k][n] (the transposing-read path),
+    ragged last tile column included: matches the oracle and is bitwise the
+    compute-only output."""
+    m, k, world, split = 2048, 1152, 4, 2
+    a, b = inputs.gemm_operands(m, n, k, 32.0, b_layout="kn")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="kn")
+    out, a_local = run_ag(m, n, k, world, a, b, layout="kn", split=split, tile=tile, backend=backend,
+                          copy_cus=cus, teams=teams, kslices=kslices, lead=lead)
+    check_f32(out, ref, world)
+    assert np.array_equal(a_local, a)
+    base, _ = run_ag(m, n, k, world, a, b, layout="kn", split=split, tile=tile, backend=A.SYNC_COPY_PRESET)
+    assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
+
+
 @pytest.mark.parametrize("cus,teams,kslices,tile,rank,lead", [
     (8, 1, 2, (256, 256), 0, 0), (32, 7, 4, (256, 256), 1, 0), (16, 3, 4, (256, 128), 2, 0),
     (8, 5, 3, (128, 128), 3, 0), (32, 7, 4, (256, 256), 1, 1), (8, 5, 3, (128, 128), 3, 1),

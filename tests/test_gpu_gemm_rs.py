@@ -242,15 +242,16 @@ def test_rs_paced_copy_out(teams):
                                                       (1024, 512, 256, 4, 2, (128, 128), 3),
                                                       (2048, 768, 320, 4, 1, (256, 256), 1),
                                                       (1024, 520, 320, 4, 1, (256, 128), 2)])
-def test_rs_epilogue_push(m, n, k, W, split, tile, rank):
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+def test_rs_epilogue_push(m, n, k, W, split, tile, rank, layout):
     """No copy pass: C exact for small integers, every chunk bitwise in its
     send slot, done and sent flags raised, counters back to zero (a ragged
-    last tile column included)."""
-    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
-    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    last tile column included), with B stored either way."""
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout=layout)
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout=layout)
     for rep in range(2):
         cn, st, tabs = run_rs(m, n, k, W, a, b, split=split, tile=tile, backend=A.SYNC_COPY_EPILOGUE, copy_cus=0,
-                              rank=rank, layout=A.SYNC_B_NK)
+                              rank=rank, layout=A.SYNC_B_NK if layout == "nk" else A.SYNC_B_KN)
         assert np.array_equal(cn.astype(np.float64), ref)
         check_staging(cn, st, tabs)
 
