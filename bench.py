@@ -187,6 +187,10 @@ def parse(argv=None):
     p.add_argument("--attention-only", action="store_true",
                    help="time only the ring-attention and head-parallel attention rows (--steps/--warmup calls "
                         "per agent) and print them as one JSON object (a profiling aid, not the bench line)")
+    p.add_argument("--row", default=None, choices=["rs", "ag70", "a2a", "attention"],
+                   help="time only one of the other rows (GEMM-RS and GEMM-AR, 70B-like AG, A2A receive side, or "
+                        "attention), --steps/--warmup calls per series, and print it as one JSON object (a "
+                        "profiling aid, not the bench line)")
     p.add_argument("--tune", action="store_true",
                    help="run the autotuner over split {1,2,4} x tile {256x256, 256x128} x copy agent (SDMA on 7 "
                         "engines, 16 or 32 copy CUs with 4 K-slices, co-located) first and bench its choice")
@@ -284,8 +288,10 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     timer = Timer(torch)
-    if args.attention_only:
-        print(json.dumps(attention_rows(timer, torch, inputs, stream, args.steps, args.warmup)), flush=True)
+    row = "attention" if args.attention_only else args.row
+    if row:
+        fn = {"rs": rs_rows, "ag70": ag70_row, "a2a": a2a_row, "attention": attention_rows}[row]
+        print(json.dumps(fn(timer, torch, inputs, stream, args.steps, args.warmup)), flush=True)
         return
     cold = args.cache == "cold"
     tuned = None
@@ -523,17 +529,35 @@ def layout_kn_row(timer, torch, inputs, stream, steps=10, warmup=3):
     return out
 
 
-def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
-    """The other rows of the hot path on their configurations, cold cache."""
-    import numpy as np
-
-    dev = torch.device("cuda:0")
-    out = {}
-
+def _cold_median(timer, stream, steps, warmup):
+    """A timer of one call: its median over `steps` cold launches after `warmup`, the workspace checked."""
     def t_of(fn, ws):
         st = timer.series(fn, steps, warmup, True)
         check(ws, stream)
         return st["median_s"]
+    return t_of
+
+
+def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
+    """The other rows of the hot path on their configurations, cold cache."""
+    out = rs_rows(timer, torch, inputs, stream, steps, warmup)
+    progress("GEMM-RS and GEMM-AR rows done")
+    out.update(ag70_row(timer, torch, inputs, stream, steps, warmup))
+    progress("70B-like AG row done")
+    out.update(a2a_row(timer, torch, inputs, stream, steps, warmup))
+    out.update(attention_rows(timer, torch, inputs, stream, steps, warmup))
+    return out
+
+
+def rs_rows(timer, torch, inputs, stream, steps=5, warmup=2):
+    """GEMM-RS on the Llama-3-8B down-projection (copy agents, send slots only,
+    the reduce-scatter step, the split baseline, emission cadence) and the
+    GEMM-AR share by split, cold cache."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    out = {}
+    t_of = _cold_median(timer, stream, steps, warmup)
 
     # GEMM-RS, Llama-3-8B down-projection (B stored [n][k], C fp32)
     m, n, k, w = (RS_SHAPE[x] for x in ("m", "n", "k", "world"))
@@ -601,7 +625,18 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
                              "gap_cv": round(float(gaps.std() / gaps.mean()), 3) if gaps.mean() > 0 else None}}
     del a, b, c, st
 
-    progress("GEMM-RS and GEMM-AR rows done")
+    return out
+
+
+def ag70_row(timer, torch, inputs, stream, steps=5, warmup=2):
+    """AG-GEMM on the 70B-like FFN shape: copy agents and the chunk-size x
+    tile-order sweep, cold cache."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    out = {}
+    t_of = _cold_median(timer, stream, steps, warmup)
+
     # AG-GEMM 70B-like: A 16384x8192 (8 shards of 2048 rows), B 8192x3584 stored [n][k], C fp32
     m, n, k, w = (AG70_SHAPE[x] for x in ("m", "n", "k", "world"))
     a_bits, b_bits = inputs.gemm_operands(m, n, k, AG70_SHAPE["divisor"], b_layout="nk")
@@ -644,7 +679,17 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
         "chunk_size_x_tile_order_sweep": {"agent": "colocated", "by_split_order": sweep}}
     del ap, b, al, c, wss, plans
 
-    progress("70B-like AG row done")
+    return out
+
+
+def a2a_row(timer, torch, inputs, stream, steps=5, warmup=2):
+    """The A2A-GEMM receive side with uneven token blocks, cold cache."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    out = {}
+    t_of = _cold_median(timer, stream, steps, warmup)
+
     # A2A-GEMM receive side, MoE-like: 8 peers send uneven token blocks to this rank's expert
     m, n, k, w = (A2A_SHAPE[x] for x in ("m", "n", "k", "world"))
     rows = inputs.routed_token_counts(m, w)
@@ -673,7 +718,6 @@ def other_rows(timer, torch, inputs, stream, steps=5, warmup=2):
         "frac_mfma_peak": round(flops / t[best] / 1e12 / PEAK_BF16_TFLOPS, 4),
         "t_overlap_us_by_agent": {nm: round(t[nm] * 1e6, 1) for nm in A2A_AGENTS}}
     del ap, b, al, c
-    out.update(attention_rows(timer, torch, inputs, stream, steps, warmup))
     return out
 
 
