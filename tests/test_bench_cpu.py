@@ -42,3 +42,14 @@ def test_traffic_only_for_the_profiled_configuration():
     for argv in (["--tile", "256x128"], ["--split", "2"], ["--backend", "cu16"], ["--kslices", "4"], ["--lead", "0"],
                  ["--c-dtype", "bf16"], ["--layout", "kn"], ["--teams", "1"], ["--copy-store", "stream"]):
         assert bench.profiled_traffic(_args(*argv)) is None, argv
+
+
+def test_single_row_option_names_every_row_function():
+    """--row picks one of the other rows (a profiling aid); the default runs the bench line."""
+    assert _args().row is None
+    for r in ("rs", "ag70", "a2a", "attention"):
+        assert _args("--row", r).row == r
+    for fn in (bench.rs_rows, bench.ag70_row, bench.a2a_row, bench.attention_rows):
+        assert callable(fn)
+    with pytest.raises(SystemExit):
+        _args("--row", "headline")
