@@ -411,6 +411,8 @@ def main(argv=None):
         progress("copy backend sweep done")
         line["split_sweep"] = split_sweep(series, torch, tm, tn, order, b_layout)
         progress("split sweep done")
+        line["tile_sweep"] = tile_sweep(series, torch, order, b_layout, agent)
+        progress("tile sweep done")
         line["trace_headline"] = trace_headline(plan, agent, a_peer, a_local, b, c_out, c_dtype, ws, stream, tabs)
         line["layout_kn_row"] = layout_kn_row(timer, torch, inputs, stream)
         line["split_baseline"] = {"ag_llama8b_up": split_baseline_ag(timer, plan, a_peer, a_local, b, c_out, c_dtype, ws,
@@ -461,6 +463,36 @@ def split_sweep(series, torch, tm, tn, order, b_layout, steps=10, warmup=3):
             t_c = series(cfg(flags=A.SYNC_RUN_COPY_ONLY, **ag), steps, warmup, True, pl, w)["median_s"]
             out[f"split{sp}_{name}"] = {"chunk_mib": round(8.0 / sp, 2), "t_overlap_us": round(t_o * 1e6, 1),
                                         "t_copy_only_us": round(t_c * 1e6, 1), "ratio": round(t_o / max(comp, t_c), 4)}
+    return out
+
+
+TILE_SWEEP = ((256, 256), (256, 128), (128, 128))  # the kernel's tile shapes (256x224 splits no wave grid in 32s)
+WG_PER_CU = {(128, 128): 2}  # workgroups per CU each tile shape runs with (others: 1)
+
+
+def tile_sweep(series, torch, order, b_layout, agent, steps=10, warmup=3):
+    """Tile shape x mode on the headline workload (split 1), cold cache, with
+    the wave efficiency T / (P ceil(T / P)) of T tiles on P resident compute
+    workgroups (all CUs for compute-only, all but the 32 copy CUs overlapped)."""
+    import math
+
+    out = {}
+    num_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for tm, tn in TILE_SWEEP:
+        pl = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, M, N, K, WORLD, tile_m=tm, tile_n=tn, tile_order=order,
+                                     b_layout=b_layout))
+        w = workspace(pl, torch)
+        t_c = series(cfg(backend=PRESET), steps, warmup, True, pl, w)["median_s"]
+        t_o = series(cfg(**agent), steps, warmup, True, pl, w)["median_s"]
+        tiles = math.ceil(M / tm) * math.ceil(N / tn)
+        wpc = WG_PER_CU.get((tm, tn), 1)
+        eff = {}
+        for mode, cus in (("compute_only", num_cus), ("overlapped", num_cus - agent.get("copy_cus", 0))):
+            p = cus * wpc
+            eff[mode] = round(tiles / (p * math.ceil(tiles / p)), 4)
+        out[f"{tm}x{tn}"] = {"tiles": tiles, "workgroups_per_cu": wpc, "t_compute_only_us": round(t_c * 1e6, 1),
+                             "t_overlap_us": round(t_o * 1e6, 1), "tflops_overlap": round(2.0 * M * N * K / t_o / 1e12, 1),
+                             "wave_efficiency": eff}
     return out
 
 

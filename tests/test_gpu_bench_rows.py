@@ -65,6 +65,18 @@ def test_headline_workload_agents(cfg2_data, name, split, ag):
     check_full_f32(out, ref, absab, K2, W2)
 
 
+@pytest.mark.parametrize("tile", [t for t in bench.TILE_SWEEP if t != bench.HEADLINE["tile"]],
+                         ids=[f"{t[0]}x{t[1]}" for t in bench.TILE_SWEEP if t != bench.HEADLINE["tile"]])
+def test_tile_sweep_agent(cfg2_data, tile):
+    """The tile sweep's other shapes with the headline agent: every output
+    element against the oracle; every copied row staged."""
+    a, b_kn, ref, absab = cfg2_data
+    out, a_local = run_ag(M2, N2, K2, W2, a, np.ascontiguousarray(b_kn.T), layout="nk", split=1, tile=tile,
+                          **_ag_kwargs(bench.HEADLINE_AGENT))
+    assert np.array_equal(a_local, a)
+    check_full_f32(out, ref, absab, K2, W2)
+
+
 def _run_ag_paced(a, b_nk, split, ag):
     plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, M2, N2, K2, W2, split=split, tile_m=256, tile_n=256,
                                    b_layout=A.SYNC_B_NK))
