@@ -338,6 +338,9 @@ def main(argv=None):
             "copy_only": series(cfg(flags=A.SYNC_RUN_COPY_ONLY, **agent), args.steps, args.warmup, mode == "cold")}
     dirty = {"overlapped": series(cfg(**agent), args.steps, args.warmup, True, clean=False),
              "compute_only": series(cfg(backend=PRESET), args.steps, args.warmup, True, clean=False)}
+    # compute-only on the workgroups the CU split leaves the GEMM (the copy CUs idle), cold
+    same_mask = series(cfg(flags=A.SYNC_RUN_COMPUTE_ONLY, backend=CU, copy_cus=agent["copy_cus"]), args.steps,
+                       args.warmup, True) if agent["backend"] == CU else None
     progress("headline series done")
     head = res[args.cache]
     flops = 2.0 * M * N * K
@@ -404,6 +407,12 @@ def main(argv=None):
             "launch_mean_us": round(t_ovl * 1e6, 2),
         },
     }
+    if same_mask is not None:
+        t_sm, t_o, t_p = same_mask["median_s"], res["cold"]["overlapped"]["median_s"], res["cold"]["copy_only"]["median_s"]
+        line["overlap"]["cold_same_cu_mask"] = {
+            "note": "compute-only on the workgroups the copy CUs leave the GEMM (the copy CUs idle)",
+            "t_compute_only_us": round(t_sm * 1e6, 1), "ratio": round(t_o / max(t_sm, t_p), 4),
+            "series": brief(same_mask)}
     if tuned is not None:
         line["autotune"] = tuned
     if not args.no_other_rows:

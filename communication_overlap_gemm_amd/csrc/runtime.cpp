@@ -635,6 +635,17 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
   return r;
 }
 
+// A GEMM launch whose workgroups only compute takes no more of them than the
+// plan has tiles, rounded up to a multiple of the XCD count, so the slot remap
+// gives every XCD an equal run of consecutive tiles.  (224 tiles on 256
+// workgroups would leave one XCD idle and give the other seven 32 tiles each,
+// spanning more distinct A rows per L2.)
+void fit_grid_to_tiles(Roles& r, int32_t tiles, int nxcd) {
+  if (r.grid <= 0 || r.copy_blocks || r.colocated || r.no_compute || nxcd < 1) return;
+  const int32_t want = (tiles + nxcd - 1) / nxcd * nxcd;
+  if (want > 0 && want < r.grid) r.grid = want;
+}
+
 // SDMA backend: reserve the call's signals; on the caller's stream the gate
 // kernel; every copied chunk queued on the SDMA engines (each copy waits for
 // the gate, so launch and queueing may happen in either order); then the
@@ -923,7 +934,8 @@ static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   const int64_t rb[kMaxCopyTensors] = {pl.desc.k * 2};
   GemmArgs g = make_gemm_args(pl, cx, a_local, b, c);
   g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
-  const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  fit_grid_to_tiles(r, pl.num_tiles, d.num_xcds);
   if (cx.cfg.copy_lead_slice && r.wait && r.grid > r.copy_blocks) {
     const int32_t withheld = (cx.cfg.flags & SYNC_RUN_WITHHOLD) ? cx.cfg.withhold_chunk : -2;
     LeadTables* lt = nullptr;
@@ -1010,7 +1022,8 @@ static int gemm_rs_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
     g.copy.out_flags = cx.ws.sent;
     g.copy.wait_flags = cx.ws.flags;
   }
-  const Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
+  if (!ar) fit_grid_to_tiles(r, pl.num_tiles, d.num_xcds);
   if (r.push) {
     const int64_t es = c_dtype == SYNC_DTYPE_F32 ? 4 : 2;
     if (pl.desc.m * pl.desc.n * es >= (int64_t(1) << 31))
