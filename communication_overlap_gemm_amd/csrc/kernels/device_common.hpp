@@ -43,6 +43,9 @@ constexpr int kMaxXcd = 16;
 __device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kMaxXcd - 1); }
 enum : uint32_t { ERR_TIMEOUT = 1u };
 
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
 __device__ __forceinline__ uint32_t ld_relaxed_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -55,8 +58,8 @@ __device__ __forceinline__ void st_release_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint32_t add_acq_rel_agent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t add_relaxed_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ bool epoch_reached(uint32_t flag, uint32_t epoch) {
@@ -70,6 +73,7 @@ __device__ __forceinline__ void record_timeout(uint32_t* hdr, int32_t chunk) {
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
     __hip_atomic_store(hdr + WS_ERR_CHUNK, static_cast<uint32_t>(chunk), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+  release_agent();  // ordered before this workgroup's exit count, which the call's last workgroup acquires
 }
 
 // Single-lane bounded wait for flags[c] to reach `epoch`.  Returns false when
@@ -106,8 +110,6 @@ __device__ __forceinline__ bool wait_flag(const uint32_t* flags, int32_t c, uint
   }
 }
 
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
 // Round-to-nearest-even float -> bf16 bits (inputs are finite in this library;
 // NaN is kept quiet).
@@ -121,17 +123,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Counting tree.  Many workgroups incrementing one word serialise on it; a
 // two-level tree keyed by the caller's rank (groups of `fan` workgroups, sizes
 // known from the count alone) keeps at most `fan` atomics on any word (16 for
-// up to 256 workgroups).  One lane per workgroup calls it after its own
-// release; it returns true for exactly one caller, the one that completes the
-// count, after clearing the words for the next use.  level1 holds up to 16
-// words.
+// up to 256 workgroups).  One lane per workgroup calls it; it returns true for
+// exactly one caller, the one that completes the count, after clearing the
+// words for the next use.  level1 holds up to 16 words.
+// Ordering: whatever a caller ordered before its call with an agent-scope
+// release fence happens-before everything the completing caller does after
+// the call.  The counts themselves are relaxed: an agent-scope acquire or
+// release on gfx950 is an L2 invalidate or write-back, so only the completer
+// of a group (acquire-release fence: it takes the group's releases over and
+// passes them on through its level-2 count) and the completer of the tree
+// (acquire fence) pay for one; every other caller pays only for its own
+// release.  (Each relaxed count returns its old value, which the caller
+// compares before it goes on, so its count is performed before anything the
+// caller issues after it.)
 __device__ __forceinline__ bool tree_count(uint32_t* level1, uint32_t* level2, int32_t rank, int32_t count) {
   const int32_t fan = count > 256 ? (count + 15) / 16 : 16;
   const int32_t g = rank / fan, groups = (count + fan - 1) / fan;
   const uint32_t in_group = static_cast<uint32_t>(count - g * fan < fan ? count - g * fan : fan);
-  if (add_acq_rel_agent(level1 + g, 1u) + 1u != in_group) return false;
+  if (add_relaxed_agent(level1 + g, 1u) + 1u != in_group) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
   st_relaxed_agent(level1 + g, 0u);
-  if (add_acq_rel_agent(level2, 1u) + 1u != static_cast<uint32_t>(groups)) return false;
+  if (add_relaxed_agent(level2, 1u) + 1u != static_cast<uint32_t>(groups)) return false;
+  acquire_agent();
   st_relaxed_agent(level2, 0u);
   return true;
 }
@@ -150,7 +163,12 @@ __device__ __forceinline__ uint32_t call_epoch(const uint32_t* hdr) {
   return e == 0u ? 1u : e;
 }
 
-// Last action of every workgroup (all threads).
+// Last action of every workgroup (all threads).  The exit count carries no
+// release of its own: the stores of the call are made visible by the end of
+// the kernel, and a recorded error by the release in record_timeout.  Each
+// workgroup's read of the old epoch was issued at its start, before the
+// barrier below, and the last workgroup stores the new epoch only after every
+// workgroup has counted out.
 __device__ __forceinline__ void end_call(uint32_t* hdr, uint32_t epoch, const CounterArrays& ca) {
   __syncthreads();
   if (threadIdx.x == 0) {

@@ -156,8 +156,9 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
 
 // GEMM-RS completion of tile t: every wave's C stores have reached the L2;
 // then one agent-scope release (a write-back of this XCD's L2, covering all
-// four waves) before the tile is counted toward each chunk it wrote; the last
-// tile of a chunk raises the chunk's done flag.
+// the waves) before the tile is counted toward each chunk it wrote, with
+// relaxed counts; the last tile of a chunk acquires the other tiles' releases
+// and raises the chunk's done flag.
 __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, uint32_t epoch, int tid) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
@@ -165,8 +166,9 @@ __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, ui
     release_agent();
     for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) {
       const int32_t c = a.dep_idx[e];
-      const uint32_t old = add_acq_rel_agent(a.cnt.counters + c, 1u);
+      const uint32_t old = add_relaxed_agent(a.cnt.counters + c, 1u);
       if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) {
+        acquire_agent();
         st_relaxed_agent(a.cnt.counters + c, 0u);  // every tile of c has counted: ready for the next call
         if (a.trace_chunks) a.trace_chunks[2 * c] = wall_clock64();
         st_release_agent(a.flags + c, epoch);
