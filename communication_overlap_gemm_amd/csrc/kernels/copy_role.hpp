@@ -181,12 +181,13 @@ __device__ __forceinline__ void copy_role(const CopyArgs& a, int32_t rank, int32
       release_agent();
       if (tree_count(a.xparts + first * kMaxXcd, a.parts + first, rank, count)) {
         const uint64_t now = wall_clock64();
+        release_agent();  // one release for every flag below (a waiter polls relaxed, then acquires)
         for (int32_t p = 0; p < a.num_chunks; ++p) {
           const int32_t c = a.arrival[p];
           if (skipped(c)) continue;
           if (a.trace_chunks) a.trace_chunks[2 * c] = now;
-          for (int32_t h = 0; a.kslices > 1 && h < a.kslices; ++h) st_release_agent(a.slice_flags + c * kMaxSlices + h, epoch);
-          st_release_agent(a.out_flags + c, epoch);
+          for (int32_t h = 0; a.kslices > 1 && h < a.kslices; ++h) st_relaxed_agent(a.slice_flags + c * kMaxSlices + h, epoch);
+          st_relaxed_agent(a.out_flags + c, epoch);
         }
       }
     }

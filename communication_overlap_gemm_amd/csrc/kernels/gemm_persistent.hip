@@ -168,13 +168,13 @@ __device__ __forceinline__ void publish_rs_tile(const GemmArgs& a, int32_t t, ui
       const int32_t c = a.dep_idx[e];
       const uint32_t old = add_relaxed_agent(a.cnt.counters + c, 1u);
       if (old + 1u == static_cast<uint32_t>(a.tiles_in[c])) {
-        acquire_agent();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");  // the chunk's other tiles, released onward with it
         st_relaxed_agent(a.cnt.counters + c, 0u);  // every tile of c has counted: ready for the next call
         if (a.trace_chunks) a.trace_chunks[2 * c] = wall_clock64();
-        st_release_agent(a.flags + c, epoch);
+        st_relaxed_agent(a.flags + c, epoch);
         if (a.push_rows) {  // the tiles also wrote the chunk into its send slot
           if (a.trace_chunks) a.trace_chunks[2 * c + 1] = wall_clock64();
-          st_release_agent(a.sent + c, epoch);
+          st_relaxed_agent(a.sent + c, epoch);
         }
       }
     }
