@@ -48,6 +48,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4_t buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Cache policy of the output stores (C and the send slots): SC1, device
+// scope.  No tile of the launch reads them back, and stored with device scope
+// they reach memory during the launch instead of sitting dirty in the XCD's
+// L2 until the launch ends and its caches are written back (measured: C
+// stores with the default policy left 3-10 us of write-back at the end of
+// the call, most for GEMM-RS, whose C is 134 MB).
+constexpr int kOutputStorePolicy = 16;
 
 
 // Epilogue.  Accumulator element e of a 32x32 block sits at row
@@ -133,7 +140,8 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
         const int r = it * RPI + rr;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + (r * SP + rc) * ES);
         if (col_ok) {
-          __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, cs, static_cast<uint32_t>(r * row_bytes + rc * ES), 0,
+                                                 kOutputStorePolicy);
           if constexpr (PUSH) {
             if (push) {
               const uint32_t off = static_cast<uint32_t>(r * row_bytes + rc * ES);
@@ -141,10 +149,7 @@ __device__ __forceinline__ void store_tile_w(const GemmArgs& a,
               if constexpr (CT == 0) {
                 if (reduce) w = add_partials(v, pv[it]);
               }
-              // the send slot is not read again by this launch's GEMM: a
-              // non-temporal store (cache policy NT) keeps it from displacing
-              // the A and B lines the other tiles still read from L2
-              __builtin_amdgcn_raw_buffer_store_b128(w, ss, off, 0, 2);
+              __builtin_amdgcn_raw_buffer_store_b128(w, ss, off, 0, kOutputStorePolicy);
             }
           }
         }
