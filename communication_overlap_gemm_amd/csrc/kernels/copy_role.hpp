@@ -38,30 +38,43 @@ typedef uint32_t copy_u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCopyUnroll = 16;  // 16-byte loads in flight per thread
 
+// The copy stores (unless STREAM) carry the device-scope cache policy (SC1):
+// the copied rows reach memory as they are written, so the agent-scope
+// release that publishes them finds little left to write back.  They go
+// through a buffer resource over the destination of one chunk, so every
+// offset must stay below 2 GiB; the runtime refuses larger chunks for the
+// backends that copy on CUs.
+constexpr int kCopyStorePolicy = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_dst_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
+}
+
 // Copies bytes [lo, hi) of src to dst (16-byte granules; both 16-byte
 // aligned), kCopyUnroll loads in flight per thread.  STREAM selects
-// non-temporal accesses.
+// non-temporal accesses; otherwise the stores carry kCopyStorePolicy and hi
+// stays below 2 GiB.
 template <int THREADS, bool STREAM>
 __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* __restrict__ dst, int64_t lo,
                                            int64_t hi) {
   const copy_u32x4_t* s = reinterpret_cast<const copy_u32x4_t*>(src);
   copy_u32x4_t* d = reinterpret_cast<copy_u32x4_t*>(dst);
+  const __amdgpu_buffer_rsrc_t drs = copy_dst_rsrc(dst);
   int64_t g = lo / 16 + threadIdx.x;
   const int64_t gend = hi / 16;
   constexpr int64_t step = THREADS;
   auto ld = [](const copy_u32x4_t* p) { return STREAM ? __builtin_nontemporal_load(p) : *p; };
-  auto st = [](copy_u32x4_t v, copy_u32x4_t* p) {
+  auto st = [&](copy_u32x4_t v, int64_t gi) {  // granule gi of dst
     if constexpr (STREAM)
-      __builtin_nontemporal_store(v, p);
+      __builtin_nontemporal_store(v, d + gi);
     else
-      *p = v;
+      __builtin_amdgcn_raw_buffer_store_b128(v, drs, static_cast<uint32_t>(gi * 16), 0, kCopyStorePolicy);
   };
   for (; g + (kCopyUnroll - 1) * step < gend; g += kCopyUnroll * step) {
     copy_u32x4_t v[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) v[u] = ld(s + g + u * step);
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) st(v[u], d + g + u * step);
+    for (int u = 0; u < kCopyUnroll; ++u) st(v[u], g + u * step);
   }
   if (g < gend) {  // the remainder, still with every load in flight before the stores
     copy_u32x4_t v[kCopyUnroll];
@@ -70,7 +83,7 @@ __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* _
       if (g + u * step < gend) v[u] = ld(s + g + u * step);
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
-      if (g + u * step < gend) st(v[u], d + g + u * step);
+      if (g + u * step < gend) st(v[u], g + u * step);
   }
 }
 
@@ -91,12 +104,12 @@ __device__ __forceinline__ void copy_block(const char* __restrict__ src, char* _
     const copy_u32x4_t* q = reinterpret_cast<const copy_u32x4_t*>(p);
     return STREAM ? __builtin_nontemporal_load(q) : *q;
   };
-  auto st = [](copy_u32x4_t v, char* p) {
-    copy_u32x4_t* q = reinterpret_cast<copy_u32x4_t*>(p);
+  const __amdgpu_buffer_rsrc_t drs = copy_dst_rsrc(dst);
+  auto st = [&](copy_u32x4_t v, int64_t off) {  // byte offset in dst
     if constexpr (STREAM)
-      __builtin_nontemporal_store(v, q);
+      __builtin_nontemporal_store(v, reinterpret_cast<copy_u32x4_t*>(dst + off));
     else
-      *q = v;
+      __builtin_amdgcn_raw_buffer_store_b128(v, drs, static_cast<uint32_t>(off), 0, kCopyStorePolicy);
   };
   while (g < hi) {
     copy_u32x4_t v[kCopyUnroll];
@@ -114,7 +127,7 @@ __device__ __forceinline__ void copy_block(const char* __restrict__ src, char* _
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
-      if (g + u * THREADS < hi) st(v[u], dst + off[u]);
+      if (g + u * THREADS < hi) st(v[u], off[u]);
     g += kCopyUnroll * THREADS;
   }
 }

@@ -701,6 +701,13 @@ template <typename Launch>
 int run_call(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed* tm, hipStream_t cs,
              const Roles& r, const char* const src[kMaxCopyTensors], char* const dst[kMaxCopyTensors],
              const int64_t rb[kMaxCopyTensors], int ntensors, Launch launch) {
+  if (r.copy_blocks || r.colocated) {  // the copy role stores with 32-bit offsets within one chunk
+    int64_t rows = 0;
+    for (int32_t c = 0; c < pl.num_chunks; ++c) rows = std::max(rows, pl.chunk_begin[c + 1] - pl.chunk_begin[c]);
+    for (int x = 0; x < ntensors; ++x)
+      if (rows * rb[x] >= (int64_t(1) << 31))
+        return fail(SYNC_EUNSUPPORTED, "the CU and COLOCATED backends copy chunks of under 2 GiB per tensor");
+  }
   auto timed = [&](hipStream_t st) -> int {
     if (tm) HIP_TRY(hipEventRecord(tm->k0, st));
     int rc = launch(st, r);

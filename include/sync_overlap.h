@@ -196,6 +196,9 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *               its share of each chunk and then computes.  GEMM-RS: every
  *               workgroup stores its tiles and then joins the copy-out, chunk
  *               by chunk in send order.
+ *   CU and COLOCATED copy each chunk with 32-bit offsets: every chunk of a
+ *               copied tensor (its rows x row bytes) must be under 2 GiB,
+ *               else EUNSUPPORTED.
  *   EPILOGUE    GEMM-RS only: no copy pass at all; the epilogue of every tile
  *               stores it both into C and, row by row, into its chunk's send
  *               slot in `staging`, and the tile that completes chunk c raises

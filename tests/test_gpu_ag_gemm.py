@@ -740,3 +740,23 @@ def test_lead_slices_copy_only_stages_everything():
                           copy_cus=16, teams=3, kslices=4, lead=2, flags=A.SYNC_RUN_COPY_ONLY)
     assert np.array_equal(a_local, a)
     assert np.isnan(out).all()
+
+
+def test_copy_role_refuses_chunks_of_2_gib():
+    """The CU and co-located copies store with 32-bit offsets inside one chunk:
+    a chunk of 2 GiB (131072 rows of 8192 bf16) is refused before any launch."""
+    m, n, k, W = 1 << 20, 256, 8192, 8
+    print(f"[ag] refusal m={m} n={n} k={k} W={W}", flush=True)
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, W, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    ws = workspace(plan)
+    a_peer = torch.empty((m, k), dtype=torch.int16, device="cuda:0")
+    a_local = torch.empty_like(a_peer)
+    b = torch.zeros((n, k), dtype=torch.int16, device="cuda:0")
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+    for kw in (dict(backend=A.SYNC_COPY_CU, copy_cus=32), dict(backend=A.SYNC_COPY_COLOCATED)):
+        with pytest.raises(A.SyncError) as ei:
+            A.sync_ag_gemm(plan, A.make_cfg(**kw), a_peer, a_local, b, c, A.SYNC_DTYPE_F32, ws,
+                           torch.cuda.current_stream(), None)
+        assert ei.value.code == A.SYNC_EUNSUPPORTED and "2 GiB" in ei.value.message
+    del a_peer, a_local, c
+    torch.cuda.empty_cache()
