@@ -509,8 +509,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWgPerCu<TM, TN>)) void gemm_dma(G
   if constexpr (!RS) {
     if (a.lead_ptr) lead_slice<THREADS>(a.copy, a.lead_ptr, a.lead_item, gb, epoch);  // slice 0 of the first tile's chunk
   }
-  const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
-  for (int32_t p = slot0; p < a.num_tiles; p += gn) {
+  const int32_t tg = (a.tile_grid > 0 && a.tile_grid < gn) ? a.tile_grid : gn;  // workgroups that take tiles
+  const int32_t slot0 = gb < tg ? xcd_slot(gb, tg, a.nxcd) : a.num_tiles;
+  for (int32_t p = slot0; p < a.num_tiles; p += tg) {
     const int32_t t = a.order[p];
     const int32_t ti = t / a.tiles_n, tj = t - ti * a.tiles_n;
     const int64_t m0 = static_cast<int64_t>(ti) * TM, n0 = static_cast<int64_t>(tj) * TN;

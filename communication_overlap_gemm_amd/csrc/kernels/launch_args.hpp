@@ -85,6 +85,7 @@ struct GemmArgs {
   int32_t wait_chunks;      // AG: 0 = every chunk is in place (compute-only)
   int32_t copy_blocks;
   int32_t colocated;        // AG: every compute workgroup first copies its share of each chunk
+  int32_t tile_grid;        // > 0: only compute workgroups [0, tile_grid) take tiles (the others only copy)
   uint64_t* trace_tiles;    // SYNC_RUN_TRACE: per tile {wait begin, wait end, end, xcc<<32 | slot}, or null
   uint64_t* trace_chunks;   // SYNC_RUN_TRACE: per chunk {ready/done, sent}, or null
   // AG with a K-sliced copy (kslices > 1): a tile waits for slice 0 of its

@@ -640,10 +640,15 @@ Roles roles_for(const CallCtx& cx, const DeviceState& d, int wpc) {
 // gives every XCD an equal run of consecutive tiles.  (224 tiles on 256
 // workgroups would leave one XCD idle and give the other seven 32 tiles each,
 // spanning more distinct A rows per L2.)
+// A co-located launch keeps its whole grid for the copy and hands the tiles
+// to that many of its workgroups (GemmArgs::tile_grid).
+int32_t tile_workgroups(int32_t tiles, int32_t workgroups, int nxcd) {
+  const int32_t want = nxcd < 1 ? tiles : (tiles + nxcd - 1) / nxcd * nxcd;
+  return want > 0 && want < workgroups ? want : workgroups;
+}
 void fit_grid_to_tiles(Roles& r, int32_t tiles, int nxcd) {
-  if (r.grid <= 0 || r.copy_blocks || r.colocated || r.no_compute || nxcd < 1) return;
-  const int32_t want = (tiles + nxcd - 1) / nxcd * nxcd;
-  if (want > 0 && want < r.grid) r.grid = want;
+  if (r.grid <= 0 || r.copy_blocks || r.colocated || r.no_compute) return;
+  r.grid = tile_workgroups(tiles, r.grid, nxcd);
 }
 
 // SDMA backend: reserve the call's signals; on the caller's stream the gate
@@ -943,6 +948,7 @@ static int ag_gemm_impl(sync_plan_t plan, const sync_copy_cfg* cfg, const void* 
   g.copy = make_copy_in(pl, cx, src, dst, rb, 1);
   Roles r = roles_for(cx, d, gemm_wg_per_cu(pl));
   fit_grid_to_tiles(r, pl.num_tiles, d.num_xcds);
+  if (r.colocated && !r.no_compute) g.tile_grid = tile_workgroups(pl.num_tiles, r.grid, d.num_xcds);
   if (cx.cfg.copy_lead_slice && r.wait && r.grid > r.copy_blocks) {
     const int32_t withheld = (cx.cfg.flags & SYNC_RUN_WITHHOLD) ? cx.cfg.withhold_chunk : -2;
     LeadTables* lt = nullptr;
