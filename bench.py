@@ -244,7 +244,7 @@ def stats(xs, wall=None):
 
     x = np.asarray(xs, dtype=np.float64)
     out = {"mean_s": float(x.mean()), "median_s": float(np.median(x)), "p10_s": float(np.percentile(x, 10)),
-           "p90_s": float(np.percentile(x, 90)), "n": int(x.size)}
+           "p90_s": float(np.percentile(x, 90)), "n": int(x.size), "samples": [float(v) for v in x]}
     if wall is not None:
         out["wall_s_per_step"] = wall
     return out
@@ -570,6 +570,24 @@ def layout_kn_row(timer, torch, inputs, stream, steps=10, warmup=3):
     return out
 
 
+def _interleaved_medians(timer, stream, calls, steps, warmup):
+    """Cold medians of several calls on one workload (name -> (call, workspace)),
+    timed in two rounds, the second in reverse order, so that a drift of the
+    chip's clock over the row (long attention launches warm it) weighs on
+    every call alike."""
+    import numpy as np
+
+    samples = {k: [] for k in calls}
+    order = list(calls)
+    for rnd, seq in enumerate((order, order[::-1])):
+        for k in seq:
+            fn, ws = calls[k]
+            st = timer.series(fn, steps, warmup if rnd == 0 else 1, True)
+            check(ws, stream)
+            samples[k] += st["samples"]
+    return {k: float(np.median(v)) for k, v in samples.items()}
+
+
 def _cold_median(timer, stream, steps, warmup):
     """A timer of one call: its median over `steps` cold launches after `warmup`, the workspace checked."""
     def t_of(fn, ws):
@@ -609,11 +627,11 @@ def rs_rows(timer, torch, inputs, stream, steps=5, warmup=2):
     c = torch.empty((m, n), dtype=torch.float32, device=dev)
     st = torch.empty_like(c)
     ws = workspace(plan, torch)
-    t = {}
-    for name, ag in RS_AGENTS.items():
-        t[name] = t_of(lambda: A.sync_gemm_rs(plan, cfg(**ag), a, b, c, A.SYNC_DTYPE_F32, st, ws, stream, None), ws)
-    t["send_only"] = t_of(lambda: A.sync_gemm_rs(plan, cfg(backend=EPI), a, b, None, A.SYNC_DTYPE_F32, st, ws, stream,
+    calls = {name: ((lambda ag=ag: A.sync_gemm_rs(plan, cfg(**ag), a, b, c, A.SYNC_DTYPE_F32, st, ws, stream, None)), ws)
+             for name, ag in RS_AGENTS.items()}
+    calls["send_only"] = (lambda: A.sync_gemm_rs(plan, cfg(backend=EPI), a, b, None, A.SYNC_DTYPE_F32, st, ws, stream,
                                                  None), ws)
+    t = _interleaved_medians(timer, stream, calls, steps, warmup)
     part = torch.from_numpy(inputs.partials_f32(m, n)).to(dev)
     t["overlapped_reduce_step"] = t_of(lambda: A.sync_gemm_rs_reduce(plan, cfg(backend=EPI), a, b, c, part, st, ws,
                                                                      stream, None), ws)
@@ -694,9 +712,10 @@ def ag70_row(timer, torch, inputs, stream, steps=5, warmup=2):
     def ag70(key, ag):
         return lambda: A.sync_ag_gemm(plans[key], cfg(**ag), ap, al, b, c, A.SYNC_DTYPE_F32, wss[key], stream, None)
 
-    t = {"compute_only": t_of(ag70((4, "chunk_major"), dict(backend=PRESET)), wss[(4, "chunk_major")])}
+    calls = {"compute_only": (ag70((4, "chunk_major"), dict(backend=PRESET)), wss[(4, "chunk_major")])}
     for name, (split, ag) in AG70_AGENTS.items():
-        t[name] = t_of(ag70((split, "chunk_major"), ag), wss[(split, "chunk_major")])
+        calls[name] = (ag70((split, "chunk_major"), ag), wss[(split, "chunk_major")])
+    t = _interleaved_medians(timer, stream, calls, steps, warmup)
     best = min(AG70_AGENTS, key=lambda nm: t[nm])
     split, ag = AG70_AGENTS[best]
     t["copy_only"] = t_of(lambda: A.sync_ag_gemm(plans[(split, "chunk_major")], cfg(flags=A.SYNC_RUN_COPY_ONLY, **ag),
@@ -742,9 +761,9 @@ def a2a_row(timer, torch, inputs, stream, steps=5, warmup=2):
     al[: rows[0]] = ap[: rows[0]]
     c = torch.empty((m, n), dtype=torch.float32, device=dev)
     ws = workspace(plan, torch)
-    t = {}
-    for name, ag in list(A2A_AGENTS.items()) + [("compute_only", dict(backend=PRESET))]:
-        t[name] = t_of(lambda: A.sync_ag_gemm(plan, cfg(**ag), ap, al, b, c, A.SYNC_DTYPE_F32, ws, stream, None), ws)
+    calls = {name: ((lambda ag=ag: A.sync_ag_gemm(plan, cfg(**ag), ap, al, b, c, A.SYNC_DTYPE_F32, ws, stream, None)),
+                    ws) for name, ag in list(A2A_AGENTS.items()) + [("compute_only", dict(backend=PRESET))]}
+    t = _interleaved_medians(timer, stream, calls, steps, warmup)
     best = min(A2A_AGENTS, key=lambda nm: t[nm])
     ag = A2A_AGENTS[best]
     t["copy_only"] = t_of(lambda: A.sync_ag_gemm(plan, cfg(flags=A.SYNC_RUN_COPY_ONLY, **ag), ap, al, b, c,
@@ -769,11 +788,6 @@ def attention_rows(timer, torch, inputs, stream, steps=5, warmup=2):
     dev = torch.device("cuda:0")
     out = {}
 
-    def t_of(fn, ws):
-        st = timer.series(fn, steps, warmup, True)
-        check(ws, stream)
-        return st["median_s"]
-
     # Ring attention: Q 4096x32x128, K/V 8 blocks of 4096 tokens x 8 heads x 128, non-causal
     sq, hq, hkv, d, nb, w = (ATTN_SHAPE[x] for x in ("sq", "hq", "hkv", "d", "n", "world"))
     q_bits, k_bits, v_bits = inputs.attention_operands(sq, hq, w * nb, hkv, d)
@@ -786,11 +800,11 @@ def attention_rows(timer, torch, inputs, stream, steps=5, warmup=2):
     o = torch.empty((sq, hq, d), dtype=torch.float32, device=dev)
     ms, ls, lse = (torch.empty((hq, sq), dtype=torch.float32, device=dev) for _ in range(3))
     ws = workspace(plan, torch)
-    t = {}
     fl = A.SYNC_ATTN_INIT | A.SYNC_ATTN_FINALIZE
-    for name, ag in ATTN_AGENTS.items():
-        t[name] = t_of(lambda: A.sync_ring_attn_step(plan, cfg(**ag), q, kp, vp, kl, vl, o, ms, ls, lse,
-                                                     1.0 / d ** 0.5, fl, ws, stream, None), ws)
+    calls = {name: ((lambda ag=ag: A.sync_ring_attn_step(plan, cfg(**ag), q, kp, vp, kl, vl, o, ms, ls, lse,
+                                                         1.0 / d ** 0.5, fl, ws, stream, None)), ws)
+             for name, ag in ATTN_AGENTS.items()}
+    t = _interleaved_medians(timer, stream, calls, steps, warmup)
     best = min((x for x in ATTN_AGENTS if x != "compute_only"), key=lambda x: t[x])
     flops = 4.0 * sq * (w * nb) * hq * d
     out["ring_attention_qwen_like"] = {
@@ -817,10 +831,10 @@ def attention_rows(timer, torch, inputs, stream, steps=5, warmup=2):
     o = torch.empty((s, hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((hq, s), dtype=torch.float32, device=dev)
     ws = workspace(plan, torch)
-    t = {}
-    for name, ag in list(HEAD_AGENTS.items()) + [("copy_only", HEAD_COPY_ONLY)]:
-        t[name] = t_of(lambda: A.sync_head_attn(plan, cfg(**ag), *peers, *local, o, lse, 1.0 / d ** 0.5, ws, stream,
-                                                None), ws)
+    calls = {name: ((lambda ag=ag: A.sync_head_attn(plan, cfg(**ag), *peers, *local, o, lse, 1.0 / d ** 0.5, ws,
+                                                    stream, None)), ws)
+             for name, ag in list(HEAD_AGENTS.items()) + [("copy_only", HEAD_COPY_ONLY)]}
+    t = _interleaved_medians(timer, stream, calls, steps, warmup)
     best = min((x for x in HEAD_AGENTS if x != "compute_only"), key=lambda x: t[x])
     flops = 4.0 * s * s * hq * d
     out["head_parallel_attention_llama8b_like"] = {

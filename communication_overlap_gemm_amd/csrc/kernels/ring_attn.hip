@@ -143,14 +143,29 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
     else
       copy_role<kAttnThreads, true>(a.copy, gb, gn, epoch);
   }
+  // Chunks this workgroup has already waited for and acquired in this call
+  // (ids below 64): later work items read them without another wait, barrier
+  // or acquire.  Every thread takes the same waits, so every thread's copy
+  // holds the same bits.
+  uint64_t known = 0;
+  auto is_known = [&](int32_t c) { return c < 64 && ((known >> c) & 1u); };
+  auto set_known = [&](int32_t c) {
+    if (c < 64) known |= uint64_t(1) << c;
+  };
   // head-parallel attention: wait for the chunks holding plan tile t's query rows
   auto wait_queries = [&](int t) {
     if (!a.wait_chunks) return 1;
+    bool need = false;
+    for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) {
+      const int32_t c = a.dep_idx[e];
+      need = need || !(a.resident[c] || is_known(c));
+    }
+    if (!need) return 1;
     if (tid == 0) {
       bool ok = true;
       for (int64_t e = a.dep_ptr[t]; ok && e < a.dep_ptr[t + 1]; ++e) {
         const int32_t c = a.dep_idx[e];
-        if (!a.resident[c]) ok = wait_flag(a.flags, c, epoch, a.hdr, a.timeout_ticks);
+        if (!a.resident[c] && !is_known(c)) ok = wait_flag(a.flags, c, epoch, a.hdr, a.timeout_ticks);
       }
       if (ok) acquire_agent();
       s_ok = ok;
@@ -158,6 +173,8 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
     __syncthreads();
     const int ok = s_ok;
     __syncthreads();
+    if (ok)
+      for (int64_t e = a.dep_ptr[t]; e < a.dep_ptr[t + 1]; ++e) set_known(a.dep_idx[e]);
     return ok;
   };
   const int32_t slot0 = xcd_slot(gb, gn, a.nxcd);
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
     u32x4_t rk[kKLoads], rv[kVLoads];
     auto wait_chunk = [&](int pos) {
       const int32_t c = a.arrival[pos];
-      if (!a.wait_chunks || a.resident[c]) return 1;  // in place before the call
+      if (!a.wait_chunks || a.resident[c] || is_known(c)) return 1;  // in place, or already acquired
       if (tid == 0) {
         const bool ok = wait_flag(a.flags, c, epoch, a.hdr, a.timeout_ticks);
         if (ok) acquire_agent();
@@ -222,6 +239,7 @@ __global__ __launch_bounds__(kAttnThreads, kAttnWgPerCu) void ring_attn_step(Att
       __syncthreads();
       const int ok = s_ok;
       __syncthreads();
+      if (ok) set_known(c);
       return ok;
     };
     // global -> registers for the tile [t, t + kKT) of chunk at position pos
