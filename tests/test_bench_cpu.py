@@ -53,3 +53,26 @@ def test_single_row_option_names_every_row_function():
         assert callable(fn)
     with pytest.raises(SystemExit):
         _args("--row", "headline")
+
+
+def test_interleaved_rows_pool_two_rounds_in_reverse_order(monkeypatch):
+    """The other rows time their calls in two rounds, the second in reverse
+    order, and report the median of both rounds' samples, so that a drift of
+    the clock over the row weighs on every call alike."""
+    seen = []
+
+    class FakeTimer:
+        def series(self, fn, steps, warmup, cold):
+            name = fn()
+            seen.append((name, warmup))
+            base = {"a": 1.0, "b": 2.0, "c": 3.0}[name]
+            drift = 0.1 * len(seen)  # later launches run slower
+            return {"samples": [base + drift] * steps}
+
+    monkeypatch.setattr(bench, "check", lambda ws, stream: None)
+    calls = {k: ((lambda k=k: k), None) for k in ("a", "b", "c")}
+    t = bench._interleaved_medians(FakeTimer(), None, calls, steps=3, warmup=2)
+    assert [n for n, _ in seen] == ["a", "b", "c", "c", "b", "a"]
+    assert [w for _, w in seen] == [2, 2, 2, 1, 1, 1]
+    # each call's samples come from one early and one late slot: the drift is the same for all
+    assert t["a"] - 1.0 == pytest.approx(t["b"] - 2.0) == pytest.approx(t["c"] - 3.0)
