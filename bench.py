@@ -61,6 +61,8 @@ BACKENDS = {"sdma": dict(backend=SDMA, copy_teams=7), "cu8": dict(backend=CU, co
             "cu64": dict(backend=CU, copy_cus=64), "colocated": dict(backend=COLOC)}
 SWEEP_AGENTS = {
     "sdma_1_engine": dict(backend=SDMA, copy_teams=1), "sdma_7_engines": dict(backend=SDMA, copy_teams=7),
+    # 14 engines for 7 copied chunks: every chunk moves as two row pieces on two engines
+    "sdma_14_engines": dict(backend=SDMA, copy_teams=14),
     "cu32_4slices_lead2": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4, copy_lead_slice=2),
     # every slice by the compute workgroups whose first tile reads the chunk: the per-tile co-located form
     "cu32_2slices_lead_all": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=2, copy_lead_slice=2),
@@ -72,7 +74,8 @@ SWEEP_AGENTS = {
     "cu32_xgmi_ring_153": dict(backend=CU, copy_cus=32, copy_teams=1, copy_kslices=4, copy_link_gbps=153.0),
     "cu32_xgmi_mesh_153": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=4, copy_link_gbps=153.0)}
 SPLIT_SWEEP_AGENTS = {"cu32": dict(backend=CU, copy_cus=32, copy_teams=7, copy_kslices=2, copy_lead_slice=1),
-                      "sdma_7_engines": dict(backend=SDMA, copy_teams=7)}
+                      "sdma_7_engines": dict(backend=SDMA, copy_teams=7),
+                      "sdma_14_engines": dict(backend=SDMA, copy_teams=14)}
 # GEMM-RS, Llama-3-8B down-projection
 RS_SHAPE = dict(m=8192, n=4096, k=1792, world=8, divisor=64.0)
 RS_AGENTS = {"overlapped": dict(backend=EPI), "overlapped_colocated": dict(backend=COLOC, copy_teams=8),
@@ -95,13 +98,13 @@ A2A_AGENTS = {"cu32_7teams_4slices": dict(backend=CU, copy_cus=32, copy_teams=7,
 # ring attention, Qwen-like GQA
 ATTN_SHAPE = dict(sq=4096, hq=32, hkv=8, d=128, n=4096, world=8)
 ATTN_AGENTS = {"colocated": dict(backend=COLOC), "cu32_7teams": dict(backend=CU, copy_cus=32, copy_teams=7),
-               "sdma_7_engines": dict(backend=SDMA, copy_teams=7), "compute_only": dict(backend=PRESET)}
+               "sdma_14_engines": dict(backend=SDMA, copy_teams=14), "compute_only": dict(backend=PRESET)}
 
 # head-parallel attention share, Llama-3-8B-like (32 query / 8 KV heads): 8 ranks x 4096 tokens, one
 # rank's head group of 4 query heads and 1 KV head over all 32768 tokens
 HEAD_SHAPE = dict(world=8, n=4096, hq=4, hkv=1, d=128)
 HEAD_AGENTS = {"colocated": dict(backend=COLOC), "cu32_7teams": dict(backend=CU, copy_cus=32, copy_teams=7),
-               "sdma_7_engines": dict(backend=A.SYNC_COPY_SDMA, copy_teams=7), "compute_only": dict(backend=PRESET)}
+               "sdma_14_engines": dict(backend=A.SYNC_COPY_SDMA, copy_teams=14), "compute_only": dict(backend=PRESET)}
 HEAD_COPY_ONLY = dict(backend=CU, copy_cus=32, copy_teams=7, flags=A.SYNC_RUN_COPY_ONLY)
 
 ORDERS = {"row_major": A.SYNC_ORDER_ROW_MAJOR, "chunk_major": A.SYNC_ORDER_CHUNK_MAJOR,

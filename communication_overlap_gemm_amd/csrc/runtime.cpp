@@ -390,8 +390,9 @@ int prepare(sync_plan_t plan, const sync_copy_cfg* cfg_in, void* ws, int op, Cal
   sync_copy_cfg cfg{};
   cfg.backend = SYNC_COPY_SDMA;
   if (cfg_in) cfg = *cfg_in;
-  if (cfg.copy_teams < 0 || cfg.copy_teams > plan->plan.num_chunks)
-    return fail(SYNC_EINVAL, "copy_teams must be in [0, number of chunks]");
+  if (cfg.backend == SYNC_COPY_SDMA ? (cfg.copy_teams < 0 || cfg.copy_teams > std::max(plan->plan.num_chunks, kMaxSdmaEngines))
+                                     : (cfg.copy_teams < 0 || cfg.copy_teams > plan->plan.num_chunks))
+    return fail(SYNC_EINVAL, "copy_teams must be in [0, number of chunks] (SDMA: [0, max(number of chunks, 16)])");
   if (cfg.copy_teams == 0) cfg.copy_teams = 1;
   if (cfg.copy_kslices < 0 || cfg.copy_kslices > kMaxSlices) return fail(SYNC_EINVAL, "copy_kslices must be in [0, 8]");
   if (cfg.copy_kslices == 0) cfg.copy_kslices = 1;
@@ -663,7 +664,7 @@ int run_engines(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed*
   int32_t copied = 0;
   for (int32_t c = 0; c < pl.num_chunks; ++c) copied += pl.resident[c] ? 0 : 1;
   SdmaCall call;
-  int rc = sdma_begin(d.device, copied, ntensors, &call);
+  int rc = sdma_begin(d.device, copied, ntensors, cx.cfg.copy_teams, &call);
   if (rc) return rc;
   SdmaJob job{};
   for (int x = 0; x < ntensors; ++x) {
@@ -678,7 +679,6 @@ int run_engines(const Plan& pl, CallCtx& cx, DeviceState& d, DeviceState::Timed*
   job.resident = pl.resident.data();
   job.flags = cx.ws.flags;
   job.epoch_word = cx.ws.hdr + WS_SDMA_EPOCH;
-  job.engines = cx.cfg.copy_teams;
   if (tm) {
     HIP_TRY(hipEventRecord(tm->k0, cs));
     HIP_TRY(hipEventRecord(tm->c0, cs));

@@ -7,8 +7,10 @@
 // hsa_amd_memory_async_copy_on_engine, with no HIP stream in between:
 //
 //   caller stream:  gate kernel -> compute kernel (or, copy-only, a join kernel)
-//   SDMA engine e:  [wait gate] copy chunk c (each tensor) -> 4-byte copy of the
-//                   call's epoch into flag[c] (after the data copy completed)
+//   SDMA engine e:  [wait gate] copy chunk c (each tensor; with more engines
+//                   than copied chunks, one row piece of it per engine) ->
+//                   4-byte copy of the call's epoch into flag[c] (after every
+//                   piece of the chunk completed)
 //
 // The gate kernel runs when the caller's stream reaches the call: it fixes the
 // call's epoch in the workspace (the word the flag copies read) and opens the
@@ -159,7 +161,7 @@ int sdma_engine_count(int dev, int* out) {
   return SYNC_OK;
 }
 
-int sdma_begin(int dev, int32_t copied_chunks, int32_t ntensors, SdmaCall* out) {
+int sdma_begin(int dev, int32_t copied_chunks, int32_t ntensors, int32_t engines, SdmaCall* out) {
   Engines* e = nullptr;
   int rc = engines_for(dev, &e);
   if (rc) return rc;
@@ -178,10 +180,14 @@ int sdma_begin(int dev, int32_t copied_chunks, int32_t ntensors, SdmaCall* out) 
     if ((rc = make_signal(0, &s))) return rc;
     r.chunk.push_back(s);
   }
+  const int32_t used = std::max(1, std::min<int32_t>(engines, static_cast<int32_t>(e->ids.size())));
+  const int32_t pieces = std::max(1, copied_chunks > 0 ? used / copied_chunks : 1);
   hsa_signal_store_screlease(r.gate, 1);
   hsa_signal_store_screlease(r.done, copied_chunks);
-  for (int32_t i = 0; i < copied_chunks; ++i) hsa_signal_store_screlease(r.chunk[i], ntensors);
+  for (int32_t i = 0; i < copied_chunks; ++i) hsa_signal_store_screlease(r.chunk[i], ntensors * pieces);
   r.used = true;
+  out->engines = used;
+  out->pieces = pieces;
   out->record = e->next;
   out->gate_value = const_cast<int64_t*>(reinterpret_cast<volatile int64_t*>(r.gate_value));
   e->next = (e->next + 1) % kRecords;
@@ -194,7 +200,7 @@ int sdma_submit(int dev, const SdmaCall& call, const SdmaJob& job) {
   if (rc) return rc;
   std::lock_guard<std::mutex> lk(e->mu);
   Record& r = e->rec[call.record];
-  const int used = std::max(1, std::min<int>(job.engines, static_cast<int>(e->ids.size())));
+  const int32_t used = call.engines, P = call.pieces;
   int32_t copied = 0;
   for (int32_t p = 0; p < job.num_chunks; ++p) copied += job.resident[job.arrival[p]] ? 0 : 1;
   int32_t i = 0;
@@ -203,22 +209,31 @@ int sdma_submit(int dev, const SdmaCall& call, const SdmaJob& job) {
   for (int32_t p = 0; p < job.num_chunks && s == HSA_STATUS_SUCCESS; ++p) {
     const int32_t c = job.arrival[p];
     if (job.resident[c]) continue;
-    const hsa_amd_sdma_engine_id_t eng = e->ids[i % used];
     const int64_t r0 = job.chunk_begin[c], r1 = job.chunk_begin[c + 1];
-    int x = 0;
-    for (; x < job.ntensors && s == HSA_STATUS_SUCCESS; ++x) {
-      const int64_t off = r0 * job.row_bytes[x], bytes = (r1 - r0) * job.row_bytes[x];
-      s = hsa_amd_memory_async_copy_on_engine(job.dst[x] + off, e->gpu, job.src[x] + off, e->gpu,
-                                              static_cast<size_t>(bytes), 1, &r.gate, r.chunk[i], eng, true);
-      what = "SDMA chunk copy";
+    int32_t queued = 0;  // data copies of this chunk queued (the chunk signal starts at ntensors x P)
+    for (int32_t q = 0; q < P && s == HSA_STATUS_SUCCESS; ++q) {
+      const hsa_amd_sdma_engine_id_t eng = e->ids[(i * P + q) % used];
+      const int64_t p0 = r0 + (r1 - r0) * q / P, p1 = r0 + (r1 - r0) * (q + 1) / P;
+      for (int x = 0; x < job.ntensors && s == HSA_STATUS_SUCCESS; ++x) {
+        if (p1 == p0) {  // an empty piece (fewer rows than pieces): nothing to copy
+          hsa_signal_subtract_screlease(r.chunk[i], 1);
+          ++queued;
+          continue;
+        }
+        const int64_t off = p0 * job.row_bytes[x], bytes = (p1 - p0) * job.row_bytes[x];
+        s = hsa_amd_memory_async_copy_on_engine(job.dst[x] + off, e->gpu, job.src[x] + off, e->gpu,
+                                                static_cast<size_t>(bytes), 1, &r.gate, r.chunk[i], eng, true);
+        what = "SDMA chunk copy";
+        if (s == HSA_STATUS_SUCCESS) ++queued;
+      }
     }
     if (s != HSA_STATUS_SUCCESS) {
       // the copies not queued will never count the chunk signal down
-      hsa_signal_subtract_screlease(r.chunk[i], job.ntensors - (x - 1));
+      hsa_signal_subtract_screlease(r.chunk[i], job.ntensors * P - queued);
       break;
     }
     s = hsa_amd_memory_async_copy_on_engine(job.flags + c, e->gpu, job.epoch_word, e->gpu, sizeof(uint32_t), 1,
-                                            &r.chunk[i], r.done, eng, true);
+                                            &r.chunk[i], r.done, e->ids[(i * P) % used], true);
     what = "SDMA flag copy";
     if (s == HSA_STATUS_SUCCESS) ++i;
   }

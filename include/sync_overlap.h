@@ -174,8 +174,9 @@ int sync_plan_export(sync_plan_t plan, sync_plan_tables* out);
  *               (hsa_amd_memory_async_copy_on_engine; copy_teams engines, 1
  *               if 0).  On `compute` a one-workgroup gate kernel fixes the
  *               call's epoch and opens the call's gate signal, which every
- *               copy waits for; after each chunk's data copy the same engine
- *               copies the epoch into the chunk's ready flag; the compute
+ *               copy waits for; once every piece of a chunk's data copy has
+ *               landed, an engine copies the epoch into the chunk's ready
+ *               flag; the compute
  *               kernel follows on `compute`, on every CU (copy-only: a join
  *               kernel that waits for every flag).  `copy` is unused.  The
  *               host may wait (bounded) for the copies of the call made 16
@@ -236,8 +237,11 @@ typedef struct {
   int32_t copy_streaming;   /* CU and COLOCATED backends: 1 = non-temporal loads/stores in the copy
                                role; 0 = plain */
   int32_t withhold_chunk;   /* SYNC_RUN_WITHHOLD only: the chunk left out, or -1 for all */
-  int32_t copy_teams;       /* SDMA backend: engines used (copied chunk i goes to engine i mod
-                               copy_teams).  CU backend: chunks in flight at once; the copy workgroups split
+  int32_t copy_teams;       /* SDMA backend: engines used, at most max(number of chunks, 16) and
+                               the engines available (copied chunk i goes to engine i mod
+                               copy_teams; with E engines for C < E copied chunks, every chunk
+                               is cut into floor(E / C) row pieces on distinct engines and its
+                               flag is written once all of them have landed).  CU backend: chunks in flight at once; the copy workgroups split
                                into this many teams, team t taking every copy_teams-th copied
                                chunk from the t-th (copy-out: in send order, each team waiting
                                for its chunk's done flag).  0 or 1 = one chunk after another

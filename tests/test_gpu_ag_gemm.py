@@ -576,7 +576,7 @@ def test_full_size_streaming_copy(streaming):
 
 # ---- SDMA engines driven through HSA: repeated calls, several engines -------
 
-@pytest.mark.parametrize("engines", [1, 7])
+@pytest.mark.parametrize("engines", [1, 7, 14, 16])
 def test_full_size_sdma_repeated_calls(engines):
     """Back-to-back SDMA calls at the Llama-3-8B up-projection size, the peer
     region alternating between two datasets: every call's chunks land while
@@ -612,6 +612,35 @@ def test_full_size_sdma_repeated_calls(engines):
     rc, chunk = A.sync_workspace_status(ws, s)
     assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
     assert np.array_equal(c[rows, cols].cpu().numpy().astype(np.float64), exact[0])
+
+
+@pytest.mark.parametrize("rows", [[40, 2, 100, 3, 111], [64, 64, 64, 64]])
+def test_sdma_chunks_cut_into_row_pieces(rows):
+    """SDMA with more engines than copied chunks: every chunk moves as row
+    pieces on distinct engines (a chunk with fewer rows than pieces leaves
+    some of them empty) and its flag is written once all of them have landed.
+    Two calls on one workspace, 16 and 9 engines, copied rows poisoned before
+    each: the staged rows and C are exact."""
+    m, n, k, world = sum(rows), 256, 512, len(rows)
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, tile_m=128, tile_n=128, b_layout=A.SYNC_B_NK,
+                                   shard_rows=rows))
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+    for engines in (16, 9):
+        print(f"[ag] SDMA row pieces, rows {rows}, {engines} engines", flush=True)
+        a_local = bf16_poison((m, k))
+        a_local[: rows[0]] = a_peer[: rows[0]]
+        c.fill_(float("nan"))
+        A.sync_ag_gemm(plan, A.make_cfg(A.SYNC_COPY_SDMA, copy_teams=engines), a_peer, a_local, b_d, c,
+                       A.SYNC_DTYPE_F32, ws, s, None)
+        rc, chunk = A.sync_workspace_status(ws, s)
+        assert rc == A.SYNC_OK, f"device wait timed out on chunk {chunk}"
+        assert np.array_equal(host_bits(a_local), a)
+        assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
 
 
 def test_sdma_copy_only_advances_the_epoch():
