@@ -789,3 +789,39 @@ def test_copy_role_refuses_chunks_of_2_gib():
         assert ei.value.code == A.SYNC_EUNSUPPORTED and "2 GiB" in ei.value.message
     del a_peer, a_local, c
     torch.cuda.empty_cache()
+
+
+def test_trace_colocated_tiles_on_an_xcd_multiple():
+    """Co-located copy with fewer tiles than workgroups: every workgroup
+    copies, and the tiles go to the tile count rounded up to a multiple of the
+    XCD count of them.  Trace of one call: slot p ran tile order[p], each tile
+    started after the chunks it reads were released, and the XCDs that ran
+    tiles ran equally many; C is exact."""
+    m, n, k, world = 2048, 1024, 512, 4
+    a, b = inputs.gemm_operands(m, n, k, 1.0, integer=True, b_layout="nk")
+    ref = oracle.gemm_f64(a, b, m, n, k, b_layout="nk")
+    plan = A.sync_plan(A.make_desc(A.SYNC_OP_AG_GEMM, m, n, k, world, tile_m=256, tile_n=256, b_layout=A.SYNC_B_NK))
+    tabs = A.sync_plan_export(plan)
+    a_peer, b_d = dev_bits(a), dev_bits(b)
+    a_local = bf16_poison((m, k))
+    a_local[: m // world] = a_peer[: m // world]
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = workspace(plan)
+    s = torch.cuda.current_stream()
+    print("[ag] co-located trace, 32 tiles", flush=True)
+    A.sync_ag_gemm(plan, A.make_cfg(A.SYNC_COPY_COLOCATED, flags=A.SYNC_RUN_TRACE), a_peer, a_local, b_d, c,
+                   A.SYNC_DTYPE_F32, ws, s, None)
+    assert A.sync_workspace_status(ws, s)[0] == A.SYNC_OK
+    tr = A.sync_trace_export(plan, ws, s)
+    T = tabs["num_tiles"]
+    assert np.array_equal(tabs["tile_order"][tr["tile_slot"]], np.arange(T))
+    for t in range(T):
+        deps = tabs["dep_idx"][tabs["dep_ptr"][t]:tabs["dep_ptr"][t + 1]]
+        ready = [tr["chunk_ready"][ch] for ch in deps if not tabs["resident"][ch]]
+        if ready:
+            assert tr["tile_wait_end"][t] >= max(ready), f"tile {t} started before its chunks were released"
+    per_xcd = np.bincount(tr["tile_xcc"])
+    per_xcd = per_xcd[per_xcd > 0]
+    assert (per_xcd == per_xcd[0]).all(), f"tiles per XCD {per_xcd.tolist()}"
+    assert np.array_equal(host_bits(a_local), a)
+    assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
